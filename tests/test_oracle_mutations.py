@@ -1,0 +1,84 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake in a temporary copy of oracle/osdn_oracle.c (on the
+CPU, never in the committed source), builds it, swaps it in for the real
+oracle, and runs the pin tests: at least one of them has to fail.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "osdn_oracle.c")
+
+EMIT = "for (int64_t i = 0; i < K; ++i) out[i] = d[i] * kt[i];"
+MUTATIONS = {
+    "write_key_not_scaled": [("out[i] = d[i] * kt[i]", "out[i] = kt[i]")],
+    "emit_after_update": [(EMIT, ""), ("d[i] = x;", "d[i] = x; out[i] = d[i] * kt[i];")],
+    "step_sign_flipped": [("double c = eta * bp", "double c = -eta * bp")],
+    "beta_dropped_in_alignment": [("(1.0 - bp * align)", "(1.0 - align)")],
+    "no_key_norm": [("(1.0 - bp * align) / n;", "(1.0 - bp * align);")],
+    "retention_on_step_too": [("rt * d[i] + c * s[i]", "rt * (d[i] + c * s[i])")],
+    "no_clamp": [("if (clamp) {", "if (0) {")],
+    "read_with_write_key": [("acc += S[i * K + j] * kt[j];\n        u[i]",
+                             "acc += S[i * K + j] * wt[j];\n        u[i]")],
+    "write_with_read_key": [("bt * u[i] * wt[j]", "bt * u[i] * kt[j]")],
+    "write_gate_dropped": [("bt * u[i] * wt[j]", "u[i] * wt[j]")],
+    "q_scale_ignored": [("(q_scale * qt[j])", "qt[j]")],
+    "decay_ignored": [("S[e] *= at;", "S[e] *= 1.0;")],
+    "decay_applied_after_read": [
+        ("for (size_t e = 0; e < VK; ++e) S[e] *= at;\n      }", "}"),
+        ("if (u_out)", "if (alpha) { double at = alpha[at_bth(b, t, h, T, H)];"
+                       " for (size_t e = 0; e < VK; ++e) S[e] *= at; }\n      if (u_out)")],
+}
+
+
+def _pin_tests():
+    out = []
+    for name in dir(pins):
+        fn = getattr(pins, name)
+        if name.startswith("test_") and callable(fn):
+            marks = getattr(fn, "pytestmark", [])
+            params = [m for m in marks if m.name == "parametrize"]
+            if not params:
+                out.append((name, fn, {}))
+                continue
+            combos = [{}]
+            for m in params:
+                argnames = [a.strip() for a in m.args[0].split(",")]
+                new = []
+                for c in combos:
+                    for val in m.args[1]:
+                        vals = val if len(argnames) > 1 else (val,)
+                        d = dict(c)
+                        d.update(zip(argnames, vals))
+                        new.append(d)
+                combos = new
+            out.extend((name, fn, c) for c in combos)
+    return out
+
+
+@pytest.mark.parametrize("mutation", sorted(MUTATIONS))
+def test_pins_catch_mutation(mutation, tmp_path, monkeypatch):
+    src = open(SRC).read()
+    for old, new in MUTATIONS[mutation]:
+        assert old in src, "mutation anchor missing: %r" % old
+        src = src.replace(old, new, 1)
+    cfile = tmp_path / "mut.c"
+    cfile.write_text(src)
+    so = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-o",
+                    str(so), str(cfile), "-lm"], check=True)
+    lib = oracle.bind(ctypes.CDLL(str(so)))
+    monkeypatch.setattr(oracle, "_lib", lib)
+    failed = []
+    for name, fn, kwargs in _pin_tests():
+        try:
+            fn(oracle_lib=oracle, **kwargs) if "oracle_lib" in fn.__code__.co_varnames else fn(**kwargs)
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(name)
+    assert failed, "no pin caught the planted mistake %s" % mutation
