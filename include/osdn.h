@@ -1,0 +1,162 @@
+/*
+ * osdn.h -- C ABI of the OSDN (Online Scaled DeltaNet) forward hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the two-phase forward of "OSDN: Improving Delta Rule with
+ * Provable Online Preconditioning in Linear Attention" (Zhou et al.,
+ * arXiv:2605.13473):
+ *
+ *   phase 1 (osdn_precond_scan) -- the online preconditioner sweep of
+ *     Section 4.2, Eq.(4) and Algorithm 1, with the retention-gated (APF) form
+ *     of Section 4.4, Eq.(7), and the non-beta-aware form of Appendix B.  Per
+ *     (b,h), starting from d = d1 (ones when NULL; d1 is not clamped):
+ *         k~_t = d (.) k_t                    (emitted before the update)
+ *         s = k_t (.) k_t,  n = max(sum s, eps),  b' = beta_t (or 1)
+ *         d = clip(r_t d + eta b' (1 - b' <d, s>) / n * s, d_min, d_max)
+ *
+ *   phase 2 (osdn_chunk_fwd) -- the delta rule with the preconditioned write
+ *     key, Section 4.3 Eq.(5), evaluated chunkwise with the WY form of
+ *     Appendix A.2, Eqs.(8)-(11); with a decay alpha it is the Gated DeltaNet
+ *     variant of Appendix B.1, Eqs.(13)-(15) (post-gate residual).  Per (b,h),
+ *     from S = S0 (zeros when NULL), S in R^{V x K}:
+ *         Sb = alpha_t S  (Sb = S without alpha)
+ *         S  = Sb + beta_t (v_t - Sb k_t) k~_t^T
+ *         o_t = S (q_scale q_t)
+ *
+ *   osdn_fwd runs both phases on one stream.
+ *
+ * Conventions for every entry point:
+ *  - Sequence tensors are contiguous row-major [B,T,H,X] (the paper's layout
+ *    before chunking, Appendix C); per-head vectors [B,H,X]; the state S is
+ *    [B,H,V,K] in float32.  q, k, v, k_tilde and o share desc->dtype; beta,
+ *    r, alpha, d1, d_out, S0 and S_out are float32.
+ *  - Pointers are DEVICE pointers owned by the caller; the library allocates
+ *    nothing and keeps no state between calls.  stream is a hipStream_t (NULL
+ *    = the default stream); work is enqueued asynchronously and outputs are
+ *    valid once the stream has been synchronised.
+ *  - Arguments are validated before anything is launched; on failure nothing
+ *    is written and a status other than OSDN_OK is returned
+ *    (osdn_last_error() then holds a message for the calling thread).  A HIP
+ *    launch failure returns OSDN_EHIP.
+ *  - d_out may alias d1 and S_out may alias S0 (in-place state update); no
+ *    other aliasing between inputs and outputs is allowed.
+ *  - Device pointers must be aligned to 16 bytes.  Device data is not checked:
+ *    alpha must lie in (0, 1] and all inputs must be finite.
+ */
+#ifndef OSDN_H
+#define OSDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { OSDN_F32 = 0, OSDN_BF16 = 1 } osdn_dtype;
+
+typedef enum {
+  OSDN_OK = 0,
+  OSDN_EINVAL = 1,       /* malformed argument (sizes, NULL, alignment, box)  */
+  OSDN_EUNSUPPORTED = 2, /* well formed but outside what the kernels cover   */
+  OSDN_EHIP = 3          /* the HIP runtime reported an error                */
+} osdn_status;
+
+/*
+ * Problem description.  Arguments follow the paper's statement of the
+ * problem (Algorithm 1's inputs; the chunk interface of Appendix C).
+ *   B, T, H     batch, tokens, heads; B, H >= 1, T >= 0.
+ *   K, V        key / value head dims; 1 <= K <= 256 for phase 1,
+ *               1 <= K, V <= 128 for phase 2.
+ *   chunk       chunk length C of the WY form, 1 <= C <= 64.  The result does
+ *               not depend on C beyond rounding (chunkwise equals sequential).
+ *   dtype       osdn_dtype of q, k, v, k_tilde, o.
+ *   eta         phase-1 step size (>= 0).
+ *   d_min,d_max box of the projection; 0 < d_min <= d_max when clamp != 0.
+ *   clamp       1: project onto [d_min, d_max] after every step; 0: no box.
+ *   eps         floor of the squared key norm (> 0).
+ *   q_scale     scale applied to q in the readout (1 = o_t = S_t q_t of the
+ *               main text; K^-1/2 = the scaling used by the paper's listing).
+ *   beta_aware  1: beta-aware feedback (Eq.(4)); 0: beta' = 1 in phase 1
+ *               only (Appendix B); the memory write always uses beta.
+ */
+typedef struct osdn_desc {
+  int64_t B, T, H, K, V;
+  int32_t chunk;
+  int32_t dtype;
+  float eta, d_min, d_max;
+  int32_t clamp;
+  float eps;
+  float q_scale;
+  int32_t beta_aware;
+} osdn_desc;
+
+/* Fill *desc with the given sizes and the paper's defaults: chunk 64,
+ * eta 0.003, box [0.5, 2], clamp on, eps 1e-6, q_scale 1, beta-aware, bf16. */
+osdn_status osdn_desc_init(osdn_desc *desc, int64_t B, int64_t T, int64_t H,
+                           int64_t K, int64_t V);
+
+/* Host-only validation of a descriptor (no device work). */
+osdn_status osdn_validate(const osdn_desc *desc);
+
+/*
+ * Phase 1, Algorithm 1 / Eq.(7) (Section 4.2, Section 4.4, Appendix B).
+ *   k       [B,T,H,K] dtype    keys (read)
+ *   beta    [B,T,H]   f32      write gates (read)
+ *   r       [B,T,H]   f32      APF retention r_{t,h}, or NULL for r = 1
+ *   d1      [B,H,K]   f32      initial preconditioner, or NULL for ones
+ *   k_tilde [B,T,H,K] dtype    OUT: write keys d_t (.) k_t (rounded to dtype)
+ *   d_out   [B,H,K]   f32      OUT: d_{T+1}, or NULL (may alias d1)
+ */
+osdn_status osdn_precond_scan(const osdn_desc *desc, const void *k,
+                              const float *beta, const float *r,
+                              const float *d1, void *k_tilde, float *d_out,
+                              void *stream);
+
+/*
+ * Phase 2, chunkwise WY delta rule with the write-key substitution of Eq.(6)
+ * (Appendix A.2 Eqs.(8)-(11); Appendix B.1 Eqs.(13)-(15) when alpha != NULL).
+ *   q, k, k_tilde [B,T,H,K] dtype   queries, physical keys, write keys
+ *   v       [B,T,H,V] dtype          values
+ *   beta    [B,T,H]   f32            write gates
+ *   alpha   [B,T,H]   f32            state decay in (0,1], or NULL (OSDN)
+ *   S0      [B,H,V,K] f32            initial state, or NULL for zeros
+ *   o       [B,T,H,V] dtype          OUT: o_t = S_t (q_scale q_t)
+ *   S_out   [B,H,V,K] f32            OUT: S_T, or NULL (may alias S0)
+ */
+osdn_status osdn_chunk_fwd(const osdn_desc *desc, const void *q,
+                           const void *k, const void *k_tilde, const void *v,
+                           const float *beta, const float *alpha,
+                           const float *S0, void *o, float *S_out,
+                           void *stream);
+
+/* Bytes of device workspace osdn_fwd needs when k_tilde_out is NULL (room
+ * for the write keys between the phases); 0 on an invalid descriptor. */
+size_t osdn_fwd_workspace_bytes(const osdn_desc *desc);
+
+/*
+ * Both phases on one stream (the two-phase schedule of Section 4.5).
+ * Arguments as above; k_tilde_out [B,T,H,K] dtype receives the write keys
+ * when not NULL, otherwise they go to workspace, which must then hold at
+ * least osdn_fwd_workspace_bytes(desc) bytes.
+ */
+osdn_status osdn_fwd(const osdn_desc *desc, const void *q, const void *k,
+                     const void *v, const float *beta, const float *r,
+                     const float *alpha, const float *d1, const float *S0,
+                     void *o, float *S_out, float *d_out, void *k_tilde_out,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Name of a status code (static string). */
+const char *osdn_status_str(int status);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char *osdn_last_error(void);
+
+/* Library version, (major << 16) | minor. */
+int osdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSDN_H */

@@ -1,0 +1,229 @@
+"""OSDN forward hot path on MI355X: thin Python binding of libosdn.so.
+
+The three calls mirror the C ABI of include/osdn.h (same names, same argument
+order); this module only checks tensor metadata, allocates outputs through
+PyTorch and passes device pointers plus the current HIP stream.  Every step of
+the computation runs in the library's gfx950 kernels.  There is no fallback:
+if libosdn.so is missing or cannot be loaded every call raises.
+
+Paper: "OSDN: Improving Delta Rule with Provable Online Preconditioning in
+Linear Attention" (arXiv:2605.13473) -- phase 1 is Algorithm 1 / Eq.(4) with
+the APF retention of Eq.(7); phase 2 is the chunkwise delta rule with the
+write key substituted in the chunk Gram and the local score (Eq.(6),
+Appendix A.2), optionally gated (Appendix B.1).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["precond_scan", "chunk_fwd", "fwd", "fwd_workspace_bytes", "Desc",
+           "OsdnError", "library_path", "load", "F32", "BF16"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libosdn.so")
+_lib = None
+
+F32, BF16 = 0, 1
+OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
+
+SYMBOLS = ("osdn_desc_init", "osdn_validate", "osdn_precond_scan", "osdn_chunk_fwd",
+           "osdn_fwd_workspace_bytes", "osdn_fwd", "osdn_status_str",
+           "osdn_last_error", "osdn_version")
+
+
+class OsdnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s: %s" % (status_name(status), message))
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    """Mirror of struct osdn_desc."""
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("V", ctypes.c_int64), ("chunk", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("eta", ctypes.c_float), ("d_min", ctypes.c_float),
+                ("d_max", ctypes.c_float), ("clamp", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("q_scale", ctypes.c_float), ("beta_aware", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libosdn.so (raises if it is missing) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libosdn.so not found at %s; build it with "
+                           "`python -m preconditioned_delta_rule_amd.build`" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, fp, i64, ci = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    dp = ctypes.POINTER(Desc)
+    lib.osdn_desc_init.argtypes = [dp, i64, i64, i64, i64, i64]
+    lib.osdn_validate.argtypes = [dp]
+    lib.osdn_precond_scan.argtypes = [dp, vp, fp, fp, fp, vp, fp, vp]
+    lib.osdn_chunk_fwd.argtypes = [dp, vp, vp, vp, vp, fp, fp, fp, vp, fp, vp]
+    lib.osdn_fwd_workspace_bytes.argtypes = [dp]
+    lib.osdn_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.osdn_fwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp, vp,
+                             ctypes.c_size_t, vp]
+    lib.osdn_status_str.argtypes = [ci]
+    lib.osdn_status_str.restype = ctypes.c_char_p
+    lib.osdn_last_error.argtypes = []
+    lib.osdn_last_error.restype = ctypes.c_char_p
+    for name in ("osdn_desc_init", "osdn_validate", "osdn_precond_scan", "osdn_chunk_fwd",
+                 "osdn_fwd", "osdn_version"):
+        getattr(lib, name).restype = ci
+    _lib = lib
+    return lib
+
+
+def status_name(status) -> str:
+    try:
+        return load().osdn_status_str(int(status)).decode()
+    except Exception:
+        return "status %d" % status
+
+
+def _check(status):
+    if status != OK:
+        raise OsdnError(status, load().osdn_last_error().decode())
+
+
+def make_desc(B, T, H, K, V, *, dtype=BF16, chunk=64, eta=0.003, d_min=0.5, d_max=2.0,
+              clamp=True, eps=1e-6, q_scale=1.0, beta_aware=True) -> Desc:
+    d = Desc()
+    _check(load().osdn_desc_init(ctypes.byref(d), B, T, H, K, V))
+    d.dtype, d.chunk = int(dtype), int(chunk)
+    d.eta, d.d_min, d.d_max = float(eta), float(d_min), float(d_max)
+    d.clamp, d.eps, d.q_scale = int(bool(clamp)), float(eps), float(q_scale)
+    d.beta_aware = int(bool(beta_aware))
+    return d
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def precond_scan(k, beta, r=None, d1=None, *, eta=0.003, d_min=0.5, d_max=2.0,
+                 clamp=True, eps=1e-6, beta_aware=True, k_tilde=None, d_out=None):
+    """Phase 1.  k [B,T,H,K] (bf16/f32), beta and r [B,T,H] f32, d1 [B,H,K] f32.
+    Returns (k_tilde [B,T,H,K] in k's dtype, d_out [B,H,K] f32)."""
+    B, T, H, K = k.shape
+    dev, f32 = k.device, torch.float32
+    _need(k, "k", (B, T, H, K), k.dtype, dev)
+    _need(beta, "beta", (B, T, H), f32, dev)
+    _need(r, "r", (B, T, H), f32, dev)
+    _need(d1, "d1", (B, H, K), f32, dev)
+    if k_tilde is None:
+        k_tilde = torch.empty_like(k)
+    if d_out is None:
+        d_out = torch.empty((B, H, K), dtype=f32, device=dev)
+    _need(k_tilde, "k_tilde", (B, T, H, K), k.dtype, dev)
+    _need(d_out, "d_out", (B, H, K), f32, dev)
+    desc = make_desc(B, T, H, K, K, dtype=_dtype_code(k), eta=eta, d_min=d_min,
+                     d_max=d_max, clamp=clamp, eps=eps, beta_aware=beta_aware)
+    _check(load().osdn_precond_scan(ctypes.byref(desc), _ptr(k), _ptr(beta), _ptr(r),
+                                    _ptr(d1), _ptr(k_tilde), _ptr(d_out), _stream(dev)))
+    return k_tilde, d_out
+
+
+def chunk_fwd(q, k, k_tilde, v, beta, alpha=None, S0=None, *, chunk=64, q_scale=1.0,
+              o=None, S_out=None):
+    """Phase 2.  q, k, k_tilde [B,T,H,K], v [B,T,H,V] (one dtype), beta and
+    alpha [B,T,H] f32, S0 [B,H,V,K] f32.  Returns (o [B,T,H,V], S_out [B,H,V,K])."""
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dev, dt, f32 = q.device, q.dtype, torch.float32
+    for name, t in (("q", q), ("k", k), ("k_tilde", k_tilde)):
+        _need(t, name, (B, T, H, K), dt, dev)
+    _need(v, "v", (B, T, H, V), dt, dev)
+    _need(beta, "beta", (B, T, H), f32, dev)
+    _need(alpha, "alpha", (B, T, H), f32, dev)
+    _need(S0, "S0", (B, H, V, K), f32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, V), dtype=dt, device=dev)
+    if S_out is None:
+        S_out = torch.empty((B, H, V, K), dtype=f32, device=dev)
+    _need(o, "o", (B, T, H, V), dt, dev)
+    _need(S_out, "S_out", (B, H, V, K), f32, dev)
+    desc = make_desc(B, T, H, K, V, dtype=_dtype_code(q), chunk=chunk, q_scale=q_scale)
+    _check(load().osdn_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(k_tilde), _ptr(v),
+                                 _ptr(beta), _ptr(alpha), _ptr(S0), _ptr(o), _ptr(S_out),
+                                 _stream(dev)))
+    return o, S_out
+
+
+def fwd_workspace_bytes(B, T, H, K, V, dtype=BF16, chunk=64) -> int:
+    desc = make_desc(B, T, H, K, V, dtype=dtype, chunk=chunk)
+    return int(load().osdn_fwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def fwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, chunk=64, eta=0.003,
+        d_min=0.5, d_max=2.0, clamp=True, eps=1e-6, q_scale=1.0, beta_aware=True,
+        o=None, S_out=None, d_out=None, k_tilde_out=None, workspace=None):
+    """Both phases on the current stream.  Returns (o, S_out, d_out)."""
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dev, dt, f32 = q.device, q.dtype, torch.float32
+    _need(k, "k", (B, T, H, K), dt, dev)
+    _need(v, "v", (B, T, H, V), dt, dev)
+    _need(beta, "beta", (B, T, H), f32, dev)
+    _need(r, "r", (B, T, H), f32, dev)
+    _need(alpha, "alpha", (B, T, H), f32, dev)
+    _need(d1, "d1", (B, H, K), f32, dev)
+    _need(S0, "S0", (B, H, V, K), f32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, V), dtype=dt, device=dev)
+    if S_out is None:
+        S_out = torch.empty((B, H, V, K), dtype=f32, device=dev)
+    if d_out is None:
+        d_out = torch.empty((B, H, K), dtype=f32, device=dev)
+    _need(k_tilde_out, "k_tilde_out", (B, T, H, K), dt, dev)
+    desc = make_desc(B, T, H, K, V, dtype=_dtype_code(q), chunk=chunk, eta=eta, d_min=d_min,
+                     d_max=d_max, clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware)
+    ws_bytes = 0
+    if k_tilde_out is None:
+        need = int(load().osdn_fwd_workspace_bytes(ctypes.byref(desc)))
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on %s" % dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().osdn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r),
+                           _ptr(alpha), _ptr(d1), _ptr(S0), _ptr(o), _ptr(S_out), _ptr(d_out),
+                           _ptr(k_tilde_out), _ptr(workspace if k_tilde_out is None else None),
+                           ctypes.c_size_t(ws_bytes), _stream(dev)))
+    return o, S_out, d_out

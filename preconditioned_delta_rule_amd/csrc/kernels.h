@@ -1,0 +1,41 @@
+// Internal launch interface between the C ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace osdn {
+
+struct ScanArgs {
+  const void *k;        // [B,T,H,K]
+  const float *beta;    // [B,T,H]
+  const float *r;       // [B,T,H] or null
+  const float *d1;      // [B,H,K] or null
+  void *k_tilde;        // [B,T,H,K]
+  float *d_out;         // [B,H,K] or null
+  int64_t B, T, H, K;
+  float eta, d_min, d_max, eps;
+  int clamp, beta_aware;
+};
+
+struct ChunkArgs {
+  const void *q, *k, *kt, *v;  // [B,T,H,K] / [B,T,H,V]
+  const float *beta;           // [B,T,H]
+  const float *alpha;          // [B,T,H] or null
+  const float *S0;             // [B,H,V,K] or null
+  void *o;                     // [B,T,H,V]
+  float *S_out;                // [B,H,V,K] or null
+  int64_t B, T, H, K, V;
+  int C;
+  float q_scale;
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_precond_scan(const ScanArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_chunk_generic(const ChunkArgs &a, bool bf16, hipStream_t s);
+hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s);
+
+// Shape coverage of the specialised MFMA path (bf16, K = V = 128, C = 64).
+bool chunk_mfma_supported(const ChunkArgs &a, bool bf16);
+
+}  // namespace osdn

@@ -1,0 +1,263 @@
+// C ABI of the OSDN forward hot path: argument validation and dispatch to the
+// gfx950 kernels.  Declarations and the argument contract are in include/osdn.h.
+#include "osdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+osdn_status fail(osdn_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+osdn_status fail(osdn_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+osdn_status ok() {
+  g_last_error.clear();
+  return OSDN_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_bytes(int32_t dtype) { return dtype == OSDN_BF16 ? 2 : 4; }
+
+osdn_status check_ptr(const void *p, const char *name, bool required) {
+  if (!p) {
+    if (required) return fail(OSDN_EINVAL, "%s must not be NULL", name);
+    return OSDN_OK;
+  }
+  if (!aligned16(p)) return fail(OSDN_EINVAL, "%s is not 16-byte aligned", name);
+  return OSDN_OK;
+}
+
+#define OSDN_TRY(expr)                 \
+  do {                                 \
+    osdn_status _st = (expr);          \
+    if (_st != OSDN_OK) return _st;    \
+  } while (0)
+
+// Common descriptor checks; `phase` 1 = scan, 2 = chunk, 3 = both.
+osdn_status validate(const osdn_desc *d, int phase) {
+  if (!d) return fail(OSDN_EINVAL, "desc must not be NULL");
+  if (d->B < 1 || d->H < 1 || d->T < 0)
+    return fail(OSDN_EINVAL, "need B >= 1, H >= 1, T >= 0 (got B=%lld H=%lld T=%lld)",
+                (long long)d->B, (long long)d->H, (long long)d->T);
+  if (d->dtype != OSDN_F32 && d->dtype != OSDN_BF16)
+    return fail(OSDN_EINVAL, "dtype must be OSDN_F32 or OSDN_BF16 (got %d)", d->dtype);
+  if (d->K < 1) return fail(OSDN_EINVAL, "K must be >= 1 (got %lld)", (long long)d->K);
+  if ((phase & 2) && d->V < 1) return fail(OSDN_EINVAL, "V must be >= 1 (got %lld)", (long long)d->V);
+  // element counts must stay far from int64 overflow
+  const double big = 4.0e18;
+  if ((double)d->B * (double)d->T * (double)d->H * (double)(d->K > d->V ? d->K : d->V) > big ||
+      (double)d->B * (double)d->H * (double)d->K * (double)d->V > big)
+    return fail(OSDN_EINVAL, "problem size overflows 64-bit indexing");
+  if (phase & 1) {
+    if (!std::isfinite(d->eta) || d->eta < 0.0f) return fail(OSDN_EINVAL, "eta must be finite and >= 0");
+    if (!std::isfinite(d->eps) || !(d->eps > 0.0f)) return fail(OSDN_EINVAL, "eps must be finite and > 0");
+    if (d->clamp) {
+      if (!std::isfinite(d->d_min) || !std::isfinite(d->d_max) || !(d->d_min > 0.0f) || d->d_min > d->d_max)
+        return fail(OSDN_EINVAL, "box needs finite 0 < d_min <= d_max (got [%g, %g])", d->d_min, d->d_max);
+    }
+    if (d->K > 256) return fail(OSDN_EUNSUPPORTED, "phase 1 supports K <= 256 (got %lld)", (long long)d->K);
+  }
+  if (phase & 2) {
+    if (d->chunk < 1) return fail(OSDN_EINVAL, "chunk must be >= 1 (got %d)", d->chunk);
+    if (d->chunk > 64) return fail(OSDN_EUNSUPPORTED, "chunk must be <= 64 (got %d)", d->chunk);
+    if (d->K > 128 || d->V > 128)
+      return fail(OSDN_EUNSUPPORTED, "phase 2 supports K, V <= 128 (got K=%lld V=%lld)", (long long)d->K,
+                  (long long)d->V);
+    if (!std::isfinite(d->q_scale)) return fail(OSDN_EINVAL, "q_scale must be finite");
+  }
+  return OSDN_OK;
+}
+
+osdn_status hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(OSDN_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return OSDN_OK;
+}
+
+osdn::ScanArgs scan_args(const osdn_desc *d, const void *k, const float *beta, const float *r,
+                         const float *d1, void *k_tilde, float *d_out) {
+  osdn::ScanArgs a;
+  a.k = k;
+  a.beta = beta;
+  a.r = r;
+  a.d1 = d1;
+  a.k_tilde = k_tilde;
+  a.d_out = d_out;
+  a.B = d->B;
+  a.T = d->T;
+  a.H = d->H;
+  a.K = d->K;
+  a.eta = d->eta;
+  a.d_min = d->d_min;
+  a.d_max = d->d_max;
+  a.eps = d->eps;
+  a.clamp = d->clamp ? 1 : 0;
+  a.beta_aware = d->beta_aware ? 1 : 0;
+  return a;
+}
+
+osdn::ChunkArgs chunk_args(const osdn_desc *d, const void *q, const void *k, const void *kt, const void *v,
+                           const float *beta, const float *alpha, const float *S0, void *o, float *S_out) {
+  osdn::ChunkArgs a;
+  a.q = q;
+  a.k = k;
+  a.kt = kt;
+  a.v = v;
+  a.beta = beta;
+  a.alpha = alpha;
+  a.S0 = S0;
+  a.o = o;
+  a.S_out = S_out;
+  a.B = d->B;
+  a.T = d->T;
+  a.H = d->H;
+  a.K = d->K;
+  a.V = d->V;
+  a.C = d->chunk;
+  a.q_scale = d->q_scale;
+  return a;
+}
+
+osdn_status run_scan(const osdn_desc *d, const osdn::ScanArgs &a, hipStream_t s) {
+  return hip_status(osdn::launch_precond_scan(a, d->dtype == OSDN_BF16, s), "phase-1 launch");
+}
+
+osdn_status run_chunk(const osdn_desc *d, const osdn::ChunkArgs &a, hipStream_t s) {
+  const bool bf = d->dtype == OSDN_BF16;
+  if (osdn::chunk_mfma_supported(a, bf)) return hip_status(osdn::launch_chunk_mfma(a, s), "phase-2 launch");
+  return hip_status(osdn::launch_chunk_generic(a, bf, s), "phase-2 launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int osdn_version(void) { return (1 << 16) | 0; }
+
+const char *osdn_status_str(int status) {
+  switch (status) {
+    case OSDN_OK: return "OSDN_OK";
+    case OSDN_EINVAL: return "OSDN_EINVAL";
+    case OSDN_EUNSUPPORTED: return "OSDN_EUNSUPPORTED";
+    case OSDN_EHIP: return "OSDN_EHIP";
+    default: return "OSDN_UNKNOWN_STATUS";
+  }
+}
+
+const char *osdn_last_error(void) { return g_last_error.c_str(); }
+
+osdn_status osdn_desc_init(osdn_desc *d, int64_t B, int64_t T, int64_t H, int64_t K, int64_t V) {
+  if (!d) return fail(OSDN_EINVAL, "desc must not be NULL");
+  std::memset(d, 0, sizeof *d);
+  d->B = B;
+  d->T = T;
+  d->H = H;
+  d->K = K;
+  d->V = V;
+  d->chunk = 64;
+  d->dtype = OSDN_BF16;
+  d->eta = 0.003f;
+  d->d_min = 0.5f;
+  d->d_max = 2.0f;
+  d->clamp = 1;
+  d->eps = 1e-6f;
+  d->q_scale = 1.0f;
+  d->beta_aware = 1;
+  return ok();
+}
+
+osdn_status osdn_validate(const osdn_desc *d) {
+  OSDN_TRY(validate(d, 3));
+  return ok();
+}
+
+osdn_status osdn_precond_scan(const osdn_desc *d, const void *k, const float *beta, const float *r,
+                              const float *d1, void *k_tilde, float *d_out, void *stream) {
+  OSDN_TRY(validate(d, 1));
+  const bool need_seq = d->T > 0;
+  OSDN_TRY(check_ptr(k, "k", need_seq));
+  OSDN_TRY(check_ptr(beta, "beta", need_seq));
+  OSDN_TRY(check_ptr(r, "r", false));
+  OSDN_TRY(check_ptr(d1, "d1", false));
+  OSDN_TRY(check_ptr(k_tilde, "k_tilde", need_seq));
+  OSDN_TRY(check_ptr(d_out, "d_out", false));
+  if (k_tilde && k_tilde == k) return fail(OSDN_EINVAL, "k_tilde must not alias k");
+  OSDN_TRY(run_scan(d, scan_args(d, k, beta, r, d1, k_tilde, d_out), static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+osdn_status osdn_chunk_fwd(const osdn_desc *d, const void *q, const void *k, const void *k_tilde, const void *v,
+                           const float *beta, const float *alpha, const float *S0, void *o, float *S_out,
+                           void *stream) {
+  OSDN_TRY(validate(d, 2));
+  const bool need_seq = d->T > 0;
+  OSDN_TRY(check_ptr(q, "q", need_seq));
+  OSDN_TRY(check_ptr(k, "k", need_seq));
+  OSDN_TRY(check_ptr(k_tilde, "k_tilde", need_seq));
+  OSDN_TRY(check_ptr(v, "v", need_seq));
+  OSDN_TRY(check_ptr(beta, "beta", need_seq));
+  OSDN_TRY(check_ptr(alpha, "alpha", false));
+  OSDN_TRY(check_ptr(S0, "S0", false));
+  OSDN_TRY(check_ptr(o, "o", need_seq));
+  OSDN_TRY(check_ptr(S_out, "S_out", false));
+  if (o && (o == q || o == k || o == k_tilde || o == v)) return fail(OSDN_EINVAL, "o must not alias an input");
+  OSDN_TRY(run_chunk(d, chunk_args(d, q, k, k_tilde, v, beta, alpha, S0, o, S_out),
+                     static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+size_t osdn_fwd_workspace_bytes(const osdn_desc *d) {
+  if (validate(d, 3) != OSDN_OK) return 0;
+  size_t n = (size_t)d->B * (size_t)d->T * (size_t)d->H * (size_t)d->K * elem_bytes(d->dtype);
+  return (n + 255) & ~(size_t)255;
+}
+
+osdn_status osdn_fwd(const osdn_desc *d, const void *q, const void *k, const void *v, const float *beta,
+                     const float *r, const float *alpha, const float *d1, const float *S0, void *o, float *S_out,
+                     float *d_out, void *k_tilde_out, void *workspace, size_t workspace_bytes, void *stream) {
+  OSDN_TRY(validate(d, 3));
+  const bool need_seq = d->T > 0;
+  OSDN_TRY(check_ptr(q, "q", need_seq));
+  OSDN_TRY(check_ptr(k, "k", need_seq));
+  OSDN_TRY(check_ptr(v, "v", need_seq));
+  OSDN_TRY(check_ptr(beta, "beta", need_seq));
+  OSDN_TRY(check_ptr(r, "r", false));
+  OSDN_TRY(check_ptr(alpha, "alpha", false));
+  OSDN_TRY(check_ptr(d1, "d1", false));
+  OSDN_TRY(check_ptr(S0, "S0", false));
+  OSDN_TRY(check_ptr(o, "o", need_seq));
+  OSDN_TRY(check_ptr(S_out, "S_out", false));
+  OSDN_TRY(check_ptr(d_out, "d_out", false));
+  OSDN_TRY(check_ptr(k_tilde_out, "k_tilde_out", false));
+  void *kt = k_tilde_out;
+  if (!kt && need_seq) {
+    OSDN_TRY(check_ptr(workspace, "workspace", true));
+    const size_t need = osdn_fwd_workspace_bytes(d);
+    if (workspace_bytes < need)
+      return fail(OSDN_EINVAL, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
+    kt = workspace;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  OSDN_TRY(run_scan(d, scan_args(d, k, beta, r, d1, kt, d_out), s));
+  OSDN_TRY(run_chunk(d, chunk_args(d, q, k, kt, v, beta, alpha, S0, o, S_out), s));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+"""The C-ABI library loads, exports every symbol include/osdn.h declares, and
+rejects malformed arguments on the host (no GPU work is started here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import preconditioned_delta_rule_amd as osdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "osdn.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(osdn_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(osdn.library_path()):
+        pytest.fail("libosdn.so is not built; run __graft_entry__.build() first")
+    return osdn.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    syms = declared_symbols()
+    assert len(syms) >= 9
+    for s in syms:
+        assert hasattr(lib, s), "libosdn.so does not export %s" % s
+    assert set(syms) == set(osdn.SYMBOLS)
+
+
+def test_desc_layout_and_defaults(lib):
+    d = osdn.Desc()
+    assert lib.osdn_desc_init(ctypes.byref(d), 4, 4096, 16, 128, 128) == osdn.OK
+    assert (d.B, d.T, d.H, d.K, d.V) == (4, 4096, 16, 128, 128)
+    assert d.chunk == 64 and d.dtype == osdn.BF16 and d.clamp == 1 and d.beta_aware == 1
+    assert d.eta == pytest.approx(0.003) and d.eps == pytest.approx(1e-6)
+    assert (d.d_min, d.d_max, d.q_scale) == (0.5, 2.0, 1.0)
+    assert ctypes.sizeof(osdn.Desc) == 80
+    assert lib.osdn_validate(ctypes.byref(d)) == osdn.OK
+    assert lib.osdn_version() >> 16 == 1
+
+
+def test_status_strings(lib):
+    names = [lib.osdn_status_str(i).decode() for i in range(4)]
+    assert names == ["OSDN_OK", "OSDN_EINVAL", "OSDN_EUNSUPPORTED", "OSDN_EHIP"]
+
+
+BAD = [
+    (dict(B=0), osdn.EINVAL), (dict(H=0), osdn.EINVAL), (dict(T=-1), osdn.EINVAL),
+    (dict(K=0), osdn.EINVAL), (dict(V=0), osdn.EINVAL), (dict(chunk=0), osdn.EINVAL),
+    (dict(chunk=65), osdn.EUNSUPPORTED), (dict(K=129), osdn.EUNSUPPORTED),
+    (dict(V=200), osdn.EUNSUPPORTED), (dict(dtype=7), osdn.EINVAL),
+    (dict(eta=-1.0), osdn.EINVAL), (dict(eps=0.0), osdn.EINVAL),
+    (dict(d_min=2.0, d_max=1.0), osdn.EINVAL), (dict(d_min=0.0), osdn.EINVAL),
+    (dict(q_scale=float("inf")), osdn.EINVAL), (dict(eta=float("nan")), osdn.EINVAL),
+]
+
+
+@pytest.mark.parametrize("change,status", BAD)
+def test_validation_rejects(lib, change, status):
+    d = osdn.Desc()
+    lib.osdn_desc_init(ctypes.byref(d), 2, 16, 2, 16, 16)
+    for k, v in change.items():
+        setattr(d, k, v)
+    assert lib.osdn_validate(ctypes.byref(d)) == status
+    assert lib.osdn_last_error().decode() != ""
+    assert lib.osdn_fwd_workspace_bytes(ctypes.byref(d)) == 0
+
+
+def test_box_unchecked_without_clamp(lib):
+    d = osdn.Desc()
+    lib.osdn_desc_init(ctypes.byref(d), 1, 8, 1, 16, 16)
+    d.clamp, d.d_min, d.d_max = 0, 3.0, 1.0
+    assert lib.osdn_validate(ctypes.byref(d)) == osdn.OK
+
+
+def test_scan_only_limits(lib):
+    # phase 1 alone accepts K up to 256, phase 2 does not
+    d = osdn.Desc()
+    lib.osdn_desc_init(ctypes.byref(d), 1, 8, 1, 256, 16)
+    assert lib.osdn_validate(ctypes.byref(d)) == osdn.EUNSUPPORTED
+    d.K = 300
+    null = ctypes.c_void_p(None)
+    st = lib.osdn_precond_scan(ctypes.byref(d), null, null, null, null, null, null, null)
+    assert st == osdn.EUNSUPPORTED
+
+
+def test_null_and_misaligned_pointers_rejected_before_launch(lib):
+    d = osdn.Desc()
+    lib.osdn_desc_init(ctypes.byref(d), 1, 8, 1, 16, 16)
+    null = ctypes.c_void_p(None)
+    st = lib.osdn_precond_scan(ctypes.byref(d), null, null, null, null, null, null, null)
+    assert st == osdn.EINVAL and "k must not be NULL" in lib.osdn_last_error().decode()
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1004)
+    st = lib.osdn_precond_scan(ctypes.byref(d), fake, odd, null, null, fake, null, null)
+    assert st == osdn.EINVAL and "aligned" in lib.osdn_last_error().decode()
+    st = lib.osdn_chunk_fwd(ctypes.byref(d), fake, fake, fake, fake, fake, null, null, fake,
+                            null, null)
+    assert st == osdn.EINVAL and "alias" in lib.osdn_last_error().decode()
+    st = lib.osdn_fwd(ctypes.byref(d), fake, fake, fake, fake, null, null, null, null,
+                      ctypes.c_void_p(0x2000), null, null, null, null, ctypes.c_size_t(0), null)
+    assert st == osdn.EINVAL and "workspace" in lib.osdn_last_error().decode()
+    st = lib.osdn_fwd(ctypes.byref(d), fake, fake, fake, fake, null, null, null, null,
+                      ctypes.c_void_p(0x2000), null, null, null, ctypes.c_void_p(0x3000),
+                      ctypes.c_size_t(16), null)
+    assert st == osdn.EINVAL and "needed" in lib.osdn_last_error().decode()
+
+
+def test_workspace_bytes(lib):
+    d = osdn.Desc()
+    lib.osdn_desc_init(ctypes.byref(d), 4, 4096, 16, 128, 128)
+    assert lib.osdn_fwd_workspace_bytes(ctypes.byref(d)) == 4 * 4096 * 16 * 128 * 2
+    d.dtype = osdn.F32
+    assert lib.osdn_fwd_workspace_bytes(ctypes.byref(d)) == 4 * 4096 * 16 * 128 * 4
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(osdn, "_lib", None)
+    monkeypatch.setattr(osdn, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="libosdn.so not found"):
+        osdn.load()
