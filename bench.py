@@ -114,6 +114,9 @@ def main(argv=None):
                          alpha=up(inp["alpha"], torch.float32),
                          o=torch.empty((B, T, H, V), dtype=tdt, device=dev),
                          kt=torch.empty((B, T, H, K), dtype=tdt, device=dev),
+                         ws=torch.empty(osdn.fwd_workspace_bytes(B, T, H, K, V, dtype=(
+                             osdn.BF16 if p["dtype"] == "bf16" else osdn.F32), chunk=C),
+                             dtype=torch.uint8, device=dev),
                          S=torch.empty((B, H, V, K), dtype=torch.float32, device=dev),
                          d=torch.empty((B, H, K), dtype=torch.float32, device=dev)))
     kw = dict(chunk=C, eta=p["eta"], d_min=p["d_min"], d_max=p["d_max"], clamp=p["clamp"],
@@ -122,7 +125,7 @@ def main(argv=None):
     def step(i):
         s = sets[i % len(sets)]
         osdn.fwd(s["q"], s["k"], s["v"], s["beta"], s["r"], s["alpha"], None, None,
-                 o=s["o"], S_out=s["S"], d_out=s["d"], k_tilde_out=s["kt"], **kw)
+                 o=s["o"], S_out=s["S"], d_out=s["d"], workspace=s["ws"], **kw)
 
     def scan(i):
         s = sets[i % len(sets)]

@@ -130,15 +130,20 @@ osdn_status osdn_chunk_fwd(const osdn_desc *desc, const void *q,
                            const float *S0, void *o, float *S_out,
                            void *stream);
 
-/* Bytes of device workspace osdn_fwd needs when k_tilde_out is NULL (room
- * for the write keys between the phases); 0 on an invalid descriptor. */
+/* Bytes of device workspace osdn_fwd needs (room for the write keys between
+ * the phases, B*T*H*K elements of dtype); 0 on an invalid descriptor. */
 size_t osdn_fwd_workspace_bytes(const osdn_desc *desc);
 
 /*
  * Both phases on one stream (the two-phase schedule of Section 4.5).
- * Arguments as above; k_tilde_out [B,T,H,K] dtype receives the write keys
- * when not NULL, otherwise they go to workspace, which must then hold at
- * least osdn_fwd_workspace_bytes(desc) bytes.
+ * Arguments as above.  k_tilde_out [B,T,H,K] dtype, when not NULL, receives
+ * the write keys d_t (.) k_t.  workspace (>= osdn_fwd_workspace_bytes(desc)
+ * bytes, 16-byte aligned) carries the write keys from phase 1 to phase 2; it
+ * is required whenever T > 0 unless dtype is OSDN_F32 and k_tilde_out is
+ * given.  For bf16 the workspace holds the residual (d_t - 1) (.) k_t rather
+ * than k~_t, so phase 2 sees the write keys to about 16 significant bits
+ * instead of bf16's 8: the result is then closer to the exact forward than
+ * osdn_precond_scan followed by osdn_chunk_fwd on a bf16 k~.
  */
 osdn_status osdn_fwd(const osdn_desc *desc, const void *q, const void *k,
                      const void *v, const float *beta, const float *r,

@@ -215,15 +215,16 @@ def fwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, chunk=64, eta=0.
     desc = make_desc(B, T, H, K, V, dtype=_dtype_code(q), chunk=chunk, eta=eta, d_min=d_min,
                      d_max=d_max, clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware)
     ws_bytes = 0
-    if k_tilde_out is None:
+    if k_tilde_out is None or dt == torch.bfloat16:
         need = int(load().osdn_fwd_workspace_bytes(ctypes.byref(desc)))
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace is not None:
         if workspace.device != dev or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous tensor on %s" % dev)
         ws_bytes = workspace.numel() * workspace.element_size()
     _check(load().osdn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r),
                            _ptr(alpha), _ptr(d1), _ptr(S0), _ptr(o), _ptr(S_out), _ptr(d_out),
-                           _ptr(k_tilde_out), _ptr(workspace if k_tilde_out is None else None),
+                           _ptr(k_tilde_out), _ptr(workspace),
                            ctypes.c_size_t(ws_bytes), _stream(dev)))
     return o, S_out, d_out

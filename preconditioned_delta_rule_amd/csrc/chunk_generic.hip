@@ -78,7 +78,7 @@ __global__ __launch_bounds__(GEN_THREADS) void chunk_generic_kernel(ChunkArgs a,
         int64_t g = ((b * T + t0 + i) * H + h) * K + c;
         xq = to_f32(q[g]) * a.q_scale;
         xk = to_f32(k[g]);
-        xw = to_f32(kt[g]);
+        xw = to_f32(kt[g]) + (a.kt_is_res ? xk : 0.0f);  // k~ = k + residual
       }
       sQ[i * KP + c] = xq;
       sK[i * KP + c] = xk;

@@ -6,18 +6,27 @@
 // Eqs.(8)-(11); with a decay alpha, Appendix B.1 Eqs.(13)-(15).  Per chunk,
 // with boundary state S (V x K, fp32), B = diag(beta) and in-chunk log decay
 // g_i = sum_{l<=i} log alpha_l (g = 0 without decay):
-//   A     = strict_lower(B [e^{g_i-g_j}] . K K~^T)      (MFMA)
-//   Tm    = (I + A)^-1                                  (forward substitution
-//                                                        on 16x16 diagonal
-//                                                        blocks, MFMA merges)
-//   R     = V - diag(e^g) K S^T                         (MFMA)
-//   Delta = Tm B R            (= U - W S^T of Eq.(11))   (MFMA)
+//   A     = strict_lower(B [e^{g_i-g_j}] . K K~^T)
+//   Tm    = (I + A)^-1            (forward substitution on the 16x16 diagonal
+//                                  blocks, MFMA merges of the off-diagonal ones)
+//   R     = B (V - diag(e^g) K S^T)
+//   Delta = Tm R                  (= U - W S^T of Eq.(11))
 //   O     = q_scale (diag(e^g) Q S^T + lower([e^{g_i-g_j}] . Q K~^T) Delta)
-//   S    <- e^{g_L} S + Delta^T (e^{g_L - g} . K~)       (MFMA, S stays in the
-//                                                        accumulators)
+//   S    <- e^{g_L} S + Delta^T (e^{g_L - g} . K~)
+//
+// Precision: every MFMA takes bf16 operands and accumulates in fp32.  Inputs
+// q, k, k~, v are bf16 already.  Intermediates that are not (S, R, Delta and
+// the scores) enter as a hi + lo pair of bf16 (x_hi = bf16(x), x_lo =
+// bf16(x - x_hi)), i.e. about 16 significant bits, so the only 8-bit roundings
+// left are Tm and the bf16 output itself.  The write keys arrive either as
+// bf16 k~ (exact operands) or as the bf16 residual E = (d - 1) (.) k, in which
+// case k~ = k + E is formed in fp32 and also enters as a hi + lo pair.
+//
 // Work split: one workgroup of 4 waves per (b,h) and tile of VT value rows,
 // so a (b,h) is spread over 128/VT CUs; the tiles of one (b,h) are placed on
-// the same XCD so their shared K/K~/Q reads hit that XCD's L2.
+// the same XCD so their shared K/K~/Q reads hit that XCD's L2.  Inside the
+// workgroup wave w owns tokens [16w, 16w+16) of the chunk; its K and Q rows go
+// straight from global memory into registers in MFMA operand layout.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -33,8 +42,6 @@ constexpr int CP = C + 8;  // LDS pitch (bf16) of 64-wide rows
 constexpr int AP = C + 4;  // LDS pitch (f32) of the Gram
 constexpr int NTHREADS = 256;
 
-typedef short shortx4 __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ floatx4 mfma32(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -42,56 +49,91 @@ __device__ __forceinline__ floatx4 mfma16(bf16x4 a, bf16x4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// 16x16 tile of X Y^T over `kdim` (multiple of 32): X, Y point at the first
-// row of 16-row tiles stored row-major with the given pitch (bf16 elements).
-// Lane l supplies row (l & 15) and k-slice 8*(l >> 4) of each 32-wide step;
-// the result holds D[4*(l>>4) + i][l & 15] in element i.
-__device__ __forceinline__ floatx4 tile_nt(const bf16 *X, int ldx, const bf16 *Y, int ldy,
-                                           int k0, int k1, floatx4 acc, int l) {
-  const int r = l & 15, ks = (l >> 4) * 8;
-  for (int k = k0; k < k1; k += 32) {
-    bf16x8 x = *reinterpret_cast<const bf16x8 *>(X + r * ldx + k + ks);
-    bf16x8 y = *reinterpret_cast<const bf16x8 *>(Y + r * ldy + k + ks);
-    acc = mfma32(x, y, acc);
-  }
-  return acc;
-}
+__device__ __forceinline__ bf16x8 ld8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+__device__ __forceinline__ bf16x4 ld4(const bf16 *p) { return *reinterpret_cast<const bf16x4 *>(p); }
 
 __device__ __forceinline__ bf16x4 pack4(floatx4 v) {
   bf16x4 r;
-  r[0] = to_bf16(v[0]);
-  r[1] = to_bf16(v[1]);
-  r[2] = to_bf16(v[2]);
-  r[3] = to_bf16(v[3]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = to_bf16(v[i]);
   return r;
 }
 
-template <int VT> struct Smem {
-  bf16 K[C][KP];      // physical keys of the chunk, row-major
-  bf16 Kt[C][KP];     // write keys, row-major
-  bf16 Q[C][KP];      // queries, row-major
-  bf16 KtT[KD][CP];   // write keys transposed ([c][j]), operand of the state update
-  bf16 V[C][VT + 8];  // value tile
-  float A[C][AP];     // chunk Gram (strict lower, gated, beta-scaled), fp32
-  bf16 Tr[C][CP];     // (I + A)^-1 row-major
-  bf16 Tc[C][CP];     // (I + A)^-1 column-major ([j][i]), for the merges
-  bf16 X[C][CP];      // merge scratch, column-major
-  bf16 M[C][CP];      // local scores (lower incl. diagonal, gated)
-  bf16 RT[VT][CP];    // (B R)^T
-  bf16 DT[VT][CP];    // Delta^T
-  bf16 DTs[VT][CP];   // Delta^T scaled by the suffix decay (gated form)
-  bf16 S[VT][KP];     // bf16 copy of the state tile, row-major [v][c]
-  float beta[C];
-  float g[C];         // inclusive in-chunk cumulative log decay
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi)
+__device__ __forceinline__ void split4(floatx4 v, bf16x4 &hi, bf16x4 &lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = to_bf16(v[i]);
+    lo[i] = to_bf16(v[i] - to_f32(hi[i]));
+  }
+}
+
+// LDS layout (bytes).  Buffers that are never live at the same time share
+// the SX region: the bf16 state pair (written after the state update, read by
+// the next chunk's products) and the scratch of the inverse.
+template <int VT> struct Lay {
+  static constexpr int KT = 0;                        // bf16 [C][KP]   write keys
+  static constexpr int KTT = KT + C * KP * 2;         // bf16 [KD][CP]  write keys^T
+  static constexpr int V = KTT + KD * CP * 2;         // bf16 [C][VT+8] value tile
+  static constexpr int BETA = V + C * (VT + 8) * 2;   // f32 [C]
+  static constexpr int G = BETA + C * 4;              // f32 [C]       cumulative log decay
+  static constexpr int MH = G + C * 4;                // bf16 [C][CP]  scores, hi
+  static constexpr int ML = MH + C * CP * 2;          // bf16 [C][CP]  scores, lo
+  static constexpr int RTH = ML + C * CP * 2;         // bf16 [VT][CP] R^T hi
+  static constexpr int RTL = RTH + VT * CP * 2;       // bf16 [VT][CP] R^T lo
+  static constexpr int TR = RTL + VT * CP * 2;        // bf16 [C][CP]  (I+A)^-1 row-major
+  static constexpr int SX = TR + C * CP * 2;          // union below
+  static constexpr int SH = SX;                       //   bf16 [VT][KP] state hi
+  static constexpr int SL = SX + VT * KP * 2;         //   bf16 [VT][KP] state lo
+  static constexpr int TC = SX;                       //   bf16 [C][CP] (I+A)^-1 column-major
+  static constexpr int X = SX + C * CP * 2;           //   bf16 [C][CP] merge scratch
+  static constexpr int SX_BYTES = (2 * VT * KP > 2 * C * CP ? 2 * VT * KP : 2 * C * CP) * 2;
+  // the gated Gram lives in the Delta^T buffers: it is written by the
+  // products stage and read by the inverse, both before Delta exists
+  static constexpr int A = SX + SX_BYTES;             // f32 [C][AP]
+  static constexpr int DTH = SX + SX_BYTES;           // bf16 [VT][CP] Delta^T hi
+  static constexpr int DTL = DTH + VT * CP * 2;       // bf16 [VT][CP] Delta^T lo
+  static constexpr int DSH = DTL + VT * CP * 2;       // bf16 [VT][CP] decayed Delta^T hi
+  static constexpr int DSL = DSH + VT * CP * 2;       // bf16 [VT][CP] decayed Delta^T lo
+  static constexpr int DT_END = DSL + VT * CP * 2;
+  static constexpr int KTL = DT_END;                  // bf16 [C][KP]  write keys, lo part
+  static constexpr int KTTL = KTL + C * KP * 2;       // bf16 [KD][CP] write keys^T, lo part
+  static constexpr int TOTAL = KTTL + KD * CP * 2;
 };
 
-template <int VT, bool GATED>
+template <int VT, bool GATED, bool KRES>
 __global__ __launch_bounds__(NTHREADS) void chunk_mfma_kernel(ChunkArgs a) {
-  constexpr int NT = VD / VT;          // value tiles per (b,h)
-  constexpr int NCT = VT / 16;         // 16-wide column tiles per value tile
-  __shared__ __attribute__((aligned(16))) Smem<VT> sm;
+  constexpr int NT = VD / VT;   // value tiles per (b,h)
+  constexpr int NCT = VT / 16;  // 16-wide column tiles per value tile
+  constexpr int VV = VT / 8;    // 16-byte vectors per value-tile row
+  typedef Lay<VT> L;
+  static_assert(L::TOTAL <= 160 * 1024, "LDS budget");
+  static_assert(L::A + C * AP * 4 <= L::DT_END, "Gram must fit in the Delta buffers");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
+  bf16(*sKt)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::KT);
+  bf16(*sKtT)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::KTT);
+  bf16(*sKtL)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::KTL);
+  bf16(*sKtTL)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::KTTL);
+  bf16(*sV)[VT + 8] = reinterpret_cast<bf16(*)[VT + 8]>(smem + L::V);
+  float *sBeta = reinterpret_cast<float *>(smem + L::BETA);
+  float *sG = reinterpret_cast<float *>(smem + L::G);
+  float(*sA)[AP] = reinterpret_cast<float(*)[AP]>(smem + L::A);
+  bf16(*sMh)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::MH);
+  bf16(*sMl)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::ML);
+  bf16(*sRh)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::RTH);
+  bf16(*sRl)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::RTL);
+  bf16(*sTr)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::TR);
+  bf16(*sSh)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::SH);
+  bf16(*sSl)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::SL);
+  bf16(*sTc)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::TC);
+  bf16(*sX)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::X);
+  bf16(*sDh)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::DTH);
+  bf16(*sDl)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::DTL);
+  bf16(*sDsh)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + (GATED ? L::DSH : L::DTH));
+  bf16(*sDsl)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + (GATED ? L::DSL : L::DTL));
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = l & 15, lq = l >> 4;
   // XCD-aware placement: block i runs on XCD i % 8; the NT tiles of one
   // sequence share i % 8.
@@ -109,7 +151,8 @@ __global__ __launch_bounds__(NTHREADS) void chunk_mfma_kernel(ChunkArgs a) {
   const bf16 *gkt = static_cast<const bf16 *>(a.kt);
   const bf16 *gv = static_cast<const bf16 *>(a.v);
   bf16 *go = static_cast<bf16 *>(a.o);
-  const int64_t tstride = H * KD;  // elements between tokens (K == V == 128)
+  const int64_t tstride = H * KD;                 // elements between tokens (K == V == 128)
+  const int64_t base = (b * T) * tstride + h * KD;  // token 0 of this (b,h)
 
   // ---- state tile in accumulators: wave w owns columns [32w, 32w+32) of the
   //      VT x 128 tile as NCT x 2 MFMA tiles; element i of tile (rt, ct) is
@@ -122,263 +165,342 @@ __global__ __launch_bounds__(NTHREADS) void chunk_mfma_kernel(ChunkArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int vr = 16 * rt + 4 * lq + i, c = 32 * w + 16 * ct + l16;
-        float s0 = a.S0 ? a.S0[(seq * VD + v0 + vr) * KD + c] : 0.0f;
+        const float s0 = a.S0 ? a.S0[(seq * VD + v0 + vr) * KD + c] : 0.0f;
         Sacc[rt][ct][i] = s0;
-        sm.S[vr][c] = to_bf16(s0);
+        const bf16 hi = to_bf16(s0);
+        sSh[vr][c] = hi;
+        sSl[vr][c] = to_bf16(s0 - to_f32(hi));
       }
 
-  // ---- global -> register prefetch of one chunk
-  // K, K~, Q: 64 rows x 16 vectors of 8 bf16; thread covers vectors tid + 256 p.
-  // V tile: 64 rows x VT/8 vectors.
-  constexpr int VV = VT / 8;  // vectors per value-tile row
-  bf16x8 pk[4], pkt[4], pq[4], pv[(C * VV + NTHREADS - 1) / NTHREADS];
-  float pbeta = 0.0f, pla = 0.0f;
+  // ---- prefetch registers for one chunk
+  //   write keys: lane l loads token l, columns [8(4w+p), 8(4w+p)+8), p < 4
+  //   values:     vectors tid (+256 p) of the 64 x VT tile
+  //   K, Q:       wave w's 16 tokens in MFMA A-operand layout (4 k-steps)
+  bf16x8 pkt[4], pkk[4], pv[(C * VV + NTHREADS - 1) / NTHREADS], pk[4], pq[4];
+  float pbeta = 0.0f, palpha = 1.0f;
   auto fetch = [&](int64_t t0) {
+    {
+      const int64_t t = t0 + l;
+      const bool ok = t < T;
+      const int64_t off = base + (ok ? t : 0) * tstride;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int vi = tid + NTHREADS * p, i = vi >> 4, cv = vi & 15;
-      const int64_t t = t0 + i;
-      if (t < T) {
-        const int64_t off = (b * T + t) * tstride + h * KD + cv * 8;
-        pk[p] = *reinterpret_cast<const bf16x8 *>(gk + off);
-        pkt[p] = *reinterpret_cast<const bf16x8 *>(gkt + off);
-        pq[p] = *reinterpret_cast<const bf16x8 *>(gq + off);
-      } else {
-        pk[p] = bf16x8{};
-        pkt[p] = bf16x8{};
-        pq[p] = bf16x8{};
+      for (int p = 0; p < 4; ++p) {
+        bf16x8 x = ld8(gkt + off + 8 * (4 * w + p));
+        pkt[p] = ok ? x : bf16x8{};
+        if (KRES) {
+          bf16x8 y = ld8(gk + off + 8 * (4 * w + p));
+          pkk[p] = ok ? y : bf16x8{};
+        }
       }
     }
 #pragma unroll
     for (int p = 0; p < (C * VV + NTHREADS - 1) / NTHREADS; ++p) {
       const int vi = tid + NTHREADS * p;
-      if (vi < C * VV) {
-        const int i = vi / VV, cv = vi % VV;
-        const int64_t t = t0 + i;
-        pv[p] = t < T ? *reinterpret_cast<const bf16x8 *>(gv + (b * T + t) * tstride + h * VD + v0 + cv * 8)
-                      : bf16x8{};
+      const int i = vi / VV, cv = vi % VV;
+      const int64_t t = t0 + i;
+      const bool ok = vi < C * VV && t < T;
+      bf16x8 x = ld8(gv + base + (ok ? t : 0) * tstride + v0 + (ok ? cv * 8 : 0));
+      pv[p] = ok ? x : bf16x8{};
+    }
+    {
+      const int64_t t = t0 + 16 * w + l16;
+      const bool ok = t < T;
+      const int64_t off = base + (ok ? t : 0) * tstride + 8 * lq;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        bf16x8 x = ld8(gk + off + 32 * kk), y = ld8(gq + off + 32 * kk);
+        pk[kk] = ok ? x : bf16x8{};
+        pq[kk] = ok ? y : bf16x8{};
       }
     }
-    if (tid < C) {
-      const int64_t t = t0 + tid;
-      pbeta = t < T ? a.beta[(b * T + t) * H + h] : 0.0f;
-      if (GATED) pla = t < T ? logf(a.alpha[(b * T + t) * H + h]) : 0.0f;
+    if (w == 0) {
+      const int64_t t = t0 + l;
+      const bool ok = t < T;
+      const int64_t gi = (b * T + (ok ? t : 0)) * H + h;
+      const float bt = a.beta[gi];
+      pbeta = ok ? bt : 0.0f;
+      if (GATED) {
+        const float al = a.alpha[gi];
+        palpha = ok ? al : 1.0f;
+      }
     }
   };
 
   if (T > 0) fetch(0);
   for (int64_t t0 = 0; t0 < T; t0 += C) {
-    const int L = (int)((T - t0) < C ? (T - t0) : C);
+    const int Lc = (int)((T - t0) < C ? (T - t0) : C);
     __syncthreads();  // previous chunk done with every LDS buffer
     // ---- stage L: registers -> LDS
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const int vi = tid + NTHREADS * p, i = vi >> 4, cv = vi & 15;
-      *reinterpret_cast<bf16x8 *>(&sm.K[i][cv * 8]) = pk[p];
-      *reinterpret_cast<bf16x8 *>(&sm.Kt[i][cv * 8]) = pkt[p];
-      *reinterpret_cast<bf16x8 *>(&sm.Q[i][cv * 8]) = pq[p];
+      const int c0 = 8 * (4 * w + p);
+      if (KRES) {
+        // k~ = k + residual in fp32 (exact), stored as a bf16 hi + lo pair
+        bf16x8 hi, lo;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm.KtT[cv * 8 + e][i] = pkt[p][e];
+        for (int e = 0; e < 8; ++e) {
+          const float x = to_f32(pkk[p][e]) + to_f32(pkt[p][e]);
+          hi[e] = to_bf16(x);
+          lo[e] = to_bf16(x - to_f32(hi[e]));
+        }
+        *reinterpret_cast<bf16x8 *>(&sKt[l][c0]) = hi;
+        *reinterpret_cast<bf16x8 *>(&sKtL[l][c0]) = lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          sKtT[c0 + e][l] = hi[e];
+          sKtTL[c0 + e][l] = lo[e];
+        }
+      } else {
+        *reinterpret_cast<bf16x8 *>(&sKt[l][c0]) = pkt[p];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sKtT[c0 + e][l] = pkt[p][e];
+      }
     }
 #pragma unroll
     for (int p = 0; p < (C * VV + NTHREADS - 1) / NTHREADS; ++p) {
       const int vi = tid + NTHREADS * p;
-      if (vi < C * VV) {
-        const int i = vi / VV, cv = vi % VV;
-        *reinterpret_cast<bf16x8 *>(&sm.V[i][cv * 8]) = pv[p];
-      }
+      if (vi < C * VV) *reinterpret_cast<bf16x8 *>(&sV[vi / VV][(vi % VV) * 8]) = pv[p];
     }
-    if (tid < C) {
-      sm.beta[tid] = pbeta;
+    if (w == 0) {
+      sBeta[l] = pbeta;
       if (GATED) {
         // inclusive scan of the log decays over the 64 lanes of wave 0
-        float x = pla;
+        float x = logf(palpha);
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-          float y = __shfl_up(x, off, 64);
-          if (tid >= off) x += y;
+          const float y = __shfl_up(x, off, 64);
+          if (l >= off) x += y;
         }
-        sm.g[tid] = x;
+        sG[l] = x;
       }
+    }
+    bf16x8 kf[4], qf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      kf[kk] = pk[kk];
+      qf[kk] = pq[kk];
     }
     __syncthreads();
     if (t0 + C < T) fetch(t0 + C);  // overlaps with the compute below
 
-    // ---- stage G: Gram A and scores M (lower tiles), K S^T and Q S^T
-    // jobs 0..9: A tiles, 10..19: M tiles, over the 10 tiles ti >= tj.
-    for (int job = w; job < 20; job += 4) {
-      const int tl = job % 10;
-      const int ti = tl < 1 ? 0 : tl < 3 ? 1 : tl < 6 ? 2 : 3;
-      const int tj = tl - ti * (ti + 1) / 2;
-      const bool isA = job < 10;
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = tile_nt(isA ? &sm.K[16 * ti][0] : &sm.Q[16 * ti][0], KP, &sm.Kt[16 * tj][0], KP, 0, KD, acc, l);
+    const int m0 = 16 * w;
+    // ---- stage G: Gram A and scores M (tiles (w, tj), tj <= w), K S^T, Q S^T
+    floatx4 accA[4], accM[4], accKS[NCT], accQS[NCT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * ti + 4 * lq + i, n = 16 * tj + l16;
-        const float ratio = GATED ? __expf(sm.g[m] - sm.g[n]) : 1.0f;
-        if (isA) {
-          sm.A[m][n] = n < m ? sm.beta[m] * ratio * acc[i] : 0.0f;
-        } else {
-          sm.M[m][n] = to_bf16(n <= m ? ratio * acc[i] : 0.0f);
+    for (int j = 0; j < 4; ++j) accA[j] = accM[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) accKS[ct] = accQS[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int ko = 32 * kk + 8 * lq;
+#pragma unroll
+      for (int tj = 0; tj < 4; ++tj) {
+        if (tj <= w) {
+          const bf16x8 bk = ld8(&sKt[16 * tj + l16][ko]);
+          accA[tj] = mfma32(kf[kk], bk, accA[tj]);
+          accM[tj] = mfma32(qf[kk], bk, accM[tj]);
+          if (KRES) {
+            const bf16x8 bl = ld8(&sKtL[16 * tj + l16][ko]);
+            accA[tj] = mfma32(kf[kk], bl, accA[tj]);
+            accM[tj] = mfma32(qf[kk], bl, accM[tj]);
+          }
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const bf16x8 sh = ld8(&sSh[16 * ct + l16][ko]), sl = ld8(&sSl[16 * ct + l16][ko]);
+        accKS[ct] = mfma32(kf[kk], sh, accKS[ct]);
+        accKS[ct] = mfma32(kf[kk], sl, accKS[ct]);
+        accQS[ct] = mfma32(qf[kk], sh, accQS[ct]);
+        accQS[ct] = mfma32(qf[kk], sl, accQS[ct]);
+      }
+    }
+    // epilogue of the Gram / scores: lane holds rows m0 + 4 lq + i, column 16 tj + l16
+    float gm[4], bm[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gm[i] = GATED ? sG[m0 + 4 * lq + i] : 0.0f;
+      bm[i] = sBeta[m0 + 4 * lq + i];
+    }
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) {
+      if (tj <= w) {
+        const int n = 16 * tj + l16;
+        const float gn = GATED ? sG[n] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + 4 * lq + i;
+          const float ratio = GATED ? __expf(gm[i] - gn) : 1.0f;
+          sA[m][n] = n < m ? bm[i] * ratio * accA[tj][i] : 0.0f;
+          const float mv = n <= m ? ratio * accM[tj][i] : 0.0f;
+          const bf16 mh = to_bf16(mv);
+          sMh[m][n] = mh;
+          sMl[m][n] = to_bf16(mv - to_f32(mh));
         }
       }
     }
-    // zero the upper tiles that the 32-wide k-steps of later products read
-    if (w < 2) {
-      const int ti = 2 * w;  // tiles (0,1) and (2,3)
+    if ((w & 1) == 0) {
+      // tiles (w, w+1) are read by the 32-wide k-steps of later products
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = 16 * ti + 4 * lq + i, n = 16 * (ti + 1) + l16;
-        sm.M[m][n] = to_bf16(0.0f);
-        sm.Tr[m][n] = to_bf16(0.0f);
+        const int m = m0 + 4 * lq + i, n = m0 + 16 + l16;
+        sMh[m][n] = sMl[m][n] = sTr[m][n] = to_bf16(0.0f);
       }
     }
     floatx4 Oacc[NCT];
-    {
-      const int m0 = 16 * w;
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        floatx4 ks = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
-        ks = tile_nt(&sm.K[m0][0], KP, &sm.S[16 * ct][0], KP, 0, KD, ks, l);
-        qs = tile_nt(&sm.Q[m0][0], KP, &sm.S[16 * ct][0], KP, 0, KD, qs, l);
-        bf16x4 rb;
+    for (int ct = 0; ct < NCT; ++ct) {
+      floatx4 r;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = m0 + 4 * lq + i, vr = 16 * ct + l16;
-          const float gm = GATED ? __expf(sm.g[m]) : 1.0f;
-          rb[i] = to_bf16(sm.beta[m] * (to_f32(sm.V[m][vr]) - gm * ks[i]));
-          Oacc[ct][i] = gm * qs[i];
-        }
-        *reinterpret_cast<bf16x4 *>(&sm.RT[16 * ct + l16][m0 + 4 * lq]) = rb;
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 4 * lq + i, vr = 16 * ct + l16;
+        const float em = GATED ? __expf(gm[i]) : 1.0f;
+        r[i] = bm[i] * (to_f32(sV[m][vr]) - em * accKS[ct][i]);
+        Oacc[ct][i] = em * accQS[ct][i];
       }
+      bf16x4 rh, rl;
+      split4(r, rh, rl);
+      *reinterpret_cast<bf16x4 *>(&sRh[16 * ct + l16][m0 + 4 * lq]) = rh;
+      *reinterpret_cast<bf16x4 *>(&sRl[16 * ct + l16][m0 + 4 * lq]) = rl;
     }
     __syncthreads();
 
-    // ---- stage T: (I + A)^-1
-    // (i) wave w inverts diagonal block w by forward substitution; lane
-    //     l & 15 computes column c of the block inverse in fp32.
+    // ---- stage T: (I + A)^-1 into sTr
+    // (i) wave w inverts diagonal block w by forward substitution in fp32;
+    //     lane l & 15 computes column c of the block inverse.
     {
-      const int c = l16, base = 16 * w;
+      const int c = l16, bb = m0;
       float x[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float acc = (i == c) ? 1.0f : 0.0f;
 #pragma unroll
-        for (int j = 0; j < i; ++j) acc -= sm.A[base + i][base + j] * x[j];
+        for (int j = 0; j < i; ++j) acc -= sA[bb + i][bb + j] * x[j];
         x[i] = acc;
       }
       if (lq == 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sm.Tr[base + i][base + c] = to_bf16(x[i]);
-        bf16x8 lo, hi;
+        for (int i = 0; i < 16; ++i) sTr[bb + i][bb + c] = to_bf16(x[i]);
+        bf16x8 lo8, hi8;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          lo[i] = to_bf16(x[i]);
-          hi[i] = to_bf16(x[i + 8]);
+          lo8[i] = to_bf16(x[i]);
+          hi8[i] = to_bf16(x[i + 8]);
         }
-        *reinterpret_cast<bf16x8 *>(&sm.Tc[base + c][base]) = lo;
-        *reinterpret_cast<bf16x8 *>(&sm.Tc[base + c][base + 8]) = hi;
+        *reinterpret_cast<bf16x8 *>(&sTc[bb + c][bb]) = lo8;
+        *reinterpret_cast<bf16x8 *>(&sTc[bb + c][bb + 8]) = hi8;
       }
     }
     __syncthreads();
-    // (ii) T_{q+1,q} = -T_{q+1,q+1} A_{q+1,q} T_{q,q} for q = 0 (wave 0), 2 (wave 1)
+    // (ii) T_{q+1,q} = -T_{q+1,q+1} A_{q+1,q} T_{q,q}, q = 0 (wave 0), q = 2 (wave 1)
     if (w < 2) {
       const int q = 2 * w, p = q + 1;
-      bf16x4 aop, bop;
+      bf16x4 aop;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) aop[e] = to_bf16(sm.A[16 * p + l16][16 * q + 4 * lq + e]);
-      bop = *reinterpret_cast<const bf16x4 *>(&sm.Tc[16 * q + l16][16 * q + 4 * lq]);
-      floatx4 X = mfma16(aop, bop, floatx4{0.f, 0.f, 0.f, 0.f});
-      aop = *reinterpret_cast<const bf16x4 *>(&sm.Tr[16 * p + l16][16 * p + 4 * lq]);
-      floatx4 Y = mfma16(aop, pack4(X), floatx4{0.f, 0.f, 0.f, 0.f});
+      for (int e = 0; e < 4; ++e) aop[e] = to_bf16(sA[16 * p + l16][16 * q + 4 * lq + e]);
+      const floatx4 X = mfma16(aop, ld4(&sTc[16 * q + l16][16 * q + 4 * lq]), floatx4{0.f, 0.f, 0.f, 0.f});
+      const floatx4 Y = mfma16(ld4(&sTr[16 * p + l16][16 * p + 4 * lq]), pack4(X), floatx4{0.f, 0.f, 0.f, 0.f});
       bf16x4 nt;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         nt[i] = to_bf16(-Y[i]);
-        sm.Tr[16 * p + 4 * lq + i][16 * q + l16] = nt[i];
+        sTr[16 * p + 4 * lq + i][16 * q + l16] = nt[i];
       }
-      *reinterpret_cast<bf16x4 *>(&sm.Tc[16 * q + l16][16 * p + 4 * lq]) = nt;
+      *reinterpret_cast<bf16x4 *>(&sTc[16 * q + l16][16 * p + 4 * lq]) = nt;
     }
     __syncthreads();
-    // (iii) lower-left 32x32 block: X = A_BA T_AA, then T_BA = -T_BB X,
+    // (iii) lower-left 32x32 block: X = A_BA T_AA, then T_BA = -T_BB X;
     //       wave w owns output block (p, q) = (2 + w/2, w%2).
     {
       const int p = 2 + (w >> 1), q = w & 1;
       floatx4 X = {0.f, 0.f, 0.f, 0.f};
       for (int kb = q; kb < 2; ++kb) {
-        bf16x4 aop, bop;
+        bf16x4 aop;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) aop[e] = to_bf16(sm.A[16 * p + l16][16 * kb + 4 * lq + e]);
-        bop = *reinterpret_cast<const bf16x4 *>(&sm.Tc[16 * q + l16][16 * kb + 4 * lq]);
-        X = mfma16(aop, bop, X);
+        for (int e = 0; e < 4; ++e) aop[e] = to_bf16(sA[16 * p + l16][16 * kb + 4 * lq + e]);
+        X = mfma16(aop, ld4(&sTc[16 * q + l16][16 * kb + 4 * lq]), X);
       }
-      *reinterpret_cast<bf16x4 *>(&sm.X[16 * q + l16][16 * p + 4 * lq]) = pack4(X);
+      *reinterpret_cast<bf16x4 *>(&sX[16 * q + l16][16 * p + 4 * lq]) = pack4(X);
       __syncthreads();
       floatx4 Y = {0.f, 0.f, 0.f, 0.f};
-      for (int mb = 2; mb <= p; ++mb) {
-        bf16x4 aop = *reinterpret_cast<const bf16x4 *>(&sm.Tr[16 * p + l16][16 * mb + 4 * lq]);
-        bf16x4 bop = *reinterpret_cast<const bf16x4 *>(&sm.X[16 * q + l16][16 * mb + 4 * lq]);
-        Y = mfma16(aop, bop, Y);
-      }
+      for (int mb = 2; mb <= p; ++mb)
+        Y = mfma16(ld4(&sTr[16 * p + l16][16 * mb + 4 * lq]), ld4(&sX[16 * q + l16][16 * mb + 4 * lq]), Y);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.Tr[16 * p + 4 * lq + i][16 * q + l16] = to_bf16(-Y[i]);
+      for (int i = 0; i < 4; ++i) sTr[16 * p + 4 * lq + i][16 * q + l16] = to_bf16(-Y[i]);
     }
     __syncthreads();
 
-    // ---- stage D: Delta = Tm (B R); wave w owns rows [16w, 16w+16)
-    const float gL = GATED ? sm.g[L - 1] : 0.0f;
-    {
-      const int m0 = 16 * w, kend = m0 < 32 ? 32 : 64;
+    // ---- stage D: Delta = Tm R (rows of wave w), split and stored transposed
+    const float gL = GATED ? sG[Lc - 1] : 0.0f;
+    const int nks = w < 2 ? 1 : 2;  // 32-wide k-steps that reach the diagonal
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = tile_nt(&sm.Tr[m0][0], CP, &sm.RT[16 * ct][0], CP, 0, kend, acc, l);
-        bf16x4 db, ds;
+    for (int ct = 0; ct < NCT; ++ct) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < nks; ++kk) {
+        const int ko = 32 * kk + 8 * lq;
+        const bf16x8 t = ld8(&sTr[m0 + l16][ko]);
+        acc = mfma32(t, ld8(&sRh[16 * ct + l16][ko]), acc);
+        acc = mfma32(t, ld8(&sRl[16 * ct + l16][ko]), acc);
+      }
+      bf16x4 dh, dl;
+      split4(acc, dh, dl);
+      *reinterpret_cast<bf16x4 *>(&sDh[16 * ct + l16][m0 + 4 * lq]) = dh;
+      *reinterpret_cast<bf16x4 *>(&sDl[16 * ct + l16][m0 + 4 * lq]) = dl;
+      if (GATED) {
+        floatx4 s;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          db[i] = to_bf16(acc[i]);
-          if (GATED) ds[i] = to_bf16(acc[i] * __expf(gL - sm.g[m0 + 4 * lq + i]));
-        }
-        *reinterpret_cast<bf16x4 *>(&sm.DT[16 * ct + l16][m0 + 4 * lq]) = db;
-        if (GATED) *reinterpret_cast<bf16x4 *>(&sm.DTs[16 * ct + l16][m0 + 4 * lq]) = ds;
+        for (int i = 0; i < 4; ++i) s[i] = acc[i] * __expf(gL - gm[i]);
+        split4(s, dh, dl);
+        *reinterpret_cast<bf16x4 *>(&sDsh[16 * ct + l16][m0 + 4 * lq]) = dh;
+        *reinterpret_cast<bf16x4 *>(&sDsl[16 * ct + l16][m0 + 4 * lq]) = dl;
       }
     }
     __syncthreads();
 
-    // ---- stage O: outputs; stage S: state update
-    {
-      const int m0 = 16 * w, kend = m0 < 32 ? 32 : 64;
+    // ---- stage O: outputs of wave w's tokens
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        floatx4 acc = tile_nt(&sm.M[m0][0], CP, &sm.DT[16 * ct][0], CP, 0, kend, Oacc[ct], l);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = m0 + 4 * lq + i;
-          if (m < L)
-            go[(b * T + t0 + m) * tstride + h * VD + v0 + 16 * ct + l16] = to_bf16(a.q_scale * acc[i]);
-        }
+    for (int ct = 0; ct < NCT; ++ct) {
+      floatx4 acc = Oacc[ct];
+      for (int kk = 0; kk < nks; ++kk) {
+        const int ko = 32 * kk + 8 * lq;
+        const bf16x8 mh = ld8(&sMh[m0 + l16][ko]), ml = ld8(&sMl[m0 + l16][ko]);
+        const bf16x8 dh = ld8(&sDh[16 * ct + l16][ko]), dl = ld8(&sDl[16 * ct + l16][ko]);
+        acc = mfma32(mh, dh, acc);
+        acc = mfma32(mh, dl, acc);
+        acc = mfma32(ml, dh, acc);
       }
-      const float decay = GATED ? __expf(gL) : 1.0f;
 #pragma unroll
-      for (int rt = 0; rt < NCT; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          floatx4 acc = Sacc[rt][ct];
-          if (GATED) acc = acc * decay;
-          acc = tile_nt(GATED ? &sm.DTs[16 * rt][0] : &sm.DT[16 * rt][0], CP,
-                        &sm.KtT[32 * w + 16 * ct][0], CP, 0, C, acc, l);
-          Sacc[rt][ct] = acc;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 4 * lq + i;
+        if (m < Lc) go[base + (t0 + m) * tstride + v0 + 16 * ct + l16] = to_bf16(a.q_scale * acc[i]);
+      }
     }
-    __syncthreads();  // everyone has read sm.S for this chunk
+    // ---- stage S: state update, then its bf16 pair for the next chunk
+    const float decay = GATED ? __expf(gL) : 1.0f;
 #pragma unroll
     for (int rt = 0; rt < NCT; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+      for (int ct = 0; ct < 2; ++ct) {
+        floatx4 acc = Sacc[rt][ct];
+        if (GATED) acc = acc * decay;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sm.S[16 * rt + 4 * lq + i][32 * w + 16 * ct + l16] = to_bf16(Sacc[rt][ct][i]);
+        for (int kk = 0; kk < 2; ++kk) {
+          const int ko = 32 * kk + 8 * lq;
+          const bf16x8 kt = ld8(&sKtT[32 * w + 16 * ct + l16][ko]);
+          const bf16x8 dsh = ld8(&sDsh[16 * rt + l16][ko]);
+          acc = mfma32(dsh, kt, acc);
+          acc = mfma32(ld8(&sDsl[16 * rt + l16][ko]), kt, acc);
+          if (KRES) acc = mfma32(dsh, ld8(&sKtTL[32 * w + 16 * ct + l16][ko]), acc);
+        }
+        Sacc[rt][ct] = acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int vr = 16 * rt + 4 * lq + i, c = 32 * w + 16 * ct + l16;
+          const bf16 hi = to_bf16(acc[i]);
+          sSh[vr][c] = hi;
+          sSl[vr][c] = to_bf16(acc[i] - to_f32(hi));
+        }
+      }
   }
 
   if (a.S_out) {
@@ -400,10 +522,17 @@ hipError_t launch_vt(const ChunkArgs &a, hipStream_t s) {
   const int64_t nseq = a.B * a.H;
   const int64_t groups = (nseq + 7) / 8;
   dim3 grid((unsigned)(groups * 8 * NT)), block(NTHREADS);
-  if (a.alpha)
-    hipLaunchKernelGGL((chunk_mfma_kernel<VT, true>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((chunk_mfma_kernel<VT, false>), grid, block, 0, s, a);
+  if (a.alpha) {
+    if (a.kt_is_res)
+      hipLaunchKernelGGL((chunk_mfma_kernel<VT, true, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((chunk_mfma_kernel<VT, true, false>), grid, block, 0, s, a);
+  } else {
+    if (a.kt_is_res)
+      hipLaunchKernelGGL((chunk_mfma_kernel<VT, false, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((chunk_mfma_kernel<VT, false, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

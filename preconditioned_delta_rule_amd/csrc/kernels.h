@@ -11,7 +11,8 @@ struct ScanArgs {
   const float *beta;    // [B,T,H]
   const float *r;       // [B,T,H] or null
   const float *d1;      // [B,H,K] or null
-  void *k_tilde;        // [B,T,H,K]
+  void *k_tilde;        // [B,T,H,K] or null: write keys d (.) k
+  void *kt_res;         // [B,T,H,K] bf16 or null: write-key residual (d - 1) (.) k
   float *d_out;         // [B,H,K] or null
   int64_t B, T, H, K;
   float eta, d_min, d_max, eps;
@@ -20,6 +21,7 @@ struct ScanArgs {
 
 struct ChunkArgs {
   const void *q, *k, *kt, *v;  // [B,T,H,K] / [B,T,H,V]
+  bool kt_is_res;              // kt holds the residual (d - 1) (.) k, so k~ = k + kt
   const float *beta;           // [B,T,H]
   const float *alpha;          // [B,T,H] or null
   const float *S0;             // [B,H,V,K] or null

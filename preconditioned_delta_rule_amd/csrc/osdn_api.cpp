@@ -99,6 +99,7 @@ osdn::ScanArgs scan_args(const osdn_desc *d, const void *k, const float *beta, c
   a.r = r;
   a.d1 = d1;
   a.k_tilde = k_tilde;
+  a.kt_res = nullptr;
   a.d_out = d_out;
   a.B = d->B;
   a.T = d->T;
@@ -119,6 +120,7 @@ osdn::ChunkArgs chunk_args(const osdn_desc *d, const void *q, const void *k, con
   a.q = q;
   a.k = k;
   a.kt = kt;
+  a.kt_is_res = false;
   a.v = v;
   a.beta = beta;
   a.alpha = alpha;
@@ -246,17 +248,32 @@ osdn_status osdn_fwd(const osdn_desc *d, const void *q, const void *k, const voi
   OSDN_TRY(check_ptr(S_out, "S_out", false));
   OSDN_TRY(check_ptr(d_out, "d_out", false));
   OSDN_TRY(check_ptr(k_tilde_out, "k_tilde_out", false));
-  void *kt = k_tilde_out;
-  if (!kt && need_seq) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  osdn::ScanArgs sa = scan_args(d, k, beta, r, d1, k_tilde_out, d_out);
+  const void *kt_for_chunk = k_tilde_out;
+  bool kt_is_res = false;
+  if (need_seq && d->dtype == OSDN_BF16) {
+    // bf16: the write keys travel between the phases as the bf16 residual
+    // (d - 1) (.) k in the workspace, which with k gives k~ to ~16 bits
     OSDN_TRY(check_ptr(workspace, "workspace", true));
     const size_t need = osdn_fwd_workspace_bytes(d);
     if (workspace_bytes < need)
       return fail(OSDN_EINVAL, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
-    kt = workspace;
+    sa.kt_res = workspace;
+    kt_for_chunk = workspace;
+    kt_is_res = true;
+  } else if (need_seq && !k_tilde_out) {
+    OSDN_TRY(check_ptr(workspace, "workspace", true));
+    const size_t need = osdn_fwd_workspace_bytes(d);
+    if (workspace_bytes < need)
+      return fail(OSDN_EINVAL, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
+    sa.k_tilde = workspace;
+    kt_for_chunk = workspace;
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  OSDN_TRY(run_scan(d, scan_args(d, k, beta, r, d1, kt, d_out), s));
-  OSDN_TRY(run_chunk(d, chunk_args(d, q, k, kt, v, beta, alpha, S0, o, S_out), s));
+  OSDN_TRY(run_scan(d, sa, s));
+  osdn::ChunkArgs ca = chunk_args(d, q, k, kt_for_chunk, v, beta, alpha, S0, o, S_out);
+  ca.kt_is_res = kt_is_res;
+  OSDN_TRY(run_chunk(d, ca, s));
   return ok();
 }
 

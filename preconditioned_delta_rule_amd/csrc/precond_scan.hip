@@ -9,7 +9,17 @@
 // Mapping: one wave64 per (b,h) sequence, d held in VGPRs (EPL coordinates
 // per lane, contiguous so a token row is one coalesced load), the two K-long
 // reductions per token done with DPP row butterflies plus row broadcasts.
-// Keys of the next U tokens are loaded while the current U are processed.
+// Only <d, k^2> sits on the token-to-token dependency chain: the step is
+// written c = a_t - b_t <d, k^2> with a_t = eta b'/n, b_t = eta b'^2/n computed
+// from the key alone.  Besides (or instead of) k~ in the input dtype the
+// sweep can emit the residual (d - 1) (.) k in bf16: k + residual carries k~ to
+// about 16 significant bits (exactly when d sits on a bound) for the chunk
+// pass, at the byte cost of a bf16 k~.  d is carried with a compensation term (d_true =
+// d - comp) so its fp32 rounding does not drift over long sequences: each step
+// forms r d exactly as p + ep with an FMA and adds c s + ep - r comp to p with
+// a Fast2Sum.  Keys of the next group of tokens are loaded (as raw
+// bf16/f32 words) while the current group is processed; beta and r arrive as
+// one lane-indexed vector load per group and are broadcast with readlane.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -23,25 +33,48 @@ template <> struct RowVec<float, 1> { typedef float type; };
 template <> struct RowVec<float, 2> { typedef floatx2 type; };
 template <> struct RowVec<float, 4> { typedef floatx4 type; };
 
-template <typename TIn, int EPL, bool FULL>
-__device__ __forceinline__ void load_row(const TIn *p, int lane, int64_t K, float (&x)[EPL]) {
-  if constexpr (FULL) {
-    typedef typename RowVec<TIn, EPL>::type V;
-    V v = *reinterpret_cast<const V *>(p + lane * EPL);
-    if constexpr (EPL == 1) {
-      x[0] = to_f32(v);
+// One token row of a lane: EPL elements kept as raw 32-bit words until used,
+// so the compiler cannot hoist their conversion up to the (prefetch) load.
+template <typename TIn, int EPL, bool FULL> struct Row {
+  static constexpr int BYTES = EPL * (int)sizeof(TIn);
+  static constexpr int WORDS = BYTES < 4 ? 1 : BYTES / 4;
+  uint32_t w[WORDS];
+  __device__ __forceinline__ void load(const TIn *p, int lane, int64_t K) {
+    TIn x[EPL];
+    if constexpr (FULL) {
+      typedef typename RowVec<TIn, EPL>::type V;
+      V v = *reinterpret_cast<const V *>(p + lane * EPL);
+      if constexpr (EPL == 1) {
+        x[0] = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) x[e] = v[e];
+      }
     } else {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) x[e] = to_f32(v[e]);
+      for (int e = 0; e < EPL; ++e) {
+        const int64_t c = (int64_t)lane * EPL + e;
+        x[e] = c < K ? p[c] : TIn(0.0f);
+      }
     }
-  } else {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      int64_t c = (int64_t)lane * EPL + e;
-      x[e] = c < K ? to_f32(p[c]) : 0.0f;
-    }
+    for (int i = 0; i < WORDS; ++i) w[i] = 0;
+    __builtin_memcpy(w, x, BYTES);
   }
-}
+  // Values as fp32, materialised at the point of use.
+  __device__ __forceinline__ void get(float (&out)[EPL]) const {
+    uint32_t t[WORDS];
+#pragma unroll
+    for (int i = 0; i < WORDS; ++i) {
+      t[i] = w[i];
+      asm volatile("" : "+v"(t[i]));
+    }
+    TIn x[EPL];
+    __builtin_memcpy(x, t, BYTES);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) out[e] = to_f32(x[e]);
+  }
+};
 
 template <typename TIn, int EPL, bool FULL>
 __device__ __forceinline__ void store_row(TIn *p, int lane, int64_t K, const float (&x)[EPL]) {
@@ -58,15 +91,19 @@ __device__ __forceinline__ void store_row(TIn *p, int lane, int64_t K, const flo
   } else {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      int64_t c = (int64_t)lane * EPL + e;
+      const int64_t c = (int64_t)lane * EPL + e;
       if (c < K) p[c] = from_f32<TIn>(x[e]);
     }
   }
 }
 
-template <typename TIn, int EPL, bool FULL, bool HAS_R>
+__device__ __forceinline__ float lane_bcast(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+template <typename TIn, int EPL, bool FULL, bool HAS_R, bool WKT, bool WRES>
 __global__ __launch_bounds__(64) void precond_scan_kernel(ScanArgs a) {
-  constexpr int U = 8;  // tokens per prefetch group
+  constexpr int G = 32;  // tokens per prefetch group
   const int lane = threadIdx.x;
   const int64_t seq = blockIdx.x;  // (b,h), one wave each
   const int64_t H = a.H, T = a.T, K = a.K;
@@ -74,91 +111,136 @@ __global__ __launch_bounds__(64) void precond_scan_kernel(ScanArgs a) {
   const int64_t tok0 = b * T * H + h;  // flat [B,T,H] index of token 0
   const int64_t stride = H * K;        // elements between consecutive tokens
   const TIn *kp = static_cast<const TIn *>(a.k) + tok0 * K;
-  TIn *op = static_cast<TIn *>(a.k_tilde) + tok0 * K;
+  TIn *op = WKT ? static_cast<TIn *>(a.k_tilde) + tok0 * K : nullptr;
+  bf16 *rp_out = WRES ? static_cast<bf16 *>(a.kt_res) + tok0 * K : nullptr;
   const float *bp = a.beta + tok0;
   const float *rp = HAS_R ? a.r + tok0 : nullptr;
 
   float d[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    int64_t c = (int64_t)lane * EPL + e;
+    const int64_t c = (int64_t)lane * EPL + e;
     d[e] = c < K ? (a.d1 ? a.d1[seq * K + c] : 1.0f) : 0.0f;
+    // re-define d after its load so no later wait has to cover the d1 loads
+    asm volatile("" : "+v"(d[e]));
   }
+  float comp[EPL];  // rounding error carried with d: the exact value is d - comp
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) comp[e] = 0.0f;
   const float eta = a.eta, eps = a.eps, dmin = a.d_min, dmax = a.d_max;
   const bool clamp = a.clamp != 0, aware = a.beta_aware != 0;
 
-  float kc[U][EPL], bc[U], rc[U];
-  float kn[U][EPL], bn[U], rn[U];
-  auto fetch = [&](int64_t t0, float (&kk)[U][EPL], float (&bb)[U], float (&rr)[U]) {
+  // two key buffers used in turn (no register copies of in-flight loads)
+  Row<TIn, EPL, FULL> kA[G], kB[G];
+  float bA = 0.0f, rA = 1.0f, bB = 0.0f, rB = 1.0f;  // lane u holds token u of the group
+  auto fetch = [&](int64_t t0, Row<TIn, EPL, FULL> (&kk)[G], float &bb, float &rr) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int64_t t = t0 + u;
-      if (t < T) {
-        load_row<TIn, EPL, FULL>(kp + t * stride, lane, K, kk[u]);
-        bb[u] = bp[t * H];
-        rr[u] = HAS_R ? rp[t * H] : 1.0f;
-      } else {
+    for (int u = 0; u < G; ++u) {
+      const int64_t t = t0 + u < T ? t0 + u : T - 1;  // stay in bounds; unused past T
+      kk[u].load(kp + t * stride, lane, K);
+    }
+    const int64_t tl = t0 + (lane < G ? lane : 0);
+    const int64_t tc = tl < T ? tl : T - 1;
+    bb = bp[tc * H];
+    rr = HAS_R ? rp[tc * H] : 1.0f;
+  };
+  auto step = [&](int64_t t, const Row<TIn, EPL, FULL> &kr, float bt, float rt) {
+    float k[EPL], w[EPL], s[EPL], pa = 0.0f, pn = 0.0f;
+    kr.get(k);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) kk[u][e] = 0.0f;
-        bb[u] = 0.0f;
-        rr[u] = 1.0f;
+    for (int e = 0; e < EPL; ++e) {
+      s[e] = k[e] * k[e];
+      pn += s[e];
+      pa += d[e] * s[e];
+    }
+    if constexpr (WKT) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) w[e] = fmaf(-comp[e], k[e], d[e] * k[e]);  // (d - comp) k
+      store_row<TIn, EPL, FULL>(op + t * stride, lane, K, w);
+    }
+    if constexpr (WRES) {
+      float rres[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) rres[e] = ((d[e] - 1.0f) - comp[e]) * k[e];  // d - 1 is exact on [0.5, 2]
+      store_row<bf16, EPL, FULL>(rp_out + t * stride, lane, K, rres);
+    }
+    // off the chain: step coefficients from the key and gates alone
+    const float norm = wave_sum(pn);
+    const float bpr = aware ? bt : 1.0f;
+    const float ea = eta * bpr / fmaxf(norm, eps);  // c = ea - eb * <d, s>
+    const float eb = ea * bpr;
+    float p[EPL], q[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      p[e] = rt * d[e];                                       // r d = p + ep exactly
+      q[e] = fmaf(-rt, comp[e], fmaf(rt, d[e], -p[e]));       // ep - r comp
+    }
+    // on the chain
+    const float align = wave_sum(pa);
+    const float c = fmaf(-eb, align, ea);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float y = fmaf(c, s[e], q[e]);
+      const float t = p[e] + y;
+      float cn = (t - p[e]) - y;  // Fast2Sum error (|p| >= |y|)
+      float x = t;
+      if (clamp) {
+        x = fminf(fmaxf(t, dmin), dmax);
+        cn = x == t ? cn : 0.0f;  // a clamped coordinate is exact
       }
+      d[e] = x;
+      comp[e] = cn;
+    }
+  };
+  auto process = [&](int64_t t0, const Row<TIn, EPL, FULL> (&kk)[G], float bv, float rv) {
+    if (t0 + G <= T) {
+      // full group: straight-line code, so load waits stay per token
+#pragma unroll
+      for (int u = 0; u < G; ++u) step(t0 + u, kk[u], lane_bcast(bv, u), lane_bcast(rv, u));
+    } else {
+      const int nu = (int)(T - t0);
+#pragma unroll
+      for (int u = 0; u < G; ++u)
+        if (u < nu) step(t0 + u, kk[u], lane_bcast(bv, u), lane_bcast(rv, u));
     }
   };
 
-  if (T > 0) fetch(0, kc, bc, rc);
-  for (int64_t t0 = 0; t0 < T; t0 += U) {
-    if (t0 + U < T) fetch(t0 + U, kn, bn, rn);
-    const int nu = (int)((T - t0) < U ? (T - t0) : U);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (u < nu) {
-        float w[EPL], s[EPL], pa = 0.0f, pn = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          w[e] = d[e] * kc[u][e];
-          s[e] = kc[u][e] * kc[u][e];
-          pn += s[e];
-          pa += d[e] * s[e];
-        }
-        store_row<TIn, EPL, FULL>(op + (t0 + u) * stride, lane, K, w);
-        const float norm = wave_sum(pn);
-        const float align = wave_sum(pa);
-        const float inv_n = 1.0f / fmaxf(norm, eps);
-        const float bpr = aware ? bc[u] : 1.0f;
-        const float c = eta * bpr * (1.0f - bpr * align) * inv_n;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          float x = rc[u] * d[e] + c * s[e];
-          if (clamp) x = fminf(fmaxf(x, dmin), dmax);
-          d[e] = x;
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      bc[u] = bn[u];
-      rc[u] = rn[u];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) kc[u][e] = kn[u][e];
-    }
+  // Fetches are unconditional (addresses clamped to the last token) so the
+  // code between them is straight-line and every load wait stays exact.
+  if (T > 0) fetch(0, kA, bA, rA);
+  for (int64_t t0 = 0; t0 < T; t0 += 2 * G) {
+    fetch(t0 + G, kB, bB, rB);
+    process(t0, kA, bA, rA);
+    if (t0 + G >= T) break;
+    fetch(t0 + 2 * G, kA, bA, rA);
+    process(t0 + G, kB, bB, rB);
   }
   if (a.d_out) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      int64_t c = (int64_t)lane * EPL + e;
+      const int64_t c = (int64_t)lane * EPL + e;
       if (c < K) a.d_out[seq * K + c] = d[e];
     }
   }
 }
 
+template <typename TIn, int EPL, bool FULL, bool HAS_R>
+static void launch_out(const ScanArgs &a, hipStream_t s) {
+  dim3 grid((unsigned)(a.B * a.H)), block(64);
+  if (a.k_tilde && a.kt_res)
+    hipLaunchKernelGGL((precond_scan_kernel<TIn, EPL, FULL, HAS_R, true, true>), grid, block, 0, s, a);
+  else if (a.kt_res)
+    hipLaunchKernelGGL((precond_scan_kernel<TIn, EPL, FULL, HAS_R, false, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((precond_scan_kernel<TIn, EPL, FULL, HAS_R, true, false>), grid, block, 0, s, a);
+}
+
 template <typename TIn, int EPL, bool FULL>
 static hipError_t launch_epl(const ScanArgs &a, hipStream_t s) {
-  dim3 grid((unsigned)(a.B * a.H)), block(64);
   if (a.r)
-    hipLaunchKernelGGL((precond_scan_kernel<TIn, EPL, FULL, true>), grid, block, 0, s, a);
+    launch_out<TIn, EPL, FULL, true>(a, s);
   else
-    hipLaunchKernelGGL((precond_scan_kernel<TIn, EPL, FULL, false>), grid, block, 0, s, a);
+    launch_out<TIn, EPL, FULL, false>(a, s);
   return hipGetLastError();
 }
 

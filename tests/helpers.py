@@ -3,9 +3,15 @@
 Parity bars (from the OSDN forward's stated tolerances):
   * float32 inputs: d and k~ within 1e-5, o and S within 1e-4, relative, measured
     element-wise as |x - ref| / max(|ref|, rms(ref));
-  * bfloat16 inputs with fp32 accumulation: o and S within 2e-2 of the output
-    RMS, i.e. max|x - ref| / rms(ref); d (fp32 arithmetic) within 1e-5 relative;
-    k~ (rounded to bf16 on the device) within one bf16 ulp of the fp64 value.
+  * bfloat16 inputs with fp32 accumulation: o and S within 2e-2 max-abs error
+    normalised by the output RMS, where "output" is one readout vector o_t (one
+    (b,t,h) row over V) and one head's final state S (V x K).  Rounding the
+    exact result to bf16 alone costs up to 2^-9 * max/rms of the normalising
+    group; per row that stays near 1%, while a tensor-wide RMS would fail even a
+    correctly rounded result whenever outputs decay over the sequence.  Rows
+    whose RMS falls below 1% of the tensor RMS are judged against that floor;
+  * d (fp32 arithmetic) within 1e-5 relative; k~ rounded to bf16 on the device
+    within one bf16 ulp of the fp64 value.
 """
 import numpy as np
 
@@ -35,6 +41,30 @@ def rms_err(x, ref):
     if ref.size == 0:
         return 0.0
     return float(np.max(np.abs(x - ref)) / max(rms(ref), 1e-30))
+
+
+def group_err(x, ref, ndim=1, floor=1e-2):
+    """max over groups of max|x - ref| / rms(ref group); a group is the last
+    `ndim` axes (1: one output vector o_t, 2: one head's state).  Group RMS is
+    floored at `floor` times the whole tensor's RMS."""
+    x, ref = np.asarray(x, np.float64), np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    axes = tuple(range(ref.ndim - ndim, ref.ndim))
+    err = np.max(np.abs(x - ref), axis=axes)
+    grp = np.sqrt(np.mean(ref * ref, axis=axes))
+    den = np.maximum(grp, floor * max(rms(ref), 1e-30))
+    return float(np.max(err / den))
+
+
+def o_err(x, ref):
+    """bf16 parity metric of the readout o [..., V]."""
+    return group_err(x, ref, 1)
+
+
+def s_err(x, ref):
+    """bf16 parity metric of a state S [..., V, K] (per head)."""
+    return group_err(x, ref, 2)
 
 
 def ulp_err(x, ref):
