@@ -117,6 +117,9 @@ def main(argv=None):
                          ws=torch.empty(osdn.fwd_workspace_bytes(B, T, H, K, V, dtype=(
                              osdn.BF16 if p["dtype"] == "bf16" else osdn.F32), chunk=C),
                              dtype=torch.uint8, device=dev),
+                         sws=torch.empty(osdn.precond_scan_workspace_bytes(B, T, H, K, dtype=(
+                             osdn.BF16 if p["dtype"] == "bf16" else osdn.F32)),
+                             dtype=torch.uint8, device=dev),
                          S=torch.empty((B, H, V, K), dtype=torch.float32, device=dev),
                          d=torch.empty((B, H, K), dtype=torch.float32, device=dev)))
     kw = dict(chunk=C, eta=p["eta"], d_min=p["d_min"], d_max=p["d_max"], clamp=p["clamp"],
@@ -127,11 +130,15 @@ def main(argv=None):
         osdn.fwd(s["q"], s["k"], s["v"], s["beta"], s["r"], s["alpha"], None, None,
                  o=s["o"], S_out=s["S"], d_out=s["d"], workspace=s["ws"], **kw)
 
-    def scan(i):
+    def scan(i, chunked=True):
         s = sets[i % len(sets)]
         osdn.precond_scan(s["k"], s["beta"], s["r"], None, eta=p["eta"], d_min=p["d_min"],
                           d_max=p["d_max"], clamp=p["clamp"], eps=p["eps"],
-                          beta_aware=p["beta_aware"], k_tilde=s["kt"], d_out=s["d"])
+                          beta_aware=p["beta_aware"], k_tilde=s["kt"], d_out=s["d"],
+                          chunked=chunked, workspace=s["sws"] if chunked else None)
+
+    def scan_seq(i):
+        scan(i, chunked=False)
 
     def chunk(i):
         s = sets[i % len(sets)]
@@ -160,13 +167,17 @@ def main(argv=None):
     ms_step = timed(step, args.steps)
     wall = time.perf_counter() - w0
     log("step %.4f ms (wall %.3f s)" % (ms_step, wall))
-    # per-kernel average durations (each entry point is one kernel launch)
+    # per-phase average durations: phase 1 is three kernels (prep, solve,
+    # emit), phase 2 one
     for i in range(2):
         scan(i)
         chunk(i)
+        scan_seq(i)
     ms_scan = timed(scan, args.steps)
     ms_chunk = timed(chunk, args.steps)
-    log("phase1 %.4f ms  phase2 %.4f ms" % (ms_scan, ms_chunk))
+    ms_scan_seq = timed(scan_seq, max(1, args.steps // 5))
+    log("phase1 %.4f ms (token-by-token kernel %.4f ms)  phase2 %.4f ms"
+        % (ms_scan, ms_scan_seq, ms_chunk))
 
     tokens = B * T
     value = tokens / (ms_step * 1e-3)
@@ -177,9 +188,10 @@ def main(argv=None):
     p2_gbs = b2 * nth / (ms_chunk * 1e-3) / 1e9
     p2_tfl = f2 * nth / (ms_chunk * 1e-3) / 1e12
     phases = {
-        "precond_scan": {"kernel": "precond_scan_kernel", "ms": ms_scan, "bound": "hbm",
-                         "bytes_per_token_head": b1, "GB/s": p1_gbs,
-                         "hbm_frac": p1_gbs / HBM_PEAK_GBS},
+        "precond_scan": {"kernel": "scan_prep_kernel + scan_solve_kernel + scan_emit_kernel",
+                         "ms": ms_scan, "bound": "hbm", "bytes_per_token_head": b1,
+                         "GB/s": p1_gbs, "hbm_frac": p1_gbs / HBM_PEAK_GBS,
+                         "token_by_token_kernel_ms": ms_scan_seq},
         "chunk_fwd": {"kernel": "chunk_mfma_kernel", "ms": ms_chunk, "bound": "hbm",
                       "bytes_per_token_head": b2, "GB/s": p2_gbs,
                       "hbm_frac": p2_gbs / HBM_PEAK_GBS,

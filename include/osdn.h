@@ -107,11 +107,32 @@ osdn_status osdn_validate(const osdn_desc *desc);
  *   d1      [B,H,K]   f32      initial preconditioner, or NULL for ones
  *   k_tilde [B,T,H,K] dtype    OUT: write keys d_t (.) k_t (rounded to dtype)
  *   d_out   [B,H,K]   f32      OUT: d_{T+1}, or NULL (may alias d1)
+ *   workspace                  NULL: one kernel sweeps each (b,h) token by
+ *                              token.  Otherwise >= osdn_precond_scan_
+ *                              workspace_bytes(desc) bytes (16-byte aligned)
+ *                              and the sweep runs chunked: a parallel pass for
+ *                              the key norms, a per-(b,h) pass that finds the
+ *                              step scalar of every token (64-token chunks
+ *                              whose coordinates all sit on d_min, or all stay
+ *                              inside the box, are solved in closed form; any
+ *                              other chunk token by token), and a parallel pass
+ *                              that replays d and writes the write keys.  Both
+ *                              give the same result up to fp32 rounding.
  */
 osdn_status osdn_precond_scan(const osdn_desc *desc, const void *k,
                               const float *beta, const float *r,
                               const float *d1, void *k_tilde, float *d_out,
+                              void *workspace, size_t workspace_bytes,
                               void *stream);
+
+/* Bytes of workspace for the chunked phase 1; 0 on an invalid descriptor. */
+size_t osdn_precond_scan_workspace_bytes(const osdn_desc *desc);
+
+/* Byte offset, inside a chunked phase-1 workspace, of B*H*3 int32 counters
+ * left by the last sweep: per (b,h), the 64-token chunks solved with every
+ * coordinate on d_min, solved with every coordinate inside the box, and swept
+ * token by token.  (Diagnostics; -1 on an invalid descriptor.) */
+int64_t osdn_precond_scan_counters_offset(const osdn_desc *desc);
 
 /*
  * Phase 2, chunkwise WY delta rule with the write-key substitution of Eq.(6)
@@ -130,17 +151,20 @@ osdn_status osdn_chunk_fwd(const osdn_desc *desc, const void *q,
                            const float *S0, void *o, float *S_out,
                            void *stream);
 
-/* Bytes of device workspace osdn_fwd needs (room for the write keys between
- * the phases, B*T*H*K elements of dtype); 0 on an invalid descriptor. */
+/* Bytes of device workspace osdn_fwd needs (the write keys between the
+ * phases, B*T*H*K elements of dtype, followed by a chunked phase-1
+ * workspace); 0 on an invalid descriptor. */
 size_t osdn_fwd_workspace_bytes(const osdn_desc *desc);
 
 /*
  * Both phases on one stream (the two-phase schedule of Section 4.5).
  * Arguments as above.  k_tilde_out [B,T,H,K] dtype, when not NULL, receives
  * the write keys d_t (.) k_t.  workspace (>= osdn_fwd_workspace_bytes(desc)
- * bytes, 16-byte aligned) carries the write keys from phase 1 to phase 2; it
- * is required whenever T > 0 unless dtype is OSDN_F32 and k_tilde_out is
- * given.  For bf16 the workspace holds the residual (d_t - 1) (.) k_t rather
+ * bytes, 16-byte aligned, required when T > 0) carries the write keys from
+ * phase 1 to phase 2 and holds the chunked phase-1 scratch (its counters at
+ * osdn_fwd_workspace_bytes(desc) - osdn_precond_scan_workspace_bytes(desc) +
+ * osdn_precond_scan_counters_offset(desc)).  For bf16 the workspace holds the
+ * residual (d_t - 1) (.) k_t rather
  * than k~_t, so phase 2 sees the write keys to about 16 significant bits
  * instead of bf16's 8: the result is then closer to the exact forward than
  * osdn_precond_scan followed by osdn_chunk_fwd on a bf16 k~.

@@ -19,8 +19,9 @@ import os
 
 import torch
 
-__all__ = ["precond_scan", "chunk_fwd", "fwd", "fwd_workspace_bytes", "Desc",
-           "OsdnError", "library_path", "load", "F32", "BF16"]
+__all__ = ["precond_scan", "precond_scan_workspace_bytes", "scan_counters", "chunk_fwd",
+           "fwd", "fwd_workspace_bytes", "fwd_scan_counters", "Desc", "OsdnError",
+           "library_path", "load", "F32", "BF16"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libosdn.so")
@@ -29,8 +30,9 @@ _lib = None
 F32, BF16 = 0, 1
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 
-SYMBOLS = ("osdn_desc_init", "osdn_validate", "osdn_precond_scan", "osdn_chunk_fwd",
-           "osdn_fwd_workspace_bytes", "osdn_fwd", "osdn_status_str",
+SYMBOLS = ("osdn_desc_init", "osdn_validate", "osdn_precond_scan",
+           "osdn_precond_scan_workspace_bytes", "osdn_precond_scan_counters_offset",
+           "osdn_chunk_fwd", "osdn_fwd_workspace_bytes", "osdn_fwd", "osdn_status_str",
            "osdn_last_error", "osdn_version")
 
 
@@ -66,7 +68,11 @@ def load():
     dp = ctypes.POINTER(Desc)
     lib.osdn_desc_init.argtypes = [dp, i64, i64, i64, i64, i64]
     lib.osdn_validate.argtypes = [dp]
-    lib.osdn_precond_scan.argtypes = [dp, vp, fp, fp, fp, vp, fp, vp]
+    lib.osdn_precond_scan.argtypes = [dp, vp, fp, fp, fp, vp, fp, vp, ctypes.c_size_t, vp]
+    lib.osdn_precond_scan_workspace_bytes.argtypes = [dp]
+    lib.osdn_precond_scan_workspace_bytes.restype = ctypes.c_size_t
+    lib.osdn_precond_scan_counters_offset.argtypes = [dp]
+    lib.osdn_precond_scan_counters_offset.restype = ctypes.c_int64
     lib.osdn_chunk_fwd.argtypes = [dp, vp, vp, vp, vp, fp, fp, fp, vp, fp, vp]
     lib.osdn_fwd_workspace_bytes.argtypes = [dp]
     lib.osdn_fwd_workspace_bytes.restype = ctypes.c_size_t
@@ -137,9 +143,40 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _workspace(workspace, need, dev):
+    if workspace is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != dev \
+            or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % dev)
+    return workspace
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def precond_scan_workspace_bytes(B, T, H, K, dtype=BF16) -> int:
+    desc = make_desc(B, T, H, K, K, dtype=dtype)
+    return int(load().osdn_precond_scan_workspace_bytes(ctypes.byref(desc)))
+
+
+def scan_counters(workspace, B, T, H, K, dtype=BF16, offset=0):
+    """Per-(b,h) chunk counters a chunked phase-1 sweep left in `workspace`
+    (starting `offset` bytes in): int32 [B,H,3] = chunks taken with d pinned on
+    d_min, in closed form with a fixed active set, and token by token."""
+    desc = make_desc(B, T, H, K, K, dtype=dtype)
+    off = offset + int(load().osdn_precond_scan_counters_offset(ctypes.byref(desc)))
+    raw = workspace.view(torch.uint8).reshape(-1)[off:off + B * H * 3 * 4]
+    return raw.cpu().view(torch.int32).reshape(B, H, 3)
+
+
 def precond_scan(k, beta, r=None, d1=None, *, eta=0.003, d_min=0.5, d_max=2.0,
-                 clamp=True, eps=1e-6, beta_aware=True, k_tilde=None, d_out=None):
+                 clamp=True, eps=1e-6, beta_aware=True, k_tilde=None, d_out=None,
+                 chunked=True, workspace=None):
     """Phase 1.  k [B,T,H,K] (bf16/f32), beta and r [B,T,H] f32, d1 [B,H,K] f32.
+    chunked=True runs the chunked kernels in `workspace` (allocated when None),
+    chunked=False the token-by-token kernel.
     Returns (k_tilde [B,T,H,K] in k's dtype, d_out [B,H,K] f32)."""
     B, T, H, K = k.shape
     dev, f32 = k.device, torch.float32
@@ -155,8 +192,14 @@ def precond_scan(k, beta, r=None, d1=None, *, eta=0.003, d_min=0.5, d_max=2.0,
     _need(d_out, "d_out", (B, H, K), f32, dev)
     desc = make_desc(B, T, H, K, K, dtype=_dtype_code(k), eta=eta, d_min=d_min,
                      d_max=d_max, clamp=clamp, eps=eps, beta_aware=beta_aware)
+    if chunked:
+        need = int(load().osdn_precond_scan_workspace_bytes(ctypes.byref(desc)))
+        workspace = _workspace(workspace, need, dev)
+    else:
+        workspace = None
     _check(load().osdn_precond_scan(ctypes.byref(desc), _ptr(k), _ptr(beta), _ptr(r),
-                                    _ptr(d1), _ptr(k_tilde), _ptr(d_out), _stream(dev)))
+                                    _ptr(d1), _ptr(k_tilde), _ptr(d_out), _ptr(workspace),
+                                    ctypes.c_size_t(_nbytes(workspace)), _stream(dev)))
     return k_tilde, d_out
 
 
@@ -191,6 +234,13 @@ def fwd_workspace_bytes(B, T, H, K, V, dtype=BF16, chunk=64) -> int:
     return int(load().osdn_fwd_workspace_bytes(ctypes.byref(desc)))
 
 
+def fwd_scan_counters(workspace, B, T, H, K, V, dtype=BF16, chunk=64):
+    """The phase-1 chunk counters (see scan_counters) inside an osdn_fwd workspace."""
+    off = fwd_workspace_bytes(B, T, H, K, V, dtype, chunk) - precond_scan_workspace_bytes(
+        B, T, H, K, dtype)
+    return scan_counters(workspace, B, T, H, K, dtype, offset=off)
+
+
 def fwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, chunk=64, eta=0.003,
         d_min=0.5, d_max=2.0, clamp=True, eps=1e-6, q_scale=1.0, beta_aware=True,
         o=None, S_out=None, d_out=None, k_tilde_out=None, workspace=None):
@@ -214,17 +264,10 @@ def fwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, chunk=64, eta=0.
     _need(k_tilde_out, "k_tilde_out", (B, T, H, K), dt, dev)
     desc = make_desc(B, T, H, K, V, dtype=_dtype_code(q), chunk=chunk, eta=eta, d_min=d_min,
                      d_max=d_max, clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware)
-    ws_bytes = 0
-    if k_tilde_out is None or dt == torch.bfloat16:
-        need = int(load().osdn_fwd_workspace_bytes(ctypes.byref(desc)))
-        if workspace is None:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    if workspace is not None:
-        if workspace.device != dev or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous tensor on %s" % dev)
-        ws_bytes = workspace.numel() * workspace.element_size()
+    need = int(load().osdn_fwd_workspace_bytes(ctypes.byref(desc)))
+    workspace = _workspace(workspace, need, dev)
     _check(load().osdn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r),
                            _ptr(alpha), _ptr(d1), _ptr(S0), _ptr(o), _ptr(S_out), _ptr(d_out),
                            _ptr(k_tilde_out), _ptr(workspace),
-                           ctypes.c_size_t(ws_bytes), _stream(dev)))
+                           ctypes.c_size_t(_nbytes(workspace)), _stream(dev)))
     return o, S_out, d_out

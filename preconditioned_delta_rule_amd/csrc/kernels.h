@@ -34,6 +34,20 @@ struct ChunkArgs {
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_precond_scan(const ScanArgs &a, bool bf16, hipStream_t s);
+
+// Chunked phase 1 (prep / solve / emit kernels).  Workspace: per-token key
+// norm and step scalar c (fp32 [B,T,H] each), d at every 64-token chunk start
+// (fp32 [B,H,N,K]), one word per chunk that says whether the chunk keeps a d
+// that sits on d_min there (int [B,H,N]), and three counters per (b,h) (int
+// [B,H,3]: chunks taken on the pinned, closed-form and token-by-token paths).
+struct ScanWork {
+  float *norm, *cstep, *dstart;
+  int *pin, *flags;
+};
+constexpr int SCAN_CHUNK = 64;
+size_t scan_work_bytes(int64_t B, int64_t T, int64_t H, int64_t K);
+ScanWork scan_work_layout(void *base, int64_t B, int64_t T, int64_t H, int64_t K);
+hipError_t launch_precond_scan_chunked(const ScanArgs &a, const ScanWork &w, bool bf16, hipStream_t s);
 hipError_t launch_chunk_generic(const ChunkArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s);
 

@@ -190,8 +190,20 @@ osdn_status osdn_validate(const osdn_desc *d) {
   return ok();
 }
 
+size_t osdn_precond_scan_workspace_bytes(const osdn_desc *d) {
+  if (validate(d, 1) != OSDN_OK) return 0;
+  return osdn::scan_work_bytes(d->B, d->T, d->H, d->K);
+}
+
+int64_t osdn_precond_scan_counters_offset(const osdn_desc *d) {
+  if (validate(d, 1) != OSDN_OK) return -1;
+  osdn::ScanWork w = osdn::scan_work_layout(nullptr, d->B, d->T, d->H, d->K);
+  return (int64_t)reinterpret_cast<uintptr_t>(w.flags);
+}
+
 osdn_status osdn_precond_scan(const osdn_desc *d, const void *k, const float *beta, const float *r,
-                              const float *d1, void *k_tilde, float *d_out, void *stream) {
+                              const float *d1, void *k_tilde, float *d_out, void *workspace,
+                              size_t workspace_bytes, void *stream) {
   OSDN_TRY(validate(d, 1));
   const bool need_seq = d->T > 0;
   OSDN_TRY(check_ptr(k, "k", need_seq));
@@ -200,8 +212,21 @@ osdn_status osdn_precond_scan(const osdn_desc *d, const void *k, const float *be
   OSDN_TRY(check_ptr(d1, "d1", false));
   OSDN_TRY(check_ptr(k_tilde, "k_tilde", need_seq));
   OSDN_TRY(check_ptr(d_out, "d_out", false));
+  OSDN_TRY(check_ptr(workspace, "workspace", false));
   if (k_tilde && k_tilde == k) return fail(OSDN_EINVAL, "k_tilde must not alias k");
-  OSDN_TRY(run_scan(d, scan_args(d, k, beta, r, d1, k_tilde, d_out), static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const osdn::ScanArgs sa = scan_args(d, k, beta, r, d1, k_tilde, d_out);
+  if (!workspace) {
+    OSDN_TRY(run_scan(d, sa, s));
+    return ok();
+  }
+  const size_t need = osdn::scan_work_bytes(d->B, d->T, d->H, d->K);
+  if (workspace_bytes < need)
+    return fail(OSDN_EINVAL, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
+  OSDN_TRY(hip_status(osdn::launch_precond_scan_chunked(
+                          sa, osdn::scan_work_layout(workspace, d->B, d->T, d->H, d->K),
+                          d->dtype == OSDN_BF16, s),
+                      "phase-1 launch"));
   return ok();
 }
 
@@ -225,10 +250,14 @@ osdn_status osdn_chunk_fwd(const osdn_desc *d, const void *q, const void *k, con
   return ok();
 }
 
+static size_t fwd_keys_bytes(const osdn_desc *d) {
+  const size_t n = (size_t)d->B * (size_t)d->T * (size_t)d->H * (size_t)d->K * elem_bytes(d->dtype);
+  return (n + 255) & ~(size_t)255;
+}
+
 size_t osdn_fwd_workspace_bytes(const osdn_desc *d) {
   if (validate(d, 3) != OSDN_OK) return 0;
-  size_t n = (size_t)d->B * (size_t)d->T * (size_t)d->H * (size_t)d->K * elem_bytes(d->dtype);
-  return (n + 255) & ~(size_t)255;
+  return fwd_keys_bytes(d) + osdn::scan_work_bytes(d->B, d->T, d->H, d->K);
 }
 
 osdn_status osdn_fwd(const osdn_desc *d, const void *q, const void *k, const void *v, const float *beta,
@@ -250,29 +279,32 @@ osdn_status osdn_fwd(const osdn_desc *d, const void *q, const void *k, const voi
   OSDN_TRY(check_ptr(k_tilde_out, "k_tilde_out", false));
   hipStream_t s = static_cast<hipStream_t>(stream);
   osdn::ScanArgs sa = scan_args(d, k, beta, r, d1, k_tilde_out, d_out);
-  const void *kt_for_chunk = k_tilde_out;
-  bool kt_is_res = false;
-  if (need_seq && d->dtype == OSDN_BF16) {
-    // bf16: the write keys travel between the phases as the bf16 residual
-    // (d - 1) (.) k in the workspace, which with k gives k~ to ~16 bits
-    OSDN_TRY(check_ptr(workspace, "workspace", true));
-    const size_t need = osdn_fwd_workspace_bytes(d);
-    if (workspace_bytes < need)
-      return fail(OSDN_EINVAL, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
-    sa.kt_res = workspace;
-    kt_for_chunk = workspace;
-    kt_is_res = true;
-  } else if (need_seq && !k_tilde_out) {
-    OSDN_TRY(check_ptr(workspace, "workspace", true));
-    const size_t need = osdn_fwd_workspace_bytes(d);
-    if (workspace_bytes < need)
-      return fail(OSDN_EINVAL, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
-    sa.k_tilde = workspace;
-    kt_for_chunk = workspace;
+  osdn::ChunkArgs ca = chunk_args(d, q, k, k_tilde_out, v, beta, alpha, S0, o, S_out);
+  if (!need_seq) {
+    // nothing to sweep: d_out = d1 and S_out = S0 (the kernels do the copy)
+    OSDN_TRY(run_scan(d, sa, s));
+    OSDN_TRY(run_chunk(d, ca, s));
+    return ok();
   }
-  OSDN_TRY(run_scan(d, sa, s));
-  osdn::ChunkArgs ca = chunk_args(d, q, k, kt_for_chunk, v, beta, alpha, S0, o, S_out);
-  ca.kt_is_res = kt_is_res;
+  OSDN_TRY(check_ptr(workspace, "workspace", true));
+  const size_t need = osdn_fwd_workspace_bytes(d);
+  if (workspace_bytes < need)
+    return fail(OSDN_EINVAL, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
+  char *ws = static_cast<char *>(workspace);
+  if (d->dtype == OSDN_BF16) {
+    // bf16: the write keys travel between the phases as the bf16 residual
+    // (d - 1) (.) k, which with k gives k~ to ~16 bits
+    sa.kt_res = ws;
+    ca.kt = ws;
+    ca.kt_is_res = true;
+  } else if (!k_tilde_out) {
+    sa.k_tilde = ws;
+    ca.kt = ws;
+  }
+  OSDN_TRY(hip_status(osdn::launch_precond_scan_chunked(
+                          sa, osdn::scan_work_layout(ws + fwd_keys_bytes(d), d->B, d->T, d->H, d->K),
+                          d->dtype == OSDN_BF16, s),
+                      "phase-1 launch"));
   OSDN_TRY(run_chunk(d, ca, s));
   return ok();
 }

@@ -1,0 +1,533 @@
+// Phase 1 of OSDN, chunked: the same sweep as precond_scan.hip (Section 4.2
+// Eq.(4) / Algorithm 1, Section 4.4 Eq.(7), Appendix B), reorganised so that
+// only a scalar per token stays on the sequential path.
+//
+// Per token the sweep is d <- clip(r_t d + c_t s_t) with s_t = k_t^2 and the
+// step scalar c_t = a_t - b_t <d, s_t>, a_t = eta b'/max(|k_t|^2, eps),
+// b_t = a_t b'.  Given every c_t, each coordinate of d follows its own
+// recurrence, so the write keys can be emitted chunk-parallel.  The kernels:
+//
+//  prep  (one wave per (b,h,64-token chunk)): |k_t|^2, and the step scalar a
+//        chunk has when every coordinate of d sits on d_min and stays there
+//        (then <d, s_t> = d_min |k_t|^2); the chunk is marked when
+//        r_t d_min + c_t max_i s_{t,i} <= d_min holds for all its tokens.
+//  solve (one wave per (b,h), chunks in order): c_t for every token and d at
+//        each chunk start.  A chunk that starts with d on d_min everywhere
+//        and is marked needs no work.  Otherwise, Section 4.2 notes that away
+//        from the box the update is affine in d.  Suppose the coordinates on a
+//        bound at the chunk start stay there and the others never reach one
+//        (a fixed active set).  Then, with R_t = prod_{l<t} r_l, a free
+//        coordinate is d_t = R_t (d_0 + sum_{j<t} x_j s_j), x_j = c_j/R_{j+1},
+//        and x solves a unit lower-triangular system whose off-diagonal part
+//        is the Gram matrix of the key squares restricted to the free
+//        coordinates (the phase-1 counterpart of the chunk's UT transform; the
+//        Gram on the matrix cores, the 64-step substitution in fp32).  The
+//        assumption is checked afterwards, exactly for the coordinates on a
+//        bound and with sum_j |x_j| s_{j,i} for the free ones; a chunk that
+//        fails it is swept token by token, as the sequential kernel does.
+//  emit  (one wave per (b,h,chunk)): replays d_{t+1} = clip(r_t d_t + c_t s_t)
+//        from the chunk's start and writes k~_t = d_t (.) k_t (and/or the
+//        bf16 residual (d_t - 1) (.) k_t).
+#include "kernels.h"
+#include "scan_common.h"
+
+namespace osdn {
+
+namespace {
+
+constexpr int CH = SCAN_CHUNK;  // tokens per chunk (64: one per lane)
+
+template <typename TIn, int EPL>
+__device__ __forceinline__ void lds_get(const TIn *p, float (&out)[EPL]) {
+  typedef typename RowVec<TIn, EPL>::type Vt;
+  const Vt v = *reinterpret_cast<const Vt *>(p);
+  if constexpr (EPL == 1) {
+    out[0] = to_f32(v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) out[e] = to_f32(v[e]);
+  }
+}
+
+template <typename TIn, int EPL, bool FULL>
+__device__ __forceinline__ void lds_put(TIn *p, const Row<TIn, EPL, FULL> &r) {
+  typedef typename RowVec<TIn, EPL>::type Vt;
+  Vt v;
+  __builtin_memcpy(&v, r.w, sizeof(Vt));
+  *reinterpret_cast<Vt *>(p) = v;
+}
+
+// ---------------------------------------------------------------- prep
+template <typename TIn, int EPL, bool FULL, bool HAS_R>
+__global__ __launch_bounds__(64) void scan_prep_kernel(ScanArgs a, ScanWork wk, int64_t N) {
+  const int lane = threadIdx.x;
+  const int64_t seq = blockIdx.x / N, n = blockIdx.x % N;
+  const int64_t H = a.H, T = a.T, K = a.K;
+  const int64_t b = seq / H, h = seq - b * H;
+  const int64_t t0 = n * CH;
+  const int L = (int)((T - t0) < CH ? (T - t0) : CH);
+  const bool tok = lane < L;
+  const TIn *kp = static_cast<const TIn *>(a.k) + ((b * T + t0) * H + h) * K;
+  const int64_t stride = H * K;
+  const int64_t gi = (b * T + t0 + (tok ? lane : 0)) * H + h;
+  const float bt = a.beta[gi];
+  const float rt = HAS_R ? a.r[gi] : 1.0f;
+  Row<TIn, EPL, FULL> rows[CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u) rows[u].load(kp + (u < L ? u : L - 1) * stride, lane, K);
+  float sn[CH], sm[CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+    float k[EPL];
+    rows[u].get(k);
+    float pn = 0.0f, pm = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float s = k[e] * k[e];
+      pn += s;
+      pm = fmaxf(pm, s);
+    }
+    sn[u] = pn;
+    sm[u] = pm;
+  }
+  const float nrm = reduce_scatter64<false>(sn, lane);  // lane u: |k_{t0+u}|^2
+  const float smx = reduce_scatter64<true>(sm, lane);   // lane u: max_i k_{t0+u,i}^2
+  const float dmin = a.d_min;
+  const float bpr = a.beta_aware ? bt : 1.0f;
+  const float ea = a.eta * bpr / fmaxf(nrm, a.eps);
+  const float eb = ea * bpr;
+  const float cpin = fmaf(-eb, dmin * nrm, ea);
+  const bool stays = !tok || fmaf(cpin, cpin > 0.0f ? smx : 0.0f, rt * dmin) <= dmin;
+  const bool pinned = a.clamp != 0 && __all(stays) != 0;
+  if (tok) {
+    wk.norm[gi] = nrm;
+    wk.cstep[gi] = cpin;
+  }
+  if (lane == 0) wk.pin[seq * N + n] = pinned ? 1 : 0;
+}
+
+// ---------------------------------------------------------------- solve
+// Shared memory: the chunk's key rows as loaded (TIn [CH][64 EPL]), the key
+// squares of the free coordinates in bf16 ([CH][64 EPL + 8]), their Gram
+// matrix (fp32 [CH][CH+1]) and per-token (x, c, r) (float4 [CH]).
+template <typename TIn, int EPL>
+constexpr size_t solve_lds_bytes() {
+  return (size_t)CH * 64 * EPL * sizeof(TIn) + (size_t)CH * (64 * EPL + 8) * 2 + (size_t)CH * (CH + 1) * 4 +
+         (size_t)CH * 16;
+}
+
+template <typename TIn, int EPL, bool FULL, bool HAS_R, bool PF>
+__global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk, int64_t N) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr int RP = 64 * EPL;      // row pitch of sR (elements)
+  constexpr int SP = 64 * EPL + 8;  // row pitch of sS (bf16)
+  TIn *sR = reinterpret_cast<TIn *>(smem);
+  bf16 *sS = reinterpret_cast<bf16 *>(smem + (size_t)CH * RP * sizeof(TIn));
+  float *sG = reinterpret_cast<float *>(smem + (size_t)CH * RP * sizeof(TIn) + (size_t)CH * SP * 2);
+  floatx4 *sTok = reinterpret_cast<floatx4 *>(sG + CH * (CH + 1));
+
+  const int lane = threadIdx.x;
+  const int64_t seq = blockIdx.x;
+  const int64_t H = a.H, T = a.T, K = a.K;
+  const int64_t b = seq / H, h = seq - b * H;
+  const int64_t stride = H * K;
+  const float eta = a.eta, eps = a.eps, dmin = a.d_min, dmax = a.d_max;
+  const bool clamp = a.clamp != 0, aware = a.beta_aware != 0;
+
+  float d[EPL];
+  bool valid[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int64_t c = (int64_t)lane * EPL + e;
+    valid[e] = c < K;
+    d[e] = valid[e] ? (a.d1 ? a.d1[seq * K + c] : 1.0f) : 0.0f;
+  }
+  int n_pinned = 0, n_active = 0, n_seq = 0;
+  uint64_t pinmask = 0;
+  Row<TIn, EPL, FULL> nrow[PF ? CH : 1];
+  float nbt = 0.0f, nrt = 1.0f, nnrm = 1.0f;
+  bool have = false;  // chunk n's rows already sit in sR, its scalars in nbt/nrt/nnrm
+
+  for (int64_t n = 0; n < N; ++n) {
+    const int64_t t0 = n * CH;
+    const int L = (int)((T - t0) < CH ? (T - t0) : CH);
+    const bool tok = lane < L;  // lane u <-> token t0 + u
+    const int64_t gi = (b * T + t0 + (tok ? lane : 0)) * H + h;
+    if ((n & 63) == 0) {
+      const int p = n + lane < N ? wk.pin[seq * N + n + lane] : 0;
+      pinmask = __ballot(p != 0);
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      if (valid[e]) wk.dstart[(seq * N + n) * K + lane * EPL + e] = d[e];
+
+    // where d sits: on d_min, on d_max, inside
+    bool onlo[EPL], onhi[EPL], fr[EPL];
+    bool lo = false, hi = false, free_ = false;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      onlo[e] = clamp && valid[e] && d[e] == dmin;
+      onhi[e] = clamp && valid[e] && d[e] == dmax && !onlo[e];
+      fr[e] = valid[e] && !onlo[e] && !onhi[e];
+      lo |= onlo[e];
+      hi |= onhi[e];
+      free_ |= fr[e];
+    }
+    const bool any_lo = __any(lo) != 0, any_hi = __any(hi) != 0, any_free = __any(free_) != 0;
+    if (!any_free && !any_hi && ((pinmask >> (n & 63)) & 1)) {
+      // pinned chunk: d stays on d_min, c_t was written by the prep pass
+      ++n_pinned;
+      have = false;
+      continue;
+    }
+
+    // this chunk's key rows and scalars
+    const TIn *kp = static_cast<const TIn *>(a.k) + ((b * T + t0) * H + h) * K;
+    float bt, rt, nrm;
+    if (PF && have) {
+      bt = nbt;
+      rt = nrt;
+      nrm = nnrm;
+    } else {
+      bt = a.beta[gi];
+      rt = HAS_R ? a.r[gi] : 1.0f;
+      nrm = wk.norm[gi];
+#pragma unroll
+      for (int u0 = 0; u0 < CH; u0 += 16) {
+        Row<TIn, EPL, FULL> tmp[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) tmp[u].load(kp + (u0 + u < L ? u0 + u : L - 1) * stride, lane, K);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) lds_put<TIn, EPL, FULL>(sR + (u0 + u) * RP + lane * EPL, tmp[u]);
+      }
+    }
+    if (!tok) {
+      bt = 0.0f;
+      rt = 1.0f;
+      nrm = 1.0f;
+    }
+    // prefetch the next chunk (rows stay in registers until this one is done)
+    const bool pf = PF && n + 1 < N;
+    if constexpr (PF) {
+      if (pf) {
+        const int64_t t1 = t0 + CH;
+        const int L1 = (int)((T - t1) < CH ? (T - t1) : CH);
+        const TIn *kp1 = kp + CH * stride;
+#pragma unroll
+        for (int u = 0; u < CH; ++u) nrow[u].load(kp1 + (u < L1 ? u : L1 - 1) * stride, lane, K);
+        const int64_t gi1 = (b * T + t1 + (lane < L1 ? lane : 0)) * H + h;
+        nbt = a.beta[gi1];
+        nrt = HAS_R ? a.r[gi1] : 1.0f;
+        nnrm = wk.norm[gi1];
+      }
+    }
+    const float bpr = aware ? bt : 1.0f;
+    const float ea = eta * bpr / fmaxf(nrm, eps);  // c_t = ea - eb <d, s_t>
+    const float eb = ea * bpr;
+    float cst = 0.0f;  // lane u: c for token t0 + u
+    bool done = false;
+    __syncthreads();
+
+    // ---- fixed active set, closed form
+    {
+      float pvF[CH], pvP[HAS_R ? CH : 1];
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        float k[EPL];
+        lds_get<TIn, EPL>(sR + u * RP + lane * EPL, k);
+        float pf_ = 0.0f, pp_ = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float s = u < L ? k[e] * k[e] : 0.0f;
+          if (HAS_R) {
+            pf_ = fmaf(fr[e] ? d[e] : 0.0f, s, pf_);
+            pp_ = fmaf(fr[e] ? 0.0f : d[e], s, pp_);
+          } else {
+            pf_ = fmaf(d[e], s, pf_);
+          }
+          if (any_free) sS[u * SP + lane * EPL + e] = to_bf16(fr[e] ? s : 0.0f);
+        }
+        pvF[u] = pf_;
+        if (HAS_R) pvP[HAS_R ? u : 0] = pp_;
+      }
+      const float p0F = reduce_scatter64<false>(pvF, lane);  // <d_0, s_t> over the free (all, without r) coords
+      float p0P = 0.0f;
+      if constexpr (HAS_R) p0P = reduce_scatter64<false>(pvP, lane);  // over the coords on a bound
+      __syncthreads();
+      if (any_free) {
+        // Gram matrix of the free key squares, lower 16x16 tiles
+        const int l16 = lane & 15, lq = lane >> 4;
+        for (int ti = 0; ti < 4; ++ti)
+          for (int tj = 0; tj <= ti; ++tj) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k0 = 0; k0 < 64 * EPL; k0 += 32) {
+              const bf16x8 x = *reinterpret_cast<const bf16x8 *>(&sS[(16 * ti + l16) * SP + k0 + 8 * lq]);
+              const bf16x8 y = *reinterpret_cast<const bf16x8 *>(&sS[(16 * tj + l16) * SP + k0 + 8 * lq]);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sG[(16 * ti + 4 * lq + i) * (CH + 1) + 16 * tj + l16] = acc[i];
+          }
+        __syncthreads();
+      }
+      float x = 0.0f, Rn = 1.0f;
+      if (!any_free) {
+        // every coordinate on a bound: <d, s_t> = <d_0, s_t>
+        if (tok) cst = fmaf(-eb, p0P + p0F, ea);
+      } else {
+        // retention products: Rn = R_{t+1}, Rt = R_t (log-space scan)
+        float Rt = 1.0f;
+        if constexpr (HAS_R) {
+          const float lr = logf(rt);
+          float lin = lr;
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(lin, off, 64);
+            if (lane >= off) lin += y;
+          }
+          Rn = __expf(lin);
+          Rt = __expf(lin - lr);
+        }
+        // x_t + g_t sum_{j<t} G_jt x_j = ea_t / R_{t+1} - g_t (p0P_t / R_t + p0F_t),
+        // g_t = eb_t R_t / R_{t+1}
+        const float g = HAS_R ? eb * (Rt / Rn) : eb;
+        float acc = 0.0f;
+        if (tok) acc = HAS_R ? ea / Rn - g * (p0P / Rt + p0F) : ea - g * p0F;
+        float grow[CH];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          const float gj = sG[lane * (CH + 1) + j];
+          grow[j] = j < lane ? g * gj : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < CH - 1; ++j) {
+          const float xj = lane_bcast(acc, j);
+          acc = fmaf(-grow[j], xj, acc);  // grow[j] = 0 on lanes <= j
+        }
+        x = tok ? acc : 0.0f;
+        cst = Rn * x;
+      }
+      sTok[lane] = floatx4{x, cst, rt, 0.0f};
+      __syncthreads();
+      // check the active set; d_L = R_L (d_0 + sum_j x_j s_j) on free coords
+      float sum[EPL], bnd[EPL], mxl[EPL], mnh[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        sum[e] = bnd[e] = 0.0f;
+        mxl[e] = dmin;
+        mnh[e] = dmax;
+      }
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        if (u < L) {
+          float k[EPL];
+          lds_get<TIn, EPL>(sR + u * RP + lane * EPL, k);
+          const floatx4 tv = sTok[u];
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) {
+            const float s = k[e] * k[e];
+            sum[e] = fmaf(tv[0], s, sum[e]);
+            bnd[e] = fmaf(fabsf(tv[0]), s, bnd[e]);
+            if (any_lo) mxl[e] = fmaxf(mxl[e], fmaf(tv[1], s, tv[2] * dmin));
+            if (any_hi) mnh[e] = fminf(mnh[e], fmaf(tv[1], s, tv[2] * dmax));
+          }
+        }
+      }
+      // the bound on free coordinates needs R_t non-increasing; R_L >= 1/4
+      // keeps the 1/R_t factors from costing more than two bits
+      const float RL = lane_bcast(Rn, L - 1);
+      bool ok = true;
+      if (HAS_R && any_free) ok = RL >= 0.25f && rt <= 1.0f;
+      float dn[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        dn[e] = fr[e] ? RL * (d[e] + sum[e]) : d[e];
+        if (fr[e] && clamp) ok = ok && RL * (d[e] - bnd[e]) >= dmin && d[e] + bnd[e] <= dmax;
+        if (onlo[e]) ok = ok && mxl[e] <= dmin;
+        if (onhi[e]) ok = ok && mnh[e] >= dmax;
+      }
+      if (__all(ok)) {
+        done = true;
+        ++n_active;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) d[e] = valid[e] ? dn[e] : 0.0f;
+      }
+    }
+
+    if (!done) {
+      // token by token, the exact sweep
+      ++n_seq;
+      cst = 0.0f;
+      for (int u = 0; u < L; ++u) {
+        float k[EPL], s[EPL], pa = 0.0f;
+        lds_get<TIn, EPL>(sR + u * RP + lane * EPL, k);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          s[e] = k[e] * k[e];
+          pa = fmaf(d[e], s[e], pa);
+        }
+        const float align = wave_sum(pa);
+        const float c = fmaf(-lane_bcast(eb, u), align, lane_bcast(ea, u));
+        const float ru = lane_bcast(rt, u);
+        cst = lane == u ? c : cst;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          float xx = fmaf(c, s[e], ru * d[e]);
+          if (clamp) xx = fminf(fmaxf(xx, dmin), dmax);
+          d[e] = valid[e] ? xx : 0.0f;
+        }
+      }
+    }
+    if (tok) wk.cstep[gi] = cst;
+    __syncthreads();
+    if constexpr (PF) {
+      if (pf) {
+#pragma unroll
+        for (int u = 0; u < CH; ++u) lds_put<TIn, EPL, FULL>(sR + u * RP + lane * EPL, nrow[u]);
+      }
+    }
+    have = pf;
+    __syncthreads();
+  }
+  if (a.d_out) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      if (valid[e]) a.d_out[seq * K + lane * EPL + e] = d[e];
+  }
+  if (lane == 0) {
+    wk.flags[3 * seq + 0] = n_pinned;
+    wk.flags[3 * seq + 1] = n_active;
+    wk.flags[3 * seq + 2] = n_seq;
+  }
+}
+
+// ---------------------------------------------------------------- emit
+template <typename TIn, int EPL, bool FULL, bool HAS_R, bool WKT, bool WRES>
+__global__ __launch_bounds__(64) void scan_emit_kernel(ScanArgs a, ScanWork wk, int64_t N) {
+  const int lane = threadIdx.x;
+  const int64_t seq = blockIdx.x / N, n = blockIdx.x % N;
+  const int64_t H = a.H, T = a.T, K = a.K;
+  const int64_t b = seq / H, h = seq - b * H;
+  const int64_t t0 = n * CH;
+  const int L = (int)((T - t0) < CH ? (T - t0) : CH);
+  const int64_t stride = H * K;
+  const int64_t row0 = ((b * T + t0) * H + h) * K;
+  const TIn *kp = static_cast<const TIn *>(a.k) + row0;
+  Row<TIn, EPL, FULL> rows[CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u) rows[u].load(kp + (u < L ? u : L - 1) * stride, lane, K);
+  const int64_t gi = (b * T + t0 + (lane < L ? lane : 0)) * H + h;
+  const float cv = wk.cstep[gi];
+  const float rv = HAS_R ? a.r[gi] : 1.0f;
+  const float dmin = a.d_min, dmax = a.d_max;
+  const bool clamp = a.clamp != 0;
+  float d[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int64_t c = (int64_t)lane * EPL + e;
+    d[e] = c < K ? wk.dstart[(seq * N + n) * K + c] : 0.0f;
+  }
+  TIn *op = WKT ? static_cast<TIn *>(a.k_tilde) + row0 : nullptr;
+  bf16 *rp = WRES ? static_cast<bf16 *>(a.kt_res) + row0 : nullptr;
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+    if (u < L) {
+      float k[EPL];
+      rows[u].get(k);
+      if constexpr (WKT) {
+        float w[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) w[e] = d[e] * k[e];
+        store_row<TIn, EPL, FULL>(op + u * stride, lane, K, w);
+      }
+      if constexpr (WRES) {
+        float w[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) w[e] = (d[e] - 1.0f) * k[e];  // d - 1 is exact on [0.5, 2]
+        store_row<bf16, EPL, FULL>(rp + u * stride, lane, K, w);
+      }
+      const float c = lane_bcast(cv, u), r = lane_bcast(rv, u);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float x = fmaf(c, k[e] * k[e], r * d[e]);
+        if (clamp) x = fminf(fmaxf(x, dmin), dmax);
+        d[e] = x;
+      }
+    }
+  }
+}
+
+template <typename TIn, int EPL, bool FULL, bool HAS_R>
+void launch_emit(const ScanArgs &a, const ScanWork &w, int64_t N, hipStream_t s) {
+  dim3 grid((unsigned)(a.B * a.H * N)), block(64);
+  if (a.k_tilde && a.kt_res)
+    hipLaunchKernelGGL((scan_emit_kernel<TIn, EPL, FULL, HAS_R, true, true>), grid, block, 0, s, a, w, N);
+  else if (a.kt_res)
+    hipLaunchKernelGGL((scan_emit_kernel<TIn, EPL, FULL, HAS_R, false, true>), grid, block, 0, s, a, w, N);
+  else
+    hipLaunchKernelGGL((scan_emit_kernel<TIn, EPL, FULL, HAS_R, true, false>), grid, block, 0, s, a, w, N);
+}
+
+template <typename TIn, int EPL, bool FULL, bool HAS_R>
+hipError_t launch_all(const ScanArgs &a, const ScanWork &w, hipStream_t s) {
+  const int64_t N = (a.T + CH - 1) / CH;
+  const int64_t nseq = a.B * a.H;
+  if (N > 0) {
+    hipLaunchKernelGGL((scan_prep_kernel<TIn, EPL, FULL, HAS_R>), dim3((unsigned)(nseq * N)), dim3(64), 0, s,
+                       a, w, N);
+  }
+  constexpr bool PF = Row<TIn, EPL, FULL>::WORDS <= 2;
+  constexpr size_t shm = solve_lds_bytes<TIn, EPL>();
+  static_assert(shm <= 160 * 1024, "solve kernel LDS");
+  auto kern = scan_solve_kernel<TIn, EPL, FULL, HAS_R, PF>;
+  hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nseq), dim3(64), shm, s, a, w, N);
+  if (N > 0) launch_emit<TIn, EPL, FULL, HAS_R>(a, w, N, s);
+  return hipGetLastError();
+}
+
+template <typename TIn, int EPL, bool FULL>
+hipError_t launch_r(const ScanArgs &a, const ScanWork &w, hipStream_t s) {
+  return a.r ? launch_all<TIn, EPL, FULL, true>(a, w, s) : launch_all<TIn, EPL, FULL, false>(a, w, s);
+}
+
+template <typename TIn>
+hipError_t launch_typed(const ScanArgs &a, const ScanWork &w, hipStream_t s) {
+  if (a.K <= 64) return a.K == 64 ? launch_r<TIn, 1, true>(a, w, s) : launch_r<TIn, 1, false>(a, w, s);
+  if (a.K <= 128) return a.K == 128 ? launch_r<TIn, 2, true>(a, w, s) : launch_r<TIn, 2, false>(a, w, s);
+  return a.K == 256 ? launch_r<TIn, 4, true>(a, w, s) : launch_r<TIn, 4, false>(a, w, s);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+size_t scan_work_bytes(int64_t B, int64_t T, int64_t H, int64_t K) {
+  const int64_t N = (T + CH - 1) / CH;
+  return 2 * align256((size_t)(B * T * H) * 4) + align256((size_t)(B * H * N * K) * 4) +
+         align256((size_t)(B * H * N) * 4) + align256((size_t)(B * H) * 3 * 4);
+}
+
+ScanWork scan_work_layout(void *base, int64_t B, int64_t T, int64_t H, int64_t K) {
+  const int64_t N = (T + CH - 1) / CH;
+  char *p = static_cast<char *>(base);
+  const size_t tok = align256((size_t)(B * T * H) * 4);
+  const size_t dst = align256((size_t)(B * H * N * K) * 4);
+  const size_t pin = align256((size_t)(B * H * N) * 4);
+  ScanWork w;
+  w.norm = reinterpret_cast<float *>(p);
+  w.cstep = reinterpret_cast<float *>(p + tok);
+  w.dstart = reinterpret_cast<float *>(p + 2 * tok);
+  w.pin = reinterpret_cast<int *>(p + 2 * tok + dst);
+  w.flags = reinterpret_cast<int *>(p + 2 * tok + dst + pin);
+  return w;
+}
+
+hipError_t launch_precond_scan_chunked(const ScanArgs &a, const ScanWork &w, bool is_bf16, hipStream_t s) {
+  if (a.B * a.H == 0) return hipSuccess;
+  return is_bf16 ? launch_typed<bf16>(a, w, s) : launch_typed<float>(a, w, s);
+}
+
+}  // namespace osdn

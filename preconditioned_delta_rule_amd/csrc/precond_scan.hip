@@ -20,86 +20,10 @@
 // a Fast2Sum.  Keys of the next group of tokens are loaded (as raw
 // bf16/f32 words) while the current group is processed; beta and r arrive as
 // one lane-indexed vector load per group and are broadcast with readlane.
-#include "device_common.h"
 #include "kernels.h"
+#include "scan_common.h"
 
 namespace osdn {
-
-template <typename TIn, int EPL> struct RowVec;
-template <> struct RowVec<bf16, 1> { typedef bf16 type; };
-template <> struct RowVec<bf16, 2> { typedef bf16x2 type; };
-template <> struct RowVec<bf16, 4> { typedef bf16x4 type; };
-template <> struct RowVec<float, 1> { typedef float type; };
-template <> struct RowVec<float, 2> { typedef floatx2 type; };
-template <> struct RowVec<float, 4> { typedef floatx4 type; };
-
-// One token row of a lane: EPL elements kept as raw 32-bit words until used,
-// so the compiler cannot hoist their conversion up to the (prefetch) load.
-template <typename TIn, int EPL, bool FULL> struct Row {
-  static constexpr int BYTES = EPL * (int)sizeof(TIn);
-  static constexpr int WORDS = BYTES < 4 ? 1 : BYTES / 4;
-  uint32_t w[WORDS];
-  __device__ __forceinline__ void load(const TIn *p, int lane, int64_t K) {
-    TIn x[EPL];
-    if constexpr (FULL) {
-      typedef typename RowVec<TIn, EPL>::type V;
-      V v = *reinterpret_cast<const V *>(p + lane * EPL);
-      if constexpr (EPL == 1) {
-        x[0] = v;
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) x[e] = v[e];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const int64_t c = (int64_t)lane * EPL + e;
-        x[e] = c < K ? p[c] : TIn(0.0f);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < WORDS; ++i) w[i] = 0;
-    __builtin_memcpy(w, x, BYTES);
-  }
-  // Values as fp32, materialised at the point of use.
-  __device__ __forceinline__ void get(float (&out)[EPL]) const {
-    uint32_t t[WORDS];
-#pragma unroll
-    for (int i = 0; i < WORDS; ++i) {
-      t[i] = w[i];
-      asm volatile("" : "+v"(t[i]));
-    }
-    TIn x[EPL];
-    __builtin_memcpy(x, t, BYTES);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) out[e] = to_f32(x[e]);
-  }
-};
-
-template <typename TIn, int EPL, bool FULL>
-__device__ __forceinline__ void store_row(TIn *p, int lane, int64_t K, const float (&x)[EPL]) {
-  if constexpr (FULL) {
-    typedef typename RowVec<TIn, EPL>::type V;
-    V v;
-    if constexpr (EPL == 1) {
-      v = from_f32<TIn>(x[0]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) v[e] = from_f32<TIn>(x[e]);
-    }
-    *reinterpret_cast<V *>(p + lane * EPL) = v;
-  } else {
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const int64_t c = (int64_t)lane * EPL + e;
-      if (c < K) p[c] = from_f32<TIn>(x[e]);
-    }
-  }
-}
-
-__device__ __forceinline__ float lane_bcast(float v, int lane) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
-}
 
 template <typename TIn, int EPL, bool FULL, bool HAS_R, bool WKT, bool WRES>
 __global__ __launch_bounds__(64) void precond_scan_kernel(ScanArgs a) {

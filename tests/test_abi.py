@@ -86,20 +86,30 @@ def test_scan_only_limits(lib):
     assert lib.osdn_validate(ctypes.byref(d)) == osdn.EUNSUPPORTED
     d.K = 300
     null = ctypes.c_void_p(None)
-    st = lib.osdn_precond_scan(ctypes.byref(d), null, null, null, null, null, null, null)
+    st = lib.osdn_precond_scan(ctypes.byref(d), null, null, null, null, null, null, null,
+                               ctypes.c_size_t(0), null)
     assert st == osdn.EUNSUPPORTED
+    assert lib.osdn_precond_scan_workspace_bytes(ctypes.byref(d)) == 0
+    assert lib.osdn_precond_scan_counters_offset(ctypes.byref(d)) == -1
 
 
 def test_null_and_misaligned_pointers_rejected_before_launch(lib):
     d = osdn.Desc()
     lib.osdn_desc_init(ctypes.byref(d), 1, 8, 1, 16, 16)
     null = ctypes.c_void_p(None)
-    st = lib.osdn_precond_scan(ctypes.byref(d), null, null, null, null, null, null, null)
+    z = ctypes.c_size_t(0)
+    st = lib.osdn_precond_scan(ctypes.byref(d), null, null, null, null, null, null, null, z, null)
     assert st == osdn.EINVAL and "k must not be NULL" in lib.osdn_last_error().decode()
     fake = ctypes.c_void_p(0x1000)
     odd = ctypes.c_void_p(0x1004)
-    st = lib.osdn_precond_scan(ctypes.byref(d), fake, odd, null, null, fake, null, null)
+    st = lib.osdn_precond_scan(ctypes.byref(d), fake, odd, null, null, fake, null, null, z, null)
     assert st == osdn.EINVAL and "aligned" in lib.osdn_last_error().decode()
+    st = lib.osdn_precond_scan(ctypes.byref(d), fake, fake, null, null, ctypes.c_void_p(0x2000),
+                               null, odd, ctypes.c_size_t(1 << 20), null)
+    assert st == osdn.EINVAL and "workspace is not" in lib.osdn_last_error().decode()
+    st = lib.osdn_precond_scan(ctypes.byref(d), fake, fake, null, null, ctypes.c_void_p(0x2000),
+                               null, ctypes.c_void_p(0x3000), ctypes.c_size_t(16), null)
+    assert st == osdn.EINVAL and "needed" in lib.osdn_last_error().decode()
     st = lib.osdn_chunk_fwd(ctypes.byref(d), fake, fake, fake, fake, fake, null, null, fake,
                             null, null)
     assert st == osdn.EINVAL and "alias" in lib.osdn_last_error().decode()
@@ -113,11 +123,24 @@ def test_null_and_misaligned_pointers_rejected_before_launch(lib):
 
 
 def test_workspace_bytes(lib):
+    # chunked phase 1 at B=4, T=4096, H=16, K=128: key norms and step scalars
+    # (fp32 per token), d at each of the 64 chunk starts, a word per chunk and
+    # three counters per (b,h), each region rounded up to 256 bytes
     d = osdn.Desc()
     lib.osdn_desc_init(ctypes.byref(d), 4, 4096, 16, 128, 128)
-    assert lib.osdn_fwd_workspace_bytes(ctypes.byref(d)) == 4 * 4096 * 16 * 128 * 2
+    tok = 4 * 4096 * 16 * 4
+    scan = 2 * tok + 4 * 16 * 64 * 128 * 4 + 4 * 16 * 64 * 4 + 256 * 3
+    assert lib.osdn_precond_scan_workspace_bytes(ctypes.byref(d)) == scan
+    assert lib.osdn_precond_scan_counters_offset(ctypes.byref(d)) == scan - 256 * 3
+    assert lib.osdn_fwd_workspace_bytes(ctypes.byref(d)) == 4 * 4096 * 16 * 128 * 2 + scan
     d.dtype = osdn.F32
-    assert lib.osdn_fwd_workspace_bytes(ctypes.byref(d)) == 4 * 4096 * 16 * 128 * 4
+    assert lib.osdn_fwd_workspace_bytes(ctypes.byref(d)) == 4 * 4096 * 16 * 128 * 4 + scan
+    # a ragged tail chunk counts as a chunk
+    d.T = 4097
+    n = 65
+    tok = -(-4 * 4097 * 16 * 4 // 256) * 256
+    scan = 2 * tok + 4 * 16 * n * 128 * 4 + -(-4 * 16 * n * 4 // 256) * 256 + 256 * 3
+    assert lib.osdn_precond_scan_workspace_bytes(ctypes.byref(d)) == scan
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):

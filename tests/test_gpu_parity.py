@@ -50,14 +50,22 @@ SCAN_CASES = {
 }
 
 
-def run_scan(inp, dtype):
+def run_scan(inp, dtype, chunked=True, counters=False):
     p = inp["params"]
     k = to_dev(inp["k"], dtype)
+    B, T, H, K = inp["k"].shape
+    code = osdn.BF16 if dtype == "bf16" else osdn.F32
+    ws = None
+    if chunked:
+        ws = torch.empty(osdn.precond_scan_workspace_bytes(B, T, H, K, code), dtype=torch.uint8,
+                         device="cuda:0")
     kt, d = osdn.precond_scan(k, to_dev(inp["beta"], "f32"), to_dev(inp["r"], "f32"),
                               to_dev(inp["d1"], "f32"), eta=p["eta"], d_min=p["d_min"],
                               d_max=p["d_max"], clamp=p["clamp"], eps=p["eps"],
-                              beta_aware=p["beta_aware"])
+                              beta_aware=p["beta_aware"], chunked=chunked, workspace=ws)
     torch.cuda.synchronize()
+    if counters:
+        return to_np(kt), to_np(d), osdn.scan_counters(ws, B, T, H, K, code).numpy()
     return to_np(kt), to_np(d)
 
 
@@ -68,16 +76,17 @@ def oracle_scan(inp):
                                eps=p["eps"], beta_aware=p["beta_aware"])
 
 
+@pytest.mark.parametrize("chunked", [False, True], ids=["sequential", "chunked"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("case", sorted(SCAN_CASES))
-def test_scan_parity(case, dtype):
+def test_scan_parity(case, dtype, chunked):
     spec = SCAN_CASES[case]
     if isinstance(spec, str):
         spec = dict(WORKLOADS[spec])
     inp = make_inputs(dict(spec, dtype=dtype))
     if case == "zero_keys":
         inp["k"][:, ::7] = 0.0
-    kt, d = run_scan(inp, dtype)
+    kt, d = run_scan(inp, dtype, chunked)
     kt_ref, d_ref = oracle_scan(inp)
     assert rel_err(d, d_ref) <= F32_D, case
     if dtype == "f32":
@@ -88,6 +97,52 @@ def test_scan_parity(case, dtype):
         assert np.any(d_ref == 2.0)       # the upper bound is reached
     if case == "apf_interior":
         assert np.any((d_ref > 0.5) & (d_ref < 2.0))
+
+
+# Chunked phase 1: which path each 64-token chunk takes (counters per (b,h):
+# pinned on d_min, closed form with a fixed active set, token by token).
+PATH_CASES = {
+    # no retention, keys spread over all coordinates: d stays inside the box
+    "free": (dict(B=2, T=700, H=2, K=128, V=128, dtype="bf16", seed=31), "active"),
+    # retention pulls every coordinate onto d_min within the first chunk
+    "pinned": (dict(B=2, T=700, H=2, K=128, V=128, dtype="bf16", seed=32, apf=True), "pinned"),
+    # retention 0.99 with sparse keys: coordinates split between d_min and the
+    # interior, a fixed active set most of the time
+    "mixed": (dict(B=1, T=1000, H=2, K=64, V=64, dtype="f32", seed=33, keys="sparse",
+                   apf_const=0.99, eta=0.05), "any"),
+    # one-hot keys, a coordinate drawn often climbs to d_max and stays there
+    "upper": (dict(B=1, T=900, H=2, K=16, V=16, dtype="f32", seed=34, keys="onehot",
+                   onehot_bias=0.6, eta=0.05, beta_mu=-1.5), "any"),
+    # a large step crosses the bounds often: many chunks swept token by token
+    "crossing": (dict(B=1, T=400, H=1, K=16, V=16, dtype="f32", seed=35, keys="onehot",
+                      eta=0.9), "seq"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(PATH_CASES))
+def test_scan_chunk_paths(case):
+    spec, expect = PATH_CASES[case]
+    inp = make_inputs(spec)
+    dtype = spec["dtype"]
+    kt, d, cnt = run_scan(inp, dtype, chunked=True, counters=True)
+    kt_ref, d_ref = oracle_scan(inp)
+    B, T, H, K = inp["k"].shape
+    N = -(-T // 64)
+    print(case, "counters [pinned, active, seq] per (b,h):", cnt.reshape(-1, 3).tolist())
+    assert np.all(cnt.sum(-1) == N)
+    assert rel_err(d, d_ref) <= F32_D
+    if dtype == "f32":
+        assert rel_err(kt, kt_ref) <= F32_KT
+    else:
+        assert ulp_err(kt, kt_ref) <= 1.0
+    if expect == "active":
+        assert np.all(cnt[..., 1] == N)
+    elif expect == "pinned":
+        assert np.all(cnt[..., 0] >= N - 2)
+    elif expect == "seq":
+        assert np.all(cnt[..., 2] >= 1)
+    if case == "upper":
+        assert np.any(d_ref == 2.0)
 
 
 CHUNK_CASES = {
@@ -198,12 +253,18 @@ def test_fwd_full_size_sampled(name):
         assert es <= BF16_OS, (name, b, h, es)
 
 
-def test_fwd_full_size_write_keys():
-    """At the 1.3B-shaped workload the emitted write keys are within one bf16
-    ulp of the fp64 values, on sampled sequences."""
-    inp = make_inputs("1p3b_apf")
-    kt, d = run_scan(inp, "bf16")
-    pairs = [(0, 0), (2, 7), (3, 15)]
+@pytest.mark.parametrize("name,path", [("1p3b_apf", 0), ("340m", 1), ("recall", 1)])
+def test_scan_full_size_write_keys(name, path):
+    """At full size the emitted write keys are within one bf16 ulp of the fp64
+    values, on sampled sequences, and the chunked sweep takes its fast path
+    (pinned with retention, closed form without) on all but the first chunks."""
+    inp = make_inputs(name)
+    kt, d, cnt = run_scan(inp, "bf16", chunked=True, counters=True)
+    B, T, H, K = inp["k"].shape
+    N = -(-T // 64)
+    print(name, "chunks per path, summed over (b,h):", cnt.reshape(-1, 3).sum(0).tolist())
+    assert np.all(cnt[..., path] >= N - 2)
+    pairs = [(0, 0), (B // 2, H // 2), (B - 1, H - 1)]
     sub = sample_sequences(inp, pairs)
     kt_ref, d_ref = oracle_scan(sub)
     for i, (b, h) in enumerate(pairs):
