@@ -37,8 +37,9 @@ hipError_t launch_precond_scan(const ScanArgs &a, bool bf16, hipStream_t s);
 
 // Chunked phase 1 (prep / solve / emit kernels).  Workspace: per-token key
 // norm and step scalar c (fp32 [B,T,H] each), d at every 64-token chunk start
-// (fp32 [B,H,N,K]), one word per chunk that says whether the chunk keeps a d
-// that sits on d_min there (int [B,H,N]), and three counters per (b,h) (int
+// (fp32 [B,H,N,K]), one word per chunk (int [B,H,N]: 1 when the chunk keeps
+// a d that sits on d_min there, rewritten to 2 when the sweep took it so, in
+// which case its d start is not stored), and three counters per (b,h) (int
 // [B,H,3]: chunks taken on the pinned, closed-form and token-by-token paths).
 struct ScanWork {
   float *norm, *cstep, *dstart;

@@ -12,8 +12,10 @@
 //        (then <d, s_t> = d_min |k_t|^2); the chunk is marked when
 //        r_t d_min + c_t max_i s_{t,i} <= d_min holds for all its tokens.
 //  solve (one wave per (b,h), chunks in order): c_t for every token and d at
-//        each chunk start.  A chunk that starts with d on d_min everywhere
-//        and is marked needs no work.  Otherwise, Section 4.2 notes that away
+//        each chunk start.  A run of marked chunks that starts with d on
+//        d_min everywhere needs no work (one step skips the whole run; its
+//        chunks are re-marked so that emit starts them from d_min).
+//        Otherwise, Section 4.2 notes that away
 //        from the box the update is affine in d.  Suppose the coordinates on a
 //        bound at the chunk start stay there and the others never reach one
 //        (a fixed active set).  Then, with R_t = prod_{l<t} r_l, a free
@@ -148,18 +150,17 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
   float nbt = 0.0f, nrt = 1.0f, nnrm = 1.0f;
   bool have = false;  // chunk n's rows already sit in sR, its scalars in nbt/nrt/nnrm
 
-  for (int64_t n = 0; n < N; ++n) {
+  // every pass of the loop advances n by step >= 1 (a pinned run sets it)
+  for (int64_t n = 0, step = 1; n < N; n += step) {
+    step = 1;
     const int64_t t0 = n * CH;
     const int L = (int)((T - t0) < CH ? (T - t0) : CH);
     const bool tok = lane < L;  // lane u <-> token t0 + u
     const int64_t gi = (b * T + t0 + (tok ? lane : 0)) * H + h;
     if ((n & 63) == 0) {
       const int p = n + lane < N ? wk.pin[seq * N + n + lane] : 0;
-      pinmask = __ballot(p != 0);
+      pinmask = __ballot(p == 1);
     }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e)
-      if (valid[e]) wk.dstart[(seq * N + n) * K + lane * EPL + e] = d[e];
 
     // where d sits: on d_min, on d_max, inside
     bool onlo[EPL], onhi[EPL], fr[EPL];
@@ -174,12 +175,23 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
       free_ |= fr[e];
     }
     const bool any_lo = __any(lo) != 0, any_hi = __any(hi) != 0, any_free = __any(free_) != 0;
-    if (!any_free && !any_hi && ((pinmask >> (n & 63)) & 1)) {
-      // pinned chunk: d stays on d_min, c_t was written by the prep pass
-      ++n_pinned;
-      have = false;
-      continue;
+    if (!any_free && !any_hi) {
+      // d on d_min everywhere: it stays there through the run of marked
+      // chunks that starts here (c_t of those was written by the prep pass);
+      // the run is marked 2 so that the emit pass starts it from d_min
+      const uint64_t m = ~(pinmask >> (n & 63));
+      const int run = m ? (int)__builtin_ctzll(m) : 64;
+      if (run > 0) {
+        if (lane < run) wk.pin[seq * N + n + lane] = 2;
+        n_pinned += run;
+        step = run;
+        have = false;
+        continue;
+      }
     }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      if (valid[e]) wk.dstart[(seq * N + n) * K + lane * EPL + e] = d[e];
 
     // this chunk's key rows and scalars
     const TIn *kp = static_cast<const TIn *>(a.k) + ((b * T + t0) * H + h) * K;
@@ -192,13 +204,14 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
       bt = a.beta[gi];
       rt = HAS_R ? a.r[gi] : 1.0f;
       nrm = wk.norm[gi];
+      constexpr int GL = CH / Row<TIn, EPL, FULL>::WORDS;  // rows per load batch (<= 64 words)
 #pragma unroll
-      for (int u0 = 0; u0 < CH; u0 += 16) {
-        Row<TIn, EPL, FULL> tmp[16];
+      for (int u0 = 0; u0 < CH; u0 += GL) {
+        Row<TIn, EPL, FULL> tmp[GL];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) tmp[u].load(kp + (u0 + u < L ? u0 + u : L - 1) * stride, lane, K);
+        for (int u = 0; u < GL; ++u) tmp[u].load(kp + (u0 + u < L ? u0 + u : L - 1) * stride, lane, K);
 #pragma unroll
-        for (int u = 0; u < 16; ++u) lds_put<TIn, EPL, FULL>(sR + (u0 + u) * RP + lane * EPL, tmp[u]);
+        for (int u = 0; u < GL; ++u) lds_put<TIn, EPL, FULL>(sR + (u0 + u) * RP + lane * EPL, tmp[u]);
       }
     }
     if (!tok) {
@@ -228,8 +241,29 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
     bool done = false;
     __syncthreads();
 
+    // retention products R_t = prod_{l<t} r_l (log-space scan): Rn = R_{t+1},
+    // Rt = R_t.  The bound on free coordinates below needs R_t non-increasing,
+    // and R_L >= 1/4 keeps the 1/R_t factors from costing more than two bits;
+    // otherwise a chunk with free coordinates goes token by token.
+    float Rn = 1.0f, Rt = 1.0f;
+    bool try_closed = true;
+    if constexpr (HAS_R) {
+      if (any_free) {
+        const float lr = logf(rt);
+        float lin = lr;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float y = __shfl_up(lin, off, 64);
+          if (lane >= off) lin += y;
+        }
+        Rn = __expf(lin);
+        Rt = __expf(lin - lr);
+        try_closed = lane_bcast(Rn, L - 1) >= 0.25f && __all(rt <= 1.0f) != 0;
+      }
+    }
+
     // ---- fixed active set, closed form
-    {
+    if (try_closed) {
       float pvF[CH], pvP[HAS_R ? CH : 1];
 #pragma unroll
       for (int u = 0; u < CH; ++u) {
@@ -271,24 +305,11 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
           }
         __syncthreads();
       }
-      float x = 0.0f, Rn = 1.0f;
+      float x = 0.0f;
       if (!any_free) {
         // every coordinate on a bound: <d, s_t> = <d_0, s_t>
         if (tok) cst = fmaf(-eb, p0P + p0F, ea);
       } else {
-        // retention products: Rn = R_{t+1}, Rt = R_t (log-space scan)
-        float Rt = 1.0f;
-        if constexpr (HAS_R) {
-          const float lr = logf(rt);
-          float lin = lr;
-#pragma unroll
-          for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(lin, off, 64);
-            if (lane >= off) lin += y;
-          }
-          Rn = __expf(lin);
-          Rt = __expf(lin - lr);
-        }
         // x_t + g_t sum_{j<t} G_jt x_j = ea_t / R_{t+1} - g_t (p0P_t / R_t + p0F_t),
         // g_t = eb_t R_t / R_{t+1}
         const float g = HAS_R ? eb * (Rt / Rn) : eb;
@@ -334,11 +355,8 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
           }
         }
       }
-      // the bound on free coordinates needs R_t non-increasing; R_L >= 1/4
-      // keeps the 1/R_t factors from costing more than two bits
       const float RL = lane_bcast(Rn, L - 1);
       bool ok = true;
-      if (HAS_R && any_free) ok = RL >= 0.25f && rt <= 1.0f;
       float dn[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
@@ -403,6 +421,84 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
 }
 
 // ---------------------------------------------------------------- emit
+template <typename T, int EPL>
+__device__ __forceinline__ typename RowVec<T, EPL>::type pack_row(const float (&x)[EPL]) {
+  typename RowVec<T, EPL>::type v;
+  if constexpr (EPL == 1) {
+    v = from_f32<T>(x[0]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) v[e] = from_f32<T>(x[e]);
+  }
+  return v;
+}
+
+template <typename T, int EPL, bool FULL>
+__device__ __forceinline__ void store_vec(T *p, int lane, int64_t K, const typename RowVec<T, EPL>::type &v) {
+  if constexpr (FULL) {
+    *reinterpret_cast<typename RowVec<T, EPL>::type *>(p + lane * EPL) = v;
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int64_t c = (int64_t)lane * EPL + e;
+      if constexpr (EPL == 1) {
+        if (c < K) p[c] = v;
+      } else {
+        if (c < K) p[c] = v[e];
+      }
+    }
+  }
+}
+
+// Rows of one chunk: the write keys of a group of rows are computed into
+// registers and then stored together, so that the stores never sit in the
+// memory counter ahead of row loads that are still awaited.
+template <typename TIn, int EPL, bool FULL, bool WKT, bool WRES, bool WHOLE>
+__device__ __forceinline__ void emit_rows(const Row<TIn, EPL, FULL> (&rows)[CH], float (&d)[EPL], float cv, float rv,
+                                          float lo, float hi, int L, TIn *op, bf16 *rp, int64_t stride, int lane,
+                                          int64_t K) {
+  typedef typename RowVec<TIn, EPL>::type VK;
+  typedef typename RowVec<bf16, EPL>::type VR;
+  constexpr int OUTW = (WKT ? (int)sizeof(VK) : 0) + (WRES ? (int)sizeof(VR) : 0);
+  constexpr int G = OUTW * CH <= 512 ? CH : 16;  // rows per store group (<= 128 words held)
+#pragma unroll
+  for (int g = 0; g < CH; g += G) {
+    VK okt[WKT ? G : 1];
+    VR ores[WRES ? G : 1];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int u = g + i;
+      if (WHOLE || u < L) {
+        float k[EPL];
+        rows[u].get(k);
+        if constexpr (WKT) {
+          float w[EPL];
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) w[e] = d[e] * k[e];
+          okt[i] = pack_row<TIn, EPL>(w);
+        }
+        if constexpr (WRES) {
+          float w[EPL];
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) w[e] = (d[e] - 1.0f) * k[e];  // d - 1 is exact on [0.5, 2]
+          ores[i] = pack_row<bf16, EPL>(w);
+        }
+        const float c = lane_bcast(cv, u), r = lane_bcast(rv, u);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) d[e] = fminf(fmaxf(fmaf(c, k[e] * k[e], r * d[e]), lo), hi);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int u = g + i;
+      if (WHOLE || u < L) {
+        if constexpr (WKT) store_vec<TIn, EPL, FULL>(op + u * stride, lane, K, okt[i]);
+        if constexpr (WRES) store_vec<bf16, EPL, FULL>(rp + u * stride, lane, K, ores[i]);
+      }
+    }
+  }
+}
+
 template <typename TIn, int EPL, bool FULL, bool HAS_R, bool WKT, bool WRES>
 __global__ __launch_bounds__(64) void scan_emit_kernel(ScanArgs a, ScanWork wk, int64_t N) {
   const int lane = threadIdx.x;
@@ -413,49 +509,36 @@ __global__ __launch_bounds__(64) void scan_emit_kernel(ScanArgs a, ScanWork wk, 
   const int L = (int)((T - t0) < CH ? (T - t0) : CH);
   const int64_t stride = H * K;
   const int64_t row0 = ((b * T + t0) * H + h) * K;
-  const TIn *kp = static_cast<const TIn *>(a.k) + row0;
-  Row<TIn, EPL, FULL> rows[CH];
-#pragma unroll
-  for (int u = 0; u < CH; ++u) rows[u].load(kp + (u < L ? u : L - 1) * stride, lane, K);
+  // per-token scalars and the chunk-start d are loaded before the rows, so
+  // waiting for them does not wait for the rows
   const int64_t gi = (b * T + t0 + (lane < L ? lane : 0)) * H + h;
   const float cv = wk.cstep[gi];
   const float rv = HAS_R ? a.r[gi] : 1.0f;
-  const float dmin = a.d_min, dmax = a.d_max;
-  const bool clamp = a.clamp != 0;
+  // a chunk the solve pass took as pinned (marked 2) starts from d_min and
+  // has no stored start
+  const bool pinned = wk.pin[seq * N + n] == 2;
   float d[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     const int64_t c = (int64_t)lane * EPL + e;
     d[e] = c < K ? wk.dstart[(seq * N + n) * K + c] : 0.0f;
   }
+  const TIn *kp = static_cast<const TIn *>(a.k) + row0;
+  Row<TIn, EPL, FULL> rows[CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u) rows[u].load(kp + (u < L ? u : L - 1) * stride, lane, K);
+  if (pinned) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) d[e] = a.d_min;
+  }
+  // without the box, clip to (-inf, inf) is the identity
+  const float lo = a.clamp ? a.d_min : -INFINITY, hi = a.clamp ? a.d_max : INFINITY;
   TIn *op = WKT ? static_cast<TIn *>(a.k_tilde) + row0 : nullptr;
   bf16 *rp = WRES ? static_cast<bf16 *>(a.kt_res) + row0 : nullptr;
-#pragma unroll
-  for (int u = 0; u < CH; ++u) {
-    if (u < L) {
-      float k[EPL];
-      rows[u].get(k);
-      if constexpr (WKT) {
-        float w[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) w[e] = d[e] * k[e];
-        store_row<TIn, EPL, FULL>(op + u * stride, lane, K, w);
-      }
-      if constexpr (WRES) {
-        float w[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) w[e] = (d[e] - 1.0f) * k[e];  // d - 1 is exact on [0.5, 2]
-        store_row<bf16, EPL, FULL>(rp + u * stride, lane, K, w);
-      }
-      const float c = lane_bcast(cv, u), r = lane_bcast(rv, u);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        float x = fmaf(c, k[e] * k[e], r * d[e]);
-        if (clamp) x = fminf(fmaxf(x, dmin), dmax);
-        d[e] = x;
-      }
-    }
-  }
+  if (L == CH)
+    emit_rows<TIn, EPL, FULL, WKT, WRES, true>(rows, d, cv, rv, lo, hi, L, op, rp, stride, lane, K);
+  else
+    emit_rows<TIn, EPL, FULL, WKT, WRES, false>(rows, d, cv, rv, lo, hi, L, op, rp, stride, lane, K);
 }
 
 template <typename TIn, int EPL, bool FULL, bool HAS_R>
