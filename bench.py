@@ -120,6 +120,9 @@ def main(argv=None):
                          sws=torch.empty(osdn.precond_scan_workspace_bytes(B, T, H, K, dtype=(
                              osdn.BF16 if p["dtype"] == "bf16" else osdn.F32)),
                              dtype=torch.uint8, device=dev),
+                         cws=torch.empty(max(1, osdn.chunk_fwd_workspace_bytes(
+                             B, T, H, K, V, dtype=(osdn.BF16 if p["dtype"] == "bf16" else osdn.F32),
+                             chunk=C)), dtype=torch.uint8, device=dev),
                          S=torch.empty((B, H, V, K), dtype=torch.float32, device=dev),
                          d=torch.empty((B, H, K), dtype=torch.float32, device=dev)))
     kw = dict(chunk=C, eta=p["eta"], d_min=p["d_min"], d_max=p["d_max"], clamp=p["clamp"],
@@ -143,7 +146,7 @@ def main(argv=None):
     def chunk(i):
         s = sets[i % len(sets)]
         osdn.chunk_fwd(s["q"], s["k"], s["kt"], s["v"], s["beta"], s["alpha"], None, chunk=C,
-                       q_scale=p["q_scale"], o=s["o"], S_out=s["S"])
+                       q_scale=p["q_scale"], o=s["o"], S_out=s["S"], workspace=s["cws"])
 
     def timed(fn, n):
         """Average device time of fn over n launches on the current stream

@@ -144,16 +144,26 @@ int64_t osdn_precond_scan_counters_offset(const osdn_desc *desc);
  *   S0      [B,H,V,K] f32            initial state, or NULL for zeros
  *   o       [B,T,H,V] dtype          OUT: o_t = S_t (q_scale q_t)
  *   S_out   [B,H,V,K] f32            OUT: S_T, or NULL (may alias S0)
+ *   workspace                        NULL, or >= osdn_chunk_fwd_workspace_bytes
+ *                                    (desc) bytes, 16-byte aligned (see below)
  */
 osdn_status osdn_chunk_fwd(const osdn_desc *desc, const void *q,
                            const void *k, const void *k_tilde, const void *v,
                            const float *beta, const float *alpha,
                            const float *S0, void *o, float *S_out,
+                           void *workspace, size_t workspace_bytes,
                            void *stream);
 
+/* Bytes of the optional phase-2 workspace: nonzero only for the matrix-core
+ * shapes (bf16, K = V = 128, chunk 64), where a workspace lets the (I + A)^-1
+ * of every chunk be formed chunk-parallel before the sweep over chunks (a
+ * bf16 64 x 64 block per chunk); without one a single kernel forms it inside
+ * the sweep.  Same result up to fp32 rounding.  0 on an invalid descriptor. */
+size_t osdn_chunk_fwd_workspace_bytes(const osdn_desc *desc);
+
 /* Bytes of device workspace osdn_fwd needs (the write keys between the
- * phases, B*T*H*K elements of dtype, followed by a chunked phase-1
- * workspace); 0 on an invalid descriptor. */
+ * phases, B*T*H*K elements of dtype, followed by a chunked phase-1 workspace
+ * and a phase-2 workspace); 0 on an invalid descriptor. */
 size_t osdn_fwd_workspace_bytes(const osdn_desc *desc);
 
 /*
@@ -162,8 +172,10 @@ size_t osdn_fwd_workspace_bytes(const osdn_desc *desc);
  * the write keys d_t (.) k_t.  workspace (>= osdn_fwd_workspace_bytes(desc)
  * bytes, 16-byte aligned, required when T > 0) carries the write keys from
  * phase 1 to phase 2 and holds the chunked phase-1 scratch (its counters at
- * osdn_fwd_workspace_bytes(desc) - osdn_precond_scan_workspace_bytes(desc) +
- * osdn_precond_scan_counters_offset(desc)).  For bf16 the workspace holds the
+ * osdn_fwd_workspace_bytes(desc) - osdn_chunk_fwd_workspace_bytes(desc) -
+ * osdn_precond_scan_workspace_bytes(desc) +
+ * osdn_precond_scan_counters_offset(desc)) and the phase-2 scratch.  For bf16
+ * the workspace holds the
  * residual (d_t - 1) (.) k_t rather
  * than k~_t, so phase 2 sees the write keys to about 16 significant bits
  * instead of bf16's 8: the result is then closer to the exact forward than

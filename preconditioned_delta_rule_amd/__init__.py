@@ -20,7 +20,7 @@ import os
 import torch
 
 __all__ = ["precond_scan", "precond_scan_workspace_bytes", "scan_counters", "chunk_fwd",
-           "fwd", "fwd_workspace_bytes", "fwd_scan_counters", "Desc", "OsdnError",
+           "chunk_fwd_workspace_bytes", "fwd", "fwd_workspace_bytes", "fwd_scan_counters", "Desc", "OsdnError",
            "library_path", "load", "F32", "BF16"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -32,7 +32,8 @@ OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 
 SYMBOLS = ("osdn_desc_init", "osdn_validate", "osdn_precond_scan",
            "osdn_precond_scan_workspace_bytes", "osdn_precond_scan_counters_offset",
-           "osdn_chunk_fwd", "osdn_fwd_workspace_bytes", "osdn_fwd", "osdn_status_str",
+           "osdn_chunk_fwd", "osdn_chunk_fwd_workspace_bytes", "osdn_fwd_workspace_bytes",
+           "osdn_fwd", "osdn_status_str",
            "osdn_last_error", "osdn_version")
 
 
@@ -73,7 +74,9 @@ def load():
     lib.osdn_precond_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.osdn_precond_scan_counters_offset.argtypes = [dp]
     lib.osdn_precond_scan_counters_offset.restype = ctypes.c_int64
-    lib.osdn_chunk_fwd.argtypes = [dp, vp, vp, vp, vp, fp, fp, fp, vp, fp, vp]
+    lib.osdn_chunk_fwd.argtypes = [dp, vp, vp, vp, vp, fp, fp, fp, vp, fp, vp, ctypes.c_size_t, vp]
+    lib.osdn_chunk_fwd_workspace_bytes.argtypes = [dp]
+    lib.osdn_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.osdn_fwd_workspace_bytes.argtypes = [dp]
     lib.osdn_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.osdn_fwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp, vp,
@@ -203,10 +206,18 @@ def precond_scan(k, beta, r=None, d1=None, *, eta=0.003, d_min=0.5, d_max=2.0,
     return k_tilde, d_out
 
 
+def chunk_fwd_workspace_bytes(B, T, H, K, V, dtype=BF16, chunk=64) -> int:
+    desc = make_desc(B, T, H, K, V, dtype=dtype, chunk=chunk)
+    return int(load().osdn_chunk_fwd_workspace_bytes(ctypes.byref(desc)))
+
+
 def chunk_fwd(q, k, k_tilde, v, beta, alpha=None, S0=None, *, chunk=64, q_scale=1.0,
-              o=None, S_out=None):
+              o=None, S_out=None, two_pass=True, workspace=None):
     """Phase 2.  q, k, k_tilde [B,T,H,K], v [B,T,H,V] (one dtype), beta and
-    alpha [B,T,H] f32, S0 [B,H,V,K] f32.  Returns (o [B,T,H,V], S_out [B,H,V,K])."""
+    alpha [B,T,H] f32, S0 [B,H,V,K] f32.  two_pass=True hands the library a
+    workspace (allocated when None) so that the matrix-core shapes form every
+    chunk's (I + A)^-1 chunk-parallel first; two_pass=False passes none.
+    Returns (o [B,T,H,V], S_out [B,H,V,K])."""
     B, T, H, K = q.shape
     V = v.shape[-1]
     dev, dt, f32 = q.device, q.dtype, torch.float32
@@ -223,8 +234,11 @@ def chunk_fwd(q, k, k_tilde, v, beta, alpha=None, S0=None, *, chunk=64, q_scale=
     _need(o, "o", (B, T, H, V), dt, dev)
     _need(S_out, "S_out", (B, H, V, K), f32, dev)
     desc = make_desc(B, T, H, K, V, dtype=_dtype_code(q), chunk=chunk, q_scale=q_scale)
+    need = int(load().osdn_chunk_fwd_workspace_bytes(ctypes.byref(desc))) if two_pass else 0
+    workspace = _workspace(workspace, need, dev) if need else None
     _check(load().osdn_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(k_tilde), _ptr(v),
                                  _ptr(beta), _ptr(alpha), _ptr(S0), _ptr(o), _ptr(S_out),
+                                 _ptr(workspace), ctypes.c_size_t(_nbytes(workspace)),
                                  _stream(dev)))
     return o, S_out
 
@@ -236,8 +250,9 @@ def fwd_workspace_bytes(B, T, H, K, V, dtype=BF16, chunk=64) -> int:
 
 def fwd_scan_counters(workspace, B, T, H, K, V, dtype=BF16, chunk=64):
     """The phase-1 chunk counters (see scan_counters) inside an osdn_fwd workspace."""
-    off = fwd_workspace_bytes(B, T, H, K, V, dtype, chunk) - precond_scan_workspace_bytes(
-        B, T, H, K, dtype)
+    off = (fwd_workspace_bytes(B, T, H, K, V, dtype, chunk)
+           - chunk_fwd_workspace_bytes(B, T, H, K, V, dtype, chunk)
+           - precond_scan_workspace_bytes(B, T, H, K, dtype))
     return scan_counters(workspace, B, T, H, K, dtype, offset=off)
 
 

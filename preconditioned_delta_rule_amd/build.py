@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libosdn.so")
 
-SOURCES = ["precond_scan.hip", "precond_chunked.hip", "chunk_generic.hip", "chunk_mfma.hip", "osdn_api.cpp"]
+SOURCES = ["precond_scan.hip", "precond_chunked.hip", "chunk_generic.hip", "chunk_mfma.hip",
+           "chunk_wy.hip", "osdn_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -27,8 +27,8 @@
 // the same XCD so their shared K/K~/Q reads hit that XCD's L2.  Inside the
 // workgroup wave w owns tokens [16w, 16w+16) of the chunk; its K and Q rows go
 // straight from global memory into registers in MFMA operand layout.
-#include "device_common.h"
 #include "kernels.h"
+#include "mfma_common.h"
 
 namespace osdn {
 
@@ -41,32 +41,6 @@ constexpr int KP = KD + 8; // LDS pitch (bf16) of 128-wide rows
 constexpr int CP = C + 8;  // LDS pitch (bf16) of 64-wide rows
 constexpr int AP = C + 4;  // LDS pitch (f32) of the Gram
 constexpr int NTHREADS = 256;
-
-__device__ __forceinline__ floatx4 mfma32(bf16x8 a, bf16x8 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ floatx4 mfma16(bf16x4 a, bf16x4 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 ld8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
-__device__ __forceinline__ bf16x4 ld4(const bf16 *p) { return *reinterpret_cast<const bf16x4 *>(p); }
-
-__device__ __forceinline__ bf16x4 pack4(floatx4 v) {
-  bf16x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = to_bf16(v[i]);
-  return r;
-}
-
-// x = hi + lo with hi = bf16(x), lo = bf16(x - hi)
-__device__ __forceinline__ void split4(floatx4 v, bf16x4 &hi, bf16x4 &lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    hi[i] = to_bf16(v[i]);
-    lo[i] = to_bf16(v[i] - to_f32(hi[i]));
-  }
-}
 
 // LDS layout (bytes).  Buffers that are never live at the same time share
 // the SX region: the bf16 state pair (written after the state update, read by

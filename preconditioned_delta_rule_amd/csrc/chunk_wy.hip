@@ -1,0 +1,658 @@
+// Phase 2 of OSDN on the matrix cores, two kernels: the state-independent UT
+// transform of every chunk first, chunk-parallel, then the sweep over chunks
+// that carries the state.  bf16 operands, fp32 accumulation, K = V = 128,
+// chunk C = 64.
+//
+// Paper: Section 4.3 Eq.(5)-(6) (write key K~ in the chunk Gram and in the
+// intra-chunk score, physical key K in the residual), Appendix A.2
+// Eqs.(8)-(11); with a decay alpha, Appendix B.1 Eqs.(13)-(15).  Per chunk,
+// with B = diag(beta) and in-chunk log decay g_i = sum_{l<=i} log alpha_l
+// (g = 0 without decay):
+//
+//  chunk_tinv_kernel (one workgroup per chunk, all chunks at once):
+//    A  = strict_lower(B [e^{g_i-g_j}] . K K~^T)
+//    Tm = (I + A)^-1, written to the workspace in bf16 (row-major 64 x 64)
+//
+//  chunk_seq_kernel (one workgroup per (b,h) and 32 value rows, chunks in
+//  order; S is the boundary state, V x K, fp32):
+//    R     = B (V - diag(e^g) K S^T)
+//    Delta = Tm R                                     (= U - W S^T of Eq.(11))
+//    O     = q_scale (diag(e^g) Q S^T + lower([e^{g_i-g_j}] . Q K~^T) Delta)
+//    S    <- e^{g_L} S + Delta^T (e^{g_L - g} . K~)
+//
+// Tm depends only on the chunk's keys, so the sweep carries no triangular
+// solve: its per-chunk work is five small products, split over 8 waves (wave
+// (rw, cw) owns token rows [16 rw, 16 rw + 16) and value columns
+// [16 cw, 16 cw + 16) of the chunk), with four barriers per chunk.
+//
+// Precision as in the single-kernel form: intermediates that are not bf16
+// (S, R, Delta, the scores, and k~ = k + residual) enter every product as a
+// hi + lo pair of bf16; Tm and the output are the only 8-bit roundings.
+#include "kernels.h"
+#include "mfma_common.h"
+
+namespace osdn {
+
+namespace {
+
+constexpr int C = 64;      // chunk length
+constexpr int KD = 128;    // key dim
+constexpr int VD = 128;    // value dim
+constexpr int VT = 32;     // value rows per sweep workgroup
+constexpr int NT = VD / VT;
+constexpr int KP = KD + 8; // LDS pitch (bf16) of 128-wide rows
+constexpr int CP = C + 8;  // LDS pitch (bf16) of 64-wide rows
+constexpr int AP = C + 4;  // LDS pitch (f32) of the Gram
+
+// ============================================================ UT transform
+struct TinvLay {
+  // the key rows are dead once the Gram is formed; the inverse reuses them
+  static constexpr int KH = 0;                   // bf16 [C][KP] write keys (hi)
+  static constexpr int KL = KH + C * KP * 2;     // bf16 [C][KP] write keys (lo)
+  static constexpr int TR = 0;                   // bf16 [C][CP] Tm row-major
+  static constexpr int TC = TR + C * CP * 2;     // bf16 [C][CP] Tm column-major
+  static constexpr int X = TC + C * CP * 2;      // bf16 [C][CP] merge scratch
+  static constexpr int R0 = KL + C * KP * 2;
+  static constexpr int A = R0;                   // f32 [C][AP]
+  static constexpr int BETA = A + C * AP * 4;    // f32 [C]
+  static constexpr int G = BETA + C * 4;         // f32 [C]
+  static constexpr int TOTAL = G + C * 4;
+  static_assert(X + C * CP * 2 <= R0, "inverse scratch must fit in the key rows");
+};
+
+template <bool GATED, bool KRES>
+__global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout, int64_t N) {
+  typedef TinvLay L;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
+  bf16(*sKh)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::KH);
+  bf16(*sKl)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::KL);
+  bf16(*sTr)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::TR);
+  bf16(*sTc)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::TC);
+  bf16(*sX)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::X);
+  float(*sA)[AP] = reinterpret_cast<float(*)[AP]>(smem + L::A);
+  float *sBeta = reinterpret_cast<float *>(smem + L::BETA);
+  float *sG = reinterpret_cast<float *>(smem + L::G);
+
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = l & 15, lq = l >> 4;
+  const int64_t seq = blockIdx.x / N, n = blockIdx.x % N;
+  const int64_t H = a.H, T = a.T;
+  const int64_t b = seq / H, h = seq - b * H;
+  const int64_t t0 = n * C;
+  const int Lc = (int)((T - t0) < C ? (T - t0) : C);
+  const bf16 *gk = static_cast<const bf16 *>(a.k);
+  const bf16 *gkt = static_cast<const bf16 *>(a.kt);
+  const int64_t tstride = H * KD;
+  const int64_t base = (b * T + t0) * tstride + h * KD;  // token t0 of this (b,h)
+
+  // write keys into LDS as a hi + lo pair: thread -> token l, columns [32 w, 32 w + 32)
+  {
+    const bool ok = l < Lc;
+    const int64_t off = base + (ok ? l : 0) * tstride + 32 * w;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      bf16x8 x = ld8(gkt + off + 8 * p);
+      x = ok ? x : bf16x8{};
+      if constexpr (KRES) {
+        bf16x8 y = ld8(gk + off + 8 * p);
+        y = ok ? y : bf16x8{};
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = to_f32(y[e]) + to_f32(x[e]);  // k~ = k + residual, exact in fp32
+          hi[e] = to_bf16(v);
+          lo[e] = to_bf16(v - to_f32(hi[e]));
+        }
+        *reinterpret_cast<bf16x8 *>(&sKh[l][32 * w + 8 * p]) = hi;
+        *reinterpret_cast<bf16x8 *>(&sKl[l][32 * w + 8 * p]) = lo;
+      } else {
+        *reinterpret_cast<bf16x8 *>(&sKh[l][32 * w + 8 * p]) = x;
+      }
+    }
+  }
+  // wave w's key rows as A operands (token 16 w + l16)
+  bf16x8 kf[4];
+  {
+    const int m = 16 * w + l16;
+    const bool ok = m < Lc;
+    const int64_t off = base + (ok ? m : 0) * tstride + 8 * lq;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 x = ld8(gk + off + 32 * kk);
+      kf[kk] = ok ? x : bf16x8{};
+    }
+  }
+  if (w == 0) {
+    const bool ok = l < Lc;
+    const int64_t gi = (b * T + t0 + (ok ? l : 0)) * H + h;
+    const float bt = a.beta[gi];
+    sBeta[l] = ok ? bt : 0.0f;
+    if constexpr (GATED) {
+      const float al = a.alpha[gi];
+      float x = ok ? logf(al) : 0.0f;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (l >= off) x += y;
+      }
+      sG[l] = x;
+    }
+  }
+  __syncthreads();
+
+  // Gram tiles (w, tj), tj <= w
+  const int m0 = 16 * w;
+  floatx4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int ko = 32 * kk + 8 * lq;
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) {
+      if (tj <= w) {
+        acc[tj] = mfma32(kf[kk], ld8(&sKh[16 * tj + l16][ko]), acc[tj]);
+        if constexpr (KRES) acc[tj] = mfma32(kf[kk], ld8(&sKl[16 * tj + l16][ko]), acc[tj]);
+      }
+    }
+  }
+  {
+    float gm[4], bm[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gm[i] = GATED ? sG[m0 + 4 * lq + i] : 0.0f;
+      bm[i] = sBeta[m0 + 4 * lq + i];
+    }
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) {
+      if (tj <= w) {
+        const int nn = 16 * tj + l16;
+        const float gn = GATED ? sG[nn] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + 4 * lq + i;
+          const float ratio = GATED ? __expf(gm[i] - gn) : 1.0f;
+          sA[m][nn] = nn < m ? bm[i] * ratio * acc[tj][i] : 0.0f;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // the key rows are dead: clear Tm (its upper triangle stays zero)
+  for (int i = tid; i < C * CP / 8; i += 256) reinterpret_cast<bf16x8 *>(&sTr[0][0])[i] = bf16x8{};
+  __syncthreads();
+
+  // (i) wave w inverts diagonal block w by forward substitution in fp32;
+  //     lane l & 15 computes column c of the block inverse.
+  {
+    const int c = l16, bb = m0;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float s = (i == c) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int j = 0; j < i; ++j) s -= sA[bb + i][bb + j] * x[j];
+      x[i] = s;
+    }
+    if (lq == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sTr[bb + i][bb + c] = to_bf16(x[i]);
+      bf16x8 lo8, hi8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo8[i] = to_bf16(x[i]);
+        hi8[i] = to_bf16(x[i + 8]);
+      }
+      *reinterpret_cast<bf16x8 *>(&sTc[bb + c][bb]) = lo8;
+      *reinterpret_cast<bf16x8 *>(&sTc[bb + c][bb + 8]) = hi8;
+    }
+  }
+  __syncthreads();
+  // (ii) T_{q+1,q} = -T_{q+1,q+1} A_{q+1,q} T_{q,q}, q = 0 (wave 0), q = 2 (wave 1)
+  if (w < 2) {
+    const int q = 2 * w, p = q + 1;
+    bf16x4 aop;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) aop[e] = to_bf16(sA[16 * p + l16][16 * q + 4 * lq + e]);
+    const floatx4 X = mfma16(aop, ld4(&sTc[16 * q + l16][16 * q + 4 * lq]), floatx4{0.f, 0.f, 0.f, 0.f});
+    const floatx4 Y = mfma16(ld4(&sTr[16 * p + l16][16 * p + 4 * lq]), pack4(X), floatx4{0.f, 0.f, 0.f, 0.f});
+    bf16x4 nt;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      nt[i] = to_bf16(-Y[i]);
+      sTr[16 * p + 4 * lq + i][16 * q + l16] = nt[i];
+    }
+    *reinterpret_cast<bf16x4 *>(&sTc[16 * q + l16][16 * p + 4 * lq]) = nt;
+  }
+  __syncthreads();
+  // (iii) lower-left 32x32 block: X = A_BA T_AA, then T_BA = -T_BB X;
+  //       wave w owns output block (p, q) = (2 + w/2, w%2).
+  {
+    const int p = 2 + (w >> 1), q = w & 1;
+    floatx4 X = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = q; kb < 2; ++kb) {
+      bf16x4 aop;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) aop[e] = to_bf16(sA[16 * p + l16][16 * kb + 4 * lq + e]);
+      X = mfma16(aop, ld4(&sTc[16 * q + l16][16 * kb + 4 * lq]), X);
+    }
+    *reinterpret_cast<bf16x4 *>(&sX[16 * q + l16][16 * p + 4 * lq]) = pack4(X);
+    __syncthreads();
+    floatx4 Y = {0.f, 0.f, 0.f, 0.f};
+    for (int mb = 2; mb <= p; ++mb)
+      Y = mfma16(ld4(&sTr[16 * p + l16][16 * mb + 4 * lq]), ld4(&sX[16 * q + l16][16 * mb + 4 * lq]), Y);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sTr[16 * p + 4 * lq + i][16 * q + l16] = to_bf16(-Y[i]);
+  }
+  __syncthreads();
+  // Tm rows to the workspace: 64 x 64 bf16, two 16-byte vectors per thread
+  bf16 *dst = tout + (seq * N + n) * (C * C);
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int v = tid + 256 * p, r = v >> 3, c8 = (v & 7) * 8;
+    *reinterpret_cast<bf16x8 *>(dst + r * C + c8) = ld8(&sTr[r][c8]);
+  }
+}
+
+// ============================================================ sweep
+struct SeqLay {
+  static constexpr int KH = 0;                       // bf16 [C][KP]  write keys hi
+  static constexpr int KL = KH + C * KP * 2;         // bf16 [C][KP]  write keys lo
+  static constexpr int KTH = KL + C * KP * 2;        // bf16 [KD][CP] write keys^T hi
+  static constexpr int KTL = KTH + KD * CP * 2;      // bf16 [KD][CP] write keys^T lo
+  static constexpr int V = KTL + KD * CP * 2;        // bf16 [C][VT+8] value tile
+  static constexpr int BETA = V + C * (VT + 8) * 2;  // f32 [C]
+  static constexpr int G = BETA + C * 4;             // f32 [C] cumulative log decay
+  static constexpr int MH = G + C * 4;               // bf16 [C][CP]  scores hi
+  static constexpr int ML = MH + C * CP * 2;         // bf16 [C][CP]  scores lo
+  static constexpr int RTH = ML + C * CP * 2;        // bf16 [VT][CP] R^T hi
+  static constexpr int RTL = RTH + VT * CP * 2;      // bf16 [VT][CP] R^T lo
+  static constexpr int DTH = RTL + VT * CP * 2;      // bf16 [VT][CP] Delta^T hi
+  static constexpr int DTL = DTH + VT * CP * 2;      // bf16 [VT][CP] Delta^T lo
+  static constexpr int DSH = DTL + VT * CP * 2;      // bf16 [VT][CP] decayed Delta^T hi
+  static constexpr int DSL = DSH + VT * CP * 2;      // bf16 [VT][CP] decayed Delta^T lo
+  static constexpr int SH = DSL + VT * CP * 2;       // bf16 [VT][KP] state hi
+  static constexpr int SL = SH + VT * KP * 2;        // bf16 [VT][KP] state lo
+  static constexpr int TOTAL = SL + VT * KP * 2;
+  static_assert(TOTAL <= 160 * 1024, "LDS budget");
+};
+
+template <bool GATED, bool KRES>
+__global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 *tin, int64_t N) {
+  typedef SeqLay L;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
+  bf16(*sKh)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::KH);
+  bf16(*sKl)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::KL);
+  bf16(*sKtTh)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::KTH);
+  bf16(*sKtTl)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::KTL);
+  bf16(*sV)[VT + 8] = reinterpret_cast<bf16(*)[VT + 8]>(smem + L::V);
+  float *sBeta = reinterpret_cast<float *>(smem + L::BETA);
+  float *sG = reinterpret_cast<float *>(smem + L::G);
+  bf16(*sMh)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::MH);
+  bf16(*sMl)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::ML);
+  bf16(*sRh)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::RTH);
+  bf16(*sRl)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::RTL);
+  bf16(*sDh)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::DTH);
+  bf16(*sDl)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::DTL);
+  bf16(*sDsh)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + (GATED ? L::DSH : L::DTH));
+  bf16(*sDsl)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + (GATED ? L::DSL : L::DTL));
+  bf16(*sSh)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::SH);
+  bf16(*sSl)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::SL);
+
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = l & 15, lq = l >> 4;
+  const int rw = w & 3, cw = w >> 2;  // token rows [16 rw, +16), value columns [16 cw, +16)
+  // XCD-aware placement: block i runs on XCD i % 8; the NT tiles of one
+  // sequence share i % 8, so their reads of the same keys meet in one L2.
+  const int bid = blockIdx.x;
+  const int slot = bid & 7, rest = bid >> 3;
+  const int vt = rest % NT;
+  const int64_t seq = (int64_t)(rest / NT) * 8 + slot;
+  const int64_t H = a.H, T = a.T;
+  if (seq >= a.B * H) return;
+  const int64_t b = seq / H, h = seq - b * H;
+  const int v0 = vt * VT;
+
+  const bf16 *gq = static_cast<const bf16 *>(a.q);
+  const bf16 *gk = static_cast<const bf16 *>(a.k);
+  const bf16 *gkt = static_cast<const bf16 *>(a.kt);
+  const bf16 *gv = static_cast<const bf16 *>(a.v);
+  bf16 *go = static_cast<bf16 *>(a.o);
+  const int64_t tstride = H * KD;                   // elements between tokens (K == V == 128)
+  const int64_t base = (b * T) * tstride + h * KD;  // token 0 of this (b,h)
+  const bf16 *tseq = tin + seq * N * (C * C);
+
+  // scores: the tiles above the diagonal are never written and stay zero
+  for (int i = tid; i < C * CP / 8; i += 512) {
+    reinterpret_cast<bf16x8 *>(&sMh[0][0])[i] = bf16x8{};
+    reinterpret_cast<bf16x8 *>(&sMl[0][0])[i] = bf16x8{};
+  }
+  // state tiles in accumulators: wave w owns tiles (rt, kt) = (w & 1, 2 (w >> 1) + j),
+  // element i of tile j is S[16 rt + 4 lq + i][16 kt + l16]
+  const int srt = w & 1;
+  floatx4 Sacc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int vr = 16 * srt + 4 * lq + i, c = 16 * (2 * (w >> 1) + j) + l16;
+      const float s0 = a.S0 ? a.S0[(seq * VD + v0 + vr) * KD + c] : 0.0f;
+      Sacc[j][i] = s0;
+      const bf16 hi = to_bf16(s0);
+      sSh[vr][c] = hi;
+      sSl[vr][c] = to_bf16(s0 - to_f32(hi));
+    }
+
+  // ---- prefetch registers for one chunk
+  //   write keys: thread -> token l, columns [16 w, 16 w + 16)
+  //   values:     threads < 256: token tid / 4, columns 8 (tid % 4) of the tile
+  //   K, Q, Tm:   rows 16 rw + l16 in MFMA A-operand layout
+  // Tokens past T (last chunk only) read token 0 instead and are never
+  // selected here: a select would wait for the load.  Their beta is zeroed
+  // at use, which makes their R and Delta rows zero; their scores fall
+  // outside the causal mask and their outputs are not stored.
+  bf16x8 pkt[2], pkk[2], pv, pk[4], pq[4], pt[2];
+  float pbeta = 0.0f, palpha = 1.0f;
+  auto fetch = [&](int64_t n) {
+    const int64_t t0 = n * C;
+    {
+      const int64_t off = base + (t0 + l < T ? t0 + l : 0) * tstride + 16 * w;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        pkt[p] = ld8(gkt + off + 8 * p);
+        if constexpr (KRES) pkk[p] = ld8(gk + off + 8 * p);
+      }
+    }
+    if (tid < 256) {
+      const int i = tid >> 2, cv = tid & 3;
+      pv = ld8(gv + base + (t0 + i < T ? t0 + i : 0) * tstride + v0 + 8 * cv);
+    }
+    {
+      const int m = 16 * rw + l16;
+      const int64_t off = base + (t0 + m < T ? t0 + m : 0) * tstride + 8 * lq;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        pk[kk] = ld8(gk + off + 32 * kk);
+        pq[kk] = ld8(gq + off + 32 * kk);
+      }
+      const bf16 *tp = tseq + n * (C * C) + m * C + 8 * lq;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) pt[kk] = ld8(tp + 32 * kk);
+    }
+    if (w == 0) {
+      const int64_t gi = (b * T + (t0 + l < T ? t0 + l : 0)) * H + h;
+      pbeta = a.beta[gi];
+      if constexpr (GATED) palpha = a.alpha[gi];
+    }
+  };
+
+  if (N > 0) fetch(0);
+  for (int64_t n = 0; n < N; ++n) {
+    const int64_t t0 = n * C;
+    const int Lc = (int)((T - t0) < C ? (T - t0) : C);
+    __syncthreads();  // the previous chunk is done with every LDS buffer
+    // ---- stage L: registers -> LDS
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int c0 = 16 * w + 8 * p;
+      if constexpr (KRES) {
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = to_f32(pkk[p][e]) + to_f32(pkt[p][e]);  // k~ = k + residual
+          hi[e] = to_bf16(x);
+          lo[e] = to_bf16(x - to_f32(hi[e]));
+        }
+        *reinterpret_cast<bf16x8 *>(&sKh[l][c0]) = hi;
+        *reinterpret_cast<bf16x8 *>(&sKl[l][c0]) = lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          sKtTh[c0 + e][l] = hi[e];
+          sKtTl[c0 + e][l] = lo[e];
+        }
+      } else {
+        *reinterpret_cast<bf16x8 *>(&sKh[l][c0]) = pkt[p];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sKtTh[c0 + e][l] = pkt[p][e];
+      }
+    }
+    if (tid < 256) *reinterpret_cast<bf16x8 *>(&sV[tid >> 2][8 * (tid & 3)]) = pv;
+    if (w == 0) {
+      const bool ok = l < Lc;
+      sBeta[l] = ok ? pbeta : 0.0f;
+      if constexpr (GATED) {
+        float x = ok ? logf(palpha) : 0.0f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float y = __shfl_up(x, off, 64);
+          if (l >= off) x += y;
+        }
+        sG[l] = x;
+      }
+    }
+    bf16x8 kf[4], qf[4], tf[2];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      kf[kk] = pk[kk];
+      qf[kk] = pq[kk];
+    }
+    tf[0] = pt[0];
+    tf[1] = pt[1];
+    __syncthreads();
+    if (n + 1 < N) fetch(n + 1);  // overlaps with the compute below
+
+    const int m0 = 16 * rw;
+    // ---- stage G: K S^T and Q S^T for tile (rw, cw); score tiles (rw, tj),
+    //      tj <= rw, tj = cw (mod 2)
+    floatx4 accKS = {0.f, 0.f, 0.f, 0.f}, accQS = {0.f, 0.f, 0.f, 0.f};
+    floatx4 accM[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    {
+      // all operands first, then the products without branches (a score tile
+      // above the diagonal is computed and dropped)
+      bf16x8 sh[4], sl[4], mh[2][4], ml[2][4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int ko = 32 * kk + 8 * lq;
+        sh[kk] = ld8(&sSh[16 * cw + l16][ko]);
+        sl[kk] = ld8(&sSl[16 * cw + l16][ko]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          mh[j][kk] = ld8(&sKh[16 * (cw + 2 * j) + l16][ko]);
+          if constexpr (KRES) ml[j][kk] = ld8(&sKl[16 * (cw + 2 * j) + l16][ko]);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        accKS = mfma32(kf[kk], sh[kk], accKS);
+        accQS = mfma32(qf[kk], sh[kk], accQS);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) accM[j] = mfma32(qf[kk], mh[j][kk], accM[j]);
+        accKS = mfma32(kf[kk], sl[kk], accKS);
+        accQS = mfma32(qf[kk], sl[kk], accQS);
+        if constexpr (KRES) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) accM[j] = mfma32(qf[kk], ml[j][kk], accM[j]);
+        }
+      }
+    }
+    float gm[4], bm[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gm[i] = GATED ? sG[m0 + 4 * lq + i] : 0.0f;
+      bm[i] = sBeta[m0 + 4 * lq + i];
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int tj = cw + 2 * j;
+      if (tj <= rw) {
+        const int nn = 16 * tj + l16;
+        const float gn = GATED ? sG[nn] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + 4 * lq + i;
+          const float ratio = GATED ? __expf(gm[i] - gn) : 1.0f;
+          const float mv = nn <= m ? ratio * accM[j][i] : 0.0f;
+          const bf16 mh = to_bf16(mv);
+          sMh[m][nn] = mh;
+          sMl[m][nn] = to_bf16(mv - to_f32(mh));
+        }
+      }
+    }
+    floatx4 Oacc;
+    {
+      floatx4 r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 4 * lq + i, vr = 16 * cw + l16;
+        const float em = GATED ? __expf(gm[i]) : 1.0f;
+        r[i] = bm[i] * (to_f32(sV[m][vr]) - em * accKS[i]);
+        Oacc[i] = em * accQS[i];
+      }
+      bf16x4 rh, rl;
+      split4(r, rh, rl);
+      *reinterpret_cast<bf16x4 *>(&sRh[16 * cw + l16][m0 + 4 * lq]) = rh;
+      *reinterpret_cast<bf16x4 *>(&sRl[16 * cw + l16][m0 + 4 * lq]) = rl;
+    }
+    __syncthreads();
+
+    // ---- stage D: Delta tile (rw, cw) = Tm R, split and stored transposed
+    const float gL = GATED ? sG[Lc - 1] : 0.0f;
+    // both 32-wide k-steps on every wave: the upper triangles of Tm and of
+    // the scores are zero
+    {
+      bf16x8 rh[2], rl[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        rh[kk] = ld8(&sRh[16 * cw + l16][32 * kk + 8 * lq]);
+        rl[kk] = ld8(&sRl[16 * cw + l16][32 * kk + 8 * lq]);
+      }
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        acc = mfma32(tf[kk], rh[kk], acc);
+        acc = mfma32(tf[kk], rl[kk], acc);
+      }
+      bf16x4 dh, dl;
+      split4(acc, dh, dl);
+      *reinterpret_cast<bf16x4 *>(&sDh[16 * cw + l16][m0 + 4 * lq]) = dh;
+      *reinterpret_cast<bf16x4 *>(&sDl[16 * cw + l16][m0 + 4 * lq]) = dl;
+      if constexpr (GATED) {
+        floatx4 s;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = acc[i] * __expf(gL - gm[i]);
+        split4(s, dh, dl);
+        *reinterpret_cast<bf16x4 *>(&sDsh[16 * cw + l16][m0 + 4 * lq]) = dh;
+        *reinterpret_cast<bf16x4 *>(&sDsl[16 * cw + l16][m0 + 4 * lq]) = dl;
+      }
+    }
+    __syncthreads();
+
+    // ---- stage O: output tile (rw, cw)
+    {
+      floatx4 acc = Oacc;
+      bf16x8 mh[2], ml[2], dh[2], dl[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int ko = 32 * kk + 8 * lq;
+        mh[kk] = ld8(&sMh[m0 + l16][ko]);
+        ml[kk] = ld8(&sMl[m0 + l16][ko]);
+        dh[kk] = ld8(&sDh[16 * cw + l16][ko]);
+        dl[kk] = ld8(&sDl[16 * cw + l16][ko]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        acc = mfma32(mh[kk], dh[kk], acc);
+        acc = mfma32(mh[kk], dl[kk], acc);
+        acc = mfma32(ml[kk], dh[kk], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 4 * lq + i;
+        if (m < Lc) go[base + (t0 + m) * tstride + v0 + 16 * cw + l16] = to_bf16(a.q_scale * acc[i]);
+      }
+    }
+    // ---- stage S: the wave's two state tiles, then their bf16 pair
+    const float decay = GATED ? __expf(gL) : 1.0f;
+    bf16x8 dsh[2], dsl[2], kth[2][2], ktl[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int ko = 32 * kk + 8 * lq;
+      dsh[kk] = ld8(&sDsh[16 * srt + l16][ko]);
+      dsl[kk] = ld8(&sDsl[16 * srt + l16][ko]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        kth[j][kk] = ld8(&sKtTh[16 * (2 * (w >> 1) + j) + l16][ko]);
+        if constexpr (KRES) ktl[j][kk] = ld8(&sKtTl[16 * (2 * (w >> 1) + j) + l16][ko]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int kt = 2 * (w >> 1) + j;
+      floatx4 acc = Sacc[j];
+      if constexpr (GATED) acc = acc * decay;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        acc = mfma32(dsh[kk], kth[j][kk], acc);
+        acc = mfma32(dsl[kk], kth[j][kk], acc);
+        if constexpr (KRES) acc = mfma32(dsh[kk], ktl[j][kk], acc);
+      }
+      Sacc[j] = acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int vr = 16 * srt + 4 * lq + i, c = 16 * kt + l16;
+        const bf16 hi = to_bf16(acc[i]);
+        sSh[vr][c] = hi;
+        sSl[vr][c] = to_bf16(acc[i] - to_f32(hi));
+      }
+    }
+  }
+
+  if (a.S_out) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int vr = 16 * srt + 4 * lq + i, c = 16 * (2 * (w >> 1) + j) + l16;
+        a.S_out[(seq * VD + v0 + vr) * KD + c] = Sacc[j][i];
+      }
+  }
+}
+
+template <bool GATED, bool KRES>
+void launch_both(const ChunkArgs &a, bf16 *tw, int64_t N, hipStream_t s) {
+  const int64_t nseq = a.B * a.H;
+  if (N > 0)
+    hipLaunchKernelGGL((chunk_tinv_kernel<GATED, KRES>), dim3((unsigned)(nseq * N)), dim3(256), 0, s, a, tw, N);
+  const int64_t groups = (nseq + 7) / 8;
+  hipLaunchKernelGGL((chunk_seq_kernel<GATED, KRES>), dim3((unsigned)(groups * 8 * NT)), dim3(512), 0, s, a,
+                     (const bf16 *)tw, N);
+}
+
+}  // namespace
+
+size_t chunk_wy_work_bytes(int64_t B, int64_t T, int64_t H) {
+  const int64_t N = (T + C - 1) / C;
+  return (size_t)(B * H * N) * C * C * 2;
+}
+
+hipError_t launch_chunk_wy(const ChunkArgs &a, void *work, hipStream_t s) {
+  if (a.B * a.H == 0) return hipSuccess;
+  const int64_t N = (a.T + C - 1) / C;
+  bf16 *tw = static_cast<bf16 *>(work);
+  if (a.alpha) {
+    if (a.kt_is_res)
+      launch_both<true, true>(a, tw, N, s);
+    else
+      launch_both<true, false>(a, tw, N, s);
+  } else {
+    if (a.kt_is_res)
+      launch_both<false, true>(a, tw, N, s);
+    else
+      launch_both<false, false>(a, tw, N, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace osdn

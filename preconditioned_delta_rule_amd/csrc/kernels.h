@@ -51,6 +51,10 @@ ScanWork scan_work_layout(void *base, int64_t B, int64_t T, int64_t H, int64_t K
 hipError_t launch_precond_scan_chunked(const ScanArgs &a, const ScanWork &w, bool bf16, hipStream_t s);
 hipError_t launch_chunk_generic(const ChunkArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s);
+// Two-kernel MFMA path (same shapes as launch_chunk_mfma): the per-chunk
+// (I + A)^-1 of every chunk goes through a bf16 workspace [B,H,N,64,64].
+size_t chunk_wy_work_bytes(int64_t B, int64_t T, int64_t H);
+hipError_t launch_chunk_wy(const ChunkArgs &a, void *work, hipStream_t s);
 
 // Shape coverage of the specialised MFMA path (bf16, K = V = 128, C = 64).
 bool chunk_mfma_supported(const ChunkArgs &a, bool bf16);

@@ -141,10 +141,25 @@ osdn_status run_scan(const osdn_desc *d, const osdn::ScanArgs &a, hipStream_t s)
   return hip_status(osdn::launch_precond_scan(a, d->dtype == OSDN_BF16, s), "phase-1 launch");
 }
 
-osdn_status run_chunk(const osdn_desc *d, const osdn::ChunkArgs &a, hipStream_t s) {
+// Phase-2 kernels: for bf16 with K = V = 128 and chunk 64 the matrix-core
+// path (two kernels when a workspace is given, one otherwise), else the
+// generic fp32-arithmetic kernel.
+osdn_status run_chunk(const osdn_desc *d, const osdn::ChunkArgs &a, void *work, hipStream_t s) {
   const bool bf = d->dtype == OSDN_BF16;
-  if (osdn::chunk_mfma_supported(a, bf)) return hip_status(osdn::launch_chunk_mfma(a, s), "phase-2 launch");
+  if (osdn::chunk_mfma_supported(a, bf)) {
+    if (work) return hip_status(osdn::launch_chunk_wy(a, work, s), "phase-2 launch");
+    return hip_status(osdn::launch_chunk_mfma(a, s), "phase-2 launch");
+  }
   return hip_status(osdn::launch_chunk_generic(a, bf, s), "phase-2 launch");
+}
+
+size_t chunk_work_bytes(const osdn_desc *d) {
+  osdn::ChunkArgs a;
+  a.K = d->K;
+  a.V = d->V;
+  a.C = d->chunk;
+  if (!osdn::chunk_mfma_supported(a, d->dtype == OSDN_BF16)) return 0;
+  return (osdn::chunk_wy_work_bytes(d->B, d->T, d->H) + 255) & ~(size_t)255;
 }
 
 }  // namespace
@@ -230,9 +245,14 @@ osdn_status osdn_precond_scan(const osdn_desc *d, const void *k, const float *be
   return ok();
 }
 
+size_t osdn_chunk_fwd_workspace_bytes(const osdn_desc *d) {
+  if (validate(d, 2) != OSDN_OK) return 0;
+  return chunk_work_bytes(d);
+}
+
 osdn_status osdn_chunk_fwd(const osdn_desc *d, const void *q, const void *k, const void *k_tilde, const void *v,
                            const float *beta, const float *alpha, const float *S0, void *o, float *S_out,
-                           void *stream) {
+                           void *workspace, size_t workspace_bytes, void *stream) {
   OSDN_TRY(validate(d, 2));
   const bool need_seq = d->T > 0;
   OSDN_TRY(check_ptr(q, "q", need_seq));
@@ -245,8 +265,12 @@ osdn_status osdn_chunk_fwd(const osdn_desc *d, const void *q, const void *k, con
   OSDN_TRY(check_ptr(o, "o", need_seq));
   OSDN_TRY(check_ptr(S_out, "S_out", false));
   if (o && (o == q || o == k || o == k_tilde || o == v)) return fail(OSDN_EINVAL, "o must not alias an input");
+  OSDN_TRY(check_ptr(workspace, "workspace", false));
+  const size_t need = chunk_work_bytes(d);
+  if (workspace && workspace_bytes < need)
+    return fail(OSDN_EINVAL, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
   OSDN_TRY(run_chunk(d, chunk_args(d, q, k, k_tilde, v, beta, alpha, S0, o, S_out),
-                     static_cast<hipStream_t>(stream)));
+                     need ? workspace : nullptr, static_cast<hipStream_t>(stream)));
   return ok();
 }
 
@@ -257,7 +281,7 @@ static size_t fwd_keys_bytes(const osdn_desc *d) {
 
 size_t osdn_fwd_workspace_bytes(const osdn_desc *d) {
   if (validate(d, 3) != OSDN_OK) return 0;
-  return fwd_keys_bytes(d) + osdn::scan_work_bytes(d->B, d->T, d->H, d->K);
+  return fwd_keys_bytes(d) + osdn::scan_work_bytes(d->B, d->T, d->H, d->K) + chunk_work_bytes(d);
 }
 
 osdn_status osdn_fwd(const osdn_desc *d, const void *q, const void *k, const void *v, const float *beta,
@@ -283,7 +307,7 @@ osdn_status osdn_fwd(const osdn_desc *d, const void *q, const void *k, const voi
   if (!need_seq) {
     // nothing to sweep: d_out = d1 and S_out = S0 (the kernels do the copy)
     OSDN_TRY(run_scan(d, sa, s));
-    OSDN_TRY(run_chunk(d, ca, s));
+    OSDN_TRY(run_chunk(d, ca, nullptr, s));
     return ok();
   }
   OSDN_TRY(check_ptr(workspace, "workspace", true));
@@ -301,11 +325,12 @@ osdn_status osdn_fwd(const osdn_desc *d, const void *q, const void *k, const voi
     sa.k_tilde = ws;
     ca.kt = ws;
   }
+  const size_t scan_bytes = osdn::scan_work_bytes(d->B, d->T, d->H, d->K);
   OSDN_TRY(hip_status(osdn::launch_precond_scan_chunked(
                           sa, osdn::scan_work_layout(ws + fwd_keys_bytes(d), d->B, d->T, d->H, d->K),
                           d->dtype == OSDN_BF16, s),
                       "phase-1 launch"));
-  OSDN_TRY(run_chunk(d, ca, s));
+  OSDN_TRY(run_chunk(d, ca, chunk_work_bytes(d) ? ws + fwd_keys_bytes(d) + scan_bytes : nullptr, s));
   return ok();
 }
 

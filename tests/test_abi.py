@@ -111,7 +111,7 @@ def test_null_and_misaligned_pointers_rejected_before_launch(lib):
                                null, ctypes.c_void_p(0x3000), ctypes.c_size_t(16), null)
     assert st == osdn.EINVAL and "needed" in lib.osdn_last_error().decode()
     st = lib.osdn_chunk_fwd(ctypes.byref(d), fake, fake, fake, fake, fake, null, null, fake,
-                            null, null)
+                            null, null, z, null)
     assert st == osdn.EINVAL and "alias" in lib.osdn_last_error().decode()
     st = lib.osdn_fwd(ctypes.byref(d), fake, fake, fake, fake, null, null, null, null,
                       ctypes.c_void_p(0x2000), null, null, null, null, ctypes.c_size_t(0), null)
@@ -132,8 +132,12 @@ def test_workspace_bytes(lib):
     scan = 2 * tok + 4 * 16 * 64 * 128 * 4 + 4 * 16 * 64 * 4 + 256 * 3
     assert lib.osdn_precond_scan_workspace_bytes(ctypes.byref(d)) == scan
     assert lib.osdn_precond_scan_counters_offset(ctypes.byref(d)) == scan - 256 * 3
-    assert lib.osdn_fwd_workspace_bytes(ctypes.byref(d)) == 4 * 4096 * 16 * 128 * 2 + scan
+    # phase 2 on the matrix cores keeps one bf16 64 x 64 block per chunk
+    wy = 4 * 16 * 64 * 64 * 64 * 2
+    assert lib.osdn_chunk_fwd_workspace_bytes(ctypes.byref(d)) == wy
+    assert lib.osdn_fwd_workspace_bytes(ctypes.byref(d)) == 4 * 4096 * 16 * 128 * 2 + scan + wy
     d.dtype = osdn.F32
+    assert lib.osdn_chunk_fwd_workspace_bytes(ctypes.byref(d)) == 0
     assert lib.osdn_fwd_workspace_bytes(ctypes.byref(d)) == 4 * 4096 * 16 * 128 * 4 + scan
     # a ragged tail chunk counts as a chunk
     d.T = 4097

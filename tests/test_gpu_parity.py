@@ -159,7 +159,7 @@ CHUNK_CASES = {
 }
 
 
-def run_chunk_case(name, dtype, gated, s0, q_scale, seed=21):
+def run_chunk_case(name, dtype, gated, s0, q_scale, seed=21, two_pass=True):
     spec = dict(CHUNK_CASES[name], dtype=dtype, seed=seed, gdn=gated, apf=True)
     inp = make_inputs(spec)
     B, T, H, K = inp["k"].shape
@@ -171,20 +171,25 @@ def run_chunk_case(name, dtype, gated, s0, q_scale, seed=21):
     o, S = osdn.chunk_fwd(to_dev(inp["q"], dtype), to_dev(inp["k"], dtype), to_dev(kt_in, dtype),
                           to_dev(inp["v"], dtype), to_dev(inp["beta"], "f32"),
                           to_dev(inp["alpha"], "f32"), to_dev(S0, "f32"), chunk=spec["chunk"],
-                          q_scale=q_scale)
+                          q_scale=q_scale, two_pass=two_pass)
     torch.cuda.synchronize()
     o_ref, S_ref = oracle.delta_rule(inp["q"], inp["k"], kt_in, inp["v"], inp["beta"],
                                      inp["alpha"], S0, q_scale=q_scale)
     return to_np(o), to_np(S), o_ref, S_ref
 
 
+@pytest.mark.parametrize("two_pass", [True, False], ids=["two_pass", "one_pass"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("gated", [False, True])
 @pytest.mark.parametrize("name", sorted(CHUNK_CASES))
-def test_chunk_parity(name, dtype, gated):
+def test_chunk_parity(name, dtype, gated, two_pass):
+    spec = CHUNK_CASES[name]
+    mfma = dtype == "bf16" and spec["K"] == spec["V"] == 128 and spec["chunk"] == 64
+    if not two_pass and not mfma:
+        pytest.skip("only the matrix-core shapes have a second phase-2 path")
     s0 = name in ("mfma_tail", "k128_c64_tail", "tiny_c16")
-    q_scale = 1.0 / math.sqrt(CHUNK_CASES[name]["K"]) if name in ("mfma_grid_pad", "k64_v32_c32") else 1.0
-    o, S, o_ref, S_ref = run_chunk_case(name, dtype, gated, s0, q_scale)
+    q_scale = 1.0 / math.sqrt(spec["K"]) if name in ("mfma_grid_pad", "k64_v32_c32") else 1.0
+    o, S, o_ref, S_ref = run_chunk_case(name, dtype, gated, s0, q_scale, two_pass=two_pass)
     if dtype == "f32":
         assert rel_err(o, o_ref) <= F32_OS, (name, rel_err(o, o_ref))
         assert rel_err(S, S_ref) <= F32_OS, (name, rel_err(S, S_ref))
