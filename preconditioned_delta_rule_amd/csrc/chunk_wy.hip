@@ -23,11 +23,15 @@
 // Tm depends only on the chunk's keys, so the sweep carries no triangular
 // solve: its per-chunk work is five small products, split over 8 waves (wave
 // (rw, cw) owns token rows [16 rw, 16 rw + 16) and value columns
-// [16 cw, 16 cw + 16) of the chunk), with four barriers per chunk.
+// [16 cw, 16 cw + 16) of the chunk), with four barriers per chunk.  Each
+// input row is loaded once per workgroup and staged in LDS; the key rows
+// serve both as row operands and, through transposed LDS reads, as the
+// token-major operand of the state update.
 //
-// Precision as in the single-kernel form: intermediates that are not bf16
-// (S, R, Delta, the scores, and k~ = k + residual) enter every product as a
-// hi + lo pair of bf16; Tm and the output are the only 8-bit roundings.
+// Precision: intermediates that are not bf16 (S, R, Delta, the scores) enter
+// every product as a hi + lo pair of bf16; the write key in its residual form
+// k~ = k + E enters as the pair (k, E), both exact; Tm and the output are the
+// only 8-bit roundings.
 #include "kernels.h"
 #include "mfma_common.h"
 
@@ -47,8 +51,8 @@ constexpr int AP = C + 4;  // LDS pitch (f32) of the Gram
 // ============================================================ UT transform
 struct TinvLay {
   // the key rows are dead once the Gram is formed; the inverse reuses them
-  static constexpr int KH = 0;                   // bf16 [C][KP] write keys (hi)
-  static constexpr int KL = KH + C * KP * 2;     // bf16 [C][KP] write keys (lo)
+  static constexpr int KH = 0;                   // bf16 [C][KP] write keys, or residual E
+  static constexpr int KL = KH + C * KP * 2;     // bf16 [C][KP] keys (residual form)
   static constexpr int TR = 0;                   // bf16 [C][CP] Tm row-major
   static constexpr int TC = TR + C * CP * 2;     // bf16 [C][CP] Tm column-major
   static constexpr int X = TC + C * CP * 2;      // bf16 [C][CP] merge scratch
@@ -86,28 +90,19 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
   const int64_t tstride = H * KD;
   const int64_t base = (b * T + t0) * tstride + h * KD;  // token t0 of this (b,h)
 
-  // write keys into LDS as a hi + lo pair: thread -> token l, columns [32 w, 32 w + 32)
+  // write keys into LDS: thread -> token l, columns [32 w, 32 w + 32).  With
+  // the residual form k~ = k + E both k and E are exact bf16 operands, so
+  // the Gram is K E^T + K K^T; otherwise the bf16 k~ rows themselves.
   {
     const bool ok = l < Lc;
     const int64_t off = base + (ok ? l : 0) * tstride + 32 * w;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       bf16x8 x = ld8(gkt + off + 8 * p);
-      x = ok ? x : bf16x8{};
+      *reinterpret_cast<bf16x8 *>(&sKh[l][32 * w + 8 * p]) = ok ? x : bf16x8{};
       if constexpr (KRES) {
         bf16x8 y = ld8(gk + off + 8 * p);
-        y = ok ? y : bf16x8{};
-        bf16x8 hi, lo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = to_f32(y[e]) + to_f32(x[e]);  // k~ = k + residual, exact in fp32
-          hi[e] = to_bf16(v);
-          lo[e] = to_bf16(v - to_f32(hi[e]));
-        }
-        *reinterpret_cast<bf16x8 *>(&sKh[l][32 * w + 8 * p]) = hi;
-        *reinterpret_cast<bf16x8 *>(&sKl[l][32 * w + 8 * p]) = lo;
-      } else {
-        *reinterpret_cast<bf16x8 *>(&sKh[l][32 * w + 8 * p]) = x;
+        *reinterpret_cast<bf16x8 *>(&sKl[l][32 * w + 8 * p]) = ok ? y : bf16x8{};
       }
     }
   }
@@ -256,12 +251,34 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
 }
 
 // ============================================================ sweep
+// Transposed operand read (gfx950 ds_read_b64_tr_b16).  Within each group of
+// 16 lanes, with D[i][p] the p-th bf16 at lane i's address, lane j receives
+// D[4 e + j / 4][j % 4] as element e.  Lane i of the group pointing at row
+// r0 + i / 4, column c0 + 4 (i % 4) of a row-major bf16 matrix X therefore
+// receives X[r0 + e][c0 + j], e < 4: four consecutive rows of column c0 + j,
+// which is the B operand layout of the matrix cores with k running over rows.
+__device__ __forceinline__ bf16x4 ld4_tr(const bf16 *p) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s4 *)(const_cast<bf16 *>(p)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// B operand of a 16x16x32 product with k over the rows [r0, r0 + 32) and n
+// over the columns [c0, c0 + 16) of a row-major [.][KP] bf16 matrix: lane l
+// (group g = l / 16) needs rows r0 + 8 g + e, e < 8, of column c0 + l % 16.
+__device__ __forceinline__ bf16x8 ld8_tr(const bf16 (*X)[KP], int r0, int c0, int l) {
+  const int g = l >> 4, i = l & 15;
+  const bf16x4 a = ld4_tr(&X[r0 + 8 * g + (i >> 2)][c0 + 4 * (i & 3)]);
+  const bf16x4 b = ld4_tr(&X[r0 + 8 * g + 4 + (i >> 2)][c0 + 4 * (i & 3)]);
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
 struct SeqLay {
-  static constexpr int KH = 0;                       // bf16 [C][KP]  write keys hi
-  static constexpr int KL = KH + C * KP * 2;         // bf16 [C][KP]  write keys lo
-  static constexpr int KTH = KL + C * KP * 2;        // bf16 [KD][CP] write keys^T hi
-  static constexpr int KTL = KTH + KD * CP * 2;      // bf16 [KD][CP] write keys^T lo
-  static constexpr int V = KTL + KD * CP * 2;        // bf16 [C][VT+8] value tile
+  static constexpr int Q = 0;                        // bf16 [C][KP]  queries
+  static constexpr int K = Q + C * KP * 2;           // bf16 [C][KP]  keys
+  static constexpr int E = K + C * KP * 2;           // bf16 [C][KP]  write keys, or residual E
+  static constexpr int V = E + C * KP * 2;           // bf16 [C][VT+8] value tile
   static constexpr int BETA = V + C * (VT + 8) * 2;  // f32 [C]
   static constexpr int G = BETA + C * 4;             // f32 [C] cumulative log decay
   static constexpr int MH = G + C * 4;               // bf16 [C][CP]  scores hi
@@ -278,14 +295,16 @@ struct SeqLay {
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
+// With the residual form (KRES) the write key is k~ = k + E with k and E both
+// exact bf16, so every product with k~ is the sum of a product with k and one
+// with E; otherwise the E buffer holds the bf16 k~ itself.
 template <bool GATED, bool KRES>
 __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 *tin, int64_t N) {
   typedef SeqLay L;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
-  bf16(*sKh)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::KH);
-  bf16(*sKl)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::KL);
-  bf16(*sKtTh)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::KTH);
-  bf16(*sKtTl)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::KTL);
+  bf16(*sQ)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::Q);
+  bf16(*sK)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::K);
+  bf16(*sE)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::E);
   bf16(*sV)[VT + 8] = reinterpret_cast<bf16(*)[VT + 8]>(smem + L::V);
   float *sBeta = reinterpret_cast<float *>(smem + L::BETA);
   float *sG = reinterpret_cast<float *>(smem + L::G);
@@ -345,39 +364,33 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
       sSl[vr][c] = to_bf16(s0 - to_f32(hi));
     }
 
-  // ---- prefetch registers for one chunk
-  //   write keys: thread -> token l, columns [16 w, 16 w + 16)
-  //   values:     threads < 256: token tid / 4, columns 8 (tid % 4) of the tile
-  //   K, Q, Tm:   rows 16 rw + l16 in MFMA A-operand layout
+  // ---- prefetch registers for one chunk (each input element is loaded once
+  //      per workgroup, in 16-byte vectors, 16 threads per token row)
+  //   q, k, E rows:  vectors tid and tid + 512 of each 64 x 128 tile
+  //   values:        threads < 256: token tid / 4, columns 8 (tid % 4) of the tile
+  //   Tm:            rows 16 rw + l16 in MFMA A-operand layout
   // Tokens past T (last chunk only) read token 0 instead and are never
   // selected here: a select would wait for the load.  Their beta is zeroed
   // at use, which makes their R and Delta rows zero; their scores fall
   // outside the causal mask and their outputs are not stored.
-  bf16x8 pkt[2], pkk[2], pv, pk[4], pq[4], pt[2];
+  bf16x8 pq[2], pk[2], pe[2], pv, pt[2];
   float pbeta = 0.0f, palpha = 1.0f;
   auto fetch = [&](int64_t n) {
     const int64_t t0 = n * C;
-    {
-      const int64_t off = base + (t0 + l < T ? t0 + l : 0) * tstride + 16 * w;
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        pkt[p] = ld8(gkt + off + 8 * p);
-        if constexpr (KRES) pkk[p] = ld8(gk + off + 8 * p);
-      }
+    for (int p = 0; p < 2; ++p) {
+      const int vi = tid + 512 * p, i = vi >> 4, c8 = 8 * (vi & 15);
+      const int64_t off = base + (t0 + i < T ? t0 + i : 0) * tstride + c8;
+      pq[p] = ld8(gq + off);
+      pk[p] = ld8(gk + off);
+      pe[p] = ld8(gkt + off);
     }
     if (tid < 256) {
       const int i = tid >> 2, cv = tid & 3;
       pv = ld8(gv + base + (t0 + i < T ? t0 + i : 0) * tstride + v0 + 8 * cv);
     }
     {
-      const int m = 16 * rw + l16;
-      const int64_t off = base + (t0 + m < T ? t0 + m : 0) * tstride + 8 * lq;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        pk[kk] = ld8(gk + off + 32 * kk);
-        pq[kk] = ld8(gq + off + 32 * kk);
-      }
-      const bf16 *tp = tseq + n * (C * C) + m * C + 8 * lq;
+      const bf16 *tp = tseq + n * (C * C) + (16 * rw + l16) * C + 8 * lq;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) pt[kk] = ld8(tp + 32 * kk);
     }
@@ -396,27 +409,10 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
     // ---- stage L: registers -> LDS
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const int c0 = 16 * w + 8 * p;
-      if constexpr (KRES) {
-        bf16x8 hi, lo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = to_f32(pkk[p][e]) + to_f32(pkt[p][e]);  // k~ = k + residual
-          hi[e] = to_bf16(x);
-          lo[e] = to_bf16(x - to_f32(hi[e]));
-        }
-        *reinterpret_cast<bf16x8 *>(&sKh[l][c0]) = hi;
-        *reinterpret_cast<bf16x8 *>(&sKl[l][c0]) = lo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          sKtTh[c0 + e][l] = hi[e];
-          sKtTl[c0 + e][l] = lo[e];
-        }
-      } else {
-        *reinterpret_cast<bf16x8 *>(&sKh[l][c0]) = pkt[p];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sKtTh[c0 + e][l] = pkt[p][e];
-      }
+      const int vi = tid + 512 * p, i = vi >> 4, c8 = 8 * (vi & 15);
+      *reinterpret_cast<bf16x8 *>(&sQ[i][c8]) = pq[p];
+      *reinterpret_cast<bf16x8 *>(&sK[i][c8]) = pk[p];
+      *reinterpret_cast<bf16x8 *>(&sE[i][c8]) = pe[p];
     }
     if (tid < 256) *reinterpret_cast<bf16x8 *>(&sV[tid >> 2][8 * (tid & 3)]) = pv;
     if (w == 0) {
@@ -432,12 +428,7 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
         sG[l] = x;
       }
     }
-    bf16x8 kf[4], qf[4], tf[2];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      kf[kk] = pk[kk];
-      qf[kk] = pq[kk];
-    }
+    bf16x8 tf[2];
     tf[0] = pt[0];
     tf[1] = pt[1];
     __syncthreads();
@@ -445,22 +436,22 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
 
     const int m0 = 16 * rw;
     // ---- stage G: K S^T and Q S^T for tile (rw, cw); score tiles (rw, tj),
-    //      tj <= rw, tj = cw (mod 2)
+    //      tj = cw, cw + 2 (a tile above the diagonal is computed and dropped)
     floatx4 accKS = {0.f, 0.f, 0.f, 0.f}, accQS = {0.f, 0.f, 0.f, 0.f};
     floatx4 accM[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     {
-      // all operands first, then the products without branches (a score tile
-      // above the diagonal is computed and dropped)
-      bf16x8 sh[4], sl[4], mh[2][4], ml[2][4];
+      bf16x8 kf[4], qf[4], sh[4], sl[4], me[2][4], mk[2][4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int ko = 32 * kk + 8 * lq;
+        kf[kk] = ld8(&sK[m0 + l16][ko]);
+        qf[kk] = ld8(&sQ[m0 + l16][ko]);
         sh[kk] = ld8(&sSh[16 * cw + l16][ko]);
         sl[kk] = ld8(&sSl[16 * cw + l16][ko]);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          mh[j][kk] = ld8(&sKh[16 * (cw + 2 * j) + l16][ko]);
-          if constexpr (KRES) ml[j][kk] = ld8(&sKl[16 * (cw + 2 * j) + l16][ko]);
+          me[j][kk] = ld8(&sE[16 * (cw + 2 * j) + l16][ko]);
+          if constexpr (KRES) mk[j][kk] = ld8(&sK[16 * (cw + 2 * j) + l16][ko]);
         }
       }
 #pragma unroll
@@ -468,12 +459,12 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
         accKS = mfma32(kf[kk], sh[kk], accKS);
         accQS = mfma32(qf[kk], sh[kk], accQS);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) accM[j] = mfma32(qf[kk], mh[j][kk], accM[j]);
+        for (int j = 0; j < 2; ++j) accM[j] = mfma32(qf[kk], me[j][kk], accM[j]);
         accKS = mfma32(kf[kk], sl[kk], accKS);
         accQS = mfma32(qf[kk], sl[kk], accQS);
         if constexpr (KRES) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) accM[j] = mfma32(qf[kk], ml[j][kk], accM[j]);
+          for (int j = 0; j < 2; ++j) accM[j] = mfma32(qf[kk], mk[j][kk], accM[j]);
         }
       }
     }
@@ -517,10 +508,10 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
     }
     __syncthreads();
 
-    // ---- stage D: Delta tile (rw, cw) = Tm R, split and stored transposed
+    // ---- stage D: Delta tile (rw, cw) = Tm R, split and stored transposed.
+    //      Both 32-wide k-steps on every wave: the upper triangles of Tm and
+    //      of the scores are zero.
     const float gL = GATED ? sG[Lc - 1] : 0.0f;
-    // both 32-wide k-steps on every wave: the upper triangles of Tm and of
-    // the scores are zero
     {
       bf16x8 rh[2], rl[2];
 #pragma unroll
@@ -573,38 +564,46 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
         if (m < Lc) go[base + (t0 + m) * tstride + v0 + 16 * cw + l16] = to_bf16(a.q_scale * acc[i]);
       }
     }
-    // ---- stage S: the wave's two state tiles, then their bf16 pair
+    // ---- stage S: the wave's two state tiles, then their bf16 pair.  The
+    //      write keys enter as B operands with k over tokens, read transposed
+    //      from the row-major key buffers.
     const float decay = GATED ? __expf(gL) : 1.0f;
-    bf16x8 dsh[2], dsl[2], kth[2][2], ktl[2][2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int ko = 32 * kk + 8 * lq;
-      dsh[kk] = ld8(&sDsh[16 * srt + l16][ko]);
-      dsl[kk] = ld8(&sDsl[16 * srt + l16][ko]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        kth[j][kk] = ld8(&sKtTh[16 * (2 * (w >> 1) + j) + l16][ko]);
-        if constexpr (KRES) ktl[j][kk] = ld8(&sKtTl[16 * (2 * (w >> 1) + j) + l16][ko]);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int kt = 2 * (w >> 1) + j;
-      floatx4 acc = Sacc[j];
-      if constexpr (GATED) acc = acc * decay;
+    {
+      bf16x8 dsh[2], dsl[2], be[2][2], bk[2][2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        acc = mfma32(dsh[kk], kth[j][kk], acc);
-        acc = mfma32(dsl[kk], kth[j][kk], acc);
-        if constexpr (KRES) acc = mfma32(dsh[kk], ktl[j][kk], acc);
-      }
-      Sacc[j] = acc;
+        const int ko = 32 * kk + 8 * lq;
+        dsh[kk] = ld8(&sDsh[16 * srt + l16][ko]);
+        dsl[kk] = ld8(&sDsl[16 * srt + l16][ko]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int vr = 16 * srt + 4 * lq + i, c = 16 * kt + l16;
-        const bf16 hi = to_bf16(acc[i]);
-        sSh[vr][c] = hi;
-        sSl[vr][c] = to_bf16(acc[i] - to_f32(hi));
+        for (int j = 0; j < 2; ++j) {
+          const int c0 = 16 * (2 * (w >> 1) + j);
+          be[j][kk] = ld8_tr(sE, 32 * kk, c0, l);
+          if constexpr (KRES) bk[j][kk] = ld8_tr(sK, 32 * kk, c0, l);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int kt = 2 * (w >> 1) + j;
+        floatx4 acc = Sacc[j];
+        if constexpr (GATED) acc = acc * decay;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          acc = mfma32(dsh[kk], be[j][kk], acc);
+          acc = mfma32(dsl[kk], be[j][kk], acc);
+          if constexpr (KRES) {
+            acc = mfma32(dsh[kk], bk[j][kk], acc);
+            acc = mfma32(dsl[kk], bk[j][kk], acc);
+          }
+        }
+        Sacc[j] = acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int vr = 16 * srt + 4 * lq + i, c = 16 * kt + l16;
+          const bf16 hi = to_bf16(acc[i]);
+          sSh[vr][c] = hi;
+          sSl[vr][c] = to_bf16(acc[i] - to_f32(hi));
+        }
       }
     }
   }
