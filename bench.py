@@ -1,24 +1,40 @@
 #!/usr/bin/env python3
 """OSDN forward throughput on one MI355X.
 
-One step = one full forward of one layer: phase 1 (preconditioner scan) and
-phase 2 (chunkwise WY delta rule) over a batch of synthetic inputs already in
-HBM, through the C ABI entry point osdn_fwd.  The default workload is the
-1.3B-shaped layer: B=4, H=16, T=4096, K=V=128, bf16 inputs, fp32 state,
-chunk 64, APF retention on.
+One step = one full forward of one layer through the C ABI entry point
+osdn_fwd: phase 1 (preconditioner scan: scan_prep, scan_solve and scan_emit
+kernels) and phase 2 (chunkwise WY delta rule: chunk_tinv and chunk_seq
+kernels) over a batch of synthetic inputs already resident in HBM.  The
+default workload is the 1.3B-shaped layer: B=4, H=16, T=4096, K=V=128, bf16
+inputs, fp32 state, chunk 64, APF retention on.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
-Roofline bookkeeping (algorithmic, per token-head, K = V = 128, bf16):
-  phase 1 bytes  = read k (2K) + beta (4) + r (4) + write k~ (2K)       = 520
-  phase 2 bytes  = read q, k, k~ (2K each) + v (2V) + beta (4) + write o (2V)
-                   (+4 for alpha)                                       = 1284
-  phase 2 flops  = dense chunk form 2(3CK + 2CV + 3KV) at C = 64        = 180224
-Peaks: HBM 8 TB/s, bf16 dense MFMA 2.5 PFLOP/s (MI355X published figures).
+Algorithmic work per token-head (K = V = 128, C = 64, bf16; +4 B for r or
+alpha where present), used for the roofline figures:
+  phase 1 (whole)   read k 2K + beta 4 (+ r 4), write k~ 2K             = 516 / 520 B
+    scan_prep       read k 2K + beta 4 (+ r 4)                          = 260 / 264 B
+    scan_solve      per-token scalars beta (+ r) and the key norm       =   8 /  12 B
+    scan_emit       read k 2K (+ r 4) + step scalar 4, write k~ 2K      = 516 / 520 B
+  phase 2 (whole)   read q, k, k~ 2K each + v 2V + beta 4, write o 2V   = 1284 B
+    chunk_tinv      read k, k~ 2K each + beta 4                         = 516 B
+                    flops: Gram 2 C K                                   = 16384
+    chunk_seq       read q, k, k~ 2K each + v 2V + beta 4, write o 2V   = 1284 B
+                    flops: K S^T, Q S^T, S update 3 x 2 K V, scores
+                    2 C K, Delta and O 2 x 2 C V                        = 147456
+Both phases sit below the MFMA ridge (2.5 PFLOP/s / 8 TB/s = 312 flop/B),
+so each kernel's roofline is HBM bandwidth (MI355X: 8 TB/s).  The bf16 MFMA
+fraction (peak 2.5 PFLOP/s dense) is reported beside it for phase 2.
+
+Per-kernel durations come from HIP events the library records on the launch
+stream around every kernel of the timed steps (osdn_profile_begin/end).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -33,36 +49,126 @@ if ROOT not in sys.path:
 METRIC = "OSDN fwd tokens/sec (phase1+phase2) at H=16,K=V=128,T=4096; % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+# where each kernel's source lives (for matching committed counter summaries)
+KERNEL_SOURCE = {
+    "scan_prep_kernel": "preconditioned_delta_rule_amd/csrc/precond_chunked.hip",
+    "scan_solve_kernel": "preconditioned_delta_rule_amd/csrc/precond_chunked.hip",
+    "scan_emit_kernel": "preconditioned_delta_rule_amd/csrc/precond_chunked.hip",
+    "chunk_tinv_kernel": "preconditioned_delta_rule_amd/csrc/chunk_wy.hip",
+    "chunk_seq_kernel": "preconditioned_delta_rule_amd/csrc/chunk_wy.hip",
+}
+COPY_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def phase_bytes(K, V, apf, gated, elem=2):
-    p1 = elem * K * 2 + 4 + (4 if apf else 0)
-    p2 = elem * (3 * K + V) + 4 + elem * V + (4 if gated else 0)
-    return p1, p2
+def kernel_work(name, K, V, C, apf, gated, elem=2):
+    """(algorithmic bytes, flops) per token-head of one kernel."""
+    r = 4 if apf else 0
+    g = 4 if gated else 0
+    if name == "scan_prep_kernel":
+        return elem * K + 4 + r, 0
+    if name == "scan_solve_kernel":
+        return 4 + 4 + r, 0
+    if name == "scan_emit_kernel":
+        return 2 * elem * K + 4 + r, 0
+    if name == "chunk_tinv_kernel":
+        return 2 * elem * K + 4 + g, 2 * C * K
+    if name == "chunk_seq_kernel":
+        return elem * (3 * K + V) + 4 + elem * V + g, 2 * (3 * K * V + C * K + 2 * C * V)
+    return 0, 0
 
 
-def phase2_flops(C, K, V):
-    return 2 * (3 * C * K + 2 * C * V + 3 * K * V)
+def source_sha(path):
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
-def cpu_baseline(inp, max_threads=None):
-    """The CPU oracle (fp64, one (b,h) sequence per thread) on the same
-    workload; returns tokens/s over the sample and the thread count."""
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+
+
+def load_traffic(workload, kernel):
+    """Measured HBM bytes per launch of `kernel` from the committed counter
+    summary, or None when there is none or the kernel source has changed."""
+    try:
+        with open(traffic_file(workload)) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get("kernels", {}).get(kernel)
+    if not ent or kernel not in KERNEL_SOURCE or ent.get("source_sha256") != source_sha(KERNEL_SOURCE[kernel]):
+        return None
+    return ent
+
+
+def pmc_summary(fetch_dir, write_dir, workload, command):
+    """Turn two rocprofv3 --pmc runs of `bench.py --pmc-pass` (FETCH_SIZE,
+    then WRITE_SIZE) into profiles/traffic_<workload>.json."""
+    def read(d, counter):
+        out = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for row in csv.DictReader(f):
+                    if row.get("Counter_Name") != counter:
+                        continue
+                    name = row["Kernel_Name"]
+                    key = None
+                    for k in KERNEL_SOURCE:
+                        if k in name:
+                            key = k
+                    if key is None and ("copy" in name.lower() or "elementwise" in name.lower()):
+                        key = "copy"
+                    if key:
+                        out.setdefault(key, []).append(float(row["Counter_Value"]))
+        return out
+    fetch, write = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
+    if "copy" not in fetch or "copy" not in write:
+        raise SystemExit("no calibration copy kernel in the counter runs")
+    # counters are in KiB per dispatch; the plain copy moves COPY_BYTES each way
+    fscale = COPY_BYTES / (1024.0 * float(np.median(fetch["copy"])))
+    wscale = COPY_BYTES / (1024.0 * float(np.median(write["copy"])))
+    kernels = {}
+    for k in KERNEL_SOURCE:
+        if k in fetch and k in write:
+            fb = float(np.median(fetch[k])) * 1024.0 * fscale
+            wb = float(np.median(write[k])) * 1024.0 * wscale
+            kernels[k] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb,
+                          "fetch_kib_raw": float(np.median(fetch[k])),
+                          "write_kib_raw": float(np.median(write[k])),
+                          "source": KERNEL_SOURCE[k], "source_sha256": source_sha(KERNEL_SOURCE[k])}
+    out = {"workload": workload, "fetch_scale": fscale, "write_scale": wscale,
+           "calibration": "plain device copy of %d MiB (torch copy_), counters per dispatch" %
+                          (COPY_BYTES >> 20),
+           "command": command, "kernels": kernels}
+    os.makedirs(os.path.dirname(traffic_file(workload)), exist_ok=True)
+    with open(traffic_file(workload), "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(out, indent=1, sort_keys=True))
+    return 0
+
+
+def cpu_baseline(inp, min_seconds):
+    """The CPU oracle (fp64, one (b,h) sequence per thread) on the whole
+    workload, repeated until `min_seconds` of wall time; returns tokens/s,
+    the thread count, the wall time and the repetitions."""
     import oracle
     B, T, H, _ = inp["k"].shape
-    threads = min(B * H, max_threads or oracle.default_threads())
+    threads = min(B * H, oracle.default_threads())
     p = inp["params"]
-    t0 = time.perf_counter()
-    oracle.forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["r"], inp["alpha"],
-                   eta=p["eta"], d_min=p["d_min"], d_max=p["d_max"], clamp=p["clamp"],
-                   eps=p["eps"], beta_aware=p["beta_aware"], q_scale=p["q_scale"],
-                   threads=threads)
-    wall = time.perf_counter() - t0
-    return B * T / wall, threads, wall
+    reps, wall = 0, 0.0
+    while wall < min_seconds or reps == 0:
+        t0 = time.perf_counter()
+        oracle.forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["r"], inp["alpha"],
+                       eta=p["eta"], d_min=p["d_min"], d_max=p["d_max"], clamp=p["clamp"],
+                       eps=p["eps"], beta_aware=p["beta_aware"], q_scale=p["q_scale"],
+                       threads=threads)
+        wall += time.perf_counter() - t0
+        reps += 1
+    return reps * B * T / wall, threads, wall, reps
 
 
 def main(argv=None):
@@ -75,9 +181,19 @@ def main(argv=None):
                     help="input sets rotated between steps (keeps the 256 MB MALL from "
                          "serving repeated reads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=16,
-                    help="(b,h) sequences of the workload the CPU oracle runs")
+    ap.add_argument("--cpu-seconds", type=float, default=1.5,
+                    help="minimum wall time of the CPU oracle run (whole workload, repeated)")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="run the steps and a %d MiB calibration copy for rocprofv3 --pmc; "
+                         "prints nothing" % (COPY_BYTES >> 20))
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs")
+    ap.add_argument("--pmc-command", default="",
+                    help="the commands that produced the --pmc-summary runs (recorded)")
     args = ap.parse_args(argv)
+
+    if args.pmc_summary:
+        return pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, args.pmc_command)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the OSDN forward shards over (b,h) with no "
@@ -87,7 +203,7 @@ def main(argv=None):
 
     import torch
     import preconditioned_delta_rule_amd as osdn
-    from workloads import make_inputs, sample_sequences
+    from workloads import make_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -102,6 +218,7 @@ def main(argv=None):
     C = p["chunk"]
     apf, gated = inp["r"] is not None, inp["alpha"] is not None
     tdt = torch.bfloat16 if p["dtype"] == "bf16" else torch.float32
+    code = osdn.BF16 if p["dtype"] == "bf16" else osdn.F32
     elem = 2 if p["dtype"] == "bf16" else 4
 
     def up(x, dt):
@@ -113,16 +230,8 @@ def main(argv=None):
                          beta=up(inp["beta"], torch.float32), r=up(inp["r"], torch.float32),
                          alpha=up(inp["alpha"], torch.float32),
                          o=torch.empty((B, T, H, V), dtype=tdt, device=dev),
-                         kt=torch.empty((B, T, H, K), dtype=tdt, device=dev),
-                         ws=torch.empty(osdn.fwd_workspace_bytes(B, T, H, K, V, dtype=(
-                             osdn.BF16 if p["dtype"] == "bf16" else osdn.F32), chunk=C),
-                             dtype=torch.uint8, device=dev),
-                         sws=torch.empty(osdn.precond_scan_workspace_bytes(B, T, H, K, dtype=(
-                             osdn.BF16 if p["dtype"] == "bf16" else osdn.F32)),
-                             dtype=torch.uint8, device=dev),
-                         cws=torch.empty(max(1, osdn.chunk_fwd_workspace_bytes(
-                             B, T, H, K, V, dtype=(osdn.BF16 if p["dtype"] == "bf16" else osdn.F32),
-                             chunk=C)), dtype=torch.uint8, device=dev),
+                         ws=torch.empty(osdn.fwd_workspace_bytes(B, T, H, K, V, dtype=code, chunk=C),
+                                        dtype=torch.uint8, device=dev),
                          S=torch.empty((B, H, V, K), dtype=torch.float32, device=dev),
                          d=torch.empty((B, H, K), dtype=torch.float32, device=dev)))
     kw = dict(chunk=C, eta=p["eta"], d_min=p["d_min"], d_max=p["d_max"], clamp=p["clamp"],
@@ -133,105 +242,89 @@ def main(argv=None):
         osdn.fwd(s["q"], s["k"], s["v"], s["beta"], s["r"], s["alpha"], None, None,
                  o=s["o"], S_out=s["S"], d_out=s["d"], workspace=s["ws"], **kw)
 
-    def scan(i, chunked=True):
-        s = sets[i % len(sets)]
-        osdn.precond_scan(s["k"], s["beta"], s["r"], None, eta=p["eta"], d_min=p["d_min"],
-                          d_max=p["d_max"], clamp=p["clamp"], eps=p["eps"],
-                          beta_aware=p["beta_aware"], k_tilde=s["kt"], d_out=s["d"],
-                          chunked=chunked, workspace=s["sws"] if chunked else None)
-
-    def scan_seq(i):
-        scan(i, chunked=False)
-
-    def chunk(i):
-        s = sets[i % len(sets)]
-        osdn.chunk_fwd(s["q"], s["k"], s["kt"], s["v"], s["beta"], s["alpha"], None, chunk=C,
-                       q_scale=p["q_scale"], o=s["o"], S_out=s["S"], workspace=s["cws"])
-
-    def timed(fn, n):
-        """Average device time of fn over n launches on the current stream
-        (HIP events recorded on that stream)."""
+    if args.pmc_pass:
+        for i in range(max(1, args.steps)):
+            step(i)
+        x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(n):
-            fn(i)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
+        return 0
 
     log("warmup", args.warmup)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     log("timing %d steps" % args.steps)
+    nsteps = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    ms_step = timed(step, args.steps)
+    e0.record()
+    launches = osdn.kernel_times(lambda: [step(i) for i in range(nsteps)], dev)
+    e1.record()
+    torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    log("step %.4f ms (wall %.3f s)" % (ms_step, wall))
-    # per-phase average durations: phase 1 is three kernels (prep, solve,
-    # emit), phase 2 one
-    for i in range(2):
-        scan(i)
-        chunk(i)
-        scan_seq(i)
-    ms_scan = timed(scan, args.steps)
-    ms_chunk = timed(chunk, args.steps)
-    ms_scan_seq = timed(scan_seq, max(1, args.steps // 5))
-    log("phase1 %.4f ms (token-by-token kernel %.4f ms)  phase2 %.4f ms"
-        % (ms_scan, ms_scan_seq, ms_chunk))
+    ms_step = e0.elapsed_time(e1) / nsteps
+    log("step %.4f ms (wall %.3f s for %d steps)" % (ms_step, wall, nsteps))
 
-    tokens = B * T
-    value = tokens / (ms_step * 1e-3)
+    # per-kernel durations over the timed steps
+    per = {}
+    for name, ms in launches:
+        per.setdefault(name, []).append(ms)
+    per_step = len(launches) // nsteps if nsteps else 0
+    step_ms = [sum(ms for _, ms in launches[i * per_step:(i + 1) * per_step]) for i in range(nsteps)]
     nth = B * T * H
-    b1, b2 = phase_bytes(K, V, apf, gated, elem)
-    f2 = phase2_flops(C, K, V)
-    p1_gbs = b1 * nth / (ms_scan * 1e-3) / 1e9
-    p2_gbs = b2 * nth / (ms_chunk * 1e-3) / 1e9
-    p2_tfl = f2 * nth / (ms_chunk * 1e-3) / 1e12
-    phases = {
-        "precond_scan": {"kernel": "scan_prep_kernel + scan_solve_kernel + scan_emit_kernel",
-                         "ms": ms_scan, "bound": "hbm", "bytes_per_token_head": b1,
-                         "GB/s": p1_gbs, "hbm_frac": p1_gbs / HBM_PEAK_GBS,
-                         "token_by_token_kernel_ms": ms_scan_seq},
-        "chunk_fwd": {"kernel": "chunk_mfma_kernel", "ms": ms_chunk, "bound": "hbm",
-                      "bytes_per_token_head": b2, "GB/s": p2_gbs,
-                      "hbm_frac": p2_gbs / HBM_PEAK_GBS,
-                      "flops_per_token_head": f2, "flop_count": "dense chunk form",
-                      "TFLOP/s": p2_tfl, "mfma_bf16_frac": p2_tfl / MFMA_BF16_PEAK_TFLOPS},
-    }
-    dom = "precond_scan" if ms_scan >= ms_chunk else "chunk_fwd"
-    dph = phases[dom]
-    roofline = {"bound": "hbm", "kernel": dph["kernel"], "achieved": dph["GB/s"],
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dph["GB/s"] / HBM_PEAK_GBS,
-                "traffic": None}
+    kernels = {}
+    for name, vals in per.items():
+        ms = float(np.mean(vals))
+        nbytes, flops = kernel_work(name, K, V, C, apf, gated, elem)
+        gbs = nbytes * nth / (ms * 1e-3) / 1e9 if ms > 0 else None
+        ent = {"ms": ms, "launches_per_step": len(vals) / nsteps, "ms_median": float(np.median(vals)),
+               "bound": "hbm", "bytes_per_token_head": nbytes, "GB/s": gbs,
+               "hbm_frac": gbs / HBM_PEAK_GBS if gbs else None}
+        if flops:
+            ent["flops_per_token_head"] = flops
+            ent["TFLOP/s"] = flops * nth / (ms * 1e-3) / 1e12
+            ent["mfma_bf16_frac"] = ent["TFLOP/s"] / MFMA_BF16_PEAK_TFLOPS
+        kernels[name] = ent
+        log("  %-20s %.4f ms  %.0f GB/s" % (name, ms, gbs or 0))
+    dom = max(kernels, key=lambda n: kernels[n]["ms"] * kernels[n]["launches_per_step"])
+    dk = kernels[dom]
+    tr = load_traffic(args.workload, dom)
+    traffic = tr["bytes_per_launch"] / (dk["ms"] * 1e-3) / 1e9 if tr else None
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": dk["GB/s"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": dk["hbm_frac"], "traffic": traffic,
+                "algorithmic_bytes_per_launch": dk["bytes_per_token_head"] * nth,
+                "measured_bytes_per_launch": tr["bytes_per_launch"] if tr else None}
+    p1 = sum(kernels[n]["ms"] * kernels[n]["launches_per_step"] for n in kernels if n.startswith("scan_"))
+    p2 = sum(kernels[n]["ms"] * kernels[n]["launches_per_step"] for n in kernels if n.startswith("chunk_"))
 
     cpu = None
     if not args.no_cpu_baseline:
-        nseq = min(args.cpu_sample_seqs, B * H)
-        pairs = [(i // H, i % H) for i in range(0, B * H, max(1, (B * H) // nseq))][:nseq]
-        sub = sample_sequences(inp, pairs)
-        log("cpu oracle on %d sequences x %d tokens" % (len(pairs), T))
-        tps, threads, cwall = cpu_baseline(sub)
-        # the sample is len(pairs) single-head sequences: tps counts token-heads,
-        # a token of the workload carries all H heads
-        value_cpu = tps / H
-        cpu = {"value": value_cpu, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-               "sample": "%d of %d (b,h) sequences x %d tokens (fp64 sequential oracle, one "
-                         "sequence per thread), %.2f s wall; tokens/s scaled to all %d "
-                         "heads" % (len(pairs), B * H, T, cwall, H)}
-        log("cpu oracle %.1f s" % cwall)
+        log("cpu oracle on the whole workload (%d sequences x %d tokens)" % (B * H, T))
+        tps, threads, cwall, reps = cpu_baseline(inp, args.cpu_seconds)
+        cpu = {"value": tps, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": "whole workload: %d (b,h) sequences x %d tokens, fp64 sequential oracle "
+                         "(both phases), one sequence per thread, %d run(s) in %.2f s wall" %
+                         (B * H, T, reps, cwall)}
+        log("cpu oracle %.2f s" % cwall)
 
     out = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "metric": METRIC, "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": nsteps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": p["dtype"],
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": V,
                    "chunk": C, "apf": apf, "gated": gated, "seed": spec["seed"],
                    "input_copies": len(sets)},
-        "roofline": roofline, "phases": phases, "cpu_baseline": cpu,
+        "roofline": roofline, "cpu_baseline": cpu,
+        "phases": {"precond_scan_ms": p1, "chunk_fwd_ms": p2,
+                   "step_device_ms_median": float(np.median(step_ms)) if step_ms else None,
+                   "step_device_ms_p10": float(np.percentile(step_ms, 10)) if step_ms else None,
+                   "step_device_ms_p90": float(np.percentile(step_ms, 90)) if step_ms else None},
+        "kernels": kernels,
     }
     print(json.dumps(out), flush=True)
     return 0

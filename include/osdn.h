@@ -187,6 +187,21 @@ osdn_status osdn_fwd(const osdn_desc *desc, const void *q, const void *k,
                      void *o, float *S_out, float *d_out, void *k_tilde_out,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Launch profile (measurement aid).  osdn_profile_begin records a HIP event on
+ * `stream`; until osdn_profile_end, every kernel the library launches from
+ * the calling thread records another event on its stream right after the
+ * launch (at most 1024 launches are recorded).  osdn_profile_end waits for the
+ * last event and writes, for up to max_entries launches in order, the kernel
+ * name (static string) and the device time in milliseconds from the previous
+ * event to this launch's event -- the kernel's duration when the launches are
+ * queued back to back on one stream.  *count receives the number of launches
+ * recorded.  Ending a profile that was not begun returns OSDN_EINVAL.
+ */
+osdn_status osdn_profile_begin(void *stream);
+osdn_status osdn_profile_end(const char **names, float *ms, int max_entries,
+                             int *count);
+
 /* Name of a status code (static string). */
 const char *osdn_status_str(int status);
 

@@ -20,7 +20,7 @@ import os
 import torch
 
 __all__ = ["precond_scan", "precond_scan_workspace_bytes", "scan_counters", "chunk_fwd",
-           "chunk_fwd_workspace_bytes", "fwd", "fwd_workspace_bytes", "fwd_scan_counters", "Desc", "OsdnError",
+           "chunk_fwd_workspace_bytes", "fwd", "kernel_times", "fwd_workspace_bytes", "fwd_scan_counters", "Desc", "OsdnError",
            "library_path", "load", "F32", "BF16"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -33,7 +33,7 @@ OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 SYMBOLS = ("osdn_desc_init", "osdn_validate", "osdn_precond_scan",
            "osdn_precond_scan_workspace_bytes", "osdn_precond_scan_counters_offset",
            "osdn_chunk_fwd", "osdn_chunk_fwd_workspace_bytes", "osdn_fwd_workspace_bytes",
-           "osdn_fwd", "osdn_status_str",
+           "osdn_fwd", "osdn_profile_begin", "osdn_profile_end", "osdn_status_str",
            "osdn_last_error", "osdn_version")
 
 
@@ -81,12 +81,15 @@ def load():
     lib.osdn_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.osdn_fwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp, vp,
                              ctypes.c_size_t, vp]
+    lib.osdn_profile_begin.argtypes = [vp]
+    lib.osdn_profile_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
+                                     ci, ctypes.POINTER(ci)]
     lib.osdn_status_str.argtypes = [ci]
     lib.osdn_status_str.restype = ctypes.c_char_p
     lib.osdn_last_error.argtypes = []
     lib.osdn_last_error.restype = ctypes.c_char_p
     for name in ("osdn_desc_init", "osdn_validate", "osdn_precond_scan", "osdn_chunk_fwd",
-                 "osdn_fwd", "osdn_version"):
+                 "osdn_fwd", "osdn_profile_begin", "osdn_profile_end", "osdn_version"):
         getattr(lib, name).restype = ci
     _lib = lib
     return lib
@@ -286,3 +289,20 @@ def fwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, chunk=64, eta=0.
                            _ptr(k_tilde_out), _ptr(workspace),
                            ctypes.c_size_t(_nbytes(workspace)), _stream(dev)))
     return o, S_out, d_out
+
+
+def kernel_times(fn, device=None):
+    """Run fn() with a launch profile open on the current stream; returns
+    [(kernel_name, milliseconds)] for every kernel the library launched."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    lib = load()
+    _check(lib.osdn_profile_begin(_stream(dev)))
+    try:
+        fn()
+    finally:
+        cap = 1024
+        names = (ctypes.c_char_p * cap)()
+        ms = (ctypes.c_float * cap)()
+        n = ctypes.c_int(0)
+        _check(lib.osdn_profile_end(names, ms, cap, ctypes.byref(n)))
+    return [(names[i].decode(), float(ms[i])) for i in range(min(n.value, cap))]

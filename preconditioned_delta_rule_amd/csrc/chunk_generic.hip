@@ -15,6 +15,7 @@
 // the chunk operands live in LDS as fp32.
 #include "device_common.h"
 #include "kernels.h"
+#include "profile.h"
 
 namespace osdn {
 
@@ -205,6 +206,7 @@ static hipError_t launch_gen(const ChunkArgs &a, hipStream_t s) {
     hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     hipLaunchKernelGGL(kern, grid, block, shm, s, a, lay, ntiles);
   }
+  prof_mark(s, "chunk_generic_kernel");
   return hipGetLastError();
 }
 

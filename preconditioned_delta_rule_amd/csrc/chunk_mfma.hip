@@ -29,6 +29,7 @@
 // straight from global memory into registers in MFMA operand layout.
 #include "kernels.h"
 #include "mfma_common.h"
+#include "profile.h"
 
 namespace osdn {
 
@@ -507,6 +508,7 @@ hipError_t launch_vt(const ChunkArgs &a, hipStream_t s) {
     else
       hipLaunchKernelGGL((chunk_mfma_kernel<VT, false, false>), grid, block, 0, s, a);
   }
+  prof_mark(s, "chunk_mfma_kernel");
   return hipGetLastError();
 }
 

@@ -34,6 +34,7 @@
 // only 8-bit roundings.
 #include "kernels.h"
 #include "mfma_common.h"
+#include "profile.h"
 
 namespace osdn {
 
@@ -622,11 +623,14 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
 template <bool GATED, bool KRES>
 void launch_both(const ChunkArgs &a, bf16 *tw, int64_t N, hipStream_t s) {
   const int64_t nseq = a.B * a.H;
-  if (N > 0)
+  if (N > 0) {
     hipLaunchKernelGGL((chunk_tinv_kernel<GATED, KRES>), dim3((unsigned)(nseq * N)), dim3(256), 0, s, a, tw, N);
+    prof_mark(s, "chunk_tinv_kernel");
+  }
   const int64_t groups = (nseq + 7) / 8;
   hipLaunchKernelGGL((chunk_seq_kernel<GATED, KRES>), dim3((unsigned)(groups * 8 * NT)), dim3(512), 0, s, a,
                      (const bf16 *)tw, N);
+  prof_mark(s, "chunk_seq_kernel");
 }
 
 }  // namespace

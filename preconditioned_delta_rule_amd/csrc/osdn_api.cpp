@@ -11,10 +11,21 @@
 #include <string>
 
 #include "kernels.h"
+#include "profile.h"
 
 namespace {
 
 thread_local std::string g_last_error;
+
+// Per-thread launch profile (osdn_profile_begin / osdn_profile_end).
+constexpr int PROF_MAX = 1024;
+struct Profile {
+  bool open = false;
+  int n = 0;
+  hipEvent_t ev[PROF_MAX + 1] = {};
+  const char *name[PROF_MAX] = {};  // events live until the process ends
+};
+thread_local Profile g_prof;
 
 osdn_status fail(osdn_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 osdn_status fail(osdn_status st, const char *fmt, ...) {
@@ -164,7 +175,42 @@ size_t chunk_work_bytes(const osdn_desc *d) {
 
 }  // namespace
 
+namespace osdn {
+void prof_mark(hipStream_t s, const char *kernel) {
+  Profile &p = g_prof;
+  if (!p.open || p.n >= PROF_MAX) return;
+  if (!p.ev[p.n + 1] && hipEventCreate(&p.ev[p.n + 1]) != hipSuccess) return;
+  if (hipEventRecord(p.ev[p.n + 1], s) != hipSuccess) return;
+  p.name[p.n++] = kernel;
+}
+}  // namespace osdn
+
 extern "C" {
+
+osdn_status osdn_profile_begin(void *stream) {
+  Profile &p = g_prof;
+  if (!p.ev[0]) OSDN_TRY(hip_status(hipEventCreate(&p.ev[0]), "profile event"));
+  OSDN_TRY(hip_status(hipEventRecord(p.ev[0], static_cast<hipStream_t>(stream)), "profile event"));
+  p.open = true;
+  p.n = 0;
+  return ok();
+}
+
+osdn_status osdn_profile_end(const char **names, float *ms, int max_entries, int *count) {
+  Profile &p = g_prof;
+  if (!p.open) return fail(OSDN_EINVAL, "no profile is open on this thread");
+  p.open = false;
+  if (count) *count = p.n;
+  if (p.n == 0) return ok();
+  OSDN_TRY(hip_status(hipEventSynchronize(p.ev[p.n]), "profile event"));
+  for (int i = 0; i < p.n && i < max_entries; ++i) {
+    float t = 0.0f;
+    OSDN_TRY(hip_status(hipEventElapsedTime(&t, p.ev[i], p.ev[i + 1]), "profile event"));
+    if (names) names[i] = p.name[i];
+    if (ms) ms[i] = t;
+  }
+  return ok();
+}
 
 int osdn_version(void) { return (1 << 16) | 0; }
 

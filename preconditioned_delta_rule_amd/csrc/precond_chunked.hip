@@ -31,6 +31,7 @@
 //        from the chunk's start and writes k~_t = d_t (.) k_t (and/or the
 //        bf16 residual (d_t - 1) (.) k_t).
 #include "kernels.h"
+#include "profile.h"
 #include "scan_common.h"
 
 namespace osdn {
@@ -550,6 +551,7 @@ void launch_emit(const ScanArgs &a, const ScanWork &w, int64_t N, hipStream_t s)
     hipLaunchKernelGGL((scan_emit_kernel<TIn, EPL, FULL, HAS_R, false, true>), grid, block, 0, s, a, w, N);
   else
     hipLaunchKernelGGL((scan_emit_kernel<TIn, EPL, FULL, HAS_R, true, false>), grid, block, 0, s, a, w, N);
+  prof_mark(s, "scan_emit_kernel");
 }
 
 template <typename TIn, int EPL, bool FULL, bool HAS_R>
@@ -559,6 +561,7 @@ hipError_t launch_all(const ScanArgs &a, const ScanWork &w, hipStream_t s) {
   if (N > 0) {
     hipLaunchKernelGGL((scan_prep_kernel<TIn, EPL, FULL, HAS_R>), dim3((unsigned)(nseq * N)), dim3(64), 0, s,
                        a, w, N);
+    prof_mark(s, "scan_prep_kernel");
   }
   constexpr bool PF = Row<TIn, EPL, FULL>::WORDS <= 2;
   constexpr size_t shm = solve_lds_bytes<TIn, EPL>();
@@ -567,6 +570,7 @@ hipError_t launch_all(const ScanArgs &a, const ScanWork &w, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)nseq), dim3(64), shm, s, a, w, N);
+  prof_mark(s, "scan_solve_kernel");
   if (N > 0) launch_emit<TIn, EPL, FULL, HAS_R>(a, w, N, s);
   return hipGetLastError();
 }

@@ -21,6 +21,7 @@
 // bf16/f32 words) while the current group is processed; beta and r arrive as
 // one lane-indexed vector load per group and are broadcast with readlane.
 #include "kernels.h"
+#include "profile.h"
 #include "scan_common.h"
 
 namespace osdn {
@@ -157,6 +158,7 @@ static void launch_out(const ScanArgs &a, hipStream_t s) {
     hipLaunchKernelGGL((precond_scan_kernel<TIn, EPL, FULL, HAS_R, false, true>), grid, block, 0, s, a);
   else
     hipLaunchKernelGGL((precond_scan_kernel<TIn, EPL, FULL, HAS_R, true, false>), grid, block, 0, s, a);
+  prof_mark(s, "precond_scan_kernel");
 }
 
 template <typename TIn, int EPL, bool FULL>

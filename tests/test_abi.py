@@ -152,3 +152,9 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(osdn, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="libosdn.so not found"):
         osdn.load()
+
+
+def test_profile_end_without_begin_is_rejected(lib):
+    n = ctypes.c_int(-1)
+    st = lib.osdn_profile_end(None, None, 0, ctypes.byref(n))
+    assert st == osdn.EINVAL and "no profile" in lib.osdn_last_error().decode()
