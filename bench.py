@@ -2,9 +2,9 @@
 """OSDN forward throughput on one MI355X.
 
 One step = one full forward of one layer through the C ABI entry point
-osdn_fwd: phase 1 (preconditioner scan: scan_prep, scan_solve and scan_emit
-kernels) and phase 2 (chunkwise WY delta rule: chunk_tinv and chunk_seq
-kernels) over a batch of synthetic inputs already resident in HBM.  The
+osdn_fwd: phase 1 (preconditioner scan: scan_prep and scan_solve kernels)
+and phase 2 (chunkwise WY delta rule: chunk_tinv, which also replays d to
+form the write-key residual, and chunk_seq) over a batch of synthetic inputs already resident in HBM.  The
 default workload is the 1.3B-shaped layer: B=4, H=16, T=4096, K=V=128, bf16
 inputs, fp32 state, chunk 64, APF retention on.
 
@@ -17,7 +17,8 @@ alpha where present), used for the roofline figures:
     scan_solve      per-token scalars beta (+ r) and the key norm       =   8 /  12 B
     scan_emit       read k 2K (+ r 4) + step scalar 4, write k~ 2K      = 516 / 520 B
   phase 2 (whole)   read q, k, k~ 2K each + v 2V + beta 4, write o 2V   = 1284 B
-    chunk_tinv      read k, k~ 2K each + beta 4                         = 516 B
+    chunk_tinv      read k 2K, step scalar 4, beta 4 (+ r 4), write the
+                    residual E 2K (the phase-1 replay is folded in)     = 520 / 524 B
                     flops: Gram 2 C K                                   = 16384
     chunk_seq       read q, k, k~ 2K each + v 2V + beta 4, write o 2V   = 1284 B
                     flops: K S^T, Q S^T, S update 3 x 2 K V, scores
@@ -75,7 +76,9 @@ def kernel_work(name, K, V, C, apf, gated, elem=2):
     if name == "scan_emit_kernel":
         return 2 * elem * K + 4 + r, 0
     if name == "chunk_tinv_kernel":
-        return 2 * elem * K + 4 + g, 2 * C * K
+        # osdn_fwd (bf16): reads k, forms and writes the residual E = (d-1) k
+        # from the phase-1 step scalars (4 B) and retention, reads beta
+        return 2 * elem * K + 4 + 4 + r + g, 2 * C * K
     if name == "chunk_seq_kernel":
         return elem * (3 * K + V) + 4 + elem * V + g, 2 * (3 * K * V + C * K + 2 * C * V)
     return 0, 0

@@ -61,12 +61,20 @@ struct TinvLay {
   static constexpr int A = R0;                   // f32 [C][AP]
   static constexpr int BETA = A + C * AP * 4;    // f32 [C]
   static constexpr int G = BETA + C * 4;         // f32 [C]
-  static constexpr int TOTAL = G + C * 4;
+  static constexpr int SC = G + C * 4;           // f32 [C] phase-1 step scalars (EMIT)
+  static constexpr int SR = SC + C * 4;          // f32 [C] retention (EMIT)
+  static constexpr int TOTAL = SR + C * 4;
   static_assert(X + C * CP * 2 <= R0, "inverse scratch must fit in the key rows");
 };
 
-template <bool GATED, bool KRES>
-__global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout, int64_t N) {
+// EMIT (residual form only): the chunk's residual E = (d - 1) (.) k is formed
+// here from the phase-1 sweep's chunk start and step scalars -- the replay
+// d_{t+1} = clip(r_t d_t + c_t k_t^2), the same fp32 expressions as the
+// phase-1 emit kernel -- and written for the sweep kernel, so phase 1 need
+// not write it and this kernel need not read it.
+template <bool GATED, bool KRES, bool EMIT>
+__global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout, int64_t N, EmitArgs em) {
+  static_assert(KRES || !EMIT, "the folded replay produces the residual form");
   typedef TinvLay L;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
   bf16(*sKh)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::KH);
@@ -77,6 +85,8 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
   float(*sA)[AP] = reinterpret_cast<float(*)[AP]>(smem + L::A);
   float *sBeta = reinterpret_cast<float *>(smem + L::BETA);
   float *sG = reinterpret_cast<float *>(smem + L::G);
+  float *sC = reinterpret_cast<float *>(smem + L::SC);
+  float *sR = reinterpret_cast<float *>(smem + L::SR);
 
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -91,6 +101,53 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
   const int64_t tstride = H * KD;
   const int64_t base = (b * T + t0) * tstride + h * KD;  // token t0 of this (b,h)
 
+  bf16x8 kf[4];  // wave w's key rows as A operands (token 16 w + l16)
+  if constexpr (EMIT) {
+    // key rows into LDS (16-byte vectors, 16 threads per row; zero past T),
+    // step scalars and retention of the chunk's tokens
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int vi = tid + 256 * p, i = vi >> 4, c8 = 8 * (vi & 15);
+      const bf16x8 x = ld8(gk + base + (i < Lc ? i : 0) * tstride + c8);
+      *reinterpret_cast<bf16x8 *>(&sKl[i][c8]) = i < Lc ? x : bf16x8{};
+    }
+    if (tid < C) {
+      const int64_t gi = (b * T + t0 + (tid < Lc ? tid : 0)) * H + h;
+      sC[tid] = em.cstep[gi];
+      sR[tid] = em.r ? em.r[gi] : 1.0f;
+    }
+    __syncthreads();
+    // one thread per coordinate: replay d through the chunk, writing E
+    if (tid < KD) {
+      const int c = tid;
+      const bool pinned = em.pin[seq * N + n] == 2;
+      float d = pinned ? em.d_min : em.dstart[(seq * N + n) * KD + c];
+      const float lo = em.clamp ? em.d_min : -INFINITY, hi = em.clamp ? em.d_max : INFINITY;
+      auto step = [&](int u) {
+        const float kv = to_f32(sKl[u][c]);
+        sKh[u][c] = to_bf16((d - 1.0f) * kv);  // d - 1 is exact on [0.5, 2]
+        d = fminf(fmaxf(fmaf(sC[u], kv * kv, sR[u] * d), lo), hi);
+      };
+      if (Lc == C) {
+        // straight-line: the LDS reads, which do not depend on d, run ahead
+#pragma unroll
+        for (int u = 0; u < C; ++u) step(u);
+      } else {
+        for (int u = 0; u < Lc; ++u) step(u);
+        for (int u = Lc; u < C; ++u) sKh[u][c] = to_bf16(0.0f);
+      }
+    }
+    __syncthreads();
+    // the residual rows, for the sweep kernel
+    bf16 *res = em.res + base;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int vi = tid + 256 * p, i = vi >> 4, c8 = 8 * (vi & 15);
+      if (i < Lc) *reinterpret_cast<bf16x8 *>(res + i * tstride + c8) = ld8(&sKh[i][c8]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) kf[kk] = ld8(&sKl[16 * w + l16][32 * kk + 8 * lq]);
+  } else {
   // write keys into LDS: thread -> token l, columns [32 w, 32 w + 32).  With
   // the residual form k~ = k + E both k and E are exact bf16 operands, so
   // the Gram is K E^T + K K^T; otherwise the bf16 k~ rows themselves.
@@ -107,8 +164,6 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
       }
     }
   }
-  // wave w's key rows as A operands (token 16 w + l16)
-  bf16x8 kf[4];
   {
     const int m = 16 * w + l16;
     const bool ok = m < Lc;
@@ -118,6 +173,7 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
       const bf16x8 x = ld8(gk + off + 32 * kk);
       kf[kk] = ok ? x : bf16x8{};
     }
+  }
   }
   if (w == 0) {
     const bool ok = l < Lc;
@@ -621,11 +677,20 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
 }
 
 template <bool GATED, bool KRES>
-void launch_both(const ChunkArgs &a, bf16 *tw, int64_t N, hipStream_t s) {
+void launch_both(const ChunkArgs &a, bf16 *tw, int64_t N, hipStream_t s, const EmitArgs *em) {
   const int64_t nseq = a.B * a.H;
   if (N > 0) {
-    hipLaunchKernelGGL((chunk_tinv_kernel<GATED, KRES>), dim3((unsigned)(nseq * N)), dim3(256), 0, s, a, tw, N);
-    prof_mark(s, "chunk_tinv_kernel");
+    const dim3 grid((unsigned)(nseq * N)), block(256);
+    if constexpr (KRES) {
+      if (em) {
+        hipLaunchKernelGGL((chunk_tinv_kernel<GATED, true, true>), grid, block, 0, s, a, tw, N, *em);
+        prof_mark(s, "chunk_tinv_kernel");
+      }
+    }
+    if (!em) {
+      hipLaunchKernelGGL((chunk_tinv_kernel<GATED, KRES, false>), grid, block, 0, s, a, tw, N, EmitArgs{});
+      prof_mark(s, "chunk_tinv_kernel");
+    }
   }
   const int64_t groups = (nseq + 7) / 8;
   hipLaunchKernelGGL((chunk_seq_kernel<GATED, KRES>), dim3((unsigned)(groups * 8 * NT)), dim3(512), 0, s, a,
@@ -640,20 +705,21 @@ size_t chunk_wy_work_bytes(int64_t B, int64_t T, int64_t H) {
   return (size_t)(B * H * N) * C * C * 2;
 }
 
-hipError_t launch_chunk_wy(const ChunkArgs &a, void *work, hipStream_t s) {
+hipError_t launch_chunk_wy(const ChunkArgs &a, void *work, hipStream_t s, const EmitArgs *em) {
   if (a.B * a.H == 0) return hipSuccess;
+  if (em && (!a.kt_is_res || C != SCAN_CHUNK)) return hipErrorInvalidValue;
   const int64_t N = (a.T + C - 1) / C;
   bf16 *tw = static_cast<bf16 *>(work);
   if (a.alpha) {
     if (a.kt_is_res)
-      launch_both<true, true>(a, tw, N, s);
+      launch_both<true, true>(a, tw, N, s, em);
     else
-      launch_both<true, false>(a, tw, N, s);
+      launch_both<true, false>(a, tw, N, s, nullptr);
   } else {
     if (a.kt_is_res)
-      launch_both<false, true>(a, tw, N, s);
+      launch_both<false, true>(a, tw, N, s, em);
     else
-      launch_both<false, false>(a, tw, N, s);
+      launch_both<false, false>(a, tw, N, s, nullptr);
   }
   return hipGetLastError();
 }

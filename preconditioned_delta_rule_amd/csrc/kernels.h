@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.h"
+
 namespace osdn {
 
 struct ScanArgs {
@@ -48,13 +50,28 @@ struct ScanWork {
 constexpr int SCAN_CHUNK = 64;
 size_t scan_work_bytes(int64_t B, int64_t T, int64_t H, int64_t K);
 ScanWork scan_work_layout(void *base, int64_t B, int64_t T, int64_t H, int64_t K);
-hipError_t launch_precond_scan_chunked(const ScanArgs &a, const ScanWork &w, bool bf16, hipStream_t s);
+// emit = false leaves the write keys to the caller (see EmitArgs).
+hipError_t launch_precond_scan_chunked(const ScanArgs &a, const ScanWork &w, bool bf16, hipStream_t s,
+                                       bool emit = true);
+
+// The phase-1 replay of one chunk (d from the chunk start through the step
+// scalars, writing the residual (d - 1) (.) k), folded into the first
+// phase-2 kernel when the residual is needed only by phase 2.
+struct EmitArgs {
+  const float *cstep;   // [B,T,H] step scalars from the chunked sweep
+  const float *dstart;  // [B,H,N,K] d at each chunk start
+  const int *pin;       // [B,H,N]; 2 = the chunk starts from d_min (no stored start)
+  const float *r;       // [B,T,H] retention, or null
+  bf16 *res;            // OUT [B,T,H,K] residual, read back by the sweep kernel
+  float d_min, d_max;
+  int clamp;
+};
 hipError_t launch_chunk_generic(const ChunkArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s);
 // Two-kernel MFMA path (same shapes as launch_chunk_mfma): the per-chunk
 // (I + A)^-1 of every chunk goes through a bf16 workspace [B,H,N,64,64].
 size_t chunk_wy_work_bytes(int64_t B, int64_t T, int64_t H);
-hipError_t launch_chunk_wy(const ChunkArgs &a, void *work, hipStream_t s);
+hipError_t launch_chunk_wy(const ChunkArgs &a, void *work, hipStream_t s, const EmitArgs *emit = nullptr);
 
 // Shape coverage of the specialised MFMA path (bf16, K = V = 128, C = 64).
 bool chunk_mfma_supported(const ChunkArgs &a, bool bf16);

@@ -372,11 +372,27 @@ osdn_status osdn_fwd(const osdn_desc *d, const void *q, const void *k, const voi
     ca.kt = ws;
   }
   const size_t scan_bytes = osdn::scan_work_bytes(d->B, d->T, d->H, d->K);
-  OSDN_TRY(hip_status(osdn::launch_precond_scan_chunked(
-                          sa, osdn::scan_work_layout(ws + fwd_keys_bytes(d), d->B, d->T, d->H, d->K),
-                          d->dtype == OSDN_BF16, s),
+  const osdn::ScanWork sw = osdn::scan_work_layout(ws + fwd_keys_bytes(d), d->B, d->T, d->H, d->K);
+  void *cw = chunk_work_bytes(d) ? ws + fwd_keys_bytes(d) + scan_bytes : nullptr;
+  // bf16 on the matrix cores without k_tilde_out: the residual is formed by
+  // the first phase-2 kernel, which replays d itself (one pass over k fewer)
+  const bool fold = d->dtype == OSDN_BF16 && cw && !k_tilde_out;
+  OSDN_TRY(hip_status(osdn::launch_precond_scan_chunked(sa, sw, d->dtype == OSDN_BF16, s, !fold),
                       "phase-1 launch"));
-  OSDN_TRY(run_chunk(d, ca, chunk_work_bytes(d) ? ws + fwd_keys_bytes(d) + scan_bytes : nullptr, s));
+  if (fold) {
+    osdn::EmitArgs em;
+    em.cstep = sw.cstep;
+    em.dstart = sw.dstart;
+    em.pin = sw.pin;
+    em.r = r;
+    em.res = static_cast<osdn::bf16 *>(workspace);
+    em.d_min = d->d_min;
+    em.d_max = d->d_max;
+    em.clamp = d->clamp ? 1 : 0;
+    OSDN_TRY(hip_status(osdn::launch_chunk_wy(ca, cw, s, &em), "phase-2 launch"));
+  } else {
+    OSDN_TRY(run_chunk(d, ca, cw, s));
+  }
   return ok();
 }
 

@@ -555,7 +555,7 @@ void launch_emit(const ScanArgs &a, const ScanWork &w, int64_t N, hipStream_t s)
 }
 
 template <typename TIn, int EPL, bool FULL, bool HAS_R>
-hipError_t launch_all(const ScanArgs &a, const ScanWork &w, hipStream_t s) {
+hipError_t launch_all(const ScanArgs &a, const ScanWork &w, hipStream_t s, bool emit) {
   const int64_t N = (a.T + CH - 1) / CH;
   const int64_t nseq = a.B * a.H;
   if (N > 0) {
@@ -571,20 +571,20 @@ hipError_t launch_all(const ScanArgs &a, const ScanWork &w, hipStream_t s) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)nseq), dim3(64), shm, s, a, w, N);
   prof_mark(s, "scan_solve_kernel");
-  if (N > 0) launch_emit<TIn, EPL, FULL, HAS_R>(a, w, N, s);
+  if (N > 0 && emit) launch_emit<TIn, EPL, FULL, HAS_R>(a, w, N, s);
   return hipGetLastError();
 }
 
 template <typename TIn, int EPL, bool FULL>
-hipError_t launch_r(const ScanArgs &a, const ScanWork &w, hipStream_t s) {
-  return a.r ? launch_all<TIn, EPL, FULL, true>(a, w, s) : launch_all<TIn, EPL, FULL, false>(a, w, s);
+hipError_t launch_r(const ScanArgs &a, const ScanWork &w, hipStream_t s, bool e) {
+  return a.r ? launch_all<TIn, EPL, FULL, true>(a, w, s, e) : launch_all<TIn, EPL, FULL, false>(a, w, s, e);
 }
 
 template <typename TIn>
-hipError_t launch_typed(const ScanArgs &a, const ScanWork &w, hipStream_t s) {
-  if (a.K <= 64) return a.K == 64 ? launch_r<TIn, 1, true>(a, w, s) : launch_r<TIn, 1, false>(a, w, s);
-  if (a.K <= 128) return a.K == 128 ? launch_r<TIn, 2, true>(a, w, s) : launch_r<TIn, 2, false>(a, w, s);
-  return a.K == 256 ? launch_r<TIn, 4, true>(a, w, s) : launch_r<TIn, 4, false>(a, w, s);
+hipError_t launch_typed(const ScanArgs &a, const ScanWork &w, hipStream_t s, bool e) {
+  if (a.K <= 64) return a.K == 64 ? launch_r<TIn, 1, true>(a, w, s, e) : launch_r<TIn, 1, false>(a, w, s, e);
+  if (a.K <= 128) return a.K == 128 ? launch_r<TIn, 2, true>(a, w, s, e) : launch_r<TIn, 2, false>(a, w, s, e);
+  return a.K == 256 ? launch_r<TIn, 4, true>(a, w, s, e) : launch_r<TIn, 4, false>(a, w, s, e);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -612,9 +612,10 @@ ScanWork scan_work_layout(void *base, int64_t B, int64_t T, int64_t H, int64_t K
   return w;
 }
 
-hipError_t launch_precond_scan_chunked(const ScanArgs &a, const ScanWork &w, bool is_bf16, hipStream_t s) {
+hipError_t launch_precond_scan_chunked(const ScanArgs &a, const ScanWork &w, bool is_bf16, hipStream_t s,
+                                       bool emit) {
   if (a.B * a.H == 0) return hipSuccess;
-  return is_bf16 ? launch_typed<bf16>(a, w, s) : launch_typed<float>(a, w, s);
+  return is_bf16 ? launch_typed<bf16>(a, w, s, emit) : launch_typed<float>(a, w, s, emit);
 }
 
 }  // namespace osdn
