@@ -65,7 +65,8 @@ typedef enum {
 /*
  * Problem description.  Arguments follow the paper's statement of the
  * problem (Algorithm 1's inputs; the chunk interface of Appendix C).
- *   B, T, H     batch, tokens, heads; B, H >= 1, T >= 0.
+ *   B, T, H     batch, tokens, heads; B, H >= 1, T >= 0; H <= 65536 for
+ *               phase 2 (OSDN_EUNSUPPORTED above it).
  *   K, V        key / value head dims; 1 <= K <= 256 for phase 1,
  *               1 <= K, V <= 128 for phase 2.
  *   chunk       chunk length C of the WY form, 1 <= C <= 64.  The result does

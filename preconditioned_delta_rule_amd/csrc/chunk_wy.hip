@@ -48,6 +48,7 @@ constexpr int NT = VD / VT;
 constexpr int KP = KD + 8; // LDS pitch (bf16) of 128-wide rows
 constexpr int CP = C + 8;  // LDS pitch (bf16) of 64-wide rows
 constexpr int AP = C + 4;  // LDS pitch (f32) of the Gram
+constexpr int SP = VT + 24; // LDS pitch (bf16) of the transposed state tile
 
 // ============================================================ UT transform
 struct TinvLay {
@@ -322,9 +323,12 @@ __device__ __forceinline__ bf16x4 ld4_tr(const bf16 *p) {
 }
 
 // B operand of a 16x16x32 product with k over the rows [r0, r0 + 32) and n
-// over the columns [c0, c0 + 16) of a row-major [.][KP] bf16 matrix: lane l
+// over the columns [c0, c0 + 16) of a row-major [.][P] bf16 matrix: lane l
 // (group g = l / 16) needs rows r0 + 8 g + e, e < 8, of column c0 + l % 16.
-__device__ __forceinline__ bf16x8 ld8_tr(const bf16 (*X)[KP], int r0, int c0, int l) {
+// The A operand has the same lane layout, so the same read gives an A operand
+// with m over the columns from a matrix stored k-major.
+template <int P>
+__device__ __forceinline__ bf16x8 ld8_tr(const bf16 (*X)[P], int r0, int c0, int l) {
   const int g = l >> 4, i = l & 15;
   const bf16x4 a = ld4_tr(&X[r0 + 8 * g + (i >> 2)][c0 + 4 * (i & 3)]);
   const bf16x4 b = ld4_tr(&X[r0 + 8 * g + 4 + (i >> 2)][c0 + 4 * (i & 3)]);
@@ -338,17 +342,17 @@ struct SeqLay {
   static constexpr int V = E + C * KP * 2;           // bf16 [C][VT+8] value tile
   static constexpr int BETA = V + C * (VT + 8) * 2;  // f32 [C]
   static constexpr int G = BETA + C * 4;             // f32 [C] cumulative log decay
-  static constexpr int MH = G + C * 4;               // bf16 [C][CP]  scores hi
-  static constexpr int ML = MH + C * CP * 2;         // bf16 [C][CP]  scores lo
+  static constexpr int MH = G + C * 4;               // bf16 [C][CP]  scores^T hi
+  static constexpr int ML = MH + C * CP * 2;         // bf16 [C][CP]  scores^T lo
   static constexpr int RTH = ML + C * CP * 2;        // bf16 [VT][CP] R^T hi
   static constexpr int RTL = RTH + VT * CP * 2;      // bf16 [VT][CP] R^T lo
   static constexpr int DTH = RTL + VT * CP * 2;      // bf16 [VT][CP] Delta^T hi
   static constexpr int DTL = DTH + VT * CP * 2;      // bf16 [VT][CP] Delta^T lo
   static constexpr int DSH = DTL + VT * CP * 2;      // bf16 [VT][CP] decayed Delta^T hi
   static constexpr int DSL = DSH + VT * CP * 2;      // bf16 [VT][CP] decayed Delta^T lo
-  static constexpr int SH = DSL + VT * CP * 2;       // bf16 [VT][KP] state hi
-  static constexpr int SL = SH + VT * KP * 2;        // bf16 [VT][KP] state lo
-  static constexpr int TOTAL = SL + VT * KP * 2;
+  static constexpr int SH = DSL + VT * CP * 2;       // bf16 [KD][SP] state^T hi
+  static constexpr int SL = SH + KD * SP * 2;        // bf16 [KD][SP] state^T lo
+  static constexpr int TOTAL = SL + KD * SP * 2;
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
@@ -365,7 +369,7 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
   bf16(*sV)[VT + 8] = reinterpret_cast<bf16(*)[VT + 8]>(smem + L::V);
   float *sBeta = reinterpret_cast<float *>(smem + L::BETA);
   float *sG = reinterpret_cast<float *>(smem + L::G);
-  bf16(*sMh)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::MH);
+  bf16(*sMh)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::MH);  // [n][m]
   bf16(*sMl)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::ML);
   bf16(*sRh)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::RTH);
   bf16(*sRl)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::RTL);
@@ -373,13 +377,14 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
   bf16(*sDl)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::DTL);
   bf16(*sDsh)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + (GATED ? L::DSH : L::DTH));
   bf16(*sDsl)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + (GATED ? L::DSL : L::DTL));
-  bf16(*sSh)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::SH);
-  bf16(*sSl)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::SL);
+  bf16(*sSh)[SP] = reinterpret_cast<bf16(*)[SP]>(smem + L::SH);  // [k][v]
+  bf16(*sSl)[SP] = reinterpret_cast<bf16(*)[SP]>(smem + L::SL);
 
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = l & 15, lq = l >> 4;
   const int rw = w & 3, cw = w >> 2;  // token rows [16 rw, +16), value columns [16 cw, +16)
+  const int m0 = 16 * rw;
   // XCD-aware placement: block i runs on XCD i % 8; the NT tiles of one
   // sequence share i % 8, so their reads of the same keys meet in one L2.
   const int bid = blockIdx.x;
@@ -417,8 +422,8 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
       const float s0 = a.S0 ? a.S0[(seq * VD + v0 + vr) * KD + c] : 0.0f;
       Sacc[j][i] = s0;
       const bf16 hi = to_bf16(s0);
-      sSh[vr][c] = hi;
-      sSl[vr][c] = to_bf16(s0 - to_f32(hi));
+      sSh[c][vr] = hi;
+      sSl[c][vr] = to_bf16(s0 - to_f32(hi));
     }
 
   // ---- prefetch registers for one chunk (each input element is loaded once
@@ -430,31 +435,56 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
   // selected here: a select would wait for the load.  Their beta is zeroed
   // at use, which makes their R and Delta rows zero; their scores fall
   // outside the causal mask and their outputs are not stored.
+  // Addresses: a chunk's base pointers are wave-uniform (scalar registers);
+  // each lane adds a 32-bit byte offset fixed for the whole sweep (the host
+  // checks that 64 token rows span less than 2 GiB).
+  const int64_t rowb = tstride * 2;  // bytes between tokens
+  const char *qb = reinterpret_cast<const char *>(gq + base);
+  const char *kb = reinterpret_cast<const char *>(gk + base);
+  const char *eb = reinterpret_cast<const char *>(gkt + base);
+  const char *vb = reinterpret_cast<const char *>(gv + base + v0);
+  char *ob = reinterpret_cast<char *>(go + base + v0);
+  const char *bb = reinterpret_cast<const char *>(a.beta + b * T * H + h);
+  const char *ab = GATED ? reinterpret_cast<const char *>(a.alpha + b * T * H + h) : nullptr;
+  uint32_t roff[2], coff[2];
+  int rrow[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int vi = tid + 512 * p;
+    rrow[p] = vi >> 4;
+    coff[p] = (uint32_t)(16 * (vi & 15));
+    roff[p] = (uint32_t)(rrow[p] * rowb) + coff[p];
+  }
+  const int vrow = tid >> 2;
+  const uint32_t vcoff = (uint32_t)(16 * (tid & 3)), voff = (uint32_t)(vrow * rowb) + vcoff;
+  const uint32_t toff = (uint32_t)(((16 * rw + l16) * C + 8 * lq) * 2);
+  const uint32_t boff = (uint32_t)(l * H * 4);
+  const uint32_t ooff = (uint32_t)((m0 + 4 * lq) * rowb + 2 * (16 * cw + l16));
+
   bf16x8 pq[2], pk[2], pe[2], pv, pt[2];
   float pbeta = 0.0f, palpha = 1.0f;
   auto fetch = [&](int64_t n) {
     const int64_t t0 = n * C;
+    const int Lc = (int)((T - t0) < C ? (T - t0) : C);
+    const int64_t cb = t0 * rowb;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const int vi = tid + 512 * p, i = vi >> 4, c8 = 8 * (vi & 15);
-      const int64_t off = base + (t0 + i < T ? t0 + i : 0) * tstride + c8;
-      pq[p] = ld8(gq + off);
-      pk[p] = ld8(gk + off);
-      pe[p] = ld8(gkt + off);
+      const uint32_t o = rrow[p] < Lc ? roff[p] : coff[p];
+      pq[p] = ld8(reinterpret_cast<const bf16 *>(qb + cb + o));
+      pk[p] = ld8(reinterpret_cast<const bf16 *>(kb + cb + o));
+      pe[p] = ld8(reinterpret_cast<const bf16 *>(eb + cb + o));
     }
-    if (tid < 256) {
-      const int i = tid >> 2, cv = tid & 3;
-      pv = ld8(gv + base + (t0 + i < T ? t0 + i : 0) * tstride + v0 + 8 * cv);
-    }
+    if (tid < 256) pv = ld8(reinterpret_cast<const bf16 *>(vb + cb + (vrow < Lc ? voff : vcoff)));
     {
-      const bf16 *tp = tseq + n * (C * C) + (16 * rw + l16) * C + 8 * lq;
+      const char *tp = reinterpret_cast<const char *>(tseq + n * (C * C)) + toff;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) pt[kk] = ld8(tp + 32 * kk);
+      for (int kk = 0; kk < 2; ++kk) pt[kk] = ld8(reinterpret_cast<const bf16 *>(tp + 64 * kk));
     }
     if (w == 0) {
-      const int64_t gi = (b * T + (t0 + l < T ? t0 + l : 0)) * H + h;
-      pbeta = a.beta[gi];
-      if constexpr (GATED) palpha = a.alpha[gi];
+      const int64_t sb = t0 * H * 4;
+      const uint32_t o = l < Lc ? boff : 0u;
+      pbeta = *reinterpret_cast<const float *>(bb + sb + o);
+      if constexpr (GATED) palpha = *reinterpret_cast<const float *>(ab + sb + o);
     }
   };
 
@@ -491,7 +521,6 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
     __syncthreads();
     if (n + 1 < N) fetch(n + 1);  // overlaps with the compute below
 
-    const int m0 = 16 * rw;
     // ---- stage G: K S^T and Q S^T for tile (rw, cw); score tiles (rw, tj),
     //      tj = cw, cw + 2 (a tile above the diagonal is computed and dropped)
     floatx4 accKS = {0.f, 0.f, 0.f, 0.f}, accQS = {0.f, 0.f, 0.f, 0.f};
@@ -503,8 +532,8 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
         const int ko = 32 * kk + 8 * lq;
         kf[kk] = ld8(&sK[m0 + l16][ko]);
         qf[kk] = ld8(&sQ[m0 + l16][ko]);
-        sh[kk] = ld8(&sSh[16 * cw + l16][ko]);
-        sl[kk] = ld8(&sSl[16 * cw + l16][ko]);
+        sh[kk] = ld8_tr(sSh, 32 * kk, 16 * cw, l);
+        sl[kk] = ld8_tr(sSl, 32 * kk, 16 * cw, l);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           me[j][kk] = ld8(&sE[16 * (cw + 2 * j) + l16][ko]);
@@ -537,25 +566,28 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
       if (tj <= rw) {
         const int nn = 16 * tj + l16;
         const float gn = GATED ? sG[nn] : 0.0f;
+        floatx4 mv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = m0 + 4 * lq + i;
           const float ratio = GATED ? __expf(gm[i] - gn) : 1.0f;
-          const float mv = nn <= m ? ratio * accM[j][i] : 0.0f;
-          const bf16 mh = to_bf16(mv);
-          sMh[m][nn] = mh;
-          sMl[m][nn] = to_bf16(mv - to_f32(mh));
+          mv[i] = nn <= m ? ratio * accM[j][i] : 0.0f;
         }
+        bf16x4 mh, ml;
+        split4(mv, mh, ml);
+        *reinterpret_cast<bf16x4 *>(&sMh[nn][m0 + 4 * lq]) = mh;
+        *reinterpret_cast<bf16x4 *>(&sMl[nn][m0 + 4 * lq]) = ml;
       }
     }
     floatx4 Oacc;
     {
+      // values V[m0 + 4 lq + i][16 cw + l16], i < 4, in one transposed read
+      const bf16x4 vv = ld4_tr(&sV[m0 + 4 * lq + (l16 >> 2)][16 * cw + 4 * (l16 & 3)]);
       floatx4 r;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = m0 + 4 * lq + i, vr = 16 * cw + l16;
         const float em = GATED ? __expf(gm[i]) : 1.0f;
-        r[i] = bm[i] * (to_f32(sV[m][vr]) - em * accKS[i]);
+        r[i] = bm[i] * (to_f32(vv[i]) - em * accKS[i]);
         Oacc[i] = em * accQS[i];
       }
       bf16x4 rh, rl;
@@ -604,8 +636,8 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int ko = 32 * kk + 8 * lq;
-        mh[kk] = ld8(&sMh[m0 + l16][ko]);
-        ml[kk] = ld8(&sMl[m0 + l16][ko]);
+        mh[kk] = ld8_tr(sMh, 32 * kk, m0, l);
+        ml[kk] = ld8_tr(sMl, 32 * kk, m0, l);
         dh[kk] = ld8(&sDh[16 * cw + l16][ko]);
         dl[kk] = ld8(&sDl[16 * cw + l16][ko]);
       }
@@ -615,11 +647,10 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
         acc = mfma32(mh[kk], dl[kk], acc);
         acc = mfma32(ml[kk], dh[kk], acc);
       }
+      char *oc = ob + t0 * rowb + ooff;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + 4 * lq + i;
-        if (m < Lc) go[base + (t0 + m) * tstride + v0 + 16 * cw + l16] = to_bf16(a.q_scale * acc[i]);
-      }
+      for (int i = 0; i < 4; ++i)
+        if (m0 + 4 * lq + i < Lc) *reinterpret_cast<bf16 *>(oc + i * rowb) = to_bf16(a.q_scale * acc[i]);
     }
     // ---- stage S: the wave's two state tiles, then their bf16 pair.  The
     //      write keys enter as B operands with k over tokens, read transposed
@@ -654,13 +685,10 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
           }
         }
         Sacc[j] = acc;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int vr = 16 * srt + 4 * lq + i, c = 16 * kt + l16;
-          const bf16 hi = to_bf16(acc[i]);
-          sSh[vr][c] = hi;
-          sSl[vr][c] = to_bf16(acc[i] - to_f32(hi));
-        }
+        bf16x4 sh4, sl4;
+        split4(acc, sh4, sl4);
+        *reinterpret_cast<bf16x4 *>(&sSh[16 * kt + l16][16 * srt + 4 * lq]) = sh4;
+        *reinterpret_cast<bf16x4 *>(&sSl[16 * kt + l16][16 * srt + 4 * lq]) = sl4;
       }
     }
   }

@@ -20,20 +20,30 @@ __device__ __forceinline__ floatx4 mfma16(bf16x4 a, bf16x4 b, floatx4 c) {
 __device__ __forceinline__ bf16x8 ld8(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 __device__ __forceinline__ bf16x4 ld4(const bf16 *p) { return *reinterpret_cast<const bf16x4 *>(p); }
 
+// two floats to a bf16 pair (v_cvt_pk_bf16_f32, round to nearest even);
+// element 0 in the low half
+__device__ __forceinline__ uint32_t pk2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, bf16x2{to_bf16(a), to_bf16(b)});
+}
+// the fp32 values of the two halves of a bf16 pair
+__device__ __forceinline__ float pk_lo(uint32_t p) { return __builtin_bit_cast(float, p << 16); }
+__device__ __forceinline__ float pk_hi(uint32_t p) { return __builtin_bit_cast(float, p & 0xffff0000u); }
+
 __device__ __forceinline__ bf16x4 pack4(floatx4 v) {
-  bf16x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = to_bf16(v[i]);
-  return r;
+  typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(bf16x4, u2{pk2(v[0], v[1]), pk2(v[2], v[3])});
 }
 
 // x = hi + lo with hi = bf16(x), lo = bf16(x - hi)
 __device__ __forceinline__ void split4(floatx4 v, bf16x4 &hi, bf16x4 &lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    hi[i] = to_bf16(v[i]);
-    lo[i] = to_bf16(v[i] - to_f32(hi[i]));
-  }
+  typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+  uint32_t h0 = pk2(v[0], v[1]), h1 = pk2(v[2], v[3]);
+  // keeps the compiler from converting element 0 a second time to unpack it
+  asm("" : "+v"(h0), "+v"(h1));
+  const uint32_t l0 = pk2(v[0] - pk_lo(h0), v[1] - pk_hi(h0));
+  const uint32_t l1 = pk2(v[2] - pk_lo(h1), v[3] - pk_hi(h1));
+  hi = __builtin_bit_cast(bf16x4, u2{h0, h1});
+  lo = __builtin_bit_cast(bf16x4, u2{l0, l1});
 }
 
 }  // namespace osdn

@@ -89,6 +89,8 @@ osdn_status validate(const osdn_desc *d, int phase) {
   if (phase & 2) {
     if (d->chunk < 1) return fail(OSDN_EINVAL, "chunk must be >= 1 (got %d)", d->chunk);
     if (d->chunk > 64) return fail(OSDN_EUNSUPPORTED, "chunk must be <= 64 (got %d)", d->chunk);
+    // the sweep addresses 64 token rows with 32-bit byte offsets
+    if (d->H > 65536) return fail(OSDN_EUNSUPPORTED, "phase 2 supports H <= 65536 (got %lld)", (long long)d->H);
     if (d->K > 128 || d->V > 128)
       return fail(OSDN_EUNSUPPORTED, "phase 2 supports K, V <= 128 (got K=%lld V=%lld)", (long long)d->K,
                   (long long)d->V);
