@@ -54,7 +54,7 @@ BAD = [
     (dict(B=0), osdn.EINVAL), (dict(H=0), osdn.EINVAL), (dict(T=-1), osdn.EINVAL),
     (dict(K=0), osdn.EINVAL), (dict(V=0), osdn.EINVAL), (dict(chunk=0), osdn.EINVAL),
     (dict(chunk=65), osdn.EUNSUPPORTED), (dict(K=129), osdn.EUNSUPPORTED),
-    (dict(V=200), osdn.EUNSUPPORTED), (dict(dtype=7), osdn.EINVAL),
+    (dict(V=200), osdn.EUNSUPPORTED), (dict(H=65537), osdn.EUNSUPPORTED), (dict(dtype=7), osdn.EINVAL),
     (dict(eta=-1.0), osdn.EINVAL), (dict(eps=0.0), osdn.EINVAL),
     (dict(d_min=2.0, d_max=1.0), osdn.EINVAL), (dict(d_min=0.0), osdn.EINVAL),
     (dict(q_scale=float("inf")), osdn.EINVAL), (dict(eta=float("nan")), osdn.EINVAL),
@@ -91,6 +91,19 @@ def test_scan_only_limits(lib):
     assert st == osdn.EUNSUPPORTED
     assert lib.osdn_precond_scan_workspace_bytes(ctypes.byref(d)) == 0
     assert lib.osdn_precond_scan_counters_offset(ctypes.byref(d)) == -1
+
+
+def test_head_limit_is_phase2_only(lib):
+    # the sweep's 32-bit row offsets bound H for phase 2; phase 1 alone has no such bound
+    null = ctypes.c_void_p(None)
+    d = osdn.Desc()
+    lib.osdn_desc_init(ctypes.byref(d), 1, 0, 65536, 16, 16)
+    assert lib.osdn_validate(ctypes.byref(d)) == osdn.OK
+    d.H = 65537
+    st = lib.osdn_chunk_fwd(ctypes.byref(d), null, null, null, null, null, null, null, null, null,
+                            null, ctypes.c_size_t(0), null)
+    assert st == osdn.EUNSUPPORTED
+    assert lib.osdn_precond_scan_workspace_bytes(ctypes.byref(d)) > 0
 
 
 def test_null_and_misaligned_pointers_rejected_before_launch(lib):
