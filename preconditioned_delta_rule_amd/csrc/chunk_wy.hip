@@ -410,34 +410,42 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
     reinterpret_cast<bf16x8 *>(&sMh[0][0])[i] = bf16x8{};
     reinterpret_cast<bf16x8 *>(&sMl[0][0])[i] = bf16x8{};
   }
-  // state tiles in accumulators: wave w owns tiles (rt, kt) = (w & 1, 2 (w >> 1) + j),
-  // element i of tile j is S[16 rt + 4 lq + i][16 kt + l16]
-  const int srt = w & 1;
-  floatx4 Sacc[2];
+  // Roles: waves 0-3 ("row waves") own token rows [16 w, 16 w + 16) of the
+  // chunk for K S^T, Q S^T, R and O, over both 16-column value tiles; waves
+  // 4-7 compute the score tiles, then own the state columns
+  // [32 sp, 32 sp + 32) (sp = w - 4) in accumulators: element i of tile
+  // (rt, j) is S[16 rt + 4 lq + i][16 (2 sp + j) + l16].
+  const bool roww = w < 4;
+  const int sp = w & 3;
+  floatx4 Sacc[2][2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int vr = 16 * srt + 4 * lq + i, c = 16 * (2 * (w >> 1) + j) + l16;
-      const float s0 = a.S0 ? a.S0[(seq * VD + v0 + vr) * KD + c] : 0.0f;
-      Sacc[j][i] = s0;
-      const bf16 hi = to_bf16(s0);
-      sSh[c][vr] = hi;
-      sSl[c][vr] = to_bf16(s0 - to_f32(hi));
-    }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int vr = 16 * rt + 4 * lq + i, c = 16 * (2 * sp + j) + l16;
+        const float s0 = a.S0 ? a.S0[(seq * VD + v0 + vr) * KD + c] : 0.0f;
+        Sacc[rt][j][i] = s0;
+        if (!roww) {
+          const bf16 hi = to_bf16(s0);
+          sSh[c][vr] = hi;
+          sSl[c][vr] = to_bf16(s0 - to_f32(hi));
+        }
+      }
 
   // ---- prefetch registers for one chunk (each input element is loaded once
   //      per workgroup, in 16-byte vectors, 16 threads per token row)
   //   q, k, E rows:  vectors tid and tid + 512 of each 64 x 128 tile
   //   values:        threads < 256: token tid / 4, columns 8 (tid % 4) of the tile
   //   Tm:            rows 16 rw + l16 in MFMA A-operand layout
-  // Tokens past T (last chunk only) read token 0 instead and are never
+  // Tokens past T (last chunk only) read the chunk's first token instead and are never
   // selected here: a select would wait for the load.  Their beta is zeroed
   // at use, which makes their R and Delta rows zero; their scores fall
   // outside the causal mask and their outputs are not stored.
   // Addresses: a chunk's base pointers are wave-uniform (scalar registers);
-  // each lane adds a 32-bit byte offset fixed for the whole sweep (the host
-  // checks that 64 token rows span less than 2 GiB).
+  // each lane adds a 32-bit byte offset fixed for the whole sweep (phase 2
+  // takes H <= 65536, so 64 token rows span at most 1 GiB).
   const int64_t rowb = tstride * 2;  // bytes between tokens
   const char *qb = reinterpret_cast<const char *>(gq + base);
   const char *kb = reinterpret_cast<const char *>(gk + base);
@@ -459,27 +467,25 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
   const uint32_t vcoff = (uint32_t)(16 * (tid & 3)), voff = (uint32_t)(vrow * rowb) + vcoff;
   const uint32_t toff = (uint32_t)(((16 * rw + l16) * C + 8 * lq) * 2);
   const uint32_t boff = (uint32_t)(l * H * 4);
-  const uint32_t ooff = (uint32_t)((m0 + 4 * lq) * rowb + 2 * (16 * cw + l16));
+  const uint32_t ooff = (uint32_t)((m0 + 4 * lq) * rowb + 2 * l16);  // row waves, value tile 0
 
   bf16x8 pq[2], pk[2], pe[2], pv, pt[2];
   float pbeta = 0.0f, palpha = 1.0f;
-  auto fetch = [&](int64_t n) {
+  // parts: FQ = q, values, beta (and alpha); FK = k; FE = E
+  constexpr int FQ = 1, FK = 2, FE = 4;
+  auto fetch = [&](int64_t n, int parts) {
     const int64_t t0 = n * C;
     const int Lc = (int)((T - t0) < C ? (T - t0) : C);
     const int64_t cb = t0 * rowb;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const uint32_t o = rrow[p] < Lc ? roff[p] : coff[p];
-      pq[p] = ld8(reinterpret_cast<const bf16 *>(qb + cb + o));
-      pk[p] = ld8(reinterpret_cast<const bf16 *>(kb + cb + o));
-      pe[p] = ld8(reinterpret_cast<const bf16 *>(eb + cb + o));
+      if (parts & FQ) pq[p] = ld8(reinterpret_cast<const bf16 *>(qb + cb + o));
+      if (parts & FK) pk[p] = ld8(reinterpret_cast<const bf16 *>(kb + cb + o));
+      if (parts & FE) pe[p] = ld8(reinterpret_cast<const bf16 *>(eb + cb + o));
     }
+    if (!(parts & FQ)) return;
     if (tid < 256) pv = ld8(reinterpret_cast<const bf16 *>(vb + cb + (vrow < Lc ? voff : vcoff)));
-    {
-      const char *tp = reinterpret_cast<const char *>(tseq + n * (C * C)) + toff;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) pt[kk] = ld8(reinterpret_cast<const bf16 *>(tp + 64 * kk));
-    }
     if (w == 0) {
       const int64_t sb = t0 * H * 4;
       const uint32_t o = l < Lc ? boff : 0u;
@@ -487,8 +493,20 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
       if constexpr (GATED) palpha = *reinterpret_cast<const float *>(ab + sb + o);
     }
   };
+  // Tm rows go straight into the registers stage D reads.  They are loaded
+  // once stage D of the previous chunk is done with them, which leaves a
+  // whole chunk for the load to land and needs no register copy (a copy into
+  // registers with a load in flight would wait for every outstanding load).
+  auto fetch_t = [&](int64_t n) {
+    const char *tp = reinterpret_cast<const char *>(tseq + n * (C * C)) + toff;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) pt[kk] = ld8(reinterpret_cast<const bf16 *>(tp + 64 * kk));
+  };
 
-  if (N > 0) fetch(0);
+  if (N > 0) {
+    fetch(0, FQ | FK | FE);
+    fetch_t(0);
+  }
   for (int64_t n = 0; n < N; ++n) {
     const int64_t t0 = n * C;
     const int Lc = (int)((T - t0) < C ? (T - t0) : C);
@@ -515,104 +533,142 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
         sG[l] = x;
       }
     }
-    bf16x8 tf[2];
-    tf[0] = pt[0];
-    tf[1] = pt[1];
     __syncthreads();
-    if (n + 1 < N) fetch(n + 1);  // overlaps with the compute below
+    // The next chunk's rows are loaded in three parts, one per phase between
+    // barriers, so that their issue overlaps with compute instead of stalling
+    // one phase.  Issued on every chunk (the last one reloads its own rows,
+    // valid and unused) so that the number of loads in flight does not depend
+    // on the path, which lets the waits for Tm count past these loads instead
+    // of draining them.
+    const int64_t nn1 = n + 1 < N ? n + 1 : n;
+    fetch(nn1, FQ);
 
-    // ---- stage G: K S^T and Q S^T for tile (rw, cw); score tiles (rw, tj),
-    //      tj = cw, cw + 2 (a tile above the diagonal is computed and dropped)
-    floatx4 accKS = {0.f, 0.f, 0.f, 0.f}, accQS = {0.f, 0.f, 0.f, 0.f};
-    floatx4 accM[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    {
-      bf16x8 kf[4], qf[4], sh[4], sl[4], me[2][4], mk[2][4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int ko = 32 * kk + 8 * lq;
-        kf[kk] = ld8(&sK[m0 + l16][ko]);
-        qf[kk] = ld8(&sQ[m0 + l16][ko]);
-        sh[kk] = ld8_tr(sSh, 32 * kk, 16 * cw, l);
-        sl[kk] = ld8_tr(sSl, 32 * kk, 16 * cw, l);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          me[j][kk] = ld8(&sE[16 * (cw + 2 * j) + l16][ko]);
-          if constexpr (KRES) mk[j][kk] = ld8(&sK[16 * (cw + 2 * j) + l16][ko]);
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        accKS = mfma32(kf[kk], sh[kk], accKS);
-        accQS = mfma32(qf[kk], sh[kk], accQS);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) accM[j] = mfma32(qf[kk], me[j][kk], accM[j]);
-        accKS = mfma32(kf[kk], sl[kk], accKS);
-        accQS = mfma32(qf[kk], sl[kk], accQS);
-        if constexpr (KRES) {
-#pragma unroll
-          for (int j = 0; j < 2; ++j) accM[j] = mfma32(qf[kk], mk[j][kk], accM[j]);
-        }
-      }
-    }
+    // ---- stage G.  Row waves: K S^T and Q S^T for their rows, both value
+    //      tiles, then R (to LDS, transposed) and the Q S^T part of O (kept).
+    //      Other waves: the ten score tiles on and below the diagonal, split
+    //      3 / 3 / 2 / 2, each wave loading a query row block once.
     float gm[4], bm[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       gm[i] = GATED ? sG[m0 + 4 * lq + i] : 0.0f;
       bm[i] = sBeta[m0 + 4 * lq + i];
     }
+    floatx4 Oacc[2];
+    if (roww) {
+      floatx4 accKS[2], accQS[2];
+      bf16x8 kf[4], qf[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int tj = cw + 2 * j;
-      if (tj <= rw) {
-        const int nn = 16 * tj + l16;
-        const float gn = GATED ? sG[nn] : 0.0f;
-        floatx4 mv;
+      for (int kk = 0; kk < 4; ++kk) {
+        const int ko = 32 * kk + 8 * lq;
+        kf[kk] = ld8(&sK[m0 + l16][ko]);
+        qf[kk] = ld8(&sQ[m0 + l16][ko]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        bf16x8 sh[4], sl[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          sh[kk] = ld8_tr(sSh, 32 * kk, 16 * ct, l);
+          sl[kk] = ld8_tr(sSl, 32 * kk, 16 * ct, l);
+        }
+        floatx4 ks = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          ks = mfma32(kf[kk], sh[kk], ks);
+          qs = mfma32(qf[kk], sh[kk], qs);
+          ks = mfma32(kf[kk], sl[kk], ks);
+          qs = mfma32(qf[kk], sl[kk], qs);
+        }
+        accKS[ct] = ks;
+        accQS[ct] = qs;
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        // values V[m0 + 4 lq + i][16 ct + l16], i < 4, in one transposed read
+        const bf16x4 vv = ld4_tr(&sV[m0 + 4 * lq + (l16 >> 2)][16 * ct + 4 * (l16 & 3)]);
+        floatx4 r;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int m = m0 + 4 * lq + i;
-          const float ratio = GATED ? __expf(gm[i] - gn) : 1.0f;
-          mv[i] = nn <= m ? ratio * accM[j][i] : 0.0f;
+          const float em = GATED ? __expf(gm[i]) : 1.0f;
+          r[i] = bm[i] * (to_f32(vv[i]) - em * accKS[ct][i]);
+          Oacc[ct][i] = em * accQS[ct][i];
         }
-        bf16x4 mh, ml;
-        split4(mv, mh, ml);
-        *reinterpret_cast<bf16x4 *>(&sMh[nn][m0 + 4 * lq]) = mh;
-        *reinterpret_cast<bf16x4 *>(&sMl[nn][m0 + 4 * lq]) = ml;
+        bf16x4 rh, rl;
+        split4(r, rh, rl);
+        *reinterpret_cast<bf16x4 *>(&sRh[16 * ct + l16][m0 + 4 * lq]) = rh;
+        *reinterpret_cast<bf16x4 *>(&sRl[16 * ct + l16][m0 + 4 * lq]) = rl;
       }
-    }
-    floatx4 Oacc;
-    {
-      // values V[m0 + 4 lq + i][16 cw + l16], i < 4, in one transposed read
-      const bf16x4 vv = ld4_tr(&sV[m0 + 4 * lq + (l16 >> 2)][16 * cw + 4 * (l16 & 3)]);
-      floatx4 r;
+    } else {
+      // score tiles (mr, tj), tj = tj0 .. tj0 + cnt - 1 <= mr, one query block
+      auto mrow = [&](int mr, int tj0, int cnt) {
+        bf16x8 qf[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float em = GATED ? __expf(gm[i]) : 1.0f;
-        r[i] = bm[i] * (to_f32(vv[i]) - em * accKS[i]);
-        Oacc[i] = em * accQS[i];
+        for (int kk = 0; kk < 4; ++kk) qf[kk] = ld8(&sQ[16 * mr + l16][32 * kk + 8 * lq]);
+        float gr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gr[i] = GATED ? sG[16 * mr + 4 * lq + i] : 0.0f;
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          if (t < cnt) {
+            const int tj = tj0 + t;
+            bf16x8 me[4], mk[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+              const int ko = 32 * kk + 8 * lq;
+              me[kk] = ld8(&sE[16 * tj + l16][ko]);
+              if constexpr (KRES) mk[kk] = ld8(&sK[16 * tj + l16][ko]);
+            }
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+              acc = mfma32(qf[kk], me[kk], acc);
+              if constexpr (KRES) acc = mfma32(qf[kk], mk[kk], acc);
+            }
+            const int nn = 16 * tj + l16;
+            const float gn = GATED ? sG[nn] : 0.0f;
+            floatx4 mv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int m = 16 * mr + 4 * lq + i;
+              const float ratio = GATED ? __expf(gr[i] - gn) : 1.0f;
+              mv[i] = nn <= m ? ratio * acc[i] : 0.0f;
+            }
+            bf16x4 mh, ml;
+            split4(mv, mh, ml);
+            *reinterpret_cast<bf16x4 *>(&sMh[nn][16 * mr + 4 * lq]) = mh;
+            *reinterpret_cast<bf16x4 *>(&sMl[nn][16 * mr + 4 * lq]) = ml;
+          }
+        }
+      };
+      if (w == 4) {
+        mrow(1, 0, 2);
+        mrow(0, 0, 1);
+      } else if (w == 5) {
+        mrow(3, 1, 3);
+      } else if (w == 6) {
+        mrow(2, 0, 2);
+      } else {
+        mrow(2, 2, 1);
+        mrow(3, 0, 1);
       }
-      bf16x4 rh, rl;
-      split4(r, rh, rl);
-      *reinterpret_cast<bf16x4 *>(&sRh[16 * cw + l16][m0 + 4 * lq]) = rh;
-      *reinterpret_cast<bf16x4 *>(&sRl[16 * cw + l16][m0 + 4 * lq]) = rl;
     }
     __syncthreads();
+    fetch(nn1, FK | FE);
 
     // ---- stage D: Delta tile (rw, cw) = Tm R, split and stored transposed.
-    //      Both 32-wide k-steps on every wave: the upper triangles of Tm and
-    //      of the scores are zero.
     const float gL = GATED ? sG[Lc - 1] : 0.0f;
     {
-      bf16x8 rh[2], rl[2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        rh[kk] = ld8(&sRh[16 * cw + l16][32 * kk + 8 * lq]);
-        rl[kk] = ld8(&sRl[16 * cw + l16][32 * kk + 8 * lq]);
-      }
+      // Tm is lower triangular: rows below 32 need only the first k-step
+      const int nks = rw < 2 ? 1 : 2;
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        acc = mfma32(tf[kk], rh[kk], acc);
-        acc = mfma32(tf[kk], rl[kk], acc);
+        if (kk < nks) {
+          const bf16x8 rh = ld8(&sRh[16 * cw + l16][32 * kk + 8 * lq]);
+          const bf16x8 rl = ld8(&sRl[16 * cw + l16][32 * kk + 8 * lq]);
+          acc = mfma32(pt[kk], rh, acc);
+          acc = mfma32(pt[kk], rl, acc);
+        }
       }
       bf16x4 dh, dl;
       split4(acc, dh, dl);
@@ -628,79 +684,96 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
       }
     }
     __syncthreads();
+    fetch_t(nn1);
 
-    // ---- stage O: output tile (rw, cw)
-    {
-      floatx4 acc = Oacc;
-      bf16x8 mh[2], ml[2], dh[2], dl[2];
+    if (roww) {
+      // ---- stage O: output rows of this wave, both value tiles.  The scores
+      //      of rows below 32 vanish past the first k-step.
+      const int nks = rw < 2 ? 1 : 2;
+      bf16x8 mh[2], ml[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const int ko = 32 * kk + 8 * lq;
-        mh[kk] = ld8_tr(sMh, 32 * kk, m0, l);
-        ml[kk] = ld8_tr(sMl, 32 * kk, m0, l);
-        dh[kk] = ld8(&sDh[16 * cw + l16][ko]);
-        dl[kk] = ld8(&sDl[16 * cw + l16][ko]);
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        acc = mfma32(mh[kk], dh[kk], acc);
-        acc = mfma32(mh[kk], dl[kk], acc);
-        acc = mfma32(ml[kk], dh[kk], acc);
+        if (kk < nks) {
+          mh[kk] = ld8_tr(sMh, 32 * kk, m0, l);
+          ml[kk] = ld8_tr(sMl, 32 * kk, m0, l);
+        }
       }
       char *oc = ob + t0 * rowb + ooff;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (m0 + 4 * lq + i < Lc) *reinterpret_cast<bf16 *>(oc + i * rowb) = to_bf16(a.q_scale * acc[i]);
-    }
-    // ---- stage S: the wave's two state tiles, then their bf16 pair.  The
-    //      write keys enter as B operands with k over tokens, read transposed
-    //      from the row-major key buffers.
-    const float decay = GATED ? __expf(gL) : 1.0f;
-    {
-      bf16x8 dsh[2], dsl[2], be[2][2], bk[2][2];
+      for (int ct = 0; ct < 2; ++ct) {
+        floatx4 acc = Oacc[ct];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          if (kk < nks) {
+            const int ko = 32 * kk + 8 * lq;
+            const bf16x8 dh = ld8(&sDh[16 * ct + l16][ko]);
+            const bf16x8 dl = ld8(&sDl[16 * ct + l16][ko]);
+            acc = mfma32(mh[kk], dh, acc);
+            acc = mfma32(mh[kk], dl, acc);
+            acc = mfma32(ml[kk], dh, acc);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (m0 + 4 * lq + i < Lc)
+            *reinterpret_cast<bf16 *>(oc + i * rowb + 32 * ct) = to_bf16(a.q_scale * acc[i]);
+      }
+    } else {
+      // ---- stage S: the wave's four state tiles, then their bf16 pairs.
+      //      The write keys enter as B operands with k over tokens, read
+      //      transposed from the row-major key buffers.
+      const float decay = GATED ? __expf(gL) : 1.0f;
+      bf16x8 dsh[2][2], dsl[2][2], be[2][2], bk[2][2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int ko = 32 * kk + 8 * lq;
-        dsh[kk] = ld8(&sDsh[16 * srt + l16][ko]);
-        dsl[kk] = ld8(&sDsl[16 * srt + l16][ko]);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          dsh[rt][kk] = ld8(&sDsh[16 * rt + l16][ko]);
+          dsl[rt][kk] = ld8(&sDsl[16 * rt + l16][ko]);
+        }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int c0 = 16 * (2 * (w >> 1) + j);
+          const int c0 = 16 * (2 * sp + j);
           be[j][kk] = ld8_tr(sE, 32 * kk, c0, l);
           if constexpr (KRES) bk[j][kk] = ld8_tr(sK, 32 * kk, c0, l);
         }
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int kt = 2 * (w >> 1) + j;
-        floatx4 acc = Sacc[j];
-        if constexpr (GATED) acc = acc * decay;
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          acc = mfma32(dsh[kk], be[j][kk], acc);
-          acc = mfma32(dsl[kk], be[j][kk], acc);
-          if constexpr (KRES) {
-            acc = mfma32(dsh[kk], bk[j][kk], acc);
-            acc = mfma32(dsl[kk], bk[j][kk], acc);
+        for (int j = 0; j < 2; ++j) {
+          floatx4 acc = Sacc[rt][j];
+          if constexpr (GATED) acc = acc * decay;
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            acc = mfma32(dsh[rt][kk], be[j][kk], acc);
+            acc = mfma32(dsl[rt][kk], be[j][kk], acc);
+            if constexpr (KRES) {
+              acc = mfma32(dsh[rt][kk], bk[j][kk], acc);
+              acc = mfma32(dsl[rt][kk], bk[j][kk], acc);
+            }
           }
+          Sacc[rt][j] = acc;
+          bf16x4 sh4, sl4;
+          split4(acc, sh4, sl4);
+          const int kt = 2 * sp + j;
+          *reinterpret_cast<bf16x4 *>(&sSh[16 * kt + l16][16 * rt + 4 * lq]) = sh4;
+          *reinterpret_cast<bf16x4 *>(&sSl[16 * kt + l16][16 * rt + 4 * lq]) = sl4;
         }
-        Sacc[j] = acc;
-        bf16x4 sh4, sl4;
-        split4(acc, sh4, sl4);
-        *reinterpret_cast<bf16x4 *>(&sSh[16 * kt + l16][16 * srt + 4 * lq]) = sh4;
-        *reinterpret_cast<bf16x4 *>(&sSl[16 * kt + l16][16 * srt + 4 * lq]) = sl4;
-      }
     }
   }
 
-  if (a.S_out) {
+  if (a.S_out && !roww) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int vr = 16 * srt + 4 * lq + i, c = 16 * (2 * (w >> 1) + j) + l16;
-        a.S_out[(seq * VD + v0 + vr) * KD + c] = Sacc[j][i];
-      }
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int vr = 16 * rt + 4 * lq + i, c = 16 * (2 * sp + j) + l16;
+          a.S_out[(seq * VD + v0 + vr) * KD + c] = Sacc[rt][j][i];
+        }
   }
 }
 
