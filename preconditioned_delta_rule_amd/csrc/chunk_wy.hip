@@ -45,7 +45,8 @@ constexpr int KD = 128;    // key dim
 constexpr int VD = 128;    // value dim
 constexpr int VT = 32;     // value rows per sweep workgroup
 constexpr int NT = VD / VT;
-constexpr int KP = KD + 8; // LDS pitch (bf16) of 128-wide rows
+constexpr int KP = KD + 16; // LDS pitch (bf16) of the sweep's 128-wide rows: 288 B keeps 16-row operand reads conflict-free
+constexpr int TKP = KD + 8; // the same in the UT transform, whose workgroups must fit three to a CU
 constexpr int CP = C + 8;  // LDS pitch (bf16) of 64-wide rows
 constexpr int AP = C + 4;  // LDS pitch (f32) of the Gram
 constexpr int SP = VT + 24; // LDS pitch (bf16) of the transposed state tile
@@ -53,12 +54,12 @@ constexpr int SP = VT + 24; // LDS pitch (bf16) of the transposed state tile
 // ============================================================ UT transform
 struct TinvLay {
   // the key rows are dead once the Gram is formed; the inverse reuses them
-  static constexpr int KH = 0;                   // bf16 [C][KP] write keys, or residual E
-  static constexpr int KL = KH + C * KP * 2;     // bf16 [C][KP] keys (residual form)
+  static constexpr int KH = 0;                   // bf16 [C][TKP] write keys, or residual E
+  static constexpr int KL = KH + C * TKP * 2;    // bf16 [C][TKP] keys (residual form)
   static constexpr int TR = 0;                   // bf16 [C][CP] Tm row-major
   static constexpr int TC = TR + C * CP * 2;     // bf16 [C][CP] Tm column-major
   static constexpr int X = TC + C * CP * 2;      // bf16 [C][CP] merge scratch
-  static constexpr int R0 = KL + C * KP * 2;
+  static constexpr int R0 = KL + C * TKP * 2;
   static constexpr int A = R0;                   // f32 [C][AP]
   static constexpr int BETA = A + C * AP * 4;    // f32 [C]
   static constexpr int G = BETA + C * 4;         // f32 [C]
@@ -78,8 +79,8 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
   static_assert(KRES || !EMIT, "the folded replay produces the residual form");
   typedef TinvLay L;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
-  bf16(*sKh)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::KH);
-  bf16(*sKl)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::KL);
+  bf16(*sKh)[TKP] = reinterpret_cast<bf16(*)[TKP]>(smem + L::KH);
+  bf16(*sKl)[TKP] = reinterpret_cast<bf16(*)[TKP]>(smem + L::KL);
   bf16(*sTr)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::TR);
   bf16(*sTc)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::TC);
   bf16(*sX)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::X);
@@ -335,6 +336,11 @@ __device__ __forceinline__ bf16x8 ld8_tr(const bf16 (*X)[P], int r0, int c0, int
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+template <int N>
+struct IConst {
+  static constexpr int value = N;
+};
+
 struct SeqLay {
   static constexpr int Q = 0;                        // bf16 [C][KP]  queries
   static constexpr int K = Q + C * KP * 2;           // bf16 [C][KP]  keys
@@ -563,25 +569,25 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
         kf[kk] = ld8(&sK[m0 + l16][ko]);
         qf[kk] = ld8(&sQ[m0 + l16][ko]);
       }
+      bf16x8 sh[2][4], sl[2][4];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        bf16x8 sh[4], sl[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          sh[kk] = ld8_tr(sSh, 32 * kk, 16 * ct, l);
-          sl[kk] = ld8_tr(sSl, 32 * kk, 16 * ct, l);
-        }
-        floatx4 ks = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          ks = mfma32(kf[kk], sh[kk], ks);
-          qs = mfma32(qf[kk], sh[kk], qs);
-          ks = mfma32(kf[kk], sl[kk], ks);
-          qs = mfma32(qf[kk], sl[kk], qs);
+          sh[ct][kk] = ld8_tr(sSh, 32 * kk, 16 * ct, l);
+          sl[ct][kk] = ld8_tr(sSl, 32 * kk, 16 * ct, l);
         }
-        accKS[ct] = ks;
-        accQS[ct] = qs;
-      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) accKS[ct] = accQS[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          accKS[ct] = mfma32(kf[kk], sh[ct][kk], accKS[ct]);
+          accQS[ct] = mfma32(qf[kk], sh[ct][kk], accQS[ct]);
+          accKS[ct] = mfma32(kf[kk], sl[ct][kk], accKS[ct]);
+          accQS[ct] = mfma32(qf[kk], sl[ct][kk], accQS[ct]);
+        }
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         // values V[m0 + 4 lq + i][16 ct + l16], i < 4, in one transposed read
@@ -599,57 +605,64 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
         *reinterpret_cast<bf16x4 *>(&sRl[16 * ct + l16][m0 + 4 * lq]) = rl;
       }
     } else {
-      // score tiles (mr, tj), tj = tj0 .. tj0 + cnt - 1 <= mr, one query block
-      auto mrow = [&](int mr, int tj0, int cnt) {
-        bf16x8 qf[4];
+      // score tiles (mr, tj), tj = tj0 .. tj0 + CNT - 1 <= mr, one query
+      // block; every operand is loaded before the products, whose chains
+      // interleave
+      auto mrow = [&](int mr, int tj0, auto cnt) {
+        constexpr int CNT = decltype(cnt)::value;
+        bf16x8 qf[4], me[CNT][4], mk[CNT][4];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qf[kk] = ld8(&sQ[16 * mr + l16][32 * kk + 8 * lq]);
+        for (int kk = 0; kk < 4; ++kk) {
+          const int ko = 32 * kk + 8 * lq;
+          qf[kk] = ld8(&sQ[16 * mr + l16][ko]);
+#pragma unroll
+          for (int t = 0; t < CNT; ++t) {
+            me[t][kk] = ld8(&sE[16 * (tj0 + t) + l16][ko]);
+            if constexpr (KRES) mk[t][kk] = ld8(&sK[16 * (tj0 + t) + l16][ko]);
+          }
+        }
+        floatx4 acc[CNT];
+#pragma unroll
+        for (int t = 0; t < CNT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int t = 0; t < CNT; ++t) {
+            acc[t] = mfma32(qf[kk], me[t][kk], acc[t]);
+            if constexpr (KRES) acc[t] = mfma32(qf[kk], mk[t][kk], acc[t]);
+          }
         float gr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) gr[i] = GATED ? sG[16 * mr + 4 * lq + i] : 0.0f;
 #pragma unroll
-        for (int t = 0; t < 3; ++t) {
-          if (t < cnt) {
-            const int tj = tj0 + t;
-            bf16x8 me[4], mk[4];
+        for (int t = 0; t < CNT; ++t) {
+          const int nn = 16 * (tj0 + t) + l16;
+          const float gn = GATED ? sG[nn] : 0.0f;
+          floatx4 mv;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-              const int ko = 32 * kk + 8 * lq;
-              me[kk] = ld8(&sE[16 * tj + l16][ko]);
-              if constexpr (KRES) mk[kk] = ld8(&sK[16 * tj + l16][ko]);
-            }
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-              acc = mfma32(qf[kk], me[kk], acc);
-              if constexpr (KRES) acc = mfma32(qf[kk], mk[kk], acc);
-            }
-            const int nn = 16 * tj + l16;
-            const float gn = GATED ? sG[nn] : 0.0f;
-            floatx4 mv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int m = 16 * mr + 4 * lq + i;
-              const float ratio = GATED ? __expf(gr[i] - gn) : 1.0f;
-              mv[i] = nn <= m ? ratio * acc[i] : 0.0f;
-            }
-            bf16x4 mh, ml;
-            split4(mv, mh, ml);
-            *reinterpret_cast<bf16x4 *>(&sMh[nn][16 * mr + 4 * lq]) = mh;
-            *reinterpret_cast<bf16x4 *>(&sMl[nn][16 * mr + 4 * lq]) = ml;
+          for (int i = 0; i < 4; ++i) {
+            const int m = 16 * mr + 4 * lq + i;
+            const float ratio = GATED ? __expf(gr[i] - gn) : 1.0f;
+            mv[i] = nn <= m ? ratio * acc[t][i] : 0.0f;
           }
+          bf16x4 mh, ml;
+          split4(mv, mh, ml);
+          *reinterpret_cast<bf16x4 *>(&sMh[nn][16 * mr + 4 * lq]) = mh;
+          *reinterpret_cast<bf16x4 *>(&sMl[nn][16 * mr + 4 * lq]) = ml;
         }
       };
       if (w == 4) {
-        mrow(1, 0, 2);
-        mrow(0, 0, 1);
+        mrow(1, 0, IConst<2>{});
+        mrow(0, 0, IConst<1>{});
       } else if (w == 5) {
-        mrow(3, 1, 3);
+        // two calls keep the operands of at most two tiles live
+        mrow(3, 1, IConst<2>{});
+        mrow(3, 3, IConst<1>{});
       } else if (w == 6) {
-        mrow(2, 0, 2);
+        mrow(2, 0, IConst<2>{});
       } else {
-        mrow(2, 2, 1);
-        mrow(3, 0, 1);
+        mrow(2, 2, IConst<1>{});
+        mrow(3, 0, IConst<1>{});
       }
     }
     __syncthreads();
@@ -698,26 +711,32 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
           ml[kk] = ld8_tr(sMl, 32 * kk, m0, l);
         }
       }
-      char *oc = ob + t0 * rowb + ooff;
+      bf16x8 dh[2][2], dl[2][2];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        floatx4 acc = Oacc[ct];
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int ct = 0; ct < 2; ++ct)
           if (kk < nks) {
             const int ko = 32 * kk + 8 * lq;
-            const bf16x8 dh = ld8(&sDh[16 * ct + l16][ko]);
-            const bf16x8 dl = ld8(&sDl[16 * ct + l16][ko]);
-            acc = mfma32(mh[kk], dh, acc);
-            acc = mfma32(mh[kk], dl, acc);
-            acc = mfma32(ml[kk], dh, acc);
+            dh[ct][kk] = ld8(&sDh[16 * ct + l16][ko]);
+            dl[ct][kk] = ld8(&sDl[16 * ct + l16][ko]);
           }
-        }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+          if (kk < nks) {
+            Oacc[ct] = mfma32(mh[kk], dh[ct][kk], Oacc[ct]);
+            Oacc[ct] = mfma32(mh[kk], dl[ct][kk], Oacc[ct]);
+            Oacc[ct] = mfma32(ml[kk], dh[ct][kk], Oacc[ct]);
+          }
+      char *oc = ob + t0 * rowb + ooff;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (m0 + 4 * lq + i < Lc)
-            *reinterpret_cast<bf16 *>(oc + i * rowb + 32 * ct) = to_bf16(a.q_scale * acc[i]);
-      }
+            *reinterpret_cast<bf16 *>(oc + i * rowb + 32 * ct) = to_bf16(a.q_scale * Oacc[ct][i]);
     } else {
       // ---- stage S: the wave's four state tiles, then their bf16 pairs.
       //      The write keys enter as B operands with k over tokens, read
@@ -739,24 +758,31 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
           if constexpr (KRES) bk[j][kk] = ld8_tr(sK, 32 * kk, c0, l);
         }
       }
+      if constexpr (GATED) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) Sacc[rt][j] = Sacc[rt][j] * decay;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            Sacc[rt][j] = mfma32(dsh[rt][kk], be[j][kk], Sacc[rt][j]);
+            Sacc[rt][j] = mfma32(dsl[rt][kk], be[j][kk], Sacc[rt][j]);
+            if constexpr (KRES) {
+              Sacc[rt][j] = mfma32(dsh[rt][kk], bk[j][kk], Sacc[rt][j]);
+              Sacc[rt][j] = mfma32(dsl[rt][kk], bk[j][kk], Sacc[rt][j]);
+            }
+          }
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          floatx4 acc = Sacc[rt][j];
-          if constexpr (GATED) acc = acc * decay;
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            acc = mfma32(dsh[rt][kk], be[j][kk], acc);
-            acc = mfma32(dsl[rt][kk], be[j][kk], acc);
-            if constexpr (KRES) {
-              acc = mfma32(dsh[rt][kk], bk[j][kk], acc);
-              acc = mfma32(dsl[rt][kk], bk[j][kk], acc);
-            }
-          }
-          Sacc[rt][j] = acc;
           bf16x4 sh4, sl4;
-          split4(acc, sh4, sl4);
+          split4(Sacc[rt][j], sh4, sl4);
           const int kt = 2 * sp + j;
           *reinterpret_cast<bf16x4 *>(&sSh[16 * kt + l16][16 * rt + 4 * lq]) = sh4;
           *reinterpret_cast<bf16x4 *>(&sSl[16 * kt + l16][16 * rt + 4 * lq]) = sl4;
