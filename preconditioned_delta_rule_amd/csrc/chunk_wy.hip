@@ -341,6 +341,19 @@ struct IConst {
   static constexpr int value = N;
 };
 
+// 64-wide bf16 rows without padding: the 16-byte chunk c of row r sits at
+// chunk c ^ (r & 7), which keeps 16-row operand reads, transposed reads and
+// 8-byte epilogue stores free of bank conflicts.  Element offset of (r, c):
+__device__ __forceinline__ int sx(int r, int c) { return r * 64 + ((((c >> 3) ^ r) & 7) << 3) + (c & 7); }
+
+// ld8_tr over an sx-layout matrix (each 8-byte read stays inside one chunk)
+__device__ __forceinline__ bf16x8 ld8_tr_sx(const bf16 *X, int r0, int c0, int l) {
+  const int g = l >> 4, i = l & 15, c = c0 + 4 * (i & 3);
+  const bf16x4 a = ld4_tr(X + sx(r0 + 8 * g + (i >> 2), c));
+  const bf16x4 b = ld4_tr(X + sx(r0 + 8 * g + 4 + (i >> 2), c));
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
 struct SeqLay {
   static constexpr int Q = 0;                        // bf16 [C][KP]  queries
   static constexpr int K = Q + C * KP * 2;           // bf16 [C][KP]  keys
@@ -348,15 +361,16 @@ struct SeqLay {
   static constexpr int V = E + C * KP * 2;           // bf16 [C][VT+8] value tile
   static constexpr int BETA = V + C * (VT + 8) * 2;  // f32 [C]
   static constexpr int G = BETA + C * 4;             // f32 [C] cumulative log decay
-  static constexpr int MH = G + C * 4;               // bf16 [C][CP]  scores^T hi
-  static constexpr int ML = MH + C * CP * 2;         // bf16 [C][CP]  scores^T lo
-  static constexpr int RTH = ML + C * CP * 2;        // bf16 [VT][CP] R^T hi
-  static constexpr int RTL = RTH + VT * CP * 2;      // bf16 [VT][CP] R^T lo
-  static constexpr int DTH = RTL + VT * CP * 2;      // bf16 [VT][CP] Delta^T hi
-  static constexpr int DTL = DTH + VT * CP * 2;      // bf16 [VT][CP] Delta^T lo
-  static constexpr int DSH = DTL + VT * CP * 2;      // bf16 [VT][CP] decayed Delta^T hi
-  static constexpr int DSL = DSH + VT * CP * 2;      // bf16 [VT][CP] decayed Delta^T lo
-  static constexpr int SH = DSL + VT * CP * 2;       // bf16 [KD][SP] state^T hi
+  // 64-wide rows below are unpadded, 16-byte chunks swizzled (sx)
+  static constexpr int MH = G + C * 4;               // bf16 [C][C]   scores^T hi
+  static constexpr int ML = MH + C * C * 2;          // bf16 [C][C]   scores^T lo
+  static constexpr int RTH = ML + C * C * 2;         // bf16 [VT][C]  R^T hi
+  static constexpr int RTL = RTH + VT * C * 2;       // bf16 [VT][C]  R^T lo
+  static constexpr int DTH = RTL + VT * C * 2;       // bf16 [VT][C]  Delta^T hi
+  static constexpr int DTL = DTH + VT * C * 2;       // bf16 [VT][C]  Delta^T lo
+  static constexpr int DSH = DTL + VT * C * 2;       // bf16 [VT][C]  decayed Delta^T hi
+  static constexpr int DSL = DSH + VT * C * 2;       // bf16 [VT][C]  decayed Delta^T lo
+  static constexpr int SH = DSL + VT * C * 2;        // bf16 [KD][SP] state^T hi
   static constexpr int SL = SH + KD * SP * 2;        // bf16 [KD][SP] state^T lo
   static constexpr int TOTAL = SL + KD * SP * 2;
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
@@ -375,14 +389,14 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
   bf16(*sV)[VT + 8] = reinterpret_cast<bf16(*)[VT + 8]>(smem + L::V);
   float *sBeta = reinterpret_cast<float *>(smem + L::BETA);
   float *sG = reinterpret_cast<float *>(smem + L::G);
-  bf16(*sMh)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::MH);  // [n][m]
-  bf16(*sMl)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::ML);
-  bf16(*sRh)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::RTH);
-  bf16(*sRl)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::RTL);
-  bf16(*sDh)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::DTH);
-  bf16(*sDl)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + L::DTL);
-  bf16(*sDsh)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + (GATED ? L::DSH : L::DTH));
-  bf16(*sDsl)[CP] = reinterpret_cast<bf16(*)[CP]>(smem + (GATED ? L::DSL : L::DTL));
+  bf16 *sMh = reinterpret_cast<bf16 *>(smem + L::MH);  // [n][m], sx layout
+  bf16 *sMl = reinterpret_cast<bf16 *>(smem + L::ML);
+  bf16 *sRh = reinterpret_cast<bf16 *>(smem + L::RTH);  // [v][t], sx layout
+  bf16 *sRl = reinterpret_cast<bf16 *>(smem + L::RTL);
+  bf16 *sDh = reinterpret_cast<bf16 *>(smem + L::DTH);
+  bf16 *sDl = reinterpret_cast<bf16 *>(smem + L::DTL);
+  bf16 *sDsh = reinterpret_cast<bf16 *>(smem + (GATED ? L::DSH : L::DTH));
+  bf16 *sDsl = reinterpret_cast<bf16 *>(smem + (GATED ? L::DSL : L::DTL));
   bf16(*sSh)[SP] = reinterpret_cast<bf16(*)[SP]>(smem + L::SH);  // [k][v]
   bf16(*sSl)[SP] = reinterpret_cast<bf16(*)[SP]>(smem + L::SL);
 
@@ -412,16 +426,17 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
   const bf16 *tseq = tin + seq * N * (C * C);
 
   // scores: the tiles above the diagonal are never written and stay zero
-  for (int i = tid; i < C * CP / 8; i += 512) {
-    reinterpret_cast<bf16x8 *>(&sMh[0][0])[i] = bf16x8{};
-    reinterpret_cast<bf16x8 *>(&sMl[0][0])[i] = bf16x8{};
+  for (int i = tid; i < C * C / 8; i += 512) {
+    reinterpret_cast<bf16x8 *>(sMh)[i] = bf16x8{};
+    reinterpret_cast<bf16x8 *>(sMl)[i] = bf16x8{};
   }
-  // Roles: waves 0-3 ("row waves") own token rows [16 w, 16 w + 16) of the
+  // Roles: waves 4-7 ("row waves") own token rows [16 rw, 16 rw + 16) of the
   // chunk for K S^T, Q S^T, R and O, over both 16-column value tiles; waves
-  // 4-7 compute the score tiles, then own the state columns
-  // [32 sp, 32 sp + 32) (sp = w - 4) in accumulators: element i of tile
-  // (rt, j) is S[16 rt + 4 lq + i][16 (2 sp + j) + l16].
-  const bool roww = w < 4;
+  // 0-3 compute the score tiles, then own the state columns
+  // [32 sp, 32 sp + 32) (sp = w) in accumulators: element i of tile (rt, j)
+  // is S[16 rt + 4 lq + i][16 (2 sp + j) + l16].  Wave w shares a SIMD with
+  // wave w + 4; this way round measured faster than the reverse.
+  const bool roww = w >= 4;
   const int sp = w & 3;
   floatx4 Sacc[2][2];
 #pragma unroll
@@ -601,8 +616,8 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
         }
         bf16x4 rh, rl;
         split4(r, rh, rl);
-        *reinterpret_cast<bf16x4 *>(&sRh[16 * ct + l16][m0 + 4 * lq]) = rh;
-        *reinterpret_cast<bf16x4 *>(&sRl[16 * ct + l16][m0 + 4 * lq]) = rl;
+        *reinterpret_cast<bf16x4 *>(sRh + sx(16 * ct + l16, m0 + 4 * lq)) = rh;
+        *reinterpret_cast<bf16x4 *>(sRl + sx(16 * ct + l16, m0 + 4 * lq)) = rl;
       }
     } else {
       // score tiles (mr, tj), tj = tj0 .. tj0 + CNT - 1 <= mr, one query
@@ -647,18 +662,18 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
           }
           bf16x4 mh, ml;
           split4(mv, mh, ml);
-          *reinterpret_cast<bf16x4 *>(&sMh[nn][16 * mr + 4 * lq]) = mh;
-          *reinterpret_cast<bf16x4 *>(&sMl[nn][16 * mr + 4 * lq]) = ml;
+          *reinterpret_cast<bf16x4 *>(sMh + sx(nn, 16 * mr + 4 * lq)) = mh;
+          *reinterpret_cast<bf16x4 *>(sMl + sx(nn, 16 * mr + 4 * lq)) = ml;
         }
       };
-      if (w == 4) {
+      if (w == 0) {
         mrow(1, 0, IConst<2>{});
         mrow(0, 0, IConst<1>{});
-      } else if (w == 5) {
+      } else if (w == 1) {
         // two calls keep the operands of at most two tiles live
         mrow(3, 1, IConst<2>{});
         mrow(3, 3, IConst<1>{});
-      } else if (w == 6) {
+      } else if (w == 2) {
         mrow(2, 0, IConst<2>{});
       } else {
         mrow(2, 2, IConst<1>{});
@@ -677,23 +692,23 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         if (kk < nks) {
-          const bf16x8 rh = ld8(&sRh[16 * cw + l16][32 * kk + 8 * lq]);
-          const bf16x8 rl = ld8(&sRl[16 * cw + l16][32 * kk + 8 * lq]);
+          const bf16x8 rh = ld8(sRh + sx(16 * cw + l16, 32 * kk + 8 * lq));
+          const bf16x8 rl = ld8(sRl + sx(16 * cw + l16, 32 * kk + 8 * lq));
           acc = mfma32(pt[kk], rh, acc);
           acc = mfma32(pt[kk], rl, acc);
         }
       }
       bf16x4 dh, dl;
       split4(acc, dh, dl);
-      *reinterpret_cast<bf16x4 *>(&sDh[16 * cw + l16][m0 + 4 * lq]) = dh;
-      *reinterpret_cast<bf16x4 *>(&sDl[16 * cw + l16][m0 + 4 * lq]) = dl;
+      *reinterpret_cast<bf16x4 *>(sDh + sx(16 * cw + l16, m0 + 4 * lq)) = dh;
+      *reinterpret_cast<bf16x4 *>(sDl + sx(16 * cw + l16, m0 + 4 * lq)) = dl;
       if constexpr (GATED) {
         floatx4 s;
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[i] = acc[i] * __expf(gL - gm[i]);
         split4(s, dh, dl);
-        *reinterpret_cast<bf16x4 *>(&sDsh[16 * cw + l16][m0 + 4 * lq]) = dh;
-        *reinterpret_cast<bf16x4 *>(&sDsl[16 * cw + l16][m0 + 4 * lq]) = dl;
+        *reinterpret_cast<bf16x4 *>(sDsh + sx(16 * cw + l16, m0 + 4 * lq)) = dh;
+        *reinterpret_cast<bf16x4 *>(sDsl + sx(16 * cw + l16, m0 + 4 * lq)) = dl;
       }
     }
     __syncthreads();
@@ -707,8 +722,8 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         if (kk < nks) {
-          mh[kk] = ld8_tr(sMh, 32 * kk, m0, l);
-          ml[kk] = ld8_tr(sMl, 32 * kk, m0, l);
+          mh[kk] = ld8_tr_sx(sMh, 32 * kk, m0, l);
+          ml[kk] = ld8_tr_sx(sMl, 32 * kk, m0, l);
         }
       }
       bf16x8 dh[2][2], dl[2][2];
@@ -718,8 +733,8 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
         for (int ct = 0; ct < 2; ++ct)
           if (kk < nks) {
             const int ko = 32 * kk + 8 * lq;
-            dh[ct][kk] = ld8(&sDh[16 * ct + l16][ko]);
-            dl[ct][kk] = ld8(&sDl[16 * ct + l16][ko]);
+            dh[ct][kk] = ld8(sDh + sx(16 * ct + l16, ko));
+            dl[ct][kk] = ld8(sDl + sx(16 * ct + l16, ko));
           }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
@@ -748,8 +763,8 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
         const int ko = 32 * kk + 8 * lq;
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-          dsh[rt][kk] = ld8(&sDsh[16 * rt + l16][ko]);
-          dsl[rt][kk] = ld8(&sDsl[16 * rt + l16][ko]);
+          dsh[rt][kk] = ld8(sDsh + sx(16 * rt + l16, ko));
+          dsl[rt][kk] = ld8(sDsl + sx(16 * rt + l16, ko));
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
