@@ -49,7 +49,6 @@ constexpr int KP = KD + 16; // LDS pitch (bf16) of the sweep's 128-wide rows: 28
 constexpr int TKP = KD + 8; // the same in the UT transform, whose workgroups must fit three to a CU
 constexpr int CP = C + 8;  // LDS pitch (bf16) of 64-wide rows
 constexpr int AP = C + 4;  // LDS pitch (f32) of the Gram
-constexpr int SP = VT + 24; // LDS pitch (bf16) of the transposed state tile
 
 // ============================================================ UT transform
 struct TinvLay {
@@ -346,6 +345,9 @@ struct IConst {
 // 8-byte epilogue stores free of bank conflicts.  Element offset of (r, c):
 __device__ __forceinline__ int sx(int r, int c) { return r * 64 + ((((c >> 3) ^ r) & 7) << 3) + (c & 7); }
 
+// 128-wide bf16 rows without padding: chunk c of row r at chunk c ^ (r & 15)
+__device__ __forceinline__ int sx128(int r, int c) { return r * 128 + ((((c >> 3) ^ r) & 15) << 3) + (c & 7); }
+
 // ld8_tr over an sx-layout matrix (each 8-byte read stays inside one chunk)
 __device__ __forceinline__ bf16x8 ld8_tr_sx(const bf16 *X, int r0, int c0, int l) {
   const int g = l >> 4, i = l & 15, c = c0 + 4 * (i & 3);
@@ -370,9 +372,9 @@ struct SeqLay {
   static constexpr int DTL = DTH + VT * C * 2;       // bf16 [VT][C]  Delta^T lo
   static constexpr int DSH = DTL + VT * C * 2;       // bf16 [VT][C]  decayed Delta^T hi
   static constexpr int DSL = DSH + VT * C * 2;       // bf16 [VT][C]  decayed Delta^T lo
-  static constexpr int SH = DSL + VT * C * 2;        // bf16 [KD][SP] state^T hi
-  static constexpr int SL = SH + KD * SP * 2;        // bf16 [KD][SP] state^T lo
-  static constexpr int TOTAL = SL + KD * SP * 2;
+  static constexpr int SH = DSL + VT * C * 2;        // bf16 [VT][KD] state hi (sx128 layout)
+  static constexpr int SL = SH + VT * KD * 2;        // bf16 [VT][KD] state lo
+  static constexpr int TOTAL = SL + VT * KD * 2;
   static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
@@ -397,8 +399,8 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
   bf16 *sDl = reinterpret_cast<bf16 *>(smem + L::DTL);
   bf16 *sDsh = reinterpret_cast<bf16 *>(smem + (GATED ? L::DSH : L::DTH));
   bf16 *sDsl = reinterpret_cast<bf16 *>(smem + (GATED ? L::DSL : L::DTL));
-  bf16(*sSh)[SP] = reinterpret_cast<bf16(*)[SP]>(smem + L::SH);  // [k][v]
-  bf16(*sSl)[SP] = reinterpret_cast<bf16(*)[SP]>(smem + L::SL);
+  bf16 *sSh = reinterpret_cast<bf16 *>(smem + L::SH);  // [v][k], sx128 layout
+  bf16 *sSl = reinterpret_cast<bf16 *>(smem + L::SL);
 
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -433,27 +435,27 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
   // Roles: waves 4-7 ("row waves") own token rows [16 rw, 16 rw + 16) of the
   // chunk for K S^T, Q S^T, R and O, over both 16-column value tiles; waves
   // 0-3 compute the score tiles, then own the state columns
-  // [32 sp, 32 sp + 32) (sp = w) in accumulators: element i of tile (rt, j)
-  // is S[16 rt + 4 lq + i][16 (2 sp + j) + l16].  Wave w shares a SIMD with
-  // wave w + 4; this way round measured faster than the reverse.
+  // [32 sp, 32 sp + 32) (sp = w) in accumulators, as tiles of S^T: element i
+  // of tile (rt, j) is S[16 rt + l16][16 (2 sp + j) + 4 lq + i].  Wave w
+  // shares a SIMD with wave w + 4; this way round measured faster than the
+  // reverse.
   const bool roww = w >= 4;
   const int sp = w & 3;
   floatx4 Sacc[2][2];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int vr = 16 * rt + 4 * lq + i, c = 16 * (2 * sp + j) + l16;
-        const float s0 = a.S0 ? a.S0[(seq * VD + v0 + vr) * KD + c] : 0.0f;
-        Sacc[rt][j][i] = s0;
-        if (!roww) {
-          const bf16 hi = to_bf16(s0);
-          sSh[c][vr] = hi;
-          sSl[c][vr] = to_bf16(s0 - to_f32(hi));
-        }
+    for (int j = 0; j < 2; ++j) {
+      const int vr = 16 * rt + l16, c = 16 * (2 * sp + j) + 4 * lq;
+      Sacc[rt][j] = a.S0 ? *reinterpret_cast<const floatx4 *>(a.S0 + (seq * VD + v0 + vr) * KD + c)
+                         : floatx4{0.f, 0.f, 0.f, 0.f};
+      if (!roww) {
+        bf16x4 sh4, sl4;
+        split4(Sacc[rt][j], sh4, sl4);
+        *reinterpret_cast<bf16x4 *>(sSh + sx128(vr, c)) = sh4;
+        *reinterpret_cast<bf16x4 *>(sSl + sx128(vr, c)) = sl4;
       }
+    }
 
   // ---- prefetch registers for one chunk (each input element is loaded once
   //      per workgroup, in 16-byte vectors, 16 threads per token row)
@@ -568,12 +570,6 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
     //      tiles, then R (to LDS, transposed) and the Q S^T part of O (kept).
     //      Other waves: the ten score tiles on and below the diagonal, split
     //      3 / 3 / 2 / 2, each wave loading a query row block once.
-    float gm[4], bm[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      gm[i] = GATED ? sG[m0 + 4 * lq + i] : 0.0f;
-      bm[i] = sBeta[m0 + 4 * lq + i];
-    }
     floatx4 Oacc[2];
     if (roww) {
       floatx4 accKS[2], accQS[2];
@@ -584,25 +580,31 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
         kf[kk] = ld8(&sK[m0 + l16][ko]);
         qf[kk] = ld8(&sQ[m0 + l16][ko]);
       }
-      bf16x8 sh[2][4], sl[2][4];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+      for (int ct = 0; ct < 2; ++ct) {
+        bf16x8 sh[4], sl[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          sh[ct][kk] = ld8_tr(sSh, 32 * kk, 16 * ct, l);
-          sl[ct][kk] = ld8_tr(sSl, 32 * kk, 16 * ct, l);
+          sh[kk] = ld8(sSh + sx128(16 * ct + l16, 32 * kk + 8 * lq));
+          sl[kk] = ld8(sSl + sx128(16 * ct + l16, 32 * kk + 8 * lq));
         }
+        floatx4 ks = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) accKS[ct] = accQS[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          accKS[ct] = mfma32(kf[kk], sh[ct][kk], accKS[ct]);
-          accQS[ct] = mfma32(qf[kk], sh[ct][kk], accQS[ct]);
-          accKS[ct] = mfma32(kf[kk], sl[ct][kk], accKS[ct]);
-          accQS[ct] = mfma32(qf[kk], sl[ct][kk], accQS[ct]);
+        for (int kk = 0; kk < 4; ++kk) {
+          ks = mfma32(kf[kk], sh[kk], ks);
+          qs = mfma32(qf[kk], sh[kk], qs);
+          ks = mfma32(kf[kk], sl[kk], ks);
+          qs = mfma32(qf[kk], sl[kk], qs);
         }
+        accKS[ct] = ks;
+        accQS[ct] = qs;
+      }
+      float gm[4], bm[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        gm[i] = GATED ? sG[m0 + 4 * lq + i] : 0.0f;
+        bm[i] = sBeta[m0 + 4 * lq + i];
+      }
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         // values V[m0 + 4 lq + i][16 ct + l16], i < 4, in one transposed read
@@ -705,7 +707,7 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
       if constexpr (GATED) {
         floatx4 s;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[i] = acc[i] * __expf(gL - gm[i]);
+        for (int i = 0; i < 4; ++i) s[i] = acc[i] * __expf(gL - sG[m0 + 4 * lq + i]);
         split4(s, dh, dl);
         *reinterpret_cast<bf16x4 *>(sDsh + sx(16 * cw + l16, m0 + 4 * lq)) = dh;
         *reinterpret_cast<bf16x4 *>(sDsl + sx(16 * cw + l16, m0 + 4 * lq)) = dl;
@@ -753,9 +755,9 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
           if (m0 + 4 * lq + i < Lc)
             *reinterpret_cast<bf16 *>(oc + i * rowb + 32 * ct) = to_bf16(a.q_scale * Oacc[ct][i]);
     } else {
-      // ---- stage S: the wave's four state tiles, then their bf16 pairs.
-      //      The write keys enter as B operands with k over tokens, read
-      //      transposed from the row-major key buffers.
+      // ---- stage S: the wave's four tiles of S^T += K~^T Delta, then their
+      //      bf16 pairs.  The write keys enter as A operands with k over
+      //      tokens, read transposed from the row-major key buffers.
       const float decay = GATED ? __expf(gL) : 1.0f;
       bf16x8 dsh[2][2], dsl[2][2], be[2][2], bk[2][2];
 #pragma unroll
@@ -785,11 +787,11 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            Sacc[rt][j] = mfma32(dsh[rt][kk], be[j][kk], Sacc[rt][j]);
-            Sacc[rt][j] = mfma32(dsl[rt][kk], be[j][kk], Sacc[rt][j]);
+            Sacc[rt][j] = mfma32(be[j][kk], dsh[rt][kk], Sacc[rt][j]);
+            Sacc[rt][j] = mfma32(be[j][kk], dsl[rt][kk], Sacc[rt][j]);
             if constexpr (KRES) {
-              Sacc[rt][j] = mfma32(dsh[rt][kk], bk[j][kk], Sacc[rt][j]);
-              Sacc[rt][j] = mfma32(dsl[rt][kk], bk[j][kk], Sacc[rt][j]);
+              Sacc[rt][j] = mfma32(bk[j][kk], dsh[rt][kk], Sacc[rt][j]);
+              Sacc[rt][j] = mfma32(bk[j][kk], dsl[rt][kk], Sacc[rt][j]);
             }
           }
 #pragma unroll
@@ -799,8 +801,8 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
           bf16x4 sh4, sl4;
           split4(Sacc[rt][j], sh4, sl4);
           const int kt = 2 * sp + j;
-          *reinterpret_cast<bf16x4 *>(&sSh[16 * kt + l16][16 * rt + 4 * lq]) = sh4;
-          *reinterpret_cast<bf16x4 *>(&sSl[16 * kt + l16][16 * rt + 4 * lq]) = sl4;
+          *reinterpret_cast<bf16x4 *>(sSh + sx128(16 * rt + l16, 16 * kt + 4 * lq)) = sh4;
+          *reinterpret_cast<bf16x4 *>(sSl + sx128(16 * rt + l16, 16 * kt + 4 * lq)) = sl4;
         }
     }
   }
@@ -809,12 +811,10 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int vr = 16 * rt + 4 * lq + i, c = 16 * (2 * sp + j) + l16;
-          a.S_out[(seq * VD + v0 + vr) * KD + c] = Sacc[rt][j][i];
-        }
+      for (int j = 0; j < 2; ++j) {
+        const int vr = 16 * rt + l16, c = 16 * (2 * sp + j) + 4 * lq;
+        *reinterpret_cast<floatx4 *>(a.S_out + (seq * VD + v0 + vr) * KD + c) = Sacc[rt][j];
+      }
   }
 }
 
