@@ -104,6 +104,13 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
 
   bf16x8 kf[4];  // wave w's key rows as A operands (token 16 w + l16)
   if constexpr (EMIT) {
+    // A chunk the phase-1 sweep took as pinned (marked 2) starts from d_min,
+    // and its mark guarantees that every step clips back to d_min (the mark
+    // tests the replay's own fp32 expression at the largest key square), so
+    // its residual is E = (d_min - 1) k, computed here in parallel and
+    // bitwise equal to the token-by-token replay below.
+    const bool pinned = em.pin[seq * N + n] == 2;
+    const float dm1 = em.d_min - 1.0f;  // exact on [0.5, 2]
     // key rows into LDS (16-byte vectors, 16 threads per row; zero past T),
     // step scalars and retention of the chunk's tokens
 #pragma unroll
@@ -111,18 +118,23 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
       const int vi = tid + 256 * p, i = vi >> 4, c8 = 8 * (vi & 15);
       const bf16x8 x = ld8(gk + base + (i < Lc ? i : 0) * tstride + c8);
       *reinterpret_cast<bf16x8 *>(&sKl[i][c8]) = i < Lc ? x : bf16x8{};
+      if (pinned) {
+        bf16x8 e;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) e[q] = to_bf16(dm1 * to_f32(x[q]));
+        *reinterpret_cast<bf16x8 *>(&sKh[i][c8]) = i < Lc ? e : bf16x8{};
+      }
     }
-    if (tid < C) {
+    if (!pinned && tid < C) {
       const int64_t gi = (b * T + t0 + (tid < Lc ? tid : 0)) * H + h;
       sC[tid] = em.cstep[gi];
       sR[tid] = em.r ? em.r[gi] : 1.0f;
     }
     __syncthreads();
     // one thread per coordinate: replay d through the chunk, writing E
-    if (tid < KD) {
+    if (!pinned && tid < KD) {
       const int c = tid;
-      const bool pinned = em.pin[seq * N + n] == 2;
-      float d = pinned ? em.d_min : em.dstart[(seq * N + n) * KD + c];
+      float d = em.dstart[(seq * N + n) * KD + c];
       const float lo = em.clamp ? em.d_min : -INFINITY, hi = em.clamp ? em.d_max : INFINITY;
       auto step = [&](int u) {
         const float kv = to_f32(sKl[u][c]);
