@@ -50,6 +50,11 @@ constexpr int TKP = KD + 8; // the same in the UT transform, whose workgroups mu
 constexpr int CP = C + 8;  // LDS pitch (bf16) of 64-wide rows
 constexpr int AP = C + 4;  // LDS pitch (f32) of the Gram
 
+template <int N>
+struct IConst {
+  static constexpr int value = N;
+};
+
 // ============================================================ UT transform
 struct TinvLay {
   // the key rows are dead once the Gram is formed; the inverse reuses them
@@ -102,7 +107,6 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
   const int64_t tstride = H * KD;
   const int64_t base = (b * T + t0) * tstride + h * KD;  // token t0 of this (b,h)
 
-  bf16x8 kf[4];  // wave w's key rows as A operands (token 16 w + l16)
   if constexpr (EMIT) {
     // A chunk the phase-1 sweep took as pinned (marked 2) starts from d_min,
     // and its mark guarantees that every step clips back to d_min (the mark
@@ -158,34 +162,18 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
       const int vi = tid + 256 * p, i = vi >> 4, c8 = 8 * (vi & 15);
       if (i < Lc) *reinterpret_cast<bf16x8 *>(res + i * tstride + c8) = ld8(&sKh[i][c8]);
     }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) kf[kk] = ld8(&sKl[16 * w + l16][32 * kk + 8 * lq]);
   } else {
-  // write keys into LDS: thread -> token l, columns [32 w, 32 w + 32).  With
-  // the residual form k~ = k + E both k and E are exact bf16 operands, so
-  // the Gram is K E^T + K K^T; otherwise the bf16 k~ rows themselves.
-  {
-    const bool ok = l < Lc;
-    const int64_t off = base + (ok ? l : 0) * tstride + 32 * w;
+  // write keys and keys into LDS (16-byte vectors, 16 threads per row; zero
+  // past T).  With the residual form k~ = k + E both k and E are exact bf16
+  // operands, so the Gram is K E^T + K K^T; otherwise the bf16 k~ rows
+  // themselves.
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      bf16x8 x = ld8(gkt + off + 8 * p);
-      *reinterpret_cast<bf16x8 *>(&sKh[l][32 * w + 8 * p]) = ok ? x : bf16x8{};
-      if constexpr (KRES) {
-        bf16x8 y = ld8(gk + off + 8 * p);
-        *reinterpret_cast<bf16x8 *>(&sKl[l][32 * w + 8 * p]) = ok ? y : bf16x8{};
-      }
-    }
-  }
-  {
-    const int m = 16 * w + l16;
-    const bool ok = m < Lc;
-    const int64_t off = base + (ok ? m : 0) * tstride + 8 * lq;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 x = ld8(gk + off + 32 * kk);
-      kf[kk] = ok ? x : bf16x8{};
-    }
+  for (int p = 0; p < 4; ++p) {
+    const int vi = tid + 256 * p, i = vi >> 4, c8 = 8 * (vi & 15);
+    const int64_t off = base + (i < Lc ? i : 0) * tstride + c8;
+    const bf16x8 x = ld8(gkt + off), y = ld8(gk + off);
+    *reinterpret_cast<bf16x8 *>(&sKh[i][c8]) = i < Lc ? x : bf16x8{};
+    *reinterpret_cast<bf16x8 *>(&sKl[i][c8]) = i < Lc ? y : bf16x8{};
   }
   }
   if (w == 0) {
@@ -206,39 +194,50 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
   }
   __syncthreads();
 
-  // Gram tiles (w, tj), tj <= w
-  const int m0 = 16 * w;
-  floatx4 acc[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int ko = 32 * kk + 8 * lq;
-#pragma unroll
-    for (int tj = 0; tj < 4; ++tj) {
-      if (tj <= w) {
-        acc[tj] = mfma32(kf[kk], ld8(&sKh[16 * tj + l16][ko]), acc[tj]);
-        if constexpr (KRES) acc[tj] = mfma32(kf[kk], ld8(&sKl[16 * tj + l16][ko]), acc[tj]);
-      }
-    }
-  }
+  // Gram tiles (rt, tj), tj <= rt, three or two per wave so that every wave
+  // has a similar share and its product chains interleave:
+  //   slot 0: (3,0) (3,2) (2,0) (2,2)   slot 1: (3,1) (3,3) (2,1) (1,1)
+  //   slot 2: (0,0) (1,0)  -      -     (waves 0 .. 3)
   {
-    float gm[4], bm[4];
+    const int rts[3] = {w < 2 ? 3 : 2, w < 2 ? 3 : (w == 2 ? 2 : 1), w};
+    const int tjs[3] = {(w & 1) * 2, w == 1 ? 3 : 1, 0};
+    floatx4 acc[3];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      gm[i] = GATED ? sG[m0 + 4 * lq + i] : 0.0f;
-      bm[i] = sBeta[m0 + 4 * lq + i];
-    }
+    for (int q = 0; q < 3; ++q) acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+    auto gram = [&](auto NS) {
+      constexpr int ns = decltype(NS)::value;
 #pragma unroll
-    for (int tj = 0; tj < 4; ++tj) {
-      if (tj <= w) {
-        const int nn = 16 * tj + l16;
+      for (int kk = 0; kk < 4; ++kk) {
+        const int ko = 32 * kk + 8 * lq;
+        bf16x8 ka[ns], bh[ns], bl[ns];
+#pragma unroll
+        for (int q = 0; q < ns; ++q) {
+          ka[q] = ld8(&sKl[16 * rts[q] + l16][ko]);
+          bh[q] = ld8(&sKh[16 * tjs[q] + l16][ko]);
+          if constexpr (KRES) bl[q] = ld8(&sKl[16 * tjs[q] + l16][ko]);
+        }
+#pragma unroll
+        for (int q = 0; q < ns; ++q) acc[q] = mfma32(ka[q], bh[q], acc[q]);
+        if constexpr (KRES) {
+#pragma unroll
+          for (int q = 0; q < ns; ++q) acc[q] = mfma32(ka[q], bl[q], acc[q]);
+        }
+      }
+    };
+    if (w < 2)
+      gram(IConst<3>{});
+    else
+      gram(IConst<2>{});
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      if (q < 2 || w < 2) {
+        const int rt = rts[q], nn = 16 * tjs[q] + l16;
         const float gn = GATED ? sG[nn] : 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int m = m0 + 4 * lq + i;
-          const float ratio = GATED ? __expf(gm[i] - gn) : 1.0f;
-          sA[m][nn] = nn < m ? bm[i] * ratio * acc[tj][i] : 0.0f;
+          const int mrow = 16 * rt + 4 * lq + i;
+          const float ratio = GATED ? __expf(sG[mrow] - gn) : 1.0f;
+          sA[mrow][nn] = nn < mrow ? sBeta[mrow] * ratio * acc[q][i] : 0.0f;
         }
       }
     }
@@ -251,7 +250,7 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
   // (i) wave w inverts diagonal block w by forward substitution in fp32;
   //     lane l & 15 computes column c of the block inverse.
   {
-    const int c = l16, bb = m0;
+    const int c = l16, bb = 16 * w;
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -346,11 +345,6 @@ __device__ __forceinline__ bf16x8 ld8_tr(const bf16 (*X)[P], int r0, int c0, int
   const bf16x4 b = ld4_tr(&X[r0 + 8 * g + 4 + (i >> 2)][c0 + 4 * (i & 3)]);
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
-
-template <int N>
-struct IConst {
-  static constexpr int value = N;
-};
 
 // 64-wide bf16 rows without padding: the 16-byte chunk c of row r sits at
 // chunk c ^ (r & 7), which keeps 16-row operand reads, transposed reads and
