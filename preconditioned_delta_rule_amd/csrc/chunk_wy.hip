@@ -97,93 +97,77 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = l & 15, lq = l >> 4;
-  const int64_t seq = blockIdx.x / N, n = blockIdx.x % N;
   const int64_t H = a.H, T = a.T;
-  const int64_t b = seq / H, h = seq - b * H;
-  const int64_t t0 = n * C;
-  const int Lc = (int)((T - t0) < C ? (T - t0) : C);
   const bf16 *gk = static_cast<const bf16 *>(a.k);
   const bf16 *gkt = static_cast<const bf16 *>(a.kt);
   const int64_t tstride = H * KD;
+  const int64_t nch = a.B * H * N;
+  // Each workgroup takes chunks blockIdx.x, blockIdx.x + gridDim.x, ...; the
+  // next chunk's key rows (and write-key rows off the folded path), beta,
+  // alpha and pin word are loaded into registers while this one is computed.
+  bf16x8 px[4], pe[4];
+  float pb = 0.0f, pa = 1.0f;
+  int ppin = 0;
+  auto fetch = [&](int64_t ci) {
+    const int64_t seq = ci / N, n = ci - seq * N;
+    const int64_t b = seq / H, h = seq - b * H;
+    const int64_t t0 = n * C;
+    const int Lc = (int)((T - t0) < C ? (T - t0) : C);
+    const int64_t base = (b * T + t0) * tstride + h * KD;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int vi = tid + 256 * p, i = vi >> 4, c8 = 8 * (vi & 15);
+      const int64_t off = base + (i < Lc ? i : 0) * tstride + c8;
+      px[p] = ld8(gk + off);
+      if constexpr (!EMIT) pe[p] = ld8(gkt + off);
+    }
+    if (w == 0) {
+      const int64_t gi = (b * T + t0 + (l < Lc ? l : 0)) * H + h;
+      pb = a.beta[gi];
+      if constexpr (GATED) pa = a.alpha[gi];
+    }
+    if constexpr (EMIT) ppin = em.pin[ci];
+  };
+  if ((int64_t)blockIdx.x < nch) fetch(blockIdx.x);
+  for (int64_t ci = blockIdx.x; ci < nch; ci += gridDim.x) {
+  const int64_t seq = ci / N, n = ci - seq * N;
+  const int64_t b = seq / H, h = seq - b * H;
+  const int64_t t0 = n * C;
+  const int Lc = (int)((T - t0) < C ? (T - t0) : C);
   const int64_t base = (b * T + t0) * tstride + h * KD;  // token t0 of this (b,h)
 
-  if constexpr (EMIT) {
-    // A chunk the phase-1 sweep took as pinned (marked 2) starts from d_min,
-    // and its mark guarantees that every step clips back to d_min (the mark
-    // tests the replay's own fp32 expression at the largest key square), so
-    // its residual is E = (d_min - 1) k, computed here in parallel and
-    // bitwise equal to the token-by-token replay below.
-    const bool pinned = em.pin[seq * N + n] == 2;
-    const float dm1 = em.d_min - 1.0f;  // exact on [0.5, 2]
-    // key rows into LDS (16-byte vectors, 16 threads per row; zero past T),
-    // step scalars and retention of the chunk's tokens
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int vi = tid + 256 * p, i = vi >> 4, c8 = 8 * (vi & 15);
-      const bf16x8 x = ld8(gk + base + (i < Lc ? i : 0) * tstride + c8);
-      *reinterpret_cast<bf16x8 *>(&sKl[i][c8]) = i < Lc ? x : bf16x8{};
-      if (pinned) {
-        bf16x8 e;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) e[q] = to_bf16(dm1 * to_f32(x[q]));
-        *reinterpret_cast<bf16x8 *>(&sKh[i][c8]) = i < Lc ? e : bf16x8{};
-      }
-    }
-    if (!pinned && tid < C) {
-      const int64_t gi = (b * T + t0 + (tid < Lc ? tid : 0)) * H + h;
-      sC[tid] = em.cstep[gi];
-      sR[tid] = em.r ? em.r[gi] : 1.0f;
-    }
-    __syncthreads();
-    // one thread per coordinate: replay d through the chunk, writing E
-    if (!pinned && tid < KD) {
-      const int c = tid;
-      float d = em.dstart[(seq * N + n) * KD + c];
-      const float lo = em.clamp ? em.d_min : -INFINITY, hi = em.clamp ? em.d_max : INFINITY;
-      auto step = [&](int u) {
-        const float kv = to_f32(sKl[u][c]);
-        sKh[u][c] = to_bf16((d - 1.0f) * kv);  // d - 1 is exact on [0.5, 2]
-        d = fminf(fmaxf(fmaf(sC[u], kv * kv, sR[u] * d), lo), hi);
-      };
-      if (Lc == C) {
-        // straight-line: the LDS reads, which do not depend on d, run ahead
-#pragma unroll
-        for (int u = 0; u < C; ++u) step(u);
-      } else {
-        for (int u = 0; u < Lc; ++u) step(u);
-        for (int u = Lc; u < C; ++u) sKh[u][c] = to_bf16(0.0f);
-      }
-    }
-    __syncthreads();
-    // the residual rows, for the sweep kernel
-    bf16 *res = em.res + base;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int vi = tid + 256 * p, i = vi >> 4, c8 = 8 * (vi & 15);
-      if (i < Lc) *reinterpret_cast<bf16x8 *>(res + i * tstride + c8) = ld8(&sKh[i][c8]);
-    }
-  } else {
-  // write keys and keys into LDS (16-byte vectors, 16 threads per row; zero
-  // past T).  With the residual form k~ = k + E both k and E are exact bf16
-  // operands, so the Gram is K E^T + K K^T; otherwise the bf16 k~ rows
-  // themselves.
+  // ---- this chunk's rows into LDS (16-byte vectors, 16 threads per row;
+  //      zero past T), beta and the cumulative log decay
+  // A chunk the phase-1 sweep took as pinned (marked 2) starts from d_min,
+  // and its mark guarantees that every step clips back to d_min (the mark
+  // tests the replay's own fp32 expression at the largest key square), so
+  // its residual is E = (d_min - 1) k, computed here in parallel and bitwise
+  // equal to the token-by-token replay below.
+  const bool pinned = EMIT && __builtin_amdgcn_readfirstlane(ppin) == 2;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int vi = tid + 256 * p, i = vi >> 4, c8 = 8 * (vi & 15);
-    const int64_t off = base + (i < Lc ? i : 0) * tstride + c8;
-    const bf16x8 x = ld8(gkt + off), y = ld8(gk + off);
-    *reinterpret_cast<bf16x8 *>(&sKh[i][c8]) = i < Lc ? x : bf16x8{};
-    *reinterpret_cast<bf16x8 *>(&sKl[i][c8]) = i < Lc ? y : bf16x8{};
-  }
+    *reinterpret_cast<bf16x8 *>(&sKl[i][c8]) = i < Lc ? px[p] : bf16x8{};
+    if constexpr (EMIT) {
+      if (pinned) {
+        const float dm1 = em.d_min - 1.0f;  // exact on [0.5, 2]
+        bf16x8 e;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) e[q] = to_bf16(dm1 * to_f32(px[p][q]));
+        *reinterpret_cast<bf16x8 *>(&sKh[i][c8]) = i < Lc ? e : bf16x8{};
+      }
+    } else {
+      // write keys (with the residual form k~ = k + E both k and E are exact
+      // bf16 operands, so the Gram is K E^T + K K^T; otherwise the bf16 k~
+      // rows themselves)
+      *reinterpret_cast<bf16x8 *>(&sKh[i][c8]) = i < Lc ? pe[p] : bf16x8{};
+    }
   }
   if (w == 0) {
     const bool ok = l < Lc;
-    const int64_t gi = (b * T + t0 + (ok ? l : 0)) * H + h;
-    const float bt = a.beta[gi];
-    sBeta[l] = ok ? bt : 0.0f;
+    sBeta[l] = ok ? pb : 0.0f;
     if constexpr (GATED) {
-      const float al = a.alpha[gi];
-      float x = ok ? logf(al) : 0.0f;
+      float x = ok ? logf(pa) : 0.0f;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(x, off, 64);
@@ -192,7 +176,48 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
       sG[l] = x;
     }
   }
+  if constexpr (EMIT) {
+    // step scalars and retention of the chunk's tokens, for the replay
+    if (!pinned && tid < C) {
+      const int64_t gi = (b * T + t0 + (tid < Lc ? tid : 0)) * H + h;
+      sC[tid] = em.cstep[gi];
+      sR[tid] = em.r ? em.r[gi] : 1.0f;
+    }
+  }
+  if (ci + (int64_t)gridDim.x < nch) fetch(ci + gridDim.x);
   __syncthreads();
+  if constexpr (EMIT) {
+    // the replay of d through the chunk (EMIT, chunks not pinned): one thread
+    // per coordinate, d_{t+1} = clip(r_t d_t + c_t k_t^2), writing E
+    if (!pinned) {
+      if (tid < KD) {
+        const int c = tid;
+        float d = em.dstart[ci * KD + c];
+        const float lo = em.clamp ? em.d_min : -INFINITY, hi = em.clamp ? em.d_max : INFINITY;
+        auto step = [&](int u) {
+          const float kv = to_f32(sKl[u][c]);
+          sKh[u][c] = to_bf16((d - 1.0f) * kv);  // d - 1 is exact on [0.5, 2]
+          d = fminf(fmaxf(fmaf(sC[u], kv * kv, sR[u] * d), lo), hi);
+        };
+        if (Lc == C) {
+          // straight-line: the LDS reads, which do not depend on d, run ahead
+#pragma unroll
+          for (int u = 0; u < C; ++u) step(u);
+        } else {
+          for (int u = 0; u < Lc; ++u) step(u);
+          for (int u = Lc; u < C; ++u) sKh[u][c] = to_bf16(0.0f);
+        }
+      }
+      __syncthreads();
+    }
+    // the residual rows, for the sweep kernel
+    bf16 *res = em.res + base;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int vi = tid + 256 * p, i = vi >> 4, c8 = 8 * (vi & 15);
+      if (i < Lc) *reinterpret_cast<bf16x8 *>(res + i * tstride + c8) = ld8(&sKh[i][c8]);
+    }
+  }
 
   // Gram tiles (rt, tj), tj <= rt, three or two per wave so that every wave
   // has a similar share and its product chains interleave:
@@ -311,11 +336,13 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
   }
   __syncthreads();
   // Tm rows to the workspace: 64 x 64 bf16, two 16-byte vectors per thread
-  bf16 *dst = tout + (seq * N + n) * (C * C);
+  bf16 *dst = tout + ci * (C * C);
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int v = tid + 256 * p, r = v >> 3, c8 = (v & 7) * 8;
     *reinterpret_cast<bf16x8 *>(dst + r * C + c8) = ld8(&sTr[r][c8]);
+  }
+  __syncthreads();  // the next chunk's rows overwrite Tm's buffers
   }
 }
 
@@ -824,11 +851,29 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
   }
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 template <bool GATED, bool KRES>
 void launch_both(const ChunkArgs &a, bf16 *tw, int64_t N, hipStream_t s, const EmitArgs *em) {
   const int64_t nseq = a.B * a.H;
   if (N > 0) {
-    const dim3 grid((unsigned)(nseq * N)), block(256);
+    // persistent UT transform: as many workgroups as fit on the device at
+    // once, each taking an equal number of chunks
+    const int64_t nch = nseq * N;
+    const int64_t slots = (int64_t)device_cus() * ((160 * 1024) / TinvLay::TOTAL);
+    const int64_t per = (nch + slots - 1) / slots;
+    const dim3 grid((unsigned)((nch + per - 1) / per)), block(256);
     if constexpr (KRES) {
       if (em) {
         hipLaunchKernelGGL((chunk_tinv_kernel<GATED, true, true>), grid, block, 0, s, a, tw, N, *em);
