@@ -109,6 +109,100 @@ __global__ __launch_bounds__(64) void scan_prep_kernel(ScanArgs a, ScanWork wk, 
   if (lane == 0) wk.pin[seq * N + n] = pinned ? 1 : 0;
 }
 
+// Sum / max over each row of 16 lanes, every lane of the row receiving it
+// (DPP: quad [1,0,3,2], quad [2,3,0,1], half-row mirror, row mirror).
+template <int CTL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x141>(x);
+  return x + dpp_f<0x140>(x);
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));
+  x = fmaxf(x, dpp_f<0x4E>(x));
+  x = fmaxf(x, dpp_f<0x141>(x));
+  return fmaxf(x, dpp_f<0x140>(x));
+}
+
+// The same pass for K = 128, four chunks per workgroup (one per wave).  Lane
+// l reads 8 consecutive coordinates (chunk l % 16) of token row 4 p + l / 16,
+// so each load instruction covers four whole rows (rows of many tokens in one
+// instruction cost several times more), and a token's sums need only a
+// 16-lane reduction.  The per-token results pass through LDS to lane = token.
+template <typename TIn, bool HAS_R>
+__global__ __launch_bounds__(256) void scan_prep128_kernel(ScanArgs a, ScanWork wk, int64_t N) {
+  __shared__ float sred[4][2][CH];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t ci = (int64_t)blockIdx.x * 4 + w;
+  const int64_t H = a.H, T = a.T;
+  if (ci >= a.B * H * N) return;
+  const int64_t seq = ci / N, n = ci - seq * N;
+  const int64_t b = seq / H, h = seq - b * H;
+  const int64_t t0 = n * CH;
+  const int L = (int)((T - t0) < CH ? (T - t0) : CH);
+  const bool tok = lane < L;
+  const int64_t stride = H * 128;
+  const TIn *kp = static_cast<const TIn *>(a.k) + ((b * T + t0) * H + h) * 128 + 8 * (lane & 15);
+  const int64_t gi = (b * T + t0 + (tok ? lane : 0)) * H + h;
+  const float bt = a.beta[gi];
+  const float rt = HAS_R ? a.r[gi] : 1.0f;
+  float x[16][8];
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const int r = 4 * p + (lane >> 4);
+    const TIn *rp = kp + (r < L ? r : L - 1) * stride;
+    if constexpr (sizeof(TIn) == 2) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8 *>(rp);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[p][e] = to_f32(v[e]);
+    } else {
+      const floatx4 v0 = *reinterpret_cast<const floatx4 *>(rp);
+      const floatx4 v1 = *reinterpret_cast<const floatx4 *>(rp + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[p][e] = v0[e];
+        x[p][4 + e] = v1[e];
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    float pn = 0.0f, pm = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float sq = x[p][e] * x[p][e];
+      pn += sq;
+      pm = fmaxf(pm, sq);
+    }
+    // over the 16 lanes of a row: DPP quad swaps, half-row and row mirrors
+    pn = row16_sum(pn);
+    pm = row16_max(pm);
+    if ((lane & 15) == 0) {
+      sred[w][0][4 * p + (lane >> 4)] = pn;
+      sred[w][1][4 * p + (lane >> 4)] = pm;
+    }
+  }
+  const float nrm = sred[w][0][lane];  // |k_{t0+lane}|^2 (this wave's own LDS)
+  const float smx = sred[w][1][lane];  // max_i k_{t0+lane,i}^2
+  const float dmin = a.d_min;
+  const float bpr = a.beta_aware ? bt : 1.0f;
+  const float ea = a.eta * bpr / fmaxf(nrm, a.eps);
+  const float eb = ea * bpr;
+  const float cpin = fmaf(-eb, dmin * nrm, ea);
+  const bool stays = !tok || fmaf(cpin, cpin > 0.0f ? smx : 0.0f, rt * dmin) <= dmin;
+  const bool pinned = a.clamp != 0 && __all(stays) != 0;
+  if (tok) {
+    wk.norm[gi] = nrm;
+    wk.cstep[gi] = cpin;
+  }
+  if (lane == 0) wk.pin[ci] = pinned ? 1 : 0;
+}
+
 // ---------------------------------------------------------------- solve
 // Shared memory: the chunk's key rows as loaded (TIn [CH][64 EPL]), the key
 // squares of the free coordinates in bf16 ([CH][64 EPL + 8]), their Gram
@@ -559,8 +653,13 @@ hipError_t launch_all(const ScanArgs &a, const ScanWork &w, hipStream_t s, bool 
   const int64_t N = (a.T + CH - 1) / CH;
   const int64_t nseq = a.B * a.H;
   if (N > 0) {
-    hipLaunchKernelGGL((scan_prep_kernel<TIn, EPL, FULL, HAS_R>), dim3((unsigned)(nseq * N)), dim3(64), 0, s,
-                       a, w, N);
+    if (a.K == 128) {
+      hipLaunchKernelGGL((scan_prep128_kernel<TIn, HAS_R>), dim3((unsigned)((nseq * N + 3) / 4)), dim3(256), 0, s,
+                         a, w, N);
+    } else {
+      hipLaunchKernelGGL((scan_prep_kernel<TIn, EPL, FULL, HAS_R>), dim3((unsigned)(nseq * N)), dim3(64), 0, s,
+                         a, w, N);
+    }
     prof_mark(s, "scan_prep_kernel");
   }
   constexpr bool PF = Row<TIn, EPL, FULL>::WORDS <= 2;
