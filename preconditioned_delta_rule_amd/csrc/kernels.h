@@ -41,11 +41,14 @@ hipError_t launch_precond_scan(const ScanArgs &a, bool bf16, hipStream_t s);
 // norm and step scalar c (fp32 [B,T,H] each), d at every 64-token chunk start
 // (fp32 [B,H,N,K]), one word per chunk (int [B,H,N]: 1 when the chunk keeps
 // a d that sits on d_min there, rewritten to 2 when the sweep took it so, in
-// which case its d start is not stored), and three counters per (b,h) (int
+// which case its d start is not stored), the same per token (uint64 [B,H,N],
+// bit u for token u of the chunk), and three counters per (b,h) (int
 // [B,H,3]: chunks taken on the pinned, closed-form and token-by-token paths).
 struct ScanWork {
   float *norm, *cstep, *dstart;
-  int *pin, *flags;
+  int *pin;
+  uint64_t *stay;  // [B,H,N]: bit u set when token u of the chunk keeps a d on d_min there
+  int *flags;
 };
 constexpr int SCAN_CHUNK = 64;
 size_t scan_work_bytes(int64_t B, int64_t T, int64_t H, int64_t K);

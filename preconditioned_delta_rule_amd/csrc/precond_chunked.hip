@@ -106,7 +106,11 @@ __global__ __launch_bounds__(64) void scan_prep_kernel(ScanArgs a, ScanWork wk, 
     wk.norm[gi] = nrm;
     wk.cstep[gi] = cpin;
   }
-  if (lane == 0) wk.pin[seq * N + n] = pinned ? 1 : 0;
+  const uint64_t stay = __ballot(stays);
+  if (lane == 0) {
+    wk.pin[seq * N + n] = pinned ? 1 : 0;
+    wk.stay[seq * N + n] = a.clamp != 0 ? stay : 0;
+  }
 }
 
 // Sum / max over each row of 16 lanes, every lane of the row receiving it
@@ -200,7 +204,11 @@ __global__ __launch_bounds__(256) void scan_prep128_kernel(ScanArgs a, ScanWork 
     wk.norm[gi] = nrm;
     wk.cstep[gi] = cpin;
   }
-  if (lane == 0) wk.pin[ci] = pinned ? 1 : 0;
+  const uint64_t stay = __ballot(stays);
+  if (lane == 0) {
+    wk.pin[ci] = pinned ? 1 : 0;
+    wk.stay[ci] = a.clamp != 0 ? stay : 0;
+  }
 }
 
 // ---------------------------------------------------------------- solve
@@ -468,10 +476,16 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
       }
     }
 
+    int u_end = L;  // tokens whose step scalar this pass computed
     if (!done) {
-      // token by token, the exact sweep
+      // token by token, the exact sweep.  Once every coordinate sits on d_min
+      // and the prep pass found that each remaining token keeps such a d
+      // there (the same test that pins a whole chunk), the rest of the chunk
+      // leaves d on d_min; those tokens keep the step scalar the prep pass
+      // wrote for exactly that case.
       ++n_seq;
       cst = 0.0f;
+      const uint64_t stay = clamp ? wk.stay[seq * N + n] : 0;
       for (int u = 0; u < L; ++u) {
         float k[EPL], s[EPL], pa = 0.0f;
         lds_get<TIn, EPL>(sR + u * RP + lane * EPL, k);
@@ -490,9 +504,22 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
           if (clamp) xx = fminf(fmaxf(xx, dmin), dmax);
           d[e] = valid[e] ? xx : 0.0f;
         }
+        if (clamp && u + 1 < L) {
+          // tokens u + 1 .. L - 1 all keep d on d_min?
+          const uint64_t rest = (L - u - 1 >= 64 ? ~0ull : ((1ull << (L - u - 1)) - 1)) << (u + 1);
+          if ((stay & rest) == rest) {
+            bool onmin = true;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) onmin = onmin && (!valid[e] || d[e] == dmin);
+            if (__all(onmin)) {
+              u_end = u + 1;
+              break;
+            }
+          }
+        }
       }
     }
-    if (tok) wk.cstep[gi] = cst;
+    if (tok && lane < u_end) wk.cstep[gi] = cst;
     __syncthreads();
     if constexpr (PF) {
       if (pf) {
@@ -693,7 +720,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t scan_work_bytes(int64_t B, int64_t T, int64_t H, int64_t K) {
   const int64_t N = (T + CH - 1) / CH;
   return 2 * align256((size_t)(B * T * H) * 4) + align256((size_t)(B * H * N * K) * 4) +
-         align256((size_t)(B * H * N) * 4) + align256((size_t)(B * H) * 3 * 4);
+         align256((size_t)(B * H * N) * 4) + align256((size_t)(B * H * N) * 8) + align256((size_t)(B * H) * 3 * 4);
 }
 
 ScanWork scan_work_layout(void *base, int64_t B, int64_t T, int64_t H, int64_t K) {
@@ -702,12 +729,14 @@ ScanWork scan_work_layout(void *base, int64_t B, int64_t T, int64_t H, int64_t K
   const size_t tok = align256((size_t)(B * T * H) * 4);
   const size_t dst = align256((size_t)(B * H * N * K) * 4);
   const size_t pin = align256((size_t)(B * H * N) * 4);
+  const size_t stay = align256((size_t)(B * H * N) * 8);
   ScanWork w;
   w.norm = reinterpret_cast<float *>(p);
   w.cstep = reinterpret_cast<float *>(p + tok);
   w.dstart = reinterpret_cast<float *>(p + 2 * tok);
   w.pin = reinterpret_cast<int *>(p + 2 * tok + dst);
-  w.flags = reinterpret_cast<int *>(p + 2 * tok + dst + pin);
+  w.stay = reinterpret_cast<uint64_t *>(p + 2 * tok + dst + pin);
+  w.flags = reinterpret_cast<int *>(p + 2 * tok + dst + pin + stay);
   return w;
 }
 
