@@ -322,8 +322,11 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
       rt = 1.0f;
       nrm = 1.0f;
     }
-    // prefetch the next chunk (rows stay in registers until this one is done)
-    const bool pf = PF && n + 1 < N;
+    // prefetch the next chunk (rows stay in registers until this one is done),
+    // unless the prep pass marked it: if d ends this chunk on d_min the run
+    // of marked chunks is skipped without its rows, else they are loaded then
+    const bool next_marked = ((n + 1) & 63) != 0 && ((pinmask >> ((n + 1) & 63)) & 1) != 0;
+    const bool pf = PF && n + 1 < N && !next_marked;
     if constexpr (PF) {
       if (pf) {
         const int64_t t1 = t0 + CH;
