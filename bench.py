@@ -117,7 +117,7 @@ def pmc_summary(fetch_dir, write_dir, workload, command):
                 for row in csv.DictReader(f):
                     if row.get("Counter_Name") != counter:
                         continue
-                    name = row["Kernel_Name"]
+                    name = row["Kernel_Name"].replace("scan_prep128_kernel", "scan_prep_kernel")
                     key = None
                     for k in KERNEL_SOURCE:
                         if k in name:
