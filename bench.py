@@ -29,6 +29,15 @@ fraction (peak 2.5 PFLOP/s dense) is reported beside it for phase 2.
 
 Per-kernel durations come from HIP events the library records on the launch
 stream around every kernel of the timed steps (osdn_profile_begin/end).
+
+With --decode a step is instead one osdn_decode call (the single-token
+recurrence): T new tokens per (b,h) continuing a carried fp32 state, default
+workload one token for each of 256 sequences of the 1.3B-shaped layer
+(B=256, H=16, K=V=128, bf16, APF).  Its algorithmic bytes per (b,h) are the
+state read and written once, 2 * 4 V K + 2 * 4 K, plus per token q, k (elem K
+each), v, o (elem V each), beta (+ r, + alpha) 4 B; HBM bounds it.  The state
+ping-pongs between two buffers, so every call reads the state the previous
+one wrote.
 """
 from __future__ import annotations
 
@@ -48,6 +57,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "OSDN fwd tokens/sec (phase1+phase2) at H=16,K=V=128,T=4096; % HBM/MFMA roofline"
+DECODE_METRIC = "OSDN decode tokens/sec (osdn_decode, new tokens x sequences per call) at H=16,K=V=128; % HBM roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 # where each kernel's source lives (for matching committed counter summaries)
@@ -57,6 +67,7 @@ KERNEL_SOURCE = {
     "scan_emit_kernel": "preconditioned_delta_rule_amd/csrc/precond_chunked.hip",
     "chunk_tinv_kernel": "preconditioned_delta_rule_amd/csrc/chunk_wy.hip",
     "chunk_seq_kernel": "preconditioned_delta_rule_amd/csrc/chunk_wy.hip",
+    "decode_kernel": "preconditioned_delta_rule_amd/csrc/decode.hip",
 }
 COPY_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written
 
@@ -82,6 +93,12 @@ def kernel_work(name, K, V, C, apf, gated, elem=2):
     if name == "chunk_seq_kernel":
         return elem * (3 * K + V) + 4 + elem * V + g, 2 * (3 * K * V + C * K + 2 * C * V)
     return 0, 0
+
+
+def decode_work(K, V, T, apf, gated, elem=2):
+    """Algorithmic bytes of one osdn_decode call per (b,h)."""
+    return 8 * V * K + 8 * K + T * (2 * elem * K + 2 * elem * V + 4 + (4 if apf else 0)
+                                    + (4 if gated else 0))
 
 
 def source_sha(path):
@@ -130,9 +147,13 @@ def pmc_summary(fetch_dir, write_dir, workload, command):
     fetch, write = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
     if "copy" not in fetch or "copy" not in write:
         raise SystemExit("no calibration copy kernel in the counter runs")
-    # counters are in KiB per dispatch; the plain copy moves COPY_BYTES each way
-    fscale = COPY_BYTES / (1024.0 * float(np.median(fetch["copy"])))
-    wscale = COPY_BYTES / (1024.0 * float(np.median(write["copy"])))
+    # counters are in KiB per dispatch; the plain copy moves COPY_BYTES each
+    # way (small copies, e.g. input uploads, and the fill are left out)
+    def calib(vals):
+        big = [v for v in vals if v >= 0.25 * max(vals)]
+        return float(np.median(big))
+    fscale = COPY_BYTES / (1024.0 * calib(fetch["copy"]))
+    wscale = COPY_BYTES / (1024.0 * calib(write["copy"]))
     kernels = {}
     for k in KERNEL_SOURCE:
         if k in fetch and k in write:
@@ -156,8 +177,9 @@ def pmc_summary(fetch_dir, write_dir, workload, command):
 
 def cpu_baseline(inp, min_seconds):
     """The CPU oracle (fp64, one (b,h) sequence per thread) on the whole
-    workload, repeated until `min_seconds` of wall time; returns tokens/s,
-    the thread count, the wall time and the repetitions."""
+    workload (from its carried state, if any), repeated until `min_seconds`
+    of wall time; returns tokens/s, the thread count, the wall time and the
+    repetitions."""
     import oracle
     B, T, H, _ = inp["k"].shape
     threads = min(B * H, oracle.default_threads())
@@ -166,6 +188,7 @@ def cpu_baseline(inp, min_seconds):
     while wall < min_seconds or reps == 0:
         t0 = time.perf_counter()
         oracle.forward(inp["q"], inp["k"], inp["v"], inp["beta"], inp["r"], inp["alpha"],
+                       inp["d1"], inp["S0"],
                        eta=p["eta"], d_min=p["d_min"], d_max=p["d_max"], clamp=p["clamp"],
                        eps=p["eps"], beta_aware=p["beta_aware"], q_scale=p["q_scale"],
                        threads=threads)
@@ -179,7 +202,10 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="1p3b_apf")
+    ap.add_argument("--workload", default=None,
+                    help="named workload (default 1p3b_apf; with --decode decode_1p3b_b256)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time osdn_decode (one call per step) instead of osdn_fwd")
     ap.add_argument("--copies", type=int, default=4,
                     help="input sets rotated between steps (keeps the 256 MB MALL from "
                          "serving repeated reads)")
@@ -194,6 +220,8 @@ def main(argv=None):
     ap.add_argument("--pmc-command", default="",
                     help="the commands that produced the --pmc-summary runs (recorded)")
     args = ap.parse_args(argv)
+    if args.workload is None:
+        args.workload = "decode_1p3b_b256" if args.decode else "1p3b_apf"
 
     if args.pmc_summary:
         return pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, args.pmc_command)
@@ -226,6 +254,9 @@ def main(argv=None):
 
     def up(x, dt):
         return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dt).to(dev)
+
+    if args.decode:
+        return decode_bench(args, inp, dev)
 
     sets = []
     for c in range(max(1, args.copies)):
@@ -328,6 +359,96 @@ def main(argv=None):
                    "step_device_ms_p10": float(np.percentile(step_ms, 10)) if step_ms else None,
                    "step_device_ms_p90": float(np.percentile(step_ms, 90)) if step_ms else None},
         "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def decode_bench(args, inp, dev):
+    """--decode: one osdn_decode call per step on a decode workload."""
+    import torch
+    import preconditioned_delta_rule_amd as osdn
+    spec, p = inp["spec"], inp["params"]
+    B, T, H, K = inp["k"].shape
+    V = inp["v"].shape[-1]
+    apf, gated = inp["r"] is not None, inp["alpha"] is not None
+    tdt = torch.bfloat16 if p["dtype"] == "bf16" else torch.float32
+    elem = 2 if p["dtype"] == "bf16" else 4
+
+    def up(x, dt):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dt).to(dev)
+
+    sets = [dict(q=up(inp["q"], tdt), k=up(inp["k"], tdt), v=up(inp["v"], tdt),
+                 beta=up(inp["beta"], torch.float32), r=up(inp["r"], torch.float32),
+                 alpha=up(inp["alpha"], torch.float32),
+                 o=torch.empty((B, T, H, V), dtype=tdt, device=dev))
+            for _ in range(max(1, args.copies))]
+    # two state buffers in turn: each call reads what the previous one wrote
+    S = [up(inp["S0"], torch.float32), torch.empty((B, H, V, K), dtype=torch.float32, device=dev)]
+    d = [up(inp["d1"], torch.float32), torch.empty((B, H, K), dtype=torch.float32, device=dev)]
+    kw = dict(eta=p["eta"], d_min=p["d_min"], d_max=p["d_max"], clamp=p["clamp"], eps=p["eps"],
+              q_scale=p["q_scale"], beta_aware=p["beta_aware"])
+
+    def step(i):
+        s = sets[i % len(sets)]
+        a, b = i % 2, (i + 1) % 2
+        osdn.decode(s["q"], s["k"], s["v"], s["beta"], s["r"], s["alpha"], d[a], S[a],
+                    o=s["o"], S_out=S[b], d_out=d[b], **kw)
+
+    if args.pmc_pass:
+        for i in range(max(1, args.steps)):
+            step(i)
+        x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        return 0
+
+    log("warmup", args.warmup)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    nsteps = args.steps
+    log("timing %d decode calls" % nsteps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    launches = osdn.kernel_times(lambda: [step(i) for i in range(nsteps)], dev)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / nsteps
+    ks = [ms for name, ms in launches if name == "decode_kernel"]
+    kms = float(np.mean(ks))
+    per_seq = decode_work(K, V, T, apf, gated, elem)
+    alg = per_seq * B * H
+    gbs = alg / (kms * 1e-3) / 1e9
+    log("call %.4f ms, kernel %.4f ms, %.0f GB/s" % (ms_step, kms, gbs))
+    tr = load_traffic(args.workload, "decode_kernel")
+    roofline = {"bound": "hbm", "kernel": "decode_kernel", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                "traffic": tr["bytes_per_launch"] / (kms * 1e-3) / 1e9 if tr else None,
+                "algorithmic_bytes_per_launch": alg,
+                "measured_bytes_per_launch": tr["bytes_per_launch"] if tr else None}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu oracle on the whole decode workload (%d sequences x %d tokens)" % (B * H, T))
+        tps, threads, cwall, reps = cpu_baseline(inp, args.cpu_seconds)
+        cpu = {"value": tps, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": "whole workload: %d (b,h) sequences x %d new token(s) from the carried "
+                         "state, fp64 sequential oracle, one sequence per thread, %d run(s) in "
+                         "%.2f s wall" % (B * H, T, reps, cwall)}
+    out = {
+        "metric": DECODE_METRIC, "value": B * T / (ms_step * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": nsteps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": p["dtype"],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": V,
+                   "apf": apf, "gated": gated, "seed": spec["seed"], "input_copies": len(sets)},
+        "roofline": roofline, "cpu_baseline": cpu,
+        "kernels": {"decode_kernel": {"ms": kms, "ms_median": float(np.median(ks)),
+                                      "ms_p10": float(np.percentile(ks, 10)),
+                                      "ms_p90": float(np.percentile(ks, 90)),
+                                      "bytes_per_sequence": per_seq, "GB/s": gbs}},
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -189,6 +189,36 @@ osdn_status osdn_fwd(const osdn_desc *desc, const void *q, const void *k,
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Decode step: the single-token recurrence of Appendix L (one launch per
+ * call), for up to OSDN_DECODE_MAX_T new tokens per (b,h) continuing from a
+ * carried state.  Per (b,h) and token, in order: the write key d (.) k_t, the
+ * phase-1 update of d (as in osdn_precond_scan), then the phase-2 write and
+ * readout (as in osdn_chunk_fwd, token by token).  The result is that of
+ * osdn_fwd on the same tokens from the same (d1, S0) up to fp32 rounding; the
+ * write keys stay in fp32 here (they are never rounded to dtype).
+ *   q, k    [B,T,H,K] dtype      queries, keys
+ *   v       [B,T,H,V] dtype      values
+ *   beta    [B,T,H]   f32        write gates
+ *   r       [B,T,H]   f32        APF retention, or NULL for r = 1
+ *   alpha   [B,T,H]   f32        state decay in (0,1], or NULL (OSDN)
+ *   d1      [B,H,K]   f32        carried preconditioner, or NULL for ones
+ *   S0      [B,H,V,K] f32        carried state, or NULL for zeros
+ *   o       [B,T,H,V] dtype      OUT: readouts
+ *   S_out   [B,H,V,K] f32        OUT: state after the last token, or NULL
+ *                                (may alias S0: in-place update)
+ *   d_out   [B,H,K]   f32        OUT: d after the last token, or NULL (may
+ *                                alias d1)
+ * The descriptor is validated as for osdn_fwd (desc->chunk is not used);
+ * T > OSDN_DECODE_MAX_T or B*H >= 2^31 returns OSDN_EUNSUPPORTED.  T = 0
+ * copies d1 to d_out and S0 to S_out.  No workspace.
+ */
+#define OSDN_DECODE_MAX_T 64
+osdn_status osdn_decode(const osdn_desc *desc, const void *q, const void *k,
+                        const void *v, const float *beta, const float *r,
+                        const float *alpha, const float *d1, const float *S0,
+                        void *o, float *S_out, float *d_out, void *stream);
+
+/*
  * Launch profile (measurement aid).  osdn_profile_begin records a HIP event on
  * `stream`; until osdn_profile_end, every kernel the library launches from
  * the calling thread records another event on its stream right after the

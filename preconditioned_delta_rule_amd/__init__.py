@@ -20,7 +20,7 @@ import os
 import torch
 
 __all__ = ["precond_scan", "precond_scan_workspace_bytes", "scan_counters", "chunk_fwd",
-           "chunk_fwd_workspace_bytes", "fwd", "kernel_times", "fwd_workspace_bytes", "fwd_scan_counters", "Desc", "OsdnError",
+           "chunk_fwd_workspace_bytes", "fwd", "decode", "DECODE_MAX_T", "kernel_times", "fwd_workspace_bytes", "fwd_scan_counters", "Desc", "OsdnError",
            "library_path", "load", "F32", "BF16"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -29,11 +29,12 @@ _lib = None
 
 F32, BF16 = 0, 1
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
+DECODE_MAX_T = 64  # OSDN_DECODE_MAX_T
 
 SYMBOLS = ("osdn_desc_init", "osdn_validate", "osdn_precond_scan",
            "osdn_precond_scan_workspace_bytes", "osdn_precond_scan_counters_offset",
            "osdn_chunk_fwd", "osdn_chunk_fwd_workspace_bytes", "osdn_fwd_workspace_bytes",
-           "osdn_fwd", "osdn_profile_begin", "osdn_profile_end", "osdn_status_str",
+           "osdn_fwd", "osdn_decode", "osdn_profile_begin", "osdn_profile_end", "osdn_status_str",
            "osdn_last_error", "osdn_version")
 
 
@@ -81,6 +82,7 @@ def load():
     lib.osdn_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.osdn_fwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp, vp,
                              ctypes.c_size_t, vp]
+    lib.osdn_decode.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp]
     lib.osdn_profile_begin.argtypes = [vp]
     lib.osdn_profile_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
                                      ci, ctypes.POINTER(ci)]
@@ -89,7 +91,7 @@ def load():
     lib.osdn_last_error.argtypes = []
     lib.osdn_last_error.restype = ctypes.c_char_p
     for name in ("osdn_desc_init", "osdn_validate", "osdn_precond_scan", "osdn_chunk_fwd",
-                 "osdn_fwd", "osdn_profile_begin", "osdn_profile_end", "osdn_version"):
+                 "osdn_fwd", "osdn_decode", "osdn_profile_begin", "osdn_profile_end", "osdn_version"):
         getattr(lib, name).restype = ci
     _lib = lib
     return lib
@@ -288,6 +290,40 @@ def fwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, chunk=64, eta=0.
                            _ptr(alpha), _ptr(d1), _ptr(S0), _ptr(o), _ptr(S_out), _ptr(d_out),
                            _ptr(k_tilde_out), _ptr(workspace),
                            ctypes.c_size_t(_nbytes(workspace)), _stream(dev)))
+    return o, S_out, d_out
+
+
+def decode(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, eta=0.003, d_min=0.5,
+           d_max=2.0, clamp=True, eps=1e-6, q_scale=1.0, beta_aware=True, o=None, S_out=None,
+           d_out=None):
+    """Decode step (the single-token recurrence, one launch): T <= DECODE_MAX_T
+    new tokens per (b,h) from the carried (d1, S0).  Shapes as in fwd.  Pass
+    S_out=S0 and d_out=d1 to update the state in place.
+    Returns (o, S_out, d_out)."""
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dev, dt, f32 = q.device, q.dtype, torch.float32
+    _need(k, "k", (B, T, H, K), dt, dev)
+    _need(v, "v", (B, T, H, V), dt, dev)
+    _need(beta, "beta", (B, T, H), f32, dev)
+    _need(r, "r", (B, T, H), f32, dev)
+    _need(alpha, "alpha", (B, T, H), f32, dev)
+    _need(d1, "d1", (B, H, K), f32, dev)
+    _need(S0, "S0", (B, H, V, K), f32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, V), dtype=dt, device=dev)
+    if S_out is None:
+        S_out = torch.empty((B, H, V, K), dtype=f32, device=dev)
+    if d_out is None:
+        d_out = torch.empty((B, H, K), dtype=f32, device=dev)
+    _need(o, "o", (B, T, H, V), dt, dev)
+    _need(S_out, "S_out", (B, H, V, K), f32, dev)
+    _need(d_out, "d_out", (B, H, K), f32, dev)
+    desc = make_desc(B, T, H, K, V, dtype=_dtype_code(q), eta=eta, d_min=d_min, d_max=d_max,
+                     clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware)
+    _check(load().osdn_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r),
+                              _ptr(alpha), _ptr(d1), _ptr(S0), _ptr(o), _ptr(S_out), _ptr(d_out),
+                              _stream(dev)))
     return o, S_out, d_out
 
 

@@ -76,6 +76,22 @@ hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s);
 size_t chunk_wy_work_bytes(int64_t B, int64_t T, int64_t H);
 hipError_t launch_chunk_wy(const ChunkArgs &a, void *work, hipStream_t s, const EmitArgs *emit = nullptr);
 
+// Decode step: up to 64 tokens per (b,h) through the recurrent form from a
+// carried (d, S), one workgroup per (b,h) (K, V <= 128).
+struct DecodeArgs {
+  const void *q, *k, *v;      // [B,T,H,K] / [B,T,H,V]
+  const float *beta;          // [B,T,H]
+  const float *r, *alpha;     // [B,T,H] or null
+  const float *d1, *S0;       // [B,H,K], [B,H,V,K] or null (ones, zeros)
+  void *o;                    // [B,T,H,V]
+  float *d_out, *S_out;       // or null; may alias d1, S0
+  int64_t B, T, H, K, V;
+  float eta, d_min, d_max, eps, q_scale;
+  int clamp, beta_aware;
+  int tb;                     // tokens staged per block (set by the launcher)
+};
+hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t s);
+
 // Shape coverage of the specialised MFMA path (bf16, K = V = 128, C = 64).
 bool chunk_mfma_supported(const ChunkArgs &a, bool bf16);
 

@@ -398,4 +398,59 @@ osdn_status osdn_fwd(const osdn_desc *d, const void *q, const void *k, const voi
   return ok();
 }
 
+osdn_status osdn_decode(const osdn_desc *d, const void *q, const void *k, const void *v, const float *beta,
+                        const float *r, const float *alpha, const float *d1, const float *S0, void *o,
+                        float *S_out, float *d_out, void *stream) {
+  OSDN_TRY(validate(d, 3));
+  if (d->T > OSDN_DECODE_MAX_T)
+    return fail(OSDN_EUNSUPPORTED, "osdn_decode takes at most %d tokens (got T=%lld)", OSDN_DECODE_MAX_T,
+                (long long)d->T);
+  if ((double)d->B * (double)d->H > 2147483647.0)
+    return fail(OSDN_EUNSUPPORTED, "osdn_decode supports B*H < 2^31 (got %lld)", (long long)(d->B * d->H));
+  const bool need_seq = d->T > 0;
+  OSDN_TRY(check_ptr(q, "q", need_seq));
+  OSDN_TRY(check_ptr(k, "k", need_seq));
+  OSDN_TRY(check_ptr(v, "v", need_seq));
+  OSDN_TRY(check_ptr(beta, "beta", need_seq));
+  OSDN_TRY(check_ptr(r, "r", false));
+  OSDN_TRY(check_ptr(alpha, "alpha", false));
+  OSDN_TRY(check_ptr(d1, "d1", false));
+  OSDN_TRY(check_ptr(S0, "S0", false));
+  OSDN_TRY(check_ptr(o, "o", need_seq));
+  OSDN_TRY(check_ptr(S_out, "S_out", false));
+  OSDN_TRY(check_ptr(d_out, "d_out", false));
+  if (o && (o == q || o == k || o == v)) return fail(OSDN_EINVAL, "o must not alias an input");
+  if (S_out && (S_out == d1 || static_cast<const void *>(S_out) == o))
+    return fail(OSDN_EINVAL, "S_out may alias S0 only");
+  if (d_out && (d_out == S0 || static_cast<const void *>(d_out) == o))
+    return fail(OSDN_EINVAL, "d_out may alias d1 only");
+  osdn::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.r = r;
+  a.alpha = alpha;
+  a.d1 = d1;
+  a.S0 = S0;
+  a.o = o;
+  a.d_out = d_out;
+  a.S_out = S_out;
+  a.B = d->B;
+  a.T = d->T;
+  a.H = d->H;
+  a.K = d->K;
+  a.V = d->V;
+  a.eta = d->eta;
+  a.d_min = d->d_min;
+  a.d_max = d->d_max;
+  a.eps = d->eps;
+  a.q_scale = d->q_scale;
+  a.clamp = d->clamp ? 1 : 0;
+  a.beta_aware = d->beta_aware ? 1 : 0;
+  OSDN_TRY(hip_status(osdn::launch_decode(a, d->dtype == OSDN_BF16, static_cast<hipStream_t>(stream)),
+                      "decode launch"));
+  return ok();
+}
+
 }  // extern "C"

@@ -173,3 +173,30 @@ def test_profile_end_without_begin_is_rejected(lib):
     n = ctypes.c_int(-1)
     st = lib.osdn_profile_end(None, None, 0, ctypes.byref(n))
     assert st == osdn.EINVAL and "no profile" in lib.osdn_last_error().decode()
+
+
+def test_decode_argument_checks(lib):
+    # decode: at most OSDN_DECODE_MAX_T tokens, required pointers, no aliasing
+    # of outputs with other inputs; all rejected on the host before any launch
+    null = ctypes.c_void_p(None)
+    fake, fake2, fake3 = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
+    d = osdn.Desc()
+    lib.osdn_desc_init(ctypes.byref(d), 2, osdn.DECODE_MAX_T + 1, 4, 128, 128)
+    args = [fake, fake, fake, fake2, null, null, null, null, fake3, null, null, null]
+    assert lib.osdn_decode(ctypes.byref(d), *args) == osdn.EUNSUPPORTED
+    assert "at most" in lib.osdn_last_error().decode()
+    d.T = 1
+    st = lib.osdn_decode(ctypes.byref(d), fake, null, fake, fake2, null, null, null, null, fake3,
+                         null, null, null)
+    assert st == osdn.EINVAL and "k must not be NULL" in lib.osdn_last_error().decode()
+    st = lib.osdn_decode(ctypes.byref(d), fake, fake, fake, fake2, null, null, null, null, fake,
+                         null, null, null)
+    assert st == osdn.EINVAL and "alias" in lib.osdn_last_error().decode()
+    st = lib.osdn_decode(ctypes.byref(d), fake, fake, fake, fake2, null, null, ctypes.c_void_p(0x4000),
+                         null, fake3, ctypes.c_void_p(0x4000), null, null)
+    assert st == osdn.EINVAL and "S_out may alias S0 only" in lib.osdn_last_error().decode()
+    st = lib.osdn_decode(ctypes.byref(d), fake, fake, fake, fake2, null, null, null, null, fake3,
+                         null, ctypes.c_void_p(0x4004), null)
+    assert st == osdn.EINVAL and "aligned" in lib.osdn_last_error().decode()
+    d.K = 129
+    assert lib.osdn_decode(ctypes.byref(d), *args) == osdn.EUNSUPPORTED

@@ -11,7 +11,11 @@ Recipe (same for every named workload unless stated):
     q, k, v are rounded to bfloat16 with round-to-nearest-even;
   * beta = sigmoid(N(mu_b, 1)), retention r = sigmoid(N(2, 1)) when APF is on,
     Gated-DeltaNet decay alpha = exp(-softplus(N(0,1)) * 0.1);
-  * d_1 = 1, S_0 = 0, eta = 0.003, box [0.5, 2], eps = 1e-6.
+  * d_1 = 1, S_0 = 0, eta = 0.003, box [0.5, 2], eps = 1e-6;
+  * decode workloads (a few new tokens continuing a carried state) draw their
+    tokens the same way and the state with ``random_state``: a second
+    generator ``default_rng(seed + 1)`` draws d_1 ~ U(0.6, 1.9) per coordinate
+    (inside the box), then S_0 ~ 0.3 N(0, 1), both float32.
 
 Float arrays are returned as float32 holding the exact (bf16-representable, for
 bf16 workloads) values that the device receives.
@@ -35,12 +39,18 @@ WORKLOADS = {
                      seed=4, apf=True),
     "long_apf_gdn": dict(B=1, T=20480, H=16, K=128, V=128, dtype="bf16",
                          chunk=64, seed=4, apf=True, gdn=True),
+    # decode: one new token per sequence of the 1.3B-shaped layer, carrying a
+    # state; the small batch and a serving batch of 256 sequences
+    "decode_1p3b": dict(B=4, T=1, H=16, K=128, V=128, dtype="bf16", chunk=64,
+                        seed=5, apf=True, state=True),
+    "decode_1p3b_b256": dict(B=256, T=1, H=16, K=128, V=128, dtype="bf16",
+                             chunk=64, seed=6, apf=True, state=True),
 }
 
 DEFAULTS = dict(eta=0.003, d_min=0.5, d_max=2.0, eps=1e-6, clamp=True,
                 beta_aware=True, q_scale=1.0, keys="normal", beta_mu=0.0,
                 apf=False, apf_const=None, gdn=False, dtype="f32", chunk=64,
-                seed=0, onehot_bias=None, sparse_nnz=3)
+                seed=0, onehot_bias=None, sparse_nnz=3, state=False)
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
@@ -166,8 +176,22 @@ def make_inputs(name_or_spec, *, T=None, B=None, H=None) -> dict:
                                        "beta_aware", "q_scale", "chunk", "dtype")}
     if params["q_scale"] == "rsqrt_k":
         params["q_scale"] = 1.0 / math.sqrt(K)
-    return dict(q=q, k=k, v=v, beta=beta, r=r, alpha=alpha, d1=None, S0=None,
-                params=params, spec=s)
+    out = dict(q=q, k=k, v=v, beta=beta, r=r, alpha=alpha, d1=None, S0=None,
+               params=params, spec=s)
+    if s["state"]:
+        out["d1"], out["S0"] = random_state(out, seed=s["seed"] + 1)
+    return out
+
+
+def random_state(inputs: dict, seed: int = 0, s_scale: float = 0.3):
+    """A carried state for the shapes of `inputs`: d_1 ~ U(0.6, 1.9) [B,H,K]
+    and S_0 ~ s_scale * N(0, 1) [B,H,V,K], float32, from default_rng(seed)."""
+    B, _, H, K = inputs["k"].shape
+    V = inputs["v"].shape[-1]
+    rng = np.random.default_rng(seed)
+    d1 = rng.uniform(0.6, 1.9, (B, H, K)).astype(np.float32)
+    S0 = (np.float32(s_scale) * rng.standard_normal((B, H, V, K), dtype=np.float32)).astype(np.float32)
+    return d1, S0
 
 
 def sample_sequences(inputs: dict, pairs) -> dict:
