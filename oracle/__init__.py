@@ -6,6 +6,8 @@ Attention" (arXiv:2605.13473).  The arithmetic lives in ``osdn_oracle.c``
 (phase 1: Section 4.2 Eq.(4), Algorithm 1, Section 4.4 Eq.(7), Appendix B;
 phase 2: Eq.(5), Appendix C Algorithm 2 (2b), Appendix B.1); this module only
 builds that file with gcc and marshals numpy arrays through ctypes.
+``osdn_oracle_bwd.c`` (same library) holds the backward pass: reverse-mode
+derivatives of that forward, pinned by finite differences of it.
 ``chunk_model.py`` holds an independent fp64 NumPy statement of the chunkwise
 WY form (Appendix A.2 Eqs.(8)-(11), Appendix B.1 Eqs.(13)-(15)).
 
@@ -23,6 +25,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "osdn_oracle.c")
+_SRC_BWD = os.path.join(_HERE, "osdn_oracle_bwd.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
@@ -30,11 +33,12 @@ _dp = ctypes.POINTER(ctypes.c_double)
 
 
 def build(force: bool = True) -> str:
-    """Compile osdn_oracle.c into liboracle.so with gcc (OpenMP over sequences)."""
+    """Compile osdn_oracle.c and osdn_oracle_bwd.c into liboracle.so with gcc
+    (OpenMP over sequences)."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
-               "-o", tmp, _SRC, "-lm"]
+               "-o", tmp, _SRC, _SRC_BWD, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -54,13 +58,20 @@ def bind(lib):
     lib.osdn_oracle_diagnostics.argtypes = [
         i64, i64, i64, i64, i64, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
     lib.osdn_oracle_diagnostics.restype = ci
+    if hasattr(lib, "osdn_oracle_backward"):
+        lib.osdn_oracle_backward.argtypes = [
+            i64, i64, i64, i64, i64, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+            cd, cd, cd, ci, cd, ci, cd, _dp, _dp, _dp,
+            _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ci]
+        lib.osdn_oracle_backward.restype = ci
     return lib
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(
+                os.path.getmtime(_SRC), os.path.getmtime(_SRC_BWD)):
             build(force=True)
         _lib = bind(ctypes.CDLL(_LIB))
     return _lib
@@ -164,3 +175,40 @@ def forward(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, eta=0.003,
     o, S = delta_rule(q, k, kt, v, beta, alpha, S0, q_scale=q_scale,
                       threads=threads)
     return {"k_tilde": kt, "d": d, "o": o, "S": S}
+
+
+def backward(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, dout, dS=None,
+             dd=None, eta=0.003, d_min=0.5, d_max=2.0, clamp=True, eps=1e-6,
+             beta_aware=True, q_scale=1.0, threads=None):
+    """Gradients of L with dL/do = dout [B,T,H,V], dL/dS_T = dS [B,H,V,K] and
+    dL/dd_{T+1} = dd [B,H,K] (both optional) through the forward above.
+
+    Returns a dict with dq, dk [B,T,H,K], dv [B,T,H,V], dbeta [B,T,H] and, for
+    the inputs given (r, alpha) or always (d1, S0), dr, dalpha [B,T,H],
+    dd1 [B,H,K], dS0 [B,H,V,K] (all fp64).
+    """
+    q, k, v, beta, r, alpha, d1, S0 = map(_f64, (q, k, v, beta, r, alpha, d1, S0))
+    dout, dS, dd = _f64(dout), _f64(dS), _f64(dd)
+    B, T, H, K = k.shape
+    V = v.shape[-1]
+    assert q.shape == k.shape and v.shape == (B, T, H, V) and beta.shape == (B, T, H)
+    assert dout.shape == (B, T, H, V)
+    if dS is not None:
+        assert dS.shape == (B, H, V, K)
+    if dd is not None:
+        assert dd.shape == (B, H, K)
+    out = {"dq": np.zeros((B, T, H, K)), "dk": np.zeros((B, T, H, K)),
+           "dv": np.zeros((B, T, H, V)), "dbeta": np.zeros((B, T, H)),
+           "dr": np.zeros((B, T, H)) if r is not None else None,
+           "dalpha": np.zeros((B, T, H)) if alpha is not None else None,
+           "dd1": np.zeros((B, H, K)), "dS0": np.zeros((B, H, V, K))}
+    rc = _load().osdn_oracle_backward(
+        B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r), _ptr(alpha),
+        _ptr(d1), _ptr(S0), float(eta), float(d_min), float(d_max), int(bool(clamp)),
+        float(eps), int(bool(beta_aware)), float(q_scale), _ptr(dout), _ptr(dS), _ptr(dd),
+        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
+        _ptr(out["dr"]), _ptr(out["dalpha"]), _ptr(out["dd1"]), _ptr(out["dS0"]),
+        int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle backward rejected its arguments (%d)" % rc)
+    return out

@@ -82,3 +82,48 @@ def test_pins_catch_mutation(mutation, tmp_path, monkeypatch):
         except (AssertionError, ValueError, FloatingPointError):
             failed.append(name)
     assert failed, "no pin caught the planted mistake %s" % mutation
+
+
+# ---- backward oracle: each planted mistake must fail a finite-difference pin
+BWD_SRC = os.path.join(os.path.dirname(oracle.__file__), "osdn_oracle_bwd.c")
+BWD_MUTATIONS = {
+    "readout_gradient_missing": [("G[i * K + jj] += q_scale * dot[i] * qt[jj];", "")],
+    "dq_unscaled": [("dqt[jj] = q_scale * acc;", "dqt[jj] = acc;")],
+    "dv_without_gate": [("dvt[i] = bt * acc;", "dvt[i] = acc;")],
+    "write_key_gradient_from_w": [("acc += G[i * K + jj] * uj[i];", "acc += G[i * K + jj] * w[i];")],
+    "read_key_gradient_sign": [("dkt_read[jj] = -bt * acc;", "dkt_read[jj] = bt * acc;")],
+    "residual_term_dropped": [("dSb[i * K + jj] = G[i * K + jj] - bt * w[i] * kt[jj];",
+                               "dSb[i * K + jj] = G[i * K + jj];")],
+    "decay_not_propagated": [("G[e] = at * dSb[e];", "G[e] = dSb[e];")],
+    "decay_gradient_wrong_state": [("da += dSb[e] * Sp[e];", "da += dSb[e] * St[e];")],
+    "clamp_mask_ignored": [("gy[i] = pass ? g[i] : 0.0;", "gy[i] = g[i];")],
+    "norm_floor_ignored": [("nraw > eps ? -c / n : 0.0", "-c / n")],
+    "write_key_path_to_k_missing": [(" + dktil[i] * d[i];", ";")],
+    "retention_not_in_carry": [("+ rt * gy[i] +", "+ gy[i] +")],
+    "beta_aware_step_term_missing": [
+        ("if (beta_aware) dbeta[bw_bth(b, t, h, T, H)] += gc * eta * (1.0 - 2.0 * bp * a) / n;", "")],
+    "alignment_term_missing": [("+ gc * dca * d[i] +", " +")],
+}
+
+
+@pytest.mark.parametrize("mutation", sorted(BWD_MUTATIONS))
+def test_backward_pins_catch_mutation(mutation, tmp_path, monkeypatch):
+    from tests import test_oracle_backward as bpins
+    src = open(BWD_SRC).read()
+    for old, new in BWD_MUTATIONS[mutation]:
+        assert old in src, "mutation anchor missing: %r" % old
+        src = src.replace(old, new, 1)
+    cfile = tmp_path / "mut_bwd.c"
+    cfile.write_text(src)
+    so = tmp_path / "libmutbwd.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-o",
+                    str(so), SRC, str(cfile), "-lm"], check=True)
+    lib = oracle.bind(ctypes.CDLL(str(so)))
+    monkeypatch.setattr(oracle, "_lib", lib)
+    failed = []
+    for name in bpins.CASES:
+        try:
+            bpins.test_backward_matches_finite_differences(name)
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(name)
+    assert failed, "no backward pin caught the planted mistake %s" % mutation
