@@ -30,6 +30,13 @@ fraction (peak 2.5 PFLOP/s dense) is reported beside it for phase 2.
 Per-kernel durations come from HIP events the library records on the launch
 stream around every kernel of the timed steps (osdn_profile_begin/end).
 
+With --backward a step is one osdn_bwd call (gradients of every input from
+dL/do, dL/dS_T, dL/dd_{T+1}) on the forward's workload.  Its kernels are
+recurrent, token by token per (b,h) in fp32, so each is reported against the
+fp32 vector peak (157.3 TFLOP/s) with its arithmetic per token-head (K = V =
+128: record 6 V K = 98,304 flops, the phase-2 reverse 14 V K = 229,376, the
+phase-1 reverse 30 K = 3,840) and against HBM with its bytes.
+
 With --decode a step is instead one osdn_decode call (the single-token
 recurrence): T new tokens per (b,h) continuing a carried fp32 state, default
 workload one token for each of 256 sequences of the 1.3B-shaped layer
@@ -57,6 +64,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "OSDN fwd tokens/sec (phase1+phase2) at H=16,K=V=128,T=4096; % HBM/MFMA roofline"
+BWD_METRIC = "OSDN bwd tokens/sec (osdn_bwd, both phases) at H=16,K=V=128,T=4096; % fp32 vector roofline"
+FP32_VALU_PEAK_TFLOPS = 157.3
 DECODE_METRIC = "OSDN decode tokens/sec (osdn_decode, new tokens x sequences per call) at H=16,K=V=128; % HBM roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -68,6 +77,9 @@ KERNEL_SOURCE = {
     "chunk_tinv_kernel": "preconditioned_delta_rule_amd/csrc/chunk_wy.hip",
     "chunk_seq_kernel": "preconditioned_delta_rule_amd/csrc/chunk_wy.hip",
     "decode_kernel": "preconditioned_delta_rule_amd/csrc/decode.hip",
+    "bwd_record_kernel": "preconditioned_delta_rule_amd/csrc/backward.hip",
+    "bwd_p2_kernel": "preconditioned_delta_rule_amd/csrc/backward.hip",
+    "bwd_p1_kernel": "preconditioned_delta_rule_amd/csrc/backward.hip",
 }
 COPY_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written
 
@@ -206,6 +218,8 @@ def main(argv=None):
                     help="named workload (default 1p3b_apf; with --decode decode_1p3b_b256)")
     ap.add_argument("--decode", action="store_true",
                     help="time osdn_decode (one call per step) instead of osdn_fwd")
+    ap.add_argument("--backward", action="store_true",
+                    help="time osdn_bwd (one call per step) instead of osdn_fwd")
     ap.add_argument("--copies", type=int, default=4,
                     help="input sets rotated between steps (keeps the 256 MB MALL from "
                          "serving repeated reads)")
@@ -257,6 +271,8 @@ def main(argv=None):
 
     if args.decode:
         return decode_bench(args, inp, dev)
+    if args.backward:
+        return bwd_bench(args, inp, dev)
 
     sets = []
     for c in range(max(1, args.copies)):
@@ -359,6 +375,122 @@ def main(argv=None):
                    "step_device_ms_p10": float(np.percentile(step_ms, 10)) if step_ms else None,
                    "step_device_ms_p90": float(np.percentile(step_ms, 90)) if step_ms else None},
         "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def bwd_work(name, K, V, elem=2):
+    """(algorithmic bytes, fp32 flops) per token-head of a backward kernel."""
+    if name == "bwd_record_kernel":
+        # k, v in; u out (fp32); state and d recorded every 16 tokens
+        return elem * (K + V) + 4 + 4 + 4 * V + (4 * V * K + 4 * K) / 16, 6 * V * K
+    if name == "bwd_p2_kernel":
+        # q, k, dout, u in; dq, dv out; dk~ and the read-key part out (fp32);
+        # a recorded state read every 16 tokens
+        return (elem * (2 * K + V) + 4 * V + elem * (K + V) + 8 * K + 12 + (4 * V * K + 4 * K) / 16,
+                14 * V * K)
+    if name == "bwd_p1_kernel":
+        # k, dk~, read-key part, phase-2 dbeta in; dk, dbeta, dr out
+        return elem * K + 8 * K + 4 + 8 + elem * K + 8, 30 * K
+    return 0, 0
+
+
+def bwd_bench(args, inp, dev):
+    """--backward: one osdn_bwd call per step on the forward's workload."""
+    import torch
+    import preconditioned_delta_rule_amd as osdn
+    from workloads import random_cotangent
+    spec, p = inp["spec"], inp["params"]
+    B, T, H, K = inp["k"].shape
+    V = inp["v"].shape[-1]
+    apf, gated = inp["r"] is not None, inp["alpha"] is not None
+    tdt = torch.bfloat16 if p["dtype"] == "bf16" else torch.float32
+    code = osdn.BF16 if p["dtype"] == "bf16" else osdn.F32
+    elem = 2 if p["dtype"] == "bf16" else 4
+    dout, dS, dd = random_cotangent(inp, seed=spec["seed"] + 2)
+
+    def up(x, dt):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dt).to(dev)
+
+    s = dict(q=up(inp["q"], tdt), k=up(inp["k"], tdt), v=up(inp["v"], tdt),
+             beta=up(inp["beta"], torch.float32), r=up(inp["r"], torch.float32),
+             alpha=up(inp["alpha"], torch.float32), dout=up(dout, tdt),
+             dS=up(dS, torch.float32), dd=up(dd, torch.float32))
+    ws = torch.empty(osdn.bwd_workspace_bytes(B, T, H, K, V, code), dtype=torch.uint8, device=dev)
+    kw = dict(eta=p["eta"], d_min=p["d_min"], d_max=p["d_max"], clamp=p["clamp"], eps=p["eps"],
+              q_scale=p["q_scale"], beta_aware=p["beta_aware"])
+
+    def step(i):
+        osdn.bwd(s["q"], s["k"], s["v"], s["beta"], s["r"], s["alpha"], None, None, dout=s["dout"],
+                 dS=s["dS"], dd=s["dd"], workspace=ws, **kw)
+
+    if args.pmc_pass:
+        for i in range(max(1, args.steps)):
+            step(i)
+        torch.cuda.synchronize()
+        return 0
+    log("warmup", args.warmup)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    nsteps = args.steps
+    log("timing %d backward calls" % nsteps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    launches = osdn.kernel_times(lambda: [step(i) for i in range(nsteps)], dev)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / nsteps
+    nth = B * T * H
+    kernels = {}
+    for name in ("bwd_record_kernel", "bwd_p2_kernel", "bwd_p1_kernel"):
+        vals = [ms for n, ms in launches if n == name]
+        ms = float(np.mean(vals))
+        nbytes, flops = bwd_work(name, K, V, elem)
+        kernels[name] = {"ms": ms, "ms_median": float(np.median(vals)),
+                         "bytes_per_token_head": nbytes, "GB/s": nbytes * nth / (ms * 1e-3) / 1e9,
+                         "flops_per_token_head": flops,
+                         "TFLOP/s": flops * nth / (ms * 1e-3) / 1e12}
+        kernels[name]["valu_fp32_frac"] = kernels[name]["TFLOP/s"] / FP32_VALU_PEAK_TFLOPS
+        kernels[name]["hbm_frac"] = kernels[name]["GB/s"] / HBM_PEAK_GBS
+        log("  %-18s %.4f ms  %.1f TFLOP/s  %.0f GB/s" % (name, ms, kernels[name]["TFLOP/s"],
+                                                        kernels[name]["GB/s"]))
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    dk = kernels[dom]
+    roofline = {"bound": "alu", "kernel": dom, "achieved": dk["TFLOP/s"], "peak": FP32_VALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": dk["valu_fp32_frac"], "traffic": None,
+                "algorithmic_flops_per_launch": dk["flops_per_token_head"] * nth}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        # a bounded sample: two whole (b,h) sequences of the workload
+        pairs = [(0, 0), (B - 1, H - 1)]
+        from workloads import sample_sequences
+        sub = sample_sequences(dict(inp), pairs)
+        sd = np.stack([dout[b, :, h] for b, h in pairs])[:, :, None, :]
+        reps, wall = 0, 0.0
+        while wall < args.cpu_seconds or reps == 0:
+            t0 = time.perf_counter()
+            oracle.backward(sub["q"], sub["k"], sub["v"], sub["beta"], sub["r"], sub["alpha"],
+                            dout=sd, eta=p["eta"], d_min=p["d_min"], d_max=p["d_max"],
+                            clamp=p["clamp"], eps=p["eps"], beta_aware=p["beta_aware"],
+                            q_scale=p["q_scale"], threads=len(pairs))
+            wall += time.perf_counter() - t0
+            reps += 1
+        # tokens/s of the whole layer at this rate: B*T tokens carry B*H sequences
+        cpu = {"value": reps * len(pairs) * T / wall / H, "unit": "tokens/s", "cores": len(pairs),
+               "kind": "oracle",
+               "sample": "%d whole (b,h) sequences of %d tokens, fp64 oracle backward (forward "
+                         "replay included), one sequence per thread, %d run(s) in %.2f s; scaled to "
+                         "layer tokens/s as sequences/s x T / H" % (len(pairs), T, reps, wall)}
+    out = {
+        "metric": BWD_METRIC, "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": nsteps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": p["dtype"], "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": V, "apf": apf,
+                   "gated": gated, "seed": spec["seed"]},
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -219,6 +219,42 @@ osdn_status osdn_decode(const osdn_desc *desc, const void *q, const void *k,
                         void *o, float *S_out, float *d_out, void *stream);
 
 /*
+ * Backward pass: gradients of a loss L through osdn_fwd, given dL/do and
+ * optionally dL/dS_T and dL/dd_{T+1}.  Phase 2 is differentiated token by
+ * token backwards (the adjoint G of the state: G += q_scale dout_t q_t^T,
+ * w = G k~_t, dv_t = beta_t w, dk~_t = beta_t G^T u_t, read-key part
+ * -beta_t Sb_t^T w, G = alpha_t (G - beta_t w k_t^T)); phase 1 is swept back
+ * through the clamped recurrence, the gradient reaching d through
+ * k~ = d (.) k as Section 4.5 describes (the clamp passes the gradient only
+ * where it did not clip; the norm floor blocks the norm's derivative).
+ *   q, k, v, beta, r, alpha, d1, S0   the forward's inputs, as for osdn_fwd
+ *   dout    [B,T,H,V] dtype      dL/do
+ *   dS      [B,H,V,K] f32        dL/dS_T, or NULL (zero)
+ *   dd      [B,H,K]   f32        dL/dd_{T+1}, or NULL (zero)
+ *   dq, dk  [B,T,H,K] dtype      OUT: dL/dq, dL/dk (both key roles)
+ *   dv      [B,T,H,V] dtype      OUT: dL/dv
+ *   dbeta   [B,T,H]   f32        OUT: dL/dbeta (write gate and phase-1 step)
+ *   dr      [B,T,H]   f32        OUT: dL/dr, or NULL (ignored when r is NULL)
+ *   dalpha  [B,T,H]   f32        OUT: dL/dalpha, or NULL (ignored when alpha is NULL)
+ *   dd1     [B,H,K]   f32        OUT: dL/dd1, or NULL
+ *   dS0     [B,H,V,K] f32        OUT: dL/dS0, or NULL
+ *   workspace  >= osdn_bwd_workspace_bytes(desc) bytes, 16-byte aligned,
+ *              required: the forward is run once more to record every
+ *              token's residual (fp32 [B,T,H,V]) and the state and d every
+ *              16 tokens, plus fp32 dL/dk~ and partial gradients.
+ * Gradient outputs must not alias inputs or each other.  K, V <= 128;
+ * B*H >= 2^31 returns OSDN_EUNSUPPORTED.  T = 0 gives dS0 = dS, dd1 = dd.
+ */
+size_t osdn_bwd_workspace_bytes(const osdn_desc *desc);
+osdn_status osdn_bwd(const osdn_desc *desc, const void *q, const void *k,
+                     const void *v, const float *beta, const float *r,
+                     const float *alpha, const float *d1, const float *S0,
+                     const void *dout, const float *dS, const float *dd,
+                     void *dq, void *dk, void *dv, float *dbeta, float *dr,
+                     float *dalpha, float *dd1, float *dS0, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/*
  * Launch profile (measurement aid).  osdn_profile_begin records a HIP event on
  * `stream`; until osdn_profile_end, every kernel the library launches from
  * the calling thread records another event on its stream right after the

@@ -20,7 +20,7 @@ import os
 import torch
 
 __all__ = ["precond_scan", "precond_scan_workspace_bytes", "scan_counters", "chunk_fwd",
-           "chunk_fwd_workspace_bytes", "fwd", "decode", "DECODE_MAX_T", "kernel_times", "fwd_workspace_bytes", "fwd_scan_counters", "Desc", "OsdnError",
+           "chunk_fwd_workspace_bytes", "fwd", "decode", "DECODE_MAX_T", "bwd", "bwd_workspace_bytes", "kernel_times", "fwd_workspace_bytes", "fwd_scan_counters", "Desc", "OsdnError",
            "library_path", "load", "F32", "BF16"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +34,7 @@ DECODE_MAX_T = 64  # OSDN_DECODE_MAX_T
 SYMBOLS = ("osdn_desc_init", "osdn_validate", "osdn_precond_scan",
            "osdn_precond_scan_workspace_bytes", "osdn_precond_scan_counters_offset",
            "osdn_chunk_fwd", "osdn_chunk_fwd_workspace_bytes", "osdn_fwd_workspace_bytes",
-           "osdn_fwd", "osdn_decode", "osdn_profile_begin", "osdn_profile_end", "osdn_status_str",
+           "osdn_fwd", "osdn_decode", "osdn_bwd_workspace_bytes", "osdn_bwd", "osdn_profile_begin", "osdn_profile_end", "osdn_status_str",
            "osdn_last_error", "osdn_version")
 
 
@@ -83,6 +83,10 @@ def load():
     lib.osdn_fwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp, vp,
                              ctypes.c_size_t, vp]
     lib.osdn_decode.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp]
+    lib.osdn_bwd_workspace_bytes.argtypes = [dp]
+    lib.osdn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.osdn_bwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp, vp, vp, fp, fp, fp,
+                             fp, fp, vp, ctypes.c_size_t, vp]
     lib.osdn_profile_begin.argtypes = [vp]
     lib.osdn_profile_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
                                      ci, ctypes.POINTER(ci)]
@@ -91,7 +95,7 @@ def load():
     lib.osdn_last_error.argtypes = []
     lib.osdn_last_error.restype = ctypes.c_char_p
     for name in ("osdn_desc_init", "osdn_validate", "osdn_precond_scan", "osdn_chunk_fwd",
-                 "osdn_fwd", "osdn_decode", "osdn_profile_begin", "osdn_profile_end", "osdn_version"):
+                 "osdn_fwd", "osdn_decode", "osdn_bwd_workspace_bytes", "osdn_bwd", "osdn_profile_begin", "osdn_profile_end", "osdn_version"):
         getattr(lib, name).restype = ci
     _lib = lib
     return lib
@@ -325,6 +329,51 @@ def decode(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, eta=0.003, d_
                               _ptr(alpha), _ptr(d1), _ptr(S0), _ptr(o), _ptr(S_out), _ptr(d_out),
                               _stream(dev)))
     return o, S_out, d_out
+
+
+def bwd_workspace_bytes(B, T, H, K, V, dtype=BF16) -> int:
+    desc = make_desc(B, T, H, K, V, dtype=dtype)
+    return int(load().osdn_bwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def bwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, dout, dS=None, dd=None,
+        eta=0.003, d_min=0.5, d_max=2.0, clamp=True, eps=1e-6, q_scale=1.0, beta_aware=True,
+        workspace=None):
+    """Backward pass of fwd: gradients of L given dout = dL/do [B,T,H,V] (dtype
+    of q), dS = dL/dS_T [B,H,V,K] f32 and dd = dL/dd_{T+1} [B,H,K] f32 (both
+    optional).  Returns a dict: dq, dk [B,T,H,K] and dv [B,T,H,V] in q's dtype;
+    dbeta [B,T,H], dr and dalpha [B,T,H] (None when r / alpha are None),
+    dd1 [B,H,K], dS0 [B,H,V,K] in f32."""
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dev, dt, f32 = q.device, q.dtype, torch.float32
+    _need(k, "k", (B, T, H, K), dt, dev)
+    _need(v, "v", (B, T, H, V), dt, dev)
+    _need(beta, "beta", (B, T, H), f32, dev)
+    _need(r, "r", (B, T, H), f32, dev)
+    _need(alpha, "alpha", (B, T, H), f32, dev)
+    _need(d1, "d1", (B, H, K), f32, dev)
+    _need(S0, "S0", (B, H, V, K), f32, dev)
+    _need(dout, "dout", (B, T, H, V), dt, dev)
+    _need(dS, "dS", (B, H, V, K), f32, dev)
+    _need(dd, "dd", (B, H, K), f32, dev)
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+           "dbeta": torch.empty((B, T, H), dtype=f32, device=dev),
+           "dr": torch.empty((B, T, H), dtype=f32, device=dev) if r is not None else None,
+           "dalpha": torch.empty((B, T, H), dtype=f32, device=dev) if alpha is not None else None,
+           "dd1": torch.empty((B, H, K), dtype=f32, device=dev),
+           "dS0": torch.empty((B, H, V, K), dtype=f32, device=dev)}
+    desc = make_desc(B, T, H, K, V, dtype=_dtype_code(q), eta=eta, d_min=d_min, d_max=d_max,
+                     clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware)
+    need = int(load().osdn_bwd_workspace_bytes(ctypes.byref(desc)))
+    workspace = _workspace(workspace, need, dev)
+    _check(load().osdn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r),
+                           _ptr(alpha), _ptr(d1), _ptr(S0), _ptr(dout), _ptr(dS), _ptr(dd),
+                           _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
+                           _ptr(out["dr"]), _ptr(out["dalpha"]), _ptr(out["dd1"]),
+                           _ptr(out["dS0"]), _ptr(workspace), ctypes.c_size_t(_nbytes(workspace)),
+                           _stream(dev)))
+    return out
 
 
 def kernel_times(fn, device=None):

@@ -92,6 +92,32 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t s);
 
+// Backward pass (three kernels, one workgroup or wave per (b,h); K, V <= 128).
+struct BwdArgs {
+  const void *q, *k, *v;        // [B,T,H,K] / [B,T,H,V]
+  const float *beta;            // [B,T,H]
+  const float *r, *alpha;       // [B,T,H] or null
+  const float *d1, *S0;         // [B,H,K], [B,H,V,K] or null (ones, zeros)
+  const void *dout;             // [B,T,H,V] dL/do
+  const float *dS, *dd;         // [B,H,V,K] dL/dS_T, [B,H,K] dL/dd_{T+1}, or null
+  void *dq, *dk, *dv;           // OUT [B,T,H,K] / [B,T,H,V]
+  float *dbeta;                 // OUT [B,T,H]
+  float *dr, *dalpha;           // OUT [B,T,H] or null
+  float *dd1, *dS0;             // OUT [B,H,K], [B,H,V,K] or null
+  // workspace regions (bwd_work_layout)
+  float *u;                     // [B,T,H,V] residual of every token
+  float *ck;                    // [B,H,NB+1,V,K] S every 16 tokens (NB = ceil(T/16))
+  float *dck;                   // [B,H,NB+1,K] d every 16 tokens
+  float *dkt, *dkr;             // [B,T,H,K] dL/dk~ and the read-key part of dL/dk
+  float *dbp2;                  // [B,T,H] phase-2 part of dL/dbeta
+  int64_t B, T, H, K, V;
+  float eta, d_min, d_max, eps, q_scale;
+  int clamp, beta_aware;
+};
+size_t bwd_work_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V);
+void bwd_work_layout(BwdArgs &a, void *base);
+hipError_t launch_bwd(const BwdArgs &a, bool bf16, hipStream_t s);
+
 // Shape coverage of the specialised MFMA path (bf16, K = V = 128, C = 64).
 bool chunk_mfma_supported(const ChunkArgs &a, bool bf16);
 

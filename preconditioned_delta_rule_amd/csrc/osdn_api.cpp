@@ -453,4 +453,89 @@ osdn_status osdn_decode(const osdn_desc *d, const void *q, const void *k, const 
   return ok();
 }
 
+size_t osdn_bwd_workspace_bytes(const osdn_desc *d) {
+  if (validate(d, 3) != OSDN_OK) return 0;
+  return osdn::bwd_work_bytes(d->B, d->T, d->H, d->K, d->V);
+}
+
+osdn_status osdn_bwd(const osdn_desc *d, const void *q, const void *k, const void *v, const float *beta,
+                     const float *r, const float *alpha, const float *d1, const float *S0, const void *dout,
+                     const float *dS, const float *dd, void *dq, void *dk, void *dv, float *dbeta, float *dr,
+                     float *dalpha, float *dd1, float *dS0, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+  OSDN_TRY(validate(d, 3));
+  if ((double)d->B * (double)d->H > 2147483647.0)
+    return fail(OSDN_EUNSUPPORTED, "osdn_bwd supports B*H < 2^31 (got %lld)", (long long)(d->B * d->H));
+  const bool need_seq = d->T > 0;
+  OSDN_TRY(check_ptr(q, "q", need_seq));
+  OSDN_TRY(check_ptr(k, "k", need_seq));
+  OSDN_TRY(check_ptr(v, "v", need_seq));
+  OSDN_TRY(check_ptr(beta, "beta", need_seq));
+  OSDN_TRY(check_ptr(r, "r", false));
+  OSDN_TRY(check_ptr(alpha, "alpha", false));
+  OSDN_TRY(check_ptr(d1, "d1", false));
+  OSDN_TRY(check_ptr(S0, "S0", false));
+  OSDN_TRY(check_ptr(dout, "dout", need_seq));
+  OSDN_TRY(check_ptr(dS, "dS", false));
+  OSDN_TRY(check_ptr(dd, "dd", false));
+  OSDN_TRY(check_ptr(dq, "dq", need_seq));
+  OSDN_TRY(check_ptr(dk, "dk", need_seq));
+  OSDN_TRY(check_ptr(dv, "dv", need_seq));
+  OSDN_TRY(check_ptr(dbeta, "dbeta", need_seq));
+  OSDN_TRY(check_ptr(dr, "dr", false));
+  OSDN_TRY(check_ptr(dalpha, "dalpha", false));
+  OSDN_TRY(check_ptr(dd1, "dd1", false));
+  OSDN_TRY(check_ptr(dS0, "dS0", false));
+  OSDN_TRY(check_ptr(workspace, "workspace", true));
+  const void *ins[] = {q, k, v, beta, r, alpha, d1, S0, dout, dS, dd};
+  const void *outs[] = {dq, dk, dv, dbeta, dr, dalpha, dd1, dS0};
+  const int nout = (int)(sizeof outs / sizeof outs[0]);
+  for (int x = 0; x < nout; ++x) {
+    if (!outs[x]) continue;
+    for (const void *i : ins)
+      if (outs[x] == i) return fail(OSDN_EINVAL, "gradient outputs must not alias inputs");
+    for (int y = x + 1; y < nout; ++y)
+      if (outs[y] == outs[x]) return fail(OSDN_EINVAL, "gradient outputs must be distinct");
+  }
+  const size_t need = osdn::bwd_work_bytes(d->B, d->T, d->H, d->K, d->V);
+  if (workspace_bytes < need)
+    return fail(OSDN_EINVAL, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
+  osdn::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.r = r;
+  a.alpha = alpha;
+  a.d1 = d1;
+  a.S0 = S0;
+  a.dout = dout;
+  a.dS = dS;
+  a.dd = dd;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dbeta = dbeta;
+  a.dr = r ? dr : nullptr;
+  a.dalpha = alpha ? dalpha : nullptr;
+  a.dd1 = dd1;
+  a.dS0 = dS0;
+  a.B = d->B;
+  a.T = d->T;
+  a.H = d->H;
+  a.K = d->K;
+  a.V = d->V;
+  a.eta = d->eta;
+  a.d_min = d->d_min;
+  a.d_max = d->d_max;
+  a.eps = d->eps;
+  a.q_scale = d->q_scale;
+  a.clamp = d->clamp ? 1 : 0;
+  a.beta_aware = d->beta_aware ? 1 : 0;
+  osdn::bwd_work_layout(a, workspace);
+  OSDN_TRY(hip_status(osdn::launch_bwd(a, d->dtype == OSDN_BF16, static_cast<hipStream_t>(stream)),
+                      "backward launch"));
+  return ok();
+}
+
 }  // extern "C"

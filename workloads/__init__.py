@@ -12,6 +12,10 @@ Recipe (same for every named workload unless stated):
   * beta = sigmoid(N(mu_b, 1)), retention r = sigmoid(N(2, 1)) when APF is on,
     Gated-DeltaNet decay alpha = exp(-softplus(N(0,1)) * 0.1);
   * d_1 = 1, S_0 = 0, eta = 0.003, box [0.5, 2], eps = 1e-6;
+  * the backward pass's upstream gradients (``random_cotangent``): a third
+    generator ``default_rng(seed + 2)`` draws dL/do ~ N(0, 1) [B,T,H,V]
+    (rounded to bf16 for bf16 workloads), then dL/dS_T ~ N(0, 1) and
+    dL/dd_{T+1} ~ N(0, 1), float32;
   * decode workloads (a few new tokens continuing a carried state) draw their
     tokens the same way and the state with ``random_state``: a second
     generator ``default_rng(seed + 1)`` draws d_1 ~ U(0.6, 1.9) per coordinate
@@ -41,6 +45,9 @@ WORKLOADS = {
                          chunk=64, seed=4, apf=True, gdn=True),
     # decode: one new token per sequence of the 1.3B-shaped layer, carrying a
     # state; the small batch and a serving batch of 256 sequences
+    # backward: the 1.3B-shaped layer at a shorter sequence
+    "bwd_1p3b_t1024": dict(B=4, T=1024, H=16, K=128, V=128, dtype="bf16", chunk=64,
+                           seed=7, apf=True),
     "decode_1p3b": dict(B=4, T=1, H=16, K=128, V=128, dtype="bf16", chunk=64,
                         seed=5, apf=True, state=True),
     "decode_1p3b_b256": dict(B=256, T=1, H=16, K=128, V=128, dtype="bf16",
@@ -207,3 +214,18 @@ def sample_sequences(inputs: dict, pairs) -> dict:
         if inputs[key] is not None:
             out[key] = np.stack([inputs[key][b, h] for b, h in pairs])[:, None]
     return out
+
+
+def random_cotangent(inputs: dict, seed: int = 0):
+    """Upstream gradients for the shapes of `inputs`: dout [B,T,H,V] (bf16
+    values for bf16 workloads), dS [B,H,V,K] and dd [B,H,K], float32, from
+    default_rng(seed)."""
+    B, T, H, K = inputs["k"].shape
+    V = inputs["v"].shape[-1]
+    rng = np.random.default_rng(seed)
+    dout = rng.standard_normal((B, T, H, V), dtype=np.float32)
+    if inputs["params"]["dtype"] == "bf16":
+        dout = bf16_round(dout)
+    dS = rng.standard_normal((B, H, V, K), dtype=np.float32)
+    dd = rng.standard_normal((B, H, K), dtype=np.float32)
+    return dout, dS, dd
