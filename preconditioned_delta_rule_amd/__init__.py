@@ -95,7 +95,8 @@ def load():
     lib.osdn_last_error.argtypes = []
     lib.osdn_last_error.restype = ctypes.c_char_p
     for name in ("osdn_desc_init", "osdn_validate", "osdn_precond_scan", "osdn_chunk_fwd",
-                 "osdn_fwd", "osdn_decode", "osdn_bwd_workspace_bytes", "osdn_bwd", "osdn_profile_begin", "osdn_profile_end", "osdn_version"):
+                 "osdn_fwd", "osdn_decode", "osdn_bwd", "osdn_profile_begin", "osdn_profile_end",
+                 "osdn_version"):
         getattr(lib, name).restype = ci
     _lib = lib
     return lib

@@ -104,12 +104,13 @@ struct BwdArgs {
   float *dbeta;                 // OUT [B,T,H]
   float *dr, *dalpha;           // OUT [B,T,H] or null
   float *dd1, *dS0;             // OUT [B,H,K], [B,H,V,K] or null
-  // workspace regions (bwd_work_layout)
+  // workspace regions (bwd_work_layout); NQ = ceil(V/32) value slices
   float *u;                     // [B,T,H,V] residual of every token
   float *ck;                    // [B,H,NB+1,V,K] S every 16 tokens (NB = ceil(T/16))
   float *dck;                   // [B,H,NB+1,K] d every 16 tokens
-  float *dkt, *dkr;             // [B,T,H,K] dL/dk~ and the read-key part of dL/dk
-  float *dbp2;                  // [B,T,H] phase-2 part of dL/dbeta
+  float *dqp, *dktp, *dkrp;     // [NQ,B,T,H,K] per-slice parts of S^T dout, dL/dk~, read-key dL/dk
+  float *dbp, *dap;             // [NQ,B,T,H] per-slice parts of dL/dbeta (phase 2) and dL/dalpha
+  int nq;
   int64_t B, T, H, K, V;
   float eta, d_min, d_max, eps, q_scale;
   int clamp, beta_aware;

@@ -200,3 +200,9 @@ def test_decode_argument_checks(lib):
     assert st == osdn.EINVAL and "aligned" in lib.osdn_last_error().decode()
     d.K = 129
     assert lib.osdn_decode(ctypes.byref(d), *args) == osdn.EUNSUPPORTED
+
+
+def test_size_queries_return_64_bit(lib):
+    # workspace sizes above 2^31 bytes come back whole through the binding
+    assert osdn.bwd_workspace_bytes(4, 4096, 16, 128, 128) > 2 ** 31
+    assert osdn.fwd_workspace_bytes(256, 4096, 16, 128, 128) > 2 ** 32
