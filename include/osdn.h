@@ -189,6 +189,31 @@ osdn_status osdn_fwd(const osdn_desc *desc, const void *q, const void *k,
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * osdn_fwd over variable-length sequences packed into one token axis (the
+ * packed training batches of Appendix F): sequence b is tokens
+ * [cu_seqlens[b], cu_seqlens[b+1]) of the packed tensors and starts from its
+ * own d1[b], S0[b] (the state is reset between sequences; nothing crosses a
+ * sequence boundary).
+ *   desc->B      number of sequences; desc->T  the longest sequence's length
+ *                (bounds every cu_seqlens[b+1] - cu_seqlens[b]; sizes the
+ *                workspace, which is osdn_fwd_workspace_bytes(desc))
+ *   cu_seqlens   [B+1] int64 DEVICE pointer, 0 = c_0 <= c_1 <= ... = total
+ *   q, k, k_tilde_out [1,total,H,K], v, o [1,total,H,V] dtype;
+ *   beta, r, alpha [1,total,H] f32; d1, d_out [B,H,K], S0, S_out [B,H,V,K] f32.
+ * Every other argument and rule is as for osdn_fwd.  cu_seqlens is device
+ * data and is not checked: it must be non-decreasing from 0 with no
+ * difference above desc->T.  Each sequence's result equals osdn_fwd on that
+ * sequence alone, bit for bit.
+ */
+osdn_status osdn_fwd_varlen(const osdn_desc *desc, const int64_t *cu_seqlens,
+                            const void *q, const void *k, const void *v,
+                            const float *beta, const float *r,
+                            const float *alpha, const float *d1,
+                            const float *S0, void *o, float *S_out,
+                            float *d_out, void *k_tilde_out, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
  * Decode step: the single-token recurrence of Appendix L (one launch per
  * call), for up to OSDN_DECODE_MAX_T new tokens per (b,h) continuing from a
  * carried state.  Per (b,h) and token, in order: the write key d (.) k_t, the

@@ -20,7 +20,7 @@ import os
 import torch
 
 __all__ = ["precond_scan", "precond_scan_workspace_bytes", "scan_counters", "chunk_fwd",
-           "chunk_fwd_workspace_bytes", "fwd", "decode", "DECODE_MAX_T", "bwd", "bwd_workspace_bytes", "kernel_times", "fwd_workspace_bytes", "fwd_scan_counters", "Desc", "OsdnError",
+           "chunk_fwd_workspace_bytes", "fwd", "fwd_varlen", "decode", "DECODE_MAX_T", "bwd", "bwd_workspace_bytes", "kernel_times", "fwd_workspace_bytes", "fwd_scan_counters", "Desc", "OsdnError",
            "library_path", "load", "F32", "BF16"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +34,7 @@ DECODE_MAX_T = 64  # OSDN_DECODE_MAX_T
 SYMBOLS = ("osdn_desc_init", "osdn_validate", "osdn_precond_scan",
            "osdn_precond_scan_workspace_bytes", "osdn_precond_scan_counters_offset",
            "osdn_chunk_fwd", "osdn_chunk_fwd_workspace_bytes", "osdn_fwd_workspace_bytes",
-           "osdn_fwd", "osdn_decode", "osdn_bwd_workspace_bytes", "osdn_bwd", "osdn_profile_begin", "osdn_profile_end", "osdn_status_str",
+           "osdn_fwd", "osdn_fwd_varlen", "osdn_decode", "osdn_bwd_workspace_bytes", "osdn_bwd", "osdn_profile_begin", "osdn_profile_end", "osdn_status_str",
            "osdn_last_error", "osdn_version")
 
 
@@ -83,6 +83,8 @@ def load():
     lib.osdn_fwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp, vp,
                              ctypes.c_size_t, vp]
     lib.osdn_decode.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp]
+    lib.osdn_fwd_varlen.argtypes = [dp, vp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp, vp,
+                                    ctypes.c_size_t, vp]
     lib.osdn_bwd_workspace_bytes.argtypes = [dp]
     lib.osdn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.osdn_bwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp, vp, vp, fp, fp, fp,
@@ -95,7 +97,8 @@ def load():
     lib.osdn_last_error.argtypes = []
     lib.osdn_last_error.restype = ctypes.c_char_p
     for name in ("osdn_desc_init", "osdn_validate", "osdn_precond_scan", "osdn_chunk_fwd",
-                 "osdn_fwd", "osdn_decode", "osdn_bwd", "osdn_profile_begin", "osdn_profile_end",
+                 "osdn_fwd", "osdn_fwd_varlen", "osdn_decode", "osdn_bwd", "osdn_profile_begin",
+                 "osdn_profile_end",
                  "osdn_version"):
         getattr(lib, name).restype = ci
     _lib = lib
@@ -295,6 +298,50 @@ def fwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, chunk=64, eta=0.
                            _ptr(alpha), _ptr(d1), _ptr(S0), _ptr(o), _ptr(S_out), _ptr(d_out),
                            _ptr(k_tilde_out), _ptr(workspace),
                            ctypes.c_size_t(_nbytes(workspace)), _stream(dev)))
+    return o, S_out, d_out
+
+
+def fwd_varlen(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, cu_seqlens,
+               max_seqlen=None, chunk=64, eta=0.003, d_min=0.5, d_max=2.0, clamp=True, eps=1e-6,
+               q_scale=1.0, beta_aware=True, o=None, S_out=None, d_out=None, k_tilde_out=None,
+               workspace=None):
+    """fwd over sequences packed on one token axis: q, k [1,total,H,K], v
+    [1,total,H,V], beta/r/alpha [1,total,H]; cu_seqlens int64 [S+1] on the
+    device (sequence b = tokens [cu[b], cu[b+1])); d1 [S,H,K], S0 [S,H,V,K].
+    max_seqlen (the longest length) is read from cu_seqlens when None.
+    Returns (o [1,total,H,V], S_out [S,H,V,K], d_out [S,H,K])."""
+    _, total, H, K = q.shape
+    V = v.shape[-1]
+    dev, dt, f32 = q.device, q.dtype, torch.float32
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int64 \
+            or cu_seqlens.device != dev or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int64 vector on %s" % dev)
+    S = cu_seqlens.numel() - 1
+    if max_seqlen is None:
+        max_seqlen = int(torch.diff(cu_seqlens).max().item()) if S > 0 else 0
+    _need(k, "k", (1, total, H, K), dt, dev)
+    _need(v, "v", (1, total, H, V), dt, dev)
+    _need(beta, "beta", (1, total, H), f32, dev)
+    _need(r, "r", (1, total, H), f32, dev)
+    _need(alpha, "alpha", (1, total, H), f32, dev)
+    _need(d1, "d1", (S, H, K), f32, dev)
+    _need(S0, "S0", (S, H, V, K), f32, dev)
+    if o is None:
+        o = torch.empty((1, total, H, V), dtype=dt, device=dev)
+    if S_out is None:
+        S_out = torch.empty((S, H, V, K), dtype=f32, device=dev)
+    if d_out is None:
+        d_out = torch.empty((S, H, K), dtype=f32, device=dev)
+    _need(k_tilde_out, "k_tilde_out", (1, total, H, K), dt, dev)
+    desc = make_desc(S, max_seqlen, H, K, V, dtype=_dtype_code(q), chunk=chunk, eta=eta,
+                     d_min=d_min, d_max=d_max, clamp=clamp, eps=eps, q_scale=q_scale,
+                     beta_aware=beta_aware)
+    need = int(load().osdn_fwd_workspace_bytes(ctypes.byref(desc)))
+    workspace = _workspace(workspace, need, dev)
+    _check(load().osdn_fwd_varlen(ctypes.byref(desc), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(beta), _ptr(r), _ptr(alpha), _ptr(d1), _ptr(S0), _ptr(o),
+                                  _ptr(S_out), _ptr(d_out), _ptr(k_tilde_out), _ptr(workspace),
+                                  ctypes.c_size_t(_nbytes(workspace)), _stream(dev)))
     return o, S_out, d_out
 
 

@@ -37,17 +37,18 @@ struct GenLayout {
   __host__ __device__ int total() const { return off_g() + C; }
 };
 
-template <typename TIn, bool GATED>
+template <typename TIn, bool GATED, bool VL>
 __global__ __launch_bounds__(GEN_THREADS) void chunk_generic_kernel(ChunkArgs a, GenLayout lay, int ntiles) {
   extern __shared__ float smem[];
   const int tid = threadIdx.x;
   const int64_t seq = blockIdx.x / ntiles;
   const int vt = blockIdx.x % ntiles;
-  const int64_t H = a.H, T = a.T, K = a.K, V = a.V;
+  const int64_t H = a.H, K = a.K, V = a.V;
   const int C = lay.C, VT = lay.VT, KP = lay.KP;
   const int v0 = vt * VT;
   const int vn = (int)((V - v0) < VT ? (V - v0) : VT);  // valid rows in this tile
   const int64_t b = seq / H, h = seq - b * H;
+  const int64_t T = seq_len<VL>(a, b), tb = seq_base<VL>(a, b);
 
   float *sQ = smem + lay.off_Q(), *sK = smem + lay.off_K(), *sKt = smem + lay.off_Kt();
   float *sV = smem + lay.off_V(), *sA = smem + lay.off_A(), *sM = smem + lay.off_M();
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(GEN_THREADS) void chunk_generic_kernel(ChunkArgs a,
       int i = e / (int)K, c = e % (int)K;
       float xq = 0.0f, xk = 0.0f, xw = 0.0f;
       if (i < L) {
-        int64_t g = ((b * T + t0 + i) * H + h) * K + c;
+        int64_t g = ((tb + t0 + i) * H + h) * K + c;
         xq = to_f32(q[g]) * a.q_scale;
         xk = to_f32(k[g]);
         xw = to_f32(kt[g]) + (a.kt_is_res ? xk : 0.0f);  // k~ = k + residual
@@ -88,14 +89,14 @@ __global__ __launch_bounds__(GEN_THREADS) void chunk_generic_kernel(ChunkArgs a,
     for (int e = tid; e < C * VT; e += GEN_THREADS) {
       int i = e / VT, c = e % VT;
       float x = 0.0f;
-      if (i < L && c < vn) x = to_f32(v[((b * T + t0 + i) * H + h) * V + v0 + c]);
+      if (i < L && c < vn) x = to_f32(v[((tb + t0 + i) * H + h) * V + v0 + c]);
       sV[i * VT + c] = x;
     }
     if (tid < C) {
       int i = tid;
       float bt = 0.0f, la = 0.0f;
       if (i < L) {
-        int64_t g = (b * T + t0 + i) * H + h;
+        int64_t g = (tb + t0 + i) * H + h;
         bt = a.beta[g];
         if (GATED) la = logf(a.alpha[g]);
       }
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(GEN_THREADS) void chunk_generic_kernel(ChunkArgs a,
       if (i < L && r < vn) {
         float acc = sP[i * VT + r];
         for (int j = 0; j <= i; ++j) acc += sM[i * CP + j] * sR[j * VT + r];
-        o[((b * T + t0 + i) * H + h) * V + v0 + r] = from_f32<TIn>(acc);
+        o[((tb + t0 + i) * H + h) * V + v0 + r] = from_f32<TIn>(acc);
       }
     }
     const float gL = GATED ? sG[L - 1] : 0.0f;
@@ -191,18 +192,18 @@ static GenLayout gen_layout(const ChunkArgs &a) {
   return lay;
 }
 
-template <typename TIn>
+template <typename TIn, bool VL>
 static hipError_t launch_gen(const ChunkArgs &a, hipStream_t s) {
   GenLayout lay = gen_layout(a);
   int ntiles = (int)((a.V + lay.VT - 1) / lay.VT);
   size_t shm = (size_t)lay.total() * sizeof(float);
   dim3 grid((unsigned)(a.B * a.H * ntiles)), block(GEN_THREADS);
   if (a.alpha) {
-    auto kern = chunk_generic_kernel<TIn, true>;
+    auto kern = chunk_generic_kernel<TIn, true, VL>;
     hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     hipLaunchKernelGGL(kern, grid, block, shm, s, a, lay, ntiles);
   } else {
-    auto kern = chunk_generic_kernel<TIn, false>;
+    auto kern = chunk_generic_kernel<TIn, false, VL>;
     hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     hipLaunchKernelGGL(kern, grid, block, shm, s, a, lay, ntiles);
   }
@@ -214,7 +215,8 @@ size_t chunk_generic_lds_bytes(const ChunkArgs &a) { return (size_t)gen_layout(a
 
 hipError_t launch_chunk_generic(const ChunkArgs &a, bool is_bf16, hipStream_t s) {
   if (a.B * a.H == 0) return hipSuccess;
-  return is_bf16 ? launch_gen<bf16>(a, s) : launch_gen<float>(a, s);
+  if (a.cu) return is_bf16 ? launch_gen<bf16, true>(a, s) : launch_gen<float, true>(a, s);
+  return is_bf16 ? launch_gen<bf16, false>(a, s) : launch_gen<float, false>(a, s);
 }
 
 }  // namespace osdn

@@ -78,7 +78,7 @@ struct TinvLay {
 // d_{t+1} = clip(r_t d_t + c_t k_t^2), the same fp32 expressions as the
 // phase-1 emit kernel -- and written for the sweep kernel, so phase 1 need
 // not write it and this kernel need not read it.
-template <bool GATED, bool KRES, bool EMIT>
+template <bool GATED, bool KRES, bool EMIT, bool VL>
 __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout, int64_t N, EmitArgs em) {
   static_assert(KRES || !EMIT, "the folded replay produces the residual form");
   typedef TinvLay L;
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = l & 15, lq = l >> 4;
-  const int64_t H = a.H, T = a.T;
+  const int64_t H = a.H;
   const bf16 *gk = static_cast<const bf16 *>(a.k);
   const bf16 *gkt = static_cast<const bf16 *>(a.kt);
   const int64_t tstride = H * KD;
@@ -111,9 +111,11 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
   auto fetch = [&](int64_t ci) {
     const int64_t seq = ci / N, n = ci - seq * N;
     const int64_t b = seq / H, h = seq - b * H;
+    const int64_t T = seq_len<VL>(a, b), tb = seq_base<VL>(a, b);
     const int64_t t0 = n * C;
+    if (VL && t0 >= T) return;  // past a shorter sequence's end: skipped below
     const int Lc = (int)((T - t0) < C ? (T - t0) : C);
-    const int64_t base = (b * T + t0) * tstride + h * KD;
+    const int64_t base = (tb + t0) * tstride + h * KD;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int vi = tid + 256 * p, i = vi >> 4, c8 = 8 * (vi & 15);
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
       if constexpr (!EMIT) pe[p] = ld8(gkt + off);
     }
     if (w == 0) {
-      const int64_t gi = (b * T + t0 + (l < Lc ? l : 0)) * H + h;
+      const int64_t gi = (tb + t0 + (l < Lc ? l : 0)) * H + h;
       pb = a.beta[gi];
       if constexpr (GATED) pa = a.alpha[gi];
     }
@@ -132,9 +134,16 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
   for (int64_t ci = blockIdx.x; ci < nch; ci += gridDim.x) {
   const int64_t seq = ci / N, n = ci - seq * N;
   const int64_t b = seq / H, h = seq - b * H;
+  const int64_t T = seq_len<VL>(a, b), tb = seq_base<VL>(a, b);
   const int64_t t0 = n * C;
+  if (VL && t0 >= T) {
+    // past a shorter sequence's end (the whole workgroup alike): nothing to
+    // form; the next chunk's loads still go out
+    if (ci + (int64_t)gridDim.x < nch) fetch(ci + gridDim.x);
+    continue;
+  }
   const int Lc = (int)((T - t0) < C ? (T - t0) : C);
-  const int64_t base = (b * T + t0) * tstride + h * KD;  // token t0 of this (b,h)
+  const int64_t base = (tb + t0) * tstride + h * KD;  // token t0 of this (b,h)
 
   // ---- this chunk's rows into LDS (16-byte vectors, 16 threads per row;
   //      zero past T), beta and the cumulative log decay
@@ -179,7 +188,7 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
   if constexpr (EMIT) {
     // step scalars and retention of the chunk's tokens, for the replay
     if (!pinned && tid < C) {
-      const int64_t gi = (b * T + t0 + (tid < Lc ? tid : 0)) * H + h;
+      const int64_t gi = (tb + t0 + (tid < Lc ? tid : 0)) * H + h;
       sC[tid] = em.cstep[gi];
       sR[tid] = em.r ? em.r[gi] : 1.0f;
     }
@@ -414,7 +423,7 @@ struct SeqLay {
 // With the residual form (KRES) the write key is k~ = k + E with k and E both
 // exact bf16, so every product with k~ is the sum of a product with k and one
 // with E; otherwise the E buffer holds the bf16 k~ itself.
-template <bool GATED, bool KRES>
+template <bool GATED, bool KRES, bool VL>
 __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 *tin, int64_t N) {
   typedef SeqLay L;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
@@ -446,9 +455,11 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
   const int slot = bid & 7, rest = bid >> 3;
   const int vt = rest % NT;
   const int64_t seq = (int64_t)(rest / NT) * 8 + slot;
-  const int64_t H = a.H, T = a.T;
+  const int64_t H = a.H;
   if (seq >= a.B * H) return;
   const int64_t b = seq / H, h = seq - b * H;
+  const int64_t T = seq_len<VL>(a, b), tb = seq_base<VL>(a, b);
+  const int64_t Nb = (T + C - 1) / C;  // this sequence's chunks (N is the workspace row stride)
   const int v0 = vt * VT;
 
   const bf16 *gq = static_cast<const bf16 *>(a.q);
@@ -457,7 +468,7 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
   const bf16 *gv = static_cast<const bf16 *>(a.v);
   bf16 *go = static_cast<bf16 *>(a.o);
   const int64_t tstride = H * KD;                   // elements between tokens (K == V == 128)
-  const int64_t base = (b * T) * tstride + h * KD;  // token 0 of this (b,h)
+  const int64_t base = tb * tstride + h * KD;  // token 0 of this (b,h)
   const bf16 *tseq = tin + seq * N * (C * C);
 
   // scores: the tiles above the diagonal are never written and stay zero
@@ -508,8 +519,8 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
   const char *eb = reinterpret_cast<const char *>(gkt + base);
   const char *vb = reinterpret_cast<const char *>(gv + base + v0);
   char *ob = reinterpret_cast<char *>(go + base + v0);
-  const char *bb = reinterpret_cast<const char *>(a.beta + b * T * H + h);
-  const char *ab = GATED ? reinterpret_cast<const char *>(a.alpha + b * T * H + h) : nullptr;
+  const char *bb = reinterpret_cast<const char *>(a.beta + tb * H + h);
+  const char *ab = GATED ? reinterpret_cast<const char *>(a.alpha + tb * H + h) : nullptr;
   uint32_t roff[2], coff[2];
   int rrow[2];
 #pragma unroll
@@ -559,11 +570,11 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
     for (int kk = 0; kk < 2; ++kk) pt[kk] = ld8(reinterpret_cast<const bf16 *>(tp + 64 * kk));
   };
 
-  if (N > 0) {
+  if (Nb > 0) {
     fetch(0, FQ | FK | FE);
     fetch_t(0);
   }
-  for (int64_t n = 0; n < N; ++n) {
+  for (int64_t n = 0; n < Nb; ++n) {
     const int64_t t0 = n * C;
     const int Lc = (int)((T - t0) < C ? (T - t0) : C);
     __syncthreads();  // the previous chunk is done with every LDS buffer
@@ -596,7 +607,7 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
     // valid and unused) so that the number of loads in flight does not depend
     // on the path, which lets the waits for Tm count past these loads instead
     // of draining them.
-    const int64_t nn1 = n + 1 < N ? n + 1 : n;
+    const int64_t nn1 = n + 1 < Nb ? n + 1 : n;
     fetch(nn1, FQ);
 
     // ---- stage G.  Row waves: K S^T and Q S^T for their rows, both value
@@ -864,7 +875,7 @@ int device_cus() {
   return cus[dev];
 }
 
-template <bool GATED, bool KRES>
+template <bool GATED, bool KRES, bool VL>
 void launch_both(const ChunkArgs &a, bf16 *tw, int64_t N, hipStream_t s, const EmitArgs *em) {
   const int64_t nseq = a.B * a.H;
   if (N > 0) {
@@ -876,19 +887,34 @@ void launch_both(const ChunkArgs &a, bf16 *tw, int64_t N, hipStream_t s, const E
     const dim3 grid((unsigned)((nch + per - 1) / per)), block(256);
     if constexpr (KRES) {
       if (em) {
-        hipLaunchKernelGGL((chunk_tinv_kernel<GATED, true, true>), grid, block, 0, s, a, tw, N, *em);
+        hipLaunchKernelGGL((chunk_tinv_kernel<GATED, true, true, VL>), grid, block, 0, s, a, tw, N, *em);
         prof_mark(s, "chunk_tinv_kernel");
       }
     }
     if (!em) {
-      hipLaunchKernelGGL((chunk_tinv_kernel<GATED, KRES, false>), grid, block, 0, s, a, tw, N, EmitArgs{});
+      hipLaunchKernelGGL((chunk_tinv_kernel<GATED, KRES, false, VL>), grid, block, 0, s, a, tw, N, EmitArgs{});
       prof_mark(s, "chunk_tinv_kernel");
     }
   }
   const int64_t groups = (nseq + 7) / 8;
-  hipLaunchKernelGGL((chunk_seq_kernel<GATED, KRES>), dim3((unsigned)(groups * 8 * NT)), dim3(512), 0, s, a,
+  hipLaunchKernelGGL((chunk_seq_kernel<GATED, KRES, VL>), dim3((unsigned)(groups * 8 * NT)), dim3(512), 0, s, a,
                      (const bf16 *)tw, N);
   prof_mark(s, "chunk_seq_kernel");
+}
+
+template <bool VL>
+void launch_gated(const ChunkArgs &a, bf16 *tw, int64_t N, hipStream_t s, const EmitArgs *em) {
+  if (a.alpha) {
+    if (a.kt_is_res)
+      launch_both<true, true, VL>(a, tw, N, s, em);
+    else
+      launch_both<true, false, VL>(a, tw, N, s, nullptr);
+  } else {
+    if (a.kt_is_res)
+      launch_both<false, true, VL>(a, tw, N, s, em);
+    else
+      launch_both<false, false, VL>(a, tw, N, s, nullptr);
+  }
 }
 
 }  // namespace
@@ -903,17 +929,10 @@ hipError_t launch_chunk_wy(const ChunkArgs &a, void *work, hipStream_t s, const 
   if (em && (!a.kt_is_res || C != SCAN_CHUNK)) return hipErrorInvalidValue;
   const int64_t N = (a.T + C - 1) / C;
   bf16 *tw = static_cast<bf16 *>(work);
-  if (a.alpha) {
-    if (a.kt_is_res)
-      launch_both<true, true>(a, tw, N, s, em);
-    else
-      launch_both<true, false>(a, tw, N, s, nullptr);
-  } else {
-    if (a.kt_is_res)
-      launch_both<false, true>(a, tw, N, s, em);
-    else
-      launch_both<false, false>(a, tw, N, s, nullptr);
-  }
+  if (a.cu)
+    launch_gated<true>(a, tw, N, s, em);
+  else
+    launch_gated<false>(a, tw, N, s, em);
   return hipGetLastError();
 }
 

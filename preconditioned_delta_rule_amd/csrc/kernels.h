@@ -8,6 +8,22 @@
 
 namespace osdn {
 
+// Sequences of a batch.  With cu == null, sequence b is tokens [b T, b T + T)
+// of [B,T,H,.] tensors; with cu (device int64 [B+1], variable lengths), it is
+// tokens [cu[b], cu[b+1]) of packed [1, cu[B], H, .] tensors and T is the
+// longest length (it sizes per-chunk workspace rows).  Kernels take VL (cu
+// present) as a template flag, so uniform batches compile as before.
+template <bool VL, class A>
+__device__ __forceinline__ int64_t seq_base(const A &a, int64_t b) {
+  if constexpr (VL) return a.cu[b];
+  else return b * a.T;
+}
+template <bool VL, class A>
+__device__ __forceinline__ int64_t seq_len(const A &a, int64_t b) {
+  if constexpr (VL) return a.cu[b + 1] - a.cu[b];
+  else return a.T;
+}
+
 struct ScanArgs {
   const void *k;        // [B,T,H,K]
   const float *beta;    // [B,T,H]
@@ -19,6 +35,7 @@ struct ScanArgs {
   int64_t B, T, H, K;
   float eta, d_min, d_max, eps;
   int clamp, beta_aware;
+  const int64_t *cu = nullptr;  // variable-length sequences (see seq_base)
 };
 
 struct ChunkArgs {
@@ -32,6 +49,7 @@ struct ChunkArgs {
   int64_t B, T, H, K, V;
   int C;
   float q_scale;
+  const int64_t *cu = nullptr;  // variable-length sequences (see seq_base)
 };
 
 // Each returns hipSuccess or the launch error.

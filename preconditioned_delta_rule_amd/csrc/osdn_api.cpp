@@ -332,9 +332,10 @@ size_t osdn_fwd_workspace_bytes(const osdn_desc *d) {
   return fwd_keys_bytes(d) + osdn::scan_work_bytes(d->B, d->T, d->H, d->K) + chunk_work_bytes(d);
 }
 
-osdn_status osdn_fwd(const osdn_desc *d, const void *q, const void *k, const void *v, const float *beta,
-                     const float *r, const float *alpha, const float *d1, const float *S0, void *o, float *S_out,
-                     float *d_out, void *k_tilde_out, void *workspace, size_t workspace_bytes, void *stream) {
+static osdn_status fwd_impl(const osdn_desc *d, const int64_t *cu, const void *q, const void *k, const void *v,
+                            const float *beta, const float *r, const float *alpha, const float *d1,
+                            const float *S0, void *o, float *S_out, float *d_out, void *k_tilde_out,
+                            void *workspace, size_t workspace_bytes, void *stream) {
   OSDN_TRY(validate(d, 3));
   const bool need_seq = d->T > 0;
   OSDN_TRY(check_ptr(q, "q", need_seq));
@@ -352,6 +353,7 @@ osdn_status osdn_fwd(const osdn_desc *d, const void *q, const void *k, const voi
   hipStream_t s = static_cast<hipStream_t>(stream);
   osdn::ScanArgs sa = scan_args(d, k, beta, r, d1, k_tilde_out, d_out);
   osdn::ChunkArgs ca = chunk_args(d, q, k, k_tilde_out, v, beta, alpha, S0, o, S_out);
+  sa.cu = ca.cu = need_seq ? cu : nullptr;
   if (!need_seq) {
     // nothing to sweep: d_out = d1 and S_out = S0 (the kernels do the copy)
     OSDN_TRY(run_scan(d, sa, s));
@@ -396,6 +398,23 @@ osdn_status osdn_fwd(const osdn_desc *d, const void *q, const void *k, const voi
     OSDN_TRY(run_chunk(d, ca, cw, s));
   }
   return ok();
+}
+
+osdn_status osdn_fwd(const osdn_desc *d, const void *q, const void *k, const void *v, const float *beta,
+                     const float *r, const float *alpha, const float *d1, const float *S0, void *o, float *S_out,
+                     float *d_out, void *k_tilde_out, void *workspace, size_t workspace_bytes, void *stream) {
+  return fwd_impl(d, nullptr, q, k, v, beta, r, alpha, d1, S0, o, S_out, d_out, k_tilde_out, workspace,
+                  workspace_bytes, stream);
+}
+
+osdn_status osdn_fwd_varlen(const osdn_desc *d, const int64_t *cu_seqlens, const void *q, const void *k,
+                            const void *v, const float *beta, const float *r, const float *alpha, const float *d1,
+                            const float *S0, void *o, float *S_out, float *d_out, void *k_tilde_out,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  OSDN_TRY(validate(d, 3));
+  OSDN_TRY(check_ptr(cu_seqlens, "cu_seqlens", true));
+  return fwd_impl(d, cu_seqlens, q, k, v, beta, r, alpha, d1, S0, o, S_out, d_out, k_tilde_out, workspace,
+                  workspace_bytes, stream);
 }
 
 osdn_status osdn_decode(const osdn_desc *d, const void *q, const void *k, const void *v, const float *beta,

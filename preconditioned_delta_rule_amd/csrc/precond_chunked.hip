@@ -61,18 +61,20 @@ __device__ __forceinline__ void lds_put(TIn *p, const Row<TIn, EPL, FULL> &r) {
 }
 
 // ---------------------------------------------------------------- prep
-template <typename TIn, int EPL, bool FULL, bool HAS_R>
+template <typename TIn, int EPL, bool FULL, bool HAS_R, bool VL>
 __global__ __launch_bounds__(64) void scan_prep_kernel(ScanArgs a, ScanWork wk, int64_t N) {
   const int lane = threadIdx.x;
   const int64_t seq = blockIdx.x / N, n = blockIdx.x % N;
-  const int64_t H = a.H, T = a.T, K = a.K;
+  const int64_t H = a.H, K = a.K;
   const int64_t b = seq / H, h = seq - b * H;
+  const int64_t T = seq_len<VL>(a, b), tb = seq_base<VL>(a, b);
   const int64_t t0 = n * CH;
+  if (VL && t0 >= T) return;  // past a shorter sequence's end
   const int L = (int)((T - t0) < CH ? (T - t0) : CH);
   const bool tok = lane < L;
-  const TIn *kp = static_cast<const TIn *>(a.k) + ((b * T + t0) * H + h) * K;
+  const TIn *kp = static_cast<const TIn *>(a.k) + ((tb + t0) * H + h) * K;
   const int64_t stride = H * K;
-  const int64_t gi = (b * T + t0 + (tok ? lane : 0)) * H + h;
+  const int64_t gi = (tb + t0 + (tok ? lane : 0)) * H + h;
   const float bt = a.beta[gi];
   const float rt = HAS_R ? a.r[gi] : 1.0f;
   Row<TIn, EPL, FULL> rows[CH];
@@ -137,22 +139,24 @@ __device__ __forceinline__ float row16_max(float x) {
 // so each load instruction covers four whole rows (rows of many tokens in one
 // instruction cost several times more), and a token's sums need only a
 // 16-lane reduction.  The per-token results pass through LDS to lane = token.
-template <typename TIn, bool HAS_R>
+template <typename TIn, bool HAS_R, bool VL>
 __global__ __launch_bounds__(256) void scan_prep128_kernel(ScanArgs a, ScanWork wk, int64_t N) {
   __shared__ float sred[4][2][CH];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t ci = (int64_t)blockIdx.x * 4 + w;
-  const int64_t H = a.H, T = a.T;
+  const int64_t H = a.H;
   if (ci >= a.B * H * N) return;
   const int64_t seq = ci / N, n = ci - seq * N;
   const int64_t b = seq / H, h = seq - b * H;
+  const int64_t T = seq_len<VL>(a, b), tb = seq_base<VL>(a, b);
   const int64_t t0 = n * CH;
+  if (VL && t0 >= T) return;  // past a shorter sequence's end (each wave has its own chunk and LDS)
   const int L = (int)((T - t0) < CH ? (T - t0) : CH);
   const bool tok = lane < L;
   const int64_t stride = H * 128;
-  const TIn *kp = static_cast<const TIn *>(a.k) + ((b * T + t0) * H + h) * 128 + 8 * (lane & 15);
-  const int64_t gi = (b * T + t0 + (tok ? lane : 0)) * H + h;
+  const TIn *kp = static_cast<const TIn *>(a.k) + ((tb + t0) * H + h) * 128 + 8 * (lane & 15);
+  const int64_t gi = (tb + t0 + (tok ? lane : 0)) * H + h;
   const float bt = a.beta[gi];
   const float rt = HAS_R ? a.r[gi] : 1.0f;
   float x[16][8];
@@ -221,7 +225,7 @@ constexpr size_t solve_lds_bytes() {
          (size_t)CH * 16;
 }
 
-template <typename TIn, int EPL, bool FULL, bool HAS_R, bool PF>
+template <typename TIn, int EPL, bool FULL, bool HAS_R, bool PF, bool VL>
 __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk, int64_t N) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int RP = 64 * EPL;      // row pitch of sR (elements)
@@ -233,8 +237,10 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
 
   const int lane = threadIdx.x;
   const int64_t seq = blockIdx.x;
-  const int64_t H = a.H, T = a.T, K = a.K;
+  const int64_t H = a.H, K = a.K;
   const int64_t b = seq / H, h = seq - b * H;
+  const int64_t T = seq_len<VL>(a, b), tb = seq_base<VL>(a, b);
+  const int64_t Nb = (T + CH - 1) / CH;  // this sequence's chunks (N is the row stride)
   const int64_t stride = H * K;
   const float eta = a.eta, eps = a.eps, dmin = a.d_min, dmax = a.d_max;
   const bool clamp = a.clamp != 0, aware = a.beta_aware != 0;
@@ -254,14 +260,14 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
   bool have = false;  // chunk n's rows already sit in sR, its scalars in nbt/nrt/nnrm
 
   // every pass of the loop advances n by step >= 1 (a pinned run sets it)
-  for (int64_t n = 0, step = 1; n < N; n += step) {
+  for (int64_t n = 0, step = 1; n < Nb; n += step) {
     step = 1;
     const int64_t t0 = n * CH;
     const int L = (int)((T - t0) < CH ? (T - t0) : CH);
     const bool tok = lane < L;  // lane u <-> token t0 + u
-    const int64_t gi = (b * T + t0 + (tok ? lane : 0)) * H + h;
+    const int64_t gi = (tb + t0 + (tok ? lane : 0)) * H + h;
     if ((n & 63) == 0) {
-      const int p = n + lane < N ? wk.pin[seq * N + n + lane] : 0;
+      const int p = n + lane < Nb ? wk.pin[seq * N + n + lane] : 0;
       pinmask = __ballot(p == 1);
     }
 
@@ -297,7 +303,7 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
       if (valid[e]) wk.dstart[(seq * N + n) * K + lane * EPL + e] = d[e];
 
     // this chunk's key rows and scalars
-    const TIn *kp = static_cast<const TIn *>(a.k) + ((b * T + t0) * H + h) * K;
+    const TIn *kp = static_cast<const TIn *>(a.k) + ((tb + t0) * H + h) * K;
     float bt, rt, nrm;
     if (PF && have) {
       bt = nbt;
@@ -326,7 +332,7 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
     // unless the prep pass marked it: if d ends this chunk on d_min the run
     // of marked chunks is skipped without its rows, else they are loaded then
     const bool next_marked = ((n + 1) & 63) != 0 && ((pinmask >> ((n + 1) & 63)) & 1) != 0;
-    const bool pf = PF && n + 1 < N && !next_marked;
+    const bool pf = PF && n + 1 < Nb && !next_marked;
     if constexpr (PF) {
       if (pf) {
         const int64_t t1 = t0 + CH;
@@ -334,7 +340,7 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
         const TIn *kp1 = kp + CH * stride;
 #pragma unroll
         for (int u = 0; u < CH; ++u) nrow[u].load(kp1 + (u < L1 ? u : L1 - 1) * stride, lane, K);
-        const int64_t gi1 = (b * T + t1 + (lane < L1 ? lane : 0)) * H + h;
+        const int64_t gi1 = (tb + t1 + (lane < L1 ? lane : 0)) * H + h;
         nbt = a.beta[gi1];
         nrt = HAS_R ? a.r[gi1] : 1.0f;
         nnrm = wk.norm[gi1];
@@ -624,19 +630,21 @@ __device__ __forceinline__ void emit_rows(const Row<TIn, EPL, FULL> (&rows)[CH],
   }
 }
 
-template <typename TIn, int EPL, bool FULL, bool HAS_R, bool WKT, bool WRES>
+template <typename TIn, int EPL, bool FULL, bool HAS_R, bool WKT, bool WRES, bool VL>
 __global__ __launch_bounds__(64) void scan_emit_kernel(ScanArgs a, ScanWork wk, int64_t N) {
   const int lane = threadIdx.x;
   const int64_t seq = blockIdx.x / N, n = blockIdx.x % N;
-  const int64_t H = a.H, T = a.T, K = a.K;
+  const int64_t H = a.H, K = a.K;
   const int64_t b = seq / H, h = seq - b * H;
+  const int64_t T = seq_len<VL>(a, b), tb = seq_base<VL>(a, b);
   const int64_t t0 = n * CH;
+  if (VL && t0 >= T) return;  // past a shorter sequence's end
   const int L = (int)((T - t0) < CH ? (T - t0) : CH);
   const int64_t stride = H * K;
-  const int64_t row0 = ((b * T + t0) * H + h) * K;
+  const int64_t row0 = ((tb + t0) * H + h) * K;
   // per-token scalars and the chunk-start d are loaded before the rows, so
   // waiting for them does not wait for the rows
-  const int64_t gi = (b * T + t0 + (lane < L ? lane : 0)) * H + h;
+  const int64_t gi = (tb + t0 + (lane < L ? lane : 0)) * H + h;
   const float cv = wk.cstep[gi];
   const float rv = HAS_R ? a.r[gi] : 1.0f;
   // a chunk the solve pass took as pinned (marked 2) starts from d_min and
@@ -666,28 +674,28 @@ __global__ __launch_bounds__(64) void scan_emit_kernel(ScanArgs a, ScanWork wk, 
     emit_rows<TIn, EPL, FULL, WKT, WRES, false>(rows, d, cv, rv, lo, hi, L, op, rp, stride, lane, K);
 }
 
-template <typename TIn, int EPL, bool FULL, bool HAS_R>
+template <typename TIn, int EPL, bool FULL, bool HAS_R, bool VL>
 void launch_emit(const ScanArgs &a, const ScanWork &w, int64_t N, hipStream_t s) {
   dim3 grid((unsigned)(a.B * a.H * N)), block(64);
   if (a.k_tilde && a.kt_res)
-    hipLaunchKernelGGL((scan_emit_kernel<TIn, EPL, FULL, HAS_R, true, true>), grid, block, 0, s, a, w, N);
+    hipLaunchKernelGGL((scan_emit_kernel<TIn, EPL, FULL, HAS_R, true, true, VL>), grid, block, 0, s, a, w, N);
   else if (a.kt_res)
-    hipLaunchKernelGGL((scan_emit_kernel<TIn, EPL, FULL, HAS_R, false, true>), grid, block, 0, s, a, w, N);
+    hipLaunchKernelGGL((scan_emit_kernel<TIn, EPL, FULL, HAS_R, false, true, VL>), grid, block, 0, s, a, w, N);
   else
-    hipLaunchKernelGGL((scan_emit_kernel<TIn, EPL, FULL, HAS_R, true, false>), grid, block, 0, s, a, w, N);
+    hipLaunchKernelGGL((scan_emit_kernel<TIn, EPL, FULL, HAS_R, true, false, VL>), grid, block, 0, s, a, w, N);
   prof_mark(s, "scan_emit_kernel");
 }
 
-template <typename TIn, int EPL, bool FULL, bool HAS_R>
+template <typename TIn, int EPL, bool FULL, bool HAS_R, bool VL>
 hipError_t launch_all(const ScanArgs &a, const ScanWork &w, hipStream_t s, bool emit) {
   const int64_t N = (a.T + CH - 1) / CH;
   const int64_t nseq = a.B * a.H;
   if (N > 0) {
     if (a.K == 128) {
-      hipLaunchKernelGGL((scan_prep128_kernel<TIn, HAS_R>), dim3((unsigned)((nseq * N + 3) / 4)), dim3(256), 0, s,
+      hipLaunchKernelGGL((scan_prep128_kernel<TIn, HAS_R, VL>), dim3((unsigned)((nseq * N + 3) / 4)), dim3(256), 0, s,
                          a, w, N);
     } else {
-      hipLaunchKernelGGL((scan_prep_kernel<TIn, EPL, FULL, HAS_R>), dim3((unsigned)(nseq * N)), dim3(64), 0, s,
+      hipLaunchKernelGGL((scan_prep_kernel<TIn, EPL, FULL, HAS_R, VL>), dim3((unsigned)(nseq * N)), dim3(64), 0, s,
                          a, w, N);
     }
     prof_mark(s, "scan_prep_kernel");
@@ -695,25 +703,26 @@ hipError_t launch_all(const ScanArgs &a, const ScanWork &w, hipStream_t s, bool 
   constexpr bool PF = Row<TIn, EPL, FULL>::WORDS <= 2;
   constexpr size_t shm = solve_lds_bytes<TIn, EPL>();
   static_assert(shm <= 160 * 1024, "solve kernel LDS");
-  auto kern = scan_solve_kernel<TIn, EPL, FULL, HAS_R, PF>;
+  auto kern = scan_solve_kernel<TIn, EPL, FULL, HAS_R, PF, VL>;
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)nseq), dim3(64), shm, s, a, w, N);
   prof_mark(s, "scan_solve_kernel");
-  if (N > 0 && emit) launch_emit<TIn, EPL, FULL, HAS_R>(a, w, N, s);
+  if (N > 0 && emit) launch_emit<TIn, EPL, FULL, HAS_R, VL>(a, w, N, s);
   return hipGetLastError();
 }
 
-template <typename TIn, int EPL, bool FULL>
+template <typename TIn, int EPL, bool FULL, bool VL>
 hipError_t launch_r(const ScanArgs &a, const ScanWork &w, hipStream_t s, bool e) {
-  return a.r ? launch_all<TIn, EPL, FULL, true>(a, w, s, e) : launch_all<TIn, EPL, FULL, false>(a, w, s, e);
+  return a.r ? launch_all<TIn, EPL, FULL, true, VL>(a, w, s, e) : launch_all<TIn, EPL, FULL, false, VL>(a, w, s, e);
 }
 
-template <typename TIn>
+template <typename TIn, bool VL>
 hipError_t launch_typed(const ScanArgs &a, const ScanWork &w, hipStream_t s, bool e) {
-  if (a.K <= 64) return a.K == 64 ? launch_r<TIn, 1, true>(a, w, s, e) : launch_r<TIn, 1, false>(a, w, s, e);
-  if (a.K <= 128) return a.K == 128 ? launch_r<TIn, 2, true>(a, w, s, e) : launch_r<TIn, 2, false>(a, w, s, e);
-  return a.K == 256 ? launch_r<TIn, 4, true>(a, w, s, e) : launch_r<TIn, 4, false>(a, w, s, e);
+  if (a.K <= 64) return a.K == 64 ? launch_r<TIn, 1, true, VL>(a, w, s, e) : launch_r<TIn, 1, false, VL>(a, w, s, e);
+  if (a.K <= 128)
+    return a.K == 128 ? launch_r<TIn, 2, true, VL>(a, w, s, e) : launch_r<TIn, 2, false, VL>(a, w, s, e);
+  return a.K == 256 ? launch_r<TIn, 4, true, VL>(a, w, s, e) : launch_r<TIn, 4, false, VL>(a, w, s, e);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -746,7 +755,8 @@ ScanWork scan_work_layout(void *base, int64_t B, int64_t T, int64_t H, int64_t K
 hipError_t launch_precond_scan_chunked(const ScanArgs &a, const ScanWork &w, bool is_bf16, hipStream_t s,
                                        bool emit) {
   if (a.B * a.H == 0) return hipSuccess;
-  return is_bf16 ? launch_typed<bf16>(a, w, s, emit) : launch_typed<float>(a, w, s, emit);
+  if (a.cu) return is_bf16 ? launch_typed<bf16, true>(a, w, s, emit) : launch_typed<float, true>(a, w, s, emit);
+  return is_bf16 ? launch_typed<bf16, false>(a, w, s, emit) : launch_typed<float, false>(a, w, s, emit);
 }
 
 }  // namespace osdn
