@@ -37,6 +37,10 @@ fp32 vector peak (157.3 TFLOP/s) with its arithmetic per token-head (K = V =
 128: record 6 V K = 98,304 flops, the phase-2 reverse 14 V K = 229,376, the
 phase-1 reverse 30 K = 3,840) and against HBM with its bytes.
 
+With --varlen a step is one osdn_fwd_varlen call over a packed batch of
+variable-length sequences (default: 65,536 tokens in sequences of 256-4,096,
+H=16, K=V=128, bf16, APF); per-token-head work is that of the forward.
+
 With --decode a step is instead one osdn_decode call (the single-token
 recurrence): T new tokens per (b,h) continuing a carried fp32 state, default
 workload one token for each of 256 sequences of the 1.3B-shaped layer
@@ -64,6 +68,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "OSDN fwd tokens/sec (phase1+phase2) at H=16,K=V=128,T=4096; % HBM/MFMA roofline"
+VARLEN_METRIC = "OSDN fwd tokens/sec over a packed variable-length batch (osdn_fwd_varlen) at H=16,K=V=128; % HBM roofline"
 BWD_METRIC = "OSDN bwd tokens/sec (osdn_bwd, both phases) at H=16,K=V=128,T=4096; % fp32 vector roofline"
 FP32_VALU_PEAK_TFLOPS = 157.3
 DECODE_METRIC = "OSDN decode tokens/sec (osdn_decode, new tokens x sequences per call) at H=16,K=V=128; % HBM roofline"
@@ -218,6 +223,8 @@ def main(argv=None):
                     help="named workload (default 1p3b_apf; with --decode decode_1p3b_b256)")
     ap.add_argument("--decode", action="store_true",
                     help="time osdn_decode (one call per step) instead of osdn_fwd")
+    ap.add_argument("--varlen", action="store_true",
+                    help="time osdn_fwd_varlen on a packed batch (default workload varlen_1p3b_65k)")
     ap.add_argument("--backward", action="store_true",
                     help="time osdn_bwd (one call per step) instead of osdn_fwd")
     ap.add_argument("--copies", type=int, default=4,
@@ -235,7 +242,8 @@ def main(argv=None):
                     help="the commands that produced the --pmc-summary runs (recorded)")
     args = ap.parse_args(argv)
     if args.workload is None:
-        args.workload = "decode_1p3b_b256" if args.decode else "1p3b_apf"
+        args.workload = ("decode_1p3b_b256" if args.decode else
+                         "varlen_1p3b_65k" if args.varlen else "1p3b_apf")
 
     if args.pmc_summary:
         return pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, args.pmc_command)
@@ -273,6 +281,8 @@ def main(argv=None):
         return decode_bench(args, inp, dev)
     if args.backward:
         return bwd_bench(args, inp, dev)
+    if args.varlen:
+        return varlen_bench(args, inp, dev)
 
     sets = []
     for c in range(max(1, args.copies)):
@@ -375,6 +385,98 @@ def main(argv=None):
                    "step_device_ms_p10": float(np.percentile(step_ms, 10)) if step_ms else None,
                    "step_device_ms_p90": float(np.percentile(step_ms, 90)) if step_ms else None},
         "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def varlen_bench(args, inp, dev):
+    """--varlen: one osdn_fwd_varlen call per step on a packed batch."""
+    import torch
+    import preconditioned_delta_rule_amd as osdn
+    from workloads import varlen_lengths
+    spec, p = inp["spec"], inp["params"]
+    _, total, H, K = inp["k"].shape
+    V = inp["v"].shape[-1]
+    apf, gated = inp["r"] is not None, inp["alpha"] is not None
+    tdt = torch.bfloat16 if p["dtype"] == "bf16" else torch.float32
+    elem = 2 if p["dtype"] == "bf16" else 4
+    lens = varlen_lengths(total, seed=spec["seed"] + 3)
+    S, Tmax = len(lens), max(lens)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int64, device=dev)
+
+    def up(x, dt):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dt).to(dev)
+
+    s = dict(q=up(inp["q"], tdt), k=up(inp["k"], tdt), v=up(inp["v"], tdt),
+             beta=up(inp["beta"], torch.float32), r=up(inp["r"], torch.float32),
+             alpha=up(inp["alpha"], torch.float32), o=torch.empty((1, total, H, V), dtype=tdt, device=dev),
+             S=torch.empty((S, H, V, K), dtype=torch.float32, device=dev),
+             d=torch.empty((S, H, K), dtype=torch.float32, device=dev))
+    ws = torch.empty(osdn.fwd_workspace_bytes(S, Tmax, H, K, V, dtype=osdn.BF16 if elem == 2 else osdn.F32,
+                                              chunk=p["chunk"]),
+                     dtype=torch.uint8, device=dev)
+    kw = dict(chunk=p["chunk"], eta=p["eta"], d_min=p["d_min"], d_max=p["d_max"], clamp=p["clamp"],
+              eps=p["eps"], q_scale=p["q_scale"], beta_aware=p["beta_aware"])
+
+    def step(i):
+        osdn.fwd_varlen(s["q"], s["k"], s["v"], s["beta"], s["r"], s["alpha"], cu_seqlens=cu,
+                        max_seqlen=Tmax, o=s["o"], S_out=s["S"], d_out=s["d"], workspace=ws, **kw)
+
+    log("warmup", args.warmup)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    nsteps = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    launches = osdn.kernel_times(lambda: [step(i) for i in range(nsteps)], dev)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / nsteps
+    nth = total * H
+    kernels = {}
+    for name in sorted(set(n for n, _ in launches)):
+        vals = [ms for n, ms in launches if n == name]
+        ms = float(np.mean(vals))
+        nbytes, flops = kernel_work(name, K, V, p["chunk"], apf, gated, elem)
+        gbs = nbytes * nth / (ms * 1e-3) / 1e9 if ms > 0 else None
+        kernels[name] = {"ms": ms, "bytes_per_token_head": nbytes, "GB/s": gbs,
+                         "hbm_frac": gbs / HBM_PEAK_GBS if gbs else None}
+        log("  %-20s %.4f ms  %.0f GB/s" % (name, ms, gbs or 0))
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    dk = kernels[dom]
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": dk["GB/s"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": dk["hbm_frac"], "traffic": None,
+                "algorithmic_bytes_per_launch": dk["bytes_per_token_head"] * nth}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        # a bounded sample: the first two sequences, all heads
+        a, b = 0, int(cu[2].item()) if S > 1 else total
+        reps, wall = 0, 0.0
+        while wall < args.cpu_seconds or reps == 0:
+            t0 = time.perf_counter()
+            for i in range(min(2, S)):
+                x, y = int(cu[i].item()), int(cu[i + 1].item())
+                sl = lambda z: None if z is None else np.ascontiguousarray(z[:, x:y])
+                oracle.forward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(inp["r"]),
+                               sl(inp["alpha"]), eta=p["eta"], d_min=p["d_min"], d_max=p["d_max"],
+                               clamp=p["clamp"], eps=p["eps"], beta_aware=p["beta_aware"],
+                               q_scale=p["q_scale"], threads=min(H, oracle.default_threads()))
+            wall += time.perf_counter() - t0
+            reps += 1
+        cpu = {"value": reps * (b - a) / wall, "unit": "tokens/s", "cores": min(H, oracle.default_threads()),
+               "kind": "oracle",
+               "sample": "the first two sequences (%d tokens, all %d heads), fp64 oracle, one (sequence, "
+                         "head) per thread, %d run(s) in %.2f s" % (b - a, H, reps, wall)}
+    out = {
+        "metric": VARLEN_METRIC, "value": total / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": nsteps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": p["dtype"], "data": "synthetic",
+        "config": {"workload": args.workload, "total_tokens": total, "sequences": S, "max_seqlen": Tmax,
+                   "H": H, "K": K, "V": V, "apf": apf, "gated": gated, "seed": spec["seed"]},
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -140,3 +140,30 @@ def test_varlen_requires_cu_seqlens():
     null = ctypes.c_void_p(None)
     st = lib.osdn_fwd_varlen(ctypes.byref(d), null, *([null] * 13), ctypes.c_size_t(0), null)
     assert st == osdn.EINVAL and "cu_seqlens" in lib.osdn_last_error().decode()
+
+
+def test_varlen_full_size_sampled():
+    """The packed 65,536-token batch timed by the bench (sequences of 256-4,096
+    tokens, H=16, K=V=128, bf16, APF) in one call; the oracle recomputes
+    sampled (sequence, head) pairs on their own."""
+    from workloads import varlen_lengths
+    inp = make_inputs("varlen_1p3b_65k")
+    p = inp["params"]
+    lens = varlen_lengths(inp["k"].shape[1], seed=inp["spec"]["seed"] + 3)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    o, S, d, _ = run_varlen(inp, cu, None, None)
+    longest = int(np.argmax(lens))
+    picks = [(0, 0), (longest, 7), (len(lens) - 1, 15)]
+    o_np = to_np(o)
+    S_np, d_np = to_np(S), to_np(d)
+    for i, h in picks:
+        a, b = int(cu[i]), int(cu[i + 1])
+        sl = {n: (None if inp[n] is None else np.ascontiguousarray(inp[n][:, a:b, h:h + 1]))
+              for n in ("q", "k", "v", "beta", "r", "alpha")}
+        ref = oracle.forward(sl["q"], sl["k"], sl["v"], sl["beta"], sl["r"], sl["alpha"], eta=p["eta"],
+                             d_min=p["d_min"], d_max=p["d_max"], clamp=p["clamp"], eps=p["eps"],
+                             beta_aware=p["beta_aware"], q_scale=p["q_scale"])
+        tag = (i, h, b - a)
+        assert o_err(o_np[:, a:b, h:h + 1], ref["o"]) <= BF16_OS, tag
+        assert s_err(S_np[i:i + 1, h:h + 1], ref["S"]) <= BF16_OS, tag
+        assert rel_err(d_np[i:i + 1, h:h + 1], ref["d"]) <= F32_D, tag

@@ -16,6 +16,9 @@ Recipe (same for every named workload unless stated):
     generator ``default_rng(seed + 2)`` draws dL/do ~ N(0, 1) [B,T,H,V]
     (rounded to bf16 for bf16 workloads), then dL/dS_T ~ N(0, 1) and
     dL/dd_{T+1} ~ N(0, 1), float32;
+  * packed variable-length batches (``varlen_lengths``): sequence lengths
+    drawn with ``default_rng(seed + 3)`` uniformly from [256, 4096] until the
+    packed length is reached (the last one cut to fit);
   * decode workloads (a few new tokens continuing a carried state) draw their
     tokens the same way and the state with ``random_state``: a second
     generator ``default_rng(seed + 1)`` draws d_1 ~ U(0.6, 1.9) per coordinate
@@ -48,6 +51,10 @@ WORKLOADS = {
     # backward: the 1.3B-shaped layer at a shorter sequence
     "bwd_1p3b_t1024": dict(B=4, T=1024, H=16, K=128, V=128, dtype="bf16", chunk=64,
                            seed=7, apf=True),
+    # packed variable-length batch (the training batches of the pages'
+    # Appendix F): 65,536 tokens, sequence lengths from varlen_lengths
+    "varlen_1p3b_65k": dict(B=1, T=65536, H=16, K=128, V=128, dtype="bf16", chunk=64,
+                            seed=8, apf=True),
     "decode_1p3b": dict(B=4, T=1, H=16, K=128, V=128, dtype="bf16", chunk=64,
                         seed=5, apf=True, state=True),
     "decode_1p3b_b256": dict(B=256, T=1, H=16, K=128, V=128, dtype="bf16",
@@ -229,3 +236,15 @@ def random_cotangent(inputs: dict, seed: int = 0):
     dS = rng.standard_normal((B, H, V, K), dtype=np.float32)
     dd = rng.standard_normal((B, H, K), dtype=np.float32)
     return dout, dS, dd
+
+
+def varlen_lengths(total: int, seed: int = 0, lo: int = 256, hi: int = 4096):
+    """Sequence lengths of a packed batch: uniform integers in [lo, hi] from
+    default_rng(seed), the last one cut so that they sum to total."""
+    rng = np.random.default_rng(seed)
+    out, acc = [], 0
+    while acc < total:
+        n = int(min(rng.integers(lo, hi + 1), total - acc))
+        out.append(n)
+        acc += n
+    return out
