@@ -25,7 +25,16 @@ gamma_i = prod_{l<=i} alpha_l:
     O    = (gamma . Q) S^T + [1[j<=i] (gamma_i/gamma_j) <q_i, k~_j>] (U - W S^T)
 
 The readout of the gated form is the post-write readout o_t = S_t q_t expanded
-the same way.  A partial last chunk (T not a multiple of C) is processed as a
+the same way.
+
+OSKDA (Appendix B.2), state S in R^{K x V}, channel-wise decay alpha_t in
+R^K, Gamma_i = prod_{l<=i} alpha_l (per channel), gamma_C = Gamma_C:
+
+    A_ij = 1[j<i] beta_i <Gamma_i . k_i, k~_j / Gamma_j>
+    M    = (I + A)^-1 B
+    W    = M (Gamma . K),  U = M V
+    S'   = Diag(gamma_C) S + ((gamma_C / Gamma) . K~)^T (U - W S)
+    O    = (Gamma . Q) S + lower_incl_diag((Gamma . Q)(K~ / Gamma)^T) (U - W S)  A partial last chunk (T not a multiple of C) is processed as a
 shorter chunk.  Arrays use the [B,T,H,X] layout; everything is float64.
 """
 from __future__ import annotations
@@ -69,6 +78,44 @@ def gated_chunk_step(S, Q, K, Kt, V, beta, alpha, q_scale=1.0):
     rho = gamma[-1] / gamma
     S_next = gamma[-1] * S + D.T @ (rho[:, None] * Kt)
     return O, S_next
+
+
+def kda_chunk_step(S, Q, K, Kt, V, beta, alpha, q_scale=1.0):
+    """One OSKDA chunk (Appendix B.2): S [K,V], alpha [C,K]; returns
+    (O [C,V], S_next [K,V])."""
+    C = K.shape[0]
+    G = np.cumprod(alpha, axis=0)                     # Gamma [C,K]
+    A = np.tril(beta[:, None] * ((G * K) @ (Kt / G).T), -1)
+    M = np.linalg.inv(np.eye(C) + A) @ np.diag(beta)
+    W = M @ (G * K)
+    U = M @ V
+    D = U - W @ S
+    Qg = G * (q_scale * Q)
+    O = Qg @ S + np.tril(Qg @ (Kt / G).T) @ D
+    S_next = G[-1][:, None] * S + ((G[-1][None, :] / G) * Kt).T @ D
+    return O, S_next
+
+
+def kda_forward(q, k, k_tilde, v, beta, alpha=None, S0=None, *, chunk=64, q_scale=1.0):
+    """Chunkwise OSKDA phase 2 over [B,T,H,*] inputs; alpha [B,T,H,K] or None,
+    S0 [B,H,K,V].  Returns (o, S_out [B,H,K,V])."""
+    q, k, k_tilde, v, beta = (np.asarray(x, np.float64) for x in (q, k, k_tilde, v, beta))
+    B, T, H, Kd = k.shape
+    Vd = v.shape[-1]
+    o = np.zeros((B, T, H, Vd))
+    S_out = np.zeros((B, H, Kd, Vd))
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((Kd, Vd)) if S0 is None else np.array(S0[b, h], np.float64)
+            for t0 in range(0, T, chunk):
+                sl = slice(t0, min(T, t0 + chunk))
+                al = (np.ones((sl.stop - t0, Kd)) if alpha is None
+                      else np.asarray(alpha[b, sl, h], np.float64))
+                O, S = kda_chunk_step(S, q[b, sl, h], k[b, sl, h], k_tilde[b, sl, h],
+                                      v[b, sl, h], beta[b, sl, h], al, q_scale=q_scale)
+                o[b, sl, h] = O
+            S_out[b, h] = S
+    return o, S_out
 
 
 def forward(q, k, k_tilde, v, beta, alpha=None, S0=None, *, chunk=64,

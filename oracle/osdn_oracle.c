@@ -13,6 +13,11 @@
  *               Appendix C Algorithm 2 part (2b); readout o_t = S_t q_t
  *               (Section 3); the Gated DeltaNet variant with the post-gate
  *               residual of Appendix B.1.
+ *   OSKDA    -- the Kimi Delta Attention backbone with online scaling,
+ *               Appendix B.2 and Table 3: K x V state, channel-wise decay,
+ *               preconditioned key on the left (storage) side.
+ *   vector retention -- diag(r_t) in place of the scalar r_t of Eq.(7),
+ *               Appendix A.5 Proposition A.3.
  *
  * Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may load
  * this library.  It shares no code with the GPU path.
@@ -50,15 +55,18 @@ int osdn_oracle_version(void) { return 1; }
  *   s      = k_t (.) k_t,  n = max(sum(s), eps)
  *   b'     = beta_t if beta_aware else 1
  *   c      = eta * b' * (1 - b' * <d, s>) / n
- *   d      = r_t * d + c * s                  (r_t = 1 when r is NULL)
+ *   d      = r_t * d + c * s                  (r_t = 1 when r is NULL;
+ *                                             r_t a vector when r_per_key)
  *   d      = min(max(d, d_min), d_max)        (only when clamp != 0)
  *
+ * r is [B,T,H] (one retention per token and head, Eq.(7)) or, with r_per_key,
+ * [B,T,H,K] (the vector-retention extension diag(r_t) of Proposition A.3).
  * k_tilde [B,T,H,K] receives every k~_t, d_out [B,H,K] receives d_{T+1}.
  * d_traj (nullable, [B,H,T+1,K]) receives d_1 .. d_{T+1}.
  */
 int osdn_oracle_precond_scan(int64_t B, int64_t T, int64_t H, int64_t K,
                              const double *k, const double *beta,
-                             const double *r, const double *d1, double eta,
+                             const double *r, int r_per_key, const double *d1, double eta,
                              double d_min, double d_max, int clamp, double eps,
                              int beta_aware, double *k_tilde, double *d_out,
                              double *d_traj, int threads) {
@@ -90,8 +98,9 @@ int osdn_oracle_precond_scan(int64_t B, int64_t T, int64_t H, int64_t K,
       double bt = beta[at_bth(b, t, h, T, H)];
       double bp = beta_aware ? bt : 1.0;
       double c = eta * bp * (1.0 - bp * align) / n;
-      double rt = r ? r[at_bth(b, t, h, T, H)] : 1.0;
       for (int64_t i = 0; i < K; ++i) {
+        double rt = 1.0;
+        if (r) rt = r_per_key ? r[at_bthx(b, t, h, i, T, H, K)] : r[at_bth(b, t, h, T, H)];
         double x = rt * d[i] + c * s[i];
         if (clamp) {
           if (x < d_min) x = d_min;
@@ -175,6 +184,68 @@ int osdn_oracle_delta_rule(int64_t B, int64_t T, int64_t H, int64_t K,
           S_traj[((size_t)bh * (size_t)(T + 1) + (size_t)(t + 1)) * VK + e] = S[e];
     }
     for (size_t e = 0; e < VK; ++e) S_out[(size_t)bh * VK + e] = S[e];
+    free(S);
+    free(u);
+  }
+  return 0;
+}
+
+/*
+ * Phase 2 of OSKDA, token by token (Appendix B.2, the online-scaled KDA row of
+ * Table 3).  The state keeps KDA's own K x V convention: S in R^{K x V} per
+ * (b,h), starting from S0 [B,H,K,V] (zeros when NULL).  For every token:
+ *
+ *   Sb  = Diag(alpha_t) S        (row i scaled by alpha_t[i]; Sb = S when
+ *                                 alpha is NULL)
+ *   u_t = v_t - Sb^T k_t         (residual read with the physical key)
+ *   S   = Sb + beta_t k~_t u_t^T (preconditioned key on the storage side)
+ *   o_t = S^T (q_scale * q_t)
+ *
+ * alpha [B,T,H,K]; o [B,T,H,V]; S_out [B,H,K,V].
+ */
+int osdn_oracle_kda_rule(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                         const double *q, const double *k, const double *k_tilde,
+                         const double *v, const double *beta, const double *alpha,
+                         const double *S0, double q_scale, double *o,
+                         double *S_out, int threads) {
+  if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0 || !q || !k || !k_tilde ||
+      !v || !beta || !o || !S_out)
+    return -1;
+  if (threads <= 0) threads = 1;
+  int64_t nseq = B * H;
+  size_t KV = (size_t)(K * V);
+#pragma omp parallel for num_threads(threads) schedule(dynamic, 1)
+  for (int64_t bh = 0; bh < nseq; ++bh) {
+    int64_t b = bh / H, h = bh % H;
+    double *S = (double *)malloc(sizeof(double) * KV);
+    double *u = (double *)malloc(sizeof(double) * (size_t)V);
+    for (size_t e = 0; e < KV; ++e) S[e] = S0 ? S0[(size_t)bh * KV + e] : 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      const double *qt = q + at_bthx(b, t, h, 0, T, H, K);
+      const double *kt = k + at_bthx(b, t, h, 0, T, H, K);
+      const double *wt = k_tilde + at_bthx(b, t, h, 0, T, H, K);
+      const double *vt = v + at_bthx(b, t, h, 0, T, H, V);
+      double bt = beta[at_bth(b, t, h, T, H)];
+      if (alpha) {
+        const double *at = alpha + at_bthx(b, t, h, 0, T, H, K);
+        for (int64_t i = 0; i < K; ++i)
+          for (int64_t j = 0; j < V; ++j) S[i * V + j] *= at[i];
+      }
+      for (int64_t j = 0; j < V; ++j) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < K; ++i) acc += S[i * V + j] * kt[i];
+        u[j] = vt[j] - acc;
+      }
+      for (int64_t i = 0; i < K; ++i)
+        for (int64_t j = 0; j < V; ++j) S[i * V + j] += bt * wt[i] * u[j];
+      double *ot = o + at_bthx(b, t, h, 0, T, H, V);
+      for (int64_t j = 0; j < V; ++j) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < K; ++i) acc += S[i * V + j] * (q_scale * qt[i]);
+        ot[j] = acc;
+      }
+    }
+    for (size_t e = 0; e < KV; ++e) S_out[(size_t)bh * KV + e] = S[e];
     free(S);
     free(u);
   }

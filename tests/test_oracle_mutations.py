@@ -37,10 +37,10 @@ MUTATIONS = {
 }
 
 
-def _pin_tests():
+def _pin_tests(module=pins):
     out = []
-    for name in dir(pins):
-        fn = getattr(pins, name)
+    for name in dir(module):
+        fn = getattr(module, name)
         if name.startswith("test_") and callable(fn):
             marks = getattr(fn, "pytestmark", [])
             params = [m for m in marks if m.name == "parametrize"]
@@ -79,6 +79,46 @@ def test_pins_catch_mutation(mutation, tmp_path, monkeypatch):
     for name, fn, kwargs in _pin_tests():
         try:
             fn(oracle_lib=oracle, **kwargs) if "oracle_lib" in fn.__code__.co_varnames else fn(**kwargs)
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(name)
+    assert failed, "no pin caught the planted mistake %s" % mutation
+
+
+# ---- OSKDA phase 2 and vector retention: the pins of tests/test_oracle_kda.py
+KDA_MUTATIONS = {
+    "kda_decay_ignored": [("S[i * V + j] *= at[i];", "S[i * V + j] *= 1.0;")],
+    "kda_decay_on_value_axis": [("S[i * V + j] *= at[i];", "S[i * V + j] *= at[j % K];")],
+    "kda_read_with_write_key": [("acc += S[i * V + j] * kt[i];", "acc += S[i * V + j] * wt[i];")],
+    "kda_write_with_read_key": [("bt * wt[i] * u[j]", "bt * kt[i] * u[j]")],
+    "kda_write_gate_dropped": [("bt * wt[i] * u[j]", "wt[i] * u[j]")],
+    "kda_readout_from_old_state": [
+        ("for (int64_t i = 0; i < K; ++i)\n        for (int64_t j = 0; j < V; ++j) S[i * V + j] += bt * wt[i] * u[j];\n", ""),
+        ("    for (size_t e = 0; e < KV; ++e) S_out[(size_t)bh * KV + e] = S[e];",
+         "    for (size_t e = 0; e < KV; ++e) S_out[(size_t)bh * KV + e] = S[e] + 0.0 * u[0];")],
+    "kda_q_scale_ignored": [("(q_scale * qt[i]);\n        ot[j] = acc;", "qt[i];\n        ot[j] = acc;")],
+    "vector_retention_first_entry_only": [("r[at_bthx(b, t, h, i, T, H, K)]", "r[at_bthx(b, t, h, 0, T, H, K)]")],
+    "vector_retention_ignored": [("r_per_key ? r[at_bthx(b, t, h, i, T, H, K)]", "r_per_key ? 1.0")],
+}
+
+
+@pytest.mark.parametrize("mutation", sorted(KDA_MUTATIONS))
+def test_kda_pins_catch_mutation(mutation, tmp_path, monkeypatch):
+    from tests import test_oracle_kda as kpins
+    src = open(SRC).read()
+    for old, new in KDA_MUTATIONS[mutation]:
+        assert old in src, "mutation anchor missing: %r" % old
+        src = src.replace(old, new, 1)
+    cfile = tmp_path / "mut.c"
+    cfile.write_text(src)
+    so = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-o",
+                    str(so), str(cfile), "-lm"], check=True)
+    lib = oracle.bind(ctypes.CDLL(str(so)))
+    monkeypatch.setattr(oracle, "_lib", lib)
+    failed = []
+    for name, fn, kwargs in _pin_tests(kpins):
+        try:
+            fn(**kwargs)
         except (AssertionError, ValueError, FloatingPointError):
             failed.append(name)
     assert failed, "no pin caught the planted mistake %s" % mutation
