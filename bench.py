@@ -41,6 +41,10 @@ With --varlen a step is one osdn_fwd_varlen call over a packed batch of
 variable-length sequences (default: 65,536 tokens in sequences of 256-4,096,
 H=16, K=V=128, bf16, APF); per-token-head work is that of the forward.
 
+With --kda a step is one osdn_kda_fwd call (OSKDA: K x V state, channel-wise
+decay; default B=8, T=2048, H=8, K=V=128, bf16, APF); its roofline is the sweep
+kernel's fp32 matrix-core arithmetic.
+
 With --decode a step is instead one osdn_decode call (the single-token
 recurrence): T new tokens per (b,h) continuing a carried fp32 state, default
 workload one token for each of 256 sequences of the 1.3B-shaped layer
@@ -68,6 +72,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "OSDN fwd tokens/sec (phase1+phase2) at H=16,K=V=128,T=4096; % HBM/MFMA roofline"
+KDA_METRIC = "OSKDA fwd tokens/sec (osdn_kda_fwd) at H=8,K=V=128; % fp32 MFMA roofline"
 VARLEN_METRIC = "OSDN fwd tokens/sec over a packed variable-length batch (osdn_fwd_varlen) at H=16,K=V=128; % HBM roofline"
 BWD_METRIC = "OSDN bwd tokens/sec (osdn_bwd, both phases) at H=16,K=V=128,T=4096; % fp32 vector roofline"
 FP32_VALU_PEAK_TFLOPS = 157.3
@@ -223,6 +228,8 @@ def main(argv=None):
                     help="named workload (default 1p3b_apf; with --decode decode_1p3b_b256)")
     ap.add_argument("--decode", action="store_true",
                     help="time osdn_decode (one call per step) instead of osdn_fwd")
+    ap.add_argument("--kda", action="store_true",
+                    help="time osdn_kda_fwd (default workload kda_340m_apf)")
     ap.add_argument("--varlen", action="store_true",
                     help="time osdn_fwd_varlen on a packed batch (default workload varlen_1p3b_65k)")
     ap.add_argument("--backward", action="store_true",
@@ -243,7 +250,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.workload is None:
         args.workload = ("decode_1p3b_b256" if args.decode else
-                         "varlen_1p3b_65k" if args.varlen else "1p3b_apf")
+                         "varlen_1p3b_65k" if args.varlen else
+                         "kda_340m_apf" if args.kda else "1p3b_apf")
 
     if args.pmc_summary:
         return pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, args.pmc_command)
@@ -283,6 +291,8 @@ def main(argv=None):
         return bwd_bench(args, inp, dev)
     if args.varlen:
         return varlen_bench(args, inp, dev)
+    if args.kda:
+        return kda_bench(args, inp, dev)
 
     sets = []
     for c in range(max(1, args.copies)):
@@ -385,6 +395,117 @@ def main(argv=None):
                    "step_device_ms_p10": float(np.percentile(step_ms, 10)) if step_ms else None,
                    "step_device_ms_p90": float(np.percentile(step_ms, 90)) if step_ms else None},
         "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def kda_work(name, K, V, C=64, elem=2):
+    """Algorithmic (bytes, flops) per (token, head) of the OSKDA kernels.
+    Sweep: X = V - (Gamma.K)S and P = (Gamma.Q)S (2KV flops each), D = TB X and
+    M D (lower-triangular C x C times V: (C+1)V each), S += Kc^T D (2KV); it
+    reads the fp32 chunk operands (Gamma.K, Gamma.Q, Kc: 3K floats per token;
+    TB, M: 2C; gamma_C: K/C) and v, writes o.  Intra: reads q, k, the bf16
+    write-key residual, alpha (K floats) and beta, writes those operands; its
+    Gram and scores are the 10 lower 16x16 blocks of two C x C x K products."""
+    if name.startswith("kda_seq"):
+        nbytes = 4 * (3 * K + 2 * C) + 4 * K / C + 2 * elem * V
+        flops = 6 * K * V + 2 * (C + 1) * V
+        return nbytes, flops
+    if name.startswith("kda_intra"):
+        nbytes = 3 * elem * K + 4 * K + 4 + 4 * (3 * K + 2 * C) + 4 * K / C
+        flops = 2 * 2 * 10 * 16 * 16 * K / C
+        return nbytes, flops
+    return kernel_work(name, K, V, C, True, False, elem)
+
+
+def kda_bench(args, inp, dev):
+    """--kda: one osdn_kda_fwd call per step."""
+    import torch
+    import preconditioned_delta_rule_amd as osdn
+    spec, p = inp["spec"], inp["params"]
+    B, T, H, K = inp["k"].shape
+    V = inp["v"].shape[-1]
+    tdt = torch.bfloat16 if p["dtype"] == "bf16" else torch.float32
+    elem = 2 if p["dtype"] == "bf16" else 4
+
+    def up(x, dt):
+        return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(dt).to(dev)
+
+    sets = []
+    for c in range(max(1, args.copies)):
+        sets.append(dict(q=up(inp["q"], tdt), k=up(inp["k"], tdt), v=up(inp["v"], tdt),
+                         beta=up(inp["beta"], torch.float32), r=up(inp["r"], torch.float32),
+                         alpha=up(inp["alpha"], torch.float32),
+                         o=torch.empty((B, T, H, V), dtype=tdt, device=dev),
+                         S=torch.empty((B, H, K, V), dtype=torch.float32, device=dev),
+                         d=torch.empty((B, H, K), dtype=torch.float32, device=dev)))
+    ws = torch.empty(osdn.kda_fwd_workspace_bytes(B, T, H, K, V, dtype=osdn.BF16 if elem == 2 else osdn.F32),
+                     dtype=torch.uint8, device=dev)
+    kw = dict(eta=p["eta"], d_min=p["d_min"], d_max=p["d_max"], clamp=p["clamp"], eps=p["eps"],
+              q_scale=p["q_scale"], beta_aware=p["beta_aware"])
+
+    def step(i):
+        s = sets[i % len(sets)]
+        osdn.kda_fwd(s["q"], s["k"], s["v"], s["beta"], s["r"], s["alpha"], o=s["o"], S_out=s["S"],
+                     d_out=s["d"], workspace=ws, **kw)
+
+    log("warmup", args.warmup)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    nsteps = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    launches = osdn.kernel_times(lambda: [step(i) for i in range(nsteps)], dev)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / nsteps
+    nth = B * T * H
+    kernels = {}
+    for name in sorted(set(n for n, _ in launches)):
+        vals = [ms for n, ms in launches if n == name]
+        ms = float(np.mean(vals))
+        nbytes, flops = kda_work(name, K, V, 64, elem)
+        gbs = nbytes * nth / (ms * 1e-3) / 1e9 if ms > 0 else None
+        ent = {"ms": ms, "bytes_per_token_head": nbytes, "GB/s": gbs,
+               "hbm_frac": gbs / HBM_PEAK_GBS if gbs else None}
+        if flops and name.startswith("kda_"):
+            ent["flops_per_token_head"] = flops
+            ent["TFLOP/s"] = flops * nth / (ms * 1e-3) / 1e12
+            ent["mfma_fp32_frac"] = ent["TFLOP/s"] / FP32_VALU_PEAK_TFLOPS
+        kernels[name] = ent
+        log("  %-20s %.4f ms  %.0f GB/s" % (name, ms, gbs or 0))
+    dom = "kda_seq_kernel"
+    dk = kernels[dom]
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": dk["TFLOP/s"], "peak": FP32_VALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": dk["mfma_fp32_frac"], "traffic": None,
+                "algorithmic_flops_per_launch": dk["flops_per_token_head"] * nth,
+                "hbm_GB/s_at_algorithmic_bytes": dk["GB/s"]}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        sl = lambda z: None if z is None else np.ascontiguousarray(z[:1])
+        reps, wall = 0, 0.0
+        while wall < args.cpu_seconds or reps == 0:
+            t0 = time.perf_counter()
+            oracle.kda_forward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["beta"]), sl(inp["r"]),
+                               sl(inp["alpha"]), eta=p["eta"], d_min=p["d_min"], d_max=p["d_max"],
+                               clamp=p["clamp"], eps=p["eps"], beta_aware=p["beta_aware"],
+                               q_scale=p["q_scale"], threads=min(H, oracle.default_threads()))
+            wall += time.perf_counter() - t0
+            reps += 1
+        cpu = {"value": reps * T / wall, "unit": "tokens/s", "cores": min(H, oracle.default_threads()),
+               "kind": "oracle",
+               "sample": "batch element 0 (%d tokens, all %d heads), fp64 oracle, one head per thread, "
+                         "%d run(s) in %.2f s" % (T, H, reps, wall)}
+    out = {
+        "metric": KDA_METRIC, "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": nsteps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": p["dtype"], "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": V,
+                   "apf": inp["r"] is not None, "seed": spec["seed"], "input_copies": len(sets)},
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
     }
     print(json.dumps(out), flush=True)
     return 0

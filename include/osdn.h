@@ -80,6 +80,11 @@ typedef enum {
  *               main text; K^-1/2 = the scaling used by the paper's listing).
  *   beta_aware  1: beta-aware feedback (Eq.(4)); 0: beta' = 1 in phase 1
  *               only (Appendix B); the memory write always uses beta.
+ *   r_per_key   0: r is [B,T,H], one retention per token and head (Eq.(7));
+ *               1: r is [B,T,H,K], the vector retention diag(r_t) of
+ *               Appendix A.5, Proposition A.3 (phase 1 then runs token by
+ *               token; osdn_fwd_varlen, osdn_decode and osdn_bwd return
+ *               OSDN_EUNSUPPORTED for it).  Ignored when r is NULL.
  */
 typedef struct osdn_desc {
   int64_t B, T, H, K, V;
@@ -90,10 +95,12 @@ typedef struct osdn_desc {
   float eps;
   float q_scale;
   int32_t beta_aware;
+  int32_t r_per_key;
 } osdn_desc;
 
 /* Fill *desc with the given sizes and the paper's defaults: chunk 64,
- * eta 0.003, box [0.5, 2], clamp on, eps 1e-6, q_scale 1, beta-aware, bf16. */
+ * eta 0.003, box [0.5, 2], clamp on, eps 1e-6, q_scale 1, beta-aware, bf16,
+ * one retention per token and head. */
 osdn_status osdn_desc_init(osdn_desc *desc, int64_t B, int64_t T, int64_t H,
                            int64_t K, int64_t V);
 
@@ -104,7 +111,8 @@ osdn_status osdn_validate(const osdn_desc *desc);
  * Phase 1, Algorithm 1 / Eq.(7) (Section 4.2, Section 4.4, Appendix B).
  *   k       [B,T,H,K] dtype    keys (read)
  *   beta    [B,T,H]   f32      write gates (read)
- *   r       [B,T,H]   f32      APF retention r_{t,h}, or NULL for r = 1
+ *   r       [B,T,H]   f32      APF retention r_{t,h} ([B,T,H,K] when
+ *                              desc->r_per_key), or NULL for r = 1
  *   d1      [B,H,K]   f32      initial preconditioner, or NULL for ones
  *   k_tilde [B,T,H,K] dtype    OUT: write keys d_t (.) k_t (rounded to dtype)
  *   d_out   [B,H,K]   f32      OUT: d_{T+1}, or NULL (may alias d1)
@@ -278,6 +286,45 @@ osdn_status osdn_bwd(const osdn_desc *desc, const void *q, const void *k,
                      void *dq, void *dk, void *dv, float *dbeta, float *dr,
                      float *dalpha, float *dd1, float *dS0, void *workspace,
                      size_t workspace_bytes, void *stream);
+
+/*
+ * OSKDA forward: online scaling on the Kimi Delta Attention backbone
+ * (Appendix B.2 and the online-scaled KDA row of Table 3).  Phase 1 is the
+ * preconditioner sweep of osdn_precond_scan (Eq.(12): beta-aware or not,
+ * optional retention r, clamp to the box); phase 2 keeps KDA's own K x V
+ * state and gates it per key channel.  Per (b,h), from S = S0 (zeros when
+ * NULL), S in R^{K x V}, for each token:
+ *     Sb  = Diag(alpha_t) S            (Sb = S when alpha is NULL)
+ *     u_t = v_t - Sb^T k_t             (residual read with the physical key)
+ *     S   = Sb + beta_t k~_t u_t^T     (preconditioned key on the storage side)
+ *     o_t = S^T (q_scale q_t)
+ * evaluated in 64-token chunks with the UT-transform form of Appendix B.2
+ * (desc->chunk is not used).
+ *   q, k    [B,T,H,K] dtype     queries, keys
+ *   v       [B,T,H,V] dtype     values
+ *   beta    [B,T,H]   f32       write gates
+ *   r       [B,T,H] (or [B,T,H,K] with desc->r_per_key) f32, or NULL
+ *   alpha   [B,T,H,K] f32       channel-wise decay in (0,1], or NULL (none)
+ *   d1      [B,H,K]   f32       initial preconditioner, or NULL for ones
+ *   S0      [B,H,K,V] f32       initial state (KDA layout), or NULL for zeros
+ *   o       [B,T,H,V] dtype     OUT: readouts
+ *   S_out   [B,H,K,V] f32       OUT: final state, or NULL (may alias S0)
+ *   d_out   [B,H,K]   f32       OUT: d_{T+1}, or NULL (may alias d1)
+ *   k_tilde_out [B,T,H,K] dtype OUT: write keys d_t (.) k_t, or NULL
+ *   workspace  >= osdn_kda_fwd_workspace_bytes(desc) bytes, 16-byte aligned,
+ *              required when T > 0: the write keys (for bf16 as the residual
+ *              (d_t - 1) (.) k_t, as in osdn_fwd), the phase-1 scratch and
+ *              about 128 KiB of fp32 chunk operands per (b,h) and 64 tokens.
+ * K, V <= 128 (OSDN_EUNSUPPORTED above).  Arithmetic is fp32 throughout;
+ * a channel whose decay over one chunk falls below e^-60 takes exact
+ * per-entry exponentials instead of the factorised products.
+ */
+size_t osdn_kda_fwd_workspace_bytes(const osdn_desc *desc);
+osdn_status osdn_kda_fwd(const osdn_desc *desc, const void *q, const void *k,
+                         const void *v, const float *beta, const float *r,
+                         const float *alpha, const float *d1, const float *S0,
+                         void *o, float *S_out, float *d_out, void *k_tilde_out,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Launch profile (measurement aid).  osdn_profile_begin records a HIP event on

@@ -20,7 +20,8 @@ import os
 import torch
 
 __all__ = ["precond_scan", "precond_scan_workspace_bytes", "scan_counters", "chunk_fwd",
-           "chunk_fwd_workspace_bytes", "fwd", "fwd_varlen", "decode", "DECODE_MAX_T", "bwd", "bwd_workspace_bytes", "kernel_times", "fwd_workspace_bytes", "fwd_scan_counters", "Desc", "OsdnError",
+           "chunk_fwd_workspace_bytes", "fwd", "fwd_varlen", "kda_fwd", "kda_fwd_workspace_bytes", "decode", "DECODE_MAX_T", "bwd",
+           "bwd_workspace_bytes", "kernel_times", "fwd_workspace_bytes", "fwd_scan_counters", "Desc", "OsdnError",
            "library_path", "load", "F32", "BF16"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -34,8 +35,9 @@ DECODE_MAX_T = 64  # OSDN_DECODE_MAX_T
 SYMBOLS = ("osdn_desc_init", "osdn_validate", "osdn_precond_scan",
            "osdn_precond_scan_workspace_bytes", "osdn_precond_scan_counters_offset",
            "osdn_chunk_fwd", "osdn_chunk_fwd_workspace_bytes", "osdn_fwd_workspace_bytes",
-           "osdn_fwd", "osdn_fwd_varlen", "osdn_decode", "osdn_bwd_workspace_bytes", "osdn_bwd", "osdn_profile_begin", "osdn_profile_end", "osdn_status_str",
-           "osdn_last_error", "osdn_version")
+           "osdn_fwd", "osdn_fwd_varlen", "osdn_decode", "osdn_bwd_workspace_bytes", "osdn_bwd",
+           "osdn_kda_fwd_workspace_bytes", "osdn_kda_fwd", "osdn_profile_begin", "osdn_profile_end",
+           "osdn_status_str", "osdn_last_error", "osdn_version")
 
 
 class OsdnError(RuntimeError):
@@ -50,7 +52,8 @@ class Desc(ctypes.Structure):
                 ("K", ctypes.c_int64), ("V", ctypes.c_int64), ("chunk", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("eta", ctypes.c_float), ("d_min", ctypes.c_float),
                 ("d_max", ctypes.c_float), ("clamp", ctypes.c_int32), ("eps", ctypes.c_float),
-                ("q_scale", ctypes.c_float), ("beta_aware", ctypes.c_int32)]
+                ("q_scale", ctypes.c_float), ("beta_aware", ctypes.c_int32),
+                ("r_per_key", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -89,6 +92,10 @@ def load():
     lib.osdn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.osdn_bwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp, vp, vp, fp, fp, fp,
                              fp, fp, vp, ctypes.c_size_t, vp]
+    lib.osdn_kda_fwd_workspace_bytes.argtypes = [dp]
+    lib.osdn_kda_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.osdn_kda_fwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp, vp,
+                                 ctypes.c_size_t, vp]
     lib.osdn_profile_begin.argtypes = [vp]
     lib.osdn_profile_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
                                      ci, ctypes.POINTER(ci)]
@@ -97,7 +104,8 @@ def load():
     lib.osdn_last_error.argtypes = []
     lib.osdn_last_error.restype = ctypes.c_char_p
     for name in ("osdn_desc_init", "osdn_validate", "osdn_precond_scan", "osdn_chunk_fwd",
-                 "osdn_fwd", "osdn_fwd_varlen", "osdn_decode", "osdn_bwd", "osdn_profile_begin",
+                 "osdn_fwd", "osdn_fwd_varlen", "osdn_decode", "osdn_bwd", "osdn_kda_fwd",
+                 "osdn_profile_begin",
                  "osdn_profile_end",
                  "osdn_version"):
         getattr(lib, name).restype = ci
@@ -118,14 +126,25 @@ def _check(status):
 
 
 def make_desc(B, T, H, K, V, *, dtype=BF16, chunk=64, eta=0.003, d_min=0.5, d_max=2.0,
-              clamp=True, eps=1e-6, q_scale=1.0, beta_aware=True) -> Desc:
+              clamp=True, eps=1e-6, q_scale=1.0, beta_aware=True, r_per_key=False) -> Desc:
     d = Desc()
     _check(load().osdn_desc_init(ctypes.byref(d), B, T, H, K, V))
     d.dtype, d.chunk = int(dtype), int(chunk)
     d.eta, d.d_min, d.d_max = float(eta), float(d_min), float(d_max)
     d.clamp, d.eps, d.q_scale = int(bool(clamp)), float(eps), float(q_scale)
     d.beta_aware = int(bool(beta_aware))
+    d.r_per_key = int(bool(r_per_key))
     return d
+
+
+def _need_r(r, B, T, H, K, dev):
+    """r is [B,T,H] (one retention per token and head) or [B,T,H,K] (vector
+    retention); returns whether it is the vector form."""
+    if r is not None and isinstance(r, torch.Tensor) and r.dim() == 4:
+        _need(r, "r", (B, T, H, K), torch.float32, dev)
+        return True
+    _need(r, "r", (B, T, H), torch.float32, dev)
+    return False
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -190,15 +209,16 @@ def scan_counters(workspace, B, T, H, K, dtype=BF16, offset=0):
 def precond_scan(k, beta, r=None, d1=None, *, eta=0.003, d_min=0.5, d_max=2.0,
                  clamp=True, eps=1e-6, beta_aware=True, k_tilde=None, d_out=None,
                  chunked=True, workspace=None):
-    """Phase 1.  k [B,T,H,K] (bf16/f32), beta and r [B,T,H] f32, d1 [B,H,K] f32.
-    chunked=True runs the chunked kernels in `workspace` (allocated when None),
-    chunked=False the token-by-token kernel.
+    """Phase 1.  k [B,T,H,K] (bf16/f32), beta [B,T,H] f32, r [B,T,H] or (vector
+    retention) [B,T,H,K] f32, d1 [B,H,K] f32.  chunked=True runs the chunked
+    kernels in `workspace` (allocated when None), chunked=False the
+    token-by-token kernel (which vector retention always takes).
     Returns (k_tilde [B,T,H,K] in k's dtype, d_out [B,H,K] f32)."""
     B, T, H, K = k.shape
     dev, f32 = k.device, torch.float32
     _need(k, "k", (B, T, H, K), k.dtype, dev)
     _need(beta, "beta", (B, T, H), f32, dev)
-    _need(r, "r", (B, T, H), f32, dev)
+    rvec = _need_r(r, B, T, H, K, dev)
     _need(d1, "d1", (B, H, K), f32, dev)
     if k_tilde is None:
         k_tilde = torch.empty_like(k)
@@ -207,7 +227,7 @@ def precond_scan(k, beta, r=None, d1=None, *, eta=0.003, d_min=0.5, d_max=2.0,
     _need(k_tilde, "k_tilde", (B, T, H, K), k.dtype, dev)
     _need(d_out, "d_out", (B, H, K), f32, dev)
     desc = make_desc(B, T, H, K, K, dtype=_dtype_code(k), eta=eta, d_min=d_min,
-                     d_max=d_max, clamp=clamp, eps=eps, beta_aware=beta_aware)
+                     d_max=d_max, clamp=clamp, eps=eps, beta_aware=beta_aware, r_per_key=rvec)
     if chunked:
         need = int(load().osdn_precond_scan_workspace_bytes(ctypes.byref(desc)))
         workspace = _workspace(workspace, need, dev)
@@ -279,7 +299,7 @@ def fwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, chunk=64, eta=0.
     _need(k, "k", (B, T, H, K), dt, dev)
     _need(v, "v", (B, T, H, V), dt, dev)
     _need(beta, "beta", (B, T, H), f32, dev)
-    _need(r, "r", (B, T, H), f32, dev)
+    rvec = _need_r(r, B, T, H, K, dev)
     _need(alpha, "alpha", (B, T, H), f32, dev)
     _need(d1, "d1", (B, H, K), f32, dev)
     _need(S0, "S0", (B, H, V, K), f32, dev)
@@ -291,7 +311,8 @@ def fwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, chunk=64, eta=0.
         d_out = torch.empty((B, H, K), dtype=f32, device=dev)
     _need(k_tilde_out, "k_tilde_out", (B, T, H, K), dt, dev)
     desc = make_desc(B, T, H, K, V, dtype=_dtype_code(q), chunk=chunk, eta=eta, d_min=d_min,
-                     d_max=d_max, clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware)
+                     d_max=d_max, clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware,
+                     r_per_key=rvec)
     need = int(load().osdn_fwd_workspace_bytes(ctypes.byref(desc)))
     workspace = _workspace(workspace, need, dev)
     _check(load().osdn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r),
@@ -299,6 +320,45 @@ def fwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, chunk=64, eta=0.
                            _ptr(k_tilde_out), _ptr(workspace),
                            ctypes.c_size_t(_nbytes(workspace)), _stream(dev)))
     return o, S_out, d_out
+
+
+def kda_fwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, eta=0.003, d_min=0.5,
+            d_max=2.0, clamp=True, eps=1e-6, q_scale=1.0, beta_aware=True, o=None, S_out=None,
+            d_out=None, k_tilde_out=None, workspace=None):
+    """OSKDA forward on the current stream: q, k [B,T,H,K], v [B,T,H,V], beta
+    [B,T,H], r [B,T,H] or [B,T,H,K], alpha [B,T,H,K] (channel-wise decay), d1
+    [B,H,K], S0 [B,H,K,V].  Returns (o [B,T,H,V], S_out [B,H,K,V], d_out)."""
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dev, dt, f32 = q.device, q.dtype, torch.float32
+    _need(k, "k", (B, T, H, K), dt, dev)
+    _need(v, "v", (B, T, H, V), dt, dev)
+    _need(beta, "beta", (B, T, H), f32, dev)
+    rvec = _need_r(r, B, T, H, K, dev)
+    _need(alpha, "alpha", (B, T, H, K), f32, dev)
+    _need(d1, "d1", (B, H, K), f32, dev)
+    _need(S0, "S0", (B, H, K, V), f32, dev)
+    if o is None:
+        o = torch.empty((B, T, H, V), dtype=dt, device=dev)
+    if S_out is None:
+        S_out = torch.empty((B, H, K, V), dtype=f32, device=dev)
+    if d_out is None:
+        d_out = torch.empty((B, H, K), dtype=f32, device=dev)
+    _need(k_tilde_out, "k_tilde_out", (B, T, H, K), dt, dev)
+    desc = make_desc(B, T, H, K, V, dtype=_dtype_code(q), eta=eta, d_min=d_min, d_max=d_max,
+                     clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware, r_per_key=rvec)
+    need = int(load().osdn_kda_fwd_workspace_bytes(ctypes.byref(desc)))
+    workspace = _workspace(workspace, need, dev)
+    _check(load().osdn_kda_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r),
+                               _ptr(alpha), _ptr(d1), _ptr(S0), _ptr(o), _ptr(S_out), _ptr(d_out),
+                               _ptr(k_tilde_out), _ptr(workspace),
+                               ctypes.c_size_t(_nbytes(workspace)), _stream(dev)))
+    return o, S_out, d_out
+
+
+def kda_fwd_workspace_bytes(B, T, H, K, V, dtype=BF16) -> int:
+    desc = make_desc(B, T, H, K, V, dtype=dtype)
+    return int(load().osdn_kda_fwd_workspace_bytes(ctypes.byref(desc)))
 
 
 def fwd_varlen(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, cu_seqlens,
@@ -322,7 +382,7 @@ def fwd_varlen(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, cu_seqlen
     _need(k, "k", (1, total, H, K), dt, dev)
     _need(v, "v", (1, total, H, V), dt, dev)
     _need(beta, "beta", (1, total, H), f32, dev)
-    _need(r, "r", (1, total, H), f32, dev)
+    rvec = _need_r(r, 1, total, H, K, dev)
     _need(alpha, "alpha", (1, total, H), f32, dev)
     _need(d1, "d1", (S, H, K), f32, dev)
     _need(S0, "S0", (S, H, V, K), f32, dev)
@@ -335,7 +395,7 @@ def fwd_varlen(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, cu_seqlen
     _need(k_tilde_out, "k_tilde_out", (1, total, H, K), dt, dev)
     desc = make_desc(S, max_seqlen, H, K, V, dtype=_dtype_code(q), chunk=chunk, eta=eta,
                      d_min=d_min, d_max=d_max, clamp=clamp, eps=eps, q_scale=q_scale,
-                     beta_aware=beta_aware)
+                     beta_aware=beta_aware, r_per_key=rvec)
     need = int(load().osdn_fwd_workspace_bytes(ctypes.byref(desc)))
     workspace = _workspace(workspace, need, dev)
     _check(load().osdn_fwd_varlen(ctypes.byref(desc), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
@@ -358,7 +418,7 @@ def decode(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, eta=0.003, d_
     _need(k, "k", (B, T, H, K), dt, dev)
     _need(v, "v", (B, T, H, V), dt, dev)
     _need(beta, "beta", (B, T, H), f32, dev)
-    _need(r, "r", (B, T, H), f32, dev)
+    rvec = _need_r(r, B, T, H, K, dev)
     _need(alpha, "alpha", (B, T, H), f32, dev)
     _need(d1, "d1", (B, H, K), f32, dev)
     _need(S0, "S0", (B, H, V, K), f32, dev)
@@ -372,7 +432,7 @@ def decode(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, eta=0.003, d_
     _need(S_out, "S_out", (B, H, V, K), f32, dev)
     _need(d_out, "d_out", (B, H, K), f32, dev)
     desc = make_desc(B, T, H, K, V, dtype=_dtype_code(q), eta=eta, d_min=d_min, d_max=d_max,
-                     clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware)
+                     clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware, r_per_key=rvec)
     _check(load().osdn_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r),
                               _ptr(alpha), _ptr(d1), _ptr(S0), _ptr(o), _ptr(S_out), _ptr(d_out),
                               _stream(dev)))
@@ -398,7 +458,7 @@ def bwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, dout, dS=None, d
     _need(k, "k", (B, T, H, K), dt, dev)
     _need(v, "v", (B, T, H, V), dt, dev)
     _need(beta, "beta", (B, T, H), f32, dev)
-    _need(r, "r", (B, T, H), f32, dev)
+    rvec = _need_r(r, B, T, H, K, dev)
     _need(alpha, "alpha", (B, T, H), f32, dev)
     _need(d1, "d1", (B, H, K), f32, dev)
     _need(S0, "S0", (B, H, V, K), f32, dev)
@@ -412,7 +472,7 @@ def bwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, dout, dS=None, d
            "dd1": torch.empty((B, H, K), dtype=f32, device=dev),
            "dS0": torch.empty((B, H, V, K), dtype=f32, device=dev)}
     desc = make_desc(B, T, H, K, V, dtype=_dtype_code(q), eta=eta, d_min=d_min, d_max=d_max,
-                     clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware)
+                     clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware, r_per_key=rvec)
     need = int(load().osdn_bwd_workspace_bytes(ctypes.byref(desc)))
     workspace = _workspace(workspace, need, dev)
     _check(load().osdn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r),

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libosdn.so")
 
 SOURCES = ["precond_scan.hip", "precond_chunked.hip", "chunk_generic.hip", "chunk_mfma.hip",
-           "chunk_wy.hip", "decode.hip", "backward.hip", "osdn_api.cpp"]
+           "chunk_wy.hip", "decode.hip", "backward.hip", "kda_chunk.hip", "osdn_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,497 @@
+// Phase 2 of OSKDA (Kimi Delta Attention with online scaling): the chunkwise
+// form of the paper's Appendix B.2, in fp32 arithmetic on the matrix cores.
+//
+// KDA keeps its state as S in R^{K x V} and gates it per key channel:
+//   Sb = Diag(alpha_t) S,  u_t = v_t - Sb^T k_t,  S = Sb + beta_t k~_t u_t^T,
+//   o_t = S^T (q_scale q_t)                       (Table 3, online-scaled KDA)
+// Per chunk of L <= 64 tokens with boundary state S, Gamma_i = prod_{l<=i}
+// alpha_l (per channel), gamma_C = Gamma_L:
+//   A_ij = 1[j<i] beta_i <Gamma_i . k_i, k~_j / Gamma_j>
+//   D    = (I + A)^-1 diag(beta) (V - (Gamma . K) S)       (= U - W S)
+//   O    = (Gamma . Q) S + tril((Gamma . Q)(K~ / Gamma)^T) D
+//   S'   = Diag(gamma_C) S + ((gamma_C / Gamma) . K~)^T D
+//
+// Two kernels:
+//  * kda_intra_kernel, one workgroup per 64-token chunk (chunk-parallel):
+//    G = cumulative log decay, the scaled operands Gamma . K, Gamma . Q and
+//    (gamma_C / Gamma) . K~ (every factor <= 1), the Gram A and the scores M,
+//    and TB = (I + A)^-1 diag(beta) by blocked substitution.  When every
+//    channel keeps G >= -60 over the chunk the Gram and scores are products
+//    of Gamma . K (or Gamma . Q) with K~ . e^{-G} (factors at most e^60) on
+//    the matrix cores; otherwise each entry takes its own exponentials
+//    e^{G_i - G_j} <= 1, so no decay can overflow or lose the product.
+//    Everything is written to the workspace in the order the sweep's MFMA
+//    operands are read, fp32.
+//  * kda_seq_kernel, one workgroup per (b,h) and 32 value columns, sweeps the
+//    chunks in order with the state tile (128 x 32 fp32) in registers and LDS.
+//
+// MFMA v_mfma_f32_16x16x4_f32 for lane l: A[m = l & 15][k = l >> 4],
+// B[k = l >> 4][n = l & 15], D[m = 4 (l >> 4) + i][n = l & 15], i < 4.  A
+// product over a contraction of length 4 S runs S steps, step s taking
+// contraction index 4 s + (l >> 4); the workspace stores each A-operand row
+// permuted so that a lane's S values are contiguous.
+#include <math.h>
+
+#include "device_common.h"
+#include "kernels.h"
+#include "profile.h"
+
+namespace osdn {
+namespace {
+
+constexpr int KC = 64;     // chunk length
+constexpr int KP = 128;    // key channels (zero-padded)
+constexpr int KVT = 32;    // value columns per sweep workgroup
+constexpr int LP = 132;    // LDS pitch of the intra kernel's [64][128] tiles
+constexpr int AP = 65;     // LDS pitch of its [64][64] tiles
+constexpr int SP = 48;     // LDS pitch of the sweep's [rows][32] tiles
+constexpr float G_SAFE = -60.0f;
+
+__device__ __forceinline__ floatx4 mfma_f32(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// token row of chunk n, channel c, with zeros past the chunk's end or K
+template <typename TIn>
+__device__ __forceinline__ float ld_tok(const TIn *p, int64_t row_off, int c, int K, bool ok) {
+  return ok && c < K ? to_f32(p[row_off + c]) : 0.0f;
+}
+
+template <typename TIn, bool RES, bool GATED>
+__global__ __launch_bounds__(256) void kda_intra_kernel(KdaArgs a, int64_t N) {
+  extern __shared__ float sm[];
+  float *sK = sm, *sKt = sK + KC * LP, *sQ = sKt + KC * LP, *sG = sQ + KC * LP;
+  __shared__ float sBeta[KC], sGL[KP];
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, l16 = l & 15, g = l >> 4;
+  const int64_t bh = blockIdx.x / N, n = blockIdx.x - bh * N;
+  const int64_t H = a.H, T = a.T;
+  const int K = (int)a.K;
+  const int64_t b = bh / H, h = bh - b * H;
+  const int64_t t0 = n * KC;
+  const int L = (int)(T - t0 < KC ? T - t0 : KC);
+  const TIn *kp = static_cast<const TIn *>(a.k);
+  const TIn *qp = static_cast<const TIn *>(a.q);
+  const TIn *ktp = static_cast<const TIn *>(a.kt);
+
+  // ---- load the chunk: k, k~, q_scale q, log alpha (zero rows past L,
+  //      zero channels past K)
+  for (int e = tid; e < KC * KP; e += 256) {
+    const int row = e >> 7, c = e & (KP - 1);
+    const bool ok = row < L;
+    const int64_t off = ((b * T + t0 + (ok ? row : 0)) * H + h) * (int64_t)K;
+    const float kv = ld_tok(kp, off, c, K, ok);
+    float kt;
+    if constexpr (RES) {
+      kt = kv + (ok && c < K ? to_f32(static_cast<const bf16 *>(a.kt)[off + c]) : 0.0f);
+    } else {
+      kt = ld_tok(ktp, off, c, K, ok);
+    }
+    sK[row * LP + c] = kv;
+    sKt[row * LP + c] = kt;
+    sQ[row * LP + c] = a.q_scale * ld_tok(qp, off, c, K, ok);
+    float la = 0.0f;
+    if (GATED && ok && c < K) la = logf(a.alpha[off + c]);
+    sG[row * LP + c] = la;
+  }
+  if (tid < KC) sBeta[tid] = tid < L ? a.beta[(b * T + t0 + tid) * H + h] : 0.0f;
+  __syncthreads();
+  // ---- G = in-chunk cumulative log decay, per channel
+  int unsafe = 0;
+  if (tid < KP) {
+    float acc = 0.0f;
+    for (int row = 0; row < KC; ++row) {
+      acc += sG[row * LP + tid];
+      sG[row * LP + tid] = acc;
+    }
+    sGL[tid] = acc;  // G at the chunk's last token (rows past L add log 1)
+    unsafe = acc < G_SAFE;
+  }
+  unsafe = __syncthreads_or(unsafe);
+
+  float *sA = sG, *sM = sG + KC * AP;  // reuse G's space once it is dead
+  const int64_t cbase = bh * N + n;
+  float *kh = a.kh + cbase * (KC * KP), *qh = a.qh + cbase * (KC * KP), *kc = a.kc + cbase * (KC * KP);
+  float *tb = a.tb + cbase * (KC * KC), *mq = a.mq + cbase * (KC * KC);
+
+  if (!unsafe) {
+    // ---- scaled operands in place: k e^G, q e^G (<= 1 factors), k~ e^-G
+    for (int e = tid; e < KC * KP; e += 256) {
+      const int row = e >> 7, c = e & (KP - 1);
+      const float gg = sG[row * LP + c];
+      const float eg = expf(gg);
+      sK[row * LP + c] *= eg;
+      sQ[row * LP + c] *= eg;
+      sKt[row * LP + c] *= expf(-gg);
+    }
+    __syncthreads();
+    // outputs of the scaled operands (k~ e^{G_L - G} = (k~ e^-G) e^{G_L})
+    for (int e = tid; e < KC * KP; e += 256) {
+      const int row = e >> 7, p = e & (KP - 1), c = 4 * (p & 31) + (p >> 5);
+      kh[e] = sK[row * LP + c];
+      qh[e] = sQ[row * LP + c];
+      const int kr = e >> 6, q = e & 63, j = 4 * (q & 15) + (q >> 4);
+      kc[e] = sKt[j * LP + kr] * expf(sGL[kr]);
+    }
+    // ---- A and M on the matrix cores, lower 16x16 blocks (I >= J)
+    for (int e = tid; e < KC * KC; e += 256) {  // upper blocks are zero
+      const int i = e >> 6, j = e & 63;
+      if ((j >> 4) > (i >> 4)) {
+        sA[i * AP + j] = 0.0f;
+        sM[i * AP + j] = 0.0f;
+      }
+    }
+    for (int task = w; task < 10; task += 4) {
+      const int I = task < 1 ? 0 : task < 3 ? 1 : task < 6 ? 2 : 3;
+      const int J = task - I * (I + 1) / 2;
+      floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
+      const float *ak = sK + (16 * I + l16) * LP + g, *aq = sQ + (16 * I + l16) * LP + g;
+      const float *bk = sKt + (16 * J + l16) * LP + g;
+#pragma unroll 8
+      for (int s = 0; s < KP / 4; ++s) {
+        const float bb = bk[4 * s];
+        accA = mfma_f32(ak[4 * s], bb, accA);
+        accM = mfma_f32(aq[4 * s], bb, accM);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * g + r, j = 16 * J + l16;
+        sA[i * AP + j] = j < i ? sBeta[i] * accA[r] : 0.0f;
+        sM[i * AP + j] = j <= i ? accM[r] : 0.0f;
+      }
+    }
+  } else {
+    // ---- exact path: every entry with its own e^{G_i - G_j} <= 1
+    float va[9], vm[9];
+#pragma unroll
+    for (int u = 0; u < 9; ++u) {
+      const int p = tid + 256 * u;
+      va[u] = vm[u] = 0.0f;
+      if (p < KC * (KC + 1) / 2) {
+        int i = (int)((sqrtf(8.0f * p + 1.0f) - 1.0f) * 0.5f);
+        while (i * (i + 1) / 2 > p) --i;
+        while ((i + 1) * (i + 2) / 2 <= p) ++i;
+        const int j = p - i * (i + 1) / 2;
+        float sa = 0.0f, smq = 0.0f;
+        for (int c = 0; c < KP; ++c) {
+          const float f = __expf(sG[i * LP + c] - sG[j * LP + c]) * sKt[j * LP + c];
+          sa = fmaf(sK[i * LP + c], f, sa);
+          smq = fmaf(sQ[i * LP + c], f, smq);
+        }
+        va[u] = j < i ? sBeta[i] * sa : 0.0f;
+        vm[u] = smq;
+      }
+    }
+    for (int e = tid; e < KC * KP; e += 256) {
+      const int row = e >> 7, p = e & (KP - 1), c = 4 * (p & 31) + (p >> 5);
+      const float eg = expf(sG[row * LP + c]);
+      kh[e] = sK[row * LP + c] * eg;
+      qh[e] = sQ[row * LP + c] * eg;
+      const int kr = e >> 6, q = e & 63, j = 4 * (q & 15) + (q >> 4);
+      kc[e] = sKt[j * LP + kr] * expf(sGL[kr] - sG[j * LP + kr]);
+    }
+    __syncthreads();  // G is dead: its space takes A and M
+    for (int e = tid; e < KC * KC; e += 256) {
+      const int i = e >> 6, j = e & 63;
+      if (j > i) {
+        sA[i * AP + j] = 0.0f;
+        sM[i * AP + j] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 9; ++u) {
+      const int p = tid + 256 * u;
+      if (p < KC * (KC + 1) / 2) {
+        int i = (int)((sqrtf(8.0f * p + 1.0f) - 1.0f) * 0.5f);
+        while (i * (i + 1) / 2 > p) --i;
+        while ((i + 1) * (i + 2) / 2 <= p) ++i;
+        const int j = p - i * (i + 1) / 2;
+        sA[i * AP + j] = va[u];
+        sM[i * AP + j] = vm[u];
+      }
+    }
+  }
+  if (tid < KP) a.gc[cbase * KP + tid] = expf(sGL[tid]);
+  __syncthreads();
+
+  // ---- T = (I + A)^-1 (unit lower triangular), 16x16 blocks.  sT takes K's
+  //      space, sY (block-row partial products) takes Q's.
+  float *sT = sK, *sY = sQ;
+  for (int e = tid; e < KC * KC; e += 256) sT[(e >> 6) * AP + (e & 63)] = 0.0f;
+  __syncthreads();
+  if (tid < KC) {
+    // diagonal blocks by forward substitution, one column per thread
+    const int I = tid >> 4, m = tid & 15, c0 = 16 * I;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float acc = i == m ? 1.0f : 0.0f;
+#pragma unroll
+      for (int j = 0; j < i; ++j) acc -= sA[(c0 + i) * AP + c0 + j] * x[j];
+      x[i] = i < m ? 0.0f : acc;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sT[(c0 + i) * AP + c0 + m] = x[i];
+  }
+  __syncthreads();
+  for (int I = 1; I < 4; ++I) {
+    // Y = A[I, 0:16I] T[0:16I, 0:16I], then T[I, 0:16I] = -T_II Y
+    for (int e = tid; e < 16 * 16 * I; e += 256) {
+      const int i = 16 * I + e / (16 * I), j = e % (16 * I);
+      float acc = 0.0f;
+      for (int m = j; m < 16 * I; ++m) acc = fmaf(sA[i * AP + m], sT[m * AP + j], acc);
+      sY[i * AP + j] = acc;
+    }
+    __syncthreads();
+    for (int e = tid; e < 16 * 16 * I; e += 256) {
+      const int i = 16 * I + e / (16 * I), j = e % (16 * I);
+      float acc = 0.0f;
+      for (int m = 16 * I; m <= i; ++m) acc = fmaf(sT[i * AP + m], sY[m * AP + j], acc);
+      sT[i * AP + j] = -acc;
+    }
+    __syncthreads();
+  }
+  // ---- TB = T diag(beta) and M, rows permuted for the sweep's A operands
+  for (int e = tid; e < KC * KC; e += 256) {
+    const int i = e >> 6, q = e & 63, j = 4 * (q & 15) + (q >> 4);
+    tb[e] = sT[i * AP + j] * sBeta[j];
+    mq[e] = sM[i * AP + j];
+  }
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(256) void kda_seq_kernel(KdaArgs a, int64_t N, int ntile) {
+  __shared__ float sS[KP * SP];
+  __shared__ float sX[KC * SP];
+  __shared__ float sD[KC * SP];
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, l16 = l & 15, g = l >> 4;
+  const int64_t H = a.H, T = a.T, V = a.V, BH = a.B * a.H;
+  const int K = (int)a.K;
+  // the value tiles of one (b,h) land on one XCD (workgroups are dealt to
+  // the 8 XCDs in turn), so they share its L2 for the chunk operands
+  const int64_t bid = blockIdx.x;
+  int64_t bh, vt;
+  if (BH % 8 == 0) {
+    const int64_t slot = bid >> 3;
+    bh = (slot / ntile) * 8 + (bid & 7);
+    vt = slot % ntile;
+  } else {
+    bh = bid / ntile;
+    vt = bid % ntile;
+  }
+  const int64_t b = bh / H, h = bh - b * H;
+  const int64_t v0 = vt * KVT;
+  const TIn *vp = static_cast<const TIn *>(a.v);
+  TIn *op = static_cast<TIn *>(a.o);
+
+  // state tile: wave w holds key rows 32 w .. 32 w + 31 (two 16-row blocks)
+  // for both 16-column blocks, in the MFMA result layout
+  floatx4 Sr[2][2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kr = 32 * w + 16 * rb + 4 * g + i;
+        const int64_t col = v0 + 16 * cb + l16;
+        float x = 0.0f;
+        if (a.S0 && kr < K && col < V) x = a.S0[(bh * K + kr) * V + col];
+        Sr[rb][cb][i] = x;
+        sS[kr * SP + 16 * cb + l16] = x;
+      }
+
+  for (int64_t n = 0; n < N; ++n) {
+    const int64_t t0 = n * KC;
+    const int L = (int)(T - t0 < KC ? T - t0 : KC);
+    const int64_t cbase = bh * N + n;
+    // this chunk's operands (all loads issued up front)
+    float ka[32], qa[32], ta[16], ma[16], kca[2][16], gcv[2][4];
+    {
+      const floatx4 *pk = reinterpret_cast<const floatx4 *>(a.kh + cbase * (KC * KP) + (16 * w + l16) * KP + 32 * g);
+      const floatx4 *pq = reinterpret_cast<const floatx4 *>(a.qh + cbase * (KC * KP) + (16 * w + l16) * KP + 32 * g);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const floatx4 x = pk[u], y = pq[u];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ka[4 * u + e] = -x[e];  // X = V - K S: the product enters negated
+          qa[4 * u + e] = y[e];
+        }
+      }
+      const floatx4 *pt = reinterpret_cast<const floatx4 *>(a.tb + cbase * (KC * KC) + (16 * w + l16) * KC + 16 * g);
+      const floatx4 *pm = reinterpret_cast<const floatx4 *>(a.mq + cbase * (KC * KC) + (16 * w + l16) * KC + 16 * g);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const floatx4 x = pt[u], y = pm[u];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ta[4 * u + e] = x[e];
+          ma[4 * u + e] = y[e];
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const floatx4 *pc = reinterpret_cast<const floatx4 *>(a.kc + cbase * (KC * KP) +
+                                                              (32 * w + 16 * rb + l16) * KC + 16 * g);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const floatx4 x = pc[u];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kca[rb][4 * u + e] = x[e];
+        }
+        const floatx4 x = *reinterpret_cast<const floatx4 *>(a.gc + cbase * KP + 32 * w + 16 * rb + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gcv[rb][e] = x[e];
+      }
+    }
+    floatx4 accX[2], accP[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * w + 4 * g + i;
+        const int64_t col = v0 + 16 * cb + l16;
+        float x = 0.0f;
+        if (row < L && col < V) x = to_f32(vp[((b * T + t0 + row) * H + h) * V + col]);
+        accX[cb][i] = x;
+        accP[cb][i] = 0.0f;
+      }
+    __syncthreads();  // sS holds the chunk's boundary state
+    // (a) X = V - (Gamma . K) S and P = (Gamma . Q) S, rows 16 w ..
+#pragma unroll
+    for (int s = 0; s < KP / 4; ++s) {
+      const float b0 = sS[(4 * s + g) * SP + l16], b1 = sS[(4 * s + g) * SP + 16 + l16];
+      accX[0] = mfma_f32(ka[s], b0, accX[0]);
+      accX[1] = mfma_f32(ka[s], b1, accX[1]);
+      accP[0] = mfma_f32(qa[s], b0, accP[0]);
+      accP[1] = mfma_f32(qa[s], b1, accP[1]);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sX[(16 * w + 4 * g + i) * SP + 16 * cb + l16] = accX[cb][i];
+    __syncthreads();
+    // (b) D = TB X (TB lower triangular: contraction up to row 16 w + 15)
+    floatx4 accD[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      if (s < 4 * w + 4) {
+        const float b0 = sX[(4 * s + g) * SP + l16], b1 = sX[(4 * s + g) * SP + 16 + l16];
+        accD[0] = mfma_f32(ta[s], b0, accD[0]);
+        accD[1] = mfma_f32(ta[s], b1, accD[1]);
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sD[(16 * w + 4 * g + i) * SP + 16 * cb + l16] = accD[cb][i];
+    __syncthreads();
+    // (c) O = P + M D
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      if (s < 4 * w + 4) {
+        const float b0 = sD[(4 * s + g) * SP + l16], b1 = sD[(4 * s + g) * SP + 16 + l16];
+        accP[0] = mfma_f32(ma[s], b0, accP[0]);
+        accP[1] = mfma_f32(ma[s], b1, accP[1]);
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * w + 4 * g + i;
+        const int64_t col = v0 + 16 * cb + l16;
+        if (row < L && col < V) op[((b * T + t0 + row) * H + h) * V + col] = from_f32<TIn>(accP[cb][i]);
+      }
+    // (d) S = Diag(gamma_C) S + Kc^T D for this wave's key rows
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Sr[rb][cb][i] *= gcv[rb][i];
+#pragma unroll
+        for (int s = 0; s < 16; ++s)
+          Sr[rb][cb] = mfma_f32(kca[rb][s], sD[(4 * s + g) * SP + 16 * cb + l16], Sr[rb][cb]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sS[(32 * w + 16 * rb + 4 * g + i) * SP + 16 * cb + l16] = Sr[rb][cb][i];
+      }
+  }
+  if (a.S_out) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kr = 32 * w + 16 * rb + 4 * g + i;
+          const int64_t col = v0 + 16 * cb + l16;
+          if (kr < K && col < V) a.S_out[(bh * K + kr) * V + col] = Sr[rb][cb][i];
+        }
+  }
+}
+
+constexpr size_t INTRA_LDS = (size_t)4 * KC * LP * sizeof(float);
+
+template <typename TIn, bool RES>
+hipError_t launch_intra(const KdaArgs &a, int64_t N, hipStream_t s) {
+  dim3 grid((unsigned)(a.B * a.H * N)), block(256);
+  if (a.alpha) {
+    auto kern = kda_intra_kernel<TIn, RES, true>;
+    hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)INTRA_LDS);
+    hipLaunchKernelGGL(kern, grid, block, INTRA_LDS, s, a, N);
+  } else {
+    auto kern = kda_intra_kernel<TIn, RES, false>;
+    hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)INTRA_LDS);
+    hipLaunchKernelGGL(kern, grid, block, INTRA_LDS, s, a, N);
+  }
+  prof_mark(s, "kda_intra_kernel");
+  return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t launch_typed(const KdaArgs &a, hipStream_t s) {
+  const int64_t N = (a.T + KC - 1) / KC;
+  if (N > 0) {
+    hipError_t e = a.kt_is_res ? launch_intra<TIn, true>(a, N, s) : launch_intra<TIn, false>(a, N, s);
+    if (e != hipSuccess) return e;
+  }
+  const int ntile = (int)((a.V + KVT - 1) / KVT);
+  dim3 grid((unsigned)(a.B * a.H * ntile)), block(256);
+  hipLaunchKernelGGL((kda_seq_kernel<TIn>), grid, block, 0, s, a, N, ntile);
+  prof_mark(s, "kda_seq_kernel");
+  return hipGetLastError();
+}
+
+inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+size_t kda_work_bytes(int64_t B, int64_t T, int64_t H) {
+  const size_t nc = (size_t)(B * H) * (size_t)((T + KC - 1) / KC);
+  return 3 * al256(nc * KC * KP * sizeof(float)) + 2 * al256(nc * KC * KC * sizeof(float)) +
+         al256(nc * KP * sizeof(float));
+}
+
+void kda_work_layout(KdaArgs &a, void *base) {
+  const size_t nc = (size_t)(a.B * a.H) * (size_t)((a.T + KC - 1) / KC);
+  char *p = static_cast<char *>(base);
+  a.kh = reinterpret_cast<float *>(p);
+  p += al256(nc * KC * KP * sizeof(float));
+  a.qh = reinterpret_cast<float *>(p);
+  p += al256(nc * KC * KP * sizeof(float));
+  a.kc = reinterpret_cast<float *>(p);
+  p += al256(nc * KC * KP * sizeof(float));
+  a.tb = reinterpret_cast<float *>(p);
+  p += al256(nc * KC * KC * sizeof(float));
+  a.mq = reinterpret_cast<float *>(p);
+  p += al256(nc * KC * KC * sizeof(float));
+  a.gc = reinterpret_cast<float *>(p);
+}
+
+hipError_t launch_kda(const KdaArgs &a, bool is_bf16, hipStream_t s) {
+  if (a.B * a.H == 0) return hipSuccess;
+  return is_bf16 ? launch_typed<bf16>(a, s) : launch_typed<float>(a, s);
+}
+
+}  // namespace osdn

@@ -27,7 +27,7 @@ __device__ __forceinline__ int64_t seq_len(const A &a, int64_t b) {
 struct ScanArgs {
   const void *k;        // [B,T,H,K]
   const float *beta;    // [B,T,H]
-  const float *r;       // [B,T,H] or null
+  const float *r;       // [B,T,H], [B,T,H,K] when r_per_key, or null
   const float *d1;      // [B,H,K] or null
   void *k_tilde;        // [B,T,H,K] or null: write keys d (.) k
   void *kt_res;         // [B,T,H,K] bf16 or null: write-key residual (d - 1) (.) k
@@ -36,6 +36,7 @@ struct ScanArgs {
   float eta, d_min, d_max, eps;
   int clamp, beta_aware;
   const int64_t *cu = nullptr;  // variable-length sequences (see seq_base)
+  int r_per_key = 0;            // vector retention: token-by-token kernel only
 };
 
 struct ChunkArgs {
@@ -136,6 +137,29 @@ struct BwdArgs {
 size_t bwd_work_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V);
 void bwd_work_layout(BwdArgs &a, void *base);
 hipError_t launch_bwd(const BwdArgs &a, bool bf16, hipStream_t s);
+
+// OSKDA phase 2 (K x V state, channel-wise decay; K, V <= 128): a
+// chunk-parallel kernel forms each 64-token chunk's operands, a sweep kernel
+// carries the state (one workgroup per (b,h) and 32 value columns).
+struct KdaArgs {
+  const void *q, *k, *kt, *v;  // [B,T,H,K] / [B,T,H,V]
+  bool kt_is_res;              // kt holds the bf16 residual (d - 1) (.) k, so k~ = k + kt
+  const float *beta;           // [B,T,H]
+  const float *alpha;          // [B,T,H,K] channel-wise decay, or null
+  const float *S0;             // [B,H,K,V] or null
+  void *o;                     // [B,T,H,V]
+  float *S_out;                // [B,H,K,V] or null
+  int64_t B, T, H, K, V;
+  float q_scale;
+  // workspace regions (kda_work_layout), per (b,h) and chunk n < N = ceil(T/64):
+  float *kh, *qh;  // [B,H,N,64,128] Gamma . k and Gamma . q_scale q, rows permuted for MFMA
+  float *kc;       // [B,H,N,128,64] ((gamma_C / Gamma) . k~)^T, rows permuted
+  float *tb, *mq;  // [B,H,N,64,64] (I + A)^-1 diag(beta) and the intra-chunk scores
+  float *gc;       // [B,H,N,128] gamma_C
+};
+size_t kda_work_bytes(int64_t B, int64_t T, int64_t H);
+void kda_work_layout(KdaArgs &a, void *base);
+hipError_t launch_kda(const KdaArgs &a, bool bf16, hipStream_t s);
 
 // Shape coverage of the specialised MFMA path (bf16, K = V = 128, C = 64).
 bool chunk_mfma_supported(const ChunkArgs &a, bool bf16);

@@ -85,6 +85,8 @@ osdn_status validate(const osdn_desc *d, int phase) {
         return fail(OSDN_EINVAL, "box needs finite 0 < d_min <= d_max (got [%g, %g])", d->d_min, d->d_max);
     }
     if (d->K > 256) return fail(OSDN_EUNSUPPORTED, "phase 1 supports K <= 256 (got %lld)", (long long)d->K);
+    if (d->r_per_key != 0 && d->r_per_key != 1)
+      return fail(OSDN_EINVAL, "r_per_key must be 0 or 1 (got %d)", d->r_per_key);
   }
   if (phase & 2) {
     if (d->chunk < 1) return fail(OSDN_EINVAL, "chunk must be >= 1 (got %d)", d->chunk);
@@ -124,6 +126,7 @@ osdn::ScanArgs scan_args(const osdn_desc *d, const void *k, const float *beta, c
   a.eps = d->eps;
   a.clamp = d->clamp ? 1 : 0;
   a.beta_aware = d->beta_aware ? 1 : 0;
+  a.r_per_key = d->r_per_key;
   return a;
 }
 
@@ -279,7 +282,7 @@ osdn_status osdn_precond_scan(const osdn_desc *d, const void *k, const float *be
   if (k_tilde && k_tilde == k) return fail(OSDN_EINVAL, "k_tilde must not alias k");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const osdn::ScanArgs sa = scan_args(d, k, beta, r, d1, k_tilde, d_out);
-  if (!workspace) {
+  if (!workspace || (d->r_per_key && r)) {
     OSDN_TRY(run_scan(d, sa, s));
     return ok();
   }
@@ -322,6 +325,14 @@ osdn_status osdn_chunk_fwd(const osdn_desc *d, const void *q, const void *k, con
   return ok();
 }
 
+// bf16 write keys cross between the phases as the bf16 residual (d - 1) (.) k
+// when the box keeps d >= 1/2: its relative error on k~ is 2^-9 |d - 1| / d,
+// at most bf16's own.  Without that bound (no clamp, or d_min < 1/2) d can
+// approach 0 and the residual would cancel, so k~ itself travels in bf16.
+static bool keys_as_residual(const osdn_desc *d) {
+  return d->dtype == OSDN_BF16 && d->clamp && d->d_min >= 0.5f;
+}
+
 static size_t fwd_keys_bytes(const osdn_desc *d) {
   const size_t n = (size_t)d->B * (size_t)d->T * (size_t)d->H * (size_t)d->K * elem_bytes(d->dtype);
   return (n + 255) & ~(size_t)255;
@@ -350,6 +361,8 @@ static osdn_status fwd_impl(const osdn_desc *d, const int64_t *cu, const void *q
   OSDN_TRY(check_ptr(S_out, "S_out", false));
   OSDN_TRY(check_ptr(d_out, "d_out", false));
   OSDN_TRY(check_ptr(k_tilde_out, "k_tilde_out", false));
+  const bool rvec = d->r_per_key && r;
+  if (rvec && cu) return fail(OSDN_EUNSUPPORTED, "vector retention is not supported for packed sequences");
   hipStream_t s = static_cast<hipStream_t>(stream);
   osdn::ScanArgs sa = scan_args(d, k, beta, r, d1, k_tilde_out, d_out);
   osdn::ChunkArgs ca = chunk_args(d, q, k, k_tilde_out, v, beta, alpha, S0, o, S_out);
@@ -365,7 +378,8 @@ static osdn_status fwd_impl(const osdn_desc *d, const int64_t *cu, const void *q
   if (workspace_bytes < need)
     return fail(OSDN_EINVAL, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
   char *ws = static_cast<char *>(workspace);
-  if (d->dtype == OSDN_BF16) {
+  const bool res = keys_as_residual(d);
+  if (res) {
     // bf16: the write keys travel between the phases as the bf16 residual
     // (d - 1) (.) k, which with k gives k~ to ~16 bits
     sa.kt_res = ws;
@@ -380,9 +394,12 @@ static osdn_status fwd_impl(const osdn_desc *d, const int64_t *cu, const void *q
   void *cw = chunk_work_bytes(d) ? ws + fwd_keys_bytes(d) + scan_bytes : nullptr;
   // bf16 on the matrix cores without k_tilde_out: the residual is formed by
   // the first phase-2 kernel, which replays d itself (one pass over k fewer)
-  const bool fold = d->dtype == OSDN_BF16 && cw && !k_tilde_out;
-  OSDN_TRY(hip_status(osdn::launch_precond_scan_chunked(sa, sw, d->dtype == OSDN_BF16, s, !fold),
-                      "phase-1 launch"));
+  const bool fold = res && cw && !k_tilde_out && !rvec;
+  if (rvec)  // vector retention: the token-by-token sweep writes the keys
+    OSDN_TRY(run_scan(d, sa, s));
+  else
+    OSDN_TRY(hip_status(osdn::launch_precond_scan_chunked(sa, sw, d->dtype == OSDN_BF16, s, !fold),
+                        "phase-1 launch"));
   if (fold) {
     osdn::EmitArgs em;
     em.cstep = sw.cstep;
@@ -421,6 +438,7 @@ osdn_status osdn_decode(const osdn_desc *d, const void *q, const void *k, const 
                         const float *r, const float *alpha, const float *d1, const float *S0, void *o,
                         float *S_out, float *d_out, void *stream) {
   OSDN_TRY(validate(d, 3));
+  if (d->r_per_key && r) return fail(OSDN_EUNSUPPORTED, "osdn_decode takes one retention per token and head");
   if (d->T > OSDN_DECODE_MAX_T)
     return fail(OSDN_EUNSUPPORTED, "osdn_decode takes at most %d tokens (got T=%lld)", OSDN_DECODE_MAX_T,
                 (long long)d->T);
@@ -483,6 +501,7 @@ osdn_status osdn_bwd(const osdn_desc *d, const void *q, const void *k, const voi
                      float *dalpha, float *dd1, float *dS0, void *workspace, size_t workspace_bytes,
                      void *stream) {
   OSDN_TRY(validate(d, 3));
+  if (d->r_per_key && r) return fail(OSDN_EUNSUPPORTED, "osdn_bwd takes one retention per token and head");
   if ((double)d->B * (double)d->H > 2147483647.0)
     return fail(OSDN_EUNSUPPORTED, "osdn_bwd supports B*H < 2^31 (got %lld)", (long long)(d->B * d->H));
   const bool need_seq = d->T > 0;
@@ -554,6 +573,89 @@ osdn_status osdn_bwd(const osdn_desc *d, const void *q, const void *k, const voi
   osdn::bwd_work_layout(a, workspace);
   OSDN_TRY(hip_status(osdn::launch_bwd(a, d->dtype == OSDN_BF16, static_cast<hipStream_t>(stream)),
                       "backward launch"));
+  return ok();
+}
+
+size_t osdn_kda_fwd_workspace_bytes(const osdn_desc *d) {
+  if (validate(d, 3) != OSDN_OK) return 0;
+  return fwd_keys_bytes(d) + osdn::scan_work_bytes(d->B, d->T, d->H, d->K) +
+         osdn::kda_work_bytes(d->B, d->T, d->H);
+}
+
+osdn_status osdn_kda_fwd(const osdn_desc *d, const void *q, const void *k, const void *v, const float *beta,
+                         const float *r, const float *alpha, const float *d1, const float *S0, void *o,
+                         float *S_out, float *d_out, void *k_tilde_out, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  OSDN_TRY(validate(d, 3));
+  const bool need_seq = d->T > 0;
+  OSDN_TRY(check_ptr(q, "q", need_seq));
+  OSDN_TRY(check_ptr(k, "k", need_seq));
+  OSDN_TRY(check_ptr(v, "v", need_seq));
+  OSDN_TRY(check_ptr(beta, "beta", need_seq));
+  OSDN_TRY(check_ptr(r, "r", false));
+  OSDN_TRY(check_ptr(alpha, "alpha", false));
+  OSDN_TRY(check_ptr(d1, "d1", false));
+  OSDN_TRY(check_ptr(S0, "S0", false));
+  OSDN_TRY(check_ptr(o, "o", need_seq));
+  OSDN_TRY(check_ptr(S_out, "S_out", false));
+  OSDN_TRY(check_ptr(d_out, "d_out", false));
+  OSDN_TRY(check_ptr(k_tilde_out, "k_tilde_out", false));
+  if (o && (o == q || o == k || o == v || o == k_tilde_out)) return fail(OSDN_EINVAL, "o must not alias an input");
+  if (k_tilde_out && (k_tilde_out == q || k_tilde_out == k || k_tilde_out == v))
+    return fail(OSDN_EINVAL, "k_tilde_out must not alias an input");
+  if (S_out && (S_out == d1 || static_cast<const void *>(S_out) == o))
+    return fail(OSDN_EINVAL, "S_out may alias S0 only");
+  if (d_out && (d_out == S0 || static_cast<const void *>(d_out) == o))
+    return fail(OSDN_EINVAL, "d_out may alias d1 only");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = d->dtype == OSDN_BF16;
+  osdn::ScanArgs sa = scan_args(d, k, beta, r, d1, k_tilde_out, d_out);
+  osdn::KdaArgs ka;
+  ka.q = q;
+  ka.k = k;
+  ka.kt = k_tilde_out;
+  ka.kt_is_res = false;
+  ka.v = v;
+  ka.beta = beta;
+  ka.alpha = alpha;
+  ka.S0 = S0;
+  ka.o = o;
+  ka.S_out = S_out;
+  ka.B = d->B;
+  ka.T = d->T;
+  ka.H = d->H;
+  ka.K = d->K;
+  ka.V = d->V;
+  ka.q_scale = d->q_scale;
+  if (!need_seq) {
+    // nothing to sweep: d_out = d1 and S_out = S0 (the kernels do the copy)
+    OSDN_TRY(run_scan(d, sa, s));
+    OSDN_TRY(hip_status(osdn::launch_kda(ka, bf, s), "phase-2 launch"));
+    return ok();
+  }
+  OSDN_TRY(check_ptr(workspace, "workspace", true));
+  const size_t need = osdn_kda_fwd_workspace_bytes(d);
+  if (workspace_bytes < need)
+    return fail(OSDN_EINVAL, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
+  char *ws = static_cast<char *>(workspace);
+  if (keys_as_residual(d)) {
+    // bf16: the write keys reach phase 2 as the bf16 residual (d - 1) (.) k
+    sa.kt_res = ws;
+    ka.kt = ws;
+    ka.kt_is_res = true;
+  } else if (!k_tilde_out) {
+    sa.k_tilde = ws;
+    ka.kt = ws;
+  }
+  const size_t scan_bytes = osdn::scan_work_bytes(d->B, d->T, d->H, d->K);
+  if (d->r_per_key && r)
+    OSDN_TRY(run_scan(d, sa, s));
+  else
+    OSDN_TRY(hip_status(osdn::launch_precond_scan_chunked(
+                            sa, osdn::scan_work_layout(ws + fwd_keys_bytes(d), d->B, d->T, d->H, d->K), bf, s),
+                        "phase-1 launch"));
+  osdn::kda_work_layout(ka, ws + fwd_keys_bytes(d) + scan_bytes);
+  OSDN_TRY(hip_status(osdn::launch_kda(ka, bf, s), "phase-2 launch"));
   return ok();
 }
 

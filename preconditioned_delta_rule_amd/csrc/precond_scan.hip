@@ -20,13 +20,15 @@
 // a Fast2Sum.  Keys of the next group of tokens are loaded (as raw
 // bf16/f32 words) while the current group is processed; beta and r arrive as
 // one lane-indexed vector load per group and are broadcast with readlane.
+// With vector retention (diag(r_t) in place of r_t, Proposition A.3 of the
+// appendix) r_t is a [K] row per token, loaded and held like the keys.
 #include "kernels.h"
 #include "profile.h"
 #include "scan_common.h"
 
 namespace osdn {
 
-template <typename TIn, int EPL, bool FULL, bool HAS_R, bool WKT, bool WRES>
+template <typename TIn, int EPL, bool FULL, bool HAS_R, bool RV, bool WKT, bool WRES>
 __global__ __launch_bounds__(64) void precond_scan_kernel(ScanArgs a) {
   constexpr int G = 32;  // tokens per prefetch group
   const int lane = threadIdx.x;
@@ -40,6 +42,7 @@ __global__ __launch_bounds__(64) void precond_scan_kernel(ScanArgs a) {
   bf16 *rp_out = WRES ? static_cast<bf16 *>(a.kt_res) + tok0 * K : nullptr;
   const float *bp = a.beta + tok0;
   const float *rp = HAS_R ? a.r + tok0 : nullptr;
+  const float *rvp = RV ? a.r + tok0 * K : nullptr;  // [B,T,H,K] rows
 
   float d[EPL];
 #pragma unroll
@@ -57,21 +60,31 @@ __global__ __launch_bounds__(64) void precond_scan_kernel(ScanArgs a) {
 
   // two key buffers used in turn (no register copies of in-flight loads)
   Row<TIn, EPL, FULL> kA[G], kB[G];
+  Row<float, EPL, FULL> vA[RV ? G : 1], vB[RV ? G : 1];  // retention rows (vector form)
   float bA = 0.0f, rA = 1.0f, bB = 0.0f, rB = 1.0f;  // lane u holds token u of the group
-  auto fetch = [&](int64_t t0, Row<TIn, EPL, FULL> (&kk)[G], float &bb, float &rr) {
+  auto fetch = [&](int64_t t0, Row<TIn, EPL, FULL> (&kk)[G], Row<float, EPL, FULL> (&vv)[RV ? G : 1],
+                   float &bb, float &rr) {
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const int64_t t = t0 + u < T ? t0 + u : T - 1;  // stay in bounds; unused past T
       kk[u].load(kp + t * stride, lane, K);
+      if constexpr (RV) vv[u].load(rvp + t * stride, lane, K);
     }
     const int64_t tl = t0 + (lane < G ? lane : 0);
     const int64_t tc = tl < T ? tl : T - 1;
     bb = bp[tc * H];
     rr = HAS_R ? rp[tc * H] : 1.0f;
   };
-  auto step = [&](int64_t t, const Row<TIn, EPL, FULL> &kr, float bt, float rt) {
-    float k[EPL], w[EPL], s[EPL], pa = 0.0f, pn = 0.0f;
+  auto step = [&](int64_t t, const Row<TIn, EPL, FULL> &kr, const Row<float, EPL, FULL> &rrow, float bt,
+                  float rs) {
+    float k[EPL], w[EPL], s[EPL], rt[EPL], pa = 0.0f, pn = 0.0f;
     kr.get(k);
+    if constexpr (RV) {
+      rrow.get(rt);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) rt[e] = rs;
+    }
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       s[e] = k[e] * k[e];
@@ -97,8 +110,8 @@ __global__ __launch_bounds__(64) void precond_scan_kernel(ScanArgs a) {
     float p[EPL], q[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      p[e] = rt * d[e];                                       // r d = p + ep exactly
-      q[e] = fmaf(-rt, comp[e], fmaf(rt, d[e], -p[e]));       // ep - r comp
+      p[e] = rt[e] * d[e];                                          // r d = p + ep exactly
+      q[e] = fmaf(-rt[e], comp[e], fmaf(rt[e], d[e], -p[e]));       // ep - r comp
     }
     // on the chain
     const float align = wave_sum(pa);
@@ -117,28 +130,29 @@ __global__ __launch_bounds__(64) void precond_scan_kernel(ScanArgs a) {
       comp[e] = cn;
     }
   };
-  auto process = [&](int64_t t0, const Row<TIn, EPL, FULL> (&kk)[G], float bv, float rv) {
+  auto process = [&](int64_t t0, const Row<TIn, EPL, FULL> (&kk)[G], const Row<float, EPL, FULL> (&vv)[RV ? G : 1],
+                     float bv, float rv) {
     if (t0 + G <= T) {
       // full group: straight-line code, so load waits stay per token
 #pragma unroll
-      for (int u = 0; u < G; ++u) step(t0 + u, kk[u], lane_bcast(bv, u), lane_bcast(rv, u));
+      for (int u = 0; u < G; ++u) step(t0 + u, kk[u], vv[RV ? u : 0], lane_bcast(bv, u), lane_bcast(rv, u));
     } else {
       const int nu = (int)(T - t0);
 #pragma unroll
       for (int u = 0; u < G; ++u)
-        if (u < nu) step(t0 + u, kk[u], lane_bcast(bv, u), lane_bcast(rv, u));
+        if (u < nu) step(t0 + u, kk[u], vv[RV ? u : 0], lane_bcast(bv, u), lane_bcast(rv, u));
     }
   };
 
   // Fetches are unconditional (addresses clamped to the last token) so the
   // code between them is straight-line and every load wait stays exact.
-  if (T > 0) fetch(0, kA, bA, rA);
+  if (T > 0) fetch(0, kA, vA, bA, rA);
   for (int64_t t0 = 0; t0 < T; t0 += 2 * G) {
-    fetch(t0 + G, kB, bB, rB);
-    process(t0, kA, bA, rA);
+    fetch(t0 + G, kB, vB, bB, rB);
+    process(t0, kA, vA, bA, rA);
     if (t0 + G >= T) break;
-    fetch(t0 + 2 * G, kA, bA, rA);
-    process(t0 + G, kB, bB, rB);
+    fetch(t0 + 2 * G, kA, vA, bA, rA);
+    process(t0 + G, kB, vB, bB, rB);
   }
   if (a.d_out) {
 #pragma unroll
@@ -149,24 +163,26 @@ __global__ __launch_bounds__(64) void precond_scan_kernel(ScanArgs a) {
   }
 }
 
-template <typename TIn, int EPL, bool FULL, bool HAS_R>
+template <typename TIn, int EPL, bool FULL, bool HAS_R, bool RV>
 static void launch_out(const ScanArgs &a, hipStream_t s) {
   dim3 grid((unsigned)(a.B * a.H)), block(64);
   if (a.k_tilde && a.kt_res)
-    hipLaunchKernelGGL((precond_scan_kernel<TIn, EPL, FULL, HAS_R, true, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((precond_scan_kernel<TIn, EPL, FULL, HAS_R, RV, true, true>), grid, block, 0, s, a);
   else if (a.kt_res)
-    hipLaunchKernelGGL((precond_scan_kernel<TIn, EPL, FULL, HAS_R, false, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((precond_scan_kernel<TIn, EPL, FULL, HAS_R, RV, false, true>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((precond_scan_kernel<TIn, EPL, FULL, HAS_R, true, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((precond_scan_kernel<TIn, EPL, FULL, HAS_R, RV, true, false>), grid, block, 0, s, a);
   prof_mark(s, "precond_scan_kernel");
 }
 
 template <typename TIn, int EPL, bool FULL>
 static hipError_t launch_epl(const ScanArgs &a, hipStream_t s) {
-  if (a.r)
-    launch_out<TIn, EPL, FULL, true>(a, s);
+  if (a.r && a.r_per_key)
+    launch_out<TIn, EPL, FULL, false, true>(a, s);
+  else if (a.r)
+    launch_out<TIn, EPL, FULL, true, false>(a, s);
   else
-    launch_out<TIn, EPL, FULL, false>(a, s);
+    launch_out<TIn, EPL, FULL, false, false>(a, s);
   return hipGetLastError();
 }
 

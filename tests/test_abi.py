@@ -40,7 +40,7 @@ def test_desc_layout_and_defaults(lib):
     assert d.chunk == 64 and d.dtype == osdn.BF16 and d.clamp == 1 and d.beta_aware == 1
     assert d.eta == pytest.approx(0.003) and d.eps == pytest.approx(1e-6)
     assert (d.d_min, d.d_max, d.q_scale) == (0.5, 2.0, 1.0)
-    assert ctypes.sizeof(osdn.Desc) == 80
+    assert ctypes.sizeof(osdn.Desc) == 80 and d.r_per_key == 0
     assert lib.osdn_validate(ctypes.byref(d)) == osdn.OK
     assert lib.osdn_version() >> 16 == 1
 
@@ -58,6 +58,7 @@ BAD = [
     (dict(eta=-1.0), osdn.EINVAL), (dict(eps=0.0), osdn.EINVAL),
     (dict(d_min=2.0, d_max=1.0), osdn.EINVAL), (dict(d_min=0.0), osdn.EINVAL),
     (dict(q_scale=float("inf")), osdn.EINVAL), (dict(eta=float("nan")), osdn.EINVAL),
+    (dict(r_per_key=2), osdn.EINVAL),
 ]
 
 
@@ -206,3 +207,45 @@ def test_size_queries_return_64_bit(lib):
     # workspace sizes above 2^31 bytes come back whole through the binding
     assert osdn.bwd_workspace_bytes(4, 4096, 16, 128, 128) > 2 ** 31
     assert osdn.fwd_workspace_bytes(256, 4096, 16, 128, 128) > 2 ** 32
+
+
+def test_kda_argument_checks(lib):
+    # OSKDA: sizes, required pointers, aliasing and workspace, all on the host
+    null = ctypes.c_void_p(None)
+    fake, fake2, fake3 = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
+    d = osdn.Desc()
+    lib.osdn_desc_init(ctypes.byref(d), 2, 100, 4, 128, 128)
+    z = ctypes.c_size_t(0)
+    st = lib.osdn_kda_fwd(ctypes.byref(d), fake, fake, fake, fake2, null, null, null, null, fake3,
+                          null, null, null, null, z, null)
+    assert st == osdn.EINVAL and "workspace" in lib.osdn_last_error().decode()
+    st = lib.osdn_kda_fwd(ctypes.byref(d), fake, fake, fake, fake2, null, null, null, null, fake,
+                          null, null, null, fake3, z, null)
+    assert st == osdn.EINVAL and "alias" in lib.osdn_last_error().decode()
+    st = lib.osdn_kda_fwd(ctypes.byref(d), fake, null, fake, fake2, null, null, null, null, fake3,
+                          null, null, null, fake3, z, null)
+    assert st == osdn.EINVAL and "k must not be NULL" in lib.osdn_last_error().decode()
+    need = lib.osdn_kda_fwd_workspace_bytes(ctypes.byref(d))
+    # 2 x 4 heads x 2 chunks of 64 tokens: 128.5 KiB of operands each, plus phase 1's share
+    assert need >= 16 * (3 * 64 * 128 + 2 * 64 * 64 + 128) * 4
+    st = lib.osdn_kda_fwd(ctypes.byref(d), fake, fake, fake, fake2, null, null, null, null, fake3,
+                          null, null, null, ctypes.c_void_p(0x10000), ctypes.c_size_t(need - 1), null)
+    assert st == osdn.EINVAL and "needed" in lib.osdn_last_error().decode()
+    d.V = 129
+    assert lib.osdn_kda_fwd_workspace_bytes(ctypes.byref(d)) == 0
+    st = lib.osdn_kda_fwd(ctypes.byref(d), fake, fake, fake, fake2, null, null, null, null, fake3,
+                          null, null, null, fake3, z, null)
+    assert st == osdn.EUNSUPPORTED
+
+
+def test_vector_retention_rejected_where_unsupported(lib):
+    null = ctypes.c_void_p(None)
+    fake, fake2, fake3 = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
+    d = osdn.Desc()
+    lib.osdn_desc_init(ctypes.byref(d), 1, 4, 2, 16, 16)
+    d.r_per_key = 1
+    st = lib.osdn_decode(ctypes.byref(d), fake, fake, fake, fake2, fake2, null, null, null, fake3,
+                         null, null, null)
+    assert st == osdn.EUNSUPPORTED and "retention" in lib.osdn_last_error().decode()
+    args = [fake, fake, fake, fake2, fake2] + [null] * 15 + [ctypes.c_size_t(0), null]
+    assert lib.osdn_bwd(ctypes.byref(d), *args) == osdn.EUNSUPPORTED

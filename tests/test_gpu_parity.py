@@ -370,3 +370,24 @@ def test_fwd_write_keys_output_and_residual_path():
     ref = oracle_fwd(inp)
     assert o_err(to_np(o1), ref["o"]) <= BF16_OS
     assert s_err(to_np(S1), ref["S"]) <= BF16_OS
+
+
+@pytest.mark.parametrize("box", ["no_clamp", "low_d_min"])
+@pytest.mark.parametrize("gated", [False, True], ids=["osdn", "gdn"])
+def test_fwd_bf16_without_half_bound(box, gated):
+    """bf16 osdn_fwd when the box does not keep d >= 1/2 (no clamp, or
+    d_min < 1/2): d can shrink far below 1, so the write keys must not cross
+    as the residual (d - 1) k (it would cancel); the outputs stay within the
+    bf16 bar on the matrix-core path."""
+    kw = dict(clamp=False, eta=0.2) if box == "no_clamp" else dict(d_min=0.02, eta=0.2)
+    inp = make_inputs(dict(B=2, T=200, H=2, K=128, V=128, dtype="bf16", chunk=64, seed=9,
+                           apf=True, gdn=gated, **kw))
+    p = inp["params"]
+    o, S, d = osdn.fwd(*(to_dev(inp[n], "bf16") for n in ("q", "k", "v")),
+                       *(to_dev(inp[n], "f32") for n in ("beta", "r", "alpha")), eta=p["eta"],
+                       d_min=p["d_min"], d_max=p["d_max"], clamp=p["clamp"], eps=p["eps"])
+    torch.cuda.synchronize()
+    ref = oracle_fwd(inp)
+    assert float(np.min(ref["d"])) < 0.1  # d really leaves [1/2, 2]
+    assert o_err(to_np(o), ref["o"]) <= BF16_OS
+    assert s_err(to_np(S), ref["S"]) <= BF16_OS

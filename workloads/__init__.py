@@ -16,6 +16,11 @@ Recipe (same for every named workload unless stated):
     generator ``default_rng(seed + 2)`` draws dL/do ~ N(0, 1) [B,T,H,V]
     (rounded to bf16 for bf16 workloads), then dL/dS_T ~ N(0, 1) and
     dL/dd_{T+1} ~ N(0, 1), float32;
+  * OSKDA workloads (``kda``) draw, after everything above, a channel-wise
+    decay alpha = exp(-softplus(N(0,1)) * kda_decay) per key channel
+    [B,T,H,K] (kda_decay 0.1 unless stated); ``r_vec`` then draws a vector
+    retention r = sigmoid(N(2,1)) per key coordinate [B,T,H,K] in place of the
+    scalar one;
   * packed variable-length batches (``varlen_lengths``): sequence lengths
     drawn with ``default_rng(seed + 3)`` uniformly from [256, 4096] until the
     packed length is reached (the last one cut to fit);
@@ -55,6 +60,10 @@ WORKLOADS = {
     # Appendix F): 65,536 tokens, sequence lengths from varlen_lengths
     "varlen_1p3b_65k": dict(B=1, T=65536, H=16, K=128, V=128, dtype="bf16", chunk=64,
                             seed=8, apf=True),
+    # OSKDA on the 340M KDA-shaped layer (8 heads of 128), APF retention,
+    # channel-wise decay
+    "kda_340m_apf": dict(B=8, T=2048, H=8, K=128, V=128, dtype="bf16", chunk=64, seed=9,
+                         apf=True, kda=True),
     "decode_1p3b": dict(B=4, T=1, H=16, K=128, V=128, dtype="bf16", chunk=64,
                         seed=5, apf=True, state=True),
     "decode_1p3b_b256": dict(B=256, T=1, H=16, K=128, V=128, dtype="bf16",
@@ -64,7 +73,8 @@ WORKLOADS = {
 DEFAULTS = dict(eta=0.003, d_min=0.5, d_max=2.0, eps=1e-6, clamp=True,
                 beta_aware=True, q_scale=1.0, keys="normal", beta_mu=0.0,
                 apf=False, apf_const=None, gdn=False, dtype="f32", chunk=64,
-                seed=0, onehot_bias=None, sparse_nnz=3, state=False)
+                seed=0, onehot_bias=None, sparse_nnz=3, state=False, kda=False,
+                kda_decay=0.1, r_vec=False)
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
@@ -184,6 +194,14 @@ def make_inputs(name_or_spec, *, T=None, B=None, H=None) -> dict:
     if s["gdn"]:
         g = rng.standard_normal((Bn, Tn, Hn), dtype=np.float32)
         alpha = np.exp(-_softplus(g) * np.float32(0.1)).astype(np.float32)
+    if s["kda"]:
+        # channel-wise decay of the KDA backbone, one gate per key channel
+        g = rng.standard_normal((Bn, Tn, Hn, K), dtype=np.float32)
+        alpha = np.exp(-_softplus(g) * np.float32(s["kda_decay"])).astype(np.float32)
+    if s["r_vec"]:
+        # vector retention: one retention per key coordinate
+        logits = rng.standard_normal((Bn, Tn, Hn, K), dtype=np.float32) + np.float32(2.0)
+        r = _sigmoid(logits).astype(np.float32)
     if s["dtype"] == "bf16":
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
     params = {key: s[key] for key in ("eta", "d_min", "d_max", "eps", "clamp",
