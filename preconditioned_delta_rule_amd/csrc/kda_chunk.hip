@@ -41,10 +41,8 @@ namespace {
 
 constexpr int KC = 64;     // chunk length
 constexpr int KP = 128;    // key channels (zero-padded)
-constexpr int KVT = 32;    // value columns per sweep workgroup
 constexpr int LP = 132;    // LDS pitch of the intra kernel's [64][128] tiles
 constexpr int AP = 65;     // LDS pitch of its [64][64] tiles
-constexpr int SP = 48;     // LDS pitch of the sweep's [rows][32] tiles
 constexpr float G_SAFE = -60.0f;
 
 __device__ __forceinline__ floatx4 mfma_f32(float a, float b, floatx4 c) {
@@ -57,11 +55,53 @@ __device__ __forceinline__ float ld_tok(const TIn *p, int64_t row_off, int c, in
   return ok && c < K ? to_f32(p[row_off + c]) : 0.0f;
 }
 
+// 4 consecutive elements of a row as fp32 (one 8-byte load for bf16, one
+// 16-byte load for fp32)
+__device__ __forceinline__ floatx4 ld4f(const bf16 *p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
+  return floatx4{to_f32(v[0]), to_f32(v[1]), to_f32(v[2]), to_f32(v[3])};
+}
+__device__ __forceinline__ floatx4 ld4f(const float *p) { return *reinterpret_cast<const floatx4 *>(p); }
+
+// Write Gamma . K and Gamma . Q ([64][128], each row permuted so that
+// output p = 32 g + s holds channel 4 s + g) and the transposed state-update
+// operand Kc^T ([128][64], output q = 16 g + s of row kr holding token
+// 4 s + g, scaled per channel by egl), from the LDS tiles sK, sQ, sKt.
+__device__ __forceinline__ void write_operands(const float *sK, const float *sQ, const float *sKt,
+                                               const float *egl, float *kh, float *qh, float *kc, int tid) {
+  // kh, qh: lane -> (g = lane & 3, 4-output block sb = (lane >> 2) & 7),
+  // two rows per wave pass
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int idx = tid + 256 * u, g = idx & 3, sb = (idx >> 2) & 7, row = idx >> 5;
+    floatx4 x, y;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c = 4 * (4 * sb + t) + g;
+      x[t] = sK[row * LP + c];
+      y[t] = sQ[row * LP + c];
+    }
+    *reinterpret_cast<floatx4 *>(kh + row * KP + 32 * g + 4 * sb) = x;
+    *reinterpret_cast<floatx4 *>(qh + row * KP + 32 * g + 4 * sb) = y;
+  }
+  // kc: lane -> channel kr (consecutive lanes read consecutive banks)
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int idx = tid + 256 * u, kr = idx & (KP - 1), blk = idx >> 7;  // blk = 16-output block
+    const int g = blk >> 2, s0 = 4 * (blk & 3);
+    const float sc = egl[kr];
+    floatx4 x;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) x[t] = sKt[(4 * (s0 + t) + g) * LP + kr] * sc;
+    *reinterpret_cast<floatx4 *>(kc + kr * KC + 16 * g + s0) = x;
+  }
+}
+
 template <typename TIn, bool RES, bool GATED>
 __global__ __launch_bounds__(256) void kda_intra_kernel(KdaArgs a, int64_t N) {
   extern __shared__ float sm[];
   float *sK = sm, *sKt = sK + KC * LP, *sQ = sKt + KC * LP, *sG = sQ + KC * LP;
-  __shared__ float sBeta[KC], sGL[KP];
+  __shared__ float sBeta[KC], sGL[KP], sEGL[KP];
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, l16 = l & 15, g = l >> 4;
   const int64_t bh = blockIdx.x / N, n = blockIdx.x - bh * N;
   const int64_t H = a.H, T = a.T;
@@ -74,7 +114,43 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(KdaArgs a, int64_t N) {
   const TIn *ktp = static_cast<const TIn *>(a.kt);
 
   // ---- load the chunk: k, k~, q_scale q, log alpha (zero rows past L,
-  //      zero channels past K)
+  //      zero channels past K).  Full rows (K = 128): every load of the chunk
+  //      is issued before the first LDS write, rows past L read row L - 1.
+  if (K == KP) {
+    // each thread: 4 consecutive channels of 8 rows; 16-byte LDS writes, a
+    // quarter-wave covering all 64 banks
+    floatx4 xk[8], xw[8], xq[8], xa[8];
+    const int c4 = (tid & 31) * 4;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int row = (tid >> 5) + 8 * u, rr = row < L ? row : L - 1;
+      const int64_t off = ((b * T + t0 + rr) * H + h) * (int64_t)KP + c4;
+      xk[u] = ld4f(kp + off);
+      if constexpr (RES)
+        xw[u] = ld4f(static_cast<const bf16 *>(a.kt) + off);
+      else
+        xw[u] = ld4f(ktp + off);
+      xq[u] = ld4f(qp + off);
+      if constexpr (GATED) xa[u] = *reinterpret_cast<const floatx4 *>(a.alpha + off);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int row = (tid >> 5) + 8 * u;
+      const bool ok = row < L;
+      floatx4 kv, kw, qv, gv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kv[e] = ok ? xk[u][e] : 0.0f;
+        kw[e] = ok ? (RES ? xk[u][e] + xw[u][e] : xw[u][e]) : 0.0f;
+        qv[e] = ok ? a.q_scale * xq[u][e] : 0.0f;
+        gv[e] = GATED && ok ? __logf(xa[u][e]) : 0.0f;
+      }
+      *reinterpret_cast<floatx4 *>(sK + row * LP + c4) = kv;
+      *reinterpret_cast<floatx4 *>(sKt + row * LP + c4) = kw;
+      *reinterpret_cast<floatx4 *>(sQ + row * LP + c4) = qv;
+      *reinterpret_cast<floatx4 *>(sG + row * LP + c4) = gv;
+    }
+  } else
   for (int e = tid; e < KC * KP; e += 256) {
     const int row = e >> 7, c = e & (KP - 1);
     const bool ok = row < L;
@@ -95,15 +171,21 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(KdaArgs a, int64_t N) {
   }
   if (tid < KC) sBeta[tid] = tid < L ? a.beta[(b * T + t0 + tid) * H + h] : 0.0f;
   __syncthreads();
-  // ---- G = in-chunk cumulative log decay, per channel
+  // ---- G = in-chunk cumulative log decay, per channel (one column per
+  //      thread, in registers)
   int unsafe = 0;
   if (tid < KP) {
+    float col[KC];
+#pragma unroll
+    for (int row = 0; row < KC; ++row) col[row] = sG[row * LP + tid];
     float acc = 0.0f;
+#pragma unroll
     for (int row = 0; row < KC; ++row) {
-      acc += sG[row * LP + tid];
+      acc += col[row];
       sG[row * LP + tid] = acc;
     }
     sGL[tid] = acc;  // G at the chunk's last token (rows past L add log 1)
+    sEGL[tid] = __expf(acc);
     unsafe = acc < G_SAFE;
   }
   unsafe = __syncthreads_or(unsafe);
@@ -118,20 +200,15 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(KdaArgs a, int64_t N) {
     for (int e = tid; e < KC * KP; e += 256) {
       const int row = e >> 7, c = e & (KP - 1);
       const float gg = sG[row * LP + c];
-      const float eg = expf(gg);
+      const float eg = __expf(gg);
       sK[row * LP + c] *= eg;
       sQ[row * LP + c] *= eg;
-      sKt[row * LP + c] *= expf(-gg);
+      sKt[row * LP + c] *= __expf(-gg);
     }
     __syncthreads();
-    // outputs of the scaled operands (k~ e^{G_L - G} = (k~ e^-G) e^{G_L})
-    for (int e = tid; e < KC * KP; e += 256) {
-      const int row = e >> 7, p = e & (KP - 1), c = 4 * (p & 31) + (p >> 5);
-      kh[e] = sK[row * LP + c];
-      qh[e] = sQ[row * LP + c];
-      const int kr = e >> 6, q = e & 63, j = 4 * (q & 15) + (q >> 4);
-      kc[e] = sKt[j * LP + kr] * expf(sGL[kr]);
-    }
+    // outputs of the scaled operands (k~ e^{G_L - G} = (k~ e^-G) e^{G_L}),
+    // four consecutive outputs per 16-byte store
+    write_operands(sK, sQ, sKt, sEGL, kh, qh, kc, tid);
     // ---- A and M on the matrix cores, lower 16x16 blocks (I >= J)
     for (int e = tid; e < KC * KC; e += 256) {  // upper blocks are zero
       const int i = e >> 6, j = e & 63;
@@ -210,7 +287,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(KdaArgs a, int64_t N) {
       }
     }
   }
-  if (tid < KP) a.gc[cbase * KP + tid] = expf(sGL[tid]);
+  if (tid < KP) a.gc[cbase * KP + tid] = sEGL[tid];
   __syncthreads();
 
   // ---- T = (I + A)^-1 (unit lower triangular), 16x16 blocks.  sT takes K's
@@ -234,19 +311,23 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(KdaArgs a, int64_t N) {
   }
   __syncthreads();
   for (int I = 1; I < 4; ++I) {
-    // Y = A[I, 0:16I] T[0:16I, 0:16I], then T[I, 0:16I] = -T_II Y
-    for (int e = tid; e < 16 * 16 * I; e += 256) {
-      const int i = 16 * I + e / (16 * I), j = e % (16 * I);
-      float acc = 0.0f;
-      for (int m = j; m < 16 * I; ++m) acc = fmaf(sA[i * AP + m], sT[m * AP + j], acc);
-      sY[i * AP + j] = acc;
+    // block row I: Y_IJ = sum_{J <= M < I} A_IM T_MJ, then T_IJ = -T_II Y_IJ,
+    // wave J < I taking block column J on the matrix cores
+    if (w < I) {
+      floatx4 y = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 4 * w; s < 4 * I; ++s)
+        y = mfma_f32(sA[(16 * I + l16) * AP + 4 * s + g], sT[(4 * s + g) * AP + 16 * w + l16], y);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sY[(16 * I + 4 * g + r) * AP + 16 * w + l16] = y[r];
     }
     __syncthreads();
-    for (int e = tid; e < 16 * 16 * I; e += 256) {
-      const int i = 16 * I + e / (16 * I), j = e % (16 * I);
-      float acc = 0.0f;
-      for (int m = 16 * I; m <= i; ++m) acc = fmaf(sT[i * AP + m], sY[m * AP + j], acc);
-      sT[i * AP + j] = -acc;
+    if (w < I) {
+      floatx4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        t = mfma_f32(sT[(16 * I + l16) * AP + 16 * I + 4 * s + g], sY[(16 * I + 4 * s + g) * AP + 16 * w + l16], t);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * g + r) * AP + 16 * w + l16] = -t[r];
     }
     __syncthreads();
   }
@@ -258,8 +339,12 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(KdaArgs a, int64_t N) {
   }
 }
 
-template <typename TIn>
+// NCB 16-column blocks of values per workgroup; the LDS pitch of the
+// [rows][16 NCB] tiles keeps the four rows an MFMA operand read touches in
+// distinct banks
+template <typename TIn, int NCB>
 __global__ __launch_bounds__(256) void kda_seq_kernel(KdaArgs a, int64_t N, int ntile) {
+  constexpr int KVT = 16 * NCB, SP = NCB == 1 ? 16 : 48;
   __shared__ float sS[KP * SP];
   __shared__ float sX[KC * SP];
   __shared__ float sD[KC * SP];
@@ -285,11 +370,11 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(KdaArgs a, int64_t N, int 
 
   // state tile: wave w holds key rows 32 w .. 32 w + 31 (two 16-row blocks)
   // for both 16-column blocks, in the MFMA result layout
-  floatx4 Sr[2][2];
+  floatx4 Sr[2][NCB];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int kr = 32 * w + 16 * rb + 4 * g + i;
@@ -300,89 +385,106 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(KdaArgs a, int64_t N, int 
         sS[kr * SP + 16 * cb + l16] = x;
       }
 
+  // Operands of a chunk, loaded in four groups; each group of chunk n + 1 is
+  // requested as soon as chunk n is done with it, so the loads land while
+  // the rest of chunk n runs (the last chunk's requests re-read chunk N - 1).
+  floatx4 kq4[8][2], tm4[4][2], kc4[2][4], gc4[2];
+  float vv[NCB][4];
+  auto load_kq = [&](int64_t n) {
+    const int64_t cb0 = bh * N + n;
+    const floatx4 *pk = reinterpret_cast<const floatx4 *>(a.kh + cb0 * (KC * KP) + (16 * w + l16) * KP + 32 * g);
+    const floatx4 *pq = reinterpret_cast<const floatx4 *>(a.qh + cb0 * (KC * KP) + (16 * w + l16) * KP + 32 * g);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      kq4[u][0] = pk[u];
+      kq4[u][1] = pq[u];
+    }
+    const int64_t t0 = n * KC;
+    const int L = (int)(T - t0 < KC ? T - t0 : KC);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * w + 4 * g + i, rr = row < L ? row : L - 1;
+        const int64_t col = v0 + 16 * cb + l16, cc = col < V ? col : V - 1;
+        vv[cb][i] = to_f32(vp[((b * T + t0 + rr) * H + h) * V + cc]);
+      }
+  };
+  auto load_tm = [&](int64_t n) {
+    const int64_t cb0 = bh * N + n;
+    const floatx4 *pt = reinterpret_cast<const floatx4 *>(a.tb + cb0 * (KC * KC) + (16 * w + l16) * KC + 16 * g);
+    const floatx4 *pm = reinterpret_cast<const floatx4 *>(a.mq + cb0 * (KC * KC) + (16 * w + l16) * KC + 16 * g);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      tm4[u][0] = pt[u];
+      tm4[u][1] = pm[u];
+    }
+  };
+  auto load_kc = [&](int64_t n) {
+    const int64_t cb0 = bh * N + n;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const floatx4 *pc = reinterpret_cast<const floatx4 *>(a.kc + cb0 * (KC * KP) +
+                                                            (32 * w + 16 * rb + l16) * KC + 16 * g);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kc4[rb][u] = pc[u];
+      gc4[rb] = *reinterpret_cast<const floatx4 *>(a.gc + cb0 * KP + 32 * w + 16 * rb + 4 * g);
+    }
+  };
+  if (N > 0) {
+    load_kq(0);
+    load_tm(0);
+    load_kc(0);
+  }
+
   for (int64_t n = 0; n < N; ++n) {
     const int64_t t0 = n * KC;
     const int L = (int)(T - t0 < KC ? T - t0 : KC);
-    const int64_t cbase = bh * N + n;
-    // this chunk's operands (all loads issued up front)
-    float ka[32], qa[32], ta[16], ma[16], kca[2][16], gcv[2][4];
-    {
-      const floatx4 *pk = reinterpret_cast<const floatx4 *>(a.kh + cbase * (KC * KP) + (16 * w + l16) * KP + 32 * g);
-      const floatx4 *pq = reinterpret_cast<const floatx4 *>(a.qh + cbase * (KC * KP) + (16 * w + l16) * KP + 32 * g);
+    const int64_t nn = n + 1 < N ? n + 1 : n;  // next chunk (in bounds)
+    floatx4 accX[NCB], accP[NCB];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const floatx4 x = pk[u], y = pq[u];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ka[4 * u + e] = -x[e];  // X = V - K S: the product enters negated
-          qa[4 * u + e] = y[e];
-        }
-      }
-      const floatx4 *pt = reinterpret_cast<const floatx4 *>(a.tb + cbase * (KC * KC) + (16 * w + l16) * KC + 16 * g);
-      const floatx4 *pm = reinterpret_cast<const floatx4 *>(a.mq + cbase * (KC * KC) + (16 * w + l16) * KC + 16 * g);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const floatx4 x = pt[u], y = pm[u];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ta[4 * u + e] = x[e];
-          ma[4 * u + e] = y[e];
-        }
-      }
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const floatx4 *pc = reinterpret_cast<const floatx4 *>(a.kc + cbase * (KC * KP) +
-                                                              (32 * w + 16 * rb + l16) * KC + 16 * g);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const floatx4 x = pc[u];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) kca[rb][4 * u + e] = x[e];
-        }
-        const floatx4 x = *reinterpret_cast<const floatx4 *>(a.gc + cbase * KP + 32 * w + 16 * rb + 4 * g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) gcv[rb][e] = x[e];
-      }
-    }
-    floatx4 accX[2], accP[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * w + 4 * g + i;
         const int64_t col = v0 + 16 * cb + l16;
-        float x = 0.0f;
-        if (row < L && col < V) x = to_f32(vp[((b * T + t0 + row) * H + h) * V + col]);
-        accX[cb][i] = x;
+        accX[cb][i] = row < L && col < V ? vv[cb][i] : 0.0f;
         accP[cb][i] = 0.0f;
       }
     __syncthreads();  // sS holds the chunk's boundary state
     // (a) X = V - (Gamma . K) S and P = (Gamma . Q) S, rows 16 w ..
 #pragma unroll
     for (int s = 0; s < KP / 4; ++s) {
-      const float b0 = sS[(4 * s + g) * SP + l16], b1 = sS[(4 * s + g) * SP + 16 + l16];
-      accX[0] = mfma_f32(ka[s], b0, accX[0]);
-      accX[1] = mfma_f32(ka[s], b1, accX[1]);
-      accP[0] = mfma_f32(qa[s], b0, accP[0]);
-      accP[1] = mfma_f32(qa[s], b1, accP[1]);
+      const float b0 = sS[(4 * s + g) * SP + l16], b1 = NCB > 1 ? sS[(4 * s + g) * SP + 16 + l16] : 0.0f;
+      const float ka = -kq4[s >> 2][0][s & 3];  // X = V - K S: the product enters negated
+      const float qa = kq4[s >> 2][1][s & 3];
+      accX[0] = mfma_f32(ka, b0, accX[0]);
+      accP[0] = mfma_f32(qa, b0, accP[0]);
+      if constexpr (NCB > 1) {
+        accX[1] = mfma_f32(ka, b1, accX[1]);
+        accP[1] = mfma_f32(qa, b1, accP[1]);
+      }
     }
+    load_kq(nn);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sX[(16 * w + 4 * g + i) * SP + 16 * cb + l16] = accX[cb][i];
     __syncthreads();
     // (b) D = TB X (TB lower triangular: contraction up to row 16 w + 15)
-    floatx4 accD[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    floatx4 accD[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) accD[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       if (s < 4 * w + 4) {
-        const float b0 = sX[(4 * s + g) * SP + l16], b1 = sX[(4 * s + g) * SP + 16 + l16];
-        accD[0] = mfma_f32(ta[s], b0, accD[0]);
-        accD[1] = mfma_f32(ta[s], b1, accD[1]);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          accD[cb] = mfma_f32(tm4[s >> 2][0][s & 3], sX[(4 * s + g) * SP + 16 * cb + l16], accD[cb]);
       }
     }
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sD[(16 * w + 4 * g + i) * SP + 16 * cb + l16] = accD[cb][i];
     __syncthreads();
@@ -390,13 +492,14 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(KdaArgs a, int64_t N, int 
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       if (s < 4 * w + 4) {
-        const float b0 = sD[(4 * s + g) * SP + l16], b1 = sD[(4 * s + g) * SP + 16 + l16];
-        accP[0] = mfma_f32(ma[s], b0, accP[0]);
-        accP[1] = mfma_f32(ma[s], b1, accP[1]);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          accP[cb] = mfma_f32(tm4[s >> 2][1][s & 3], sD[(4 * s + g) * SP + 16 * cb + l16], accP[cb]);
       }
     }
+    load_tm(nn);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * w + 4 * g + i;
@@ -407,21 +510,22 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(KdaArgs a, int64_t N, int 
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
+      for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Sr[rb][cb][i] *= gcv[rb][i];
+        for (int i = 0; i < 4; ++i) Sr[rb][cb][i] *= gc4[rb][i];
 #pragma unroll
         for (int s = 0; s < 16; ++s)
-          Sr[rb][cb] = mfma_f32(kca[rb][s], sD[(4 * s + g) * SP + 16 * cb + l16], Sr[rb][cb]);
+          Sr[rb][cb] = mfma_f32(kc4[rb][s >> 2][s & 3], sD[(4 * s + g) * SP + 16 * cb + l16], Sr[rb][cb]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sS[(32 * w + 16 * rb + 4 * g + i) * SP + 16 * cb + l16] = Sr[rb][cb][i];
       }
+    load_kc(nn);
   }
   if (a.S_out) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int kr = 32 * w + 16 * rb + 4 * g + i;
@@ -456,9 +560,12 @@ hipError_t launch_typed(const KdaArgs &a, hipStream_t s) {
     hipError_t e = a.kt_is_res ? launch_intra<TIn, true>(a, N, s) : launch_intra<TIn, false>(a, N, s);
     if (e != hipSuccess) return e;
   }
-  const int ntile = (int)((a.V + KVT - 1) / KVT);
+  // 32 value columns per workgroup: 16 columns (two workgroups per CU) measured
+  // slower, each workgroup fetching the whole chunk operands for half the work
+  constexpr int NCB = 2;
+  const int ntile = (int)((a.V + 16 * NCB - 1) / (16 * NCB));
   dim3 grid((unsigned)(a.B * a.H * ntile)), block(256);
-  hipLaunchKernelGGL((kda_seq_kernel<TIn>), grid, block, 0, s, a, N, ntile);
+  hipLaunchKernelGGL((kda_seq_kernel<TIn, NCB>), grid, block, 0, s, a, N, ntile);
   prof_mark(s, "kda_seq_kernel");
   return hipGetLastError();
 }
