@@ -42,8 +42,10 @@ variable-length sequences (default: 65,536 tokens in sequences of 256-4,096,
 H=16, K=V=128, bf16, APF); per-token-head work is that of the forward.
 
 With --kda a step is one osdn_kda_fwd call (OSKDA: K x V state, channel-wise
-decay; default B=8, T=2048, H=8, K=V=128, bf16, APF); its roofline is the sweep
-kernel's fp32 matrix-core arithmetic.
+decay; default B=8, T=2048, H=8, K=V=128, bf16, APF).  Its roofline is that of
+the longest kernel, against whichever roof it comes closer to: HBM at its
+algorithmic bytes, or the matrix cores at its algorithmic flops (bf16 peak for
+bf16 inputs, whose sweep runs hi/lo bf16 pairs; fp32 peak for fp32 inputs).
 
 With --decode a step is instead one osdn_decode call (the single-token
 recurrence): T new tokens per (b,h) continuing a carried fp32 state, default
@@ -72,7 +74,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "OSDN fwd tokens/sec (phase1+phase2) at H=16,K=V=128,T=4096; % HBM/MFMA roofline"
-KDA_METRIC = "OSKDA fwd tokens/sec (osdn_kda_fwd) at H=8,K=V=128; % fp32 MFMA roofline"
+KDA_METRIC = "OSKDA fwd tokens/sec (osdn_kda_fwd) at H=8,K=V=128; % roofline of the dominant kernel"
 VARLEN_METRIC = "OSDN fwd tokens/sec over a packed variable-length batch (osdn_fwd_varlen) at H=16,K=V=128; % HBM roofline"
 BWD_METRIC = "OSDN bwd tokens/sec (osdn_bwd, both phases) at H=16,K=V=128,T=4096; % fp32 vector roofline"
 FP32_VALU_PEAK_TFLOPS = 157.3
@@ -471,17 +473,25 @@ def kda_bench(args, inp, dev):
         ent = {"ms": ms, "bytes_per_token_head": nbytes, "GB/s": gbs,
                "hbm_frac": gbs / HBM_PEAK_GBS if gbs else None}
         if flops and name.startswith("kda_"):
+            # the sweep multiplies bf16 hi/lo pairs for bf16 inputs, fp32 otherwise;
+            # the intra kernel's Gram runs fp32 matrix instructions
+            peak = MFMA_BF16_PEAK_TFLOPS if (elem == 2 and name.startswith("kda_seq")) else FP32_VALU_PEAK_TFLOPS
             ent["flops_per_token_head"] = flops
             ent["TFLOP/s"] = flops * nth / (ms * 1e-3) / 1e12
-            ent["mfma_fp32_frac"] = ent["TFLOP/s"] / FP32_VALU_PEAK_TFLOPS
+            ent["mfma_peak_TFLOP/s"] = peak
+            ent["mfma_frac"] = ent["TFLOP/s"] / peak
         kernels[name] = ent
         log("  %-20s %.4f ms  %.0f GB/s" % (name, ms, gbs or 0))
-    dom = "kda_seq_kernel"
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
     dk = kernels[dom]
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": dk["TFLOP/s"], "peak": FP32_VALU_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": dk["mfma_fp32_frac"], "traffic": None,
-                "algorithmic_flops_per_launch": dk["flops_per_token_head"] * nth,
-                "hbm_GB/s_at_algorithmic_bytes": dk["GB/s"]}
+    if dk.get("mfma_frac", 0.0) > dk["hbm_frac"]:
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": dk["TFLOP/s"], "peak": dk["mfma_peak_TFLOP/s"],
+                    "unit": "TFLOP/s", "frac": dk["mfma_frac"], "traffic": None,
+                    "algorithmic_flops_per_launch": dk["flops_per_token_head"] * nth}
+    else:
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": dk["GB/s"], "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": dk["hbm_frac"], "traffic": None,
+                    "algorithmic_bytes_per_launch": dk["bytes_per_token_head"] * nth}
     cpu = None
     if not args.no_cpu_baseline:
         import oracle

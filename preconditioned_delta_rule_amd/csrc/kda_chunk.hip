@@ -69,6 +69,7 @@ __device__ __forceinline__ floatx4 ld4f(const float *p) { return *reinterpret_ca
 // 4 s + g, scaled per channel by egl), from the LDS tiles sK, sQ, sKt.
 __device__ __forceinline__ void write_operands(const float *sK, const float *sQ, const float *sKt,
                                                const float *egl, float *kh, float *qh, float *kc, int tid) {
+  // egl == nullptr: sKt already holds (gamma_C / Gamma) . K~
   // kh, qh: lane -> (g = lane & 3, 4-output block sb = (lane >> 2) & 7),
   // two rows per wave pass
 #pragma unroll
@@ -89,7 +90,7 @@ __device__ __forceinline__ void write_operands(const float *sK, const float *sQ,
   for (int u = 0; u < 8; ++u) {
     const int idx = tid + 256 * u, kr = idx & (KP - 1), blk = idx >> 7;  // blk = 16-output block
     const int g = blk >> 2, s0 = 4 * (blk & 3);
-    const float sc = egl[kr];
+    const float sc = egl ? egl[kr] : 1.0f;
     floatx4 x;
 #pragma unroll
     for (int t = 0; t < 4; ++t) x[t] = sKt[(4 * (s0 + t) + g) * LP + kr] * sc;
@@ -97,8 +98,58 @@ __device__ __forceinline__ void write_operands(const float *sK, const float *sQ,
   }
 }
 
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi): 8 values as two bf16x8
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    hi[e] = to_bf16(x[e]);
+    lo[e] = to_bf16(x[e] - to_f32(hi[e]));
+  }
+}
+
+// The same operands as bf16 hi/lo pairs for the bf16 sweep, rows in natural
+// order (a 16x16x32 MFMA lane reads 8 consecutive contraction indices): in
+// each chunk slab the hi half comes first, the lo half after it.  Also TB
+// (= T diag(beta)) and M.
+__device__ __forceinline__ void write_operands_hilo(const float *sK, const float *sQ, const float *sKt,
+                                                    const float *egl, float *kh, float *qh, float *kc,
+                                                    int tid) {
+  bf16 *khb = reinterpret_cast<bf16 *>(kh), *qhb = reinterpret_cast<bf16 *>(qh);
+  bf16 *kcb = reinterpret_cast<bf16 *>(kc);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = tid + 256 * u, row = idx >> 4, c0 = (idx & 15) * 8;
+    float x[8], y[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      x[t] = sK[row * LP + c0 + t];
+      y[t] = sQ[row * LP + c0 + t];
+    }
+    bf16x8 h, lo;
+    split8(x, h, lo);
+    *reinterpret_cast<bf16x8 *>(khb + row * KP + c0) = h;
+    *reinterpret_cast<bf16x8 *>(khb + KC * KP + row * KP + c0) = lo;
+    split8(y, h, lo);
+    *reinterpret_cast<bf16x8 *>(qhb + row * KP + c0) = h;
+    *reinterpret_cast<bf16x8 *>(qhb + KC * KP + row * KP + c0) = lo;
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = tid + 256 * u, kr = idx & (KP - 1), j0 = (idx >> 7) * 8;
+    const float sc = egl ? egl[kr] : 1.0f;
+    float x[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) x[t] = sKt[(j0 + t) * LP + kr] * sc;
+    bf16x8 h, lo;
+    split8(x, h, lo);
+    *reinterpret_cast<bf16x8 *>(kcb + kr * KC + j0) = h;
+    *reinterpret_cast<bf16x8 *>(kcb + KC * KP + kr * KC + j0) = lo;
+  }
+}
+
 template <typename TIn, bool RES, bool GATED>
 __global__ __launch_bounds__(256) void kda_intra_kernel(KdaArgs a, int64_t N) {
+  constexpr bool HILO = sizeof(TIn) == 2;  // bf16 inputs: the sweep takes hi/lo pairs
   extern __shared__ float sm[];
   float *sK = sm, *sKt = sK + KC * LP, *sQ = sKt + KC * LP, *sG = sQ + KC * LP;
   __shared__ float sBeta[KC], sGL[KP], sEGL[KP];
@@ -208,7 +259,10 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(KdaArgs a, int64_t N) {
     __syncthreads();
     // outputs of the scaled operands (k~ e^{G_L - G} = (k~ e^-G) e^{G_L}),
     // four consecutive outputs per 16-byte store
-    write_operands(sK, sQ, sKt, sEGL, kh, qh, kc, tid);
+    if constexpr (HILO)
+      write_operands_hilo(sK, sQ, sKt, sEGL, kh, qh, kc, tid);
+    else
+      write_operands(sK, sQ, sKt, sEGL, kh, qh, kc, tid);
     // ---- A and M on the matrix cores, lower 16x16 blocks (I >= J)
     for (int e = tid; e < KC * KC; e += 256) {  // upper blocks are zero
       const int i = e >> 6, j = e & 63;
@@ -258,14 +312,20 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(KdaArgs a, int64_t N) {
         vm[u] = smq;
       }
     }
+    __syncthreads();  // every pair is read: scale the operands in place
     for (int e = tid; e < KC * KP; e += 256) {
-      const int row = e >> 7, p = e & (KP - 1), c = 4 * (p & 31) + (p >> 5);
-      const float eg = expf(sG[row * LP + c]);
-      kh[e] = sK[row * LP + c] * eg;
-      qh[e] = sQ[row * LP + c] * eg;
-      const int kr = e >> 6, q = e & 63, j = 4 * (q & 15) + (q >> 4);
-      kc[e] = sKt[j * LP + kr] * expf(sGL[kr] - sG[j * LP + kr]);
+      const int row = e >> 7, c = e & (KP - 1);
+      const float gg = sG[row * LP + c];
+      const float eg = expf(gg);
+      sK[row * LP + c] *= eg;
+      sQ[row * LP + c] *= eg;
+      sKt[row * LP + c] *= expf(sGL[c] - gg);
     }
+    __syncthreads();
+    if constexpr (HILO)
+      write_operands_hilo(sK, sQ, sKt, nullptr, kh, qh, kc, tid);
+    else
+      write_operands(sK, sQ, sKt, nullptr, kh, qh, kc, tid);
     __syncthreads();  // G is dead: its space takes A and M
     for (int e = tid; e < KC * KC; e += 256) {
       const int i = e >> 6, j = e & 63;
@@ -332,10 +392,32 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(KdaArgs a, int64_t N) {
     __syncthreads();
   }
   // ---- TB = T diag(beta) and M, rows permuted for the sweep's A operands
-  for (int e = tid; e < KC * KC; e += 256) {
-    const int i = e >> 6, q = e & 63, j = 4 * (q & 15) + (q >> 4);
-    tb[e] = sT[i * AP + j] * sBeta[j];
-    mq[e] = sM[i * AP + j];
+  //      (fp32) or as natural-order hi/lo pairs (bf16)
+  if constexpr (HILO) {
+    bf16 *tbb = reinterpret_cast<bf16 *>(tb), *mqb = reinterpret_cast<bf16 *>(mq);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + 256 * u, i = idx >> 3, j0 = (idx & 7) * 8;
+      float x[8], y[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        x[t] = sT[i * AP + j0 + t] * sBeta[j0 + t];
+        y[t] = sM[i * AP + j0 + t];
+      }
+      bf16x8 h, lo;
+      split8(x, h, lo);
+      *reinterpret_cast<bf16x8 *>(tbb + i * KC + j0) = h;
+      *reinterpret_cast<bf16x8 *>(tbb + KC * KC + i * KC + j0) = lo;
+      split8(y, h, lo);
+      *reinterpret_cast<bf16x8 *>(mqb + i * KC + j0) = h;
+      *reinterpret_cast<bf16x8 *>(mqb + KC * KC + i * KC + j0) = lo;
+    }
+  } else {
+    for (int e = tid; e < KC * KC; e += 256) {
+      const int i = e >> 6, q = e & 63, j = 4 * (q & 15) + (q >> 4);
+      tb[e] = sT[i * AP + j] * sBeta[j];
+      mq[e] = sM[i * AP + j];
+    }
   }
 }
 
@@ -535,6 +617,226 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(KdaArgs a, int64_t N, int 
   }
 }
 
+__device__ __forceinline__ floatx4 mfma_bf16(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// c += (ah + al)(bh + bl) without the al bl term (relative error ~2^-16)
+__device__ __forceinline__ floatx4 mfma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, floatx4 c) {
+  c = mfma_bf16(ah, bh, c);
+  c = mfma_bf16(ah, bl, c);
+  return mfma_bf16(al, bh, c);
+}
+// 8 consecutive fp32 values from LDS as a hi/lo bf16 pair
+__device__ __forceinline__ void lds_split8(const float *p, bf16x8 &hi, bf16x8 &lo) {
+  const floatx4 u = *reinterpret_cast<const floatx4 *>(p), v = *reinterpret_cast<const floatx4 *>(p + 4);
+  const float x[8] = {u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
+  split8(x, hi, lo);
+}
+__device__ __forceinline__ bf16x8 neg8(bf16x8 x) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(bf16x8, __builtin_bit_cast(u4, x) ^ 0x80008000u);
+}
+
+// The bf16 sweep: the same chunk algebra as kda_seq_kernel with every product
+// on v_mfma_f32_16x16x32_bf16 over hi/lo pairs (A from the workspace, B split
+// from the fp32 LDS tiles as it is read).  The LDS tiles are stored
+// transposed (value column major) so that a lane's 8 contraction indices are
+// contiguous; pitches of 4 (mod 64) floats keep a quarter-wave's 16-byte
+// accesses on distinct banks.
+__global__ __launch_bounds__(256) void kda_seq_hilo_kernel(KdaArgs a, int64_t N, int ntile) {
+  constexpr int NCB = 2, KVT = 32, PS = KP + 4, PX = KC + 4;
+  __shared__ float sSt[KVT * PS];  // S^T: [value column][key row]
+  __shared__ float sXt[KVT * PX];  // X^T: [value column][token]
+  __shared__ float sDt[KVT * PX];  // D^T
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, l16 = l & 15, g = l >> 4;
+  const int64_t H = a.H, T = a.T, V = a.V, BH = a.B * a.H;
+  const int K = (int)a.K;
+  const int64_t bid = blockIdx.x;
+  int64_t bh, vt;
+  if (BH % 8 == 0) {
+    const int64_t slot = bid >> 3;
+    bh = (slot / ntile) * 8 + (bid & 7);
+    vt = slot % ntile;
+  } else {
+    bh = bid / ntile;
+    vt = bid % ntile;
+  }
+  const int64_t b = bh / H, h = bh - b * H;
+  const int64_t v0 = vt * KVT;
+  const bf16 *vp = static_cast<const bf16 *>(a.v);
+  bf16 *op = static_cast<bf16 *>(a.o);
+
+  floatx4 Sr[2][NCB];  // key rows 32 w + 16 rb + 4 g + i, value column 16 cb + l16
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int64_t col = v0 + 16 * cb + l16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kr = 32 * w + 16 * rb + 4 * g + i;
+        Sr[rb][cb][i] = a.S0 && kr < K && col < V ? a.S0[(bh * K + kr) * V + col] : 0.0f;
+      }
+      *reinterpret_cast<floatx4 *>(sSt + (16 * cb + l16) * PS + 32 * w + 16 * rb + 4 * g) = Sr[rb][cb];
+    }
+
+  bf16x8 kah[4], kal[4], qah[4], qal[4], tah[2], tal[2], mah[2], mal[2], kch[2][2], kcl[2][2];
+  floatx4 gc4[2];
+  float vv[NCB][4];
+  auto load_kq = [&](int64_t n) {
+    const int64_t cb0 = bh * N + n;
+    const bf16 *pk = reinterpret_cast<const bf16 *>(a.kh + cb0 * (KC * KP)) + (16 * w + l16) * KP + 8 * g;
+    const bf16 *pq = reinterpret_cast<const bf16 *>(a.qh + cb0 * (KC * KP)) + (16 * w + l16) * KP + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      kah[s] = *reinterpret_cast<const bf16x8 *>(pk + 32 * s);
+      kal[s] = *reinterpret_cast<const bf16x8 *>(pk + KC * KP + 32 * s);
+      qah[s] = *reinterpret_cast<const bf16x8 *>(pq + 32 * s);
+      qal[s] = *reinterpret_cast<const bf16x8 *>(pq + KC * KP + 32 * s);
+    }
+    const int64_t t0 = n * KC;
+    const int L = (int)(T - t0 < KC ? T - t0 : KC);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * w + 4 * g + i, rr = row < L ? row : L - 1;
+        const int64_t col = v0 + 16 * cb + l16, cc = col < V ? col : V - 1;
+        vv[cb][i] = to_f32(vp[((b * T + t0 + rr) * H + h) * V + cc]);
+      }
+  };
+  auto load_tm = [&](int64_t n) {
+    const int64_t cb0 = bh * N + n;
+    const bf16 *pt = reinterpret_cast<const bf16 *>(a.tb + cb0 * (KC * KC)) + (16 * w + l16) * KC + 8 * g;
+    const bf16 *pm = reinterpret_cast<const bf16 *>(a.mq + cb0 * (KC * KC)) + (16 * w + l16) * KC + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      tah[s] = *reinterpret_cast<const bf16x8 *>(pt + 32 * s);
+      tal[s] = *reinterpret_cast<const bf16x8 *>(pt + KC * KC + 32 * s);
+      mah[s] = *reinterpret_cast<const bf16x8 *>(pm + 32 * s);
+      mal[s] = *reinterpret_cast<const bf16x8 *>(pm + KC * KC + 32 * s);
+    }
+  };
+  auto load_kc = [&](int64_t n) {
+    const int64_t cb0 = bh * N + n;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const bf16 *pc = reinterpret_cast<const bf16 *>(a.kc + cb0 * (KC * KP)) + (32 * w + 16 * rb + l16) * KC + 8 * g;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        kch[rb][s] = *reinterpret_cast<const bf16x8 *>(pc + 32 * s);
+        kcl[rb][s] = *reinterpret_cast<const bf16x8 *>(pc + KC * KP + 32 * s);
+      }
+      gc4[rb] = *reinterpret_cast<const floatx4 *>(a.gc + cb0 * KP + 32 * w + 16 * rb + 4 * g);
+    }
+  };
+  if (N > 0) {
+    load_kq(0);
+    load_tm(0);
+    load_kc(0);
+  }
+
+  for (int64_t n = 0; n < N; ++n) {
+    const int64_t t0 = n * KC;
+    const int L = (int)(T - t0 < KC ? T - t0 : KC);
+    const int64_t nn = n + 1 < N ? n + 1 : n;
+    floatx4 accX[NCB], accP[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * w + 4 * g + i;
+        const int64_t col = v0 + 16 * cb + l16;
+        accX[cb][i] = row < L && col < V ? vv[cb][i] : 0.0f;
+        accP[cb][i] = 0.0f;
+      }
+    __syncthreads();  // sSt holds the chunk's boundary state
+    // (a) X = V - (Gamma . K) S and P = (Gamma . Q) S, rows 16 w ..
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 nh = neg8(kah[s]), nl = neg8(kal[s]);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        bf16x8 bh_, bl_;
+        lds_split8(sSt + (16 * cb + l16) * PS + 32 * s + 8 * g, bh_, bl_);
+        accX[cb] = mfma3(nh, nl, bh_, bl_, accX[cb]);
+        accP[cb] = mfma3(qah[s], qal[s], bh_, bl_, accP[cb]);
+      }
+    }
+    load_kq(nn);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      *reinterpret_cast<floatx4 *>(sXt + (16 * cb + l16) * PX + 16 * w + 4 * g) = accX[cb];
+    __syncthreads();
+    // (b) D = TB X (TB lower triangular: tokens up to 16 w + 15)
+    floatx4 accD[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) accD[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (s == 0 || w >= 2) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          bf16x8 bh_, bl_;
+          lds_split8(sXt + (16 * cb + l16) * PX + 32 * s + 8 * g, bh_, bl_);
+          accD[cb] = mfma3(tah[s], tal[s], bh_, bl_, accD[cb]);
+        }
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      *reinterpret_cast<floatx4 *>(sDt + (16 * cb + l16) * PX + 16 * w + 4 * g) = accD[cb];
+    __syncthreads();
+    // D as B operand, split once for (c) and (d)
+    bf16x8 dh[2][NCB], dl[2][NCB];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) lds_split8(sDt + (16 * cb + l16) * PX + 32 * s + 8 * g, dh[s][cb], dl[s][cb]);
+    // (c) O = P + M D
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (s == 0 || w >= 2) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) accP[cb] = mfma3(mah[s], mal[s], dh[s][cb], dl[s][cb], accP[cb]);
+      }
+    }
+    load_tm(nn);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * w + 4 * g + i;
+        const int64_t col = v0 + 16 * cb + l16;
+        if (row < L && col < V) op[((b * T + t0 + row) * H + h) * V + col] = to_bf16(accP[cb][i]);
+      }
+    // (d) S = Diag(gamma_C) S + Kc^T D for this wave's key rows
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Sr[rb][cb][i] *= gc4[rb][i];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) Sr[rb][cb] = mfma3(kch[rb][s], kcl[rb][s], dh[s][cb], dl[s][cb], Sr[rb][cb]);
+        *reinterpret_cast<floatx4 *>(sSt + (16 * cb + l16) * PS + 32 * w + 16 * rb + 4 * g) = Sr[rb][cb];
+      }
+    load_kc(nn);
+  }
+  if (a.S_out) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kr = 32 * w + 16 * rb + 4 * g + i;
+          const int64_t col = v0 + 16 * cb + l16;
+          if (kr < K && col < V) a.S_out[(bh * K + kr) * V + col] = Sr[rb][cb][i];
+        }
+  }
+}
+
 constexpr size_t INTRA_LDS = (size_t)4 * KC * LP * sizeof(float);
 
 template <typename TIn, bool RES>
@@ -565,7 +867,12 @@ hipError_t launch_typed(const KdaArgs &a, hipStream_t s) {
   constexpr int NCB = 2;
   const int ntile = (int)((a.V + 16 * NCB - 1) / (16 * NCB));
   dim3 grid((unsigned)(a.B * a.H * ntile)), block(256);
-  hipLaunchKernelGGL((kda_seq_kernel<TIn, NCB>), grid, block, 0, s, a, N, ntile);
+  if constexpr (sizeof(TIn) == 2) {
+    // bf16 inputs: hi/lo pairs on the bf16 matrix cores
+    hipLaunchKernelGGL(kda_seq_hilo_kernel, grid, block, 0, s, a, N, ntile);
+  } else {
+    hipLaunchKernelGGL((kda_seq_kernel<TIn, NCB>), grid, block, 0, s, a, N, ntile);
+  }
   prof_mark(s, "kda_seq_kernel");
   return hipGetLastError();
 }
