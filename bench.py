@@ -100,10 +100,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_work(name, K, V, C, apf, gated, elem=2):
-    """(algorithmic bytes, flops) per token-head of one kernel."""
-    r = 4 if apf else 0
+def kernel_work(name, K, V, C, apf, gated, elem=2, rvec=False):
+    """(algorithmic bytes, flops) per token-head of one kernel (rvec: the
+    retention is a [K] row per token)."""
+    r = (4 * K if rvec else 4) if apf else 0
     g = 4 if gated else 0
+    if name == "precond_scan_kernel":
+        # token-by-token phase 1 inside osdn_fwd: reads k, beta, r, writes the
+        # bf16 write-key residual
+        return elem * K + 4 + r + 2 * K, 0
     if name == "scan_prep_kernel":
         return elem * K + 4 + r, 0
     if name == "scan_solve_kernel":
@@ -280,6 +285,7 @@ def main(argv=None):
     V = inp["v"].shape[-1]
     C = p["chunk"]
     apf, gated = inp["r"] is not None, inp["alpha"] is not None
+    rvec = apf and inp["r"].ndim == 4
     tdt = torch.bfloat16 if p["dtype"] == "bf16" else torch.float32
     code = osdn.BF16 if p["dtype"] == "bf16" else osdn.F32
     elem = 2 if p["dtype"] == "bf16" else 4
@@ -351,7 +357,7 @@ def main(argv=None):
     kernels = {}
     for name, vals in per.items():
         ms = float(np.mean(vals))
-        nbytes, flops = kernel_work(name, K, V, C, apf, gated, elem)
+        nbytes, flops = kernel_work(name, K, V, C, apf, gated, elem, rvec)
         gbs = nbytes * nth / (ms * 1e-3) / 1e9 if ms > 0 else None
         ent = {"ms": ms, "launches_per_step": len(vals) / nsteps, "ms_median": float(np.median(vals)),
                "bound": "hbm", "bytes_per_token_head": nbytes, "GB/s": gbs,
@@ -389,7 +395,7 @@ def main(argv=None):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": p["dtype"],
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": V,
-                   "chunk": C, "apf": apf, "gated": gated, "seed": spec["seed"],
+                   "chunk": C, "apf": apf, "vector_retention": rvec, "gated": gated, "seed": spec["seed"],
                    "input_copies": len(sets)},
         "roofline": roofline, "cpu_baseline": cpu,
         "phases": {"precond_scan_ms": p1, "chunk_fwd_ms": p2,

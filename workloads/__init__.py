@@ -60,6 +60,10 @@ WORKLOADS = {
     # Appendix F): 65,536 tokens, sequence lengths from varlen_lengths
     "varlen_1p3b_65k": dict(B=1, T=65536, H=16, K=128, V=128, dtype="bf16", chunk=64,
                             seed=8, apf=True),
+    # the 1.3B-shaped layer with vector retention (one retention per key
+    # coordinate, Proposition A.3)
+    "1p3b_rvec": dict(B=4, T=4096, H=16, K=128, V=128, dtype="bf16", chunk=64,
+                      seed=10, apf=True, r_vec=True),
     # OSKDA on the 340M KDA-shaped layer (8 heads of 128), APF retention,
     # channel-wise decay
     "kda_340m_apf": dict(B=8, T=2048, H=8, K=128, V=128, dtype="bf16", chunk=64, seed=9,
