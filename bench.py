@@ -112,7 +112,8 @@ def kernel_work(name, K, V, C, apf, gated, elem=2, rvec=False):
     if name == "scan_prep_kernel":
         return elem * K + 4 + r, 0
     if name == "scan_solve_kernel":
-        return 4 + 4 + r, 0
+        # vector retention rows are read only for the chunks it sweeps
+        return 4 + 4 + (0 if rvec else r), 0
     if name == "scan_emit_kernel":
         return 2 * elem * K + 4 + r, 0
     if name == "chunk_tinv_kernel":

@@ -82,9 +82,10 @@ typedef enum {
  *               only (Appendix B); the memory write always uses beta.
  *   r_per_key   0: r is [B,T,H], one retention per token and head (Eq.(7));
  *               1: r is [B,T,H,K], the vector retention diag(r_t) of
- *               Appendix A.5, Proposition A.3 (phase 1 then runs token by
- *               token; osdn_fwd_varlen, osdn_decode and osdn_bwd return
- *               OSDN_EUNSUPPORTED for it).  Ignored when r is NULL.
+ *               Appendix A.5, Proposition A.3 (the chunked phase-1 sweep for
+ *               K <= 128, token by token above; osdn_decode and osdn_bwd,
+ *               and osdn_fwd_varlen above K = 128, return OSDN_EUNSUPPORTED
+ *               for it).  Ignored when r is NULL.
  */
 typedef struct osdn_desc {
   int64_t B, T, H, K, V;

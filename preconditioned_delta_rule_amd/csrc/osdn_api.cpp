@@ -282,7 +282,8 @@ osdn_status osdn_precond_scan(const osdn_desc *d, const void *k, const float *be
   if (k_tilde && k_tilde == k) return fail(OSDN_EINVAL, "k_tilde must not alias k");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const osdn::ScanArgs sa = scan_args(d, k, beta, r, d1, k_tilde, d_out);
-  if (!workspace || (d->r_per_key && r)) {
+  // vector retention above K = 128 has only the token-by-token kernel
+  if (!workspace || (d->r_per_key && r && d->K > 128)) {
     OSDN_TRY(run_scan(d, sa, s));
     return ok();
   }
@@ -362,7 +363,9 @@ static osdn_status fwd_impl(const osdn_desc *d, const int64_t *cu, const void *q
   OSDN_TRY(check_ptr(d_out, "d_out", false));
   OSDN_TRY(check_ptr(k_tilde_out, "k_tilde_out", false));
   const bool rvec = d->r_per_key && r;
-  if (rvec && cu) return fail(OSDN_EUNSUPPORTED, "vector retention is not supported for packed sequences");
+  const bool rvec_tok = rvec && d->K > 128;  // token-by-token phase 1
+  if (rvec_tok && cu)
+    return fail(OSDN_EUNSUPPORTED, "vector retention with K > 128 is not supported for packed sequences");
   hipStream_t s = static_cast<hipStream_t>(stream);
   osdn::ScanArgs sa = scan_args(d, k, beta, r, d1, k_tilde_out, d_out);
   osdn::ChunkArgs ca = chunk_args(d, q, k, k_tilde_out, v, beta, alpha, S0, o, S_out);
@@ -395,7 +398,7 @@ static osdn_status fwd_impl(const osdn_desc *d, const int64_t *cu, const void *q
   // bf16 on the matrix cores without k_tilde_out: the residual is formed by
   // the first phase-2 kernel, which replays d itself (one pass over k fewer)
   const bool fold = res && cw && !k_tilde_out && !rvec;
-  if (rvec)  // vector retention: the token-by-token sweep writes the keys
+  if (rvec_tok)  // vector retention above K = 128: the token-by-token sweep writes the keys
     OSDN_TRY(run_scan(d, sa, s));
   else
     OSDN_TRY(hip_status(osdn::launch_precond_scan_chunked(sa, sw, d->dtype == OSDN_BF16, s, !fold),
@@ -648,7 +651,7 @@ osdn_status osdn_kda_fwd(const osdn_desc *d, const void *q, const void *k, const
     ka.kt = ws;
   }
   const size_t scan_bytes = osdn::scan_work_bytes(d->B, d->T, d->H, d->K);
-  if (d->r_per_key && r)
+  if (d->r_per_key && r && d->K > 128)
     OSDN_TRY(run_scan(d, sa, s));
   else
     OSDN_TRY(hip_status(osdn::launch_precond_scan_chunked(

@@ -30,6 +30,11 @@
 //  emit  (one wave per (b,h,chunk)): replays d_{t+1} = clip(r_t d_t + c_t s_t)
 //        from the chunk's start and writes k~_t = d_t (.) k_t (and/or the
 //        bf16 residual (d_t - 1) (.) k_t).
+// With vector retention (diag(r_t), Proposition A.3 of the appendix; the RV
+// instantiations, K <= 128) prep marks a token with its largest retention
+// (max_i r_{t,i} d_min + c_t max_i s_{t,i} <= d_min is sufficient), solve
+// skips pinned runs as above and sweeps every other chunk token by token
+// with the chunk's retention rows in LDS, and emit replays per coordinate.
 #include "kernels.h"
 #include "profile.h"
 #include "scan_common.h"
@@ -61,7 +66,7 @@ __device__ __forceinline__ void lds_put(TIn *p, const Row<TIn, EPL, FULL> &r) {
 }
 
 // ---------------------------------------------------------------- prep
-template <typename TIn, int EPL, bool FULL, bool HAS_R, bool VL>
+template <typename TIn, int EPL, bool FULL, bool HAS_R, bool VL, bool RV = false>
 __global__ __launch_bounds__(64) void scan_prep_kernel(ScanArgs a, ScanWork wk, int64_t N) {
   const int lane = threadIdx.x;
   const int64_t seq = blockIdx.x / N, n = blockIdx.x % N;
@@ -76,10 +81,27 @@ __global__ __launch_bounds__(64) void scan_prep_kernel(ScanArgs a, ScanWork wk, 
   const int64_t stride = H * K;
   const int64_t gi = (tb + t0 + (tok ? lane : 0)) * H + h;
   const float bt = a.beta[gi];
-  const float rt = HAS_R ? a.r[gi] : 1.0f;
+  float rt = HAS_R ? a.r[gi] : 1.0f;
   Row<TIn, EPL, FULL> rows[CH];
 #pragma unroll
   for (int u = 0; u < CH; ++u) rows[u].load(kp + (u < L ? u : L - 1) * stride, lane, K);
+  if constexpr (RV) {
+    // the token's largest retention (a sufficient bound for the pinned test)
+    const float *rp = a.r + ((tb + t0) * H + h) * K;
+    float rm[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      Row<float, EPL, FULL> rr;
+      rr.load(rp + (u < L ? u : L - 1) * stride, lane, K);
+      float rv[EPL];
+      rr.get(rv);
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) m = fmaxf(m, rv[e]);
+      rm[u] = m;
+    }
+    rt = reduce_scatter64<true>(rm, lane);
+  }
   float sn[CH], sm[CH];
 #pragma unroll
   for (int u = 0; u < CH; ++u) {
@@ -225,7 +247,7 @@ constexpr size_t solve_lds_bytes() {
          (size_t)CH * 16;
 }
 
-template <typename TIn, int EPL, bool FULL, bool HAS_R, bool PF, bool VL>
+template <typename TIn, int EPL, bool FULL, bool HAS_R, bool PF, bool VL, bool RV = false>
 __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk, int64_t N) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int RP = 64 * EPL;      // row pitch of sR (elements)
@@ -234,6 +256,7 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
   bf16 *sS = reinterpret_cast<bf16 *>(smem + (size_t)CH * RP * sizeof(TIn));
   float *sG = reinterpret_cast<float *>(smem + (size_t)CH * RP * sizeof(TIn) + (size_t)CH * SP * 2);
   floatx4 *sTok = reinterpret_cast<floatx4 *>(sG + CH * (CH + 1));
+  float *sRv = reinterpret_cast<float *>(sTok + CH);  // RV: the chunk's retention rows [CH][RP]
 
   const int lane = threadIdx.x;
   const int64_t seq = blockIdx.x;
@@ -322,6 +345,18 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
 #pragma unroll
         for (int u = 0; u < GL; ++u) lds_put<TIn, EPL, FULL>(sR + (u0 + u) * RP + lane * EPL, tmp[u]);
       }
+      if constexpr (RV) {
+        const float *rp = a.r + ((tb + t0) * H + h) * K;
+        constexpr int GV = CH / Row<float, EPL, FULL>::WORDS;
+#pragma unroll
+        for (int u0 = 0; u0 < CH; u0 += GV) {
+          Row<float, EPL, FULL> tmp[GV];
+#pragma unroll
+          for (int u = 0; u < GV; ++u) tmp[u].load(rp + (u0 + u < L ? u0 + u : L - 1) * stride, lane, K);
+#pragma unroll
+          for (int u = 0; u < GV; ++u) lds_put<float, EPL, FULL>(sRv + (u0 + u) * RP + lane * EPL, tmp[u]);
+        }
+      }
     }
     if (!tok) {
       bt = 0.0f;
@@ -358,7 +393,7 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
     // and R_L >= 1/4 keeps the 1/R_t factors from costing more than two bits;
     // otherwise a chunk with free coordinates goes token by token.
     float Rn = 1.0f, Rt = 1.0f;
-    bool try_closed = true;
+    bool try_closed = !RV;  // vector retention: no closed form, token by token
     if constexpr (HAS_R) {
       if (any_free) {
         const float lr = logf(rt);
@@ -505,11 +540,18 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
         }
         const float align = wave_sum(pa);
         const float c = fmaf(-lane_bcast(eb, u), align, lane_bcast(ea, u));
-        const float ru = lane_bcast(rt, u);
+        float ru[EPL];
+        if constexpr (RV) {
+          lds_get<float, EPL>(sRv + u * RP + lane * EPL, ru);
+        } else {
+          const float rb = lane_bcast(rt, u);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) ru[e] = rb;
+        }
         cst = lane == u ? c : cst;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-          float xx = fmaf(c, s[e], ru * d[e]);
+          float xx = fmaf(c, s[e], ru[e] * d[e]);
           if (clamp) xx = fminf(fmaxf(xx, dmin), dmax);
           d[e] = valid[e] ? xx : 0.0f;
         }
@@ -584,10 +626,10 @@ __device__ __forceinline__ void store_vec(T *p, int lane, int64_t K, const typen
 // Rows of one chunk: the write keys of a group of rows are computed into
 // registers and then stored together, so that the stores never sit in the
 // memory counter ahead of row loads that are still awaited.
-template <typename TIn, int EPL, bool FULL, bool WKT, bool WRES, bool WHOLE>
+template <typename TIn, int EPL, bool FULL, bool WKT, bool WRES, bool WHOLE, bool RV = false>
 __device__ __forceinline__ void emit_rows(const Row<TIn, EPL, FULL> (&rows)[CH], float (&d)[EPL], float cv, float rv,
                                           float lo, float hi, int L, TIn *op, bf16 *rp, int64_t stride, int lane,
-                                          int64_t K) {
+                                          int64_t K, const Row<float, EPL, FULL> *rvrows = nullptr) {
   typedef typename RowVec<TIn, EPL>::type VK;
   typedef typename RowVec<bf16, EPL>::type VR;
   constexpr int OUTW = (WKT ? (int)sizeof(VK) : 0) + (WRES ? (int)sizeof(VR) : 0);
@@ -614,9 +656,17 @@ __device__ __forceinline__ void emit_rows(const Row<TIn, EPL, FULL> (&rows)[CH],
           for (int e = 0; e < EPL; ++e) w[e] = (d[e] - 1.0f) * k[e];  // d - 1 is exact on [0.5, 2]
           ores[i] = pack_row<bf16, EPL>(w);
         }
-        const float c = lane_bcast(cv, u), r = lane_bcast(rv, u);
+        const float c = lane_bcast(cv, u);
+        float r[EPL];
+        if constexpr (RV) {
+          rvrows[u].get(r);
+        } else {
+          const float rb = lane_bcast(rv, u);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) d[e] = fminf(fmaxf(fmaf(c, k[e] * k[e], r * d[e]), lo), hi);
+          for (int e = 0; e < EPL; ++e) r[e] = rb;
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) d[e] = fminf(fmaxf(fmaf(c, k[e] * k[e], r[e] * d[e]), lo), hi);
       }
     }
 #pragma unroll
@@ -630,7 +680,7 @@ __device__ __forceinline__ void emit_rows(const Row<TIn, EPL, FULL> (&rows)[CH],
   }
 }
 
-template <typename TIn, int EPL, bool FULL, bool HAS_R, bool WKT, bool WRES, bool VL>
+template <typename TIn, int EPL, bool FULL, bool HAS_R, bool WKT, bool WRES, bool VL, bool RV = false>
 __global__ __launch_bounds__(64) void scan_emit_kernel(ScanArgs a, ScanWork wk, int64_t N) {
   const int lane = threadIdx.x;
   const int64_t seq = blockIdx.x / N, n = blockIdx.x % N;
@@ -660,6 +710,12 @@ __global__ __launch_bounds__(64) void scan_emit_kernel(ScanArgs a, ScanWork wk, 
   Row<TIn, EPL, FULL> rows[CH];
 #pragma unroll
   for (int u = 0; u < CH; ++u) rows[u].load(kp + (u < L ? u : L - 1) * stride, lane, K);
+  Row<float, EPL, FULL> rvrows[RV ? CH : 1];
+  if constexpr (RV) {
+    const float *rp0 = a.r + row0;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) rvrows[u].load(rp0 + (u < L ? u : L - 1) * stride, lane, K);
+  }
   if (pinned) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) d[e] = a.d_min;
@@ -669,29 +725,32 @@ __global__ __launch_bounds__(64) void scan_emit_kernel(ScanArgs a, ScanWork wk, 
   TIn *op = WKT ? static_cast<TIn *>(a.k_tilde) + row0 : nullptr;
   bf16 *rp = WRES ? static_cast<bf16 *>(a.kt_res) + row0 : nullptr;
   if (L == CH)
-    emit_rows<TIn, EPL, FULL, WKT, WRES, true>(rows, d, cv, rv, lo, hi, L, op, rp, stride, lane, K);
+    emit_rows<TIn, EPL, FULL, WKT, WRES, true, RV>(rows, d, cv, rv, lo, hi, L, op, rp, stride, lane, K, rvrows);
   else
-    emit_rows<TIn, EPL, FULL, WKT, WRES, false>(rows, d, cv, rv, lo, hi, L, op, rp, stride, lane, K);
+    emit_rows<TIn, EPL, FULL, WKT, WRES, false, RV>(rows, d, cv, rv, lo, hi, L, op, rp, stride, lane, K, rvrows);
 }
 
-template <typename TIn, int EPL, bool FULL, bool HAS_R, bool VL>
+template <typename TIn, int EPL, bool FULL, bool HAS_R, bool VL, bool RV>
 void launch_emit(const ScanArgs &a, const ScanWork &w, int64_t N, hipStream_t s) {
   dim3 grid((unsigned)(a.B * a.H * N)), block(64);
   if (a.k_tilde && a.kt_res)
-    hipLaunchKernelGGL((scan_emit_kernel<TIn, EPL, FULL, HAS_R, true, true, VL>), grid, block, 0, s, a, w, N);
+    hipLaunchKernelGGL((scan_emit_kernel<TIn, EPL, FULL, HAS_R, true, true, VL, RV>), grid, block, 0, s, a, w, N);
   else if (a.kt_res)
-    hipLaunchKernelGGL((scan_emit_kernel<TIn, EPL, FULL, HAS_R, false, true, VL>), grid, block, 0, s, a, w, N);
+    hipLaunchKernelGGL((scan_emit_kernel<TIn, EPL, FULL, HAS_R, false, true, VL, RV>), grid, block, 0, s, a, w, N);
   else
-    hipLaunchKernelGGL((scan_emit_kernel<TIn, EPL, FULL, HAS_R, true, false, VL>), grid, block, 0, s, a, w, N);
+    hipLaunchKernelGGL((scan_emit_kernel<TIn, EPL, FULL, HAS_R, true, false, VL, RV>), grid, block, 0, s, a, w, N);
   prof_mark(s, "scan_emit_kernel");
 }
 
-template <typename TIn, int EPL, bool FULL, bool HAS_R, bool VL>
+template <typename TIn, int EPL, bool FULL, bool HAS_R, bool VL, bool RV = false>
 hipError_t launch_all(const ScanArgs &a, const ScanWork &w, hipStream_t s, bool emit) {
   const int64_t N = (a.T + CH - 1) / CH;
   const int64_t nseq = a.B * a.H;
   if (N > 0) {
-    if (a.K == 128) {
+    if constexpr (RV) {
+      hipLaunchKernelGGL((scan_prep_kernel<TIn, EPL, FULL, false, VL, true>), dim3((unsigned)(nseq * N)), dim3(64),
+                         0, s, a, w, N);
+    } else if (a.K == 128) {
       hipLaunchKernelGGL((scan_prep128_kernel<TIn, HAS_R, VL>), dim3((unsigned)((nseq * N + 3) / 4)), dim3(256), 0, s,
                          a, w, N);
     } else {
@@ -700,20 +759,24 @@ hipError_t launch_all(const ScanArgs &a, const ScanWork &w, hipStream_t s, bool 
     }
     prof_mark(s, "scan_prep_kernel");
   }
-  constexpr bool PF = Row<TIn, EPL, FULL>::WORDS <= 2;
-  constexpr size_t shm = solve_lds_bytes<TIn, EPL>();
+  constexpr bool PF = !RV && Row<TIn, EPL, FULL>::WORDS <= 2;
+  constexpr size_t shm = solve_lds_bytes<TIn, EPL>() + (RV ? (size_t)CH * 64 * EPL * 4 : 0);
   static_assert(shm <= 160 * 1024, "solve kernel LDS");
-  auto kern = scan_solve_kernel<TIn, EPL, FULL, HAS_R, PF, VL>;
+  auto kern = scan_solve_kernel<TIn, EPL, FULL, HAS_R, PF, VL, RV>;
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)nseq), dim3(64), shm, s, a, w, N);
   prof_mark(s, "scan_solve_kernel");
-  if (N > 0 && emit) launch_emit<TIn, EPL, FULL, HAS_R, VL>(a, w, N, s);
+  if (N > 0 && emit) launch_emit<TIn, EPL, FULL, HAS_R, VL, RV>(a, w, N, s);
   return hipGetLastError();
 }
 
 template <typename TIn, int EPL, bool FULL, bool VL>
 hipError_t launch_r(const ScanArgs &a, const ScanWork &w, hipStream_t s, bool e) {
+  if (a.r && a.r_per_key) {
+    if constexpr (EPL <= 2) return launch_all<TIn, EPL, FULL, false, VL, true>(a, w, s, e);
+    return hipErrorInvalidValue;  // vector retention above K = 128 takes the token-by-token kernel
+  }
   return a.r ? launch_all<TIn, EPL, FULL, true, VL>(a, w, s, e) : launch_all<TIn, EPL, FULL, false, VL>(a, w, s, e);
 }
 

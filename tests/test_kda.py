@@ -181,10 +181,6 @@ def test_vector_retention_unsupported_paths():
     with pytest.raises(osdn.OsdnError) as e:
         osdn.decode(*args)
     assert e.value.status == osdn.EUNSUPPORTED
-    cu = torch.tensor([0, 8], dtype=torch.int64, device="cuda:0")
-    with pytest.raises(osdn.OsdnError) as e:
-        osdn.fwd_varlen(*args, cu_seqlens=cu)
-    assert e.value.status == osdn.EUNSUPPORTED
 
 
 def test_kda_full_size_sampled():

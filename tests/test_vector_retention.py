@@ -1,0 +1,109 @@
+"""GPU parity of vector retention (r [B,T,H,K], the diag(r_t) form of
+Appendix A.5 Proposition A.3) in phase 1: the chunked sweep (K <= 128) and the
+token-by-token kernel against the oracle, and through osdn_fwd on packed
+sequences.  Bars as for phase 1: d within 1e-5 relative; fp32 write keys
+within 1e-5, bf16 ones within one bf16 ulp of the fp64 value."""
+import numpy as np
+import pytest
+
+import oracle
+import preconditioned_delta_rule_amd as osdn
+from tests.helpers import F32_D, F32_KT, rel_err, to_dev, to_np, ulp_err
+from workloads import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    osdn.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def case(K, T=150, retention="apf", eta=0.003, clamp=True, seed=81, B=2, H=2):
+    inp = make_inputs(dict(B=B, T=T, H=H, K=K, V=16, seed=seed, apf=True, r_vec=True, eta=eta, clamp=clamp))
+    if retention == "near_one":
+        # retention close to 1 and a large step: d leaves d_min, chunks are swept
+        rng = np.random.default_rng(seed + 7)
+        inp["r"] = (1.0 - 0.02 * rng.random(inp["r"].shape)).astype(np.float32)
+    return inp
+
+
+CASES = {
+    "k16_apf": dict(K=16),
+    "k64_apf": dict(K=64, T=200),
+    "k100_apf": dict(K=100, T=130),
+    "k128_apf": dict(K=128, T=260),
+    "k128_near_one": dict(K=128, T=260, retention="near_one", eta=0.3),
+    "k33_near_one": dict(K=33, T=90, retention="near_one", eta=0.5),
+    "k128_no_clamp": dict(K=128, T=130, retention="near_one", eta=0.2, clamp=False),
+    "k256_token_kernel": dict(K=256, T=70),
+    "t1": dict(K=128, T=1),
+}
+
+
+def oracle_scan(inp, d1):
+    p = inp["params"]
+    return oracle.precond_scan(inp["k"], inp["beta"], inp["r"], d1, eta=p["eta"], d_min=p["d_min"],
+                               d_max=p["d_max"], clamp=p["clamp"], eps=p["eps"], beta_aware=p["beta_aware"])
+
+
+@pytest.mark.parametrize("chunked", [True, False], ids=["chunked", "token"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_vector_retention_phase1(name, dtype, chunked):
+    inp = case(**CASES[name])
+    p = inp["params"]
+    B, T, H, K = inp["k"].shape
+    d1 = np.random.default_rng(3).uniform(0.6, 1.9, (B, H, K)).astype(np.float32)
+    kt, d = osdn.precond_scan(to_dev(inp["k"], dtype), to_dev(inp["beta"], "f32"), to_dev(inp["r"], "f32"),
+                              to_dev(d1, "f32"), eta=p["eta"], d_min=p["d_min"], d_max=p["d_max"],
+                              clamp=p["clamp"], eps=p["eps"], beta_aware=p["beta_aware"], chunked=chunked)
+    torch.cuda.synchronize()
+    kin = inp["k"] if dtype == "f32" else to_np(to_dev(inp["k"], "bf16"))
+    ref_kt, ref_d = oracle_scan(dict(inp, k=kin), d1)
+    assert rel_err(to_np(d), ref_d) <= F32_D, name
+    if dtype == "f32":
+        assert rel_err(to_np(kt), ref_kt) <= F32_KT, name
+    else:
+        assert ulp_err(to_np(kt), ref_kt) <= 1.0, name
+
+
+def test_vector_retention_chunked_skips_pinned_chunks():
+    """APF-like retention keeps d on d_min: the chunked sweep takes most chunks
+    as pinned (counters), and agrees with the token-by-token kernel."""
+    inp = case(K=128, T=1024, B=1, H=4)
+    p = inp["params"]
+    k, beta, r = to_dev(inp["k"], "bf16"), to_dev(inp["beta"], "f32"), to_dev(inp["r"], "f32")
+    ws = torch.empty(osdn.precond_scan_workspace_bytes(1, 1024, 4, 128, osdn.BF16), dtype=torch.uint8,
+                     device="cuda:0")
+    kt1, d1 = osdn.precond_scan(k, beta, r, eta=p["eta"], workspace=ws)
+    kt2, d2 = osdn.precond_scan(k, beta, r, eta=p["eta"], chunked=False)
+    torch.cuda.synchronize()
+    cnt = osdn.scan_counters(ws, 1, 1024, 4, 128, osdn.BF16)
+    assert int(cnt[..., 0].sum()) >= 32, cnt  # of 64 chunks
+    assert rel_err(to_np(d1), to_np(d2)) <= F32_D
+    assert ulp_err(to_np(kt1), to_np(kt2).astype(np.float64)) <= 1.0
+
+
+def test_vector_retention_packed_sequences():
+    """osdn_fwd_varlen with vector retention equals osdn_fwd on each sequence."""
+    lens = [100, 1, 64, 0, 190]
+    total = sum(lens)
+    inp = make_inputs(dict(B=1, T=total, H=2, K=128, V=128, dtype="bf16", seed=82, apf=True, r_vec=True))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    args = [to_dev(inp[n], "bf16") for n in ("q", "k", "v")] + [to_dev(inp[n], "f32") for n in ("beta", "r")]
+    o, S, d = osdn.fwd_varlen(*args, cu_seqlens=torch.from_numpy(cu).to("cuda:0"))
+    torch.cuda.synchronize()
+    for i, L in enumerate(lens):
+        a, b = int(cu[i]), int(cu[i + 1])
+        sl = [to_dev(np.ascontiguousarray(inp[n][:, a:b]), "bf16") for n in ("q", "k", "v")]
+        sl += [to_dev(np.ascontiguousarray(inp[n][:, a:b]), "f32") for n in ("beta", "r")]
+        o1, S1, d1 = osdn.fwd(*sl)
+        torch.cuda.synchronize()
+        assert torch.equal(o[:, a:b], o1) and torch.equal(S[i:i + 1], S1) and torch.equal(d[i:i + 1], d1), i
