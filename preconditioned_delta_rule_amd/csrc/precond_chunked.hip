@@ -161,9 +161,9 @@ __device__ __forceinline__ float row16_max(float x) {
 // so each load instruction covers four whole rows (rows of many tokens in one
 // instruction cost several times more), and a token's sums need only a
 // 16-lane reduction.  The per-token results pass through LDS to lane = token.
-template <typename TIn, bool HAS_R, bool VL>
+template <typename TIn, bool HAS_R, bool VL, bool RV = false>
 __global__ __launch_bounds__(256) void scan_prep128_kernel(ScanArgs a, ScanWork wk, int64_t N) {
-  __shared__ float sred[4][2][CH];
+  __shared__ float sred[4][RV ? 3 : 2][CH];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t ci = (int64_t)blockIdx.x * 4 + w;
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256) void scan_prep128_kernel(ScanArgs a, ScanWork 
   const TIn *kp = static_cast<const TIn *>(a.k) + ((tb + t0) * H + h) * 128 + 8 * (lane & 15);
   const int64_t gi = (tb + t0 + (tok ? lane : 0)) * H + h;
   const float bt = a.beta[gi];
-  const float rt = HAS_R ? a.r[gi] : 1.0f;
+  float rt = HAS_R ? a.r[gi] : 1.0f;
   float x[16][8];
 #pragma unroll
   for (int p = 0; p < 16; ++p) {
@@ -216,6 +216,31 @@ __global__ __launch_bounds__(256) void scan_prep128_kernel(ScanArgs a, ScanWork 
       sred[w][0][4 * p + (lane >> 4)] = pn;
       sred[w][1][4 * p + (lane >> 4)] = pm;
     }
+  }
+  if constexpr (RV) {
+    // second pass, same layout: each token's largest retention
+    const float *rp0 = a.r + ((tb + t0) * H + h) * 128 + 8 * (lane & 15);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int r = 4 * p + (lane >> 4);
+      const float *rp = rp0 + (r < L ? r : L - 1) * stride;
+      const floatx4 v0 = *reinterpret_cast<const floatx4 *>(rp);
+      const floatx4 v1 = *reinterpret_cast<const floatx4 *>(rp + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[p][e] = v0[e];
+        x[p][4 + e] = v1[e];
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, x[p][e]);
+      m = row16_max(m);
+      if ((lane & 15) == 0) sred[w][RV ? 2 : 0][4 * p + (lane >> 4)] = m;
+    }
+    rt = sred[w][RV ? 2 : 0][lane];
   }
   const float nrm = sred[w][0][lane];  // |k_{t0+lane}|^2 (this wave's own LDS)
   const float smx = sred[w][1][lane];  // max_i k_{t0+lane,i}^2
@@ -748,8 +773,12 @@ hipError_t launch_all(const ScanArgs &a, const ScanWork &w, hipStream_t s, bool 
   const int64_t nseq = a.B * a.H;
   if (N > 0) {
     if constexpr (RV) {
-      hipLaunchKernelGGL((scan_prep_kernel<TIn, EPL, FULL, false, VL, true>), dim3((unsigned)(nseq * N)), dim3(64),
-                         0, s, a, w, N);
+      if (a.K == 128)
+        hipLaunchKernelGGL((scan_prep128_kernel<TIn, false, VL, true>), dim3((unsigned)((nseq * N + 3) / 4)),
+                           dim3(256), 0, s, a, w, N);
+      else
+        hipLaunchKernelGGL((scan_prep_kernel<TIn, EPL, FULL, false, VL, true>), dim3((unsigned)(nseq * N)),
+                           dim3(64), 0, s, a, w, N);
     } else if (a.K == 128) {
       hipLaunchKernelGGL((scan_prep128_kernel<TIn, HAS_R, VL>), dim3((unsigned)((nseq * N + 3) / 4)), dim3(256), 0, s,
                          a, w, N);
