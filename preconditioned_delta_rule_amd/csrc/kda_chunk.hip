@@ -147,6 +147,84 @@ __device__ __forceinline__ void write_operands_hilo(const float *sK, const float
   }
 }
 
+// T = (I + A)^-1 for the strictly lower A in sA (pitch AP) by forward
+// substitution in the four diagonal 16x16 blocks and matrix-core products for
+// the off-diagonal ones (sT, sY: two free [64][AP] LDS tiles), then TB =
+// T diag(beta) and the scores M (sM) to the workspace: fp32 rows permuted for
+// the fp32 sweep, or natural-order hi/lo bf16 pairs.
+template <bool HILO>
+__device__ __forceinline__ void invert_and_write(const float *sA, const float *sM, float *sT, float *sY,
+                                                 const float *sBeta, float *tb, float *mq, int tid, int w, int l16,
+                                                 int g) {
+  // ---- T = (I + A)^-1 (unit lower triangular), 16x16 blocks
+  for (int e = tid; e < KC * KC; e += 256) sT[(e >> 6) * AP + (e & 63)] = 0.0f;
+  __syncthreads();
+  if (tid < KC) {
+    // diagonal blocks by forward substitution, one column per thread
+    const int I = tid >> 4, m = tid & 15, c0 = 16 * I;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float acc = i == m ? 1.0f : 0.0f;
+#pragma unroll
+      for (int j = 0; j < i; ++j) acc -= sA[(c0 + i) * AP + c0 + j] * x[j];
+      x[i] = i < m ? 0.0f : acc;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sT[(c0 + i) * AP + c0 + m] = x[i];
+  }
+  __syncthreads();
+  for (int I = 1; I < 4; ++I) {
+    // block row I: Y_IJ = sum_{J <= M < I} A_IM T_MJ, then T_IJ = -T_II Y_IJ,
+    // wave J < I taking block column J on the matrix cores
+    if (w < I) {
+      floatx4 y = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 4 * w; s < 4 * I; ++s)
+        y = mfma_f32(sA[(16 * I + l16) * AP + 4 * s + g], sT[(4 * s + g) * AP + 16 * w + l16], y);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sY[(16 * I + 4 * g + r) * AP + 16 * w + l16] = y[r];
+    }
+    __syncthreads();
+    if (w < I) {
+      floatx4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        t = mfma_f32(sT[(16 * I + l16) * AP + 16 * I + 4 * s + g], sY[(16 * I + 4 * s + g) * AP + 16 * w + l16], t);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * g + r) * AP + 16 * w + l16] = -t[r];
+    }
+    __syncthreads();
+  }
+  // ---- TB = T diag(beta) and M, rows permuted for the sweep's A operands
+  //      (fp32) or as natural-order hi/lo pairs (bf16)
+  if constexpr (HILO) {
+    bf16 *tbb = reinterpret_cast<bf16 *>(tb), *mqb = reinterpret_cast<bf16 *>(mq);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + 256 * u, i = idx >> 3, j0 = (idx & 7) * 8;
+      float x[8], y[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        x[t] = sT[i * AP + j0 + t] * sBeta[j0 + t];
+        y[t] = sM[i * AP + j0 + t];
+      }
+      bf16x8 h, lo;
+      split8(x, h, lo);
+      *reinterpret_cast<bf16x8 *>(tbb + i * KC + j0) = h;
+      *reinterpret_cast<bf16x8 *>(tbb + KC * KC + i * KC + j0) = lo;
+      split8(y, h, lo);
+      *reinterpret_cast<bf16x8 *>(mqb + i * KC + j0) = h;
+      *reinterpret_cast<bf16x8 *>(mqb + KC * KC + i * KC + j0) = lo;
+    }
+  } else {
+    for (int e = tid; e < KC * KC; e += 256) {
+      const int i = e >> 6, q = e & 63, j = 4 * (q & 15) + (q >> 4);
+      tb[e] = sT[i * AP + j] * sBeta[j];
+      mq[e] = sM[i * AP + j];
+    }
+  }
+}
+
 template <typename TIn, bool RES, bool GATED>
 __global__ __launch_bounds__(256) void kda_intra_kernel(KdaArgs a, int64_t N) {
   constexpr bool HILO = sizeof(TIn) == 2;  // bf16 inputs: the sweep takes hi/lo pairs
@@ -350,75 +428,7 @@ __global__ __launch_bounds__(256) void kda_intra_kernel(KdaArgs a, int64_t N) {
   if (tid < KP) a.gc[cbase * KP + tid] = sEGL[tid];
   __syncthreads();
 
-  // ---- T = (I + A)^-1 (unit lower triangular), 16x16 blocks.  sT takes K's
-  //      space, sY (block-row partial products) takes Q's.
-  float *sT = sK, *sY = sQ;
-  for (int e = tid; e < KC * KC; e += 256) sT[(e >> 6) * AP + (e & 63)] = 0.0f;
-  __syncthreads();
-  if (tid < KC) {
-    // diagonal blocks by forward substitution, one column per thread
-    const int I = tid >> 4, m = tid & 15, c0 = 16 * I;
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float acc = i == m ? 1.0f : 0.0f;
-#pragma unroll
-      for (int j = 0; j < i; ++j) acc -= sA[(c0 + i) * AP + c0 + j] * x[j];
-      x[i] = i < m ? 0.0f : acc;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sT[(c0 + i) * AP + c0 + m] = x[i];
-  }
-  __syncthreads();
-  for (int I = 1; I < 4; ++I) {
-    // block row I: Y_IJ = sum_{J <= M < I} A_IM T_MJ, then T_IJ = -T_II Y_IJ,
-    // wave J < I taking block column J on the matrix cores
-    if (w < I) {
-      floatx4 y = {0.f, 0.f, 0.f, 0.f};
-      for (int s = 4 * w; s < 4 * I; ++s)
-        y = mfma_f32(sA[(16 * I + l16) * AP + 4 * s + g], sT[(4 * s + g) * AP + 16 * w + l16], y);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sY[(16 * I + 4 * g + r) * AP + 16 * w + l16] = y[r];
-    }
-    __syncthreads();
-    if (w < I) {
-      floatx4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        t = mfma_f32(sT[(16 * I + l16) * AP + 16 * I + 4 * s + g], sY[(16 * I + 4 * s + g) * AP + 16 * w + l16], t);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * g + r) * AP + 16 * w + l16] = -t[r];
-    }
-    __syncthreads();
-  }
-  // ---- TB = T diag(beta) and M, rows permuted for the sweep's A operands
-  //      (fp32) or as natural-order hi/lo pairs (bf16)
-  if constexpr (HILO) {
-    bf16 *tbb = reinterpret_cast<bf16 *>(tb), *mqb = reinterpret_cast<bf16 *>(mq);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = tid + 256 * u, i = idx >> 3, j0 = (idx & 7) * 8;
-      float x[8], y[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        x[t] = sT[i * AP + j0 + t] * sBeta[j0 + t];
-        y[t] = sM[i * AP + j0 + t];
-      }
-      bf16x8 h, lo;
-      split8(x, h, lo);
-      *reinterpret_cast<bf16x8 *>(tbb + i * KC + j0) = h;
-      *reinterpret_cast<bf16x8 *>(tbb + KC * KC + i * KC + j0) = lo;
-      split8(y, h, lo);
-      *reinterpret_cast<bf16x8 *>(mqb + i * KC + j0) = h;
-      *reinterpret_cast<bf16x8 *>(mqb + KC * KC + i * KC + j0) = lo;
-    }
-  } else {
-    for (int e = tid; e < KC * KC; e += 256) {
-      const int i = e >> 6, q = e & 63, j = 4 * (q & 15) + (q >> 4);
-      tb[e] = sT[i * AP + j] * sBeta[j];
-      mq[e] = sM[i * AP + j];
-    }
-  }
+  invert_and_write<HILO>(sA, sM, sK, sQ, sBeta, tb, mq, tid, w, l16, g);
 }
 
 // NCB 16-column blocks of values per workgroup; the LDS pitch of the
@@ -837,11 +847,264 @@ __global__ __launch_bounds__(256) void kda_seq_hilo_kernel(KdaArgs a, int64_t N,
   }
 }
 
+// kc (the transposed state-update operand) as hi/lo bf16 pairs from the
+// [64][LP] LDS tile sKt; egl scales channel kr (null: already scaled).
+__device__ __forceinline__ void write_kc_hilo(const float *sKt, const float *egl, float *kc, int tid) {
+  bf16 *kcb = reinterpret_cast<bf16 *>(kc);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = tid + 256 * u, kr = idx & (KP - 1), j0 = (idx >> 7) * 8;
+    const float sc = egl ? egl[kr] : 1.0f;
+    float x[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) x[t] = sKt[(j0 + t) * LP + kr] * sc;
+    bf16x8 h, lo;
+    split8(x, h, lo);
+    *reinterpret_cast<bf16x8 *>(kcb + kr * KC + j0) = h;
+    *reinterpret_cast<bf16x8 *>(kcb + KC * KP + kr * KC + j0) = lo;
+  }
+}
+
+// The intra-chunk pass for bf16 inputs with K = 128, in 68 KiB of LDS (two
+// chunks per CU).  Lane (l16, g) of wave w owns token row 16 w + l16 and the
+// channels 32 s + 8 g + e (s < 4, e < 8): exactly the A operand of a
+// v_mfma_f32_16x16x32_bf16 product over the channels, so Gamma . K and
+// Gamma . Q stay in registers (as hi/lo pairs) and go to the workspace from
+// there; only K~ e^-G (the Gram's B operand, read by every wave) and G sit in
+// LDS.  Wave w forms block row w of the Gram and of the scores.  The exact
+// path (some channel decays below e^-60 in the chunk) sums e^{G_i - G_j}
+// per entry over the lane's channels and across its four lanes; its entries
+// pass through the chunk's TB/M workspace slab until G's LDS is free.
+template <bool RES, bool GATED>
+__global__ __launch_bounds__(256) void kda_intra128_kernel(KdaArgs a, int64_t N) {
+  extern __shared__ float sm[];
+  float *sKt = sm, *sG = sm + KC * LP;
+  __shared__ float sBeta[KC], sGL[KP], sEGL[KP];
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, l16 = l & 15, g = l >> 4;
+  const int64_t bh = blockIdx.x / N, n = blockIdx.x - bh * N;
+  const int64_t H = a.H, T = a.T;
+  const int64_t b = bh / H, h = bh - b * H;
+  const int64_t t0 = n * KC;
+  const int L = (int)(T - t0 < KC ? T - t0 : KC);
+  const int64_t cbase = bh * N + n;
+  float *kh = a.kh + cbase * (KC * KP), *qh = a.qh + cbase * (KC * KP), *kc = a.kc + cbase * (KC * KP);
+  float *tb = a.tb + cbase * (KC * KC), *mq = a.mq + cbase * (KC * KC);
+
+  // ---- this lane's row of k, q and the write keys; log alpha into LDS
+  const int row = 16 * w + l16;
+  const bool ok = row < L;
+  const int64_t roff = ((b * T + t0 + (ok ? row : L - 1)) * H + h) * (int64_t)KP + 8 * g;
+  bf16x8 kr[4], qr[4], er[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    kr[s] = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(a.k) + roff + 32 * s);
+    qr[s] = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(a.q) + roff + 32 * s);
+    er[s] = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(a.kt) + roff + 32 * s);
+  }
+  {
+    const int c4 = (tid & 31) * 4;
+    floatx4 xa[8];
+    if constexpr (GATED) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r2 = (tid >> 5) + 8 * u;
+        xa[u] = *reinterpret_cast<const floatx4 *>(a.alpha + ((b * T + t0 + (r2 < L ? r2 : L - 1)) * H + h) * KP + c4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r2 = (tid >> 5) + 8 * u;
+      floatx4 gv4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gv4[e] = GATED && r2 < L ? __logf(xa[u][e]) : 0.0f;
+      *reinterpret_cast<floatx4 *>(sG + r2 * LP + c4) = gv4;
+    }
+  }
+  if (tid < KC) sBeta[tid] = tid < L ? a.beta[(b * T + t0 + tid) * H + h] : 0.0f;
+  __syncthreads();
+  int unsafe = 0;
+  if (tid < KP) {
+    float col[KC];
+#pragma unroll
+    for (int r2 = 0; r2 < KC; ++r2) col[r2] = sG[r2 * LP + tid];
+    float acc = 0.0f;
+#pragma unroll
+    for (int r2 = 0; r2 < KC; ++r2) {
+      acc += col[r2];
+      sG[r2 * LP + tid] = acc;
+    }
+    sGL[tid] = acc;
+    sEGL[tid] = __expf(acc);
+    unsafe = acc < G_SAFE;
+  }
+  unsafe = __syncthreads_or(unsafe);
+
+  // this lane's G, k, q (q_scale applied) and write keys as fp32
+  float gv[4][8], kv[4][8], qv[4][8], wv[4][8];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const floatx4 g0 = *reinterpret_cast<const floatx4 *>(sG + row * LP + 32 * s + 8 * g);
+    const floatx4 g1 = *reinterpret_cast<const floatx4 *>(sG + row * LP + 32 * s + 8 * g + 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      gv[s][e] = e < 4 ? g0[e] : g1[e - 4];
+      const float k = ok ? to_f32(kr[s][e]) : 0.0f;
+      kv[s][e] = k;
+      qv[s][e] = ok ? a.q_scale * to_f32(qr[s][e]) : 0.0f;
+      wv[s][e] = ok ? (RES ? k + to_f32(er[s][e]) : to_f32(er[s][e])) : 0.0f;
+    }
+  }
+  float *sA = sG, *sM = sG + KC * AP;  // G's space once it is dead
+  bf16 *khb = reinterpret_cast<bf16 *>(kh), *qhb = reinterpret_cast<bf16 *>(qh);
+  auto write_kq = [&](float (&xk)[4][8], float (&xq)[4][8]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 hh, ll;
+      split8(xk[s], hh, ll);
+      *reinterpret_cast<bf16x8 *>(khb + row * KP + 32 * s + 8 * g) = hh;
+      *reinterpret_cast<bf16x8 *>(khb + KC * KP + row * KP + 32 * s + 8 * g) = ll;
+      split8(xq[s], hh, ll);
+      *reinterpret_cast<bf16x8 *>(qhb + row * KP + 32 * s + 8 * g) = hh;
+      *reinterpret_cast<bf16x8 *>(qhb + KC * KP + row * KP + 32 * s + 8 * g) = ll;
+    }
+  };
+
+  if (!unsafe) {
+    // Gamma . K, Gamma . Q in registers; K~ e^-G to LDS
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      floatx4 t0v, t1v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float eg = __expf(gv[s][e]);
+        kv[s][e] *= eg;
+        qv[s][e] *= eg;
+        const float x = wv[s][e] * __expf(-gv[s][e]);
+        if (e < 4) t0v[e] = x; else t1v[e - 4] = x;
+      }
+      *reinterpret_cast<floatx4 *>(sKt + row * LP + 32 * s + 8 * g) = t0v;
+      *reinterpret_cast<floatx4 *>(sKt + row * LP + 32 * s + 8 * g + 4) = t1v;
+    }
+    write_kq(kv, qv);
+    bf16x8 kah[4], kal[4], qah[4], qal[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      split8(kv[s], kah[s], kal[s]);
+      split8(qv[s], qah[s], qal[s]);
+    }
+    __syncthreads();  // K~ e^-G complete; G is dead
+    write_kc_hilo(sKt, sEGL, kc, tid);
+    for (int e = tid; e < KC * KC; e += 256) {  // upper blocks are zero
+      const int i = e >> 6, j = e & 63;
+      if ((j >> 4) > (i >> 4)) {
+        sA[i * AP + j] = 0.0f;
+        sM[i * AP + j] = 0.0f;
+      }
+    }
+    // block row w of the Gram and of the scores: J = 0 .. w
+    for (int J = 0; J <= w; ++J) {
+      floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 bh_, bl_;
+        lds_split8(sKt + (16 * J + l16) * LP + 32 * s + 8 * g, bh_, bl_);
+        accA = mfma3(kah[s], kal[s], bh_, bl_, accA);
+        accM = mfma3(qah[s], qal[s], bh_, bl_, accM);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * w + 4 * g + r, j = 16 * J + l16;
+        sA[i * AP + j] = j < i ? sBeta[i] * accA[r] : 0.0f;
+        sM[i * AP + j] = j <= i ? accM[r] : 0.0f;
+      }
+    }
+  } else {
+    // ---- exact path: raw write keys to LDS, every entry with e^{G_i - G_j} <= 1
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      floatx4 t0v, t1v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (e < 4) t0v[e] = wv[s][e]; else t1v[e - 4] = wv[s][e];
+      }
+      *reinterpret_cast<floatx4 *>(sKt + row * LP + 32 * s + 8 * g) = t0v;
+      *reinterpret_cast<floatx4 *>(sKt + row * LP + 32 * s + 8 * g + 4) = t1v;
+    }
+    __syncthreads();
+    for (int j = 0; j < 16 * w + 16; ++j) {
+      float pa = 0.0f, pm = 0.0f;
+      if (j <= row) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int c = 32 * s + 8 * g + e;
+            const float f = __expf(gv[s][e] - sG[j * LP + c]) * sKt[j * LP + c];
+            pa = fmaf(kv[s][e], f, pa);
+            pm = fmaf(qv[s][e], f, pm);
+          }
+      }
+      pa += __shfl_xor(pa, 16, 64);
+      pa += __shfl_xor(pa, 32, 64);
+      pm += __shfl_xor(pm, 16, 64);
+      pm += __shfl_xor(pm, 32, 64);
+      if (g == 0 && j <= row) {
+        tb[row * KC + j] = j < row ? sBeta[row] * pa : 0.0f;
+        mq[row * KC + j] = pm;
+      }
+    }
+    // outputs: Gamma . K, Gamma . Q, and Kc = K~ e^{G_L - G} (factors <= 1)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float eg = expf(gv[s][e]);
+        kv[s][e] *= eg;
+        qv[s][e] *= eg;
+      }
+    write_kq(kv, qv);
+    {
+      bf16 *kcb = reinterpret_cast<bf16 *>(kc);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int idx = tid + 256 * u, kr2 = idx & (KP - 1), j0 = (idx >> 7) * 8;
+        float x[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) x[t] = sKt[(j0 + t) * LP + kr2] * expf(sGL[kr2] - sG[(j0 + t) * LP + kr2]);
+        bf16x8 hh, ll;
+        split8(x, hh, ll);
+        *reinterpret_cast<bf16x8 *>(kcb + kr2 * KC + j0) = hh;
+        *reinterpret_cast<bf16x8 *>(kcb + KC * KP + kr2 * KC + j0) = ll;
+      }
+    }
+    __syncthreads();  // G is dead; the entries in the workspace are visible
+    for (int e = tid; e < KC * KC; e += 256) {
+      const int i = e >> 6, j = e & 63;
+      sA[i * AP + j] = j <= i ? tb[i * KC + j] : 0.0f;
+      sM[i * AP + j] = j <= i ? mq[i * KC + j] : 0.0f;
+    }
+  }
+  if (tid < KP) a.gc[cbase * KP + tid] = sEGL[tid];
+  __syncthreads();
+  invert_and_write<true>(sA, sM, sKt, sKt + KC * AP, sBeta, tb, mq, tid, w, l16, g);
+}
+
+constexpr size_t INTRA128_LDS = (size_t)2 * KC * LP * sizeof(float);
+
 constexpr size_t INTRA_LDS = (size_t)4 * KC * LP * sizeof(float);
 
 template <typename TIn, bool RES>
 hipError_t launch_intra(const KdaArgs &a, int64_t N, hipStream_t s) {
   dim3 grid((unsigned)(a.B * a.H * N)), block(256);
+  if constexpr (sizeof(TIn) == 2) {
+    if (a.K == KP) {
+      auto kern = a.alpha ? kda_intra128_kernel<RES, true> : kda_intra128_kernel<RES, false>;
+      hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)INTRA128_LDS);
+      hipLaunchKernelGGL(kern, grid, block, INTRA128_LDS, s, a, N);
+      prof_mark(s, "kda_intra_kernel");
+      return hipGetLastError();
+    }
+  }
   if (a.alpha) {
     auto kern = kda_intra_kernel<TIn, RES, true>;
     hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)INTRA_LDS);
