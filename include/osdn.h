@@ -189,7 +189,9 @@ size_t osdn_fwd_workspace_bytes(const osdn_desc *desc);
  * residual (d_t - 1) (.) k_t rather
  * than k~_t, so phase 2 sees the write keys to about 16 significant bits
  * instead of bf16's 8: the result is then closer to the exact forward than
- * osdn_precond_scan followed by osdn_chunk_fwd on a bf16 k~.
+ * osdn_precond_scan followed by osdn_chunk_fwd on a bf16 k~.  That holds while
+ * the box keeps d >= 1/2 (clamp on and d_min >= 1/2); otherwise d may approach
+ * 0, where the residual would cancel, and the workspace holds k~_t in bf16.
  */
 osdn_status osdn_fwd(const osdn_desc *desc, const void *q, const void *k,
                      const void *v, const float *beta, const float *r,
