@@ -33,6 +33,7 @@
 #include <math.h>
 
 #include "device_common.h"
+#include "mfma_common.h"
 #include "kernels.h"
 #include "profile.h"
 
@@ -654,10 +655,20 @@ __device__ __forceinline__ bf16x8 neg8(bf16x8 x) {
 // contiguous; pitches of 4 (mod 64) floats keep a quarter-wave's 16-byte
 // accesses on distinct banks.
 __global__ __launch_bounds__(256) void kda_seq_hilo_kernel(KdaArgs a, int64_t N, int ntile) {
-  constexpr int NCB = 2, KVT = 32, PS = KP + 4, PX = KC + 4;
-  __shared__ float sSt[KVT * PS];  // S^T: [value column][key row]
-  __shared__ float sXt[KVT * PX];  // X^T: [value column][token]
-  __shared__ float sDt[KVT * PX];  // D^T
+  // the tiles are kept as hi/lo bf16 pairs, split once by their writer; row
+  // pitches of 8 (mod 128) bf16 keep a quarter-wave's 16-byte reads on
+  // distinct banks
+  constexpr int NCB = 2, KVT = 32, PS = KP + 8, PX = KC + 8;
+  __shared__ __attribute__((aligned(16))) bf16 sSh[KVT * PS], sSl[KVT * PS];  // S^T: [value column][key row]
+  __shared__ __attribute__((aligned(16))) bf16 sXh[KVT * PX], sXl[KVT * PX];  // X^T: [value column][token]
+  __shared__ __attribute__((aligned(16))) bf16 sDh[KVT * PX], sDl[KVT * PX];  // D^T
+  // four consecutive rows of one column of a tile, split
+  auto put4 = [](bf16 *hi, bf16 *lo, int off, floatx4 v) {
+    bf16x4 h, l;
+    split4(v, h, l);
+    *reinterpret_cast<bf16x4 *>(hi + off) = h;
+    *reinterpret_cast<bf16x4 *>(lo + off) = l;
+  };
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, l16 = l & 15, g = l >> 4;
   const int64_t H = a.H, T = a.T, V = a.V, BH = a.B * a.H;
   const int K = (int)a.K;
@@ -687,7 +698,7 @@ __global__ __launch_bounds__(256) void kda_seq_hilo_kernel(KdaArgs a, int64_t N,
         const int kr = 32 * w + 16 * rb + 4 * g + i;
         Sr[rb][cb][i] = a.S0 && kr < K && col < V ? a.S0[(bh * K + kr) * V + col] : 0.0f;
       }
-      *reinterpret_cast<floatx4 *>(sSt + (16 * cb + l16) * PS + 32 * w + 16 * rb + 4 * g) = Sr[rb][cb];
+      put4(sSh, sSl, (16 * cb + l16) * PS + 32 * w + 16 * rb + 4 * g, Sr[rb][cb]);
     }
 
   bf16x8 kah[4], kal[4], qah[4], qal[4], tah[2], tal[2], mah[2], mal[2], kch[2][2], kcl[2][2];
@@ -760,23 +771,23 @@ __global__ __launch_bounds__(256) void kda_seq_hilo_kernel(KdaArgs a, int64_t N,
         accX[cb][i] = row < L && col < V ? vv[cb][i] : 0.0f;
         accP[cb][i] = 0.0f;
       }
-    __syncthreads();  // sSt holds the chunk's boundary state
+    __syncthreads();  // sSh/sSl hold the chunk's boundary state
     // (a) X = V - (Gamma . K) S and P = (Gamma . Q) S, rows 16 w ..
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bf16x8 nh = neg8(kah[s]), nl = neg8(kal[s]);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        bf16x8 bh_, bl_;
-        lds_split8(sSt + (16 * cb + l16) * PS + 32 * s + 8 * g, bh_, bl_);
+        const int off = (16 * cb + l16) * PS + 32 * s + 8 * g;
+        const bf16x8 bh_ = *reinterpret_cast<const bf16x8 *>(sSh + off);
+        const bf16x8 bl_ = *reinterpret_cast<const bf16x8 *>(sSl + off);
         accX[cb] = mfma3(nh, nl, bh_, bl_, accX[cb]);
         accP[cb] = mfma3(qah[s], qal[s], bh_, bl_, accP[cb]);
       }
     }
     load_kq(nn);
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-      *reinterpret_cast<floatx4 *>(sXt + (16 * cb + l16) * PX + 16 * w + 4 * g) = accX[cb];
+    for (int cb = 0; cb < NCB; ++cb) put4(sXh, sXl, (16 * cb + l16) * PX + 16 * w + 4 * g, accX[cb]);
     __syncthreads();
     // (b) D = TB X (TB lower triangular: tokens up to 16 w + 15)
     floatx4 accD[NCB];
@@ -787,22 +798,25 @@ __global__ __launch_bounds__(256) void kda_seq_hilo_kernel(KdaArgs a, int64_t N,
       if (s == 0 || w >= 2) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          bf16x8 bh_, bl_;
-          lds_split8(sXt + (16 * cb + l16) * PX + 32 * s + 8 * g, bh_, bl_);
-          accD[cb] = mfma3(tah[s], tal[s], bh_, bl_, accD[cb]);
+          const int off = (16 * cb + l16) * PX + 32 * s + 8 * g;
+          accD[cb] = mfma3(tah[s], tal[s], *reinterpret_cast<const bf16x8 *>(sXh + off),
+                           *reinterpret_cast<const bf16x8 *>(sXl + off), accD[cb]);
         }
       }
     }
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-      *reinterpret_cast<floatx4 *>(sDt + (16 * cb + l16) * PX + 16 * w + 4 * g) = accD[cb];
+    for (int cb = 0; cb < NCB; ++cb) put4(sDh, sDl, (16 * cb + l16) * PX + 16 * w + 4 * g, accD[cb]);
     __syncthreads();
-    // D as B operand, split once for (c) and (d)
+    // D as B operand for (c) and (d)
     bf16x8 dh[2][NCB], dl[2][NCB];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) lds_split8(sDt + (16 * cb + l16) * PX + 32 * s + 8 * g, dh[s][cb], dl[s][cb]);
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int off = (16 * cb + l16) * PX + 32 * s + 8 * g;
+        dh[s][cb] = *reinterpret_cast<const bf16x8 *>(sDh + off);
+        dl[s][cb] = *reinterpret_cast<const bf16x8 *>(sDl + off);
+      }
     // (c) O = P + M D
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -829,7 +843,7 @@ __global__ __launch_bounds__(256) void kda_seq_hilo_kernel(KdaArgs a, int64_t N,
         for (int i = 0; i < 4; ++i) Sr[rb][cb][i] *= gc4[rb][i];
 #pragma unroll
         for (int s = 0; s < 2; ++s) Sr[rb][cb] = mfma3(kch[rb][s], kcl[rb][s], dh[s][cb], dl[s][cb], Sr[rb][cb]);
-        *reinterpret_cast<floatx4 *>(sSt + (16 * cb + l16) * PS + 32 * w + 16 * rb + 4 * g) = Sr[rb][cb];
+        put4(sSh, sSl, (16 * cb + l16) * PS + 32 * w + 16 * rb + 4 * g, Sr[rb][cb]);
       }
     load_kc(nn);
   }
