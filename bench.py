@@ -92,6 +92,8 @@ KERNEL_SOURCE = {
     "bwd_record_kernel": "preconditioned_delta_rule_amd/csrc/backward.hip",
     "bwd_p2_kernel": "preconditioned_delta_rule_amd/csrc/backward.hip",
     "bwd_p1_kernel": "preconditioned_delta_rule_amd/csrc/backward.hip",
+    "kda_intra_kernel": "preconditioned_delta_rule_amd/csrc/kda_chunk.hip",
+    "kda_seq_kernel": "preconditioned_delta_rule_amd/csrc/kda_chunk.hip",
 }
 COPY_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written
 
@@ -165,6 +167,8 @@ def pmc_summary(fetch_dir, write_dir, workload, command):
                     if row.get("Counter_Name") != counter:
                         continue
                     name = row["Kernel_Name"].replace("scan_prep128_kernel", "scan_prep_kernel")
+                    name = name.replace("kda_seq_hilo_kernel", "kda_seq_kernel")
+                    name = name.replace("kda_intra128_kernel", "kda_intra_kernel")
                     key = None
                     for k in KERNEL_SOURCE:
                         if k in name:
@@ -459,6 +463,16 @@ def kda_bench(args, inp, dev):
         osdn.kda_fwd(s["q"], s["k"], s["v"], s["beta"], s["r"], s["alpha"], o=s["o"], S_out=s["S"],
                      d_out=s["d"], workspace=ws, **kw)
 
+    if args.pmc_pass:
+        for i in range(max(1, args.steps)):
+            step(i)
+        x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        return 0
+
     log("warmup", args.warmup)
     for i in range(args.warmup):
         step(i)
@@ -499,6 +513,10 @@ def kda_bench(args, inp, dev):
         roofline = {"bound": "hbm", "kernel": dom, "achieved": dk["GB/s"], "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": dk["hbm_frac"], "traffic": None,
                     "algorithmic_bytes_per_launch": dk["bytes_per_token_head"] * nth}
+    tr = load_traffic(args.workload, dom)
+    if tr:
+        roofline["traffic"] = tr["bytes_per_launch"] / (dk["ms"] * 1e-3) / 1e9
+        roofline["measured_bytes_per_launch"] = tr["bytes_per_launch"]
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
