@@ -107,3 +107,28 @@ def test_vector_retention_packed_sequences():
         o1, S1, d1 = osdn.fwd(*sl)
         torch.cuda.synchronize()
         assert torch.equal(o[:, a:b], o1) and torch.equal(S[i:i + 1], S1) and torch.equal(d[i:i + 1], d1), i
+
+
+def test_vector_retention_full_size_sampled():
+    """The bench's vector-retention workload (osdn_fwd, B=4, T=4096, H=16,
+    K=V=128, bf16, r [B,T,H,K]) in one call; the oracle recomputes sampled
+    (b,h) sequences."""
+    from tests.helpers import BF16_OS, o_err, s_err
+    from workloads import sample_sequences
+    inp = make_inputs("1p3b_rvec")
+    p = inp["params"]
+    args = [to_dev(inp[n], "bf16") for n in ("q", "k", "v")] + [to_dev(inp[n], "f32") for n in ("beta", "r")]
+    o, S, d = osdn.fwd(*args, eta=p["eta"], d_min=p["d_min"], d_max=p["d_max"], clamp=p["clamp"],
+                       eps=p["eps"], q_scale=p["q_scale"], beta_aware=p["beta_aware"])
+    torch.cuda.synchronize()
+    o, S, d = to_np(o), to_np(S), to_np(d)
+    pairs = [(0, 0), (3, 15), (2, 7)]
+    sub = sample_sequences(dict(inp), pairs)
+    sub["r"] = np.stack([inp["r"][b, :, h] for b, h in pairs])[:, :, None]
+    ref = oracle.forward(sub["q"], sub["k"], sub["v"], sub["beta"], sub["r"], None, eta=p["eta"],
+                         d_min=p["d_min"], d_max=p["d_max"], clamp=p["clamp"], eps=p["eps"],
+                         beta_aware=p["beta_aware"], q_scale=p["q_scale"])
+    for i, (b, h) in enumerate(pairs):
+        assert o_err(o[b, :, h][None, :, None], ref["o"][i][None]) <= BF16_OS, (b, h)
+        assert s_err(S[b, h][None, None], ref["S"][i][None]) <= BF16_OS, (b, h)
+        assert rel_err(d[b, h], ref["d"][i, 0]) <= F32_D, (b, h)
