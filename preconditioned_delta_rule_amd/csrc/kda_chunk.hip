@@ -889,11 +889,16 @@ __device__ __forceinline__ void write_kc_hilo(const float *sKt, const float *egl
 // path (some channel decays below e^-60 in the chunk) sums e^{G_i - G_j}
 // per entry over the lane's channels and across its four lanes; its entries
 // pass through the chunk's TB/M workspace slab until G's LDS is free.
-template <bool RES, bool GATED>
-__global__ __launch_bounds__(256) void kda_intra128_kernel(KdaArgs a, int64_t N) {
+// FOLD: the write-key residual is formed here from the phase-1 sweep's marks,
+// chunk starts and step scalars (a chunk marked 2 has E = (d_min - 1) k; any
+// other replays d_{t+1} = clip(r_t d_t + c_t k_t^2) from its start, one
+// thread per key coordinate, with the phase-1 emit kernel's fp32 expression
+// and bf16 rounding), so phase 1 writes no residual.
+template <bool RES, bool GATED, bool FOLD = false>
+__global__ __launch_bounds__(256) void kda_intra128_kernel(KdaArgs a, int64_t N, EmitArgs em) {
   extern __shared__ float sm[];
   float *sKt = sm, *sG = sm + KC * LP;
-  __shared__ float sBeta[KC], sGL[KP], sEGL[KP];
+  __shared__ float sBeta[KC], sGL[KP], sEGL[KP], sC[FOLD ? KC : 1], sRt[FOLD ? KC : 1];
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, l16 = l & 15, g = l >> 4;
   const int64_t bh = blockIdx.x / N, n = blockIdx.x - bh * N;
   const int64_t H = a.H, T = a.T;
@@ -909,11 +914,63 @@ __global__ __launch_bounds__(256) void kda_intra128_kernel(KdaArgs a, int64_t N)
   const bool ok = row < L;
   const int64_t roff = ((b * T + t0 + (ok ? row : L - 1)) * H + h) * (int64_t)KP + 8 * g;
   bf16x8 kr[4], qr[4], er[4];
+  const int fpin = FOLD ? __builtin_amdgcn_readfirstlane(em.pin[cbase]) : 0;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     kr[s] = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(a.k) + roff + 32 * s);
     qr[s] = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(a.q) + roff + 32 * s);
-    er[s] = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(a.kt) + roff + 32 * s);
+    if constexpr (!FOLD) er[s] = *reinterpret_cast<const bf16x8 *>(static_cast<const bf16 *>(a.kt) + roff + 32 * s);
+  }
+  if constexpr (FOLD) {
+    if (fpin == 2) {
+      // d sits on d_min through the chunk: E = (d_min - 1) k
+      const float dm1 = em.d_min - 1.0f;  // exact on [0.5, 2]
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) er[s][e] = to_bf16(dm1 * to_f32(kr[s][e]));
+    } else {
+      // the replay: k rows to LDS (sKt's space, free until the scaled keys),
+      // one thread per coordinate writes E over them in place
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        floatx4 x0, x1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x0[e] = ok ? to_f32(kr[s][e]) : 0.0f;
+          x1[e] = ok ? to_f32(kr[s][4 + e]) : 0.0f;
+        }
+        *reinterpret_cast<floatx4 *>(sKt + row * LP + 32 * s + 8 * g) = x0;
+        *reinterpret_cast<floatx4 *>(sKt + row * LP + 32 * s + 8 * g + 4) = x1;
+      }
+      if (tid < KC) {
+        const int64_t gi = (b * T + t0 + (tid < L ? tid : 0)) * H + h;
+        sC[tid] = em.cstep[gi];
+        sRt[tid] = em.r ? em.r[gi] : 1.0f;
+      }
+      __syncthreads();
+      if (tid < KP) {
+        float d = em.dstart[cbase * KP + tid];
+        const float lo = em.clamp ? em.d_min : -INFINITY, hi = em.clamp ? em.d_max : INFINITY;
+        for (int u = 0; u < L; ++u) {
+          const float kv = sKt[u * LP + tid];
+          sKt[u * LP + tid] = to_f32(to_bf16((d - 1.0f) * kv));  // d - 1 is exact on [0.5, 2]
+          d = fminf(fmaxf(fmaf(sC[u], kv * kv, sRt[u] * d), lo), hi);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const floatx4 x0 = *reinterpret_cast<const floatx4 *>(sKt + row * LP + 32 * s + 8 * g);
+        const floatx4 x1 = *reinterpret_cast<const floatx4 *>(sKt + row * LP + 32 * s + 8 * g + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          er[s][e] = to_bf16(x0[e]);
+          er[s][4 + e] = to_bf16(x1[e]);
+        }
+      }
+      __syncthreads();  // sKt is reused below
+    }
   }
   {
     const int c4 = (tid & 31) * 4;
@@ -1108,13 +1165,16 @@ constexpr size_t INTRA128_LDS = (size_t)2 * KC * LP * sizeof(float);
 constexpr size_t INTRA_LDS = (size_t)4 * KC * LP * sizeof(float);
 
 template <typename TIn, bool RES>
-hipError_t launch_intra(const KdaArgs &a, int64_t N, hipStream_t s) {
+hipError_t launch_intra(const KdaArgs &a, int64_t N, hipStream_t s, const EmitArgs *em) {
   dim3 grid((unsigned)(a.B * a.H * N)), block(256);
   if constexpr (sizeof(TIn) == 2) {
     if (a.K == KP) {
-      auto kern = a.alpha ? kda_intra128_kernel<RES, true> : kda_intra128_kernel<RES, false>;
+      auto kern = a.alpha ? kda_intra128_kernel<RES, true, false> : kda_intra128_kernel<RES, false, false>;
+      if constexpr (RES) {
+        if (em) kern = a.alpha ? kda_intra128_kernel<true, true, true> : kda_intra128_kernel<true, false, true>;
+      }
       hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)INTRA128_LDS);
-      hipLaunchKernelGGL(kern, grid, block, INTRA128_LDS, s, a, N);
+      hipLaunchKernelGGL(kern, grid, block, INTRA128_LDS, s, a, N, em ? *em : EmitArgs{});
       prof_mark(s, "kda_intra_kernel");
       return hipGetLastError();
     }
@@ -1133,10 +1193,10 @@ hipError_t launch_intra(const KdaArgs &a, int64_t N, hipStream_t s) {
 }
 
 template <typename TIn>
-hipError_t launch_typed(const KdaArgs &a, hipStream_t s) {
+hipError_t launch_typed(const KdaArgs &a, hipStream_t s, const EmitArgs *em) {
   const int64_t N = (a.T + KC - 1) / KC;
   if (N > 0) {
-    hipError_t e = a.kt_is_res ? launch_intra<TIn, true>(a, N, s) : launch_intra<TIn, false>(a, N, s);
+    hipError_t e = a.kt_is_res ? launch_intra<TIn, true>(a, N, s, em) : launch_intra<TIn, false>(a, N, s, em);
     if (e != hipSuccess) return e;
   }
   // 32 value columns per workgroup: 16 columns (two workgroups per CU) measured
@@ -1180,9 +1240,12 @@ void kda_work_layout(KdaArgs &a, void *base) {
   a.gc = reinterpret_cast<float *>(p);
 }
 
-hipError_t launch_kda(const KdaArgs &a, bool is_bf16, hipStream_t s) {
+bool kda_can_fold(const KdaArgs &a, bool is_bf16) { return is_bf16 && a.K == KP && a.kt_is_res; }
+
+hipError_t launch_kda(const KdaArgs &a, bool is_bf16, hipStream_t s, const EmitArgs *em) {
   if (a.B * a.H == 0) return hipSuccess;
-  return is_bf16 ? launch_typed<bf16>(a, s) : launch_typed<float>(a, s);
+  if (em && !kda_can_fold(a, is_bf16)) return hipErrorInvalidValue;
+  return is_bf16 ? launch_typed<bf16>(a, s, em) : launch_typed<float>(a, s, nullptr);
 }
 
 }  // namespace osdn

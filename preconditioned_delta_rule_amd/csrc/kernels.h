@@ -159,7 +159,11 @@ struct KdaArgs {
 };
 size_t kda_work_bytes(int64_t B, int64_t T, int64_t H);
 void kda_work_layout(KdaArgs &a, void *base);
-hipError_t launch_kda(const KdaArgs &a, bool bf16, hipStream_t s);
+// em (bf16, K = 128, residual form): the intra pass forms the write-key
+// residual itself from the phase-1 sweep's marks and step scalars (run that
+// sweep with emit = false); kt is then not read.
+bool kda_can_fold(const KdaArgs &a, bool bf16);
+hipError_t launch_kda(const KdaArgs &a, bool bf16, hipStream_t s, const EmitArgs *em = nullptr);
 
 // Shape coverage of the specialised MFMA path (bf16, K = V = 128, C = 64).
 bool chunk_mfma_supported(const ChunkArgs &a, bool bf16);

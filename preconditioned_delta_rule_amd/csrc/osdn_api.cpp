@@ -651,14 +651,29 @@ osdn_status osdn_kda_fwd(const osdn_desc *d, const void *q, const void *k, const
     ka.kt = ws;
   }
   const size_t scan_bytes = osdn::scan_work_bytes(d->B, d->T, d->H, d->K);
+  const osdn::ScanWork sw = osdn::scan_work_layout(ws + fwd_keys_bytes(d), d->B, d->T, d->H, d->K);
+  // bf16, K = 128, residual form, one retention per token: the intra pass
+  // forms the residual from the chunked sweep's marks and step scalars
+  const bool fold = osdn::kda_can_fold(ka, bf) && !(d->r_per_key && r) && !k_tilde_out;
   if (d->r_per_key && r && d->K > 128)
     OSDN_TRY(run_scan(d, sa, s));
   else
-    OSDN_TRY(hip_status(osdn::launch_precond_scan_chunked(
-                            sa, osdn::scan_work_layout(ws + fwd_keys_bytes(d), d->B, d->T, d->H, d->K), bf, s),
-                        "phase-1 launch"));
+    OSDN_TRY(hip_status(osdn::launch_precond_scan_chunked(sa, sw, bf, s, !fold), "phase-1 launch"));
   osdn::kda_work_layout(ka, ws + fwd_keys_bytes(d) + scan_bytes);
-  OSDN_TRY(hip_status(osdn::launch_kda(ka, bf, s), "phase-2 launch"));
+  if (fold) {
+    osdn::EmitArgs em;
+    em.cstep = sw.cstep;
+    em.dstart = sw.dstart;
+    em.pin = sw.pin;
+    em.r = r;
+    em.res = nullptr;
+    em.d_min = d->d_min;
+    em.d_max = d->d_max;
+    em.clamp = d->clamp ? 1 : 0;
+    OSDN_TRY(hip_status(osdn::launch_kda(ka, bf, s, &em), "phase-2 launch"));
+  } else {
+    OSDN_TRY(hip_status(osdn::launch_kda(ka, bf, s), "phase-2 launch"));
+  }
   return ok();
 }
 
