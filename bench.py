@@ -420,13 +420,16 @@ def kda_work(name, K, V, C=64, elem=2):
     reads the fp32 chunk operands (Gamma.K, Gamma.Q, Kc: 3K floats per token;
     TB, M: 2C; gamma_C: K/C) and v, writes o.  Intra: reads q, k, the bf16
     write-key residual, alpha (K floats) and beta, writes those operands; its
-    Gram and scores are the 10 lower 16x16 blocks of two C x C x K products."""
+    Gram and scores are the 10 lower 16x16 blocks of two C x C x K products.
+    The intra count is that of the bf16 path, which forms the write-key
+    residual itself (q, k, alpha, beta, the phase-1 step scalar and the
+    retention in; no residual read)."""
     if name.startswith("kda_seq"):
         nbytes = 4 * (3 * K + 2 * C) + 4 * K / C + 2 * elem * V
         flops = 6 * K * V + 2 * (C + 1) * V
         return nbytes, flops
     if name.startswith("kda_intra"):
-        nbytes = 3 * elem * K + 4 * K + 4 + 4 * (3 * K + 2 * C) + 4 * K / C
+        nbytes = 2 * elem * K + 4 * K + 4 + 4 + 4 + 4 * (3 * K + 2 * C) + 4 * K / C
         flops = 2 * 2 * 10 * 16 * 16 * K / C
         return nbytes, flops
     return kernel_work(name, K, V, C, True, False, elem)

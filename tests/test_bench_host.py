@@ -43,7 +43,8 @@ def test_oskda_work_counts():
     # X and P (2KV each), D and M D ((C+1)V each), state update (2KV)
     assert flops == 6 * 128 * 128 + 2 * 65 * 128 == 114944
     nbytes, flops = bench.kda_work("kda_intra_kernel", 128, 128, 64, 2)
-    assert nbytes == 3 * 256 + 512 + 4 + 2048 + 8 == 3340
+    # q, k (2 x 256 B), alpha (512 B), beta, step scalar, retention; operands out
+    assert nbytes == 2 * 256 + 512 + 12 + 2048 + 8 == 3092
     assert flops == 20480
 
 
