@@ -197,3 +197,15 @@ def test_kda_full_size_sampled():
         assert o_err(o[b, :, h][None, :, None], ref["o"][i][None]) <= BF16_OS, (b, h)
         assert s_err(S[b, h][None, None], ref["S"][i][None]) <= BF16_OS, (b, h)
         assert rel_err(d[b, h], ref["d"][i, 0]) <= F32_D, (b, h)
+
+
+@pytest.mark.parametrize("case", ["k128", "no_retention", "strong_decay"])
+def test_kda_folded_residual_is_bitwise_the_emitted_one(case):
+    """bf16, K = 128 without k_tilde_out: the intra pass forms the write-key
+    residual from the phase-1 marks and step scalars; with k_tilde_out the
+    phase-1 emit kernel writes it.  Both give the same bits."""
+    inp = make_inputs(dict(CASES[case], dtype="bf16"))
+    d1, S0 = kda_state(inp, seed=9)
+    o1, S1, dd1, _ = run_kda(inp, d1, S0)
+    o2, S2, dd2, _ = run_kda(inp, d1, S0, k_tilde=True)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2) and np.array_equal(dd1, dd2), case
