@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
     if (!pinned && tid < C) {
       const int64_t gi = (tb + t0 + (tid < Lc ? tid : 0)) * H + h;
       sC[tid] = em.cstep[gi];
-      sR[tid] = em.r ? em.r[gi] : 1.0f;
+      if (!em.r_vec) sR[tid] = em.r ? em.r[gi] : 1.0f;
     }
   }
   if (ci + (int64_t)gridDim.x < nch) fetch(ci + gridDim.x);
@@ -203,17 +203,25 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
         const int c = tid;
         float d = em.dstart[ci * KD + c];
         const float lo = em.clamp ? em.d_min : -INFINITY, hi = em.clamp ? em.d_max : INFINITY;
-        auto step = [&](int u) {
+        auto step = [&](int u, float ru) {
           const float kv = to_f32(sKl[u][c]);
           sKh[u][c] = to_bf16((d - 1.0f) * kv);  // d - 1 is exact on [0.5, 2]
-          d = fminf(fmaxf(fmaf(sC[u], kv * kv, sR[u] * d), lo), hi);
+          d = fminf(fmaxf(fmaf(sC[u], kv * kv, ru * d), lo), hi);
         };
+        // with per-coordinate retention (diag(r_t)) thread c reads r_{t,c}
+        // from the [B,T,H,K] rows, which share the key rows' layout
+        const float *rc = em.r + base + c;
         if (Lc == C) {
-          // straight-line: the LDS reads, which do not depend on d, run ahead
+          // straight-line: the reads, which do not depend on d, run ahead
+          if (em.r_vec) {
 #pragma unroll
-          for (int u = 0; u < C; ++u) step(u);
+            for (int u = 0; u < C; ++u) step(u, rc[u * tstride]);
+          } else {
+#pragma unroll
+            for (int u = 0; u < C; ++u) step(u, sR[u]);
+          }
         } else {
-          for (int u = 0; u < Lc; ++u) step(u);
+          for (int u = 0; u < Lc; ++u) step(u, em.r_vec ? rc[u * tstride] : sR[u]);
           for (int u = Lc; u < C; ++u) sKh[u][c] = to_bf16(0.0f);
         }
       }

@@ -83,10 +83,11 @@ struct EmitArgs {
   const float *cstep;   // [B,T,H] step scalars from the chunked sweep
   const float *dstart;  // [B,H,N,K] d at each chunk start
   const int *pin;       // [B,H,N]; 2 = the chunk starts from d_min (no stored start)
-  const float *r;       // [B,T,H] retention, or null
+  const float *r;       // [B,T,H] retention ([B,T,H,K] when r_vec), or null
   bf16 *res;            // OUT [B,T,H,K] residual, read back by the sweep kernel
   float d_min, d_max;
   int clamp;
+  int r_vec = 0;         // per-coordinate retention (the chunk_wy replay only)
 };
 hipError_t launch_chunk_generic(const ChunkArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s);

@@ -397,7 +397,7 @@ static osdn_status fwd_impl(const osdn_desc *d, const int64_t *cu, const void *q
   void *cw = chunk_work_bytes(d) ? ws + fwd_keys_bytes(d) + scan_bytes : nullptr;
   // bf16 on the matrix cores without k_tilde_out: the residual is formed by
   // the first phase-2 kernel, which replays d itself (one pass over k fewer)
-  const bool fold = res && cw && !k_tilde_out && !rvec;
+  const bool fold = res && cw && !k_tilde_out && !rvec_tok;
   if (rvec_tok)  // vector retention above K = 128: the token-by-token sweep writes the keys
     OSDN_TRY(run_scan(d, sa, s));
   else
@@ -413,6 +413,7 @@ static osdn_status fwd_impl(const osdn_desc *d, const int64_t *cu, const void *q
     em.d_min = d->d_min;
     em.d_max = d->d_max;
     em.clamp = d->clamp ? 1 : 0;
+    em.r_vec = rvec ? 1 : 0;
     OSDN_TRY(hip_status(osdn::launch_chunk_wy(ca, cw, s, &em), "phase-2 launch"));
   } else {
     OSDN_TRY(run_chunk(d, ca, cw, s));
