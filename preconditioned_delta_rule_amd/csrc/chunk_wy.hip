@@ -78,7 +78,7 @@ struct TinvLay {
 // d_{t+1} = clip(r_t d_t + c_t k_t^2), the same fp32 expressions as the
 // phase-1 emit kernel -- and written for the sweep kernel, so phase 1 need
 // not write it and this kernel need not read it.
-template <bool GATED, bool KRES, bool EMIT, bool VL>
+template <bool GATED, bool KRES, bool EMIT, bool VL, bool RVEC = false>
 __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout, int64_t N, EmitArgs em) {
   static_assert(KRES || !EMIT, "the folded replay produces the residual form");
   typedef TinvLay L;
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
     if (!pinned && tid < C) {
       const int64_t gi = (tb + t0 + (tid < Lc ? tid : 0)) * H + h;
       sC[tid] = em.cstep[gi];
-      if (!em.r_vec) sR[tid] = em.r ? em.r[gi] : 1.0f;
+      if constexpr (!RVEC) sR[tid] = em.r ? em.r[gi] : 1.0f;
     }
   }
   if (ci + (int64_t)gridDim.x < nch) fetch(ci + gridDim.x);
@@ -213,15 +213,22 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
         const float *rc = em.r + base + c;
         if (Lc == C) {
           // straight-line: the reads, which do not depend on d, run ahead
-          if (em.r_vec) {
+          if constexpr (RVEC) {
+            // sixteen rows of r in flight at a time keeps the register count
+            // within three workgroups per CU
+            for (int u0 = 0; u0 < C; u0 += 16) {
+              float rr[16];
 #pragma unroll
-            for (int u = 0; u < C; ++u) step(u, rc[u * tstride]);
+              for (int j = 0; j < 16; ++j) rr[j] = rc[(u0 + j) * tstride];
+#pragma unroll
+              for (int j = 0; j < 16; ++j) step(u0 + j, rr[j]);
+            }
           } else {
 #pragma unroll
             for (int u = 0; u < C; ++u) step(u, sR[u]);
           }
         } else {
-          for (int u = 0; u < Lc; ++u) step(u, em.r_vec ? rc[u * tstride] : sR[u]);
+          for (int u = 0; u < Lc; ++u) step(u, RVEC ? rc[u * tstride] : sR[u]);
           for (int u = Lc; u < C; ++u) sKh[u][c] = to_bf16(0.0f);
         }
       }
@@ -895,7 +902,12 @@ void launch_both(const ChunkArgs &a, bf16 *tw, int64_t N, hipStream_t s, const E
     const dim3 grid((unsigned)((nch + per - 1) / per)), block(256);
     if constexpr (KRES) {
       if (em) {
-        hipLaunchKernelGGL((chunk_tinv_kernel<GATED, true, true, VL>), grid, block, 0, s, a, tw, N, *em);
+        // per-coordinate retention has an instantiation of its own, so that
+        // the scalar one keeps its register count (three workgroups per CU)
+        if (em->r_vec)
+          hipLaunchKernelGGL((chunk_tinv_kernel<GATED, true, true, VL, true>), grid, block, 0, s, a, tw, N, *em);
+        else
+          hipLaunchKernelGGL((chunk_tinv_kernel<GATED, true, true, VL>), grid, block, 0, s, a, tw, N, *em);
         prof_mark(s, "chunk_tinv_kernel");
       }
     }

@@ -87,7 +87,7 @@ struct EmitArgs {
   bf16 *res;            // OUT [B,T,H,K] residual, read back by the sweep kernel
   float d_min, d_max;
   int clamp;
-  int r_vec = 0;         // per-coordinate retention (the chunk_wy replay only)
+  int r_vec = 0;        // r is [B,T,H,K] (the chunk_wy replay only)
 };
 hipError_t launch_chunk_generic(const ChunkArgs &a, bool bf16, hipStream_t s);
 hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s);
