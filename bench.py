@@ -4,7 +4,7 @@
 One step = one full forward of one layer through the C ABI entry point
 osdn_fwd: phase 1 (preconditioner scan: scan_prep and scan_solve kernels)
 and phase 2 (chunkwise WY delta rule: chunk_tinv, which also replays d to
-form the write-key residual, and chunk_seq) over a batch of synthetic inputs already resident in HBM.  The
+form the write-key residual, and chunk_sweep) over a batch of synthetic inputs already resident in HBM.  The
 default workload is the 1.3B-shaped layer: B=4, H=16, T=4096, K=V=128, bf16
 inputs, fp32 state, chunk 64, APF retention on.
 
@@ -20,7 +20,9 @@ alpha where present), used for the roofline figures:
     chunk_tinv      read k 2K, step scalar 4, beta 4 (+ r 4), write the
                     residual E 2K (the phase-1 replay is folded in)     = 520 / 524 B
                     flops: Gram 2 C K                                   = 16384
-    chunk_seq       read q, k, k~ 2K each + v 2V + beta 4, write o 2V   = 1284 B
+    chunk_sweep     read q, k, k~ 2K each + v 2V + beta 4, write o 2V   = 1284 B
+                    (a chunk phase 1 took as pinned on d_min has write keys
+                    d_min k: its k~ is not read, 1028 B)
                     flops: K S^T, Q S^T, S update 3 x 2 K V, scores
                     2 C K, Delta and O 2 x 2 C V                        = 147456
 Both phases sit below the MFMA ridge (2.5 PFLOP/s / 8 TB/s = 312 flop/B),
@@ -87,7 +89,7 @@ KERNEL_SOURCE = {
     "scan_solve_kernel": "preconditioned_delta_rule_amd/csrc/precond_chunked.hip",
     "scan_emit_kernel": "preconditioned_delta_rule_amd/csrc/precond_chunked.hip",
     "chunk_tinv_kernel": "preconditioned_delta_rule_amd/csrc/chunk_wy.hip",
-    "chunk_seq_kernel": "preconditioned_delta_rule_amd/csrc/chunk_wy.hip",
+    "chunk_sweep_kernel": "preconditioned_delta_rule_amd/csrc/chunk_wy.hip",
     "decode_kernel": "preconditioned_delta_rule_amd/csrc/decode.hip",
     "bwd_record_kernel": "preconditioned_delta_rule_amd/csrc/backward.hip",
     "bwd_p2_kernel": "preconditioned_delta_rule_amd/csrc/backward.hip",
@@ -102,9 +104,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_work(name, K, V, C, apf, gated, elem=2, rvec=False):
+def kernel_work(name, K, V, C, apf, gated, elem=2, rvec=False, fused=True, swept=1.0):
     """(algorithmic bytes, flops) per token-head of one kernel (rvec: the
-    retention is a [K] row per token)."""
+    retention is a [K] row per token).  fused: osdn_fwd, whose first phase-2
+    kernel replays phase 1 and forms the write-key residual; otherwise
+    osdn_precond_scan then osdn_chunk_fwd, where the emit kernel writes k~ and
+    phase 2 reads it.  swept: the fraction of 64-token chunks that phase 1 did
+    not take as pinned on d_min (only those chunks read the step scalars, the
+    chunk-start d and the retention in the replay)."""
     r = (4 * K if rvec else 4) if apf else 0
     g = 4 if gated else 0
     if name == "precond_scan_kernel":
@@ -119,11 +126,17 @@ def kernel_work(name, K, V, C, apf, gated, elem=2, rvec=False):
     if name == "scan_emit_kernel":
         return 2 * elem * K + 4 + r, 0
     if name == "chunk_tinv_kernel":
-        # osdn_fwd (bf16): reads k, forms and writes the residual E = (d-1) k
-        # from the phase-1 step scalars (4 B) and retention, reads beta
-        return 2 * elem * K + 4 + 4 + r + g, 2 * C * K
-    if name == "chunk_seq_kernel":
-        return elem * (3 * K + V) + 4 + elem * V + g, 2 * (3 * K * V + C * K + 2 * C * V)
+        if not fused:
+            # reads k and k~, beta (and alpha)
+            return 2 * elem * K + 4 + g, 2 * C * K
+        # osdn_fwd (bf16): reads k, forms and writes the residual E = (d-1) k,
+        # reads beta (and alpha); a swept chunk also reads its step scalars,
+        # retention and chunk-start d
+        return 2 * elem * K + 4 + g + swept * (4 + r + 4.0 * K / C), 2 * C * K
+    if name == "chunk_sweep_kernel":
+        # osdn_fwd reads no write keys for a pinned chunk
+        kt = elem * K * (swept if fused else 1.0)
+        return elem * (2 * K + V) + kt + 4 + elem * V + g, 2 * (3 * K * V + C * K + 2 * C * V)
     return 0, 0
 
 
@@ -246,6 +259,9 @@ def main(argv=None):
                     help="time osdn_fwd_varlen on a packed batch (default workload varlen_1p3b_65k)")
     ap.add_argument("--backward", action="store_true",
                     help="time osdn_bwd (one call per step) instead of osdn_fwd")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time osdn_precond_scan then osdn_chunk_fwd (the write keys cross HBM "
+                         "in the input dtype) instead of osdn_fwd")
     ap.add_argument("--copies", type=int, default=4,
                     help="input sets rotated between steps (keeps the 256 MB MALL from "
                          "serving repeated reads)")
@@ -309,21 +325,36 @@ def main(argv=None):
 
     sets = []
     for c in range(max(1, args.copies)):
-        sets.append(dict(q=up(inp["q"], tdt), k=up(inp["k"], tdt), v=up(inp["v"], tdt),
-                         beta=up(inp["beta"], torch.float32), r=up(inp["r"], torch.float32),
-                         alpha=up(inp["alpha"], torch.float32),
-                         o=torch.empty((B, T, H, V), dtype=tdt, device=dev),
-                         ws=torch.empty(osdn.fwd_workspace_bytes(B, T, H, K, V, dtype=code, chunk=C),
-                                        dtype=torch.uint8, device=dev),
-                         S=torch.empty((B, H, V, K), dtype=torch.float32, device=dev),
-                         d=torch.empty((B, H, K), dtype=torch.float32, device=dev)))
+        st = dict(q=up(inp["q"], tdt), k=up(inp["k"], tdt), v=up(inp["v"], tdt),
+                  beta=up(inp["beta"], torch.float32), r=up(inp["r"], torch.float32),
+                  alpha=up(inp["alpha"], torch.float32),
+                  o=torch.empty((B, T, H, V), dtype=tdt, device=dev),
+                  S=torch.empty((B, H, V, K), dtype=torch.float32, device=dev),
+                  d=torch.empty((B, H, K), dtype=torch.float32, device=dev))
+        if args.unfused:
+            st["kt"] = torch.empty((B, T, H, K), dtype=tdt, device=dev)
+            st["sws"] = torch.empty(osdn.precond_scan_workspace_bytes(B, T, H, K, code),
+                                    dtype=torch.uint8, device=dev)
+            st["cws"] = torch.empty(max(1, osdn.chunk_fwd_workspace_bytes(B, T, H, K, V, code, C)),
+                                    dtype=torch.uint8, device=dev)
+        else:
+            st["ws"] = torch.empty(osdn.fwd_workspace_bytes(B, T, H, K, V, dtype=code, chunk=C),
+                                   dtype=torch.uint8, device=dev)
+        sets.append(st)
     kw = dict(chunk=C, eta=p["eta"], d_min=p["d_min"], d_max=p["d_max"], clamp=p["clamp"],
               eps=p["eps"], q_scale=p["q_scale"], beta_aware=p["beta_aware"])
+    skw = {n: kw[n] for n in ("eta", "d_min", "d_max", "clamp", "eps", "beta_aware")}
 
     def step(i):
         s = sets[i % len(sets)]
-        osdn.fwd(s["q"], s["k"], s["v"], s["beta"], s["r"], s["alpha"], None, None,
-                 o=s["o"], S_out=s["S"], d_out=s["d"], workspace=s["ws"], **kw)
+        if args.unfused:
+            osdn.precond_scan(s["k"], s["beta"], s["r"], None, k_tilde=s["kt"], d_out=s["d"],
+                              workspace=s["sws"], **skw)
+            osdn.chunk_fwd(s["q"], s["k"], s["kt"], s["v"], s["beta"], s["alpha"], None, chunk=C,
+                           q_scale=p["q_scale"], o=s["o"], S_out=s["S"], workspace=s["cws"])
+        else:
+            osdn.fwd(s["q"], s["k"], s["v"], s["beta"], s["r"], s["alpha"], None, None,
+                     o=s["o"], S_out=s["S"], d_out=s["d"], workspace=s["ws"], **kw)
 
     if args.pmc_pass:
         for i in range(max(1, args.steps)):
@@ -352,6 +383,16 @@ def main(argv=None):
     ms_step = e0.elapsed_time(e1) / nsteps
     log("step %.4f ms (wall %.3f s for %d steps)" % (ms_step, wall, nsteps))
 
+    # which path phase 1 took per 64-token chunk (pinned on d_min, closed form,
+    # token by token), summed over (b,h): a pinned chunk reads no step scalar
+    if args.unfused:
+        cnt = osdn.scan_counters(sets[0]["sws"], B, T, H, K, code).numpy()
+    else:
+        cnt = osdn.fwd_scan_counters(sets[0]["ws"], B, T, H, K, V, code, C).numpy()
+    paths = cnt.reshape(-1, 3).sum(0).tolist()
+    swept = 1.0 - paths[0] / max(1, sum(paths))
+    log("phase-1 chunks [pinned, closed form, token by token]:", paths)
+
     # per-kernel durations over the timed steps
     per = {}
     for name, ms in launches:
@@ -362,7 +403,8 @@ def main(argv=None):
     kernels = {}
     for name, vals in per.items():
         ms = float(np.mean(vals))
-        nbytes, flops = kernel_work(name, K, V, C, apf, gated, elem, rvec)
+        nbytes, flops = kernel_work(name, K, V, C, apf, gated, elem, rvec, fused=not args.unfused,
+                                    swept=swept)
         gbs = nbytes * nth / (ms * 1e-3) / 1e9 if ms > 0 else None
         ent = {"ms": ms, "launches_per_step": len(vals) / nsteps, "ms_median": float(np.median(vals)),
                "bound": "hbm", "bytes_per_token_head": nbytes, "GB/s": gbs,
@@ -394,14 +436,18 @@ def main(argv=None):
                          (B * H, T, reps, cwall)}
         log("cpu oracle %.2f s" % cwall)
 
+    metric = METRIC if (H, K, V, T) == (16, 128, 128, 4096) else (
+        "OSDN fwd tokens/sec (phase1+phase2) at H=%d,K=%d,V=%d,T=%d; %% HBM/MFMA roofline" % (H, K, V, T))
     out = {
-        "metric": METRIC, "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "metric": metric, "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": nsteps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": p["dtype"],
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "T": T, "H": H, "K": K, "V": V,
                    "chunk": C, "apf": apf, "vector_retention": rvec, "gated": gated, "seed": spec["seed"],
-                   "input_copies": len(sets)},
+                   "input_copies": len(sets),
+                   "path": "unfused (osdn_precond_scan + osdn_chunk_fwd)" if args.unfused else "osdn_fwd",
+                   "phase1_chunks_pinned_closed_token": paths},
         "roofline": roofline, "cpu_baseline": cpu,
         "phases": {"precond_scan_ms": p1, "chunk_fwd_ms": p2,
                    "step_device_ms_median": float(np.median(step_ms)) if step_ms else None,

@@ -28,10 +28,14 @@
  * Conventions for every entry point:
  *  - Sequence tensors are contiguous row-major [B,T,H,X] (the paper's layout
  *    before chunking, Appendix C); per-head vectors [B,H,X]; the state S is
- *    [B,H,V,K] in float32.  q, k, v, k_tilde and o share desc->dtype; beta,
- *    r, alpha, d1, d_out, S0 and S_out are float32.
+ *    [B,H,V,K] in float32.  q, k, v, k_tilde and o share desc->dtype (o is
+ *    float32 instead when desc->o_f32 is set); beta, r, alpha, d1, d_out, S0
+ *    and S_out are float32.
  *  - Pointers are DEVICE pointers owned by the caller; the library allocates
- *    nothing and keeps no state between calls.  stream is a hipStream_t (NULL
+ *    no memory and keeps no state between calls beyond the calling thread's
+ *    last error message and its open launch profile (osdn_profile_begin /
+ *    osdn_profile_end, whose HIP events live from the first launch recorded
+ *    to osdn_profile_end).  stream is a hipStream_t (NULL
  *    = the default stream); work is enqueued asynchronously and outputs are
  *    valid once the stream has been synchronised.
  *  - Arguments are validated before anything is launched; on failure nothing
@@ -82,10 +86,17 @@ typedef enum {
  *               only (Appendix B); the memory write always uses beta.
  *   r_per_key   0: r is [B,T,H], one retention per token and head (Eq.(7));
  *               1: r is [B,T,H,K], the vector retention diag(r_t) of
- *               Appendix A.5, Proposition A.3 (the chunked phase-1 sweep for
- *               K <= 128, token by token above; osdn_decode and osdn_bwd,
- *               and osdn_fwd_varlen above K = 128, return OSDN_EUNSUPPORTED
- *               for it).  Ignored when r is NULL.
+ *               Appendix A.5, Proposition A.3 (osdn_precond_scan sweeps it
+ *               chunked for K <= 128, token by token above; the forward
+ *               entry points take K <= 128; osdn_decode and osdn_bwd return
+ *               OSDN_EUNSUPPORTED for it).  Ignored when r is NULL.
+ *   o_f32       0: the readout o has desc->dtype (rounded to nearest even
+ *               from the fp32 accumulation, as the paper's listing returns
+ *               o in the value dtype); 1: o is float32 whatever dtype is,
+ *               i.e. the same readout before that final rounding (bf16
+ *               inputs with fp32 outputs).  Taken by osdn_chunk_fwd,
+ *               osdn_fwd, osdn_fwd_varlen, osdn_decode and osdn_kda_fwd;
+ *               for osdn_bwd it makes dq, dk and dv float32 likewise.
  */
 typedef struct osdn_desc {
   int64_t B, T, H, K, V;
@@ -97,11 +108,12 @@ typedef struct osdn_desc {
   float q_scale;
   int32_t beta_aware;
   int32_t r_per_key;
+  int32_t o_f32;
 } osdn_desc;
 
 /* Fill *desc with the given sizes and the paper's defaults: chunk 64,
  * eta 0.003, box [0.5, 2], clamp on, eps 1e-6, q_scale 1, beta-aware, bf16,
- * one retention per token and head. */
+ * one retention per token and head, o in the input dtype. */
 osdn_status osdn_desc_init(osdn_desc *desc, int64_t B, int64_t T, int64_t H,
                            int64_t K, int64_t V);
 
@@ -152,7 +164,8 @@ int64_t osdn_precond_scan_counters_offset(const osdn_desc *desc);
  *   beta    [B,T,H]   f32            write gates
  *   alpha   [B,T,H]   f32            state decay in (0,1], or NULL (OSDN)
  *   S0      [B,H,V,K] f32            initial state, or NULL for zeros
- *   o       [B,T,H,V] dtype          OUT: o_t = S_t (q_scale q_t)
+ *   o       [B,T,H,V] dtype          OUT: o_t = S_t (q_scale q_t) (f32 when
+ *                                    desc->o_f32)
  *   S_out   [B,H,V,K] f32            OUT: S_T, or NULL (may alias S0)
  *   workspace                        NULL, or >= osdn_chunk_fwd_workspace_bytes
  *                                    (desc) bytes, 16-byte aligned (see below)
@@ -239,7 +252,7 @@ osdn_status osdn_fwd_varlen(const osdn_desc *desc, const int64_t *cu_seqlens,
  *   alpha   [B,T,H]   f32        state decay in (0,1], or NULL (OSDN)
  *   d1      [B,H,K]   f32        carried preconditioner, or NULL for ones
  *   S0      [B,H,V,K] f32        carried state, or NULL for zeros
- *   o       [B,T,H,V] dtype      OUT: readouts
+ *   o       [B,T,H,V] dtype      OUT: readouts (f32 when desc->o_f32)
  *   S_out   [B,H,V,K] f32        OUT: state after the last token, or NULL
  *                                (may alias S0: in-place update)
  *   d_out   [B,H,K]   f32        OUT: d after the last token, or NULL (may
@@ -267,8 +280,9 @@ osdn_status osdn_decode(const osdn_desc *desc, const void *q, const void *k,
  *   dout    [B,T,H,V] dtype      dL/do
  *   dS      [B,H,V,K] f32        dL/dS_T, or NULL (zero)
  *   dd      [B,H,K]   f32        dL/dd_{T+1}, or NULL (zero)
- *   dq, dk  [B,T,H,K] dtype      OUT: dL/dq, dL/dk (both key roles)
- *   dv      [B,T,H,V] dtype      OUT: dL/dv
+ *   dq, dk  [B,T,H,K] dtype      OUT: dL/dq, dL/dk (both key roles) (f32
+ *                                when desc->o_f32)
+ *   dv      [B,T,H,V] dtype      OUT: dL/dv (f32 when desc->o_f32)
  *   dbeta   [B,T,H]   f32        OUT: dL/dbeta (write gate and phase-1 step)
  *   dr      [B,T,H]   f32        OUT: dL/dr, or NULL (ignored when r is NULL)
  *   dalpha  [B,T,H]   f32        OUT: dL/dalpha, or NULL (ignored when alpha is NULL)
@@ -310,7 +324,7 @@ osdn_status osdn_bwd(const osdn_desc *desc, const void *q, const void *k,
  *   alpha   [B,T,H,K] f32       channel-wise decay in (0,1], or NULL (none)
  *   d1      [B,H,K]   f32       initial preconditioner, or NULL for ones
  *   S0      [B,H,K,V] f32       initial state (KDA layout), or NULL for zeros
- *   o       [B,T,H,V] dtype     OUT: readouts
+ *   o       [B,T,H,V] dtype     OUT: readouts (f32 when desc->o_f32)
  *   S_out   [B,H,K,V] f32       OUT: final state, or NULL (may alias S0)
  *   d_out   [B,H,K]   f32       OUT: d_{T+1}, or NULL (may alias d1)
  *   k_tilde_out [B,T,H,K] dtype OUT: write keys d_t (.) k_t, or NULL
@@ -338,7 +352,9 @@ osdn_status osdn_kda_fwd(const osdn_desc *desc, const void *q, const void *k,
  * name (static string) and the device time in milliseconds from the previous
  * event to this launch's event -- the kernel's duration when the launches are
  * queued back to back on one stream.  *count receives the number of launches
- * recorded.  Ending a profile that was not begun returns OSDN_EINVAL.
+ * recorded.  Ending a profile that was not begun returns OSDN_EINVAL.  The
+ * events are created as launches are recorded and destroyed by
+ * osdn_profile_end.
  */
 osdn_status osdn_profile_begin(void *stream);
 osdn_status osdn_profile_end(const char **names, float *ms, int max_entries,

@@ -53,7 +53,7 @@ class Desc(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("eta", ctypes.c_float), ("d_min", ctypes.c_float),
                 ("d_max", ctypes.c_float), ("clamp", ctypes.c_int32), ("eps", ctypes.c_float),
                 ("q_scale", ctypes.c_float), ("beta_aware", ctypes.c_int32),
-                ("r_per_key", ctypes.c_int32)]
+                ("r_per_key", ctypes.c_int32), ("o_f32", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -126,7 +126,8 @@ def _check(status):
 
 
 def make_desc(B, T, H, K, V, *, dtype=BF16, chunk=64, eta=0.003, d_min=0.5, d_max=2.0,
-              clamp=True, eps=1e-6, q_scale=1.0, beta_aware=True, r_per_key=False) -> Desc:
+              clamp=True, eps=1e-6, q_scale=1.0, beta_aware=True, r_per_key=False,
+              o_f32=False) -> Desc:
     d = Desc()
     _check(load().osdn_desc_init(ctypes.byref(d), B, T, H, K, V))
     d.dtype, d.chunk = int(dtype), int(chunk)
@@ -134,6 +135,7 @@ def make_desc(B, T, H, K, V, *, dtype=BF16, chunk=64, eta=0.003, d_min=0.5, d_ma
     d.clamp, d.eps, d.q_scale = int(bool(clamp)), float(eps), float(q_scale)
     d.beta_aware = int(bool(beta_aware))
     d.r_per_key = int(bool(r_per_key))
+    d.o_f32 = int(bool(o_f32))
     return d
 
 
@@ -245,11 +247,12 @@ def chunk_fwd_workspace_bytes(B, T, H, K, V, dtype=BF16, chunk=64) -> int:
 
 
 def chunk_fwd(q, k, k_tilde, v, beta, alpha=None, S0=None, *, chunk=64, q_scale=1.0,
-              o=None, S_out=None, two_pass=True, workspace=None):
+              o=None, S_out=None, two_pass=True, workspace=None, o_f32=False):
     """Phase 2.  q, k, k_tilde [B,T,H,K], v [B,T,H,V] (one dtype), beta and
     alpha [B,T,H] f32, S0 [B,H,V,K] f32.  two_pass=True hands the library a
     workspace (allocated when None) so that the matrix-core shapes form every
     chunk's (I + A)^-1 chunk-parallel first; two_pass=False passes none.
+    o_f32=True returns o in float32 (the readout before rounding to q's dtype).
     Returns (o [B,T,H,V], S_out [B,H,V,K])."""
     B, T, H, K = q.shape
     V = v.shape[-1]
@@ -260,13 +263,14 @@ def chunk_fwd(q, k, k_tilde, v, beta, alpha=None, S0=None, *, chunk=64, q_scale=
     _need(beta, "beta", (B, T, H), f32, dev)
     _need(alpha, "alpha", (B, T, H), f32, dev)
     _need(S0, "S0", (B, H, V, K), f32, dev)
+    odt = f32 if o_f32 else dt
     if o is None:
-        o = torch.empty((B, T, H, V), dtype=dt, device=dev)
+        o = torch.empty((B, T, H, V), dtype=odt, device=dev)
     if S_out is None:
         S_out = torch.empty((B, H, V, K), dtype=f32, device=dev)
-    _need(o, "o", (B, T, H, V), dt, dev)
+    _need(o, "o", (B, T, H, V), odt, dev)
     _need(S_out, "S_out", (B, H, V, K), f32, dev)
-    desc = make_desc(B, T, H, K, V, dtype=_dtype_code(q), chunk=chunk, q_scale=q_scale)
+    desc = make_desc(B, T, H, K, V, dtype=_dtype_code(q), chunk=chunk, q_scale=q_scale, o_f32=o_f32)
     need = int(load().osdn_chunk_fwd_workspace_bytes(ctypes.byref(desc))) if two_pass else 0
     workspace = _workspace(workspace, need, dev) if need else None
     _check(load().osdn_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(k_tilde), _ptr(v),
@@ -291,8 +295,9 @@ def fwd_scan_counters(workspace, B, T, H, K, V, dtype=BF16, chunk=64):
 
 def fwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, chunk=64, eta=0.003,
         d_min=0.5, d_max=2.0, clamp=True, eps=1e-6, q_scale=1.0, beta_aware=True,
-        o=None, S_out=None, d_out=None, k_tilde_out=None, workspace=None):
-    """Both phases on the current stream.  Returns (o, S_out, d_out)."""
+        o=None, S_out=None, d_out=None, k_tilde_out=None, workspace=None, o_f32=False):
+    """Both phases on the current stream.  o_f32=True returns o in float32 (the
+    readout before rounding to q's dtype).  Returns (o, S_out, d_out)."""
     B, T, H, K = q.shape
     V = v.shape[-1]
     dev, dt, f32 = q.device, q.dtype, torch.float32
@@ -303,16 +308,18 @@ def fwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, chunk=64, eta=0.
     _need(alpha, "alpha", (B, T, H), f32, dev)
     _need(d1, "d1", (B, H, K), f32, dev)
     _need(S0, "S0", (B, H, V, K), f32, dev)
+    odt = f32 if o_f32 else dt
     if o is None:
-        o = torch.empty((B, T, H, V), dtype=dt, device=dev)
+        o = torch.empty((B, T, H, V), dtype=odt, device=dev)
     if S_out is None:
         S_out = torch.empty((B, H, V, K), dtype=f32, device=dev)
     if d_out is None:
         d_out = torch.empty((B, H, K), dtype=f32, device=dev)
+    _need(o, "o", (B, T, H, V), odt, dev)
     _need(k_tilde_out, "k_tilde_out", (B, T, H, K), dt, dev)
     desc = make_desc(B, T, H, K, V, dtype=_dtype_code(q), chunk=chunk, eta=eta, d_min=d_min,
                      d_max=d_max, clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware,
-                     r_per_key=rvec)
+                     r_per_key=rvec, o_f32=o_f32)
     need = int(load().osdn_fwd_workspace_bytes(ctypes.byref(desc)))
     workspace = _workspace(workspace, need, dev)
     _check(load().osdn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r),
@@ -324,7 +331,7 @@ def fwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, chunk=64, eta=0.
 
 def kda_fwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, eta=0.003, d_min=0.5,
             d_max=2.0, clamp=True, eps=1e-6, q_scale=1.0, beta_aware=True, o=None, S_out=None,
-            d_out=None, k_tilde_out=None, workspace=None):
+            d_out=None, k_tilde_out=None, workspace=None, o_f32=False):
     """OSKDA forward on the current stream: q, k [B,T,H,K], v [B,T,H,V], beta
     [B,T,H], r [B,T,H] or [B,T,H,K], alpha [B,T,H,K] (channel-wise decay), d1
     [B,H,K], S0 [B,H,K,V].  Returns (o [B,T,H,V], S_out [B,H,K,V], d_out)."""
@@ -338,15 +345,18 @@ def kda_fwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, eta=0.003, d
     _need(alpha, "alpha", (B, T, H, K), f32, dev)
     _need(d1, "d1", (B, H, K), f32, dev)
     _need(S0, "S0", (B, H, K, V), f32, dev)
+    odt = f32 if o_f32 else dt
     if o is None:
-        o = torch.empty((B, T, H, V), dtype=dt, device=dev)
+        o = torch.empty((B, T, H, V), dtype=odt, device=dev)
     if S_out is None:
         S_out = torch.empty((B, H, K, V), dtype=f32, device=dev)
     if d_out is None:
         d_out = torch.empty((B, H, K), dtype=f32, device=dev)
+    _need(o, "o", (B, T, H, V), odt, dev)
     _need(k_tilde_out, "k_tilde_out", (B, T, H, K), dt, dev)
     desc = make_desc(B, T, H, K, V, dtype=_dtype_code(q), eta=eta, d_min=d_min, d_max=d_max,
-                     clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware, r_per_key=rvec)
+                     clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware, r_per_key=rvec,
+                     o_f32=o_f32)
     need = int(load().osdn_kda_fwd_workspace_bytes(ctypes.byref(desc)))
     workspace = _workspace(workspace, need, dev)
     _check(load().osdn_kda_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r),
@@ -364,7 +374,7 @@ def kda_fwd_workspace_bytes(B, T, H, K, V, dtype=BF16) -> int:
 def fwd_varlen(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, cu_seqlens,
                max_seqlen=None, chunk=64, eta=0.003, d_min=0.5, d_max=2.0, clamp=True, eps=1e-6,
                q_scale=1.0, beta_aware=True, o=None, S_out=None, d_out=None, k_tilde_out=None,
-               workspace=None):
+               workspace=None, o_f32=False):
     """fwd over sequences packed on one token axis: q, k [1,total,H,K], v
     [1,total,H,V], beta/r/alpha [1,total,H]; cu_seqlens int64 [S+1] on the
     device (sequence b = tokens [cu[b], cu[b+1])); d1 [S,H,K], S0 [S,H,V,K].
@@ -386,16 +396,18 @@ def fwd_varlen(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, cu_seqlen
     _need(alpha, "alpha", (1, total, H), f32, dev)
     _need(d1, "d1", (S, H, K), f32, dev)
     _need(S0, "S0", (S, H, V, K), f32, dev)
+    odt = f32 if o_f32 else dt
     if o is None:
-        o = torch.empty((1, total, H, V), dtype=dt, device=dev)
+        o = torch.empty((1, total, H, V), dtype=odt, device=dev)
     if S_out is None:
         S_out = torch.empty((S, H, V, K), dtype=f32, device=dev)
     if d_out is None:
         d_out = torch.empty((S, H, K), dtype=f32, device=dev)
+    _need(o, "o", (1, total, H, V), odt, dev)
     _need(k_tilde_out, "k_tilde_out", (1, total, H, K), dt, dev)
     desc = make_desc(S, max_seqlen, H, K, V, dtype=_dtype_code(q), chunk=chunk, eta=eta,
                      d_min=d_min, d_max=d_max, clamp=clamp, eps=eps, q_scale=q_scale,
-                     beta_aware=beta_aware, r_per_key=rvec)
+                     beta_aware=beta_aware, r_per_key=rvec, o_f32=o_f32)
     need = int(load().osdn_fwd_workspace_bytes(ctypes.byref(desc)))
     workspace = _workspace(workspace, need, dev)
     _check(load().osdn_fwd_varlen(ctypes.byref(desc), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
@@ -407,7 +419,7 @@ def fwd_varlen(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, cu_seqlen
 
 def decode(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, eta=0.003, d_min=0.5,
            d_max=2.0, clamp=True, eps=1e-6, q_scale=1.0, beta_aware=True, o=None, S_out=None,
-           d_out=None):
+           d_out=None, o_f32=False):
     """Decode step (the single-token recurrence, one launch): T <= DECODE_MAX_T
     new tokens per (b,h) from the carried (d1, S0).  Shapes as in fwd.  Pass
     S_out=S0 and d_out=d1 to update the state in place.
@@ -422,17 +434,19 @@ def decode(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, eta=0.003, d_
     _need(alpha, "alpha", (B, T, H), f32, dev)
     _need(d1, "d1", (B, H, K), f32, dev)
     _need(S0, "S0", (B, H, V, K), f32, dev)
+    odt = f32 if o_f32 else dt
     if o is None:
-        o = torch.empty((B, T, H, V), dtype=dt, device=dev)
+        o = torch.empty((B, T, H, V), dtype=odt, device=dev)
     if S_out is None:
         S_out = torch.empty((B, H, V, K), dtype=f32, device=dev)
     if d_out is None:
         d_out = torch.empty((B, H, K), dtype=f32, device=dev)
-    _need(o, "o", (B, T, H, V), dt, dev)
+    _need(o, "o", (B, T, H, V), odt, dev)
     _need(S_out, "S_out", (B, H, V, K), f32, dev)
     _need(d_out, "d_out", (B, H, K), f32, dev)
     desc = make_desc(B, T, H, K, V, dtype=_dtype_code(q), eta=eta, d_min=d_min, d_max=d_max,
-                     clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware, r_per_key=rvec)
+                     clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware, r_per_key=rvec,
+                     o_f32=o_f32)
     _check(load().osdn_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r),
                               _ptr(alpha), _ptr(d1), _ptr(S0), _ptr(o), _ptr(S_out), _ptr(d_out),
                               _stream(dev)))
@@ -446,12 +460,13 @@ def bwd_workspace_bytes(B, T, H, K, V, dtype=BF16) -> int:
 
 def bwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, dout, dS=None, dd=None,
         eta=0.003, d_min=0.5, d_max=2.0, clamp=True, eps=1e-6, q_scale=1.0, beta_aware=True,
-        workspace=None):
+        workspace=None, o_f32=False):
     """Backward pass of fwd: gradients of L given dout = dL/do [B,T,H,V] (dtype
     of q), dS = dL/dS_T [B,H,V,K] f32 and dd = dL/dd_{T+1} [B,H,K] f32 (both
     optional).  Returns a dict: dq, dk [B,T,H,K] and dv [B,T,H,V] in q's dtype;
     dbeta [B,T,H], dr and dalpha [B,T,H] (None when r / alpha are None),
-    dd1 [B,H,K], dS0 [B,H,V,K] in f32."""
+    dd1 [B,H,K], dS0 [B,H,V,K] in f32.  o_f32=True returns dq, dk, dv in float32
+    (before the rounding to q's dtype)."""
     B, T, H, K = q.shape
     V = v.shape[-1]
     dev, dt, f32 = q.device, q.dtype, torch.float32
@@ -465,14 +480,17 @@ def bwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, dout, dS=None, d
     _need(dout, "dout", (B, T, H, V), dt, dev)
     _need(dS, "dS", (B, H, V, K), f32, dev)
     _need(dd, "dd", (B, H, K), f32, dev)
-    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+    gdt = f32 if o_f32 else dt
+    out = {"dq": torch.empty_like(q, dtype=gdt), "dk": torch.empty_like(k, dtype=gdt),
+           "dv": torch.empty_like(v, dtype=gdt),
            "dbeta": torch.empty((B, T, H), dtype=f32, device=dev),
            "dr": torch.empty((B, T, H), dtype=f32, device=dev) if r is not None else None,
            "dalpha": torch.empty((B, T, H), dtype=f32, device=dev) if alpha is not None else None,
            "dd1": torch.empty((B, H, K), dtype=f32, device=dev),
            "dS0": torch.empty((B, H, V, K), dtype=f32, device=dev)}
     desc = make_desc(B, T, H, K, V, dtype=_dtype_code(q), eta=eta, d_min=d_min, d_max=d_max,
-                     clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware, r_per_key=rvec)
+                     clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware, r_per_key=rvec,
+                     o_f32=o_f32)
     need = int(load().osdn_bwd_workspace_bytes(ctypes.byref(desc)))
     workspace = _workspace(workspace, need, dev)
     _check(load().osdn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r),

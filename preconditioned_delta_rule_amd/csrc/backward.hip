@@ -308,7 +308,6 @@ __global__ __launch_bounds__(1024) void bwd_p2_kernel(BwdArgs a) {
   const TIn *qp = static_cast<const TIn *>(a.q);
   const TIn *kp = static_cast<const TIn *>(a.k);
   const TIn *dop = static_cast<const TIn *>(a.dout);
-  TIn *dvp = static_cast<TIn *>(a.dv);
   const int64_t tok0 = b * T * H + h;
 
   for (int64_t blk = NB - 1; blk >= 0; --blk) {
@@ -432,7 +431,7 @@ __global__ __launch_bounds__(1024) void bwd_p2_kernel(BwdArgs a) {
     }
     for (int e = tid; e < nb * VS; e += nt) {
       const int t = e / VS, il = e - t * VS;
-      if (il < ncol) dvp[(tok0 + (t0 + t) * H) * V + c0 + il] = from_f32<TIn>(sDv[t][il]);
+      if (il < ncol) store_out<TIn>(a.dv, (tok0 + (t0 + t) * H) * V + c0 + il, sDv[t][il], a.o_f32);
     }
     if (tid < nb) {
       const int64_t x = (int64_t)q * tok + tok0 + (t0 + tid) * H;
@@ -473,8 +472,6 @@ __global__ __launch_bounds__(640) void bwd_p1_kernel(BwdArgs a) {
   const int NQ = a.nq;
   const P1 p{a.eta, a.eps, a.d_min, a.d_max, a.clamp != 0, a.beta_aware != 0};
   const TIn *kp = static_cast<const TIn *>(a.k);
-  TIn *dkp = static_cast<TIn *>(a.dk);
-  TIn *dqp = static_cast<TIn *>(a.dq);
   const int64_t tok0 = b * T * H + h;
 
   auto stage = [&](int64_t blk, int buf) {
@@ -508,7 +505,7 @@ __global__ __launch_bounds__(640) void bwd_p1_kernel(BwdArgs a) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
           const int e = gt + 128 * u, t = e >> 7, j = e & 127;
-          if (j < K && t < nb) dqp[(tok0 + (t0 + t) * H) * K + j] = from_f32<TIn>(a.q_scale * x[u]);
+          if (j < K && t < nb) store_out<TIn>(a.dq, (tok0 + (t0 + t) * H) * K + j, a.q_scale * x[u], a.o_f32);
         }
       } else {
         float(*dst)[BP] = grp == 0 ? sK[buf] : (grp == 1 ? sDkt[buf] : sDkr[buf]);
@@ -596,7 +593,7 @@ __global__ __launch_bounds__(640) void bwd_p1_kernel(BwdArgs a) {
           const float ds = fmaf(c, gy[e], gc * fmaf(dca, dv[e], dcn));
           if (j < K) {
             const float dk = sDkr[buf][t][lane + 64 * e] + fmaf(2.0f * k[e], ds, dkt[e] * dv[e]);
-            dkp[tr * K + j] = from_f32<TIn>(dk);
+            store_out<TIn>(a.dk, tr * K + j, dk, a.o_f32);
           }
           g[e] = j < K ? fmaf(dkt[e], k[e], fmaf(rt, gy[e], dca * s[e] * gc)) : 0.0f;
         }

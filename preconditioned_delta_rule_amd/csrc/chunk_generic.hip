@@ -60,7 +60,6 @@ __global__ __launch_bounds__(GEN_THREADS) void chunk_generic_kernel(ChunkArgs a,
   const TIn *k = static_cast<const TIn *>(a.k);
   const TIn *kt = static_cast<const TIn *>(a.kt);
   const TIn *v = static_cast<const TIn *>(a.v);
-  TIn *o = static_cast<TIn *>(a.o);
 
   for (int e = tid; e < VT * K; e += GEN_THREADS) {
     int r = e / (int)K, c = e % (int)K;
@@ -159,7 +158,7 @@ __global__ __launch_bounds__(GEN_THREADS) void chunk_generic_kernel(ChunkArgs a,
       if (i < L && r < vn) {
         float acc = sP[i * VT + r];
         for (int j = 0; j <= i; ++j) acc += sM[i * CP + j] * sR[j * VT + r];
-        o[((tb + t0 + i) * H + h) * V + v0 + r] = from_f32<TIn>(acc);
+        store_out<TIn>(a.o, ((tb + t0 + i) * H + h) * V + v0 + r, acc, a.o_f32);
       }
     }
     const float gL = GATED ? sG[L - 1] : 0.0f;

@@ -125,7 +125,6 @@ __global__ __launch_bounds__(NTHREADS) void chunk_mfma_kernel(ChunkArgs a) {
   const bf16 *gk = static_cast<const bf16 *>(a.k);
   const bf16 *gkt = static_cast<const bf16 *>(a.kt);
   const bf16 *gv = static_cast<const bf16 *>(a.v);
-  bf16 *go = static_cast<bf16 *>(a.o);
   const int64_t tstride = H * KD;                 // elements between tokens (K == V == 128)
   const int64_t base = (b * T) * tstride + h * KD;  // token 0 of this (b,h)
 
@@ -447,7 +446,7 @@ __global__ __launch_bounds__(NTHREADS) void chunk_mfma_kernel(ChunkArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = m0 + 4 * lq + i;
-        if (m < Lc) go[base + (t0 + m) * tstride + v0 + 16 * ct + l16] = to_bf16(a.q_scale * acc[i]);
+        if (m < Lc) store_out<bf16>(a.o, base + (t0 + m) * tstride + v0 + 16 * ct + l16, a.q_scale * acc[i], a.o_f32);
       }
     }
     // ---- stage S: state update, then its bf16 pair for the next chunk

@@ -45,10 +45,34 @@ constexpr int KD = 128;    // key dim
 constexpr int VD = 128;    // value dim
 constexpr int VT = 32;     // value rows per sweep workgroup
 constexpr int NT = VD / VT;
-constexpr int KP = KD + 16; // LDS pitch (bf16) of the sweep's 128-wide rows: 288 B keeps 16-row operand reads conflict-free
 constexpr int TKP = KD + 8; // the same in the UT transform, whose workgroups must fit three to a CU
 constexpr int CP = C + 8;  // LDS pitch (bf16) of 64-wide rows
 constexpr int AP = C + 4;  // LDS pitch (f32) of the Gram
+
+// The (I + A)^-1 operands of a chunk as the sweep reads them: block j of
+// (mt, s) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1) (the blocks
+// below and on the diagonal), lane l = (l16, g) holding row 16 mt + l16 at
+// columns 32 s + 4 g + {0..3} and 32 s + 16 + 4 g + {0..3} (tile order).
+constexpr int TDUMP = 6 * 64 * 8;  // bf16 elements per chunk
+// The intra-chunk scores lower([e^{g_i - g_j}] . Q K~^T) as the sweep's
+// output products read them: blocks j as above, each as hi then lo bf16
+// (block 2 j + 0 / 2 j + 1), lane (l16, g) holding score row 16 mt + l16 at
+// key positions 32 s + 4 g + {0..3} and 32 s + 16 + 4 g + {0..3}.
+constexpr int MDUMP = 12 * 64 * 8;
+constexpr int CHUNKW = TDUMP + MDUMP;  // workspace per chunk: Tm operands, then the scores
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// hi / lo bf16 pairs of two result tiles, packed as tile-order operands
+__device__ __forceinline__ void split8(floatx4 a, floatx4 b, bf16x8 &hi, bf16x8 &lo) {
+  bf16x4 ah, al, bh, bl;
+  split4(a, ah, al);
+  split4(b, bh, bl);
+  hi = cat8(ah, bh);
+  lo = cat8(al, bl);
+}
 
 template <int N>
 struct IConst {
@@ -78,8 +102,13 @@ struct TinvLay {
 // d_{t+1} = clip(r_t d_t + c_t k_t^2), the same fp32 expressions as the
 // phase-1 emit kernel -- and written for the sweep kernel, so phase 1 need
 // not write it and this kernel need not read it.
+// The chunk's intra scores are formed here as well (state-independent), so
+// that the sweep only multiplies them: wave w forms the scores of token rows
+// [16 w, 16 w + 16) against every earlier key of the chunk.
+// A chunk the chunked phase 1 marked as pinned on d_min (a.pin, residual form)
+// has write keys d_min k: its Gram and scores are d_min times those of k.
 template <bool GATED, bool KRES, bool EMIT, bool VL, bool RVEC = false>
-__global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout, int64_t N, EmitArgs em) {
+__global__ __launch_bounds__(256, 3) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout, int64_t N, EmitArgs em) {
   static_assert(KRES || !EMIT, "the folded replay produces the residual form");
   typedef TinvLay L;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
@@ -100,12 +129,14 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
   const int64_t H = a.H;
   const bf16 *gk = static_cast<const bf16 *>(a.k);
   const bf16 *gkt = static_cast<const bf16 *>(a.kt);
+  const bf16 *gq = static_cast<const bf16 *>(a.q);
   const int64_t tstride = H * KD;
   const int64_t nch = a.B * H * N;
+  const int *pins = KRES ? a.pin : nullptr;
   // Each workgroup takes chunks blockIdx.x, blockIdx.x + gridDim.x, ...; the
   // next chunk's key rows (and write-key rows off the folded path), beta,
   // alpha and pin word are loaded into registers while this one is computed.
-  bf16x8 px[4], pe[4];
+  bf16x8 px[4], pe[4], pq[4];
   float pb = 0.0f, pa = 1.0f;
   int ppin = 0;
   auto fetch = [&](int64_t ci) {
@@ -116,19 +147,26 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
     if (VL && t0 >= T) return;  // past a shorter sequence's end: skipped below
     const int Lc = (int)((T - t0) < C ? (T - t0) : C);
     const int64_t base = (tb + t0) * tstride + h * KD;
+    ppin = pins ? __builtin_amdgcn_readfirstlane(pins[ci]) : 0;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int vi = tid + 256 * p, i = vi >> 4, c8 = 8 * (vi & 15);
       const int64_t off = base + (i < Lc ? i : 0) * tstride + c8;
       px[p] = ld8(gk + off);
-      if constexpr (!EMIT) pe[p] = ld8(gkt + off);
+      if (!EMIT && ppin != 2) pe[p] = ld8(gkt + off);
+    }
+    // queries of this wave's score rows, as B operands (lane (n, g): row
+    // 16 w + n, columns 32 kk + 8 g ..)
+    {
+      const int i = 16 * w + l16;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) pq[kk] = ld8(gq + base + (i < Lc ? i : 0) * tstride + 32 * kk + 8 * lq);
     }
     if (w == 0) {
       const int64_t gi = (tb + t0 + (l < Lc ? l : 0)) * H + h;
       pb = a.beta[gi];
       if constexpr (GATED) pa = a.alpha[gi];
     }
-    if constexpr (EMIT) ppin = em.pin[ci];
   };
   if ((int64_t)blockIdx.x < nch) fetch(blockIdx.x);
   for (int64_t ci = blockIdx.x; ci < nch; ci += gridDim.x) {
@@ -149,28 +187,19 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
   //      zero past T), beta and the cumulative log decay
   // A chunk the phase-1 sweep took as pinned (marked 2) starts from d_min,
   // and its mark guarantees that every step clips back to d_min (the mark
-  // tests the replay's own fp32 expression at the largest key square), so
-  // its residual is E = (d_min - 1) k, computed here in parallel and bitwise
-  // equal to the token-by-token replay below.
-  const bool pinned = EMIT && __builtin_amdgcn_readfirstlane(ppin) == 2;
+  // tests the replay's own fp32 expression at the largest key square), so its
+  // write keys are d_min k: no replay, no residual.
+  const bool pinned = ppin == 2;
+  const float kscale = pinned ? a.d_min : 1.0f;  // write keys d_min k
+  const bf16x8 qop[4] = {pq[0], pq[1], pq[2], pq[3]};
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int vi = tid + 256 * p, i = vi >> 4, c8 = 8 * (vi & 15);
     *reinterpret_cast<bf16x8 *>(&sKl[i][c8]) = i < Lc ? px[p] : bf16x8{};
-    if constexpr (EMIT) {
-      if (pinned) {
-        const float dm1 = em.d_min - 1.0f;  // exact on [0.5, 2]
-        bf16x8 e;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) e[q] = to_bf16(dm1 * to_f32(px[p][q]));
-        *reinterpret_cast<bf16x8 *>(&sKh[i][c8]) = i < Lc ? e : bf16x8{};
-      }
-    } else {
-      // write keys (with the residual form k~ = k + E both k and E are exact
-      // bf16 operands, so the Gram is K E^T + K K^T; otherwise the bf16 k~
-      // rows themselves)
-      *reinterpret_cast<bf16x8 *>(&sKh[i][c8]) = i < Lc ? pe[p] : bf16x8{};
-    }
+    // write keys (with the residual form k~ = k + E both k and E are exact
+    // bf16 operands, so the Gram is K E^T + K K^T; otherwise the bf16 k~
+    // rows themselves)
+    if (!EMIT && !pinned) *reinterpret_cast<bf16x8 *>(&sKh[i][c8]) = i < Lc ? pe[p] : bf16x8{};
   }
   if (w == 0) {
     const bool ok = l < Lc;
@@ -234,12 +263,57 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
       }
       __syncthreads();
     }
-    // the residual rows, for the sweep kernel
-    bf16 *res = em.res + base;
+    // the residual rows, for the sweep kernel (which takes a pinned chunk's
+    // write keys as d_min k and does not read them)
+    if (!pinned) {
+      bf16 *res = em.res + base;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int vi = tid + 256 * p, i = vi >> 4, c8 = 8 * (vi & 15);
-      if (i < Lc) *reinterpret_cast<bf16x8 *>(res + i * tstride + c8) = ld8(&sKh[i][c8]);
+      for (int p = 0; p < 4; ++p) {
+        const int vi = tid + 256 * p, i = vi >> 4, c8 = 8 * (vi & 15);
+        if (i < Lc) *reinterpret_cast<bf16x8 *>(res + i * tstride + c8) = ld8(&sKh[i][c8]);
+      }
+    }
+  }
+
+  // scores of token rows [16 w, 16 w + 16): tiles (jt, w) of M^T = K~ Q^T,
+  // jt <= w (lane (n, g) of tile jt holds M[16 w + n][16 jt + 4 g + i], the
+  // sweep's A operand in tile order), masked to the causal part, with the
+  // decay ratios, as hi/lo bf16 pairs
+  {
+    floatx4 acc[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) acc[jt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int ko = 32 * kk + 8 * lq;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        if (jt <= w) {
+          if (KRES || pinned) acc[jt] = mfma32(ld8(&sKl[16 * jt + l16][ko]), qop[kk], acc[jt]);
+          if (!pinned) acc[jt] = mfma32(ld8(&sKh[16 * jt + l16][ko]), qop[kk], acc[jt]);
+        }
+      }
+    }
+    const int t = 16 * w + l16;
+    const float gt = GATED ? sG[t] : 0.0f;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tj = 16 * jt + 4 * lq + i;
+        const float ratio = GATED ? __expf(gt - sG[tj]) : 1.0f;
+        acc[jt][i] = (jt <= w && tj <= t) ? kscale * ratio * acc[jt][i] : 0.0f;
+      }
+    bf16 *md = tout + ci * CHUNKW + TDUMP;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      if (2 * sb <= w) {
+        const int j = w < 2 ? w : 2 + 2 * (w - 2) + sb;  // block (mt = w, s = sb)
+        bf16x8 hi, lo;
+        split8(acc[2 * sb], acc[2 * sb + 1], hi, lo);
+        *reinterpret_cast<bf16x8 *>(md + ((2 * j) * 64 + l) * 8) = hi;
+        *reinterpret_cast<bf16x8 *>(md + ((2 * j + 1) * 64 + l) * 8) = lo;
+      }
     }
   }
 
@@ -262,12 +336,14 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
 #pragma unroll
         for (int q = 0; q < ns; ++q) {
           ka[q] = ld8(&sKl[16 * rts[q] + l16][ko]);
-          bh[q] = ld8(&sKh[16 * tjs[q] + l16][ko]);
-          if constexpr (KRES) bl[q] = ld8(&sKl[16 * tjs[q] + l16][ko]);
+          if (!pinned) bh[q] = ld8(&sKh[16 * tjs[q] + l16][ko]);
+          if (KRES || pinned) bl[q] = ld8(&sKl[16 * tjs[q] + l16][ko]);
         }
+        if (!pinned) {
 #pragma unroll
-        for (int q = 0; q < ns; ++q) acc[q] = mfma32(ka[q], bh[q], acc[q]);
-        if constexpr (KRES) {
+          for (int q = 0; q < ns; ++q) acc[q] = mfma32(ka[q], bh[q], acc[q]);
+        }
+        if (KRES || pinned) {
 #pragma unroll
           for (int q = 0; q < ns; ++q) acc[q] = mfma32(ka[q], bl[q], acc[q]);
         }
@@ -286,7 +362,7 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
         for (int i = 0; i < 4; ++i) {
           const int mrow = 16 * rt + 4 * lq + i;
           const float ratio = GATED ? __expf(sG[mrow] - gn) : 1.0f;
-          sA[mrow][nn] = nn < mrow ? sBeta[mrow] * ratio * acc[q][i] : 0.0f;
+          sA[mrow][nn] = nn < mrow ? sBeta[mrow] * ratio * kscale * acc[q][i] : 0.0f;
         }
       }
     }
@@ -359,12 +435,16 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
     for (int i = 0; i < 4; ++i) sTr[16 * p + 4 * lq + i][16 * q + l16] = to_bf16(-Y[i]);
   }
   __syncthreads();
-  // Tm rows to the workspace: 64 x 64 bf16, two 16-byte vectors per thread
-  bf16 *dst = tout + ci * (C * C);
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int v = tid + 256 * p, r = v >> 3, c8 = (v & 7) * 8;
-    *reinterpret_cast<bf16x8 *>(dst + r * C + c8) = ld8(&sTr[r][c8]);
+  // Tm to the workspace in the sweep's operand order: block j of
+  // (mt, s) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1), lane (l16, g) holding row
+  // 16 mt + l16 at columns 32 s + 4 g + {0..3} and 32 s + 16 + 4 g + {0..3}
+  // (the blocks above the diagonal are zero and are not stored)
+  bf16 *dst = tout + ci * CHUNKW;
+  for (int e = tid; e < 6 * 64; e += 256) {
+    const int j = e >> 6, ln = e & 63;
+    const int mt = j < 2 ? j : 2 + ((j - 2) >> 1), sb = j < 2 ? 0 : ((j - 2) & 1);
+    const int row = 16 * mt + (ln & 15), c0 = 32 * sb + 4 * (ln >> 4);
+    *reinterpret_cast<bf16x8 *>(dst + e * 8) = cat8(ld4(&sTr[row][c0]), ld4(&sTr[row][c0 + 16]));
   }
   __syncthreads();  // the next chunk's rows overwrite Tm's buffers
   }
@@ -375,8 +455,7 @@ __global__ __launch_bounds__(256) void chunk_tinv_kernel(ChunkArgs a, bf16 *tout
 // 16 lanes, with D[i][p] the p-th bf16 at lane i's address, lane j receives
 // D[4 e + j / 4][j % 4] as element e.  Lane i of the group pointing at row
 // r0 + i / 4, column c0 + 4 (i % 4) of a row-major bf16 matrix X therefore
-// receives X[r0 + e][c0 + j], e < 4: four consecutive rows of column c0 + j,
-// which is the B operand layout of the matrix cores with k running over rows.
+// receives X[r0 + e][c0 + j], e < 4: four consecutive rows of column c0 + j.
 __device__ __forceinline__ bf16x4 ld4_tr(const bf16 *p) {
   typedef short s4 __attribute__((ext_vector_type(4)));
   const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -384,88 +463,91 @@ __device__ __forceinline__ bf16x4 ld4_tr(const bf16 *p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-// B operand of a 16x16x32 product with k over the rows [r0, r0 + 32) and n
-// over the columns [c0, c0 + 16) of a row-major [.][P] bf16 matrix: lane l
-// (group g = l / 16) needs rows r0 + 8 g + e, e < 8, of column c0 + l % 16.
-// The A operand has the same lane layout, so the same read gives an A operand
-// with m over the columns from a matrix stored k-major.
-template <int P>
-__device__ __forceinline__ bf16x8 ld8_tr(const bf16 (*X)[P], int r0, int c0, int l) {
-  const int g = l >> 4, i = l & 15;
-  const bf16x4 a = ld4_tr(&X[r0 + 8 * g + (i >> 2)][c0 + 4 * (i & 3)]);
-  const bf16x4 b = ld4_tr(&X[r0 + 8 * g + 4 + (i >> 2)][c0 + 4 * (i & 3)]);
-  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// 64-wide bf16 rows without padding: the 16-byte chunk c of row r sits at
-// chunk c ^ (r & 7), which keeps 16-row operand reads, transposed reads and
-// 8-byte epilogue stores free of bank conflicts.  Element offset of (r, c):
-__device__ __forceinline__ int sx(int r, int c) { return r * 64 + ((((c >> 3) ^ r) & 7) << 3) + (c & 7); }
-
-// 128-wide bf16 rows without padding: chunk c of row r at chunk c ^ (r & 15)
+// 128-wide bf16 rows without padding: the 16-byte chunk c of row r sits at
+// chunk c ^ (r & 15), so that sixteen consecutive rows read at one column
+// hit sixteen different chunk positions.  Element offset of (r, c):
 __device__ __forceinline__ int sx128(int r, int c) { return r * 128 + ((((c >> 3) ^ r) & 15) << 3) + (c & 7); }
 
-// ld8_tr over an sx-layout matrix (each 8-byte read stays inside one chunk)
-__device__ __forceinline__ bf16x8 ld8_tr_sx(const bf16 *X, int r0, int c0, int l) {
-  const int g = l >> 4, i = l & 15, c = c0 + 4 * (i & 3);
-  const bf16x4 a = ld4_tr(X + sx(r0 + 8 * g + (i >> 2), c));
-  const bf16x4 b = ld4_tr(X + sx(r0 + 8 * g + 4 + (i >> 2), c));
-  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+// Contraction slabs in "tile order".  A 16 x 16 result tile leaves lane
+// (n = l % 16, g = l / 16) holding rows 4 g .. 4 g + 3 of column n.  Two such
+// tiles covering rows [32 s, 32 s + 32) of a matrix therefore give every lane
+// the B operand of a 16x16x32 product over those rows with the contraction
+// index kappa = 8 g + p mapped to row 32 s + 4 g + p (p < 4) or
+// 32 s + 16 + 4 g + (p - 4) (p >= 4) -- no data movement.  The A operand of
+// the same product must then take its columns in that order: two 8-byte
+// pieces per lane instead of one 16-byte read.
+__device__ __forceinline__ bf16x8 lda_tile_order(const bf16 *X, int row, int s, int g) {
+  const int c0 = 32 * s + 4 * g;
+  return cat8(*reinterpret_cast<const bf16x4 *>(X + sx128(row, c0)),
+              *reinterpret_cast<const bf16x4 *>(X + sx128(row, c0 + 16)));
+}
+// A operand with m over columns [16 kt, 16 kt + 16) of a row-major key matrix
+// and the contraction over its rows in tile order (slab s): transposed reads.
+__device__ __forceinline__ bf16x8 lda_tr_tile_order(const bf16 *X, int kt, int s, int g, int j) {
+  const int col = 16 * kt + 4 * (j & 3), r = 32 * s + 4 * g + (j >> 2);
+  return cat8(ld4_tr(X + sx128(r, col)), ld4_tr(X + sx128(r + 16, col)));
 }
 
-struct SeqLay {
-  static constexpr int Q = 0;                        // bf16 [C][KP]  queries
-  static constexpr int K = Q + C * KP * 2;           // bf16 [C][KP]  keys
-  static constexpr int E = K + C * KP * 2;           // bf16 [C][KP]  write keys, or residual E
-  static constexpr int V = E + C * KP * 2;           // bf16 [C][VT+8] value tile
-  static constexpr int BETA = V + C * (VT + 8) * 2;  // f32 [C]
-  static constexpr int G = BETA + C * 4;             // f32 [C] cumulative log decay
-  // 64-wide rows below are unpadded, 16-byte chunks swizzled (sx)
-  static constexpr int MH = G + C * 4;               // bf16 [C][C]   scores^T hi
-  static constexpr int ML = MH + C * C * 2;          // bf16 [C][C]   scores^T lo
-  static constexpr int RTH = ML + C * C * 2;         // bf16 [VT][C]  R^T hi
-  static constexpr int RTL = RTH + VT * C * 2;       // bf16 [VT][C]  R^T lo
-  static constexpr int DTH = RTL + VT * C * 2;       // bf16 [VT][C]  Delta^T hi
-  static constexpr int DTL = DTH + VT * C * 2;       // bf16 [VT][C]  Delta^T lo
-  static constexpr int DSH = DTL + VT * C * 2;       // bf16 [VT][C]  decayed Delta^T hi
-  static constexpr int DSL = DSH + VT * C * 2;       // bf16 [VT][C]  decayed Delta^T lo
-  static constexpr int SH = DSL + VT * C * 2;        // bf16 [VT][KD] state hi (sx128 layout)
-  static constexpr int SL = SH + VT * KD * 2;        // bf16 [VT][KD] state lo
-  static constexpr int TOTAL = SL + VT * KD * 2;
-  static_assert(TOTAL <= 160 * 1024, "LDS budget");
+// One 16-byte (or 4-byte) global -> LDS copy per lane (global_load_lds):
+// lane i of the wave writes bytes [16 i, 16 i + 16) ([4 i, 4 i + 4)) after
+// `lds`, which must be the same for every lane.
+__device__ __forceinline__ void dma16(const void *src, void *lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *src, void *lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 4, 0, 0);
+}
+// Workgroup barrier that does not wait for this wave's outstanding global
+// loads (the copies into the other LDS buffer stay in flight across it); LDS
+// writes before it are complete.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS of one chunk's inputs (the sweep keeps two: the current chunk and the
+// next one, which arrives by global_load_lds while the current one is used).
+struct SwBuf {
+  static constexpr int Q = 0;               // bf16 [64][128] queries (sx128)
+  static constexpr int K = Q + C * KD * 2;  // bf16 [64][128] keys (sx128)
+  static constexpr int W = K + C * KD * 2;  // bf16 [64][128] write-key residual E, or k~ itself (sx128)
+  static constexpr int V = W + C * KD * 2;  // bf16 [64][32] value tile
+  static constexpr int BETA = V + C * 32 * 2;  // f32 [64], zero past the chunk end
+  static constexpr int G = BETA + C * 4;       // f32 [64] cumulative log decay
+  static constexpr int BYTES = G + C * 4;
 };
 
-// With the residual form (KRES) the write key is k~ = k + E with k and E both
-// exact bf16, so every product with k~ is the sum of a product with k and one
-// with E; otherwise the E buffer holds the bf16 k~ itself.
+// Phase 2 sweep over the chunks of one (b,h) and 32 value rows.  Four waves:
+//  waves 0, 1 ("chain" waves) own value rows v0 + 16 w .. + 16 of the state
+//    with every key column, as 16 x 16 tiles of S^T in registers, and run the
+//    state-dependent chain of every chunk without waiting for any other wave:
+//      X = K S^T, R = B (V - diag(e^g) X), Delta = Tm R,
+//      S <- e^{g_L} S + Delta^T (e^{g_L - g} . K~)
+//    (S as hi + lo bf16 operands taken straight from the result tiles in
+//    tile order; K~ = k + E as the two exact bf16 operands k and E, or d_min k
+//    on a chunk phase 1 took as pinned on d_min);
+//  waves 2, 3 ("helper" waves) issue the next chunk's loads and produce the
+//    outputs of two token-row tiles each,
+//      O = q_scale (diag(e^g) Q S^T + scores Delta),
+//    from S and Delta, which the chain waves leave in LDS as their operand
+//    registers, and the scores, formed chunk-parallel beside Tm.
+// Two barriers per chunk: after the chain waves have Delta (and the helpers
+// Q S^T), and at the end of the chunk (next chunk's inputs in place, the new
+// state written out).
 template <bool GATED, bool KRES, bool VL>
-__global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 *tin, int64_t N) {
-  typedef SeqLay L;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
-  bf16(*sQ)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::Q);
-  bf16(*sK)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::K);
-  bf16(*sE)[KP] = reinterpret_cast<bf16(*)[KP]>(smem + L::E);
-  bf16(*sV)[VT + 8] = reinterpret_cast<bf16(*)[VT + 8]>(smem + L::V);
-  float *sBeta = reinterpret_cast<float *>(smem + L::BETA);
-  float *sG = reinterpret_cast<float *>(smem + L::G);
-  bf16 *sMh = reinterpret_cast<bf16 *>(smem + L::MH);  // [n][m], sx layout
-  bf16 *sMl = reinterpret_cast<bf16 *>(smem + L::ML);
-  bf16 *sRh = reinterpret_cast<bf16 *>(smem + L::RTH);  // [v][t], sx layout
-  bf16 *sRl = reinterpret_cast<bf16 *>(smem + L::RTL);
-  bf16 *sDh = reinterpret_cast<bf16 *>(smem + L::DTH);
-  bf16 *sDl = reinterpret_cast<bf16 *>(smem + L::DTL);
-  bf16 *sDsh = reinterpret_cast<bf16 *>(smem + (GATED ? L::DSH : L::DTH));
-  bf16 *sDsl = reinterpret_cast<bf16 *>(smem + (GATED ? L::DSL : L::DTL));
-  bf16 *sSh = reinterpret_cast<bf16 *>(smem + L::SH);  // [v][k], sx128 layout
-  bf16 *sSl = reinterpret_cast<bf16 *>(smem + L::SL);
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
+  typedef SwBuf L;
+  __shared__ __attribute__((aligned(16))) unsigned char lb0[L::BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lb1[L::BYTES];
+  // the chain waves' S operands [chain][s hi, s lo ...][lane] and Delta operands [chain][slot][lane]
+  __shared__ bf16x8 sdump[2][8][64];
+  __shared__ bf16x8 ddump[2][4][64];
 
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l16 = l & 15, lq = l >> 4;
-  const int rw = w & 3, cw = w >> 2;  // token rows [16 rw, +16), value columns [16 cw, +16)
-  const int m0 = 16 * rw;
-  // XCD-aware placement: block i runs on XCD i % 8; the NT tiles of one
-  // sequence share i % 8, so their reads of the same keys meet in one L2.
+  const int l16 = l & 15, g = l >> 4;
+  const int hw = w & 1;  // chain index (value rows 16 hw ..) or helper index
+  // XCD-aware placement: block i runs on XCD i % 8; the NT value tiles of one
+  // sequence share i % 8, so their reads of the same rows meet in one L2.
   const int bid = blockIdx.x;
   const int slot = bid & 7, rest = bid >> 3;
   const int vt = rest % NT;
@@ -474,420 +556,358 @@ __global__ __launch_bounds__(512) void chunk_seq_kernel(ChunkArgs a, const bf16 
   if (seq >= a.B * H) return;
   const int64_t b = seq / H, h = seq - b * H;
   const int64_t T = seq_len<VL>(a, b), tb = seq_base<VL>(a, b);
-  const int64_t Nb = (T + C - 1) / C;  // this sequence's chunks (N is the workspace row stride)
+  const int64_t Nb = (T + C - 1) / C;
   const int v0 = vt * VT;
 
-  const bf16 *gq = static_cast<const bf16 *>(a.q);
-  const bf16 *gk = static_cast<const bf16 *>(a.k);
-  const bf16 *gkt = static_cast<const bf16 *>(a.kt);
-  const bf16 *gv = static_cast<const bf16 *>(a.v);
-  bf16 *go = static_cast<bf16 *>(a.o);
-  const int64_t tstride = H * KD;                   // elements between tokens (K == V == 128)
-  const int64_t base = tb * tstride + h * KD;  // token 0 of this (b,h)
-  const bf16 *tseq = tin + seq * N * (C * C);
-
-  // scores: the tiles above the diagonal are never written and stay zero
-  for (int i = tid; i < C * C / 8; i += 512) {
-    reinterpret_cast<bf16x8 *>(sMh)[i] = bf16x8{};
-    reinterpret_cast<bf16x8 *>(sMl)[i] = bf16x8{};
-  }
-  // Roles: waves 4-7 ("row waves") own token rows [16 rw, 16 rw + 16) of the
-  // chunk for K S^T, Q S^T, R and O, over both 16-column value tiles; waves
-  // 0-3 compute the score tiles, then own the state columns
-  // [32 sp, 32 sp + 32) (sp = w) in accumulators, as tiles of S^T: element i
-  // of tile (rt, j) is S[16 rt + l16][16 (2 sp + j) + 4 lq + i].  Wave w
-  // shares a SIMD with wave w + 4; this way round measured faster than the
-  // reverse.
-  const bool roww = w >= 4;
-  const int sp = w & 3;
-  floatx4 Sacc[2][2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int vr = 16 * rt + l16, c = 16 * (2 * sp + j) + 4 * lq;
-      Sacc[rt][j] = a.S0 ? *reinterpret_cast<const floatx4 *>(a.S0 + (seq * VD + v0 + vr) * KD + c)
-                         : floatx4{0.f, 0.f, 0.f, 0.f};
-      if (!roww) {
-        bf16x4 sh4, sl4;
-        split4(Sacc[rt][j], sh4, sl4);
-        *reinterpret_cast<bf16x4 *>(sSh + sx128(vr, c)) = sh4;
-        *reinterpret_cast<bf16x4 *>(sSl + sx128(vr, c)) = sl4;
-      }
-    }
-
-  // ---- prefetch registers for one chunk (each input element is loaded once
-  //      per workgroup, in 16-byte vectors, 16 threads per token row)
-  //   q, k, E rows:  vectors tid and tid + 512 of each 64 x 128 tile
-  //   values:        threads < 256: token tid / 4, columns 8 (tid % 4) of the tile
-  //   Tm:            rows 16 rw + l16 in MFMA A-operand layout
-  // Tokens past T (last chunk only) read the chunk's first token instead and are never
-  // selected here: a select would wait for the load.  Their beta is zeroed
-  // at use, which makes their R and Delta rows zero; their scores fall
-  // outside the causal mask and their outputs are not stored.
-  // Addresses: a chunk's base pointers are wave-uniform (scalar registers);
-  // each lane adds a 32-bit byte offset fixed for the whole sweep (phase 2
-  // takes H <= 65536, so 64 token rows span at most 1 GiB).
+  const int64_t tstride = H * KD;
   const int64_t rowb = tstride * 2;  // bytes between tokens
-  const char *qb = reinterpret_cast<const char *>(gq + base);
-  const char *kb = reinterpret_cast<const char *>(gk + base);
-  const char *eb = reinterpret_cast<const char *>(gkt + base);
-  const char *vb = reinterpret_cast<const char *>(gv + base + v0);
-  char *ob = reinterpret_cast<char *>(go + base + v0);
-  const char *bb = reinterpret_cast<const char *>(a.beta + tb * H + h);
-  const char *ab = GATED ? reinterpret_cast<const char *>(a.alpha + tb * H + h) : nullptr;
-  uint32_t roff[2], coff[2];
-  int rrow[2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int vi = tid + 512 * p;
-    rrow[p] = vi >> 4;
-    coff[p] = (uint32_t)(16 * (vi & 15));
-    roff[p] = (uint32_t)(rrow[p] * rowb) + coff[p];
-  }
-  const int vrow = tid >> 2;
-  const uint32_t vcoff = (uint32_t)(16 * (tid & 3)), voff = (uint32_t)(vrow * rowb) + vcoff;
-  const uint32_t toff = (uint32_t)(((16 * rw + l16) * C + 8 * lq) * 2);
-  const uint32_t boff = (uint32_t)(l * H * 4);
-  const uint32_t ooff = (uint32_t)((m0 + 4 * lq) * rowb + 2 * l16);  // row waves, value tile 0
+  const int64_t base = tb * tstride + h * KD;
+  const bf16 *tseq = tdump + seq * N * CHUNKW;
+  const int *pins = KRES && a.pin ? a.pin + seq * N : nullptr;
+  // a chunk's mark from the chunked phase 1 (loaded a chunk or two ahead)
+  auto load_pin = [&](int64_t n) -> int { return pins && n < Nb ? pins[n] : 0; };
+  auto chunk_len = [&](int64_t n) -> int { return (int)((T - n * C) < C ? (T - n * C) : C); };
 
-  bf16x8 pq[2], pk[2], pe[2], pv, pt[2];
-  float pbeta = 0.0f, palpha = 1.0f;
-  // parts: FQ = q, values, beta (and alpha); FK = k; FE = E
-  constexpr int FQ = 1, FK = 2, FE = 4;
-  auto fetch = [&](int64_t n, int parts) {
-    const int64_t t0 = n * C;
-    const int Lc = (int)((T - t0) < C ? (T - t0) : C);
-    const int64_t cb = t0 * rowb;
+  if (w < 2) {
+    // ================================================================ chain waves
+    const int vc = v0 + 16 * hw;  // first value row
+    // tiles of S^T: element i of tile kt is S[vc + l16][16 kt + 4 g + i];
+    // Bh / Bl: S as hi / lo operands over the key index in tile order
+    floatx4 ST[8];
+    bf16x8 Bh[4], Bl[4];
+    bf16x8 Tm[6];  // this chunk's (I + A)^-1 operands
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const uint32_t o = rrow[p] < Lc ? roff[p] : coff[p];
-      if (parts & FQ) pq[p] = ld8(reinterpret_cast<const bf16 *>(qb + cb + o));
-      if (parts & FK) pk[p] = ld8(reinterpret_cast<const bf16 *>(kb + cb + o));
-      if (parts & FE) pe[p] = ld8(reinterpret_cast<const bf16 *>(eb + cb + o));
-    }
-    if (!(parts & FQ)) return;
-    if (tid < 256) pv = ld8(reinterpret_cast<const bf16 *>(vb + cb + (vrow < Lc ? voff : vcoff)));
-    if (w == 0) {
-      const int64_t sb = t0 * H * 4;
-      const uint32_t o = l < Lc ? boff : 0u;
-      pbeta = *reinterpret_cast<const float *>(bb + sb + o);
-      if constexpr (GATED) palpha = *reinterpret_cast<const float *>(ab + sb + o);
-    }
-  };
-  // Tm rows go straight into the registers stage D reads.  They are loaded
-  // once stage D of the previous chunk is done with them, which leaves a
-  // whole chunk for the load to land and needs no register copy (a copy into
-  // registers with a load in flight would wait for every outstanding load).
-  auto fetch_t = [&](int64_t n) {
-    const char *tp = reinterpret_cast<const char *>(tseq + n * (C * C)) + toff;
+    for (int kt = 0; kt < 8; ++kt)
+      ST[kt] = a.S0 ? *reinterpret_cast<const floatx4 *>(a.S0 + (seq * VD + vc + l16) * KD + 16 * kt + 4 * g)
+                    : floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) pt[kk] = ld8(reinterpret_cast<const bf16 *>(tp + 64 * kk));
-  };
+    for (int s = 0; s < 4; ++s) {
+      split8(ST[2 * s], ST[2 * s + 1], Bh[s], Bl[s]);
+      sdump[hw][2 * s][l] = Bh[s];
+      sdump[hw][2 * s + 1][l] = Bl[s];
+    }
+    if (Nb > 0) {
+#pragma unroll
+      for (int j = 0; j < 6; ++j) Tm[j] = ld8(tseq + (j * 64 + l) * 8);
+    }
+    int pin_next = load_pin(0);
+    lds_barrier();
 
-  if (Nb > 0) {
-    fetch(0, FQ | FK | FE);
-    fetch_t(0);
-  }
-  for (int64_t n = 0; n < Nb; ++n) {
-    const int64_t t0 = n * C;
-    const int Lc = (int)((T - t0) < C ? (T - t0) : C);
-    __syncthreads();  // the previous chunk is done with every LDS buffer
-    // ---- stage L: registers -> LDS
+    auto body = [&](int64_t n, const unsigned char *cur) {
+      const bf16 *sK = reinterpret_cast<const bf16 *>(cur + L::K);
+      const bf16 *sW = reinterpret_cast<const bf16 *>(cur + L::W);
+      const bf16 *sV = reinterpret_cast<const bf16 *>(cur + L::V);
+      const float *sBeta = reinterpret_cast<const float *>(cur + L::BETA);
+      const float *sG = reinterpret_cast<const float *>(cur + L::G);
+      const bool pinned = __builtin_amdgcn_readfirstlane(pin_next) == 2;
+      pin_next = load_pin(n + 1);
+      const bool more = n + 1 < Nb;
+      const float gL = GATED ? sG[C - 1] : 0.0f;
+
+      // X = K S^T (token rows x this wave's 16 value rows)
+      floatx4 X[4];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int vi = tid + 512 * p, i = vi >> 4, c8 = 8 * (vi & 15);
-      *reinterpret_cast<bf16x8 *>(&sQ[i][c8]) = pq[p];
-      *reinterpret_cast<bf16x8 *>(&sK[i][c8]) = pk[p];
-      *reinterpret_cast<bf16x8 *>(&sE[i][c8]) = pe[p];
+      for (int mt = 0; mt < 4; ++mt) X[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 ak[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) ak[mt] = lda_tile_order(sK, 16 * mt + l16, s, g);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) X[mt] = mfma32(ak[mt], Bh[s], X[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) X[mt] = mfma32(ak[mt], Bl[s], X[mt]);
+      }
+      // R = beta (V - e^g X); V[16 mt + 4 g + i][vc + l16] by one transposed read
+      floatx4 R[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x4 vv = ld4_tr(sV + (16 * mt + 4 * g + (l16 >> 2)) * 32 + 16 * hw + 4 * (l16 & 3));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * mt + 4 * g + i;
+          const float em = GATED ? __expf(sG[t]) : 1.0f;
+          R[mt][i] = sBeta[t] * (to_f32(vv[i]) - em * X[mt][i]);
+        }
+      }
+      bf16x8 Rh[2], Rl[2];
+      split8(R[0], R[1], Rh[0], Rl[0]);
+      split8(R[2], R[3], Rh[1], Rl[1]);
+      // Delta = Tm R (Tm lower triangular: token rows below 32 need slab 0 only)
+      floatx4 D[4];
+      D[0] = mfma32(Tm[0], Rh[0], floatx4{0.f, 0.f, 0.f, 0.f});
+      D[1] = mfma32(Tm[1], Rh[0], floatx4{0.f, 0.f, 0.f, 0.f});
+      D[2] = mfma32(Tm[2], Rh[0], floatx4{0.f, 0.f, 0.f, 0.f});
+      D[3] = mfma32(Tm[4], Rh[0], floatx4{0.f, 0.f, 0.f, 0.f});
+      D[0] = mfma32(Tm[0], Rl[0], D[0]);
+      D[1] = mfma32(Tm[1], Rl[0], D[1]);
+      D[2] = mfma32(Tm[2], Rl[0], D[2]);
+      D[3] = mfma32(Tm[4], Rl[0], D[3]);
+      D[2] = mfma32(Tm[3], Rh[1], D[2]);
+      D[3] = mfma32(Tm[5], Rh[1], D[3]);
+      D[2] = mfma32(Tm[3], Rl[1], D[2]);
+      D[3] = mfma32(Tm[5], Rl[1], D[3]);
+      // the next chunk's (I + A)^-1 operands (Tm is free now)
+      if (more) {
+        const bf16 *tp = tseq + (n + 1) * CHUNKW;
+#pragma unroll
+        for (int j = 0; j < 6; ++j) Tm[j] = ld8(tp + (j * 64 + l) * 8);
+      }
+      // Delta for the outputs (helper waves), as tile-order hi/lo operands
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 dh, dl;
+        split8(D[2 * s], D[2 * s + 1], dh, dl);
+        ddump[hw][2 * s][l] = dh;
+        ddump[hw][2 * s + 1][l] = dl;
+      }
+      // the state update's Delta: decayed to the chunk end, and scaled by
+      // d_min when the write keys are d_min k
+      const float dscale = pinned ? a.d_min : 1.0f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float f = dscale;
+          if (GATED) f *= __expf(gL - sG[16 * mt + 4 * g + i]);
+          D[mt][i] *= f;
+        }
+      bf16x8 Dh[2], Dl[2];
+      split8(D[0], D[1], Dh[0], Dl[0]);
+      split8(D[2], D[3], Dh[1], Dl[1]);
+      lds_barrier();  // ---- B2: Delta is in LDS, the helpers are done with S_n
+      // S <- e^{g_L} S + K~^T Delta
+      if (GATED) {
+        const float decay = __expf(gL);
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) ST[kt] = ST[kt] * decay;
+      }
+      if (!KRES || !pinned) {
+        // general write keys: K and E (residual form), or k~ alone
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+          for (int k0 = 0; k0 < 8; k0 += 4) {
+            bf16x8 ak[4], ae[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              if (KRES) ak[u] = lda_tr_tile_order(sK, k0 + u, s, g, l16);
+              ae[u] = lda_tr_tile_order(sW, k0 + u, s, g, l16);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              if (KRES) {
+                ST[k0 + u] = mfma32(ak[u], Dh[s], ST[k0 + u]);
+                ST[k0 + u] = mfma32(ak[u], Dl[s], ST[k0 + u]);
+              }
+              ST[k0 + u] = mfma32(ae[u], Dh[s], ST[k0 + u]);
+              ST[k0 + u] = mfma32(ae[u], Dl[s], ST[k0 + u]);
+            }
+          }
+        }
+      } else {
+        // write keys d_min k (Delta carries d_min)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          bf16x8 ak[8];
+#pragma unroll
+          for (int kt = 0; kt < 8; ++kt) ak[kt] = lda_tr_tile_order(sK, kt, s, g, l16);
+#pragma unroll
+          for (int kt = 0; kt < 8; ++kt) ST[kt] = mfma32(ak[kt], Dh[s], ST[kt]);
+#pragma unroll
+          for (int kt = 0; kt < 8; ++kt) ST[kt] = mfma32(ak[kt], Dl[s], ST[kt]);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        split8(ST[2 * s], ST[2 * s + 1], Bh[s], Bl[s]);
+        sdump[hw][2 * s][l] = Bh[s];
+        sdump[hw][2 * s + 1][l] = Bl[s];
+      }
+      lds_barrier();  // ---- B1 of the next chunk
+    };
+    for (int64_t n = 0; n < Nb; n += 2) {
+      body(n, lb0);
+      if (n + 1 < Nb) body(n + 1, lb1);
     }
-    if (tid < 256) *reinterpret_cast<bf16x8 *>(&sV[tid >> 2][8 * (tid & 3)]) = pv;
-    if (w == 0) {
-      const bool ok = l < Lc;
-      sBeta[l] = ok ? pbeta : 0.0f;
-      if constexpr (GATED) {
-        float x = ok ? logf(palpha) : 0.0f;
+    if (a.S_out) {
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt)
+        *reinterpret_cast<floatx4 *>(a.S_out + (seq * VD + vc + l16) * KD + 16 * kt + 4 * g) = ST[kt];
+    }
+  } else {
+    // ================================================================ helper waves
+    const char *qb = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.q) + base);
+    const char *kb = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.k) + base);
+    const char *eb = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.kt) + base);
+    const char *vb = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.v) + base + v0);
+    const char *bb = reinterpret_cast<const char *>(a.beta + tb * H + h);
+    const char *ab = GATED ? reinterpret_cast<const char *>(a.alpha + tb * H + h) : nullptr;
+    // per-lane byte offsets of the copies (within a chunk), fixed for the sweep:
+    //  128-wide rows: block j = 2 jj + hw (rows 4 j ..), lane l -> row 4 j + l / 16,
+    //  16-byte position l % 16 holding chunk (l % 16) ^ (row % 16) (sx128);
+    //  value tile: block j = 2 jj + hw (rows 16 j ..), lane l -> row 16 j + l / 4, chunk l % 4
+    uint32_t roff[8], rcol[8], voff[2], vcol[2];
+    int rrow[8], vrow[2];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = 2 * jj + hw, r = 4 * j + (l >> 4);
+      rrow[jj] = r;
+      rcol[jj] = (uint32_t)(16 * (((l & 15) ^ r) & 15));
+      roff[jj] = (uint32_t)(r * rowb) + rcol[jj];
+    }
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = 2 * jj + hw, r = 16 * j + (l >> 2);
+      vrow[jj] = r;
+      vcol[jj] = (uint32_t)(16 * (l & 3));
+      voff[jj] = (uint32_t)(r * rowb) + vcol[jj];
+    }
+    const uint32_t soff = (uint32_t)(l * H * 4);
+    // the loads of chunk n into buffer lb (rows past T read the chunk's first
+    // row; beta past T is zeroed after arrival); skip_w: a chunk whose write
+    // keys are d_min k (its residual is neither written nor read)
+    auto issue = [&](int64_t n, unsigned char *lb, bool skip_w) {
+      const int64_t t0 = n * C;
+      const int Lc = chunk_len(n);
+      const char *q0 = qb + t0 * rowb, *k0 = kb + t0 * rowb, *e0 = eb + t0 * rowb, *v0p = vb + t0 * rowb;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int j = 2 * jj + hw;
+        const uint32_t off = rrow[jj] < Lc ? roff[jj] : rcol[jj];
+        dma16(q0 + off, lb + L::Q + 1024 * j);
+        dma16(k0 + off, lb + L::K + 1024 * j);
+        if (!skip_w) dma16(e0 + off, lb + L::W + 1024 * j);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * jj + hw;
+        dma16(v0p + (vrow[jj] < Lc ? voff[jj] : vcol[jj]), lb + L::V + 1024 * j);
+      }
+      const uint32_t so = l < Lc ? soff : 0u;
+      if (hw == 0) dma4(bb + t0 * H * 4 + so, lb + L::BETA);
+      else if (GATED) dma4(ab + t0 * H * 4 + so, lb + L::G);
+    };
+    // after the loads of chunk n have landed: beta past T to zero, alpha to the
+    // cumulative log decay (log 1 = 0 past T, so g stays at g_{Lc-1})
+    auto finish = [&](int64_t n, unsigned char *lb) {
+      const int Lc = chunk_len(n);
+      if (hw == 0) {
+        if (l >= Lc) reinterpret_cast<float *>(lb + L::BETA)[l] = 0.0f;
+      } else if (GATED) {
+        float *gp = reinterpret_cast<float *>(lb + L::G);
+        float x = l < Lc ? logf(gp[l]) : 0.0f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
           const float y = __shfl_up(x, off, 64);
           if (l >= off) x += y;
         }
-        sG[l] = x;
+        gp[l] = x;
       }
-    }
-    __syncthreads();
-    // The next chunk's rows are loaded in three parts, one per phase between
-    // barriers, so that their issue overlaps with compute instead of stalling
-    // one phase.  Issued on every chunk (the last one reloads its own rows,
-    // valid and unused) so that the number of loads in flight does not depend
-    // on the path, which lets the waits for Tm count past these loads instead
-    // of draining them.
-    const int64_t nn1 = n + 1 < Nb ? n + 1 : n;
-    fetch(nn1, FQ);
+    };
 
-    // ---- stage G.  Row waves: K S^T and Q S^T for their rows, both value
-    //      tiles, then R (to LDS, transposed) and the Q S^T part of O (kept).
-    //      Other waves: the ten score tiles on and below the diagonal, split
-    //      3 / 3 / 2 / 2, each wave loading a query row block once.
-    floatx4 Oacc[2];
-    if (roww) {
-      floatx4 accKS[2], accQS[2];
-      bf16x8 kf[4], qf[4];
+    int pin1 = load_pin(1);  // marks of chunks n + 1 and n + 2
+    int pin2 = load_pin(2);
+    if (Nb > 0) {
+      issue(0, lb0, __builtin_amdgcn_readfirstlane(load_pin(0)) == 2);
+      wait_loads();
+      finish(0, lb0);
+    }
+    lds_barrier();
+
+    auto body = [&](int64_t n, const unsigned char *cur, unsigned char *nxt) {
+      const bf16 *sQ = reinterpret_cast<const bf16 *>(cur + L::Q);
+      const float *sG = reinterpret_cast<const float *>(cur + L::G);
+      const int64_t t0 = n * C;
+      const int Lc = chunk_len(n);
+      const bool more = n + 1 < Nb;
+      if (more) issue(n + 1, nxt, __builtin_amdgcn_readfirstlane(pin1) == 2);
+      pin1 = pin2;
+      pin2 = load_pin(n + 3);
+      // this chunk's scores (formed chunk-parallel with Tm): token-row tiles
+      // mta = hw (slab 0) and mtb = 3 - hw (slabs 0, 1), hi/lo operands
+      const bf16 *md = tseq + n * CHUNKW + TDUMP;
+      const int js[3] = {hw, 4 - 2 * hw, 5 - 2 * hw};
+      bf16x8 Mh[3], Ml[3];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int ko = 32 * kk + 8 * lq;
-        kf[kk] = ld8(&sK[m0 + l16][ko]);
-        qf[kk] = ld8(&sQ[m0 + l16][ko]);
+      for (int u = 0; u < 3; ++u) {
+        Mh[u] = ld8(md + ((2 * js[u]) * 64 + l) * 8);
+        Ml[u] = ld8(md + ((2 * js[u] + 1) * 64 + l) * 8);
       }
+      // e^g Q S_n^T for both token-row tiles and both value tiles (S_n as the
+      // chain waves left it)
+      const int mts[2] = {hw, 3 - hw};
+      floatx4 O[2][2];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        bf16x8 sh[4], sl[4];
+      for (int u = 0; u < 2; ++u) {
+        const int mt = mts[u];
+        bf16x8 aq[4];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          sh[kk] = ld8(sSh + sx128(16 * ct + l16, 32 * kk + 8 * lq));
-          sl[kk] = ld8(sSl + sx128(16 * ct + l16, 32 * kk + 8 * lq));
-        }
-        floatx4 ks = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 4; ++s) aq[s] = lda_tile_order(sQ, 16 * mt + l16, s, g);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          ks = mfma32(kf[kk], sh[kk], ks);
-          qs = mfma32(qf[kk], sh[kk], qs);
-          ks = mfma32(kf[kk], sl[kk], ks);
-          qs = mfma32(qf[kk], sl[kk], qs);
-        }
-        accKS[ct] = ks;
-        accQS[ct] = qs;
-      }
-      float gm[4], bm[4];
+        for (int c = 0; c < 2; ++c) {
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        gm[i] = GATED ? sG[m0 + 4 * lq + i] : 0.0f;
-        bm[i] = sBeta[m0 + 4 * lq + i];
-      }
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        // values V[m0 + 4 lq + i][16 ct + l16], i < 4, in one transposed read
-        const bf16x4 vv = ld4_tr(&sV[m0 + 4 * lq + (l16 >> 2)][16 * ct + 4 * (l16 & 3)]);
-        floatx4 r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float em = GATED ? __expf(gm[i]) : 1.0f;
-          r[i] = bm[i] * (to_f32(vv[i]) - em * accKS[ct][i]);
-          Oacc[ct][i] = em * accQS[ct][i];
-        }
-        bf16x4 rh, rl;
-        split4(r, rh, rl);
-        *reinterpret_cast<bf16x4 *>(sRh + sx(16 * ct + l16, m0 + 4 * lq)) = rh;
-        *reinterpret_cast<bf16x4 *>(sRl + sx(16 * ct + l16, m0 + 4 * lq)) = rl;
-      }
-    } else {
-      // score tiles (mr, tj), tj = tj0 .. tj0 + CNT - 1 <= mr, one query
-      // block; every operand is loaded before the products, whose chains
-      // interleave
-      auto mrow = [&](int mr, int tj0, auto cnt) {
-        constexpr int CNT = decltype(cnt)::value;
-        bf16x8 qf[4], me[CNT][4], mk[CNT][4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int ko = 32 * kk + 8 * lq;
-          qf[kk] = ld8(&sQ[16 * mr + l16][ko]);
-#pragma unroll
-          for (int t = 0; t < CNT; ++t) {
-            me[t][kk] = ld8(&sE[16 * (tj0 + t) + l16][ko]);
-            if constexpr (KRES) mk[t][kk] = ld8(&sK[16 * (tj0 + t) + l16][ko]);
+          for (int s = 0; s < 4; ++s) {
+            acc = mfma32(aq[s], sdump[c][2 * s][l], acc);
+            acc = mfma32(aq[s], sdump[c][2 * s + 1][l], acc);
           }
-        }
-        floatx4 acc[CNT];
+          if (GATED) {
 #pragma unroll
-        for (int t = 0; t < CNT; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-          for (int t = 0; t < CNT; ++t) {
-            acc[t] = mfma32(qf[kk], me[t][kk], acc[t]);
-            if constexpr (KRES) acc[t] = mfma32(qf[kk], mk[t][kk], acc[t]);
+            for (int i = 0; i < 4; ++i) acc[i] *= __expf(sG[16 * mt + 4 * g + i]);
           }
-        float gr[4];
+          O[u][c] = acc;
+        }
+      }
+      lds_barrier();  // ---- B2: Delta is in LDS; the chain waves may rewrite S
+      // O = q_scale (e^g Q S_n^T + scores Delta)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) gr[i] = GATED ? sG[16 * mr + 4 * lq + i] : 0.0f;
+      for (int c = 0; c < 2; ++c) {
+        // tile mta: slab 0; tile mtb: slabs 0 and 1
+        const bf16x8 d0h = ddump[c][0][l], d0l = ddump[c][1][l];
+        const bf16x8 d1h = ddump[c][2][l], d1l = ddump[c][3][l];
+        O[0][c] = mfma32(Mh[0], d0h, O[0][c]);
+        O[1][c] = mfma32(Mh[1], d0h, O[1][c]);
+        O[0][c] = mfma32(Mh[0], d0l, O[0][c]);
+        O[1][c] = mfma32(Mh[1], d0l, O[1][c]);
+        O[0][c] = mfma32(Ml[0], d0h, O[0][c]);
+        O[1][c] = mfma32(Ml[1], d0h, O[1][c]);
+        O[1][c] = mfma32(Mh[2], d1h, O[1][c]);
+        O[1][c] = mfma32(Mh[2], d1l, O[1][c]);
+        O[1][c] = mfma32(Ml[2], d1h, O[1][c]);
+      }
 #pragma unroll
-        for (int t = 0; t < CNT; ++t) {
-          const int nn = 16 * (tj0 + t) + l16;
-          const float gn = GATED ? sG[nn] : 0.0f;
-          floatx4 mv;
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int m = 16 * mr + 4 * lq + i;
-            const float ratio = GATED ? __expf(gr[i] - gn) : 1.0f;
-            mv[i] = nn <= m ? ratio * acc[t][i] : 0.0f;
+            const int m = 16 * mts[u] + 4 * g + i;
+            if (m < Lc)
+              store_out<bf16>(a.o, base + v0 + (t0 + m) * tstride + 16 * c + l16, a.q_scale * O[u][c][i],
+                              a.o_f32);
           }
-          bf16x4 mh, ml;
-          split4(mv, mh, ml);
-          *reinterpret_cast<bf16x4 *>(sMh + sx(nn, 16 * mr + 4 * lq)) = mh;
-          *reinterpret_cast<bf16x4 *>(sMl + sx(nn, 16 * mr + 4 * lq)) = ml;
-        }
-      };
-      if (w == 0) {
-        mrow(1, 0, IConst<2>{});
-        mrow(0, 0, IConst<1>{});
-      } else if (w == 1) {
-        // two calls keep the operands of at most two tiles live
-        mrow(3, 1, IConst<2>{});
-        mrow(3, 3, IConst<1>{});
-      } else if (w == 2) {
-        mrow(2, 0, IConst<2>{});
-      } else {
-        mrow(2, 2, IConst<1>{});
-        mrow(3, 0, IConst<1>{});
+      if (more) {
+        wait_loads();
+        finish(n + 1, nxt);
       }
+      lds_barrier();  // ---- B1 of the next chunk
+    };
+    for (int64_t n = 0; n < Nb; n += 2) {
+      body(n, lb0, lb1);
+      if (n + 1 < Nb) body(n + 1, lb1, lb0);
     }
-    __syncthreads();
-    fetch(nn1, FK | FE);
-
-    // ---- stage D: Delta tile (rw, cw) = Tm R, split and stored transposed.
-    const float gL = GATED ? sG[Lc - 1] : 0.0f;
-    {
-      // Tm is lower triangular: rows below 32 need only the first k-step
-      const int nks = rw < 2 ? 1 : 2;
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if (kk < nks) {
-          const bf16x8 rh = ld8(sRh + sx(16 * cw + l16, 32 * kk + 8 * lq));
-          const bf16x8 rl = ld8(sRl + sx(16 * cw + l16, 32 * kk + 8 * lq));
-          acc = mfma32(pt[kk], rh, acc);
-          acc = mfma32(pt[kk], rl, acc);
-        }
-      }
-      bf16x4 dh, dl;
-      split4(acc, dh, dl);
-      *reinterpret_cast<bf16x4 *>(sDh + sx(16 * cw + l16, m0 + 4 * lq)) = dh;
-      *reinterpret_cast<bf16x4 *>(sDl + sx(16 * cw + l16, m0 + 4 * lq)) = dl;
-      if constexpr (GATED) {
-        floatx4 s;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[i] = acc[i] * __expf(gL - sG[m0 + 4 * lq + i]);
-        split4(s, dh, dl);
-        *reinterpret_cast<bf16x4 *>(sDsh + sx(16 * cw + l16, m0 + 4 * lq)) = dh;
-        *reinterpret_cast<bf16x4 *>(sDsl + sx(16 * cw + l16, m0 + 4 * lq)) = dl;
-      }
-    }
-    __syncthreads();
-    fetch_t(nn1);
-
-    if (roww) {
-      // ---- stage O: output rows of this wave, both value tiles.  The scores
-      //      of rows below 32 vanish past the first k-step.
-      const int nks = rw < 2 ? 1 : 2;
-      bf16x8 mh[2], ml[2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if (kk < nks) {
-          mh[kk] = ld8_tr_sx(sMh, 32 * kk, m0, l);
-          ml[kk] = ld8_tr_sx(sMl, 32 * kk, m0, l);
-        }
-      }
-      bf16x8 dh[2][2], dl[2][2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-          if (kk < nks) {
-            const int ko = 32 * kk + 8 * lq;
-            dh[ct][kk] = ld8(sDh + sx(16 * ct + l16, ko));
-            dl[ct][kk] = ld8(sDl + sx(16 * ct + l16, ko));
-          }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-          if (kk < nks) {
-            Oacc[ct] = mfma32(mh[kk], dh[ct][kk], Oacc[ct]);
-            Oacc[ct] = mfma32(mh[kk], dl[ct][kk], Oacc[ct]);
-            Oacc[ct] = mfma32(ml[kk], dh[ct][kk], Oacc[ct]);
-          }
-      char *oc = ob + t0 * rowb + ooff;
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (m0 + 4 * lq + i < Lc)
-            *reinterpret_cast<bf16 *>(oc + i * rowb + 32 * ct) = to_bf16(a.q_scale * Oacc[ct][i]);
-    } else {
-      // ---- stage S: the wave's four tiles of S^T += K~^T Delta, then their
-      //      bf16 pairs.  The write keys enter as A operands with k over
-      //      tokens, read transposed from the row-major key buffers.
-      const float decay = GATED ? __expf(gL) : 1.0f;
-      bf16x8 dsh[2][2], dsl[2][2], be[2][2], bk[2][2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int ko = 32 * kk + 8 * lq;
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          dsh[rt][kk] = ld8(sDsh + sx(16 * rt + l16, ko));
-          dsl[rt][kk] = ld8(sDsl + sx(16 * rt + l16, ko));
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int c0 = 16 * (2 * sp + j);
-          be[j][kk] = ld8_tr(sE, 32 * kk, c0, l);
-          if constexpr (KRES) bk[j][kk] = ld8_tr(sK, 32 * kk, c0, l);
-        }
-      }
-      if constexpr (GATED) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) Sacc[rt][j] = Sacc[rt][j] * decay;
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            Sacc[rt][j] = mfma32(be[j][kk], dsh[rt][kk], Sacc[rt][j]);
-            Sacc[rt][j] = mfma32(be[j][kk], dsl[rt][kk], Sacc[rt][j]);
-            if constexpr (KRES) {
-              Sacc[rt][j] = mfma32(bk[j][kk], dsh[rt][kk], Sacc[rt][j]);
-              Sacc[rt][j] = mfma32(bk[j][kk], dsl[rt][kk], Sacc[rt][j]);
-            }
-          }
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          bf16x4 sh4, sl4;
-          split4(Sacc[rt][j], sh4, sl4);
-          const int kt = 2 * sp + j;
-          *reinterpret_cast<bf16x4 *>(sSh + sx128(16 * rt + l16, 16 * kt + 4 * lq)) = sh4;
-          *reinterpret_cast<bf16x4 *>(sSl + sx128(16 * rt + l16, 16 * kt + 4 * lq)) = sl4;
-        }
-    }
-  }
-
-  if (a.S_out && !roww) {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int vr = 16 * rt + l16, c = 16 * (2 * sp + j) + 4 * lq;
-        *reinterpret_cast<floatx4 *>(a.S_out + (seq * VD + v0 + vr) * KD + c) = Sacc[rt][j];
-      }
   }
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (queried each call: a host-side
+// attribute read, no device work).
 int device_cus() {
-  static int cus[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cus[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
 }
 
 template <bool GATED, bool KRES, bool VL>
@@ -917,9 +937,9 @@ void launch_both(const ChunkArgs &a, bf16 *tw, int64_t N, hipStream_t s, const E
     }
   }
   const int64_t groups = (nseq + 7) / 8;
-  hipLaunchKernelGGL((chunk_seq_kernel<GATED, KRES, VL>), dim3((unsigned)(groups * 8 * NT)), dim3(512), 0, s, a,
+  hipLaunchKernelGGL((chunk_sweep_kernel<GATED, KRES, VL>), dim3((unsigned)(groups * 8 * NT)), dim3(256), 0, s, a,
                      (const bf16 *)tw, N);
-  prof_mark(s, "chunk_seq_kernel");
+  prof_mark(s, "chunk_sweep_kernel");
 }
 
 template <bool VL>
@@ -941,7 +961,7 @@ void launch_gated(const ChunkArgs &a, bf16 *tw, int64_t N, hipStream_t s, const 
 
 size_t chunk_wy_work_bytes(int64_t B, int64_t T, int64_t H) {
   const int64_t N = (T + C - 1) / C;
-  return (size_t)(B * H * N) * C * C * 2;
+  return (size_t)(B * H * N) * CHUNKW * 2;
 }
 
 hipError_t launch_chunk_wy(const ChunkArgs &a, void *work, hipStream_t s, const EmitArgs *em) {

@@ -108,7 +108,6 @@ __global__ __launch_bounds__(1024, 8) void decode_kernel(DecodeArgs a) {
   const TIn *qp = static_cast<const TIn *>(a.q);
   const TIn *kp = static_cast<const TIn *>(a.k);
   const TIn *vp = static_cast<const TIn *>(a.v);
-  TIn *op = static_cast<TIn *>(a.o);
   const int64_t tok0 = b * T * H + h;  // flat [B,T,H] index of this (b,h)'s token 0
   const float eta = a.eta, eps = a.eps, dmin = a.d_min, dmax = a.d_max, qs = a.q_scale;
   const bool clamp = a.clamp != 0, aware = a.beta_aware != 0, gated = a.alpha != nullptr;
@@ -212,7 +211,7 @@ __global__ __launch_bounds__(1024, 8) void decode_kernel(DecodeArgs a) {
     __syncthreads();
     for (int e = tid; e < nb * (int)V; e += nt) {
       const int t = e / (int)V, i = e - t * (int)V;
-      op[(tok0 + (t0 + t) * H) * V + i] = from_f32<TIn>(sO[t][i]);
+      store_out<TIn>(a.o, (tok0 + (t0 + t) * H) * V + i, sO[t][i], a.o_f32);
     }
     // the next block's staging touches sK, sQ, sV, sB, sR, sA only, whose last
     // readers finished before the barrier above; sKt and sO are rewritten

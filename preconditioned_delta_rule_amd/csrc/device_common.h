@@ -23,6 +23,14 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
+// One element of the readout o: float32 when the caller asked for float32
+// outputs (o_f32), else rounded to the input type T.
+template <typename T>
+__device__ __forceinline__ void store_out(void *o, int64_t i, float x, int o_f32) {
+  if (o_f32) static_cast<float *>(o)[i] = x;
+  else static_cast<T *>(o)[i] = from_f32<T>(x);
+}
+
 // Sum over the 64 lanes of a wave; every lane receives the total.
 // Rows of 16 lanes are reduced with DPP butterflies (xor 1, xor 2, half-row
 // mirror, row mirror); rows are then combined with row broadcasts into lane

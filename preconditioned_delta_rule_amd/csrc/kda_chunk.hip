@@ -459,7 +459,6 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(KdaArgs a, int64_t N, int 
   const int64_t b = bh / H, h = bh - b * H;
   const int64_t v0 = vt * KVT;
   const TIn *vp = static_cast<const TIn *>(a.v);
-  TIn *op = static_cast<TIn *>(a.o);
 
   // state tile: wave w holds key rows 32 w .. 32 w + 31 (two 16-row blocks)
   // for both 16-column blocks, in the MFMA result layout
@@ -597,7 +596,7 @@ __global__ __launch_bounds__(256) void kda_seq_kernel(KdaArgs a, int64_t N, int 
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * w + 4 * g + i;
         const int64_t col = v0 + 16 * cb + l16;
-        if (row < L && col < V) op[((b * T + t0 + row) * H + h) * V + col] = from_f32<TIn>(accP[cb][i]);
+        if (row < L && col < V) store_out<TIn>(a.o, ((b * T + t0 + row) * H + h) * V + col, accP[cb][i], a.o_f32);
       }
     // (d) S = Diag(gamma_C) S + Kc^T D for this wave's key rows
 #pragma unroll
@@ -685,7 +684,6 @@ __global__ __launch_bounds__(256) void kda_seq_hilo_kernel(KdaArgs a, int64_t N,
   const int64_t b = bh / H, h = bh - b * H;
   const int64_t v0 = vt * KVT;
   const bf16 *vp = static_cast<const bf16 *>(a.v);
-  bf16 *op = static_cast<bf16 *>(a.o);
 
   floatx4 Sr[2][NCB];  // key rows 32 w + 16 rb + 4 g + i, value column 16 cb + l16
 #pragma unroll
@@ -832,7 +830,7 @@ __global__ __launch_bounds__(256) void kda_seq_hilo_kernel(KdaArgs a, int64_t N,
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * w + 4 * g + i;
         const int64_t col = v0 + 16 * cb + l16;
-        if (row < L && col < V) op[((b * T + t0 + row) * H + h) * V + col] = to_bf16(accP[cb][i]);
+        if (row < L && col < V) store_out<bf16>(a.o, ((b * T + t0 + row) * H + h) * V + col, accP[cb][i], a.o_f32);
       }
     // (d) S = Diag(gamma_C) S + Kc^T D for this wave's key rows
 #pragma unroll

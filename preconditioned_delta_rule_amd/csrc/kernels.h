@@ -45,12 +45,17 @@ struct ChunkArgs {
   const float *beta;           // [B,T,H]
   const float *alpha;          // [B,T,H] or null
   const float *S0;             // [B,H,V,K] or null
-  void *o;                     // [B,T,H,V]
+  void *o;                     // [B,T,H,V], float32 when o_f32
   float *S_out;                // [B,H,V,K] or null
   int64_t B, T, H, K, V;
   int C;
   float q_scale;
+  int o_f32 = 0;               // o is float32 whatever the input type
   const int64_t *cu = nullptr;  // variable-length sequences (see seq_base)
+  // residual form only: the chunked phase 1's marks ([B,H,N] per 64-token
+  // chunk, 2 = every write key of the chunk is d_min k), or null
+  const int *pin = nullptr;
+  float d_min = 0.0f;
 };
 
 // Each returns hipSuccess or the launch error.
@@ -103,8 +108,9 @@ struct DecodeArgs {
   const float *beta;          // [B,T,H]
   const float *r, *alpha;     // [B,T,H] or null
   const float *d1, *S0;       // [B,H,K], [B,H,V,K] or null (ones, zeros)
-  void *o;                    // [B,T,H,V]
+  void *o;                    // [B,T,H,V], float32 when o_f32
   float *d_out, *S_out;       // or null; may alias d1, S0
+  int o_f32 = 0;
   int64_t B, T, H, K, V;
   float eta, d_min, d_max, eps, q_scale;
   int clamp, beta_aware;
@@ -134,6 +140,7 @@ struct BwdArgs {
   int64_t B, T, H, K, V;
   float eta, d_min, d_max, eps, q_scale;
   int clamp, beta_aware;
+  int o_f32 = 0;                // dq, dk, dv are float32 whatever the input type
 };
 size_t bwd_work_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V);
 void bwd_work_layout(BwdArgs &a, void *base);
@@ -148,10 +155,11 @@ struct KdaArgs {
   const float *beta;           // [B,T,H]
   const float *alpha;          // [B,T,H,K] channel-wise decay, or null
   const float *S0;             // [B,H,K,V] or null
-  void *o;                     // [B,T,H,V]
+  void *o;                     // [B,T,H,V], float32 when o_f32
   float *S_out;                // [B,H,K,V] or null
   int64_t B, T, H, K, V;
   float q_scale;
+  int o_f32 = 0;
   // workspace regions (kda_work_layout), per (b,h) and chunk n < N = ceil(T/64):
   float *kh, *qh;  // [B,H,N,64,128] Gamma . k and Gamma . q_scale q, rows permuted for MFMA
   float *kc;       // [B,H,N,128,64] ((gamma_C / Gamma) . k~)^T, rows permuted

@@ -22,8 +22,8 @@ constexpr int PROF_MAX = 1024;
 struct Profile {
   bool open = false;
   int n = 0;
-  hipEvent_t ev[PROF_MAX + 1] = {};
-  const char *name[PROF_MAX] = {};  // events live until the process ends
+  hipEvent_t ev[PROF_MAX + 1] = {};  // created as needed, destroyed by osdn_profile_end
+  const char *name[PROF_MAX] = {};
 };
 thread_local Profile g_prof;
 
@@ -97,6 +97,7 @@ osdn_status validate(const osdn_desc *d, int phase) {
       return fail(OSDN_EUNSUPPORTED, "phase 2 supports K, V <= 128 (got K=%lld V=%lld)", (long long)d->K,
                   (long long)d->V);
     if (!std::isfinite(d->q_scale)) return fail(OSDN_EINVAL, "q_scale must be finite");
+    if (d->o_f32 != 0 && d->o_f32 != 1) return fail(OSDN_EINVAL, "o_f32 must be 0 or 1 (got %d)", d->o_f32);
   }
   return OSDN_OK;
 }
@@ -150,6 +151,7 @@ osdn::ChunkArgs chunk_args(const osdn_desc *d, const void *q, const void *k, con
   a.V = d->V;
   a.C = d->chunk;
   a.q_scale = d->q_scale;
+  a.o_f32 = d->o_f32;
   return a;
 }
 
@@ -206,15 +208,21 @@ osdn_status osdn_profile_end(const char **names, float *ms, int max_entries, int
   if (!p.open) return fail(OSDN_EINVAL, "no profile is open on this thread");
   p.open = false;
   if (count) *count = p.n;
-  if (p.n == 0) return ok();
-  OSDN_TRY(hip_status(hipEventSynchronize(p.ev[p.n]), "profile event"));
-  for (int i = 0; i < p.n && i < max_entries; ++i) {
+  osdn_status st = OSDN_OK;
+  if (p.n > 0) st = hip_status(hipEventSynchronize(p.ev[p.n]), "profile event");
+  for (int i = 0; st == OSDN_OK && i < p.n && i < max_entries; ++i) {
     float t = 0.0f;
-    OSDN_TRY(hip_status(hipEventElapsedTime(&t, p.ev[i], p.ev[i + 1]), "profile event"));
+    st = hip_status(hipEventElapsedTime(&t, p.ev[i], p.ev[i + 1]), "profile event");
     if (names) names[i] = p.name[i];
     if (ms) ms[i] = t;
   }
-  return ok();
+  // the events are not kept between profiles
+  for (int i = 0; i <= PROF_MAX; ++i)
+    if (p.ev[i]) {
+      hipEventDestroy(p.ev[i]);
+      p.ev[i] = nullptr;
+    }
+  return st == OSDN_OK ? ok() : st;
 }
 
 int osdn_version(void) { return (1 << 16) | 0; }
@@ -362,10 +370,8 @@ static osdn_status fwd_impl(const osdn_desc *d, const int64_t *cu, const void *q
   OSDN_TRY(check_ptr(S_out, "S_out", false));
   OSDN_TRY(check_ptr(d_out, "d_out", false));
   OSDN_TRY(check_ptr(k_tilde_out, "k_tilde_out", false));
+  // (phase 2 takes K <= 128, so vector retention always has the chunked phase 1 here)
   const bool rvec = d->r_per_key && r;
-  const bool rvec_tok = rvec && d->K > 128;  // token-by-token phase 1
-  if (rvec_tok && cu)
-    return fail(OSDN_EUNSUPPORTED, "vector retention with K > 128 is not supported for packed sequences");
   hipStream_t s = static_cast<hipStream_t>(stream);
   osdn::ScanArgs sa = scan_args(d, k, beta, r, d1, k_tilde_out, d_out);
   osdn::ChunkArgs ca = chunk_args(d, q, k, k_tilde_out, v, beta, alpha, S0, o, S_out);
@@ -397,12 +403,15 @@ static osdn_status fwd_impl(const osdn_desc *d, const int64_t *cu, const void *q
   void *cw = chunk_work_bytes(d) ? ws + fwd_keys_bytes(d) + scan_bytes : nullptr;
   // bf16 on the matrix cores without k_tilde_out: the residual is formed by
   // the first phase-2 kernel, which replays d itself (one pass over k fewer)
-  const bool fold = res && cw && !k_tilde_out && !rvec_tok;
-  if (rvec_tok)  // vector retention above K = 128: the token-by-token sweep writes the keys
-    OSDN_TRY(run_scan(d, sa, s));
-  else
-    OSDN_TRY(hip_status(osdn::launch_precond_scan_chunked(sa, sw, d->dtype == OSDN_BF16, s, !fold),
-                        "phase-1 launch"));
+  const bool fold = res && cw && !k_tilde_out;
+  if (res) {
+    // a chunk the chunked phase 1 marks as pinned keeps d = d_min at every
+    // token: phase 2 takes its write keys as d_min k (exact operands)
+    ca.pin = sw.pin;
+    ca.d_min = d->d_min;
+  }
+  OSDN_TRY(hip_status(osdn::launch_precond_scan_chunked(sa, sw, d->dtype == OSDN_BF16, s, !fold),
+                      "phase-1 launch"));
   if (fold) {
     osdn::EmitArgs em;
     em.cstep = sw.cstep;
@@ -487,6 +496,7 @@ osdn_status osdn_decode(const osdn_desc *d, const void *q, const void *k, const 
   a.d_max = d->d_max;
   a.eps = d->eps;
   a.q_scale = d->q_scale;
+  a.o_f32 = d->o_f32;
   a.clamp = d->clamp ? 1 : 0;
   a.beta_aware = d->beta_aware ? 1 : 0;
   OSDN_TRY(hip_status(osdn::launch_decode(a, d->dtype == OSDN_BF16, static_cast<hipStream_t>(stream)),
@@ -574,6 +584,7 @@ osdn_status osdn_bwd(const osdn_desc *d, const void *q, const void *k, const voi
   a.q_scale = d->q_scale;
   a.clamp = d->clamp ? 1 : 0;
   a.beta_aware = d->beta_aware ? 1 : 0;
+  a.o_f32 = d->o_f32;
   osdn::bwd_work_layout(a, workspace);
   OSDN_TRY(hip_status(osdn::launch_bwd(a, d->dtype == OSDN_BF16, static_cast<hipStream_t>(stream)),
                       "backward launch"));
@@ -631,6 +642,7 @@ osdn_status osdn_kda_fwd(const osdn_desc *d, const void *q, const void *k, const
   ka.K = d->K;
   ka.V = d->V;
   ka.q_scale = d->q_scale;
+  ka.o_f32 = d->o_f32;
   if (!need_seq) {
     // nothing to sweep: d_out = d1 and S_out = S0 (the kernels do the copy)
     OSDN_TRY(run_scan(d, sa, s));
@@ -656,10 +668,7 @@ osdn_status osdn_kda_fwd(const osdn_desc *d, const void *q, const void *k, const
   // bf16, K = 128, residual form, one retention per token: the intra pass
   // forms the residual from the chunked sweep's marks and step scalars
   const bool fold = osdn::kda_can_fold(ka, bf) && !(d->r_per_key && r) && !k_tilde_out;
-  if (d->r_per_key && r && d->K > 128)
-    OSDN_TRY(run_scan(d, sa, s));
-  else
-    OSDN_TRY(hip_status(osdn::launch_precond_scan_chunked(sa, sw, bf, s, !fold), "phase-1 launch"));
+  OSDN_TRY(hip_status(osdn::launch_precond_scan_chunked(sa, sw, bf, s, !fold), "phase-1 launch"));
   osdn::kda_work_layout(ka, ws + fwd_keys_bytes(d) + scan_bytes);
   if (fold) {
     osdn::EmitArgs em;

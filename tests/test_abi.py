@@ -40,7 +40,7 @@ def test_desc_layout_and_defaults(lib):
     assert d.chunk == 64 and d.dtype == osdn.BF16 and d.clamp == 1 and d.beta_aware == 1
     assert d.eta == pytest.approx(0.003) and d.eps == pytest.approx(1e-6)
     assert (d.d_min, d.d_max, d.q_scale) == (0.5, 2.0, 1.0)
-    assert ctypes.sizeof(osdn.Desc) == 80 and d.r_per_key == 0
+    assert ctypes.sizeof(osdn.Desc) == 88 and d.r_per_key == 0 and d.o_f32 == 0
     assert lib.osdn_validate(ctypes.byref(d)) == osdn.OK
     assert lib.osdn_version() >> 16 == 1
 
@@ -58,7 +58,7 @@ BAD = [
     (dict(eta=-1.0), osdn.EINVAL), (dict(eps=0.0), osdn.EINVAL),
     (dict(d_min=2.0, d_max=1.0), osdn.EINVAL), (dict(d_min=0.0), osdn.EINVAL),
     (dict(q_scale=float("inf")), osdn.EINVAL), (dict(eta=float("nan")), osdn.EINVAL),
-    (dict(r_per_key=2), osdn.EINVAL),
+    (dict(r_per_key=2), osdn.EINVAL), (dict(o_f32=2), osdn.EINVAL),
 ]
 
 
@@ -147,8 +147,10 @@ def test_workspace_bytes(lib):
     scan = 2 * tok + 4 * 16 * 64 * 128 * 4 + 4 * 16 * 64 * 4 + 4 * 16 * 64 * 8 + 256 * 3
     assert lib.osdn_precond_scan_workspace_bytes(ctypes.byref(d)) == scan
     assert lib.osdn_precond_scan_counters_offset(ctypes.byref(d)) == scan - 256 * 3
-    # phase 2 on the matrix cores keeps one bf16 64 x 64 block per chunk
-    wy = 4 * 16 * 64 * 64 * 64 * 2
+    # phase 2 on the matrix cores keeps, per chunk, the six 16 x 64 blocks of
+    # (I + A)^-1 on and below the diagonal (bf16) and the intra-chunk scores
+    # in the same blocks as hi/lo bf16 pairs
+    wy = 4 * 16 * 64 * 6 * 16 * 32 * 2 * 3
     assert lib.osdn_chunk_fwd_workspace_bytes(ctypes.byref(d)) == wy
     assert lib.osdn_fwd_workspace_bytes(ctypes.byref(d)) == 4 * 4096 * 16 * 128 * 2 + scan + wy
     d.dtype = osdn.F32

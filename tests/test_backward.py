@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import preconditioned_delta_rule_amd as osdn
-from tests.helpers import BF16_OS, F32_OS, o_err, rel_err, to_dev, to_np
+from tests.helpers import BF16_OS, F32_OS, check_bf16_readout, rel_err, to_dev, to_np
 from workloads import make_inputs, random_cotangent, random_state, sample_sequences
 
 pytestmark = pytest.mark.gpu
@@ -55,7 +55,7 @@ CASES = {
 FP32_OUT = ("dbeta", "dr", "dalpha", "dd1", "dS0")
 
 
-def run_bwd(inp, dout, dS, dd):
+def run_bwd(inp, dout, dS, dd, o_f32=False):
     p = inp["params"]
     dt = p["dtype"]
     g = osdn.bwd(to_dev(inp["q"], dt), to_dev(inp["k"], dt), to_dev(inp["v"], dt),
@@ -63,7 +63,7 @@ def run_bwd(inp, dout, dS, dd):
                  to_dev(inp["d1"], "f32"), to_dev(inp["S0"], "f32"), dout=to_dev(dout, dt),
                  dS=to_dev(dS, "f32"), dd=to_dev(dd, "f32"), eta=p["eta"], d_min=p["d_min"],
                  d_max=p["d_max"], clamp=p["clamp"], eps=p["eps"], q_scale=p["q_scale"],
-                 beta_aware=p["beta_aware"])
+                 beta_aware=p["beta_aware"], o_f32=o_f32)
     torch.cuda.synchronize()
     return {k: (None if v is None else to_np(v)) for k, v in g.items()}
 
@@ -76,14 +76,18 @@ def oracle_bwd(inp, dout, dS, dd):
                            beta_aware=p["beta_aware"], q_scale=p["q_scale"])
 
 
-def check(g, ref, dtype, tag):
+def check(g, ref, dtype, tag, g32=None):
+    """fp32 gradients within 1e-4 relative.  Gradients stored in the input
+    dtype (dq, dk, dv) for bf16: the float32 ones of the same call (g32,
+    o_f32) within 2e-2 tensor-wide, the bf16 ones their nearest-even rounding
+    and within 2e-2 per row."""
     errs = {}
     for key, val in ref.items():
         if val is None:
             assert g[key] is None, (tag, key)
             continue
         if dtype == "bf16" and key not in FP32_OUT:
-            errs[key] = (o_err(g[key], val), BF16_OS)
+            check_bf16_readout(g[key], g32[key], val, "%s %s" % (tag, key))
         else:
             errs[key] = (rel_err(g[key], val), F32_OS)
     print(tag, {k: "%.2e" % e for k, (e, _) in errs.items()})
@@ -99,8 +103,9 @@ def test_backward_parity(case, dtype):
     inp = dict(inp, d1=d1, S0=S0)
     dout, dS, dd = random_cotangent(inp, seed=8)
     g = run_bwd(inp, dout, dS, dd)
+    g32 = run_bwd(inp, dout, dS, dd, o_f32=True) if dtype == "bf16" else None
     ref = oracle_bwd(inp, dout, dS, dd)
-    check(g, ref, dtype, case)
+    check(g, ref, dtype, case, g32)
 
 
 def test_backward_defaults_and_no_upstream_state_gradient():
@@ -134,28 +139,30 @@ def test_backward_empty_sequence(dtype):
 
 
 def test_backward_full_size_sampled():
-    """The bench's backward workload (B=4, T=1024, H=16, K=V=128, bf16, APF)
-    in one call; the oracle recomputes the gradients of sampled sequences."""
-    inp = make_inputs("bwd_1p3b_t1024")
+    """The forward bench's workload (B=4, T=4096, H=16, K=V=128, bf16, APF) in
+    one osdn_bwd call; the oracle recomputes the gradients of eight whole
+    (b,h) sequences (two heads of every batch element)."""
+    inp = make_inputs("1p3b_apf")
     dout, dS, dd = random_cotangent(inp, seed=10)
     g = run_bwd(inp, dout, dS, dd)
-    pairs = [(0, 0), (3, 15)]
+    g32 = run_bwd(inp, dout, dS, dd, o_f32=True)
+    pairs = [(b, h) for b in range(4) for h in (b, 15 - b)]
     sub = sample_sequences(dict(inp), pairs)
     sub_dout = np.stack([dout[b, :, h] for b, h in pairs])[:, :, None, :]
     sub_dS = np.stack([dS[b, h] for b, h in pairs])[:, None]
     sub_dd = np.stack([dd[b, h] for b, h in pairs])[:, None]
     ref = oracle_bwd(sub, sub_dout, sub_dS, sub_dd)
-    for i, (b, h) in enumerate(pairs):
-        ref_i = {key: (None if val is None else val[i][None]) for key, val in ref.items()}
+    def pick(gr):
         gi = {}
-        for key, val in g.items():
+        for key, val in gr.items():
             if val is None:
                 gi[key] = None
             elif key in ("dq", "dk", "dv", "dbeta", "dr"):
-                gi[key] = val[b, :, h][None, :, None]
+                gi[key] = np.stack([val[b, :, h] for b, h in pairs])[:, :, None]
             else:
-                gi[key] = val[b, h][None, None]
-        check(gi, ref_i, "bf16", "full(%d,%d)" % (b, h))
+                gi[key] = np.stack([val[b, h] for b, h in pairs])[:, None]
+        return gi
+    check(pick(g), ref, "bf16", "1p3b_apf x8", pick(g32))
 
 
 def test_backward_rejects_aliasing():

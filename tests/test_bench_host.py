@@ -20,9 +20,24 @@ def test_more_than_one_gpu_is_refused():
 
 def test_forward_sweep_bytes():
     # q, k, E (bf16 residual) and v in (4 x 256 B), beta (4 B), o out (256 B)
-    assert bench.kernel_work("chunk_seq_kernel", 128, 128, 64, True, False)[0] == 1284
+    assert bench.kernel_work("chunk_sweep_kernel", 128, 128, 64, True, False)[0] == 1284
     # alpha adds 4 B per token-head
-    assert bench.kernel_work("chunk_seq_kernel", 128, 128, 64, True, True)[0] == 1288
+    assert bench.kernel_work("chunk_sweep_kernel", 128, 128, 64, True, True)[0] == 1288
+    # inside osdn_fwd a chunk phase 1 took as pinned reads no write keys
+    assert bench.kernel_work("chunk_sweep_kernel", 128, 128, 64, True, False, swept=0.0)[0] == 1028
+    assert bench.kernel_work("chunk_sweep_kernel", 128, 128, 64, True, False, fused=False, swept=0.0)[0] == 1284
+
+
+def test_forward_tinv_bytes():
+    # osdn_fwd: k in, E out (2 x 256 B), beta; a swept chunk adds its step
+    # scalar, retention and chunk-start d (512 B per 64 tokens)
+    assert bench.kernel_work("chunk_tinv_kernel", 128, 128, 64, True, False, swept=0.0)[0] == 516
+    assert bench.kernel_work("chunk_tinv_kernel", 128, 128, 64, True, False, swept=1.0)[0] == 516 + 4 + 4 + 8
+    # vector retention: a [K] row per token, read only for swept chunks
+    assert bench.kernel_work("chunk_tinv_kernel", 128, 128, 64, True, False, 2, True, swept=0.5)[0] == \
+        516 + 0.5 * (4 + 512 + 8)
+    # osdn_chunk_fwd: k and k~ in, beta
+    assert bench.kernel_work("chunk_tinv_kernel", 128, 128, 64, True, False, fused=False)[0] == 516
 
 
 def test_phase1_bytes_scalar_and_vector_retention():

@@ -45,6 +45,8 @@ WORKLOADS = {
     "340m": dict(B=8, T=2048, H=8, K=128, V=128, dtype="bf16", chunk=64, seed=1),
     "1p3b_apf": dict(B=4, T=4096, H=16, K=128, V=128, dtype="bf16", chunk=64,
                      seed=2, apf=True),
+    # the same layer without the APF retention
+    "1p3b": dict(B=4, T=4096, H=16, K=128, V=128, dtype="bf16", chunk=64, seed=2),
     "recall": dict(B=8, T=2048, H=8, K=128, V=128, dtype="bf16", chunk=64,
                    seed=3, keys="recall", beta_mu=1.0),
     "long_apf": dict(B=1, T=20480, H=16, K=128, V=128, dtype="bf16", chunk=64,
