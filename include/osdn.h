@@ -238,6 +238,28 @@ osdn_status osdn_fwd_varlen(const osdn_desc *desc, const int64_t *cu_seqlens,
                             size_t workspace_bytes, void *stream);
 
 /*
+ * osdn_fwd without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Arguments and results are those of osdn_fwd; the
+ * workspace is a scratch array of OSDN_FWD_NOALLOC_MAX_WORKSPACE bytes that
+ * the library holds on every GPU it runs on, from first use until the process
+ * ends.  Problems whose osdn_fwd_workspace_bytes(desc) exceeds it return
+ * OSDN_EUNSUPPORTED before anything is launched.  Nothing here allocates:
+ * the first call on a device looks up that device's copy of the array.  All
+ * calls on one GPU share its array: calls that overlap in time on one GPU
+ * (different streams or threads) race and must not be issued; consecutive
+ * calls on one stream are safe (no word of the scratch is read before the
+ * same call writes it).
+ */
+#define OSDN_FWD_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+osdn_status osdn_fwd_noalloc(const osdn_desc *desc, const void *q,
+                             const void *k, const void *v, const float *beta,
+                             const float *r, const float *alpha,
+                             const float *d1, const float *S0, void *o,
+                             float *S_out, float *d_out, void *k_tilde_out,
+                             void *stream);
+
+/*
  * Decode step: the single-token recurrence of Appendix L (one launch per
  * call), for up to OSDN_DECODE_MAX_T new tokens per (b,h) continuing from a
  * carried state.  Per (b,h) and token, in order: the write key d (.) k_t, the

@@ -20,7 +20,7 @@ import os
 import torch
 
 __all__ = ["precond_scan", "precond_scan_workspace_bytes", "scan_counters", "chunk_fwd",
-           "chunk_fwd_workspace_bytes", "fwd", "fwd_varlen", "kda_fwd", "kda_fwd_workspace_bytes", "decode", "DECODE_MAX_T", "bwd",
+           "chunk_fwd_workspace_bytes", "fwd", "fwd_varlen", "fwd_noalloc", "FWD_NOALLOC_MAX_WORKSPACE", "kda_fwd", "kda_fwd_workspace_bytes", "decode", "DECODE_MAX_T", "bwd",
            "bwd_workspace_bytes", "kernel_times", "fwd_workspace_bytes", "fwd_scan_counters", "Desc", "OsdnError",
            "library_path", "load", "F32", "BF16"]
 
@@ -35,7 +35,7 @@ DECODE_MAX_T = 64  # OSDN_DECODE_MAX_T
 SYMBOLS = ("osdn_desc_init", "osdn_validate", "osdn_precond_scan",
            "osdn_precond_scan_workspace_bytes", "osdn_precond_scan_counters_offset",
            "osdn_chunk_fwd", "osdn_chunk_fwd_workspace_bytes", "osdn_fwd_workspace_bytes",
-           "osdn_fwd", "osdn_fwd_varlen", "osdn_decode", "osdn_bwd_workspace_bytes", "osdn_bwd",
+           "osdn_fwd", "osdn_fwd_varlen", "osdn_fwd_noalloc", "osdn_decode", "osdn_bwd_workspace_bytes", "osdn_bwd",
            "osdn_kda_fwd_workspace_bytes", "osdn_kda_fwd", "osdn_profile_begin", "osdn_profile_end",
            "osdn_status_str", "osdn_last_error", "osdn_version")
 
@@ -86,6 +86,7 @@ def load():
     lib.osdn_fwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp, vp,
                              ctypes.c_size_t, vp]
     lib.osdn_decode.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp]
+    lib.osdn_fwd_noalloc.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp, vp]
     lib.osdn_fwd_varlen.argtypes = [dp, vp, vp, vp, vp, fp, fp, fp, fp, fp, vp, fp, fp, vp, vp,
                                     ctypes.c_size_t, vp]
     lib.osdn_bwd_workspace_bytes.argtypes = [dp]
@@ -104,7 +105,7 @@ def load():
     lib.osdn_last_error.argtypes = []
     lib.osdn_last_error.restype = ctypes.c_char_p
     for name in ("osdn_desc_init", "osdn_validate", "osdn_precond_scan", "osdn_chunk_fwd",
-                 "osdn_fwd", "osdn_fwd_varlen", "osdn_decode", "osdn_bwd", "osdn_kda_fwd",
+                 "osdn_fwd", "osdn_fwd_varlen", "osdn_fwd_noalloc", "osdn_decode", "osdn_bwd", "osdn_kda_fwd",
                  "osdn_profile_begin",
                  "osdn_profile_end",
                  "osdn_version"):
@@ -326,6 +327,38 @@ def fwd(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, chunk=64, eta=0.
                            _ptr(alpha), _ptr(d1), _ptr(S0), _ptr(o), _ptr(S_out), _ptr(d_out),
                            _ptr(k_tilde_out), _ptr(workspace),
                            ctypes.c_size_t(_nbytes(workspace)), _stream(dev)))
+    return o, S_out, d_out
+
+
+FWD_NOALLOC_MAX_WORKSPACE = 64 << 20  # OSDN_FWD_NOALLOC_MAX_WORKSPACE
+
+
+def fwd_noalloc(q, k, v, beta, r=None, alpha=None, d1=None, S0=None, *, o, S_out, d_out, chunk=64,
+                eta=0.003, d_min=0.5, d_max=2.0, clamp=True, eps=1e-6, q_scale=1.0, beta_aware=True,
+                k_tilde_out=None, o_f32=False):
+    """fwd with the library's built-in scratch as workspace (osdn_fwd_noalloc):
+    the outputs o, S_out, d_out are the caller's and nothing is allocated.
+    Returns (o, S_out, d_out)."""
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dev, dt, f32 = q.device, q.dtype, torch.float32
+    _need(k, "k", (B, T, H, K), dt, dev)
+    _need(v, "v", (B, T, H, V), dt, dev)
+    _need(beta, "beta", (B, T, H), f32, dev)
+    rvec = _need_r(r, B, T, H, K, dev)
+    _need(alpha, "alpha", (B, T, H), f32, dev)
+    _need(d1, "d1", (B, H, K), f32, dev)
+    _need(S0, "S0", (B, H, V, K), f32, dev)
+    _need(o, "o", (B, T, H, V), f32 if o_f32 else dt, dev)
+    _need(S_out, "S_out", (B, H, V, K), f32, dev)
+    _need(d_out, "d_out", (B, H, K), f32, dev)
+    _need(k_tilde_out, "k_tilde_out", (B, T, H, K), dt, dev)
+    desc = make_desc(B, T, H, K, V, dtype=_dtype_code(q), chunk=chunk, eta=eta, d_min=d_min,
+                     d_max=d_max, clamp=clamp, eps=eps, q_scale=q_scale, beta_aware=beta_aware,
+                     r_per_key=rvec, o_f32=o_f32)
+    _check(load().osdn_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(r),
+                                   _ptr(alpha), _ptr(d1), _ptr(S0), _ptr(o), _ptr(S_out), _ptr(d_out),
+                                   _ptr(k_tilde_out), _stream(dev)))
     return o, S_out, d_out
 
 

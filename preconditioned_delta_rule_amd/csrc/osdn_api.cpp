@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
@@ -16,6 +17,16 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// Workspace of osdn_fwd_noalloc: one copy of this array per GPU.  Host code
+// never uses the name itself as a device address: the device address of each
+// GPU's copy is looked up once per device (hipGetSymbolAddress, with that
+// device current) and kept in g_scratch.
+__device__ __align__(256) unsigned char scratch[OSDN_FWD_NOALLOC_MAX_WORKSPACE];
+constexpr int MAX_DEVICES = 64;
+void *g_scratch[MAX_DEVICES] = {};
+hipError_t g_scratch_err[MAX_DEVICES] = {};
+std::once_flag g_scratch_once[MAX_DEVICES];
 
 // Per-thread launch profile (osdn_profile_begin / osdn_profile_end).
 constexpr int PROF_MAX = 1024;
@@ -445,6 +456,28 @@ osdn_status osdn_fwd_varlen(const osdn_desc *d, const int64_t *cu_seqlens, const
   OSDN_TRY(check_ptr(cu_seqlens, "cu_seqlens", true));
   return fwd_impl(d, cu_seqlens, q, k, v, beta, r, alpha, d1, S0, o, S_out, d_out, k_tilde_out, workspace,
                   workspace_bytes, stream);
+}
+
+osdn_status osdn_fwd_noalloc(const osdn_desc *d, const void *q, const void *k, const void *v, const float *beta,
+                             const float *r, const float *alpha, const float *d1, const float *S0, void *o,
+                             float *S_out, float *d_out, void *k_tilde_out, void *stream) {
+  OSDN_TRY(validate(d, 3));
+  const size_t need = osdn_fwd_workspace_bytes(d);
+  if (need > OSDN_FWD_NOALLOC_MAX_WORKSPACE)
+    return fail(OSDN_EUNSUPPORTED, "osdn_fwd_noalloc: this problem needs %zu bytes of workspace, the built-in "
+                "scratch holds %zu (call osdn_fwd with a workspace)", need, (size_t)OSDN_FWD_NOALLOC_MAX_WORKSPACE);
+  int dev = -1;
+  OSDN_TRY(hip_status(hipGetDevice(&dev), "osdn_fwd_noalloc: current device"));
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(OSDN_EUNSUPPORTED, "osdn_fwd_noalloc: device %d out of range", dev);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void *p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (g_scratch_err[dev] == hipSuccess) g_scratch[dev] = p;
+  });
+  OSDN_TRY(hip_status(g_scratch_err[dev], "osdn_fwd_noalloc: scratch address"));
+  if (!g_scratch[dev]) return fail(OSDN_EHIP, "osdn_fwd_noalloc: no scratch address on device %d", dev);
+  return fwd_impl(d, nullptr, q, k, v, beta, r, alpha, d1, S0, o, S_out, d_out, k_tilde_out, g_scratch[dev],
+                  OSDN_FWD_NOALLOC_MAX_WORKSPACE, stream);
 }
 
 osdn_status osdn_decode(const osdn_desc *d, const void *q, const void *k, const void *v, const float *beta,
