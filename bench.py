@@ -120,6 +120,10 @@ def kernel_work(name, K, V, C, apf, gated, elem=2, rvec=False, fused=True, swept
         return elem * K + 4 + r + 2 * K, 0
     if name == "scan_prep_kernel":
         return elem * K + 4 + r, 0
+    if name == "scan_factor_kernel":
+        # per chunk not pinned by the prep pass: reads k, beta, r and the key
+        # norms, writes the 64 x 64 fp32 inverse factor (4 C bytes per token)
+        return swept * (elem * K + 4 + 4 + r + 4 * C), 0
     if name == "scan_solve_kernel":
         # vector retention rows are read only for the chunks it sweeps
         return 4 + 4 + (0 if rvec else r), 0

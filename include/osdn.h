@@ -133,13 +133,16 @@ osdn_status osdn_validate(const osdn_desc *desc);
  *                              token.  Otherwise >= osdn_precond_scan_
  *                              workspace_bytes(desc) bytes (16-byte aligned)
  *                              and the sweep runs chunked: a parallel pass for
- *                              the key norms, a per-(b,h) pass that finds the
- *                              step scalar of every token (64-token chunks
- *                              whose coordinates all sit on d_min, or all stay
- *                              inside the box, are solved in closed form; any
- *                              other chunk token by token), and a parallel pass
- *                              that replays d and writes the write keys.  Both
- *                              give the same result up to fp32 rounding.
+ *                              the key norms, a parallel pass that factors
+ *                              each chunk's closed form (the inverse of its
+ *                              64 x 64 unit triangular system), a per-(b,h)
+ *                              pass that finds the step scalar of every token
+ *                              (64-token chunks whose coordinates all sit on
+ *                              d_min, or all stay inside the box, are solved
+ *                              in closed form; any other chunk token by
+ *                              token), and a parallel pass that replays d and
+ *                              writes the write keys.  Both give the same
+ *                              result up to fp32 rounding.
  */
 osdn_status osdn_precond_scan(const osdn_desc *desc, const void *k,
                               const float *beta, const float *r,

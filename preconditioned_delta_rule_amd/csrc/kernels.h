@@ -73,6 +73,8 @@ struct ScanWork {
   int *pin;
   uint64_t *stay;  // [B,H,N]: bit u set when token u of the chunk keeps a d on d_min there
   int *flags;
+  int *fok;     // [B,H,N]: 1 when ainv holds the chunk's factor (see precond_chunked.hip)
+  float *ainv;  // [B,H,N][64*64]: strictly lower part of the chunk's inverse triangular factor
 };
 constexpr int SCAN_CHUNK = 64;
 size_t scan_work_bytes(int64_t B, int64_t T, int64_t H, int64_t K);

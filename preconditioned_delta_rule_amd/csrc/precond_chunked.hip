@@ -68,6 +68,7 @@ __device__ __forceinline__ void lds_put(TIn *p, const Row<TIn, EPL, FULL> &r) {
 // ---------------------------------------------------------------- prep
 template <typename TIn, int EPL, bool FULL, bool HAS_R, bool VL, bool RV = false>
 __global__ __launch_bounds__(64) void scan_prep_kernel(ScanArgs a, ScanWork wk, int64_t N) {
+  __shared__ float sbuf[64 * RS_PITCH];
   const int lane = threadIdx.x;
   const int64_t seq = blockIdx.x / N, n = blockIdx.x % N;
   const int64_t H = a.H, K = a.K;
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(64) void scan_prep_kernel(ScanArgs a, ScanWork wk, 
       for (int e = 0; e < EPL; ++e) m = fmaxf(m, rv[e]);
       rm[u] = m;
     }
-    rt = reduce_scatter64<true>(rm, lane);
+    rt = reduce_scatter64<true>(rm, lane, sbuf);
   }
   float sn[CH], sm[CH];
 #pragma unroll
@@ -117,8 +118,8 @@ __global__ __launch_bounds__(64) void scan_prep_kernel(ScanArgs a, ScanWork wk, 
     sn[u] = pn;
     sm[u] = pm;
   }
-  const float nrm = reduce_scatter64<false>(sn, lane);  // lane u: |k_{t0+u}|^2
-  const float smx = reduce_scatter64<true>(sm, lane);   // lane u: max_i k_{t0+u,i}^2
+  const float nrm = reduce_scatter64<false>(sn, lane, sbuf);  // lane u: |k_{t0+u}|^2
+  const float smx = reduce_scatter64<true>(sm, lane, sbuf);   // lane u: max_i k_{t0+u,i}^2
   const float dmin = a.d_min;
   const float bpr = a.beta_aware ? bt : 1.0f;
   const float ea = a.eta * bpr / fmaxf(nrm, a.eps);
@@ -262,26 +263,198 @@ __global__ __launch_bounds__(256) void scan_prep128_kernel(ScanArgs a, ScanWork 
   }
 }
 
-// ---------------------------------------------------------------- solve
-// Shared memory: the chunk's key rows as loaded (TIn [CH][64 EPL]), the key
-// squares of the free coordinates in bf16 ([CH][64 EPL + 8]), their Gram
-// matrix (fp32 [CH][CH+1]) and per-token (x, c, r) (float4 [CH]).
-template <typename TIn, int EPL>
-constexpr size_t solve_lds_bytes() {
-  return (size_t)CH * 64 * EPL * sizeof(TIn) + (size_t)CH * (64 * EPL + 8) * 2 + (size_t)CH * (CH + 1) * 4 +
-         (size_t)CH * 16;
+// ---------------------------------------------------------------- factor
+// The part of the closed form below that does not depend on d, for a chunk
+// whose coordinates are all free.  With every coordinate free the step
+// scalars solve A x = y, A = I + diag(g) tril(G, -1) unit lower triangular,
+// G the Gram matrix of the chunk's key squares, g_t = b_t R_t / R_{t+1};
+// only y_t = a_t / R_{t+1} - g_t <d_0, s_t> involves d_0.  This pass (one
+// wave per chunk, all chunks at once) forms A^{-1} - I, so that the
+// per-(b,h) pass replaces the Gram matrix and the 64-step substitution by one
+// 64 x 64 matrix-vector product.  Lane c computes column c of A^{-1} by
+// forward elimination in fp32 (the Gram matrix on the matrix cores, from bf16
+// key squares, as in the solve pass).  The result goes out in the order the
+// solve pass copies it into LDS: element (t, j) at float ((j/4) 64 + t) 4 + j%4.
+// Chunks marked pinned, or outside the closed form's range (some r_t > 1, or
+// R_L < 1/4), get fok = 0 and no factor.
+template <typename TIn, int EPL, bool FULL, bool HAS_R, bool VL>
+__global__ __launch_bounds__(64) void scan_factor_kernel(ScanArgs a, ScanWork wk, int64_t N) {
+  constexpr int SP = 64 * EPL + 8;  // bf16 row pitch of the key squares
+  constexpr int GP = CH + 4;        // fp32 row pitch of the Gram matrix (16-byte rows)
+  __shared__ __attribute__((aligned(16))) bf16 sS[CH * SP];
+  __shared__ __attribute__((aligned(16))) float sG[CH * GP];
+  const int lane = threadIdx.x;
+  const int64_t ci = blockIdx.x;
+  const int64_t seq = ci / N, n = ci - seq * N;
+  const int64_t H = a.H, K = a.K;
+  const int64_t b = seq / H, h = seq - b * H;
+  const int64_t T = seq_len<VL>(a, b), tb = seq_base<VL>(a, b);
+  const int64_t t0 = n * CH;
+  if (VL && t0 >= T) return;  // past a shorter sequence's end
+  if (wk.pin[ci] == 1) {
+    if (lane == 0) wk.fok[ci] = 0;
+    return;
+  }
+  const int L = (int)((T - t0) < CH ? (T - t0) : CH);
+  const bool tok = lane < L;
+  const int64_t gi = (tb + t0 + (tok ? lane : 0)) * H + h;
+  float bt = a.beta[gi], rt = HAS_R ? a.r[gi] : 1.0f, nrm = wk.norm[gi];
+  if (!tok) {
+    bt = 0.0f;
+    rt = 1.0f;
+    nrm = 1.0f;
+  }
+  const float bpr = a.beta_aware ? bt : 1.0f;
+  const float ea = a.eta * bpr / fmaxf(nrm, a.eps);
+  const float eb = ea * bpr;
+  float g = eb;
+  if constexpr (HAS_R) {
+    // the same retention products and range test as the solve pass
+    const float lr = logf(rt);
+    float lin = lr;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(lin, off, 64);
+      if (lane >= off) lin += y;
+    }
+    const float Rn = __expf(lin), Rt = __expf(lin - lr);
+    if (!(lane_bcast(Rn, L - 1) >= 0.25f && __all(rt <= 1.0f) != 0)) {
+      if (lane == 0) wk.fok[ci] = 0;
+      return;
+    }
+    g = eb * (Rt / Rn);
+  }
+  // key squares of every coordinate (bf16; rows past the end are zero)
+  {
+    const int64_t stride = H * K;
+    const TIn *rp = static_cast<const TIn *>(a.k) + ((tb + t0) * H + h) * K;
+    Row<TIn, EPL, FULL> rows[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      rows[u].load(rp, lane, K);
+      if (u + 1 < L) rp += stride;
+    }
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      float k[EPL];
+      rows[u].get(k);
+      typedef typename RowVec<bf16, EPL>::type Bv;
+      Bv v;
+      bf16 sq[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sq[e] = to_bf16(u < L ? k[e] * k[e] : 0.0f);
+      __builtin_memcpy(&v, sq, sizeof(Bv));
+      *reinterpret_cast<Bv *>(sS + u * SP + lane * EPL) = v;
+    }
+  }
+  wave_lds_sync();
+  // the whole (symmetric) Gram matrix, so that each of its rows is contiguous
+  {
+    const int l16 = lane & 15, lq = lane >> 4;
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < 4; ++tj) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < 64 * EPL; k0 += 32) {
+          const bf16x8 x = *reinterpret_cast<const bf16x8 *>(&sS[(16 * ti + l16) * SP + k0 + 8 * lq]);
+          const bf16x8 y = *reinterpret_cast<const bf16x8 *>(&sS[(16 * tj + l16) * SP + k0 + 8 * lq]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sG[(16 * ti + 4 * lq + i) * GP + 16 * tj + l16] = acc[i];
+      }
+  }
+  wave_lds_sync();
+  // M[j][t] = g_t G[j][t] = (diag(g) G)[t][j]: lane t scales column t
+#pragma unroll
+  for (int j = 0; j < CH; ++j) sG[j * GP + lane] *= g;
+  wave_lds_sync();
+  // column `lane` of A^{-1}: once z_j is final, z_t -= M[j][t] z_j for t > j
+  // (row j + 1 of M is read while row j is applied)
+  float z[CH];
+#pragma unroll
+  for (int t = 0; t < CH; ++t) z[t] = t == lane ? 1.0f : 0.0f;
+  floatx4 mc[CH / 4];
+#pragma unroll
+  for (int q = 0; q < CH / 4; ++q) mc[q] = *reinterpret_cast<const floatx4 *>(&sG[4 * q]);
+#pragma unroll
+  for (int j = 0; j < CH - 1; ++j) {
+    floatx4 mn[CH / 4];
+#pragma unroll
+    for (int q = (j + 2) / 4; q < CH / 4; ++q)
+      if (j + 1 < CH - 1) mn[q] = *reinterpret_cast<const floatx4 *>(&sG[(j + 1) * GP + 4 * q]);
+    const float zj = z[j];
+#pragma unroll
+    for (int q = (j + 1) / 4; q < CH / 4; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * q + i > j) z[4 * q + i] = fmaf(-mc[q][i], zj, z[4 * q + i]);
+#pragma unroll
+    for (int q = (j + 2) / 4; q < CH / 4; ++q) mc[q] = mn[q];
+  }
+  wave_lds_sync();  // every lane is done with M
+  // transpose through LDS (pitch 65: conflict-free both ways), then one
+  // contiguous kilobyte per store instruction
+  float *sX = sG;
+#pragma unroll
+  for (int t = 0; t < CH; ++t) sX[lane * (CH + 1) + t] = t > lane ? z[t] : 0.0f;
+  wave_lds_sync();
+  float *dst = wk.ainv + ci * (CH * CH);
+#pragma unroll
+  for (int q = 0; q < CH / 4; ++q) {
+    floatx4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = sX[(4 * q + i) * (CH + 1) + lane];
+    *reinterpret_cast<floatx4 *>(dst + (q * 64 + lane) * 4) = v;
+  }
+  if (lane == 0) wk.fok[ci] = 1;
 }
+
+// ---------------------------------------------------------------- solve
+// Key rows reach LDS by direct copies (global_load_lds, two buffers: the
+// next chunk's arrive while this one is used) when a row is a whole number of
+// 16-byte pieces and both buffers fit; otherwise through registers.
+template <typename TIn, int EPL, bool FULL, bool RV>
+constexpr bool solve_rows_dma() {
+  return FULL && !RV && 64 * EPL * sizeof(TIn) <= 512;
+}
+
+// Shared memory: the chunk's key rows (TIn [CH][64 EPL], two buffers with
+// direct copies), the key squares of the free coordinates in bf16
+// ([CH][64 EPL + 8]), their Gram matrix (fp32 [CH][CH+1]), per-token
+// (x, c, r) (float4 [CH]), then either two chunks' A^{-1} - I from the factor
+// pass (fp32 [2][CH CH], by chunk parity) or, with vector retention, the
+// chunk's retention rows (fp32 [CH][64 EPL]).
+template <typename TIn, int EPL, bool FULL, bool RV>
+constexpr size_t solve_lds_bytes() {
+  return (size_t)CH * 64 * EPL * sizeof(TIn) * (solve_rows_dma<TIn, EPL, FULL, RV>() ? 2 : 1) +
+         (size_t)CH * (64 * EPL + 8) * 2 + (size_t)CH * (CH + 1) * 4 + (size_t)CH * 16 +
+         (RV ? (size_t)CH * 64 * EPL * 4 : (size_t)2 * CH * CH * 4);
+}
+
+// One 16-byte global -> LDS copy per lane (global_load_lds): lane i writes
+// bytes [16 i, 16 i + 16) after `lds`, which must be the same for every lane.
+// The compiler does not track these copies: wait on vmcnt before reading.
+__device__ __forceinline__ void dma16(const void *src, void *lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <typename TIn, int EPL, bool FULL, bool HAS_R, bool PF, bool VL, bool RV = false>
 __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk, int64_t N) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int RP = 64 * EPL;      // row pitch of sR (elements)
   constexpr int SP = 64 * EPL + 8;  // row pitch of sS (bf16)
-  TIn *sR = reinterpret_cast<TIn *>(smem);
-  bf16 *sS = reinterpret_cast<bf16 *>(smem + (size_t)CH * RP * sizeof(TIn));
-  float *sG = reinterpret_cast<float *>(smem + (size_t)CH * RP * sizeof(TIn) + (size_t)CH * SP * 2);
+  constexpr bool DMA = solve_rows_dma<TIn, EPL, FULL, RV>();
+  constexpr size_t RB = (size_t)CH * RP * sizeof(TIn) * (DMA ? 2 : 1);  // bytes of the row buffers
+  TIn *sRb = reinterpret_cast<TIn *>(smem);
+  bf16 *sS = reinterpret_cast<bf16 *>(smem + RB);
+  float *sG = reinterpret_cast<float *>(smem + RB + (size_t)CH * SP * 2);
   floatx4 *sTok = reinterpret_cast<floatx4 *>(sG + CH * (CH + 1));
-  float *sRv = reinterpret_cast<float *>(sTok + CH);  // RV: the chunk's retention rows [CH][RP]
+  float *sA = reinterpret_cast<float *>(sTok + CH);  // factors of chunks n, n + 1 ([2][CH CH], by n & 1)
+  float *sRv = sA;                                    // RV: the chunk's retention rows [CH][RP]
 
   const int lane = threadIdx.x;
   const int64_t seq = blockIdx.x;
@@ -302,10 +475,36 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
     d[e] = valid[e] ? (a.d1 ? a.d1[seq * K + c] : 1.0f) : 0.0f;
   }
   int n_pinned = 0, n_active = 0, n_seq = 0;
-  uint64_t pinmask = 0;
+  uint64_t pinmask = 0, fokmask = 0;
+  bool ahave = false;    // chunk n's factor copy was issued during chunk n - 1
+  float pend_c = 0.0f;   // a chunk's step scalars are stored at the top of the next
+  int64_t pend_gi = -1;  // pass (after its wait), so no store is in flight at that wait
+  // the factor pass's A^{-1} - I of chunk m into sA (16 copies of 1 KB)
+  auto dma_factor = [&](int64_t m) {
+    const float *src = wk.ainv + (seq * N + m) * (CH * CH);
+    float *dst = sA + (m & 1) * (CH * CH);
+#pragma unroll
+    for (int q = 0; q < CH / 4; ++q) dma16(src + q * 256 + lane * 4, dst + q * 256);
+  };
+  // chunk m's key rows into row buffer m & 1 (rows past the end repeat the
+  // last one): lane l of copy i brings 16 bytes of row i RPI + l / (RB16)
+  auto dma_rows = [&](int64_t m) {
+    constexpr int RB16 = 64 * EPL * (int)sizeof(TIn) / 16;  // 16-byte pieces per row
+    constexpr int RPI = 64 / RB16;                           // rows per copy
+    const int64_t tm = m * CH;
+    const int Lm = (int)((T - tm) < CH ? (T - tm) : CH);
+    const TIn *src = static_cast<const TIn *>(a.k) + ((tb + tm) * H + h) * K + (lane % RB16) * (16 / sizeof(TIn));
+    TIn *dst = sRb + (m & 1) * (CH * RP);
+    const int lr = lane / RB16;
+#pragma unroll
+    for (int i = 0; i < CH / RPI; ++i) {
+      const int row = i * RPI + lr;
+      dma16(src + (int64_t)(row < Lm ? row : Lm - 1) * stride, dst + i * RPI * RP);
+    }
+  };
   Row<TIn, EPL, FULL> nrow[PF ? CH : 1];
   float nbt = 0.0f, nrt = 1.0f, nnrm = 1.0f;
-  bool have = false;  // chunk n's rows already sit in sR, its scalars in nbt/nrt/nnrm
+  bool have = false;  // chunk n's rows already sit in (or are on their way to) LDS, its scalars in nbt/nrt/nnrm
 
   // every pass of the loop advances n by step >= 1 (a pinned run sets it)
   for (int64_t n = 0, step = 1; n < Nb; n += step) {
@@ -317,6 +516,10 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
     if ((n & 63) == 0) {
       const int p = n + lane < Nb ? wk.pin[seq * N + n + lane] : 0;
       pinmask = __ballot(p == 1);
+      if constexpr (!RV) {
+        const int f = n + lane < Nb ? wk.fok[seq * N + n + lane] : 0;
+        fokmask = __ballot(f == 1);
+      }
     }
 
     // where d sits: on d_min, on d_max, inside
@@ -343,17 +546,38 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
         n_pinned += run;
         step = run;
         have = false;
+        ahave = false;
         continue;
       }
     }
+    wait_loads();  // the copies issued during the previous chunk have landed
+    if (pend_gi >= 0) wk.cstep[pend_gi] = pend_c;
+    pend_gi = -1;
 #pragma unroll
     for (int e = 0; e < EPL; ++e)
       if (valid[e]) wk.dstart[(seq * N + n) * K + lane * EPL + e] = d[e];
+    // every coordinate free and the chunk has a factor: the closed form
+    // needs only a matrix-vector product with it
+    const bool fast = !RV && ((fokmask >> (n & 63)) & 1) != 0 && !any_lo && !any_hi && any_free;
+    TIn *sR = sRb + (DMA ? (n & 1) * (CH * RP) : 0);
+    {
+      // copies not issued during the previous chunk: now, and wait for them
+      bool issued = false;
+      if (DMA && !have) {
+        dma_rows(n);
+        issued = true;
+      }
+      if (fast && !ahave) {
+        dma_factor(n);
+        issued = true;
+      }
+      if (issued) wait_loads();
+    }
 
     // this chunk's key rows and scalars
     const TIn *kp = static_cast<const TIn *>(a.k) + ((tb + t0) * H + h) * K;
     float bt, rt, nrm;
-    if (PF && have) {
+    if ((PF || DMA) && have) {
       bt = nbt;
       rt = nrt;
       nrm = nnrm;
@@ -362,11 +586,15 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
       rt = HAS_R ? a.r[gi] : 1.0f;
       nrm = wk.norm[gi];
       constexpr int GL = CH / Row<TIn, EPL, FULL>::WORDS;  // rows per load batch (<= 64 words)
+      const TIn *rp = kp;  // row u0 + u, the last row repeated past the end
 #pragma unroll
-      for (int u0 = 0; u0 < CH; u0 += GL) {
+      for (int u0 = 0; u0 < (DMA ? 0 : CH); u0 += GL) {
         Row<TIn, EPL, FULL> tmp[GL];
 #pragma unroll
-        for (int u = 0; u < GL; ++u) tmp[u].load(kp + (u0 + u < L ? u0 + u : L - 1) * stride, lane, K);
+        for (int u = 0; u < GL; ++u) {
+          tmp[u].load(rp, lane, K);
+          if (u0 + u + 1 < L) rp += stride;
+        }
 #pragma unroll
         for (int u = 0; u < GL; ++u) lds_put<TIn, EPL, FULL>(sR + (u0 + u) * RP + lane * EPL, tmp[u]);
       }
@@ -392,14 +620,26 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
     // unless the prep pass marked it: if d ends this chunk on d_min the run
     // of marked chunks is skipped without its rows, else they are loaded then
     const bool next_marked = ((n + 1) & 63) != 0 && ((pinmask >> ((n + 1) & 63)) & 1) != 0;
-    const bool pf = PF && n + 1 < Nb && !next_marked;
-    if constexpr (PF) {
+    const bool pf = (PF || DMA) && n + 1 < Nb && !next_marked;
+    bool ahave_next = false;
+    if constexpr (PF || DMA) {
       if (pf) {
+        if (!RV && ((n + 1) & 63) != 0 && ((fokmask >> ((n + 1) & 63)) & 1) != 0) {
+          dma_factor(n + 1);
+          ahave_next = true;
+        }
         const int64_t t1 = t0 + CH;
         const int L1 = (int)((T - t1) < CH ? (T - t1) : CH);
-        const TIn *kp1 = kp + CH * stride;
+        if constexpr (DMA) {
+          dma_rows(n + 1);
+        } else {
+          const TIn *rp = kp + CH * stride;
 #pragma unroll
-        for (int u = 0; u < CH; ++u) nrow[u].load(kp1 + (u < L1 ? u : L1 - 1) * stride, lane, K);
+          for (int u = 0; u < CH; ++u) {
+            nrow[u].load(rp, lane, K);
+            if (u + 1 < L1) rp += stride;
+          }
+        }
         const int64_t gi1 = (tb + t1 + (lane < L1 ? lane : 0)) * H + h;
         nbt = a.beta[gi1];
         nrt = HAS_R ? a.r[gi1] : 1.0f;
@@ -411,7 +651,7 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
     const float eb = ea * bpr;
     float cst = 0.0f;  // lane u: c for token t0 + u
     bool done = false;
-    __syncthreads();
+    wave_lds_sync();
 
     // retention products R_t = prod_{l<t} r_l (log-space scan): Rn = R_{t+1},
     // Rt = R_t.  The bound on free coordinates below needs R_t non-increasing,
@@ -437,34 +677,53 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
     // ---- fixed active set, closed form
     if (try_closed) {
       float pvF[CH], pvP[HAS_R ? CH : 1];
+      // one pass over the rows; the branch on writing the squares is taken
+      // once, outside the unrolled loop, so that the row reads can overlap
+      auto sq_pass = [&](auto ws) {
+        constexpr bool WS = decltype(ws)::value;
 #pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        float k[EPL];
-        lds_get<TIn, EPL>(sR + u * RP + lane * EPL, k);
-        float pf_ = 0.0f, pp_ = 0.0f;
+        for (int u = 0; u < CH; ++u) {
+          float k[EPL];
+          lds_get<TIn, EPL>(sR + u * RP + lane * EPL, k);
+          float pf_ = 0.0f, pp_ = 0.0f;
+          bf16 sq[EPL];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          const float s = u < L ? k[e] * k[e] : 0.0f;
-          if (HAS_R) {
-            pf_ = fmaf(fr[e] ? d[e] : 0.0f, s, pf_);
-            pp_ = fmaf(fr[e] ? 0.0f : d[e], s, pp_);
-          } else {
-            pf_ = fmaf(d[e], s, pf_);
+          for (int e = 0; e < EPL; ++e) {
+            const float s = u < L ? k[e] * k[e] : 0.0f;
+            if (HAS_R) {
+              pf_ = fmaf(fr[e] ? d[e] : 0.0f, s, pf_);
+              pp_ = fmaf(fr[e] ? 0.0f : d[e], s, pp_);
+            } else {
+              pf_ = fmaf(d[e], s, pf_);
+            }
+            sq[e] = to_bf16(fr[e] ? s : 0.0f);
           }
-          if (any_free) sS[u * SP + lane * EPL + e] = to_bf16(fr[e] ? s : 0.0f);
+          if constexpr (WS) {
+            typedef typename RowVec<bf16, EPL>::type Bv;
+            Bv v;
+            __builtin_memcpy(&v, sq, sizeof(Bv));
+            *reinterpret_cast<Bv *>(sS + u * SP + lane * EPL) = v;
+          }
+          pvF[u] = pf_;
+          if (HAS_R) pvP[HAS_R ? u : 0] = pp_;
         }
-        pvF[u] = pf_;
-        if (HAS_R) pvP[HAS_R ? u : 0] = pp_;
-      }
-      const float p0F = reduce_scatter64<false>(pvF, lane);  // <d_0, s_t> over the free (all, without r) coords
+      };
+      if (any_free && !fast)
+        sq_pass(std::true_type{});
+      else
+        sq_pass(std::false_type{});
+      const float p0F = reduce_scatter64<false>(pvF, lane, sG);  // <d_0, s_t> over the free (all, without r) coords
       float p0P = 0.0f;
-      if constexpr (HAS_R) p0P = reduce_scatter64<false>(pvP, lane);  // over the coords on a bound
-      __syncthreads();
-      if (any_free) {
+      if constexpr (HAS_R)
+        if (!fast) p0P = reduce_scatter64<false>(pvP, lane, sG);  // over the coords on a bound
+      wave_lds_sync();
+      if (any_free && !fast) {
         // Gram matrix of the free key squares, lower 16x16 tiles
         const int l16 = lane & 15, lq = lane >> 4;
         for (int ti = 0; ti < 4; ++ti)
-          for (int tj = 0; tj <= ti; ++tj) {
+#pragma unroll
+          for (int tj = 0; tj < 4; ++tj) {
+            if (tj > ti) continue;
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k0 = 0; k0 < 64 * EPL; k0 += 32) {
@@ -475,12 +734,29 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
 #pragma unroll
             for (int i = 0; i < 4; ++i) sG[(16 * ti + 4 * lq + i) * (CH + 1) + 16 * tj + l16] = acc[i];
           }
-        __syncthreads();
+        wave_lds_sync();
       }
       float x = 0.0f;
       if (!any_free) {
         // every coordinate on a bound: <d, s_t> = <d_0, s_t>
         if (tok) cst = fmaf(-eb, p0P + p0F, ea);
+      } else if (fast) {
+        // x = y + (A^{-1} - I) y, y_t = ea_t / R_{t+1} - g_t p0F_t
+        const float g = HAS_R ? eb * (Rt / Rn) : eb;
+        const float y = tok ? (HAS_R ? ea / Rn - g * p0F : ea - g * p0F) : 0.0f;
+        sG[lane] = y;
+        wave_lds_sync();
+        const float *Ai = sA + (n & 1) * (CH * CH);
+        float acc = y;
+#pragma unroll
+        for (int q = 0; q < CH / 4; ++q) {
+          const floatx4 av = *reinterpret_cast<const floatx4 *>(Ai + (q * 64 + lane) * 4);
+          const floatx4 yv = *reinterpret_cast<const floatx4 *>(sG + 4 * q);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc = fmaf(av[i], yv[i], acc);
+        }
+        x = tok ? acc : 0.0f;
+        cst = Rn * x;
       } else {
         // x_t + g_t sum_{j<t} G_jt x_j = ea_t / R_{t+1} - g_t (p0P_t / R_t + p0F_t),
         // g_t = eb_t R_t / R_{t+1}
@@ -502,7 +778,7 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
         cst = Rn * x;
       }
       sTok[lane] = floatx4{x, cst, rt, 0.0f};
-      __syncthreads();
+      wave_lds_sync();
       // check the active set; d_L = R_L (d_0 + sum_j x_j s_j) on free coords
       float sum[EPL], bnd[EPL], mxl[EPL], mnh[EPL];
 #pragma unroll
@@ -511,9 +787,13 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
         mxl[e] = dmin;
         mnh[e] = dmax;
       }
-#pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        if (u < L) {
+      // tokens past the sequence's end carry x = c = 0 and r = 1, which
+      // leave every sum and bound below unchanged: no branch in the loop;
+      // the bounds of coordinates sitting on d_min / d_max only when some do
+      auto check_pass = [&](auto bounds) {
+        constexpr bool BOUNDS = decltype(bounds)::value;
+#pragma unroll 8
+        for (int u = 0; u < CH; ++u) {
           float k[EPL];
           lds_get<TIn, EPL>(sR + u * RP + lane * EPL, k);
           const floatx4 tv = sTok[u];
@@ -522,11 +802,17 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
             const float s = k[e] * k[e];
             sum[e] = fmaf(tv[0], s, sum[e]);
             bnd[e] = fmaf(fabsf(tv[0]), s, bnd[e]);
-            if (any_lo) mxl[e] = fmaxf(mxl[e], fmaf(tv[1], s, tv[2] * dmin));
-            if (any_hi) mnh[e] = fminf(mnh[e], fmaf(tv[1], s, tv[2] * dmax));
+            if constexpr (BOUNDS) {
+              mxl[e] = fmaxf(mxl[e], fmaf(tv[1], s, tv[2] * dmin));
+              mnh[e] = fminf(mnh[e], fmaf(tv[1], s, tv[2] * dmax));
+            }
           }
         }
-      }
+      };
+      if (any_lo || any_hi)
+        check_pass(std::true_type{});
+      else
+        check_pass(std::false_type{});
       const float RL = lane_bcast(Rn, L - 1);
       bool ok = true;
       float dn[EPL];
@@ -595,8 +881,9 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
         }
       }
     }
-    if (tok && lane < u_end) wk.cstep[gi] = cst;
-    __syncthreads();
+    pend_c = cst;
+    pend_gi = tok && lane < u_end ? gi : -1;
+    wave_lds_sync();
     if constexpr (PF) {
       if (pf) {
 #pragma unroll
@@ -604,8 +891,10 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
       }
     }
     have = pf;
-    __syncthreads();
+    ahave = ahave_next;
+    wave_lds_sync();
   }
+  if (pend_gi >= 0) wk.cstep[pend_gi] = pend_c;
   if (a.d_out) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e)
@@ -787,9 +1076,15 @@ hipError_t launch_all(const ScanArgs &a, const ScanWork &w, hipStream_t s, bool 
                          a, w, N);
     }
     prof_mark(s, "scan_prep_kernel");
+    if constexpr (!RV) {
+      hipLaunchKernelGGL((scan_factor_kernel<TIn, EPL, FULL, HAS_R, VL>), dim3((unsigned)(nseq * N)), dim3(64), 0, s,
+                         a, w, N);
+      prof_mark(s, "scan_factor_kernel");
+    }
   }
-  constexpr bool PF = !RV && Row<TIn, EPL, FULL>::WORDS <= 2;
-  constexpr size_t shm = solve_lds_bytes<TIn, EPL>() + (RV ? (size_t)CH * 64 * EPL * 4 : 0);
+  // register prefetch of the next chunk's rows where they do not come by direct copies
+  constexpr bool PF = !RV && !solve_rows_dma<TIn, EPL, FULL, RV>() && Row<TIn, EPL, FULL>::WORDS <= 2;
+  constexpr size_t shm = solve_lds_bytes<TIn, EPL, FULL, RV>();
   static_assert(shm <= 160 * 1024, "solve kernel LDS");
   auto kern = scan_solve_kernel<TIn, EPL, FULL, HAS_R, PF, VL, RV>;
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
@@ -824,7 +1119,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t scan_work_bytes(int64_t B, int64_t T, int64_t H, int64_t K) {
   const int64_t N = (T + CH - 1) / CH;
   return 2 * align256((size_t)(B * T * H) * 4) + align256((size_t)(B * H * N * K) * 4) +
-         align256((size_t)(B * H * N) * 4) + align256((size_t)(B * H * N) * 8) + align256((size_t)(B * H) * 3 * 4);
+         align256((size_t)(B * H * N) * 4) + align256((size_t)(B * H * N) * 8) + align256((size_t)(B * H) * 3 * 4) +
+         align256((size_t)(B * H * N) * 4) + align256((size_t)(B * H * N) * CH * CH * 4);
 }
 
 ScanWork scan_work_layout(void *base, int64_t B, int64_t T, int64_t H, int64_t K) {
@@ -841,6 +1137,9 @@ ScanWork scan_work_layout(void *base, int64_t B, int64_t T, int64_t H, int64_t K
   w.pin = reinterpret_cast<int *>(p + 2 * tok + dst);
   w.stay = reinterpret_cast<uint64_t *>(p + 2 * tok + dst + pin);
   w.flags = reinterpret_cast<int *>(p + 2 * tok + dst + pin + stay);
+  const size_t flags = align256((size_t)(B * H) * 3 * 4);
+  w.fok = reinterpret_cast<int *>(p + 2 * tok + dst + pin + stay + flags);
+  w.ainv = reinterpret_cast<float *>(p + 2 * tok + dst + 2 * pin + stay + flags);
   return w;
 }
 

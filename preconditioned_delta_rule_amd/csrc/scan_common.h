@@ -89,30 +89,40 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
-// Transposed reduction over the 64 lanes of a wave: on entry every lane holds
-// 64 partial values v[0..63]; on return lane l holds the combination over all
-// lanes of entry l.  Recursive halving: at each level a lane keeps the half of
-// its values its partner gives away and combines the partner's copy of it.
+// Transposed reduction over the 64 lanes of a one-wave workgroup (the only
+// kind that calls it; the exchange is ordered with wave_lds_sync): on entry
+// every lane holds 64 partial values v[0..63]; on return lane l holds the
+// combination over all lanes of entry l.  The transpose goes through LDS
+// (buf: RS_PITCH * 64 floats): lane l writes its entries to row l, then
+// reads column l.  With a row pitch of 65 words both the row writes and the
+// column reads touch 64 distinct banks.  (Lane permutes would need a chain of
+// dependent exchanges; here the 64 writes and the 64 reads each pipeline.)
+constexpr int RS_PITCH = 65;
+
+// Orders the LDS accesses of a one-wave workgroup around a cross-lane
+// exchange.  The LDS unit executes one wave's operations in order, so only
+// the compiler has to be kept from moving them; unlike __syncthreads this
+// does not also wait for the wave's outstanding global loads.
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <bool MAX>
-__device__ __forceinline__ float reduce_scatter64(float (&v)[64], int lane) {
+__device__ __forceinline__ float reduce_scatter64(const float (&v)[64], int lane, float *buf) {
+  wave_lds_sync();  // earlier readers of buf are done
 #pragma unroll
-  for (int lvl = 0; lvl < 6; ++lvl) {
-    const int m = 32 >> lvl, n = 64 >> lvl;
-    const bool upper = (lane & m) != 0;
+  for (int j = 0; j < 64; ++j) buf[lane * RS_PITCH + j] = v[j];
+  wave_lds_sync();
+  float acc = buf[lane];
 #pragma unroll
-    for (int j = 0; j < n / 2; ++j) {
-      // the empty asm makes both halves plain values, so the per-lane choice
-      // stays a register select instead of becoming an indexed (scratch)
-      // access to v
-      float a = v[j], b = v[j + n / 2];
-      asm("" : "+v"(a), "+v"(b));
-      const float give = upper ? a : b;
-      const float keep = upper ? b : a;
-      const float got = __shfl_xor(give, m, 64);
-      v[j] = MAX ? fmaxf(keep, got) : keep + got;
-    }
+  for (int u = 1; u < 64; ++u) {
+    const float x = buf[u * RS_PITCH + lane];
+    acc = MAX ? fmaxf(acc, x) : acc + x;
   }
-  return v[0];
+  wave_lds_sync();  // buf may be reused at once
+  return acc;
 }
 
 }  // namespace osdn

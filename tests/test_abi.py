@@ -139,14 +139,16 @@ def test_null_and_misaligned_pointers_rejected_before_launch(lib):
 def test_workspace_bytes(lib):
     # chunked phase 1 at B=4, T=4096, H=16, K=128: key norms and step scalars
     # (fp32 per token), d at each of the 64 chunk starts, a word and a 64-bit
-    # token mask per chunk and three counters per (b,h), each region rounded
-    # up to 256 bytes
+    # token mask per chunk, three counters per (b,h), then a flag word and a
+    # 64 x 64 fp32 triangular factor per chunk, each region rounded up to 256
+    # bytes
     d = osdn.Desc()
     lib.osdn_desc_init(ctypes.byref(d), 4, 4096, 16, 128, 128)
     tok = 4 * 4096 * 16 * 4
-    scan = 2 * tok + 4 * 16 * 64 * 128 * 4 + 4 * 16 * 64 * 4 + 4 * 16 * 64 * 8 + 256 * 3
+    counters = 2 * tok + 4 * 16 * 64 * 128 * 4 + 4 * 16 * 64 * 4 + 4 * 16 * 64 * 8
+    scan = counters + 256 * 3 + 4 * 16 * 64 * 4 + 4 * 16 * 64 * 64 * 64 * 4
     assert lib.osdn_precond_scan_workspace_bytes(ctypes.byref(d)) == scan
-    assert lib.osdn_precond_scan_counters_offset(ctypes.byref(d)) == scan - 256 * 3
+    assert lib.osdn_precond_scan_counters_offset(ctypes.byref(d)) == counters
     # phase 2 on the matrix cores keeps, per chunk, the six 16 x 64 blocks of
     # (I + A)^-1 on and below the diagonal (bf16) and the intra-chunk scores
     # in the same blocks as hi/lo bf16 pairs
@@ -161,7 +163,8 @@ def test_workspace_bytes(lib):
     n = 65
     tok = -(-4 * 4097 * 16 * 4 // 256) * 256
     scan = (2 * tok + 4 * 16 * n * 128 * 4 + -(-4 * 16 * n * 4 // 256) * 256
-            + -(-4 * 16 * n * 8 // 256) * 256 + 256 * 3)
+            + -(-4 * 16 * n * 8 // 256) * 256 + 256 * 3
+            + -(-4 * 16 * n * 4 // 256) * 256 + 4 * 16 * n * 64 * 64 * 4)
     assert lib.osdn_precond_scan_workspace_bytes(ctypes.byref(d)) == scan
 
 
