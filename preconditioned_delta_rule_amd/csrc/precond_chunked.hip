@@ -281,8 +281,12 @@ template <typename TIn, int EPL, bool FULL, bool HAS_R, bool VL>
 __global__ __launch_bounds__(64) void scan_factor_kernel(ScanArgs a, ScanWork wk, int64_t N) {
   constexpr int SP = 64 * EPL + 8;  // bf16 row pitch of the key squares
   constexpr int GP = CH + 4;        // fp32 row pitch of the Gram matrix (16-byte rows)
-  __shared__ __attribute__((aligned(16))) bf16 sS[CH * SP];
-  __shared__ __attribute__((aligned(16))) float sG[CH * GP];
+  // the Gram matrix overwrites the key squares once they are consumed (less
+  // LDS per workgroup, more workgroups per CU)
+  constexpr int SB = CH * SP * 2, GB = CH * GP * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char sbuf[SB > GB ? SB : GB];
+  bf16 *sS = reinterpret_cast<bf16 *>(sbuf);
+  float *sG = reinterpret_cast<float *>(sbuf);
   const int lane = threadIdx.x;
   const int64_t ci = blockIdx.x;
   const int64_t seq = ci / N, n = ci - seq * N;
@@ -351,20 +355,26 @@ __global__ __launch_bounds__(64) void scan_factor_kernel(ScanArgs a, ScanWork wk
   // the whole (symmetric) Gram matrix, so that each of its rows is contiguous
   {
     const int l16 = lane & 15, lq = lane >> 4;
+    floatx4 acc[4][4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
       for (int tj = 0; tj < 4; ++tj) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc[ti][tj] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k0 = 0; k0 < 64 * EPL; k0 += 32) {
           const bf16x8 x = *reinterpret_cast<const bf16x8 *>(&sS[(16 * ti + l16) * SP + k0 + 8 * lq]);
           const bf16x8 y = *reinterpret_cast<const bf16x8 *>(&sS[(16 * tj + l16) * SP + k0 + 8 * lq]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, acc, 0, 0, 0);
+          acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, acc[ti][tj], 0, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sG[(16 * ti + 4 * lq + i) * GP + 16 * tj + l16] = acc[i];
       }
+    wave_lds_sync();  // the squares are consumed
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < 4; ++tj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sG[(16 * ti + 4 * lq + i) * GP + 16 * tj + l16] = acc[ti][tj][i];
   }
   wave_lds_sync();
   // M[j][t] = g_t G[j][t] = (diag(g) G)[t][j]: lane t scales column t
@@ -907,6 +917,381 @@ __global__ __launch_bounds__(64) void scan_solve_kernel(ScanArgs a, ScanWork wk,
   }
 }
 
+// ---------------------------------------------------------------- solve, K = 128
+// The same pass for K = 128 with scalar (or no) retention, over four waves so
+// that a chunk's closed form is spread across the CU's four SIMDs.  Wave w
+// owns coordinates [32 w, 32 w + 32); lane l of it the pair 32 w + 2 (l % 16)
+// + {0, 1} for tokens 16 (l / 16) .. 16 (l / 16) + 15 of the chunk, holding
+// their key squares in registers.  A chunk whose coordinates are all free and
+// that has a factor: <d_0, s_t> by partial sums (a reduce-scatter over the 16
+// lanes of a DPP row, then over the waves through LDS); y and x = y +
+// (A^{-1} - I) y in every wave (lane = token); d_L and the bound of the
+// active-set check per coordinate pair (partial sums combined over the four
+// token groups).  Two workgroup barriers per chunk: after the partial sums,
+// and after the check (which also publishes the new d's position in the box).
+// Any other chunk is swept token by token by wave 0 with d gathered in LDS.
+// Key rows and factors arrive by direct copies, a quarter issued by each
+// wave, each wave waiting for its own before the check's barrier.
+template <typename TIn>
+constexpr size_t solve4_lds_bytes() {
+  // rows [2][CH][128], factors [2][CH CH], per-wave partial sums, y, x
+  // ([3][4][CH]), d (128) and the per-wave flags (4)
+  return (size_t)2 * CH * 128 * sizeof(TIn) + (size_t)2 * CH * CH * 4 + (size_t)3 * 4 * CH * 4 + 128 * 4 + 16;
+}
+
+// Workgroup barrier that does not wait for outstanding global loads (the
+// next chunk's copies stay in flight across it); LDS accesses before it are
+// complete.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Reduce-scatter over the 16 lanes of a DPP row: on entry lane j of the row
+// holds v[0..15]; on return it holds the sum over the row of entry j.  Each
+// level pairs lanes that differ in one bit of j (row mirror: bit 3, half-row
+// mirror: bit 2, quad permutations: bits 1 and 0) and agree above it; a lane
+// keeps the half of its entries whose index bit matches its own.
+template <int M, int CTL>
+__device__ __forceinline__ void rs16_level(float (&v)[16], int j) {
+  const bool upper = (j & M) != 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    float a = v[i], b = v[i + M];
+    asm("" : "+v"(a), "+v"(b));  // plain values: a register select, not an indexed access
+    const float give = upper ? a : b;
+    const float keep = upper ? b : a;
+    v[i] = keep + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, give), CTL, 0xF,
+                                                                         0xF, false));
+  }
+}
+__device__ __forceinline__ float reduce_scatter16(float (&v)[16], int j) {
+  rs16_level<8, 0x140>(v, j);
+  rs16_level<4, 0x141>(v, j);
+  rs16_level<2, 0x4E>(v, j);
+  rs16_level<1, 0xB1>(v, j);
+  return v[0];
+}
+
+template <typename TIn, bool HAS_R, bool VL>
+__global__ __launch_bounds__(256) void scan_solve4_kernel(ScanArgs a, ScanWork wk, int64_t N) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr int RP = 128;
+  TIn *sRb = reinterpret_cast<TIn *>(smem);                                        // [2][CH][RP]
+  float *sA = reinterpret_cast<float *>(smem + (size_t)2 * CH * RP * sizeof(TIn));  // [2][CH CH]
+  float *sPw = sA + 2 * CH * CH;                                                    // [4][CH]
+  float *sY = sPw + 4 * CH;                                                         // [4][CH]
+  float *sX = sY + 4 * CH;                                                          // [4][CH]
+  float *sD = sX + 4 * CH;                                                          // [128]
+  int *sF = reinterpret_cast<int *>(sD + 128);                                      // [4]
+
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cp = l & 15, tq = l >> 4;
+  const int c0 = 32 * w + 2 * cp;  // this lane's coordinates c0, c0 + 1
+  const int64_t seq = blockIdx.x;
+  const int64_t H = a.H;
+  const int64_t b = seq / H, h = seq - b * H;
+  const int64_t T = seq_len<VL>(a, b), tb = seq_base<VL>(a, b);
+  const int64_t Nb = (T + CH - 1) / CH;
+  const int64_t stride = H * RP;
+  const float eta = a.eta, eps = a.eps, dmin = a.d_min, dmax = a.d_max;
+  const bool clamp = a.clamp != 0, aware = a.beta_aware != 0;
+
+  float d[2];
+  d[0] = a.d1 ? a.d1[seq * RP + c0] : 1.0f;
+  d[1] = a.d1 ? a.d1[seq * RP + c0 + 1] : 1.0f;
+
+  // flags of this wave's coordinates: bit 0 some on d_min, 1 some on d_max, 2 some free
+  auto wave_flags = [&]() {
+    bool lo = false, hi = false, fr = false;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const bool onlo = clamp && d[e] == dmin;
+      const bool onhi = clamp && d[e] == dmax && !onlo;
+      lo |= onlo;
+      hi |= onhi;
+      fr |= !onlo && !onhi;
+    }
+    return (__any(lo) ? 1 : 0) | (__any(hi) ? 2 : 0) | (__any(fr) ? 4 : 0);
+  };
+  int gflags;  // the same flags over all coordinates
+  if (l == 0) sF[w] = wave_flags();
+  lds_barrier();
+  gflags = sF[0] | sF[1] | sF[2] | sF[3];
+  lds_barrier();  // sF is rewritten at the end of the first chunk
+
+  // this wave's quarter of the copies of chunk m's rows and factor
+  auto dma_rows = [&](int64_t m) {
+    constexpr int RB16 = RP * (int)sizeof(TIn) / 16;  // 16-byte pieces per row (16 or 32)
+    constexpr int RPI = 64 / RB16;                    // rows per copy (4 or 2)
+    const int64_t tm = m * CH;
+    const int Lm = (int)((T - tm) < CH ? (T - tm) : CH);
+    const TIn *src = static_cast<const TIn *>(a.k) + ((tb + tm) * H + h) * RP + (l % RB16) * (16 / sizeof(TIn));
+    TIn *dst = sRb + (m & 1) * (CH * RP);
+    constexpr int NC = CH / RPI;  // copies per chunk (16 or 32), a quarter per wave
+#pragma unroll
+    for (int i0 = 0; i0 < NC / 4; ++i0) {
+      const int i = w * (NC / 4) + i0;
+      const int row = i * RPI + l / RB16;
+      dma16(src + (int64_t)(row < Lm ? row : Lm - 1) * stride, dst + i * RPI * RP);
+    }
+  };
+  auto dma_factor = [&](int64_t m) {
+    const float *src = wk.ainv + (seq * N + m) * (CH * CH);
+    float *dst = sA + (m & 1) * (CH * CH);
+#pragma unroll
+    for (int q0 = 0; q0 < 4; ++q0) {
+      const int q = 4 * w + q0;
+      dma16(src + q * 256 + l * 4, dst + q * 256);
+    }
+  };
+
+  int n_pinned = 0, n_active = 0, n_seq = 0;
+  uint64_t pinmask = 0, fokmask = 0;
+  bool have = false, ahave = false;  // chunk n's rows / factor were copied during chunk n - 1
+  float nbt = 0.0f, nrt = 1.0f, nnrm = 1.0f;
+  float pend_c = 0.0f;  // wave 0: step scalars of the last chunk, stored after the next wait
+  int64_t pend_gi = -1;
+
+  for (int64_t n = 0, step = 1; n < Nb; n += step) {
+    step = 1;
+    const int64_t t0 = n * CH;
+    const int L = (int)((T - t0) < CH ? (T - t0) : CH);
+    const bool tok = l < L;  // lane l <-> token t0 + l in the token views
+    const int64_t gi = (tb + t0 + (tok ? l : 0)) * H + h;
+    if ((n & 63) == 0) {
+      const int p = n + l < Nb ? wk.pin[seq * N + n + l] : 0;
+      pinmask = __ballot(p == 1);
+      const int f = n + l < Nb ? wk.fok[seq * N + n + l] : 0;
+      fokmask = __ballot(f == 1);
+    }
+    const bool any_lo = (gflags & 1) != 0, any_hi = (gflags & 2) != 0, any_free = (gflags & 4) != 0;
+    if (!any_free && !any_hi) {
+      // d on d_min everywhere: skip the run of marked chunks (see scan_solve_kernel)
+      const uint64_t m = ~(pinmask >> (n & 63));
+      const int run = m ? (int)__builtin_ctzll(m) : 64;
+      if (run > 0) {
+        if (w == 0 && l < run) wk.pin[seq * N + n + l] = 2;
+        n_pinned += run;
+        step = run;
+        have = false;
+        ahave = false;
+        continue;
+      }
+    }
+    const bool fast = ((fokmask >> (n & 63)) & 1) != 0 && !any_lo && !any_hi;
+    if (!have || (fast && !ahave)) {
+      // copies not issued during the previous chunk: now, and wait for them
+      if (!have) dma_rows(n);
+      if (fast && !ahave) dma_factor(n);
+      wait_loads();
+      lds_barrier();
+    }
+    if (w == 0 && pend_gi >= 0) wk.cstep[pend_gi] = pend_c;
+    pend_gi = -1;
+    if (tq == 0) {
+      wk.dstart[(seq * N + n) * RP + c0] = d[0];
+      wk.dstart[(seq * N + n) * RP + c0 + 1] = d[1];
+    }
+    // per-token scalars (every wave, lane = token)
+    float bt, rt, nrm;
+    if (have) {
+      bt = nbt;
+      rt = nrt;
+      nrm = nnrm;
+    } else {
+      bt = a.beta[gi];
+      rt = HAS_R ? a.r[gi] : 1.0f;
+      nrm = wk.norm[gi];
+    }
+    if (!tok) {
+      bt = 0.0f;
+      rt = 1.0f;
+      nrm = 1.0f;
+    }
+    // the next chunk's copies and scalars, unless the prep pass marked it
+    const bool next_marked = ((n + 1) & 63) != 0 && ((pinmask >> ((n + 1) & 63)) & 1) != 0;
+    const bool pf = n + 1 < Nb && !next_marked;
+    bool ahave_next = false;
+    if (pf) {
+      if (((n + 1) & 63) != 0 && ((fokmask >> ((n + 1) & 63)) & 1) != 0) {
+        dma_factor(n + 1);
+        ahave_next = true;
+      }
+      dma_rows(n + 1);
+      const int64_t t1 = t0 + CH;
+      const int L1 = (int)((T - t1) < CH ? (T - t1) : CH);
+      const int64_t gi1 = (tb + t1 + (l < L1 ? l : 0)) * H + h;
+      nbt = a.beta[gi1];
+      nrt = HAS_R ? a.r[gi1] : 1.0f;
+      nnrm = wk.norm[gi1];
+    }
+    const float bpr = aware ? bt : 1.0f;
+    const float ea = eta * bpr / fmaxf(nrm, eps);  // c_t = ea - eb <d, s_t>
+    const float eb = ea * bpr;
+    float Rn = 1.0f, Rt = 1.0f;
+    if constexpr (HAS_R) {
+      const float lr = logf(rt);
+      float lin = lr;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(lin, off, 64);
+        if (l >= off) lin += y;
+      }
+      Rn = __expf(lin);
+      Rt = __expf(lin - lr);
+    }
+    const TIn *R = sRb + (n & 1) * (CH * RP);
+
+    bool done = false;
+    float cst = 0.0f;  // wave 0, lane = token: the step scalar
+    if (fast) {
+      // key squares of this lane's pair over its 16 tokens (rows past the end: 0)
+      float s0[16], s1[16], pp[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int t = 16 * tq + i;
+        float k[2];
+        lds_get<TIn, 2>(R + t * RP + c0, k);
+        s0[i] = t < L ? k[0] * k[0] : 0.0f;
+        s1[i] = t < L ? k[1] * k[1] : 0.0f;
+        pp[i] = fmaf(d[0], s0[i], d[1] * s1[i]);
+      }
+      sPw[w * CH + 16 * tq + cp] = reduce_scatter16(pp, cp);  // token 16 tq + cp, this wave's coordinates
+      lds_barrier();  // ---- A: partial sums of every wave in LDS
+      const float p0 = sPw[l] + sPw[CH + l] + sPw[2 * CH + l] + sPw[3 * CH + l];
+      const float g = HAS_R ? eb * (Rt / Rn) : eb;
+      const float y = tok ? (HAS_R ? ea / Rn - g * p0 : ea - g * p0) : 0.0f;
+      float *sYw = sY + w * CH, *sXw = sX + w * CH;
+      sYw[l] = y;
+      wave_lds_sync();
+      const float *Ai = sA + (n & 1) * (CH * CH);
+      float x = y;
+#pragma unroll
+      for (int q = 0; q < CH / 4; ++q) {
+        const floatx4 av = *reinterpret_cast<const floatx4 *>(Ai + (q * 64 + l) * 4);
+        const floatx4 yv = *reinterpret_cast<const floatx4 *>(sYw + 4 * q);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x = fmaf(av[i], yv[i], x);
+      }
+      x = tok ? x : 0.0f;
+      sXw[l] = x;
+      wave_lds_sync();
+      // d_L = R_L (d_0 + sum_t x_t s_t) and the bound sum_t |x_t| s_t on this pair
+      float sm[2] = {0.0f, 0.0f}, bd[2] = {0.0f, 0.0f};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const floatx4 xv = *reinterpret_cast<const floatx4 *>(sXw + 16 * tq + 4 * q);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sm[0] = fmaf(xv[i], s0[4 * q + i], sm[0]);
+          sm[1] = fmaf(xv[i], s1[4 * q + i], sm[1]);
+          bd[0] = fmaf(fabsf(xv[i]), s0[4 * q + i], bd[0]);
+          bd[1] = fmaf(fabsf(xv[i]), s1[4 * q + i], bd[1]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        sm[e] += __shfl_xor(sm[e], 16, 64);
+        sm[e] += __shfl_xor(sm[e], 32, 64);
+        bd[e] += __shfl_xor(bd[e], 16, 64);
+        bd[e] += __shfl_xor(bd[e], 32, 64);
+      }
+      const float RL = lane_bcast(Rn, L - 1);
+      bool ok = true;
+      float dn[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        dn[e] = RL * (d[e] + sm[e]);
+        if (clamp) ok = ok && RL * (d[e] - bd[e]) >= dmin && d[e] + bd[e] <= dmax;
+      }
+      // publish the check and where the new d sits; the next chunk's copies
+      // issued by this wave land before the barrier
+      const float dsave0 = d[0], dsave1 = d[1];
+      d[0] = dn[0];
+      d[1] = dn[1];
+      const int fl = wave_flags() | (__all(ok) ? 8 : 0);
+      wait_loads();
+      if (l == 0) sF[w] = fl;
+      lds_barrier();  // ---- B
+      const int f0 = sF[0], f1 = sF[1], f2 = sF[2], f3 = sF[3];
+      if ((f0 & f1 & f2 & f3 & 8) != 0) {
+        done = true;
+        ++n_active;
+        gflags = (f0 | f1 | f2 | f3) & 7;
+        cst = Rn * x;
+      } else {
+        d[0] = dsave0;
+        d[1] = dsave1;
+      }
+    }
+    int u_end = L;
+    if (!done) {
+      // token by token in wave 0 (see scan_solve_kernel) with d gathered in LDS
+      ++n_seq;
+      if (tq == 0) {
+        sD[c0] = d[0];
+        sD[c0 + 1] = d[1];
+      }
+      wait_loads();
+      lds_barrier();
+      if (w == 0) {
+        float dv[2] = {sD[2 * l], sD[2 * l + 1]};
+        const uint64_t stay = clamp ? wk.stay[seq * N + n] : 0;
+        for (int u = 0; u < L; ++u) {
+          float k[2], sq[2];
+          lds_get<TIn, 2>(R + u * RP + 2 * l, k);
+          sq[0] = k[0] * k[0];
+          sq[1] = k[1] * k[1];
+          const float align = wave_sum(fmaf(dv[0], sq[0], dv[1] * sq[1]));
+          const float c = fmaf(-lane_bcast(eb, u), align, lane_bcast(ea, u));
+          const float rb = lane_bcast(rt, u);
+          cst = l == u ? c : cst;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            float xx = fmaf(c, sq[e], rb * dv[e]);
+            if (clamp) xx = fminf(fmaxf(xx, dmin), dmax);
+            dv[e] = xx;
+          }
+          if (clamp && u + 1 < L) {
+            // tokens u + 1 .. L - 1 all keep d on d_min?
+            const uint64_t rest = (L - u - 1 >= 64 ? ~0ull : ((1ull << (L - u - 1)) - 1)) << (u + 1);
+            if ((stay & rest) == rest && __all(dv[0] == dmin && dv[1] == dmin)) {
+              u_end = u + 1;
+              break;
+            }
+          }
+        }
+        sD[2 * l] = dv[0];
+        sD[2 * l + 1] = dv[1];
+      }
+      lds_barrier();
+      d[0] = sD[c0];
+      d[1] = sD[c0 + 1];
+      if (l == 0) sF[w] = wave_flags();
+      lds_barrier();
+      gflags = sF[0] | sF[1] | sF[2] | sF[3];
+      lds_barrier();  // sD, sF are rewritten by the next chunk
+    }
+    if (w == 0) {
+      pend_c = cst;
+      pend_gi = tok && l < u_end ? gi : -1;
+    }
+    have = pf;
+    ahave = ahave_next;
+  }
+  if (w == 0 && pend_gi >= 0) wk.cstep[pend_gi] = pend_c;
+  if (a.d_out) {
+    if (tq == 0) {
+      a.d_out[seq * RP + c0] = d[0];
+      a.d_out[seq * RP + c0 + 1] = d[1];
+    }
+  }
+  if (w == 0 && l == 0) {
+    wk.flags[3 * seq + 0] = n_pinned;
+    wk.flags[3 * seq + 1] = n_active;
+    wk.flags[3 * seq + 2] = n_seq;
+  }
+}
+
 // ---------------------------------------------------------------- emit
 template <typename T, int EPL>
 __device__ __forceinline__ typename RowVec<T, EPL>::type pack_row(const float (&x)[EPL]) {
@@ -1082,14 +1467,24 @@ hipError_t launch_all(const ScanArgs &a, const ScanWork &w, hipStream_t s, bool 
       prof_mark(s, "scan_factor_kernel");
     }
   }
-  // register prefetch of the next chunk's rows where they do not come by direct copies
-  constexpr bool PF = !RV && !solve_rows_dma<TIn, EPL, FULL, RV>() && Row<TIn, EPL, FULL>::WORDS <= 2;
-  constexpr size_t shm = solve_lds_bytes<TIn, EPL, FULL, RV>();
-  static_assert(shm <= 160 * 1024, "solve kernel LDS");
-  auto kern = scan_solve_kernel<TIn, EPL, FULL, HAS_R, PF, VL, RV>;
-  hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)nseq), dim3(64), shm, s, a, w, N);
+  if constexpr (!RV && EPL == 2 && FULL) {
+    // K = 128: four waves per (b,h)
+    constexpr size_t shm = solve4_lds_bytes<TIn>();
+    static_assert(shm <= 160 * 1024, "solve kernel LDS");
+    auto kern = scan_solve4_kernel<TIn, HAS_R, VL>;
+    hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nseq), dim3(256), shm, s, a, w, N);
+  } else {
+    // register prefetch of the next chunk's rows where they do not come by direct copies
+    constexpr bool PF = !RV && !solve_rows_dma<TIn, EPL, FULL, RV>() && Row<TIn, EPL, FULL>::WORDS <= 2;
+    constexpr size_t shm = solve_lds_bytes<TIn, EPL, FULL, RV>();
+    static_assert(shm <= 160 * 1024, "solve kernel LDS");
+    auto kern = scan_solve_kernel<TIn, EPL, FULL, HAS_R, PF, VL, RV>;
+    hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nseq), dim3(64), shm, s, a, w, N);
+  }
   prof_mark(s, "scan_solve_kernel");
   if (N > 0 && emit) launch_emit<TIn, EPL, FULL, HAS_R, VL, RV>(a, w, N, s);
   return hipGetLastError();
