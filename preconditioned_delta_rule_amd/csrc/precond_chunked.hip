@@ -1157,13 +1157,8 @@ __global__ __launch_bounds__(256) void scan_solve4_kernel(ScanArgs a, ScanWork w
       wait_loads();
       lds_barrier();
     }
-    if (w == 0 && pend_gi >= 0) wk.cstep[pend_gi] = pend_c;
-    pend_gi = -1;
-    if (tq == 0) {
-      wk.dstart[(seq * N + n) * RP + c0] = d[0];
-      wk.dstart[(seq * N + n) * RP + c0 + 1] = d[1];
-    }
-    // per-token scalars (every wave, lane = token)
+    // per-token scalars (every wave, lane = token), used before any new
+    // global access is issued so that waiting for them waits for nothing else
     float bt, rt, nrm;
     if (have) {
       bt = nbt;
@@ -1178,6 +1173,28 @@ __global__ __launch_bounds__(256) void scan_solve4_kernel(ScanArgs a, ScanWork w
       bt = 0.0f;
       rt = 1.0f;
       nrm = 1.0f;
+    }
+    const float bpr = aware ? bt : 1.0f;
+    const float ea = eta * bpr / fmaxf(nrm, eps);  // c_t = ea - eb <d, s_t>
+    const float eb = ea * bpr;
+    float Rn = 1.0f, Rt = 1.0f;
+    if constexpr (HAS_R) {
+      const float lr = logf(rt);
+      float lin = lr;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(lin, off, 64);
+        if (l >= off) lin += y;
+      }
+      Rn = __expf(lin);
+      Rt = __expf(lin - lr);
+    }
+    asm volatile("" ::"v"(ea), "v"(eb), "v"(Rn), "v"(Rt), "v"(rt) : "memory");
+    if (w == 0 && pend_gi >= 0) wk.cstep[pend_gi] = pend_c;
+    pend_gi = -1;
+    if (tq == 0) {
+      wk.dstart[(seq * N + n) * RP + c0] = d[0];
+      wk.dstart[(seq * N + n) * RP + c0 + 1] = d[1];
     }
     // the next chunk's copies and scalars, unless the prep pass marked it
     const bool next_marked = ((n + 1) & 63) != 0 && ((pinmask >> ((n + 1) & 63)) & 1) != 0;
@@ -1195,21 +1212,6 @@ __global__ __launch_bounds__(256) void scan_solve4_kernel(ScanArgs a, ScanWork w
       nbt = a.beta[gi1];
       nrt = HAS_R ? a.r[gi1] : 1.0f;
       nnrm = wk.norm[gi1];
-    }
-    const float bpr = aware ? bt : 1.0f;
-    const float ea = eta * bpr / fmaxf(nrm, eps);  // c_t = ea - eb <d, s_t>
-    const float eb = ea * bpr;
-    float Rn = 1.0f, Rt = 1.0f;
-    if constexpr (HAS_R) {
-      const float lr = logf(rt);
-      float lin = lr;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(lin, off, 64);
-        if (l >= off) lin += y;
-      }
-      Rn = __expf(lin);
-      Rt = __expf(lin - lr);
     }
     const TIn *R = sRb + (n & 1) * (CH * RP);
 
@@ -1236,15 +1238,15 @@ __global__ __launch_bounds__(256) void scan_solve4_kernel(ScanArgs a, ScanWork w
       sYw[l] = y;
       wave_lds_sync();
       const float *Ai = sA + (n & 1) * (CH * CH);
-      float x = y;
+      float xa[4] = {y, 0.0f, 0.0f, 0.0f};  // four independent chains
 #pragma unroll
       for (int q = 0; q < CH / 4; ++q) {
         const floatx4 av = *reinterpret_cast<const floatx4 *>(Ai + (q * 64 + l) * 4);
         const floatx4 yv = *reinterpret_cast<const floatx4 *>(sYw + 4 * q);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x = fmaf(av[i], yv[i], x);
+        for (int i = 0; i < 4; ++i) xa[i] = fmaf(av[i], yv[i], xa[i]);
       }
-      x = tok ? x : 0.0f;
+      const float x = tok ? (xa[0] + xa[1]) + (xa[2] + xa[3]) : 0.0f;
       sXw[l] = x;
       wave_lds_sync();
       // d_L = R_L (d_0 + sum_t x_t s_t) and the bound sum_t |x_t| s_t on this pair
