@@ -86,6 +86,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # where each kernel's source lives (for matching committed counter summaries)
 KERNEL_SOURCE = {
     "scan_prep_kernel": "preconditioned_delta_rule_amd/csrc/precond_chunked.hip",
+    "scan_factor_kernel": "preconditioned_delta_rule_amd/csrc/precond_chunked.hip",
     "scan_solve_kernel": "preconditioned_delta_rule_amd/csrc/precond_chunked.hip",
     "scan_emit_kernel": "preconditioned_delta_rule_amd/csrc/precond_chunked.hip",
     "chunk_tinv_kernel": "preconditioned_delta_rule_amd/csrc/chunk_wy.hip",
@@ -159,6 +160,10 @@ def traffic_file(workload):
     return os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
 
 
+def mfma_file(workload):
+    return os.path.join(ROOT, "profiles", "mfma_%s.json" % workload)
+
+
 def load_traffic(workload, kernel):
     """Measured HBM bytes per launch of `kernel` from the committed counter
     summary, or None when there is none or the kernel source has changed."""
@@ -184,6 +189,7 @@ def pmc_summary(fetch_dir, write_dir, workload, command):
                     if row.get("Counter_Name") != counter:
                         continue
                     name = row["Kernel_Name"].replace("scan_prep128_kernel", "scan_prep_kernel")
+                    name = name.replace("scan_solve4_kernel", "scan_solve_kernel")
                     name = name.replace("kda_seq_hilo_kernel", "kda_seq_kernel")
                     name = name.replace("kda_intra128_kernel", "kda_intra_kernel")
                     key = None
@@ -220,6 +226,48 @@ def pmc_summary(fetch_dir, write_dir, workload, command):
            "command": command, "kernels": kernels}
     os.makedirs(os.path.dirname(traffic_file(workload)), exist_ok=True)
     with open(traffic_file(workload), "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(out, indent=1, sort_keys=True))
+    return 0
+
+
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA",
+                 "SQ_INSTS_VALU_MFMA_BF16", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE")
+SIMD_NUM = 1024  # 256 CUs x 4 SIMDs
+
+
+def mfma_summary(pmc_dir, workload, command):
+    """Matrix-core counters of one rocprofv3 --pmc run of `bench.py
+    --pmc-pass` (MFMA_COUNTERS, one pass) into profiles/mfma_<workload>.json:
+    per kernel, the median per dispatch of each counter, the bf16 MFMA flops
+    (MOPS x 512), and MFMA busy cycles over GRBM_GUI_ACTIVE x SIMDs (the share
+    of the dispatch's wall time the average SIMD's matrix core was busy)."""
+    vals = {}
+    for path in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                name = row["Kernel_Name"].replace("scan_prep128_kernel", "scan_prep_kernel").replace(
+                    "scan_solve4_kernel", "scan_solve_kernel")
+                key = None
+                for k in KERNEL_SOURCE:
+                    if k in name:
+                        key = k
+                if key and row.get("Counter_Name") in MFMA_COUNTERS:
+                    vals.setdefault(key, {}).setdefault(row["Counter_Name"], []).append(
+                        float(row["Counter_Value"]))
+    kernels = {}
+    for k, cs in vals.items():
+        med = {c: float(np.median(v)) for c, v in cs.items()}
+        ent = {"counters_median_per_dispatch": med, "dispatches": max(len(v) for v in cs.values()),
+               "source": KERNEL_SOURCE[k], "source_sha256": source_sha(KERNEL_SOURCE[k])}
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in med:
+            ent["bf16_mfma_flops"] = med["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in med and med.get("GRBM_GUI_ACTIVE"):
+            ent["mfma_busy_frac"] = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (med["GRBM_GUI_ACTIVE"] * SIMD_NUM)
+        kernels[k] = ent
+    out = {"workload": workload, "command": command, "simd_num": SIMD_NUM, "kernels": kernels}
+    with open(mfma_file(workload), "w") as f:
         json.dump(out, f, indent=1, sort_keys=True)
         f.write("\n")
     print(json.dumps(out, indent=1, sort_keys=True))
@@ -277,6 +325,9 @@ def main(argv=None):
                          "prints nothing" % (COPY_BYTES >> 20))
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs")
+    ap.add_argument("--mfma-summary", metavar="PMC_DIR",
+                    help="write profiles/mfma_<workload>.json from one rocprofv3 --pmc run of the "
+                         "matrix-core counters")
     ap.add_argument("--pmc-command", default="",
                     help="the commands that produced the --pmc-summary runs (recorded)")
     args = ap.parse_args(argv)
@@ -285,8 +336,11 @@ def main(argv=None):
                          "varlen_1p3b_65k" if args.varlen else
                          "kda_340m_apf" if args.kda else "1p3b_apf")
 
+    tag = args.workload + ("_unfused" if args.unfused else "")
     if args.pmc_summary:
-        return pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.workload, args.pmc_command)
+        return pmc_summary(args.pmc_summary[0], args.pmc_summary[1], tag, args.pmc_command)
+    if args.mfma_summary:
+        return mfma_summary(args.mfma_summary, tag, args.pmc_command)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the OSDN forward shards over (b,h) with no "
@@ -421,7 +475,7 @@ def main(argv=None):
         log("  %-20s %.4f ms  %.0f GB/s" % (name, ms, gbs or 0))
     dom = max(kernels, key=lambda n: kernels[n]["ms"] * kernels[n]["launches_per_step"])
     dk = kernels[dom]
-    tr = load_traffic(args.workload, dom)
+    tr = load_traffic(tag, dom)
     traffic = tr["bytes_per_launch"] / (dk["ms"] * 1e-3) / 1e9 if tr else None
     roofline = {"bound": "hbm", "kernel": dom, "achieved": dk["GB/s"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": dk["hbm_frac"], "traffic": traffic,
