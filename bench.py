@@ -235,14 +235,16 @@ def pmc_summary(fetch_dir, write_dir, workload, command):
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA",
                  "SQ_INSTS_VALU_MFMA_BF16", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE")
 SIMD_NUM = 1024  # 256 CUs x 4 SIMDs
+XCD_NUM = 8      # rocprofv3 reports GRBM_GUI_ACTIVE summed over the eight XCDs
 
 
 def mfma_summary(pmc_dir, workload, command):
     """Matrix-core counters of one rocprofv3 --pmc run of `bench.py
     --pmc-pass` (MFMA_COUNTERS, one pass) into profiles/mfma_<workload>.json:
     per kernel, the median per dispatch of each counter, the bf16 MFMA flops
-    (MOPS x 512), and MFMA busy cycles over GRBM_GUI_ACTIVE x SIMDs (the share
-    of the dispatch's wall time the average SIMD's matrix core was busy)."""
+    (MOPS x 512), and MFMA busy cycles over (GRBM_GUI_ACTIVE / XCDs) x SIMDs
+    (the share of the dispatch's wall time the average SIMD's matrix core was
+    busy; the GRBM count as reported is the sum of the eight XCDs' own)."""
     vals = {}
     for path in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
         with open(path) as f:
@@ -264,9 +266,11 @@ def mfma_summary(pmc_dir, workload, command):
         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in med:
             ent["bf16_mfma_flops"] = med["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
         if "SQ_VALU_MFMA_BUSY_CYCLES" in med and med.get("GRBM_GUI_ACTIVE"):
-            ent["mfma_busy_frac"] = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (med["GRBM_GUI_ACTIVE"] * SIMD_NUM)
+            ent["gui_active_cycles_per_xcd"] = med["GRBM_GUI_ACTIVE"] / XCD_NUM
+            ent["mfma_busy_frac"] = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (med["GRBM_GUI_ACTIVE"] / XCD_NUM * SIMD_NUM)
         kernels[k] = ent
-    out = {"workload": workload, "command": command, "simd_num": SIMD_NUM, "kernels": kernels}
+    out = {"workload": workload, "command": command, "simd_num": SIMD_NUM, "xcd_num": XCD_NUM,
+           "kernels": kernels}
     with open(mfma_file(workload), "w") as f:
         json.dump(out, f, indent=1, sort_keys=True)
         f.write("\n")
