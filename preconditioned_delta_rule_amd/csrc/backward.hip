@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256) void bwd_record_kernel(BwdArgs a) {
 // One workgroup per (b,h) and slice of 32 value columns, the state held
 // transposed: lane (key row j, l8) holds S[c0 + 4 l8 + c][j], c < 4, and the
 // same slots of G.
-template <typename TIn>
+template <typename TIn, bool OF32>
 __global__ __launch_bounds__(1024) void bwd_p2_kernel(BwdArgs a) {
   __shared__ float sQ[BT][BP], sK[BT][BP], sKt[BT][BP], sDo[BT][VS], sU[BT][VS];
   __shared__ float sDq[BT][BP], sDkt[BT][BP], sDkr[BT][BP], sDv[BT][VS];
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(1024) void bwd_p2_kernel(BwdArgs a) {
     }
     for (int e = tid; e < nb * VS; e += nt) {
       const int t = e / VS, il = e - t * VS;
-      if (il < ncol) store_out<TIn>(a.dv, (tok0 + (t0 + t) * H) * V + c0 + il, sDv[t][il], a.o_f32);
+      if (il < ncol) store_out_t<TIn, OF32>(a.dv, (tok0 + (t0 + t) * H) * V + c0 + il, sDv[t][il]);
     }
     if (tid < nb) {
       const int64_t x = (int64_t)q * tok + tok0 + (t0 + tid) * H;
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(1024) void bwd_p2_kernel(BwdArgs a) {
 // keys; dk~ and the read-key part, each summed over the value slices; dq,
 // summed, scaled and stored) and wave 9 its gates (and dalpha, summed and
 // stored), into the other half of a double buffer.
-template <typename TIn>
+template <typename TIn, bool OF32>
 __global__ __launch_bounds__(640) void bwd_p1_kernel(BwdArgs a) {
   __shared__ float sK[2][BT][BP], sDkt[2][BT][BP], sDkr[2][BT][BP];
   __shared__ float sB[2][BT], sR[2][BT], sDb[2][BT];
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(640) void bwd_p1_kernel(BwdArgs a) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
           const int e = gt + 128 * u, t = e >> 7, j = e & 127;
-          if (j < K && t < nb) store_out<TIn>(a.dq, (tok0 + (t0 + t) * H) * K + j, a.q_scale * x[u], a.o_f32);
+          if (j < K && t < nb) store_out_t<TIn, OF32>(a.dq, (tok0 + (t0 + t) * H) * K + j, a.q_scale * x[u]);
         }
       } else {
         float(*dst)[BP] = grp == 0 ? sK[buf] : (grp == 1 ? sDkt[buf] : sDkr[buf]);
@@ -593,7 +593,7 @@ __global__ __launch_bounds__(640) void bwd_p1_kernel(BwdArgs a) {
           const float ds = fmaf(c, gy[e], gc * fmaf(dca, dv[e], dcn));
           if (j < K) {
             const float dk = sDkr[buf][t][lane + 64 * e] + fmaf(2.0f * k[e], ds, dkt[e] * dv[e]);
-            store_out<TIn>(a.dk, tr * K + j, dk, a.o_f32);
+            store_out_t<TIn, OF32>(a.dk, tr * K + j, dk);
           }
           g[e] = j < K ? fmaf(dkt[e], k[e], fmaf(rt, gy[e], dca * s[e] * gc)) : 0.0f;
         }
@@ -630,9 +630,17 @@ hipError_t launch_typed(const BwdArgs &a, hipStream_t s) {
     default: hipLaunchKernelGGL((bwd_record_kernel<TIn, 4>), gsplit, dim3(256), 0, s, a); break;
   }
   prof_mark(s, "bwd_record_kernel");
-  hipLaunchKernelGGL((bwd_p2_kernel<TIn>), gsplit, bp2, 0, s, a);
+  // float32 gradients for bf16 inputs: a variant of each reverse kernel
+  const bool f32 = a.o_f32 && sizeof(TIn) == 2;
+  if (f32)
+    hipLaunchKernelGGL((bwd_p2_kernel<TIn, true>), gsplit, bp2, 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_p2_kernel<TIn, false>), gsplit, bp2, 0, s, a);
   prof_mark(s, "bwd_p2_kernel");
-  hipLaunchKernelGGL((bwd_p1_kernel<TIn>), grid, dim3(640), 0, s, a);
+  if (f32)
+    hipLaunchKernelGGL((bwd_p1_kernel<TIn, true>), grid, dim3(640), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_p1_kernel<TIn, false>), grid, dim3(640), 0, s, a);
   prof_mark(s, "bwd_p1_kernel");
   return hipGetLastError();
 }

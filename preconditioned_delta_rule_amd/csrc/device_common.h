@@ -30,6 +30,13 @@ __device__ __forceinline__ void store_out(void *o, int64_t i, float x, int o_f32
   if (o_f32) static_cast<float *>(o)[i] = x;
   else static_cast<T *>(o)[i] = from_f32<T>(x);
 }
+// The same with the choice made at compile time (kernels that store inside a
+// sequential loop take it as a template argument: no branch in the loop).
+template <typename T, bool F32>
+__device__ __forceinline__ void store_out_t(void *o, int64_t i, float x) {
+  if constexpr (F32) static_cast<float *>(o)[i] = x;
+  else static_cast<T *>(o)[i] = from_f32<T>(x);
+}
 
 // Sum over the 64 lanes of a wave; every lane receives the total.
 // Rows of 16 lanes are reduced with DPP butterflies (xor 1, xor 2, half-row

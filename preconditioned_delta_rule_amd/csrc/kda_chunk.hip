@@ -653,6 +653,7 @@ __device__ __forceinline__ bf16x8 neg8(bf16x8 x) {
 // transposed (value column major) so that a lane's 8 contraction indices are
 // contiguous; pitches of 4 (mod 64) floats keep a quarter-wave's 16-byte
 // accesses on distinct banks.
+template <bool OF32>
 __global__ __launch_bounds__(256) void kda_seq_hilo_kernel(KdaArgs a, int64_t N, int ntile) {
   // the tiles are kept as hi/lo bf16 pairs, split once by their writer; row
   // pitches of 8 (mod 128) bf16 keep a quarter-wave's 16-byte reads on
@@ -830,7 +831,7 @@ __global__ __launch_bounds__(256) void kda_seq_hilo_kernel(KdaArgs a, int64_t N,
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * w + 4 * g + i;
         const int64_t col = v0 + 16 * cb + l16;
-        if (row < L && col < V) store_out<bf16>(a.o, ((b * T + t0 + row) * H + h) * V + col, accP[cb][i], a.o_f32);
+        if (row < L && col < V) store_out_t<bf16, OF32>(a.o, ((b * T + t0 + row) * H + h) * V + col, accP[cb][i]);
       }
     // (d) S = Diag(gamma_C) S + Kc^T D for this wave's key rows
 #pragma unroll
@@ -1204,7 +1205,11 @@ hipError_t launch_typed(const KdaArgs &a, hipStream_t s, const EmitArgs *em) {
   dim3 grid((unsigned)(a.B * a.H * ntile)), block(256);
   if constexpr (sizeof(TIn) == 2) {
     // bf16 inputs: hi/lo pairs on the bf16 matrix cores
-    hipLaunchKernelGGL(kda_seq_hilo_kernel, grid, block, 0, s, a, N, ntile);
+    // float32 readout for bf16 inputs: a variant (no branch at the stores)
+    if (a.o_f32)
+      hipLaunchKernelGGL(kda_seq_hilo_kernel<true>, grid, block, 0, s, a, N, ntile);
+    else
+      hipLaunchKernelGGL(kda_seq_hilo_kernel<false>, grid, block, 0, s, a, N, ntile);
   } else {
     hipLaunchKernelGGL((kda_seq_kernel<TIn, NCB>), grid, block, 0, s, a, N, ntile);
   }

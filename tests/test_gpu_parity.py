@@ -233,7 +233,7 @@ def test_fwd_tiny_workload():
     assert rel_err(to_np(S), ref["S"]) <= F32_OS
 
 
-FULL = ["340m", "1p3b_apf", "recall", "long_apf", "long_apf_gdn"]
+FULL = ["340m", "1p3b_apf", "1p3b", "1p3b_clamp", "recall", "long_apf", "long_apf_gdn"]
 
 
 @pytest.mark.parametrize("name", FULL)

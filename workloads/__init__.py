@@ -47,6 +47,11 @@ WORKLOADS = {
                      seed=2, apf=True),
     # the same layer without the APF retention
     "1p3b": dict(B=4, T=4096, H=16, K=128, V=128, dtype="bf16", chunk=64, seed=2),
+    # the same layer with a tighter box and a larger step, so that the clamp
+    # binds intermittently (some coordinate on a bound in about one chunk in
+    # seven, more towards the end as d approaches d_max)
+    "1p3b_clamp": dict(B=4, T=4096, H=16, K=128, V=128, dtype="bf16", chunk=64, seed=2,
+                       eta=0.05, d_min=0.8, d_max=1.25),
     "recall": dict(B=8, T=2048, H=8, K=128, V=128, dtype="bf16", chunk=64,
                    seed=3, keys="recall", beta_mu=1.0),
     "long_apf": dict(B=1, T=20480, H=16, K=128, V=128, dtype="bf16", chunk=64,
