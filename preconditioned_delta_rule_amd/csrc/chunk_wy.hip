@@ -488,23 +488,13 @@ __device__ __forceinline__ bf16x8 lda_tr_tile_order(const bf16 *X, int kt, int s
   return cat8(ld4_tr(X + sx128(r, col)), ld4_tr(X + sx128(r + 16, col)));
 }
 
-// One 16-byte (or 4-byte) global -> LDS copy per lane (global_load_lds):
-// lane i of the wave writes bytes [16 i, 16 i + 16) ([4 i, 4 i + 4)) after
-// `lds`, which must be the same for every lane.
-__device__ __forceinline__ void dma16(const void *src, void *lds) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void *src, void *lds) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 4, 0, 0);
-}
 // Workgroup barrier that does not wait for this wave's outstanding global
-// loads (the copies into the other LDS buffer stay in flight across it); LDS
-// writes before it are complete.
+// loads (the next chunk's inputs stay in flight across it); LDS writes
+// before it are complete.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // LDS of one chunk's inputs (the sweep keeps two: the current chunk and the
-// next one, which arrives by global_load_lds while the current one is used).
+// next one, which the helper waves write while the current one is used).
 struct SwBuf {
   static constexpr int Q = 0;               // bf16 [64][128] queries (sx128)
   static constexpr int K = Q + C * KD * 2;  // bf16 [64][128] keys (sx128)
@@ -541,6 +531,9 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
   // the chain waves' S operands [chain][s hi, s lo ...][lane] and Delta operands [chain][slot][lane]
   __shared__ bf16x8 sdump[2][8][64];
   __shared__ bf16x8 ddump[2][4][64];
+  // each helper wave's output tile (32 token rows x 32 value columns, fp32),
+  // staged so that a lane stores whole 16-byte pieces of one row
+  __shared__ __attribute__((aligned(16))) float ostage[2][32][36];
 
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -764,30 +757,60 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       voff[jj] = (uint32_t)(r * rowb) + vcol[jj];
     }
     const uint32_t soff = (uint32_t)(l * H * 4);
-    // the loads of chunk n into buffer lb (rows past T read the chunk's first
-    // row; beta past T is zeroed after arrival); skip_w: a chunk whose write
-    // keys are d_min k (its residual is neither written nor read)
-    auto issue = [&](int64_t n, unsigned char *lb, bool skip_w) {
-      const int64_t t0 = n * C;
-      const int Lc = chunk_len(n);
-      const char *q0 = qb + t0 * rowb, *k0 = kb + t0 * rowb, *e0 = eb + t0 * rowb, *v0p = vb + t0 * rowb;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int j = 2 * jj + hw;
-        const uint32_t off = rrow[jj] < Lc ? roff[jj] : rcol[jj];
-        dma16(q0 + off, lb + L::Q + 1024 * j);
-        dma16(k0 + off, lb + L::K + 1024 * j);
-        if (!skip_w) dma16(e0 + off, lb + L::W + 1024 * j);
-      }
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int j = 2 * jj + hw;
-        dma16(v0p + (vrow[jj] < Lc ? voff[jj] : vcol[jj]), lb + L::V + 1024 * j);
-      }
-      const uint32_t so = l < Lc ? soff : 0u;
-      if (hw == 0) dma4(bb + t0 * H * 4 + so, lb + L::BETA);
-      else if (GATED) dma4(ab + t0 * H * 4 + so, lb + L::G);
-    };
+    // The next chunk's inputs travel through registers: loaded at the start
+    // of a chunk (16 bytes a lane per 1 KB block), written to the other LDS
+    // buffer at its end, a whole chunk later.  (Direct global -> LDS copies
+    // took about 130 cycles each to issue here, on the helper's critical
+    // path.)  Rows past T read the chunk's first row; beta past T is zeroed
+    // after arrival; skip_w: a chunk whose write keys are d_min k (its
+    // residual is neither written nor read).
+    // issue: chunk n's pieces into registers (held as wide vector values, not
+    // arrays, so that they never go through private memory); put: into
+    // buffer lb (the residual only when the chunk reads it)
+    typedef unsigned u32x32 __attribute__((ext_vector_type(32)));
+    typedef unsigned u32x8 __attribute__((ext_vector_type(8)));
+#define SW_ISSUE(n_, skip_w_)                                                                          \
+  do {                                                                                                 \
+    const int64_t t0_ = (n_) * C;                                                                      \
+    const int Lc_ = chunk_len(n_);                                                                     \
+    const char *q0_ = qb + t0_ * rowb, *k0_ = kb + t0_ * rowb;                                        \
+    const char *e0_ = (skip_w_) ? k0_ : eb + t0_ * rowb; /* a skipped residual reads k again (hits) */ \
+    const char *v0_ = vb + t0_ * rowb;                                                                 \
+    _Pragma("unroll") for (int jj = 0; jj < 8; ++jj) {                                                 \
+      const uint32_t off = rrow[jj] < Lc_ ? roff[jj] : rcol[jj];                                       \
+      const uint4 a_ = *reinterpret_cast<const uint4 *>(q0_ + off);                                   \
+      const uint4 b_ = *reinterpret_cast<const uint4 *>(k0_ + off);                                   \
+      pq[4 * jj] = a_.x; pq[4 * jj + 1] = a_.y; pq[4 * jj + 2] = a_.z; pq[4 * jj + 3] = a_.w;         \
+      pk[4 * jj] = b_.x; pk[4 * jj + 1] = b_.y; pk[4 * jj + 2] = b_.z; pk[4 * jj + 3] = b_.w;         \
+      const uint4 c_ = *reinterpret_cast<const uint4 *>(e0_ + off);                                   \
+      pw[4 * jj] = c_.x; pw[4 * jj + 1] = c_.y; pw[4 * jj + 2] = c_.z; pw[4 * jj + 3] = c_.w;         \
+    }                                                                                                  \
+    _Pragma("unroll") for (int jj = 0; jj < 2; ++jj) {                                                 \
+      const uint4 d_ = *reinterpret_cast<const uint4 *>(v0_ + (vrow[jj] < Lc_ ? voff[jj] : vcol[jj])); \
+      pv[4 * jj] = d_.x; pv[4 * jj + 1] = d_.y; pv[4 * jj + 2] = d_.z; pv[4 * jj + 3] = d_.w;         \
+    }                                                                                                  \
+    const uint32_t so_ = l < Lc_ ? soff : 0u;                                                          \
+    if (hw == 0) ps = *reinterpret_cast<const float *>(bb + t0_ * H * 4 + so_);                       \
+    else if (GATED) ps = *reinterpret_cast<const float *>(ab + t0_ * H * 4 + so_);                    \
+  } while (0)
+#define SW_PUT(lb_, skip_w_)                                                                           \
+  do {                                                                                                 \
+    _Pragma("unroll") for (int jj = 0; jj < 8; ++jj) {                                                 \
+      const int j = 2 * jj + hw;                                                                       \
+      *reinterpret_cast<uint4 *>((lb_) + L::Q + 1024 * j + 16 * l) =                                  \
+          uint4{pq[4 * jj], pq[4 * jj + 1], pq[4 * jj + 2], pq[4 * jj + 3]};                           \
+      *reinterpret_cast<uint4 *>((lb_) + L::K + 1024 * j + 16 * l) =                                  \
+          uint4{pk[4 * jj], pk[4 * jj + 1], pk[4 * jj + 2], pk[4 * jj + 3]};                           \
+      if (!(skip_w_))                                                                                  \
+        *reinterpret_cast<uint4 *>((lb_) + L::W + 1024 * j + 16 * l) =                                \
+            uint4{pw[4 * jj], pw[4 * jj + 1], pw[4 * jj + 2], pw[4 * jj + 3]};                         \
+    }                                                                                                  \
+    _Pragma("unroll") for (int jj = 0; jj < 2; ++jj)                                                   \
+        *reinterpret_cast<uint4 *>((lb_) + L::V + 1024 * (2 * jj + hw) + 16 * l) =                    \
+            uint4{pv[4 * jj], pv[4 * jj + 1], pv[4 * jj + 2], pv[4 * jj + 3]};                         \
+    if (hw == 0) reinterpret_cast<float *>((lb_) + L::BETA)[l] = ps;                                  \
+    else if (GATED) reinterpret_cast<float *>((lb_) + L::G)[l] = ps;                                  \
+  } while (0)
     // after the loads of chunk n have landed: beta past T to zero, alpha to the
     // cumulative log decay (log 1 = 0 past T, so g stays at g_{Lc-1})
     auto finish = [&](int64_t n, unsigned char *lb) {
@@ -809,8 +832,12 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
     int pin1 = load_pin(1);  // marks of chunks n + 1 and n + 2
     int pin2 = load_pin(2);
     if (Nb > 0) {
-      issue(0, lb0, __builtin_amdgcn_readfirstlane(load_pin(0)) == 2);
-      wait_loads();
+      const bool p0 = __builtin_amdgcn_readfirstlane(load_pin(0)) == 2;
+      u32x32 pq = {}, pk = {}, pw = {};
+      u32x8 pv = {};
+      float ps = 0.0f;
+      SW_ISSUE(0, p0);
+      SW_PUT(lb0, p0);
       finish(0, lb0);
     }
     lds_barrier();
@@ -821,11 +848,10 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       const int64_t t0 = n * C;
       const int Lc = chunk_len(n);
       const bool more = n + 1 < Nb;
-      if (more) issue(n + 1, nxt, __builtin_amdgcn_readfirstlane(pin1) == 2);
-      pin1 = pin2;
-      pin2 = load_pin(n + 3);
       // this chunk's scores (formed chunk-parallel with Tm): token-row tiles
-      // mta = hw (slab 0) and mtb = 3 - hw (slabs 0, 1), hi/lo operands
+      // mta = hw (slab 0) and mtb = 3 - hw (slabs 0, 1), hi/lo operands;
+      // requested before the next chunk's inputs, so that waiting for them
+      // leaves those in flight
       const bf16 *md = tseq + n * CHUNKW + TDUMP;
       const int js[3] = {hw, 4 - 2 * hw, 5 - 2 * hw};
       bf16x8 Mh[3], Ml[3];
@@ -834,6 +860,16 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
         Mh[u] = ld8(md + ((2 * js[u]) * 64 + l) * 8);
         Ml[u] = ld8(md + ((2 * js[u] + 1) * 64 + l) * 8);
       }
+      const bool skip_next = __builtin_amdgcn_readfirstlane(pin1) == 2;
+      u32x32 pq = {}, pk = {}, pw = {};
+      u32x8 pv = {};
+      float ps = 0.0f;
+      // every load is issued on every path (the last chunk reads itself again
+      // and writes nothing), so that the wait for the scores above counts
+      // exactly the loads issued after them
+      SW_ISSUE(more ? n + 1 : n, skip_next || !more);
+      pin1 = pin2;
+      pin2 = load_pin(n + 3);
       // e^g Q S_n^T for both token-row tiles and both value tiles (S_n as the
       // chain waves left it)
       const int mts[2] = {hw, 3 - hw};
@@ -876,19 +912,49 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
         O[1][c] = mfma32(Mh[2], d1l, O[1][c]);
         O[1][c] = mfma32(Ml[2], d1h, O[1][c]);
       }
+      // O through LDS: lane (l16, g) holds rows 4 g + i of each tile; after the
+      // exchange lane l holds row l / 2 (tile l / 32), value columns 16 (l % 2) ..,
+      // stored as 16-byte pieces (scattered 2-byte stores cost ~100 cycles each)
+      float(*os)[36] = ostage[hw];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = 16 * mts[u] + 4 * g + i;
-            if (m < Lc)
-              store_out<bf16>(a.o, base + v0 + (t0 + m) * tstride + 16 * c + l16, a.q_scale * O[u][c][i],
-                              a.o_f32);
+          for (int i = 0; i < 4; ++i) os[16 * u + 4 * g + i][16 * c + l16] = a.q_scale * O[u][c][i];
+      // (a wave's own LDS accesses execute in order: only the compiler is held)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
+      asm volatile("" ::: "memory");
+      {
+        const int r = l >> 1, hc = 16 * (l & 1);
+        const int m = 16 * mts[r >> 4] + (r & 15);
+        floatx4 x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const floatx4 *>(&os[r][hc + 4 * j]);
+        if (m < Lc) {
+          const int64_t oi = base + v0 + (t0 + m) * tstride + hc;
+          if (a.o_f32) {
+            float *op = static_cast<float *>(a.o) + oi;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) *reinterpret_cast<floatx4 *>(op + 4 * j) = x[j];
+          } else {
+            bf16x8 y0, y1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              y0[e] = to_bf16(x[0][e]);
+              y0[4 + e] = to_bf16(x[1][e]);
+              y1[e] = to_bf16(x[2][e]);
+              y1[4 + e] = to_bf16(x[3][e]);
+            }
+            bf16 *op = static_cast<bf16 *>(a.o) + oi;
+            *reinterpret_cast<bf16x8 *>(op) = y0;
+            *reinterpret_cast<bf16x8 *>(op + 8) = y1;
           }
+        }
+      }
       if (more) {
-        wait_loads();
+        SW_PUT(nxt, skip_next);
         finish(n + 1, nxt);
       }
       lds_barrier();  // ---- B1 of the next chunk
@@ -897,6 +963,8 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       body(n, lb0, lb1);
       if (n + 1 < Nb) body(n + 1, lb1, lb0);
     }
+#undef SW_ISSUE
+#undef SW_PUT
   }
 }
 
