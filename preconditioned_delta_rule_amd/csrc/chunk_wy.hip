@@ -502,7 +502,8 @@ struct SwBuf {
   static constexpr int V = W + C * KD * 2;  // bf16 [64][32] value tile
   static constexpr int BETA = V + C * 32 * 2;  // f32 [64], zero past the chunk end
   static constexpr int G = BETA + C * 4;       // f32 [64] cumulative log decay
-  static constexpr int BYTES = G + C * 4;
+  static constexpr int TM = G + C * 4;         // bf16x8 [6][64] (I + A)^-1 operands (TDUMP order)
+  static constexpr int BYTES = TM + 6 * 64 * 16;
 };
 
 // Phase 2 sweep over the chunks of one (b,h) and 32 value rows.  Four waves:
@@ -568,7 +569,7 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
     // Bh / Bl: S as hi / lo operands over the key index in tile order
     floatx4 ST[8];
     bf16x8 Bh[4], Bl[4];
-    bf16x8 Tm[6];  // this chunk's (I + A)^-1 operands
+    bf16x8 Tm[6];  // this chunk's (I + A)^-1 operands (from LDS: the helpers copy them)
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt)
       ST[kt] = a.S0 ? *reinterpret_cast<const floatx4 *>(a.S0 + (seq * VD + vc + l16) * KD + 16 * kt + 4 * g)
@@ -579,10 +580,6 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       sdump[hw][2 * s][l] = Bh[s];
       sdump[hw][2 * s + 1][l] = Bl[s];
     }
-    if (Nb > 0) {
-#pragma unroll
-      for (int j = 0; j < 6; ++j) Tm[j] = ld8(tseq + (j * 64 + l) * 8);
-    }
     int pin_next = load_pin(0);
     lds_barrier();
 
@@ -592,6 +589,8 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       const bf16 *sV = reinterpret_cast<const bf16 *>(cur + L::V);
       const float *sBeta = reinterpret_cast<const float *>(cur + L::BETA);
       const float *sG = reinterpret_cast<const float *>(cur + L::G);
+#pragma unroll
+      for (int j = 0; j < 6; ++j) Tm[j] = *reinterpret_cast<const bf16x8 *>(cur + L::TM + (j * 64 + l) * 16);
       const bool pinned = __builtin_amdgcn_readfirstlane(pin_next) == 2;
       pin_next = load_pin(n + 1);
       const bool more = n + 1 < Nb;
@@ -640,12 +639,6 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       D[3] = mfma32(Tm[5], Rh[1], D[3]);
       D[2] = mfma32(Tm[3], Rl[1], D[2]);
       D[3] = mfma32(Tm[5], Rl[1], D[3]);
-      // the next chunk's (I + A)^-1 operands (Tm is free now)
-      if (more) {
-        const bf16 *tp = tseq + (n + 1) * CHUNKW;
-#pragma unroll
-        for (int j = 0; j < 6; ++j) Tm[j] = ld8(tp + (j * 64 + l) * 8);
-      }
       // Delta for the outputs (helper waves), as tile-order hi/lo operands
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -769,6 +762,7 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
     // buffer lb (the residual only when the chunk reads it)
     typedef unsigned u32x32 __attribute__((ext_vector_type(32)));
     typedef unsigned u32x8 __attribute__((ext_vector_type(8)));
+    typedef unsigned u32x12 __attribute__((ext_vector_type(12)));
 #define SW_ISSUE(n_, skip_w_)                                                                          \
   do {                                                                                                 \
     const int64_t t0_ = (n_) * C;                                                                      \
@@ -789,6 +783,10 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       const uint4 d_ = *reinterpret_cast<const uint4 *>(v0_ + (vrow[jj] < Lc_ ? voff[jj] : vcol[jj])); \
       pv[4 * jj] = d_.x; pv[4 * jj + 1] = d_.y; pv[4 * jj + 2] = d_.z; pv[4 * jj + 3] = d_.w;         \
     }                                                                                                  \
+    _Pragma("unroll") for (int jj = 0; jj < 3; ++jj) {                                                 \
+      const uint4 t_ = *reinterpret_cast<const uint4 *>(tseq + (n_) * CHUNKW + ((2 * jj + hw) * 64 + l) * 8); \
+      pt[4 * jj] = t_.x; pt[4 * jj + 1] = t_.y; pt[4 * jj + 2] = t_.z; pt[4 * jj + 3] = t_.w;         \
+    }                                                                                                  \
     const uint32_t so_ = l < Lc_ ? soff : 0u;                                                          \
     if (hw == 0) ps = *reinterpret_cast<const float *>(bb + t0_ * H * 4 + so_);                       \
     else if (GATED) ps = *reinterpret_cast<const float *>(ab + t0_ * H * 4 + so_);                    \
@@ -808,6 +806,9 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
     _Pragma("unroll") for (int jj = 0; jj < 2; ++jj)                                                   \
         *reinterpret_cast<uint4 *>((lb_) + L::V + 1024 * (2 * jj + hw) + 16 * l) =                    \
             uint4{pv[4 * jj], pv[4 * jj + 1], pv[4 * jj + 2], pv[4 * jj + 3]};                         \
+    _Pragma("unroll") for (int jj = 0; jj < 3; ++jj)                                                   \
+        *reinterpret_cast<uint4 *>((lb_) + L::TM + ((2 * jj + hw) * 64 + l) * 16) =                   \
+            uint4{pt[4 * jj], pt[4 * jj + 1], pt[4 * jj + 2], pt[4 * jj + 3]};                         \
     if (hw == 0) reinterpret_cast<float *>((lb_) + L::BETA)[l] = ps;                                  \
     else if (GATED) reinterpret_cast<float *>((lb_) + L::G)[l] = ps;                                  \
   } while (0)
@@ -835,6 +836,7 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       const bool p0 = __builtin_amdgcn_readfirstlane(load_pin(0)) == 2;
       u32x32 pq = {}, pk = {}, pw = {};
       u32x8 pv = {};
+      u32x12 pt = {};
       float ps = 0.0f;
       SW_ISSUE(0, p0);
       SW_PUT(lb0, p0);
@@ -863,6 +865,7 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       const bool skip_next = __builtin_amdgcn_readfirstlane(pin1) == 2;
       u32x32 pq = {}, pk = {}, pw = {};
       u32x8 pv = {};
+      u32x12 pt = {};
       float ps = 0.0f;
       // every load is issued on every path (the last chunk reads itself again
       // and writes nothing), so that the wait for the scores above counts
