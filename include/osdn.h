@@ -33,9 +33,11 @@
  *    and S_out are float32.
  *  - Pointers are DEVICE pointers owned by the caller; the library allocates
  *    no memory and keeps no state between calls beyond the calling thread's
- *    last error message and its open launch profile (osdn_profile_begin /
+ *    last error message, its open launch profile (osdn_profile_begin /
  *    osdn_profile_end, whose HIP events live from the first launch recorded
- *    to osdn_profile_end).  stream is a hipStream_t (NULL
+ *    to osdn_profile_end), and, for osdn_fwd_noalloc only, its scratch array
+ *    (a device array of the library, one copy per GPU) with that copy's
+ *    address, looked up once per device.  stream is a hipStream_t (NULL
  *    = the default stream); work is enqueued asynchronously and outputs are
  *    valid once the stream has been synchronised.
  *  - Arguments are validated before anything is launched; on failure nothing

@@ -53,7 +53,7 @@ __device__ __forceinline__ floatx4 lds4(const float *p) { return *reinterpret_ca
 // then beta, r, alpha [TB].  At most 64 VGPRs, so two 1024-lane workgroups
 // share a CU and one's state loads overlap the other's updates and stores.
 // VEC (K % 4 == 0): state rows move as 16-byte vectors, else element-wise.
-template <typename TIn, int KM, bool VEC>
+template <typename TIn, int KM, bool VEC, bool OF32>
 __global__ __launch_bounds__(1024, 8) void decode_kernel(DecodeArgs a) {
   extern __shared__ floatx4 dec_smem[];
   const int TB = a.tb;
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(1024, 8) void decode_kernel(DecodeArgs a) {
     __syncthreads();
     for (int e = tid; e < nb * (int)V; e += nt) {
       const int t = e / (int)V, i = e - t * (int)V;
-      store_out<TIn>(a.o, (tok0 + (t0 + t) * H) * V + i, sO[t][i], a.o_f32);
+      store_out_t<TIn, OF32>(a.o, (tok0 + (t0 + t) * H) * V + i, sO[t][i]);
     }
     // the next block's staging touches sK, sQ, sV, sB, sR, sA only, whose last
     // readers finished before the barrier above; sKt and sO are rewritten
@@ -243,17 +243,17 @@ __global__ __launch_bounds__(1024, 8) void decode_kernel(DecodeArgs a) {
   }
 }
 
-template <typename TIn, bool VEC>
+template <typename TIn, bool VEC, bool OF32>
 hipError_t launch_vec(DecodeArgs a, hipStream_t s) {
   const dim3 grid((unsigned)(a.B * a.H));
   const dim3 block((unsigned)(((8 * a.V + 63) / 64) * 64));
   a.tb = (int)(a.T < DEC_TB ? (a.T > 0 ? a.T : 1) : DEC_TB);
   const size_t lds = (size_t)a.tb * (5 * DEC_P + 3) * sizeof(float);
   switch ((a.K + 31) / 32) {
-    case 1: hipLaunchKernelGGL((decode_kernel<TIn, 1, VEC>), grid, block, lds, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<TIn, 2, VEC>), grid, block, lds, s, a); break;
-    case 3: hipLaunchKernelGGL((decode_kernel<TIn, 3, VEC>), grid, block, lds, s, a); break;
-    default: hipLaunchKernelGGL((decode_kernel<TIn, 4, VEC>), grid, block, lds, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<TIn, 1, VEC, OF32>), grid, block, lds, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<TIn, 2, VEC, OF32>), grid, block, lds, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_kernel<TIn, 3, VEC, OF32>), grid, block, lds, s, a); break;
+    default: hipLaunchKernelGGL((decode_kernel<TIn, 4, VEC, OF32>), grid, block, lds, s, a); break;
   }
   prof_mark(s, "decode_kernel");
   return hipGetLastError();
@@ -261,7 +261,10 @@ hipError_t launch_vec(DecodeArgs a, hipStream_t s) {
 
 template <typename TIn>
 hipError_t launch_typed(const DecodeArgs &a, hipStream_t s) {
-  return a.K % 4 == 0 ? launch_vec<TIn, true>(a, s) : launch_vec<TIn, false>(a, s);
+  // float32 readout for bf16 inputs: a variant (no branch at the stores)
+  if (a.o_f32 && sizeof(TIn) == 2)
+    return a.K % 4 == 0 ? launch_vec<TIn, true, true>(a, s) : launch_vec<TIn, false, true>(a, s);
+  return a.K % 4 == 0 ? launch_vec<TIn, true, false>(a, s) : launch_vec<TIn, false, false>(a, s);
 }
 
 }  // namespace
