@@ -9,24 +9,24 @@
 // with B = diag(beta) and in-chunk log decay g_i = sum_{l<=i} log alpha_l
 // (g = 0 without decay):
 //
-//  chunk_tinv_kernel (one workgroup per chunk, all chunks at once):
+//  chunk_tinv_kernel (chunk-parallel, persistent workgroups):
 //    A  = strict_lower(B [e^{g_i-g_j}] . K K~^T)
-//    Tm = (I + A)^-1, written to the workspace in bf16 (row-major 64 x 64)
+//    Tm = (I + A)^-1 and the scores M = lower([e^{g_i-g_j}] . Q K~^T), written
+//         to the workspace in bf16 (M as hi/lo pairs) in the sweep's operand order
 //
-//  chunk_seq_kernel (one workgroup per (b,h) and 32 value rows, chunks in
+//  chunk_sweep_kernel (one workgroup per (b,h) and 32 value rows, chunks in
 //  order; S is the boundary state, V x K, fp32):
 //    R     = B (V - diag(e^g) K S^T)
 //    Delta = Tm R                                     (= U - W S^T of Eq.(11))
-//    O     = q_scale (diag(e^g) Q S^T + lower([e^{g_i-g_j}] . Q K~^T) Delta)
+//    O     = q_scale (diag(e^g) Q S^T + M Delta)
 //    S    <- e^{g_L} S + Delta^T (e^{g_L - g} . K~)
 //
-// Tm depends only on the chunk's keys, so the sweep carries no triangular
-// solve: its per-chunk work is five small products, split over 8 waves (wave
-// (rw, cw) owns token rows [16 rw, 16 rw + 16) and value columns
-// [16 cw, 16 cw + 16) of the chunk), with four barriers per chunk.  Each
-// input row is loaded once per workgroup and staged in LDS; the key rows
-// serve both as row operands and, through transposed LDS reads, as the
-// token-major operand of the state update.
+// Tm and M depend only on the chunk's keys and queries, so the sweep carries
+// no triangular solve: two of its waves run the state-dependent chain (K S^T,
+// R, Tm R, the state update), two bring in the next chunk and form the
+// outputs, with two barriers per chunk.  The key rows serve both as row
+// operands and, through transposed LDS reads, as the token-major operand of
+// the state update.
 //
 // Precision: intermediates that are not bf16 (S, R, Delta, the scores) enter
 // every product as a hi + lo pair of bf16; the write key in its residual form
