@@ -59,7 +59,11 @@ constexpr int TDUMP = 6 * 64 * 8;  // bf16 elements per chunk
 // (block 2 j + 0 / 2 j + 1), lane (l16, g) holding score row 16 mt + l16 at
 // key positions 32 s + 4 g + {0..3} and 32 s + 16 + 4 g + {0..3}.
 constexpr int MDUMP = 12 * 64 * 8;
-constexpr int CHUNKW = TDUMP + MDUMP;  // workspace per chunk: Tm operands, then the scores
+// Then the chunk's scalars as fp32: beta (zero past the chunk end) and the
+// cumulative log decay (constant past the chunk end; gated form only), so that
+// the sweep reads them as two 256-byte pieces rather than 64 strided words.
+constexpr int SDUMP = 2 * 64 * 2;  // in bf16 elements
+constexpr int CHUNKW = TDUMP + MDUMP + SDUMP;  // workspace per chunk
 
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -446,6 +450,9 @@ __global__ __launch_bounds__(256, 3) void chunk_tinv_kernel(ChunkArgs a, bf16 *t
     const int row = 16 * mt + (ln & 15), c0 = 32 * sb + 4 * (ln >> 4);
     *reinterpret_cast<bf16x8 *>(dst + e * 8) = cat8(ld4(&sTr[row][c0]), ld4(&sTr[row][c0 + 16]));
   }
+  // beta and the cumulative log decay, as the sweep reads them
+  if (tid < C) reinterpret_cast<float *>(dst + TDUMP + MDUMP)[tid] = sBeta[tid];
+  else if (GATED && tid < 2 * C) reinterpret_cast<float *>(dst + TDUMP + MDUMP)[tid] = sG[tid - C];
   __syncthreads();  // the next chunk's rows overwrite Tm's buffers
   }
 }
@@ -532,9 +539,6 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
   // the chain waves' S operands [chain][s hi, s lo ...][lane] and Delta operands [chain][slot][lane]
   __shared__ bf16x8 sdump[2][8][64];
   __shared__ bf16x8 ddump[2][4][64];
-  // each helper wave's output tile (32 token rows x 32 value columns, fp32),
-  // staged so that a lane stores whole 16-byte pieces of one row
-  __shared__ __attribute__((aligned(16))) float ostage[2][32][36];
 
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -640,27 +644,28 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       D[2] = mfma32(Tm[3], Rl[1], D[2]);
       D[3] = mfma32(Tm[5], Rl[1], D[3]);
       // Delta for the outputs (helper waves), as tile-order hi/lo operands
+      bf16x8 Dh[2], Dl[2];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        bf16x8 dh, dl;
-        split8(D[2 * s], D[2 * s + 1], dh, dl);
-        ddump[hw][2 * s][l] = dh;
-        ddump[hw][2 * s + 1][l] = dl;
+        split8(D[2 * s], D[2 * s + 1], Dh[s], Dl[s]);
+        ddump[hw][2 * s][l] = Dh[s];
+        ddump[hw][2 * s + 1][l] = Dl[s];
       }
       // the state update's Delta: decayed to the chunk end, and scaled by
-      // d_min when the write keys are d_min k
-      const float dscale = pinned ? a.d_min : 1.0f;
+      // d_min when the write keys are d_min k (otherwise the same operands)
+      if (GATED || pinned) {
+        const float dscale = pinned ? a.d_min : 1.0f;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float f = dscale;
-          if (GATED) f *= __expf(gL - sG[16 * mt + 4 * g + i]);
-          D[mt][i] *= f;
-        }
-      bf16x8 Dh[2], Dl[2];
-      split8(D[0], D[1], Dh[0], Dl[0]);
-      split8(D[2], D[3], Dh[1], Dl[1]);
+          for (int i = 0; i < 4; ++i) {
+            float f = dscale;
+            if (GATED) f *= __expf(gL - sG[16 * mt + 4 * g + i]);
+            D[mt][i] *= f;
+          }
+        split8(D[0], D[1], Dh[0], Dl[0]);
+        split8(D[2], D[3], Dh[1], Dl[1]);
+      }
       lds_barrier();  // ---- B2: Delta is in LDS, the helpers are done with S_n
       // S <- e^{g_L} S + K~^T Delta
       if (GATED) {
@@ -727,8 +732,6 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
     const char *kb = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.k) + base);
     const char *eb = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.kt) + base);
     const char *vb = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.v) + base + v0);
-    const char *bb = reinterpret_cast<const char *>(a.beta + tb * H + h);
-    const char *ab = GATED ? reinterpret_cast<const char *>(a.alpha + tb * H + h) : nullptr;
     // per-lane byte offsets of the copies (within a chunk), fixed for the sweep:
     //  128-wide rows: block j = 2 jj + hw (rows 4 j ..), lane l -> row 4 j + l / 16,
     //  16-byte position l % 16 holding chunk (l % 16) ^ (row % 16) (sx128);
@@ -749,14 +752,14 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       vcol[jj] = (uint32_t)(16 * (l & 3));
       voff[jj] = (uint32_t)(r * rowb) + vcol[jj];
     }
-    const uint32_t soff = (uint32_t)(l * H * 4);
     // The next chunk's inputs travel through registers: loaded at the start
     // of a chunk (16 bytes a lane per 1 KB block), written to the other LDS
     // buffer at its end, a whole chunk later.  (Direct global -> LDS copies
     // took about 130 cycles each to issue here, on the helper's critical
-    // path.)  Rows past T read the chunk's first row; beta past T is zeroed
-    // after arrival; skip_w: a chunk whose write keys are d_min k (its
-    // residual is neither written nor read).
+    // path.)  Rows past T read the chunk's first row (their beta, as the UT
+    // transform writes it, is zero, and so is their log decay); skip_w: a
+    // chunk whose write keys are d_min k (its residual is neither written nor
+    // read).
     // issue: chunk n's pieces into registers (held as wide vector values, not
     // arrays, so that they never go through private memory); put: into
     // buffer lb (the residual only when the chunk reads it)
@@ -787,9 +790,9 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       const uint4 t_ = *reinterpret_cast<const uint4 *>(tseq + (n_) * CHUNKW + ((2 * jj + hw) * 64 + l) * 8); \
       pt[4 * jj] = t_.x; pt[4 * jj + 1] = t_.y; pt[4 * jj + 2] = t_.z; pt[4 * jj + 3] = t_.w;         \
     }                                                                                                  \
-    const uint32_t so_ = l < Lc_ ? soff : 0u;                                                          \
-    if (hw == 0) ps = *reinterpret_cast<const float *>(bb + t0_ * H * 4 + so_);                       \
-    else if (GATED) ps = *reinterpret_cast<const float *>(ab + t0_ * H * 4 + so_);                    \
+    const float *sc_ = reinterpret_cast<const float *>(tseq + (n_) * CHUNKW + TDUMP + MDUMP);       \
+    if (hw == 0) ps = sc_[l];                                                                          \
+    else if (GATED) ps = sc_[64 + l];                                                                  \
   } while (0)
 #define SW_PUT(lb_, skip_w_)                                                                           \
   do {                                                                                                 \
@@ -812,24 +815,6 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
     if (hw == 0) reinterpret_cast<float *>((lb_) + L::BETA)[l] = ps;                                  \
     else if (GATED) reinterpret_cast<float *>((lb_) + L::G)[l] = ps;                                  \
   } while (0)
-    // after the loads of chunk n have landed: beta past T to zero, alpha to the
-    // cumulative log decay (log 1 = 0 past T, so g stays at g_{Lc-1})
-    auto finish = [&](int64_t n, unsigned char *lb) {
-      const int Lc = chunk_len(n);
-      if (hw == 0) {
-        if (l >= Lc) reinterpret_cast<float *>(lb + L::BETA)[l] = 0.0f;
-      } else if (GATED) {
-        float *gp = reinterpret_cast<float *>(lb + L::G);
-        float x = l < Lc ? logf(gp[l]) : 0.0f;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const float y = __shfl_up(x, off, 64);
-          if (l >= off) x += y;
-        }
-        gp[l] = x;
-      }
-    };
-
     int pin1 = load_pin(1);  // marks of chunks n + 1 and n + 2
     int pin2 = load_pin(2);
     if (Nb > 0) {
@@ -840,11 +825,14 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       float ps = 0.0f;
       SW_ISSUE(0, p0);
       SW_PUT(lb0, p0);
-      finish(0, lb0);
     }
     lds_barrier();
 
-    auto body = [&](int64_t n, const unsigned char *cur, unsigned char *nxt) {
+    // SKIP: the next chunk's write keys are d_min k (its residual is neither
+    // loaded nor written); a compile-time choice, so that every wait below
+    // counts exactly the loads of its own path
+    auto body = [&](auto SKIP, int64_t n, const unsigned char *cur, unsigned char *nxt) {
+      constexpr bool skip_next = decltype(SKIP)::value;
       const bf16 *sQ = reinterpret_cast<const bf16 *>(cur + L::Q);
       const float *sG = reinterpret_cast<const float *>(cur + L::G);
       const int64_t t0 = n * C;
@@ -862,19 +850,21 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
         Mh[u] = ld8(md + ((2 * js[u]) * 64 + l) * 8);
         Ml[u] = ld8(md + ((2 * js[u] + 1) * 64 + l) * 8);
       }
-      const bool skip_next = __builtin_amdgcn_readfirstlane(pin1) == 2;
       u32x32 pq = {}, pk = {}, pw = {};
       u32x8 pv = {};
       u32x12 pt = {};
       float ps = 0.0f;
-      // every load is issued on every path (the last chunk reads itself again
-      // and writes nothing), so that the wait for the scores above counts
-      // exactly the loads issued after them
-      SW_ISSUE(more ? n + 1 : n, skip_next || !more);
+      // the last chunk reads itself again and writes nothing, so that the
+      // wait for the scores above counts exactly the loads issued after them
+      SW_ISSUE(more ? n + 1 : n, skip_next);
       pin1 = pin2;
       pin2 = load_pin(n + 3);
-      // e^g Q S_n^T for both token-row tiles and both value tiles (S_n as the
-      // chain waves left it)
+      // The outputs are formed transposed, O^T = e^g S_n Q^T + Delta^T M^T
+      // (value rows x token columns): an operand register of a 16x16x32
+      // product holds X[i][kappa] for lane (i, g) whether it serves as the A
+      // operand of X or the B operand of X^T, so the same registers serve with
+      // the operands swapped, and each lane ends up with four consecutive
+      // values of one token, stored as one piece.
       const int mts[2] = {hw, 3 - hw};
       floatx4 O[2][2];
 #pragma unroll
@@ -883,88 +873,67 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
         bf16x8 aq[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) aq[s] = lda_tile_order(sQ, 16 * mt + l16, s, g);
+        const float eg = GATED ? __expf(sG[16 * mt + l16]) : 1.0f;  // token column l16
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            acc = mfma32(aq[s], sdump[c][2 * s][l], acc);
-            acc = mfma32(aq[s], sdump[c][2 * s + 1][l], acc);
+            acc = mfma32(sdump[c][2 * s][l], aq[s], acc);
+            acc = mfma32(sdump[c][2 * s + 1][l], aq[s], acc);
           }
-          if (GATED) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] *= __expf(sG[16 * mt + 4 * g + i]);
-          }
+          if (GATED) acc = acc * eg;
           O[u][c] = acc;
         }
       }
       lds_barrier();  // ---- B2: Delta is in LDS; the chain waves may rewrite S
-      // O = q_scale (e^g Q S_n^T + scores Delta)
+      // O^T += Delta^T M^T (tile mta: slab 0; tile mtb: slabs 0 and 1)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        // tile mta: slab 0; tile mtb: slabs 0 and 1
         const bf16x8 d0h = ddump[c][0][l], d0l = ddump[c][1][l];
         const bf16x8 d1h = ddump[c][2][l], d1l = ddump[c][3][l];
-        O[0][c] = mfma32(Mh[0], d0h, O[0][c]);
-        O[1][c] = mfma32(Mh[1], d0h, O[1][c]);
-        O[0][c] = mfma32(Mh[0], d0l, O[0][c]);
-        O[1][c] = mfma32(Mh[1], d0l, O[1][c]);
-        O[0][c] = mfma32(Ml[0], d0h, O[0][c]);
-        O[1][c] = mfma32(Ml[1], d0h, O[1][c]);
-        O[1][c] = mfma32(Mh[2], d1h, O[1][c]);
-        O[1][c] = mfma32(Mh[2], d1l, O[1][c]);
-        O[1][c] = mfma32(Ml[2], d1h, O[1][c]);
+        O[0][c] = mfma32(d0h, Mh[0], O[0][c]);
+        O[1][c] = mfma32(d0h, Mh[1], O[1][c]);
+        O[0][c] = mfma32(d0l, Mh[0], O[0][c]);
+        O[1][c] = mfma32(d0l, Mh[1], O[1][c]);
+        O[0][c] = mfma32(d0h, Ml[0], O[0][c]);
+        O[1][c] = mfma32(d0h, Ml[1], O[1][c]);
+        O[1][c] = mfma32(d1h, Mh[2], O[1][c]);
+        O[1][c] = mfma32(d1l, Mh[2], O[1][c]);
+        O[1][c] = mfma32(d1h, Ml[2], O[1][c]);
       }
-      // O through LDS: lane (l16, g) holds rows 4 g + i of each tile; after the
-      // exchange lane l holds row l / 2 (tile l / 32), value columns 16 (l % 2) ..,
-      // stored as 16-byte pieces (scattered 2-byte stores cost ~100 cycles each)
-      float(*os)[36] = ostage[hw];
+      // lane (l16, g): token 16 mt + l16, value columns 16 c + 4 g .. + 3
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) os[16 * u + 4 * g + i][16 * c + l16] = a.q_scale * O[u][c][i];
-      // (a wave's own LDS accesses execute in order: only the compiler is held)
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_wave_barrier();
-      asm volatile("" ::: "memory");
-      {
-        const int r = l >> 1, hc = 16 * (l & 1);
-        const int m = 16 * mts[r >> 4] + (r & 15);
-        floatx4 x[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = *reinterpret_cast<const floatx4 *>(&os[r][hc + 4 * j]);
+      for (int u = 0; u < 2; ++u) {
+        const int m = 16 * mts[u] + l16;
         if (m < Lc) {
-          const int64_t oi = base + v0 + (t0 + m) * tstride + hc;
-          if (a.o_f32) {
-            float *op = static_cast<float *>(a.o) + oi;
+          const int64_t oi = base + v0 + (t0 + m) * tstride + 4 * g;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) *reinterpret_cast<floatx4 *>(op + 4 * j) = x[j];
-          } else {
-            bf16x8 y0, y1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              y0[e] = to_bf16(x[0][e]);
-              y0[4 + e] = to_bf16(x[1][e]);
-              y1[e] = to_bf16(x[2][e]);
-              y1[4 + e] = to_bf16(x[3][e]);
-            }
-            bf16 *op = static_cast<bf16 *>(a.o) + oi;
-            *reinterpret_cast<bf16x8 *>(op) = y0;
-            *reinterpret_cast<bf16x8 *>(op + 8) = y1;
+          for (int c = 0; c < 2; ++c) {
+            const floatx4 x = O[u][c] * a.q_scale;
+            if (a.o_f32)
+              *reinterpret_cast<floatx4 *>(static_cast<float *>(a.o) + oi + 16 * c) = x;
+            else
+              *reinterpret_cast<bf16x4 *>(static_cast<bf16 *>(a.o) + oi + 16 * c) = pack4(x);
           }
         }
       }
       if (more) {
         SW_PUT(nxt, skip_next);
-        finish(n + 1, nxt);
       }
       lds_barrier();  // ---- B1 of the next chunk
     };
     for (int64_t n = 0; n < Nb; n += 2) {
-      body(n, lb0, lb1);
-      if (n + 1 < Nb) body(n + 1, lb1, lb0);
+      if (__builtin_amdgcn_readfirstlane(pin1) == 2)
+        body(IConst<1>{}, n, lb0, lb1);
+      else
+        body(IConst<0>{}, n, lb0, lb1);
+      if (n + 1 < Nb) {
+        if (__builtin_amdgcn_readfirstlane(pin1) == 2)
+          body(IConst<1>{}, n + 1, lb1, lb0);
+        else
+          body(IConst<0>{}, n + 1, lb1, lb0);
+      }
     }
 #undef SW_ISSUE
 #undef SW_PUT
