@@ -501,7 +501,7 @@ __device__ __forceinline__ bf16x8 lda_tr_tile_order(const bf16 *X, int kt, int s
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // LDS of one chunk's inputs (the sweep keeps two: the current chunk and the
-// next one, which the helper waves write while the current one is used).
+// next one, which the loader waves fill while the current one is used).
 struct SwBuf {
   static constexpr int Q = 0;               // bf16 [64][128] queries (sx128)
   static constexpr int K = Q + C * KD * 2;  // bf16 [64][128] keys (sx128)
@@ -513,7 +513,8 @@ struct SwBuf {
   static constexpr int BYTES = TM + 6 * 64 * 16;
 };
 
-// Phase 2 sweep over the chunks of one (b,h) and 32 value rows.  Four waves:
+// Phase 2 sweep over the chunks of one (b,h) and 32 value rows.  Eight waves,
+// two to a SIMD:
 //  waves 0, 1 ("chain" waves) own value rows v0 + 16 w .. + 16 of the state
 //    with every key column, as 16 x 16 tiles of S^T in registers, and run the
 //    state-dependent chain of every chunk without waiting for any other wave:
@@ -522,16 +523,21 @@ struct SwBuf {
 //    (S as hi + lo bf16 operands taken straight from the result tiles in
 //    tile order; K~ = k + E as the two exact bf16 operands k and E, or d_min k
 //    on a chunk phase 1 took as pinned on d_min);
-//  waves 2, 3 ("helper" waves) issue the next chunk's loads and produce the
-//    outputs of two token-row tiles each,
-//      O = q_scale (diag(e^g) Q S^T + scores Delta),
-//    from S and Delta, which the chain waves leave in LDS as their operand
-//    registers, and the scores, formed chunk-parallel beside Tm.
-// Two barriers per chunk: after the chain waves have Delta (and the helpers
-// Q S^T), and at the end of the chunk (next chunk's inputs in place, the new
-// state written out).
+//  waves 2, 3 ("output" waves) produce the outputs of two token-row tiles
+//    each, transposed,
+//      O^T = q_scale (e^g S_n Q^T + Delta^T M^T),
+//    from S_n and Delta, which the chain waves leave in LDS as their operand
+//    registers, and the scores M, formed chunk-parallel beside Tm;
+//  waves 4 .. 7 ("loader" waves) bring the next chunk's rows, value tile,
+//    (I + A)^-1 operands and scalars into the other buffer.  A wave moves
+//    data from L2 at a limited rate of its own, so four waves share the
+//    chunk's rows.
+// Two barriers per chunk: after the chain waves have Delta (and the output
+// waves Q S^T), and at the end of the chunk (next chunk's inputs in place,
+// the new state written out).  A loader reaches the first one without
+// waiting for its loads.
 template <bool GATED, bool KRES, bool VL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
   typedef SwBuf L;
   __shared__ __attribute__((aligned(16))) unsigned char lb0[L::BYTES];
@@ -543,7 +549,7 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = l & 15, g = l >> 4;
-  const int hw = w & 1;  // chain index (value rows 16 hw ..) or helper index
+  const int hw = w & 1;  // chain index (value rows 16 hw ..) or output-wave index
   // XCD-aware placement: block i runs on XCD i % 8; the NT value tiles of one
   // sequence share i % 8, so their reads of the same rows meet in one L2.
   const int bid = blockIdx.x;
@@ -562,7 +568,7 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
   const int64_t base = tb * tstride + h * KD;
   const bf16 *tseq = tdump + seq * N * CHUNKW;
   const int *pins = KRES && a.pin ? a.pin + seq * N : nullptr;
-  // a chunk's mark from the chunked phase 1 (loaded a chunk or two ahead)
+  // a chunk's mark from the chunked phase 1 (loaded a chunk ahead)
   auto load_pin = [&](int64_t n) -> int { return pins && n < Nb ? pins[n] : 0; };
   auto chunk_len = [&](int64_t n) -> int { return (int)((T - n * C) < C ? (T - n * C) : C); };
 
@@ -573,7 +579,7 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
     // Bh / Bl: S as hi / lo operands over the key index in tile order
     floatx4 ST[8];
     bf16x8 Bh[4], Bl[4];
-    bf16x8 Tm[6];  // this chunk's (I + A)^-1 operands (from LDS: the helpers copy them)
+    bf16x8 Tm[6];  // this chunk's (I + A)^-1 operands (from LDS: the loader waves copy them)
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt)
       ST[kt] = a.S0 ? *reinterpret_cast<const floatx4 *>(a.S0 + (seq * VD + vc + l16) * KD + 16 * kt + 4 * g)
@@ -643,7 +649,7 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       D[3] = mfma32(Tm[5], Rh[1], D[3]);
       D[2] = mfma32(Tm[3], Rl[1], D[2]);
       D[3] = mfma32(Tm[5], Rl[1], D[3]);
-      // Delta for the outputs (helper waves), as tile-order hi/lo operands
+      // Delta for the outputs (output waves), as tile-order hi/lo operands
       bf16x8 Dh[2], Dl[2];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -666,7 +672,7 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
         split8(D[0], D[1], Dh[0], Dl[0]);
         split8(D[2], D[3], Dh[1], Dl[1]);
       }
-      lds_barrier();  // ---- B2: Delta is in LDS, the helpers are done with S_n
+      lds_barrier();  // ---- B2: Delta is in LDS, the output waves are done with S_n
       // S <- e^{g_L} S + K~^T Delta
       if (GATED) {
         const float decay = __expf(gL);
@@ -726,122 +732,18 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       for (int kt = 0; kt < 8; ++kt)
         *reinterpret_cast<floatx4 *>(a.S_out + (seq * VD + vc + l16) * KD + 16 * kt + 4 * g) = ST[kt];
     }
-  } else {
-    // ================================================================ helper waves
-    const char *qb = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.q) + base);
-    const char *kb = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.k) + base);
-    const char *eb = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.kt) + base);
-    const char *vb = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.v) + base + v0);
-    // per-lane byte offsets of the copies (within a chunk), fixed for the sweep:
-    //  128-wide rows: block j = 2 jj + hw (rows 4 j ..), lane l -> row 4 j + l / 16,
-    //  16-byte position l % 16 holding chunk (l % 16) ^ (row % 16) (sx128);
-    //  value tile: block j = 2 jj + hw (rows 16 j ..), lane l -> row 16 j + l / 4, chunk l % 4
-    uint32_t roff[8], rcol[8], voff[2], vcol[2];
-    int rrow[8], vrow[2];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int j = 2 * jj + hw, r = 4 * j + (l >> 4);
-      rrow[jj] = r;
-      rcol[jj] = (uint32_t)(16 * (((l & 15) ^ r) & 15));
-      roff[jj] = (uint32_t)(r * rowb) + rcol[jj];
-    }
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int j = 2 * jj + hw, r = 16 * j + (l >> 2);
-      vrow[jj] = r;
-      vcol[jj] = (uint32_t)(16 * (l & 3));
-      voff[jj] = (uint32_t)(r * rowb) + vcol[jj];
-    }
-    // The next chunk's inputs travel through registers: loaded at the start
-    // of a chunk (16 bytes a lane per 1 KB block), written to the other LDS
-    // buffer at its end, a whole chunk later.  (Direct global -> LDS copies
-    // took about 130 cycles each to issue here, on the helper's critical
-    // path.)  Rows past T read the chunk's first row (their beta, as the UT
-    // transform writes it, is zero, and so is their log decay); skip_w: a
-    // chunk whose write keys are d_min k (its residual is neither written nor
-    // read).
-    // issue: chunk n's pieces into registers (held as wide vector values, not
-    // arrays, so that they never go through private memory); put: into
-    // buffer lb (the residual only when the chunk reads it)
-    typedef unsigned u32x32 __attribute__((ext_vector_type(32)));
-    typedef unsigned u32x8 __attribute__((ext_vector_type(8)));
-    typedef unsigned u32x12 __attribute__((ext_vector_type(12)));
-#define SW_ISSUE(n_, skip_w_)                                                                          \
-  do {                                                                                                 \
-    const int64_t t0_ = (n_) * C;                                                                      \
-    const int Lc_ = chunk_len(n_);                                                                     \
-    const char *q0_ = qb + t0_ * rowb, *k0_ = kb + t0_ * rowb;                                        \
-    const char *e0_ = (skip_w_) ? k0_ : eb + t0_ * rowb; /* a skipped residual reads k again (hits) */ \
-    const char *v0_ = vb + t0_ * rowb;                                                                 \
-    _Pragma("unroll") for (int jj = 0; jj < 8; ++jj) {                                                 \
-      const uint32_t off = rrow[jj] < Lc_ ? roff[jj] : rcol[jj];                                       \
-      const uint4 a_ = *reinterpret_cast<const uint4 *>(q0_ + off);                                   \
-      const uint4 b_ = *reinterpret_cast<const uint4 *>(k0_ + off);                                   \
-      pq[4 * jj] = a_.x; pq[4 * jj + 1] = a_.y; pq[4 * jj + 2] = a_.z; pq[4 * jj + 3] = a_.w;         \
-      pk[4 * jj] = b_.x; pk[4 * jj + 1] = b_.y; pk[4 * jj + 2] = b_.z; pk[4 * jj + 3] = b_.w;         \
-      const uint4 c_ = *reinterpret_cast<const uint4 *>(e0_ + off);                                   \
-      pw[4 * jj] = c_.x; pw[4 * jj + 1] = c_.y; pw[4 * jj + 2] = c_.z; pw[4 * jj + 3] = c_.w;         \
-    }                                                                                                  \
-    _Pragma("unroll") for (int jj = 0; jj < 2; ++jj) {                                                 \
-      const uint4 d_ = *reinterpret_cast<const uint4 *>(v0_ + (vrow[jj] < Lc_ ? voff[jj] : vcol[jj])); \
-      pv[4 * jj] = d_.x; pv[4 * jj + 1] = d_.y; pv[4 * jj + 2] = d_.z; pv[4 * jj + 3] = d_.w;         \
-    }                                                                                                  \
-    _Pragma("unroll") for (int jj = 0; jj < 3; ++jj) {                                                 \
-      const uint4 t_ = *reinterpret_cast<const uint4 *>(tseq + (n_) * CHUNKW + ((2 * jj + hw) * 64 + l) * 8); \
-      pt[4 * jj] = t_.x; pt[4 * jj + 1] = t_.y; pt[4 * jj + 2] = t_.z; pt[4 * jj + 3] = t_.w;         \
-    }                                                                                                  \
-    const float *sc_ = reinterpret_cast<const float *>(tseq + (n_) * CHUNKW + TDUMP + MDUMP);       \
-    if (hw == 0) ps = sc_[l];                                                                          \
-    else if (GATED) ps = sc_[64 + l];                                                                  \
-  } while (0)
-#define SW_PUT(lb_, skip_w_)                                                                           \
-  do {                                                                                                 \
-    _Pragma("unroll") for (int jj = 0; jj < 8; ++jj) {                                                 \
-      const int j = 2 * jj + hw;                                                                       \
-      *reinterpret_cast<uint4 *>((lb_) + L::Q + 1024 * j + 16 * l) =                                  \
-          uint4{pq[4 * jj], pq[4 * jj + 1], pq[4 * jj + 2], pq[4 * jj + 3]};                           \
-      *reinterpret_cast<uint4 *>((lb_) + L::K + 1024 * j + 16 * l) =                                  \
-          uint4{pk[4 * jj], pk[4 * jj + 1], pk[4 * jj + 2], pk[4 * jj + 3]};                           \
-      if (!(skip_w_))                                                                                  \
-        *reinterpret_cast<uint4 *>((lb_) + L::W + 1024 * j + 16 * l) =                                \
-            uint4{pw[4 * jj], pw[4 * jj + 1], pw[4 * jj + 2], pw[4 * jj + 3]};                         \
-    }                                                                                                  \
-    _Pragma("unroll") for (int jj = 0; jj < 2; ++jj)                                                   \
-        *reinterpret_cast<uint4 *>((lb_) + L::V + 1024 * (2 * jj + hw) + 16 * l) =                    \
-            uint4{pv[4 * jj], pv[4 * jj + 1], pv[4 * jj + 2], pv[4 * jj + 3]};                         \
-    _Pragma("unroll") for (int jj = 0; jj < 3; ++jj)                                                   \
-        *reinterpret_cast<uint4 *>((lb_) + L::TM + ((2 * jj + hw) * 64 + l) * 16) =                   \
-            uint4{pt[4 * jj], pt[4 * jj + 1], pt[4 * jj + 2], pt[4 * jj + 3]};                         \
-    if (hw == 0) reinterpret_cast<float *>((lb_) + L::BETA)[l] = ps;                                  \
-    else if (GATED) reinterpret_cast<float *>((lb_) + L::G)[l] = ps;                                  \
-  } while (0)
-    int pin1 = load_pin(1);  // marks of chunks n + 1 and n + 2
-    int pin2 = load_pin(2);
-    if (Nb > 0) {
-      const bool p0 = __builtin_amdgcn_readfirstlane(load_pin(0)) == 2;
-      u32x32 pq = {}, pk = {}, pw = {};
-      u32x8 pv = {};
-      u32x12 pt = {};
-      float ps = 0.0f;
-      SW_ISSUE(0, p0);
-      SW_PUT(lb0, p0);
-    }
+  } else if (w < 4) {
+    // ================================================================ output waves
     lds_barrier();
-
-    // SKIP: the next chunk's write keys are d_min k (its residual is neither
-    // loaded nor written); a compile-time choice, so that every wait below
-    // counts exactly the loads of its own path
-    auto body = [&](auto SKIP, int64_t n, const unsigned char *cur, unsigned char *nxt) {
-      constexpr bool skip_next = decltype(SKIP)::value;
+    auto body = [&](int64_t n, const unsigned char *cur) {
       const bf16 *sQ = reinterpret_cast<const bf16 *>(cur + L::Q);
       const float *sG = reinterpret_cast<const float *>(cur + L::G);
       const int64_t t0 = n * C;
       const int Lc = chunk_len(n);
-      const bool more = n + 1 < Nb;
-      // this chunk's scores (formed chunk-parallel with Tm): token-row tiles
-      // mta = hw (slab 0) and mtb = 3 - hw (slabs 0, 1), hi/lo operands;
-      // requested before the next chunk's inputs, so that waiting for them
-      // leaves those in flight
+      // this chunk's scores (formed chunk-parallel with Tm) for token-row tiles
+      // mts[0] = hw (slab 0) and mts[1] = 3 - hw (slabs 0, 1), hi/lo operands;
+      // needed only after the first barrier
+      const int mts[2] = {hw, 3 - hw};
       const bf16 *md = tseq + n * CHUNKW + TDUMP;
       const int js[3] = {hw, 4 - 2 * hw, 5 - 2 * hw};
       bf16x8 Mh[3], Ml[3];
@@ -850,30 +752,19 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
         Mh[u] = ld8(md + ((2 * js[u]) * 64 + l) * 8);
         Ml[u] = ld8(md + ((2 * js[u] + 1) * 64 + l) * 8);
       }
-      u32x32 pq = {}, pk = {}, pw = {};
-      u32x8 pv = {};
-      u32x12 pt = {};
-      float ps = 0.0f;
-      // the last chunk reads itself again and writes nothing, so that the
-      // wait for the scores above counts exactly the loads issued after them
-      SW_ISSUE(more ? n + 1 : n, skip_next);
-      pin1 = pin2;
-      pin2 = load_pin(n + 3);
-      // The outputs are formed transposed, O^T = e^g S_n Q^T + Delta^T M^T
-      // (value rows x token columns): an operand register of a 16x16x32
-      // product holds X[i][kappa] for lane (i, g) whether it serves as the A
-      // operand of X or the B operand of X^T, so the same registers serve with
-      // the operands swapped, and each lane ends up with four consecutive
-      // values of one token, stored as one piece.
-      const int mts[2] = {hw, 3 - hw};
+      // O^T = e^g S_n Q^T (value rows x token columns) for both token tiles and
+      // both value tiles (S_n as the chain waves left it): an operand register
+      // of a 16x16x32 product holds X[i][kappa] for lane (i, g) whether it
+      // serves as the A operand of X or the B operand of X^T, so the chain's
+      // S^T operands and the query operands serve with their roles swapped,
+      // and each lane ends up with four consecutive values of one token.
       floatx4 O[2][2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int mt = mts[u];
         bf16x8 aq[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) aq[s] = lda_tile_order(sQ, 16 * mt + l16, s, g);
-        const float eg = GATED ? __expf(sG[16 * mt + l16]) : 1.0f;  // token column l16
+        for (int s = 0; s < 4; ++s) aq[s] = lda_tile_order(sQ, 16 * mts[u] + l16, s, g);
+        const float eg = GATED ? __expf(sG[16 * mts[u] + l16]) : 1.0f;  // token column l16
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -887,7 +778,7 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
         }
       }
       lds_barrier();  // ---- B2: Delta is in LDS; the chain waves may rewrite S
-      // O^T += Delta^T M^T (tile mta: slab 0; tile mtb: slabs 0 and 1)
+      // O^T += Delta^T M^T (tile 0: slab 0; tile 1: slabs 0 and 1)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const bf16x8 d0h = ddump[c][0][l], d0l = ddump[c][1][l];
@@ -918,25 +809,99 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
           }
         }
       }
-      if (more) {
-        SW_PUT(nxt, skip_next);
-      }
       lds_barrier();  // ---- B1 of the next chunk
     };
     for (int64_t n = 0; n < Nb; n += 2) {
-      if (__builtin_amdgcn_readfirstlane(pin1) == 2)
-        body(IConst<1>{}, n, lb0, lb1);
-      else
-        body(IConst<0>{}, n, lb0, lb1);
-      if (n + 1 < Nb) {
-        if (__builtin_amdgcn_readfirstlane(pin1) == 2)
-          body(IConst<1>{}, n + 1, lb1, lb0);
-        else
-          body(IConst<0>{}, n + 1, lb1, lb0);
-      }
+      body(n, lb0);
+      if (n + 1 < Nb) body(n + 1, lb1);
     }
-#undef SW_ISSUE
-#undef SW_PUT
+  } else {
+    // ================================================================ loader waves
+    // Loader li brings, for a chunk: the 1 KB blocks j = 4 jj + li (jj < 4) of
+    // the query, key and write-key rows (block j: rows 4 j .., lane l -> row
+    // 4 j + l / 16, 16-byte piece l % 16 stored at position (l % 16) ^ (row %
+    // 16), the sx128 layout), block li of the value tile (rows 16 li + l / 4,
+    // piece l % 4), blocks li and li + 4 (< 6) of the (I + A)^-1 operands, and
+    // (li = 0) beta or (li = 1) the cumulative log decay, both as the UT
+    // transform writes them (zero past the chunk end, constant past it).
+    // Rows past T read the chunk's first row (their beta is zero).
+    const int li = w - 4;
+    const char *qb = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.q) + base);
+    const char *kb = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.k) + base);
+    const char *eb = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.kt) + base);
+    const char *vb = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.v) + base + v0);
+    const int r0 = 4 * li + (l >> 4);  // row of block jj = 0; block jj adds 16 jj
+    const uint32_t rcol = (uint32_t)(16 * (((l & 15) ^ r0) & 15));  // the same for every block
+    const int vrow = 16 * li + (l >> 2);
+    const uint32_t vcol = (uint32_t)(16 * (l & 3)), voff = (uint32_t)(vrow * rowb) + vcol;
+    // chunk n's pieces: loaded into registers, then (after the first barrier,
+    // which does not wait for them) written to buffer lb; a chunk whose write
+    // keys are d_min k (mark 2) has its residual neither loaded nor written
+    auto fill = [&](int64_t n, unsigned char *lb, int pin, bool mid_barrier) {
+      const bool skip_w = __builtin_amdgcn_readfirstlane(pin) == 2;
+      const int64_t t0 = n * C;
+      const int Lc = chunk_len(n);
+      const char *q0 = qb + t0 * rowb, *k0 = kb + t0 * rowb, *e0 = eb + t0 * rowb, *vv = vb + t0 * rowb;
+      // (held as wide vector values, not arrays, so that they stay in
+      // registers across the barrier)
+      typedef unsigned u32x16 __attribute__((ext_vector_type(16)));
+      u32x16 rq = {}, rk = {}, rw = {};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = r0 + 16 * jj;
+        const uint32_t off = r < Lc ? (uint32_t)(r * rowb) + rcol : rcol;
+        const uint4 x = *reinterpret_cast<const uint4 *>(q0 + off);
+        const uint4 y = *reinterpret_cast<const uint4 *>(k0 + off);
+        rq[4 * jj] = x.x; rq[4 * jj + 1] = x.y; rq[4 * jj + 2] = x.z; rq[4 * jj + 3] = x.w;
+        rk[4 * jj] = y.x; rk[4 * jj + 1] = y.y; rk[4 * jj + 2] = y.z; rk[4 * jj + 3] = y.w;
+        if (!skip_w) {
+          const uint4 z = *reinterpret_cast<const uint4 *>(e0 + off);
+          rw[4 * jj] = z.x; rw[4 * jj + 1] = z.y; rw[4 * jj + 2] = z.z; rw[4 * jj + 3] = z.w;
+        }
+      }
+      const uint4 rv = *reinterpret_cast<const uint4 *>(vv + (vrow < Lc ? voff : vcol));
+      const bf16 *tm = tseq + n * CHUNKW;
+      const uint4 rt0 = *reinterpret_cast<const uint4 *>(tm + (li * 64 + l) * 8);
+      uint4 rt1 = {0u, 0u, 0u, 0u};
+      if (li < 2) rt1 = *reinterpret_cast<const uint4 *>(tm + ((li + 4) * 64 + l) * 8);
+      const float *sc = reinterpret_cast<const float *>(tm + TDUMP + MDUMP);
+      float rs = 0.0f;
+      if (li == 0) rs = sc[l];
+      else if (GATED && li == 1) rs = sc[64 + l];
+      if (mid_barrier) lds_barrier();  // ---- B2 (no wait for the loads)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = 4 * jj + li;
+        *reinterpret_cast<uint4 *>(lb + L::Q + 1024 * j + 16 * l) =
+            uint4{rq[4 * jj], rq[4 * jj + 1], rq[4 * jj + 2], rq[4 * jj + 3]};
+        *reinterpret_cast<uint4 *>(lb + L::K + 1024 * j + 16 * l) =
+            uint4{rk[4 * jj], rk[4 * jj + 1], rk[4 * jj + 2], rk[4 * jj + 3]};
+        if (!skip_w)
+          *reinterpret_cast<uint4 *>(lb + L::W + 1024 * j + 16 * l) =
+              uint4{rw[4 * jj], rw[4 * jj + 1], rw[4 * jj + 2], rw[4 * jj + 3]};
+      }
+      *reinterpret_cast<uint4 *>(lb + L::V + 1024 * li + 16 * l) = rv;
+      *reinterpret_cast<uint4 *>(lb + L::TM + (li * 64 + l) * 16) = rt0;
+      if (li < 2) *reinterpret_cast<uint4 *>(lb + L::TM + ((li + 4) * 64 + l) * 16) = rt1;
+      if (li == 0) reinterpret_cast<float *>(lb + L::BETA)[l] = rs;
+      else if (GATED && li == 1) reinterpret_cast<float *>(lb + L::G)[l] = rs;
+    };
+    int pin_next = load_pin(1);
+    if (Nb > 0) fill(0, lb0, load_pin(0), false);
+    lds_barrier();
+    auto body = [&](int64_t n, unsigned char *nxt) {
+      const int pin = pin_next;
+      pin_next = load_pin(n + 2);
+      if (n + 1 < Nb)
+        fill(n + 1, nxt, pin, true);
+      else
+        lds_barrier();  // ---- B2
+      lds_barrier();    // ---- B1 of the next chunk
+    };
+    for (int64_t n = 0; n < Nb; n += 2) {
+      body(n, lb1);
+      if (n + 1 < Nb) body(n + 1, lb0);
+    }
   }
 }
 
@@ -977,7 +942,7 @@ void launch_both(const ChunkArgs &a, bf16 *tw, int64_t N, hipStream_t s, const E
     }
   }
   const int64_t groups = (nseq + 7) / 8;
-  hipLaunchKernelGGL((chunk_sweep_kernel<GATED, KRES, VL>), dim3((unsigned)(groups * 8 * NT)), dim3(256), 0, s, a,
+  hipLaunchKernelGGL((chunk_sweep_kernel<GATED, KRES, VL>), dim3((unsigned)(groups * 8 * NT)), dim3(512), 0, s, a,
                      (const bf16 *)tw, N);
   prof_mark(s, "chunk_sweep_kernel");
 }
