@@ -59,10 +59,11 @@ constexpr int TDUMP = 6 * 64 * 8;  // bf16 elements per chunk
 // (block 2 j + 0 / 2 j + 1), lane (l16, g) holding score row 16 mt + l16 at
 // key positions 32 s + 4 g + {0..3} and 32 s + 16 + 4 g + {0..3}.
 constexpr int MDUMP = 12 * 64 * 8;
-// Then the chunk's scalars as fp32: beta (zero past the chunk end) and the
-// cumulative log decay (constant past the chunk end; gated form only), so that
-// the sweep reads them as two 256-byte pieces rather than 64 strided words.
-constexpr int SDUMP = 2 * 64 * 2;  // in bf16 elements
+// Then the chunk's scalars as fp32: beta (zero past the chunk end) and, in the
+// gated form, the decay factors e^{g_t} and e^{g_L - g_t} (g the cumulative
+// log decay, constant past the chunk end), so that the sweep reads them as
+// 256-byte pieces rather than 64 strided words, and evaluates no exponential.
+constexpr int SDUMP = 3 * 64 * 2;  // in bf16 elements
 constexpr int CHUNKW = TDUMP + MDUMP + SDUMP;  // workspace per chunk
 
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
@@ -450,9 +451,13 @@ __global__ __launch_bounds__(256, 3) void chunk_tinv_kernel(ChunkArgs a, bf16 *t
     const int row = 16 * mt + (ln & 15), c0 = 32 * sb + 4 * (ln >> 4);
     *reinterpret_cast<bf16x8 *>(dst + e * 8) = cat8(ld4(&sTr[row][c0]), ld4(&sTr[row][c0 + 16]));
   }
-  // beta and the cumulative log decay, as the sweep reads them
-  if (tid < C) reinterpret_cast<float *>(dst + TDUMP + MDUMP)[tid] = sBeta[tid];
-  else if (GATED && tid < 2 * C) reinterpret_cast<float *>(dst + TDUMP + MDUMP)[tid] = sG[tid - C];
+  // beta and the decay factors, as the sweep reads them
+  {
+    float *sc = reinterpret_cast<float *>(dst + TDUMP + MDUMP);
+    if (tid < C) sc[tid] = sBeta[tid];
+    else if (GATED && tid < 2 * C) sc[tid] = __expf(sG[tid - C]);
+    else if (GATED && tid < 3 * C) sc[tid] = __expf(sG[C - 1] - sG[tid - 2 * C]);
+  }
   __syncthreads();  // the next chunk's rows overwrite Tm's buffers
   }
 }
@@ -508,8 +513,9 @@ struct SwBuf {
   static constexpr int W = K + C * KD * 2;  // bf16 [64][128] write-key residual E, or k~ itself (sx128)
   static constexpr int V = W + C * KD * 2;  // bf16 [64][32] value tile
   static constexpr int BETA = V + C * 32 * 2;  // f32 [64], zero past the chunk end
-  static constexpr int G = BETA + C * 4;       // f32 [64] cumulative log decay
-  static constexpr int TM = G + C * 4;         // bf16x8 [6][64] (I + A)^-1 operands (TDUMP order)
+  static constexpr int G = BETA + C * 4;       // f32 [64] e^{g_t} (g the cumulative log decay)
+  static constexpr int GR = G + C * 4;         // f32 [64] e^{g_L - g_t}
+  static constexpr int TM = GR + C * 4;        // bf16x8 [6][64] (I + A)^-1 operands (TDUMP order)
   static constexpr int BYTES = TM + 6 * 64 * 16;
 };
 
@@ -593,19 +599,29 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
     int pin_next = load_pin(0);
     lds_barrier();
 
-    auto body = [&](int64_t n, const unsigned char *cur) {
+    // The state update reads its operands from LDS one stage ahead of the
+    // matrix-core instructions that use them (the scheduling fences keep the
+    // compiler from regrouping the reads behind their uses); its first
+    // operands do not depend on Delta and are requested before it is formed.
+    // PIN: the chunk's write keys are d_min k.
+    auto body = [&](auto PIN, int64_t n, const unsigned char *cur) __attribute__((always_inline)) {
+      constexpr bool pinned = KRES && decltype(PIN)::value;
+      // the state update reads one key matrix (k on a pinned chunk, k~ without
+      // the residual form) or two (k and E)
+      constexpr bool two = KRES && !pinned;
+      constexpr int KPS = two ? 2 : 4;        // key tiles per stage
+      constexpr int NST = 2 * (8 / KPS);      // stages
       const bf16 *sK = reinterpret_cast<const bf16 *>(cur + L::K);
       const bf16 *sW = reinterpret_cast<const bf16 *>(cur + L::W);
+      const bf16 *sU = KRES ? sK : sW;        // k (with E as the second), or k~
       const bf16 *sV = reinterpret_cast<const bf16 *>(cur + L::V);
       const float *sBeta = reinterpret_cast<const float *>(cur + L::BETA);
       const float *sG = reinterpret_cast<const float *>(cur + L::G);
+      const float *sGR = reinterpret_cast<const float *>(cur + L::GR);
+      pin_next = load_pin(n + 1);
+
 #pragma unroll
       for (int j = 0; j < 6; ++j) Tm[j] = *reinterpret_cast<const bf16x8 *>(cur + L::TM + (j * 64 + l) * 16);
-      const bool pinned = __builtin_amdgcn_readfirstlane(pin_next) == 2;
-      pin_next = load_pin(n + 1);
-      const bool more = n + 1 < Nb;
-      const float gL = GATED ? sG[C - 1] : 0.0f;
-
       // X = K S^T (token rows x this wave's 16 value rows)
       floatx4 X[4];
 #pragma unroll
@@ -620,17 +636,17 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) X[mt] = mfma32(ak[mt], Bl[s], X[mt]);
       }
-      // R = beta (V - e^g X); V[16 mt + 4 g + i][vc + l16] by one transposed read
+      // R = beta (V - e^g X); V[16 mt + 4 g + i][vc + l16] by one transposed
+      // read, beta and e^g of tokens 16 mt + 4 g .. + 3 as one piece each
       floatx4 R[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const bf16x4 vv = ld4_tr(sV + (16 * mt + 4 * g + (l16 >> 2)) * 32 + 16 * hw + 4 * (l16 & 3));
+        const floatx4 bt = *reinterpret_cast<const floatx4 *>(sBeta + 16 * mt + 4 * g);
+        floatx4 em = {1.f, 1.f, 1.f, 1.f};
+        if (GATED) em = *reinterpret_cast<const floatx4 *>(sG + 16 * mt + 4 * g);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * mt + 4 * g + i;
-          const float em = GATED ? __expf(sG[t]) : 1.0f;
-          R[mt][i] = sBeta[t] * (to_f32(vv[i]) - em * X[mt][i]);
-        }
+        for (int i = 0; i < 4; ++i) R[mt][i] = bt[i] * (to_f32(vv[i]) - em[i] * X[mt][i]);
       }
       bf16x8 Rh[2], Rl[2];
       split8(R[0], R[1], Rh[0], Rl[0]);
@@ -649,6 +665,13 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       D[3] = mfma32(Tm[5], Rh[1], D[3]);
       D[2] = mfma32(Tm[3], Rl[1], D[2]);
       D[3] = mfma32(Tm[5], Rl[1], D[3]);
+      // the state update's first operands (stage 0: slab 0, key tiles 0 ..)
+      bf16x8 ua[4], ub[4], una[4], unb[4];
+#pragma unroll
+      for (int u = 0; u < KPS; ++u) {
+        ua[u] = lda_tr_tile_order(sU, u, 0, g, l16);
+        if (two) ub[u] = lda_tr_tile_order(sW, u, 0, g, l16);
+      }
       // Delta for the outputs (output waves), as tile-order hi/lo operands
       bf16x8 Dh[2], Dl[2];
 #pragma unroll
@@ -657,63 +680,71 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
         ddump[hw][2 * s][l] = Dh[s];
         ddump[hw][2 * s + 1][l] = Dl[s];
       }
-      // the state update's Delta: decayed to the chunk end, and scaled by
-      // d_min when the write keys are d_min k (otherwise the same operands)
-      if (GATED || pinned) {
+      // the state update's Delta, decayed to the chunk end (and scaled by
+      // d_min when the write keys are d_min k); without decay the same
+      // operands serve, and d_min scales the pinned chunk's product instead
+      if (GATED) {
         const float dscale = pinned ? a.d_min : 1.0f;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt) {
+          const floatx4 gr = *reinterpret_cast<const floatx4 *>(sGR + 16 * mt + 4 * g);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float f = dscale;
-            if (GATED) f *= __expf(gL - sG[16 * mt + 4 * g + i]);
-            D[mt][i] *= f;
-          }
+          for (int i = 0; i < 4; ++i) D[mt][i] *= dscale * gr[i];
+        }
         split8(D[0], D[1], Dh[0], Dl[0]);
         split8(D[2], D[3], Dh[1], Dl[1]);
       }
       lds_barrier();  // ---- B2: Delta is in LDS, the output waves are done with S_n
-      // S <- e^{g_L} S + K~^T Delta
+      // S <- e^{g_L} S + K~^T Delta, stage by stage
+      constexpr bool apart = pinned && !GATED;  // K^T Delta formed apart, then d_min times it added
+      floatx4 P[8];
       if (GATED) {
-        const float decay = __expf(gL);
+        const float decay = sG[C - 1];  // e^{g_L}
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt) ST[kt] = ST[kt] * decay;
       }
-      if (!KRES || !pinned) {
-        // general write keys: K and E (residual form), or k~ alone
+      if (apart) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int kt = 0; kt < 8; ++kt) P[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-          for (int k0 = 0; k0 < 8; k0 += 4) {
-            bf16x8 ak[4], ae[4];
+      for (int st = 0; st < NST; ++st) {
+        const int s = st / (NST / 2), k0 = (st % (NST / 2)) * KPS;
+        if (st + 1 < NST) {
+          const int s1 = (st + 1) / (NST / 2), k1 = ((st + 1) % (NST / 2)) * KPS;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              if (KRES) ak[u] = lda_tr_tile_order(sK, k0 + u, s, g, l16);
-              ae[u] = lda_tr_tile_order(sW, k0 + u, s, g, l16);
-            }
+          for (int u = 0; u < KPS; ++u) {
+            una[u] = lda_tr_tile_order(sU, k1 + u, s1, g, l16);
+            if (two) unb[u] = lda_tr_tile_order(sW, k1 + u, s1, g, l16);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              if (KRES) {
-                ST[k0 + u] = mfma32(ak[u], Dh[s], ST[k0 + u]);
-                ST[k0 + u] = mfma32(ak[u], Dl[s], ST[k0 + u]);
-              }
-              ST[k0 + u] = mfma32(ae[u], Dh[s], ST[k0 + u]);
-              ST[k0 + u] = mfma32(ae[u], Dl[s], ST[k0 + u]);
+        for (int u = 0; u < KPS; ++u) {
+          if (apart) {
+            P[k0 + u] = mfma32(ua[u], Dh[s], P[k0 + u]);
+            P[k0 + u] = mfma32(ua[u], Dl[s], P[k0 + u]);
+          } else {
+            ST[k0 + u] = mfma32(ua[u], Dh[s], ST[k0 + u]);
+            ST[k0 + u] = mfma32(ua[u], Dl[s], ST[k0 + u]);
+            if (two) {
+              ST[k0 + u] = mfma32(ub[u], Dh[s], ST[k0 + u]);
+              ST[k0 + u] = mfma32(ub[u], Dl[s], ST[k0 + u]);
             }
           }
         }
-      } else {
-        // write keys d_min k (Delta carries d_min)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          bf16x8 ak[8];
-#pragma unroll
-          for (int kt = 0; kt < 8; ++kt) ak[kt] = lda_tr_tile_order(sK, kt, s, g, l16);
-#pragma unroll
-          for (int kt = 0; kt < 8; ++kt) ST[kt] = mfma32(ak[kt], Dh[s], ST[kt]);
-#pragma unroll
-          for (int kt = 0; kt < 8; ++kt) ST[kt] = mfma32(ak[kt], Dl[s], ST[kt]);
+        for (int u = 0; u < KPS; ++u) {
+          ua[u] = una[u];
+          if (two) ub[u] = unb[u];
         }
+      }
+      if (apart) {
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ST[kt][i] = fmaf(a.d_min, P[kt][i], ST[kt][i]);
       }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -723,9 +754,15 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       }
       lds_barrier();  // ---- B1 of the next chunk
     };
+    auto run = [&](int64_t n, const unsigned char *cur) __attribute__((always_inline)) {
+      if (__builtin_amdgcn_readfirstlane(pin_next) == 2)
+        body(IConst<1>{}, n, cur);
+      else
+        body(IConst<0>{}, n, cur);
+    };
     for (int64_t n = 0; n < Nb; n += 2) {
-      body(n, lb0);
-      if (n + 1 < Nb) body(n + 1, lb1);
+      run(n, lb0);
+      if (n + 1 < Nb) run(n + 1, lb1);
     }
     if (a.S_out) {
 #pragma unroll
@@ -764,7 +801,7 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
         bf16x8 aq[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) aq[s] = lda_tile_order(sQ, 16 * mts[u] + l16, s, g);
-        const float eg = GATED ? __expf(sG[16 * mts[u] + l16]) : 1.0f;  // token column l16
+        const float eg = GATED ? sG[16 * mts[u] + l16] : 1.0f;  // e^g of token column l16
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -822,8 +859,8 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
     // 4 j + l / 16, 16-byte piece l % 16 stored at position (l % 16) ^ (row %
     // 16), the sx128 layout), block li of the value tile (rows 16 li + l / 4,
     // piece l % 4), blocks li and li + 4 (< 6) of the (I + A)^-1 operands, and
-    // (li = 0) beta or (li = 1) the cumulative log decay, both as the UT
-    // transform writes them (zero past the chunk end, constant past it).
+    // (li = 0) beta, (li = 1) e^{g_t} or (li = 2) e^{g_L - g_t}, as the UT
+    // transform writes them (beta zero past the chunk end, g constant past it).
     // Rows past T read the chunk's first row (their beta is zero).
     const int li = w - 4;
     const char *qb = reinterpret_cast<const char *>(static_cast<const bf16 *>(a.q) + base);
@@ -867,7 +904,7 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       const float *sc = reinterpret_cast<const float *>(tm + TDUMP + MDUMP);
       float rs = 0.0f;
       if (li == 0) rs = sc[l];
-      else if (GATED && li == 1) rs = sc[64 + l];
+      else if (GATED && li < 3) rs = sc[64 * li + l];
       if (mid_barrier) lds_barrier();  // ---- B2 (no wait for the loads)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -885,6 +922,7 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       if (li < 2) *reinterpret_cast<uint4 *>(lb + L::TM + ((li + 4) * 64 + l) * 16) = rt1;
       if (li == 0) reinterpret_cast<float *>(lb + L::BETA)[l] = rs;
       else if (GATED && li == 1) reinterpret_cast<float *>(lb + L::G)[l] = rs;
+      else if (GATED && li == 2) reinterpret_cast<float *>(lb + L::GR)[l] = rs;
     };
     int pin_next = load_pin(1);
     if (Nb > 0) fill(0, lb0, load_pin(0), false);

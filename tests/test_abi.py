@@ -152,8 +152,8 @@ def test_workspace_bytes(lib):
     # phase 2 on the matrix cores keeps, per chunk, the six 16 x 32 blocks of
     # (I + A)^-1 on and below the diagonal (bf16: each lane's 4 + 4 columns of
     # two 16-wide halves), the intra-chunk scores in the same blocks as hi/lo
-    # bf16 pairs, and beta and the cumulative log decay (fp32)
-    wy = 4 * 16 * 64 * (6 * 16 * 32 * 2 * 3 + 2 * 64 * 4)
+    # bf16 pairs, and beta and the two decay factors e^g_t, e^(g_L - g_t) (fp32)
+    wy = 4 * 16 * 64 * (6 * 16 * 32 * 2 * 3 + 3 * 64 * 4)
     assert lib.osdn_chunk_fwd_workspace_bytes(ctypes.byref(d)) == wy
     assert lib.osdn_fwd_workspace_bytes(ctypes.byref(d)) == 4 * 4096 * 16 * 128 * 2 + scan + wy
     d.dtype = osdn.F32
