@@ -22,11 +22,11 @@
 //    S    <- e^{g_L} S + Delta^T (e^{g_L - g} . K~)
 //
 // Tm and M depend only on the chunk's keys and queries, so the sweep carries
-// no triangular solve: two of its waves run the state-dependent chain (K S^T,
-// R, Tm R, the state update), two bring in the next chunk and form the
-// outputs, with two barriers per chunk.  The key rows serve both as row
-// operands and, through transposed LDS reads, as the token-major operand of
-// the state update.
+// no triangular solve.  It runs eight waves: two run the state-dependent
+// chain (K S^T, R, Tm R, the state update), two form the outputs, four bring
+// the next chunk's rows into the other LDS buffer; two barriers per chunk.
+// The key rows serve both as row operands and, through transposed LDS reads,
+// as the token-major operand of the state update.
 //
 // Precision: intermediates that are not bf16 (S, R, Delta, the scores) enter
 // every product as a hi + lo pair of bf16; the write key in its residual form
