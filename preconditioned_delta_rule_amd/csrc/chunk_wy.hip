@@ -620,10 +620,12 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       const float *sGR = reinterpret_cast<const float *>(cur + L::GR);
       pin_next = load_pin(n + 1);
 
-#pragma unroll
-      for (int j = 0; j < 6; ++j) Tm[j] = *reinterpret_cast<const bf16x8 *>(cur + L::TM + (j * 64 + l) * 16);
-      // X = K S^T (token rows x this wave's 16 value rows)
+      // X = K S^T (token rows x this wave's 16 value rows).  V and beta do
+      // not depend on S: their reads go out behind the key operands of the
+      // first two slabs, so that they are in place when X is done.
       floatx4 X[4];
+      bf16x4 vv[4];
+      floatx4 bt[4], em[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) X[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -631,22 +633,33 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
         bf16x8 ak[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) ak[mt] = lda_tile_order(sK, 16 * mt + l16, s, g);
+        if (s == 0) {
+          // V[16 mt + 4 g + i][vc + l16] by one transposed read
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) vv[mt] = ld4_tr(sV + (16 * mt + 4 * g + (l16 >> 2)) * 32 + 16 * hw + 4 * (l16 & 3));
+        } else if (s == 1) {
+          // beta and e^g of tokens 16 mt + 4 g .. + 3 as one piece each
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) bt[mt] = *reinterpret_cast<const floatx4 *>(sBeta + 16 * mt + 4 * g);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) X[mt] = mfma32(ak[mt], Bh[s], X[mt]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) X[mt] = mfma32(ak[mt], Bl[s], X[mt]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // R = beta (V - e^g X); V[16 mt + 4 g + i][vc + l16] by one transposed
-      // read, beta and e^g of tokens 16 mt + 4 g .. + 3 as one piece each
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        em[mt] = GATED ? *reinterpret_cast<const floatx4 *>(sG + 16 * mt + 4 * g) : floatx4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+      for (int j = 0; j < 6; ++j) Tm[j] = *reinterpret_cast<const bf16x8 *>(cur + L::TM + (j * 64 + l) * 16);
+      // R = beta (V - e^g X)
       floatx4 R[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const bf16x4 vv = ld4_tr(sV + (16 * mt + 4 * g + (l16 >> 2)) * 32 + 16 * hw + 4 * (l16 & 3));
-        const floatx4 bt = *reinterpret_cast<const floatx4 *>(sBeta + 16 * mt + 4 * g);
-        floatx4 em = {1.f, 1.f, 1.f, 1.f};
-        if (GATED) em = *reinterpret_cast<const floatx4 *>(sG + 16 * mt + 4 * g);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) R[mt][i] = bt[i] * (to_f32(vv[i]) - em[i] * X[mt][i]);
+        for (int i = 0; i < 4; ++i) R[mt][i] = bt[mt][i] * (to_f32(vv[mt][i]) - em[mt][i] * X[mt][i]);
       }
       bf16x8 Rh[2], Rl[2];
       split8(R[0], R[1], Rh[0], Rl[0]);
@@ -707,6 +720,22 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt) P[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
+      // key tiles 2 sp, 2 sp + 1 are final after stage done(sp); they are
+      // split into the next chunk's operands (and left for the output waves)
+      // during the following stage's products
+      constexpr bool OVL = !GATED;
+      auto done = [](int sp) { return NST / 2 + (2 * sp + 1) / KPS; };
+      auto finish = [&](int sp) __attribute__((always_inline)) {
+        if (apart) {
+#pragma unroll
+          for (int kt = 2 * sp; kt < 2 * sp + 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ST[kt][i] = fmaf(a.d_min, P[kt][i], ST[kt][i]);
+        }
+        split8(ST[2 * sp], ST[2 * sp + 1], Bh[sp], Bl[sp]);
+        sdump[hw][2 * sp][l] = Bh[sp];
+        sdump[hw][2 * sp + 1][l] = Bl[sp];
+      };
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
         const int s = st / (NST / 2), k0 = (st % (NST / 2)) * KPS;
@@ -733,6 +762,9 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
             }
           }
         }
+#pragma unroll
+        for (int sp = 0; sp < 4; ++sp)
+          if (OVL && done(sp) == st - 1) finish(sp);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < KPS; ++u) {
@@ -740,18 +772,9 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
           if (two) ub[u] = unb[u];
         }
       }
-      if (apart) {
 #pragma unroll
-        for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ST[kt][i] = fmaf(a.d_min, P[kt][i], ST[kt][i]);
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        split8(ST[2 * s], ST[2 * s + 1], Bh[s], Bl[s]);
-        sdump[hw][2 * s][l] = Bh[s];
-        sdump[hw][2 * s + 1][l] = Bl[s];
-      }
+      for (int sp = 0; sp < 4; ++sp)
+        if (!OVL || done(sp) == NST - 1) finish(sp);
       lds_barrier();  // ---- B1 of the next chunk
     };
     auto run = [&](int64_t n, const unsigned char *cur) __attribute__((always_inline)) {
