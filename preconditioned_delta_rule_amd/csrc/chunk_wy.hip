@@ -622,7 +622,7 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
 
       // X = K S^T (token rows x this wave's 16 value rows).  V and beta do
       // not depend on S: their reads go out behind the key operands of the
-      // first two slabs, so that they are in place when X is done.
+      // second and third slabs, so that they are in place when X is done.
       floatx4 X[4];
       bf16x4 vv[4];
       floatx4 bt[4], em[4];
@@ -633,14 +633,17 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
         bf16x8 ak[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) ak[mt] = lda_tile_order(sK, 16 * mt + l16, s, g);
-        if (s == 0) {
+        if (s == 1) {
           // V[16 mt + 4 g + i][vc + l16] by one transposed read
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) vv[mt] = ld4_tr(sV + (16 * mt + 4 * g + (l16 >> 2)) * 32 + 16 * hw + 4 * (l16 & 3));
-        } else if (s == 1) {
+        } else if (s == 2) {
           // beta and e^g of tokens 16 mt + 4 g .. + 3 as one piece each
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) bt[mt] = *reinterpret_cast<const floatx4 *>(sBeta + 16 * mt + 4 * g);
+        } else if (s == 3 && !GATED) {
+#pragma unroll
+          for (int j = 0; j < 6; ++j) Tm[j] = *reinterpret_cast<const bf16x8 *>(cur + L::TM + (j * 64 + l) * 16);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -652,8 +655,11 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
         em[mt] = GATED ? *reinterpret_cast<const floatx4 *>(sG + 16 * mt + 4 * g) : floatx4{1.f, 1.f, 1.f, 1.f};
+      if (GATED) {
 #pragma unroll
-      for (int j = 0; j < 6; ++j) Tm[j] = *reinterpret_cast<const bf16x8 *>(cur + L::TM + (j * 64 + l) * 16);
+        for (int j = 0; j < 6; ++j) Tm[j] = *reinterpret_cast<const bf16x8 *>(cur + L::TM + (j * 64 + l) * 16);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       // R = beta (V - e^g X)
       floatx4 R[4];
 #pragma unroll
