@@ -144,7 +144,14 @@ __global__ __launch_bounds__(256, 3) void chunk_tinv_kernel(ChunkArgs a, bf16 *t
   bf16x8 px[4], pe[4], pq[4];
   float pb = 0.0f, pa = 1.0f;
   int ppin = 0;
-  auto fetch = [&](int64_t ci) {
+  // EMIT: the next chunk's start d (thread = coordinate), step scalars and
+  // retention (thread = token).  No vector load is issued after the
+  // prefetch in a chunk, so no wait of the chunk's own work waits for it.
+  float pd = 1.0f, pc = 0.0f, pr = 1.0f;
+  // The loads go out in two parts (a wave's loads queue behind each other):
+  // part 0 at the start of a chunk, part 1 after its scores.
+  auto fetch = [&](int64_t ci, auto PART) {
+    constexpr int part = decltype(PART)::value;
     const int64_t seq = ci / N, n = ci - seq * N;
     const int64_t b = seq / H, h = seq - b * H;
     const int64_t T = seq_len<VL>(a, b), tb = seq_base<VL>(a, b);
@@ -152,28 +159,46 @@ __global__ __launch_bounds__(256, 3) void chunk_tinv_kernel(ChunkArgs a, bf16 *t
     if (VL && t0 >= T) return;  // past a shorter sequence's end: skipped below
     const int Lc = (int)((T - t0) < C ? (T - t0) : C);
     const int64_t base = (tb + t0) * tstride + h * KD;
-    ppin = pins ? __builtin_amdgcn_readfirstlane(pins[ci]) : 0;
+    if constexpr (part == 1) {
+      // queries of this wave's score rows, as B operands (lane (n, g): row
+      // 16 w + n, columns 32 kk + 8 g ..)
+      const int i = 16 * w + l16;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) pq[kk] = ld8(gq + base + (i < Lc ? i : 0) * tstride + 32 * kk + 8 * lq);
+      if (w == 0) {
+        const int64_t gi = (tb + t0 + (l < Lc ? l : 0)) * H + h;
+        pb = a.beta[gi];
+        if constexpr (GATED) pa = a.alpha[gi];
+      }
+      return;
+    }
+    if constexpr (EMIT && !GATED) {
+      // the replay's inputs first (read for pinned chunks too, which do not
+      // use them: every index is in range; the gated form, short of
+      // registers, reads them with the chunk)
+      if (tid < KD) pd = em.dstart[ci * KD + tid];
+      if (tid < C) {
+        const int64_t gi = (tb + t0 + (tid < Lc ? tid : 0)) * H + h;
+        pc = em.cstep[gi];
+        if constexpr (!RVEC) pr = em.r ? em.r[gi] : 1.0f;
+      }
+    }
+    // (made wave-uniform where it is used, so that it is not waited for here
+    // on the folded path)
+    ppin = pins ? pins[ci] : 0;
+    const bool need_e = !EMIT && __builtin_amdgcn_readfirstlane(ppin) != 2;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int vi = tid + 256 * p, i = vi >> 4, c8 = 8 * (vi & 15);
       const int64_t off = base + (i < Lc ? i : 0) * tstride + c8;
       px[p] = ld8(gk + off);
-      if (!EMIT && ppin != 2) pe[p] = ld8(gkt + off);
-    }
-    // queries of this wave's score rows, as B operands (lane (n, g): row
-    // 16 w + n, columns 32 kk + 8 g ..)
-    {
-      const int i = 16 * w + l16;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) pq[kk] = ld8(gq + base + (i < Lc ? i : 0) * tstride + 32 * kk + 8 * lq);
-    }
-    if (w == 0) {
-      const int64_t gi = (tb + t0 + (l < Lc ? l : 0)) * H + h;
-      pb = a.beta[gi];
-      if constexpr (GATED) pa = a.alpha[gi];
+      if (need_e) pe[p] = ld8(gkt + off);
     }
   };
-  if ((int64_t)blockIdx.x < nch) fetch(blockIdx.x);
+  if ((int64_t)blockIdx.x < nch) {
+    fetch(blockIdx.x, IConst<0>{});
+    fetch(blockIdx.x, IConst<1>{});
+  }
   for (int64_t ci = blockIdx.x; ci < nch; ci += gridDim.x) {
   const int64_t seq = ci / N, n = ci - seq * N;
   const int64_t b = seq / H, h = seq - b * H;
@@ -182,7 +207,10 @@ __global__ __launch_bounds__(256, 3) void chunk_tinv_kernel(ChunkArgs a, bf16 *t
   if (VL && t0 >= T) {
     // past a shorter sequence's end (the whole workgroup alike): nothing to
     // form; the next chunk's loads still go out
-    if (ci + (int64_t)gridDim.x < nch) fetch(ci + gridDim.x);
+    if (ci + (int64_t)gridDim.x < nch) {
+      fetch(ci + gridDim.x, IConst<0>{});
+      fetch(ci + gridDim.x, IConst<1>{});
+    }
     continue;
   }
   const int Lc = (int)((T - t0) < C ? (T - t0) : C);
@@ -194,7 +222,7 @@ __global__ __launch_bounds__(256, 3) void chunk_tinv_kernel(ChunkArgs a, bf16 *t
   // and its mark guarantees that every step clips back to d_min (the mark
   // tests the replay's own fp32 expression at the largest key square), so its
   // write keys are d_min k: no replay, no residual.
-  const bool pinned = ppin == 2;
+  const bool pinned = __builtin_amdgcn_readfirstlane(ppin) == 2;
   const float kscale = pinned ? a.d_min : 1.0f;  // write keys d_min k
   const bf16x8 qop[4] = {pq[0], pq[1], pq[2], pq[3]};
 #pragma unroll
@@ -219,15 +247,21 @@ __global__ __launch_bounds__(256, 3) void chunk_tinv_kernel(ChunkArgs a, bf16 *t
       sG[l] = x;
     }
   }
+  float d0 = pd;  // this chunk's start d of coordinate tid (EMIT)
   if constexpr (EMIT) {
     // step scalars and retention of the chunk's tokens, for the replay
     if (!pinned && tid < C) {
-      const int64_t gi = (tb + t0 + (tid < Lc ? tid : 0)) * H + h;
-      sC[tid] = em.cstep[gi];
-      if constexpr (!RVEC) sR[tid] = em.r ? em.r[gi] : 1.0f;
+      if constexpr (GATED) {
+        const int64_t gi = (tb + t0 + (tid < Lc ? tid : 0)) * H + h;
+        sC[tid] = em.cstep[gi];
+        if constexpr (!RVEC) sR[tid] = em.r ? em.r[gi] : 1.0f;
+      } else {
+        sC[tid] = pc;
+        if constexpr (!RVEC) sR[tid] = pr;
+      }
     }
   }
-  if (ci + (int64_t)gridDim.x < nch) fetch(ci + gridDim.x);
+  if (ci + (int64_t)gridDim.x < nch) fetch(ci + gridDim.x, IConst<0>{});
   __syncthreads();
   if constexpr (EMIT) {
     // the replay of d through the chunk (EMIT, chunks not pinned): one thread
@@ -235,7 +269,7 @@ __global__ __launch_bounds__(256, 3) void chunk_tinv_kernel(ChunkArgs a, bf16 *t
     if (!pinned) {
       if (tid < KD) {
         const int c = tid;
-        float d = em.dstart[ci * KD + c];
+        float d = GATED ? em.dstart[ci * KD + c] : d0;
         const float lo = em.clamp ? em.d_min : -INFINITY, hi = em.clamp ? em.d_max : INFINITY;
         auto step = [&](int u, float ru) {
           const float kv = to_f32(sKl[u][c]);
@@ -283,21 +317,50 @@ __global__ __launch_bounds__(256, 3) void chunk_tinv_kernel(ChunkArgs a, bf16 *t
   // scores of token rows [16 w, 16 w + 16): tiles (jt, w) of M^T = K~ Q^T,
   // jt <= w (lane (n, g) of tile jt holds M[16 w + n][16 jt + 4 g + i], the
   // sweep's A operand in tile order), masked to the causal part, with the
-  // decay ratios, as hi/lo bf16 pairs
+  // decay ratios, as hi/lo bf16 pairs.  Without decay every wave forms all
+  // four tiles (the ones above the diagonal are masked): no branch between
+  // the operand reads and the products, so the reads of a slab go out
+  // together.
   {
     floatx4 acc[4];
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) acc[jt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    auto prod = [&](auto UK, auto UE) __attribute__((always_inline)) {
+      constexpr bool uk = decltype(UK)::value, ue = decltype(UE)::value;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int ko = 32 * kk + 8 * lq;
+      for (int kk = 0; kk < 4; ++kk) {
+        const int ko = 32 * kk + 8 * lq;
+        bf16x8 ak[4], ae[4];
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        if (jt <= w) {
-          if (KRES || pinned) acc[jt] = mfma32(ld8(&sKl[16 * jt + l16][ko]), qop[kk], acc[jt]);
-          if (!pinned) acc[jt] = mfma32(ld8(&sKh[16 * jt + l16][ko]), qop[kk], acc[jt]);
+        for (int jt = 0; jt < 4; ++jt) {
+          if (uk) ak[jt] = ld8(&sKl[16 * jt + l16][ko]);
+          if (ue) ae[jt] = ld8(&sKh[16 * jt + l16][ko]);
+        }
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          if (uk) acc[jt] = mfma32(ak[jt], qop[kk], acc[jt]);
+          if (ue) acc[jt] = mfma32(ae[jt], qop[kk], acc[jt]);
         }
       }
+    };
+    if constexpr (GATED) {
+      // (the gated form keeps the causal tiles only: its decay ratios need
+      // the registers)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int ko = 32 * kk + 8 * lq;
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          if (jt <= w) {
+            if (KRES || pinned) acc[jt] = mfma32(ld8(&sKl[16 * jt + l16][ko]), qop[kk], acc[jt]);
+            if (!pinned) acc[jt] = mfma32(ld8(&sKh[16 * jt + l16][ko]), qop[kk], acc[jt]);
+          }
+        }
+      }
+    } else if (pinned) {
+      prod(IConst<1>{}, IConst<0>{});
+    } else {
+      prod(IConst<KRES ? 1 : 0>{}, IConst<1>{});
     }
     const int t = 16 * w + l16;
     const float gt = GATED ? sG[t] : 0.0f;
@@ -321,6 +384,9 @@ __global__ __launch_bounds__(256, 3) void chunk_tinv_kernel(ChunkArgs a, bf16 *t
       }
     }
   }
+
+  // the next chunk's queries and scalars (this chunk's are in use no longer)
+  if (ci + (int64_t)gridDim.x < nch) fetch(ci + gridDim.x, IConst<1>{});
 
   // Gram tiles (rt, tj), tj <= rt, three or two per wave so that every wave
   // has a similar share and its product chains interleave:
