@@ -398,8 +398,11 @@ __global__ __launch_bounds__(256, 3) void chunk_tinv_kernel(ChunkArgs a, bf16 *t
     floatx4 acc[3];
 #pragma unroll
     for (int q = 0; q < 3; ++q) acc[q] = floatx4{0.f, 0.f, 0.f, 0.f};
-    auto gram = [&](auto NS) {
+    // (the chunk's mark selects the form outside the loop, so that no branch
+    // separates a slab's operand reads from its products)
+    auto gram = [&](auto NS, auto PIN) __attribute__((always_inline)) {
       constexpr int ns = decltype(NS)::value;
+      constexpr bool pin = decltype(PIN)::value;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int ko = 32 * kk + 8 * lq;
@@ -407,23 +410,30 @@ __global__ __launch_bounds__(256, 3) void chunk_tinv_kernel(ChunkArgs a, bf16 *t
 #pragma unroll
         for (int q = 0; q < ns; ++q) {
           ka[q] = ld8(&sKl[16 * rts[q] + l16][ko]);
-          if (!pinned) bh[q] = ld8(&sKh[16 * tjs[q] + l16][ko]);
-          if (KRES || pinned) bl[q] = ld8(&sKl[16 * tjs[q] + l16][ko]);
+          if (!pin) bh[q] = ld8(&sKh[16 * tjs[q] + l16][ko]);
+          if (KRES || pin) bl[q] = ld8(&sKl[16 * tjs[q] + l16][ko]);
         }
-        if (!pinned) {
+        if (!pin) {
 #pragma unroll
           for (int q = 0; q < ns; ++q) acc[q] = mfma32(ka[q], bh[q], acc[q]);
         }
-        if (KRES || pinned) {
+        if (KRES || pin) {
 #pragma unroll
           for (int q = 0; q < ns; ++q) acc[q] = mfma32(ka[q], bl[q], acc[q]);
         }
       }
     };
-    if (w < 2)
-      gram(IConst<3>{});
-    else
-      gram(IConst<2>{});
+    if (w < 2) {
+      if (pinned)
+        gram(IConst<3>{}, IConst<1>{});
+      else
+        gram(IConst<3>{}, IConst<0>{});
+    } else {
+      if (pinned)
+        gram(IConst<2>{}, IConst<1>{});
+      else
+        gram(IConst<2>{}, IConst<0>{});
+    }
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
       if (q < 2 || w < 2) {
