@@ -726,7 +726,7 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
         for (int mt = 0; mt < 4; ++mt) X[mt] = mfma32(ak[mt], Bh[s], X[mt]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) X[mt] = mfma32(ak[mt], Bl[s], X[mt]);
-        __builtin_amdgcn_sched_barrier(0);
+        if (s < 3) __builtin_amdgcn_sched_barrier(0);  // (R may start under the last slab's products)
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -804,7 +804,8 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       }
       // key tiles 2 sp, 2 sp + 1 are final after stage done(sp); they are
       // split into the next chunk's operands (and left for the output waves)
-      // during the following stage's products
+      // during the following stage's products, or, in the last stage, after
+      // its own products of them
       constexpr bool OVL = !GATED;
       auto done = [](int sp) { return NST / 2 + (2 * sp + 1) / KPS; };
       auto finish = [&](int sp) __attribute__((always_inline)) {
@@ -846,7 +847,7 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
         }
 #pragma unroll
         for (int sp = 0; sp < 4; ++sp)
-          if (OVL && done(sp) == st - 1) finish(sp);
+          if (OVL && (done(sp) == st - 1 || (st == NST - 1 && done(sp) == st))) finish(sp);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < KPS; ++u) {
@@ -856,7 +857,7 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       }
 #pragma unroll
       for (int sp = 0; sp < 4; ++sp)
-        if (!OVL || done(sp) == NST - 1) finish(sp);
+        if (!OVL) finish(sp);
       lds_barrier();  // ---- B1 of the next chunk
     };
     auto run = [&](int64_t n, const unsigned char *cur) __attribute__((always_inline)) {
