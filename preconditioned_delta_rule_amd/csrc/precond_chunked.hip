@@ -1218,15 +1218,17 @@ __global__ __launch_bounds__(256) void scan_solve4_kernel(ScanArgs a, ScanWork w
     bool done = false;
     float cst = 0.0f;  // wave 0, lane = token: the step scalar
     if (fast) {
-      // key squares of this lane's pair over its 16 tokens (rows past the end: 0)
+      // key squares of this lane's pair over its 16 tokens.  Rows past the
+      // chunk end hold copies of its last row (finite); every use of their
+      // squares is weighted by x_t = 0 or lands in a masked token's p0.
       float s0[16], s1[16], pp[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int t = 16 * tq + i;
         float k[2];
         lds_get<TIn, 2>(R + t * RP + c0, k);
-        s0[i] = t < L ? k[0] * k[0] : 0.0f;
-        s1[i] = t < L ? k[1] * k[1] : 0.0f;
+        s0[i] = k[0] * k[0];
+        s1[i] = k[1] * k[1];
         pp[i] = fmaf(d[0], s0[i], d[1] * s1[i]);
       }
       sPw[w * CH + 16 * tq + cp] = reduce_scatter16(pp, cp);  // token 16 tq + cp, this wave's coordinates
