@@ -1241,12 +1241,27 @@ __global__ __launch_bounds__(256) void scan_solve4_kernel(ScanArgs a, ScanWork w
       wave_lds_sync();
       const float *Ai = sA + (n & 1) * (CH * CH);
       float xa[4] = {y, 0.0f, 0.0f, 0.0f};  // four independent chains
+      // the factor's rows and y in batches of four 4-column slabs, each batch
+      // requested before the previous one's products (so the LDS latency is
+      // paid about once, not once per pair of slabs)
+      floatx4 av[2][4], yv[2][4];
+      auto fetch_ay = [&](int bt, int buf) __attribute__((always_inline)) {
 #pragma unroll
-      for (int q = 0; q < CH / 4; ++q) {
-        const floatx4 av = *reinterpret_cast<const floatx4 *>(Ai + (q * 64 + l) * 4);
-        const floatx4 yv = *reinterpret_cast<const floatx4 *>(sYw + 4 * q);
+        for (int u = 0; u < 4; ++u) {
+          av[buf][u] = *reinterpret_cast<const floatx4 *>(Ai + ((4 * bt + u) * 64 + l) * 4);
+          yv[buf][u] = *reinterpret_cast<const floatx4 *>(sYw + 4 * (4 * bt + u));
+        }
+      };
+      fetch_ay(0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xa[i] = fmaf(av[i], yv[i], xa[i]);
+      for (int bt = 0; bt < CH / 16; ++bt) {
+        if (bt + 1 < CH / 16) fetch_ay(bt + 1, (bt + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xa[i] = fmaf(av[bt & 1][u][i], yv[bt & 1][u][i], xa[i]);
+        __builtin_amdgcn_sched_barrier(0);
       }
       const float x = tok ? (xa[0] + xa[1]) + (xa[2] + xa[3]) : 0.0f;
       sXw[l] = x;
