@@ -704,11 +704,17 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
       floatx4 bt[4], em[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) X[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      // (the key operands of slab s + 1 are requested before the products of
+      // slab s)
+      bf16x8 ak[2][4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) ak[0][mt] = lda_tile_order(sK, 16 * mt + l16, 0, g);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        bf16x8 ak[4];
+        if (s + 1 < 4) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) ak[mt] = lda_tile_order(sK, 16 * mt + l16, s, g);
+          for (int mt = 0; mt < 4; ++mt) ak[(s + 1) & 1][mt] = lda_tile_order(sK, 16 * mt + l16, s + 1, g);
+        }
         if (s == 1) {
           // V[16 mt + 4 g + i][vc + l16] by one transposed read
 #pragma unroll
@@ -723,9 +729,9 @@ void chunk_sweep_kernel(ChunkArgs a, const bf16 *tdump, int64_t N) {
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) X[mt] = mfma32(ak[mt], Bh[s], X[mt]);
+        for (int mt = 0; mt < 4; ++mt) X[mt] = mfma32(ak[s & 1][mt], Bh[s], X[mt]);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) X[mt] = mfma32(ak[mt], Bl[s], X[mt]);
+        for (int mt = 0; mt < 4; ++mt) X[mt] = mfma32(ak[s & 1][mt], Bl[s], X[mt]);
         if (s < 3) __builtin_amdgcn_sched_barrier(0);  // (R may start under the last slab's products)
       }
 #pragma unroll
